@@ -1,0 +1,20 @@
+"""fp64 CPU oracle for the Mamba-2 SSD forward and the decode state update.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()``
+and the CPU-baseline leg of ``bench.py`` may import anything from here.  The
+HIP library and its Python binding never import, load or call this package,
+and this package never imports them: the two sides share nothing but the
+seeded input generator.
+
+Contents
+--------
+``serial``   the plain serial recurrence in C (``ssd_oracle.c``), built with
+             gcc + OpenMP and called through ctypes; the definition every GPU
+             result is compared against.
+``forms``    independent NumPy formulations used to pin the serial oracle:
+             a NumPy serial loop, the quadratic (masked semiseparable-matrix)
+             form and the four-step chunked form.
+``metrics``  the two error measures that the parity tolerances are stated in.
+"""
+from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
+from . import forms, metrics  # noqa: F401

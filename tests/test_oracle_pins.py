@@ -1,0 +1,307 @@
+"""Pins for the fp64 oracle: checks against things other than itself.
+
+Every check here runs on the CPU.  The serial C oracle is tied to
+  * hand-derived exact values (tests/golden/hand_derived_recurrence.json),
+  * closed forms (first-order IIR filter, single token, zero decay = causal
+    linear attention, which reduces to library matrix products),
+  * a library routine (scipy.signal.lfilter for the scalar case),
+  * two independent formulations of the same result (brute-force quadratic
+    form and the four-step chunked form of the burn-mamba rustdoc),
+  * invariances the method guarantees (chunk length, split/resume, zero
+    padding, group expansion, decode steps vs forward).
+A final test plants plausible mistakes in a copy of the recurrence and checks
+that these pins catch each one.
+"""
+import json
+import os
+
+import numpy as np
+import pytest
+
+from state_space_sequence_amd.inputs import make_inputs
+
+pytestmark = pytest.mark.filterwarnings("ignore::RuntimeWarning")
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "hand_derived_recurrence.json")
+
+
+def _rand(b=2, L=37, H=4, P=3, N=5, G=2, init=True, seed=0, io="f32"):
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1 if init else 0.0,
+                      seed=seed)
+    return inp
+
+
+def _fwd(oracle_mod, inp, **kw):
+    return oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                              inp["D"], inp["initial_state"], **kw)
+
+
+# ---------------------------------------------------------------- golden
+
+def test_hand_derived_values(oracle_mod):
+    with open(GOLDEN) as f:
+        cases = json.load(f)["cases"]
+    for c in cases:
+        b, L, H, P, N, G = (c[k] for k in ("batch", "seqlen", "nheads", "headdim",
+                                           "dstate", "ngroups"))
+        x = np.array(c["x"], dtype=np.float64).reshape(b, L, H, P)
+        dt = np.array(c["dt"], dtype=np.float64).reshape(b, L, H)
+        Bm = np.array(c["B"], dtype=np.float64).reshape(b, L, G, N)
+        Cm = np.array(c["C"], dtype=np.float64).reshape(b, L, G, N)
+        init = None if c["initial_state"] is None else \
+            np.array(c["initial_state"], dtype=np.float64).reshape(b, H, P, N)
+        y, fin = oracle_mod.forward(x, dt, np.array(c["A"]), Bm, Cm, np.array(c["D"]), init)
+        np.testing.assert_allclose(y.reshape(-1), np.array(c["y"]).reshape(-1),
+                                   rtol=1e-14, atol=1e-14, err_msg=c["name"])
+        np.testing.assert_allclose(fin.reshape(-1), np.array(c["final_state"]).reshape(-1),
+                                   rtol=1e-14, atol=1e-14, err_msg=c["name"])
+
+
+# ---------------------------------------------------------------- closed forms
+
+@pytest.mark.parametrize("L", [1, 5, 40])
+def test_first_order_iir_closed_form(oracle_mod, L):
+    """H=P=N=1, constant dt, B=C=1, x=1: the state is a geometric sum,
+    h_t = dt (1 - a^(t+1)) / (1 - a) + a^(t+1) h_-1 with a = exp(dt A)."""
+    dt0, A0, D0, S0 = 0.3, -1.7, 0.4, 0.25
+    a = np.exp(dt0 * A0)
+    t = np.arange(L)
+    h = dt0 * (1 - a ** (t + 1)) / (1 - a) + a ** (t + 1) * S0
+    y, fin = oracle_mod.forward(np.ones((1, L, 1, 1)), np.full((1, L, 1), dt0),
+                                np.array([A0]), np.ones((1, L, 1, 1)), np.ones((1, L, 1, 1)),
+                                np.array([D0]), np.full((1, 1, 1, 1), S0))
+    np.testing.assert_allclose(y[0, :, 0, 0], h + D0, rtol=1e-13)
+    np.testing.assert_allclose(fin[0, 0, 0, 0], h[-1], rtol=1e-13)
+
+
+def test_scalar_case_is_lfilter(oracle_mod):
+    """With H=P=N=1, B=C=1 and constant dt the recurrence is the IIR filter
+    h_t - a h_{t-1} = dt x_t, i.e. scipy.signal.lfilter([dt], [1, -a], x)."""
+    from scipy.signal import lfilter
+    rng = np.random.default_rng(5)
+    L = 300
+    x = rng.standard_normal(L)
+    dt0, A0 = 0.05, -3.0
+    a = np.exp(dt0 * A0)
+    ref = lfilter([dt0], [1.0, -a], x)
+    y, fin = oracle_mod.forward(x.reshape(1, L, 1, 1), np.full((1, L, 1), dt0),
+                                np.array([A0]), np.ones((1, L, 1, 1)), np.ones((1, L, 1, 1)))
+    np.testing.assert_allclose(y[0, :, 0, 0], ref, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fin[0, 0, 0, 0], ref[-1], rtol=1e-12)
+
+
+def test_single_token_closed_form(oracle_mod):
+    """L=1: y = dt x (B.C) + D x + exp(dt A) S0 C, final = exp(dt A) S0 + dt x (outer) B."""
+    inp = _rand(b=2, L=1, H=4, P=3, N=5, G=2, seed=3)
+    y, fin = _fwd(oracle_mod, inp)
+    x, dt, A, Bm, Cm, D, S0 = (inp[k].astype(np.float64) for k in
+                               ("x", "dt", "A", "B", "C", "D", "initial_state"))
+    g = np.arange(4) // 2
+    for b in range(2):
+        for h in range(4):
+            al = np.exp(dt[b, 0, h] * A[h])
+            Bv, Cv, xv = Bm[b, 0, g[h]], Cm[b, 0, g[h]], x[b, 0, h]
+            exp_fin = al * S0[b, h] + dt[b, 0, h] * np.outer(xv, Bv)
+            exp_y = dt[b, 0, h] * xv * (Bv @ Cv) + D[h] * xv + al * S0[b, h] @ Cv
+            np.testing.assert_allclose(fin[b, h], exp_fin, rtol=1e-13, atol=1e-15)
+            np.testing.assert_allclose(y[b, 0, h], exp_y, rtol=1e-13, atol=1e-15)
+
+
+def test_zero_decay_is_causal_linear_attention(oracle_mod):
+    """A = 0 removes all decay: per (b,h),
+    final = S0 + X^T diag(dt) B  and  y = tril(C B^T) diag(dt) X + D X + C S0^T,
+    each a plain library matrix product."""
+    inp = _rand(b=2, L=23, H=4, P=3, N=5, G=2, seed=4)
+    inp["A"] = np.zeros_like(inp["A"])
+    y, fin = _fwd(oracle_mod, inp)
+    x, dt, Bm, Cm, D, S0 = (inp[k].astype(np.float64) for k in
+                            ("x", "dt", "B", "C", "D", "initial_state"))
+    for b in range(2):
+        for h in range(4):
+            g = h // 2
+            X, Bg, Cg, d = x[b, :, h], Bm[b, :, g], Cm[b, :, g], dt[b, :, h]
+            exp_fin = S0[b, h] + X.T @ np.diag(d) @ Bg
+            exp_y = np.tril(Cg @ Bg.T) @ np.diag(d) @ X + D[h] * X + Cg @ S0[b, h].T
+            np.testing.assert_allclose(fin[b, h], exp_fin, rtol=1e-12, atol=1e-13)
+            np.testing.assert_allclose(y[b, :, h], exp_y, rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------- other formulations
+
+def test_numpy_serial_matches_c(oracle_mod):
+    from oracle.forms import serial_numpy
+    inp = _rand(seed=7)
+    y, fin = _fwd(oracle_mod, inp)
+    y2, fin2 = serial_numpy(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                            inp["D"], inp["initial_state"])
+    np.testing.assert_allclose(y, y2, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(fin, fin2, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("init", [False, True])
+def test_quadratic_form_matches_serial(oracle_mod, init):
+    from oracle.forms import quadratic
+    inp = _rand(b=2, L=29, H=4, P=3, N=5, G=2, init=init, seed=8)
+    y, fin = _fwd(oracle_mod, inp)
+    yq, finq = quadratic(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                         inp["D"], inp["initial_state"])
+    np.testing.assert_allclose(yq, y, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(finq, fin, rtol=1e-11, atol=1e-13)
+
+
+@pytest.mark.parametrize("Q", [1, 2, 4, 8, 16, 32, 64])
+def test_chunked_form_matches_serial(oracle_mod, Q):
+    """Chunk-length invariance: the four-step chunked result equals the serial
+    recurrence for every chunk length, including a ragged last chunk (L=45)."""
+    from oracle.forms import chunked
+    inp = _rand(b=2, L=45, H=4, P=3, N=5, G=2, seed=9)
+    y, fin = _fwd(oracle_mod, inp)
+    yc, finc = chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                       inp["D"], inp["initial_state"], chunk_len=Q)
+    np.testing.assert_allclose(yc, y, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(finc, fin, rtol=1e-10, atol=1e-12)
+
+
+def test_tiny_workload_all_forms_agree(oracle_mod):
+    """The 128-token fp32 workload, brute-forced whole by all three forms."""
+    from oracle.forms import chunked, quadratic
+    inp = make_inputs(1, 128, 2, 16, 16, 1, io_dtype="f32", seed=1234)
+    y, fin = _fwd(oracle_mod, inp)
+    yq, finq = quadratic(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], None)
+    yc, finc = chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"], None, 32)
+    for a, b_ in ((yq, y), (finq, fin), (yc, y), (finc, fin)):
+        np.testing.assert_allclose(a, b_, rtol=1e-10, atol=1e-12)
+
+
+# ---------------------------------------------------------------- invariances
+
+def test_split_resume_invariance(oracle_mod):
+    """Running the first L1 tokens, then the rest from the resulting state,
+    equals one pass: the prefill -> cached state -> continue semantics."""
+    inp = _rand(b=2, L=50, H=4, P=3, N=5, G=2, seed=10)
+    y, fin = _fwd(oracle_mod, inp)
+    L1 = 19
+    sl = lambda a, s: a[:, s]  # noqa: E731
+    y1, s1 = oracle_mod.forward(sl(inp["x"], slice(0, L1)), sl(inp["dt"], slice(0, L1)),
+                                inp["A"], sl(inp["B"], slice(0, L1)), sl(inp["C"], slice(0, L1)),
+                                inp["D"], inp["initial_state"])
+    y2, s2 = oracle_mod.forward(sl(inp["x"], slice(L1, None)), sl(inp["dt"], slice(L1, None)),
+                                inp["A"], sl(inp["B"], slice(L1, None)),
+                                sl(inp["C"], slice(L1, None)), inp["D"], s1)
+    np.testing.assert_allclose(np.concatenate([y1, y2], axis=1), y, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(s2, fin, rtol=1e-13, atol=1e-15)
+
+
+def test_zero_padding_invariance(oracle_mod):
+    """Extra tokens with dt = 0, x = 0, B = C = 0 change neither the earlier
+    outputs nor the final state (decay exp(0) = 1, contribution 0)."""
+    from oracle.forms import chunked
+    inp = _rand(b=1, L=30, H=2, P=3, N=4, G=1, seed=11)
+    y, fin = _fwd(oracle_mod, inp)
+    pad = {k: (np.concatenate([v, np.zeros((v.shape[0], 2) + v.shape[2:], v.dtype)], axis=1)
+               if k in ("x", "dt", "B", "C") else v) for k, v in inp.items()}
+    yp, finp = _fwd(oracle_mod, pad)
+    np.testing.assert_allclose(yp[:, :30], y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(yp[:, 30:], 0.0, atol=0)
+    np.testing.assert_allclose(finp, fin, rtol=1e-14, atol=1e-15)
+    yc, finc = chunked(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                       inp["initial_state"], chunk_len=16)
+    np.testing.assert_allclose(yc, y, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(finc, fin, rtol=1e-10, atol=1e-12)
+
+
+def test_group_expansion(oracle_mod):
+    """G groups equal G = H with B/C repeated so head h sees group h // (H/G);
+    the other plausible map (h % G) gives a different answer."""
+    inp = _rand(b=1, L=20, H=8, P=2, N=3, G=2, seed=12)
+    y, fin = _fwd(oracle_mod, inp)
+    H, G = 8, 2
+    idx_div = np.arange(H) // (H // G)
+    full = dict(inp, B=inp["B"][:, :, idx_div], C=inp["C"][:, :, idx_div])
+    yf, finf = _fwd(oracle_mod, full)
+    np.testing.assert_allclose(yf, y, rtol=1e-14, atol=1e-15)
+    np.testing.assert_allclose(finf, fin, rtol=1e-14, atol=1e-15)
+    idx_mod = np.arange(H) % G
+    wrong = dict(inp, B=inp["B"][:, :, idx_mod], C=inp["C"][:, :, idx_mod])
+    yw, _ = _fwd(oracle_mod, wrong)
+    assert np.max(np.abs(yw - y)) > 1e-3
+
+
+def test_decode_steps_equal_forward(oracle_mod):
+    """Tokens fed one decode step at a time (C oracle with L=1, and the NumPy
+    transcription of the fla decode branch) equal one forward pass."""
+    from oracle.forms import decode_step_numpy
+    inp = _rand(b=2, L=12, H=4, P=3, N=5, G=2, seed=13)
+    y, fin = _fwd(oracle_mod, inp)
+    s_c = inp["initial_state"].astype(np.float64)
+    s_np = s_c.copy()
+    for t in range(12):
+        args = (inp["x"][:, t], inp["dt"][:, t], inp["A"], inp["B"][:, t], inp["C"][:, t],
+                inp["D"])
+        s_c, yc = oracle_mod.state_update(s_c, *args)
+        s_np, ynp = decode_step_numpy(s_np, *args)
+        np.testing.assert_allclose(yc, y[:, t], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(ynp, y[:, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(s_c, fin, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(s_np, fin, rtol=1e-12, atol=1e-14)
+
+
+def test_sampled_slices_equal_full(oracle_mod):
+    inp = _rand(b=3, L=17, H=6, P=2, N=3, G=3, seed=14)
+    y, fin = _fwd(oracle_mod, inp)
+    slices = [(0, 0), (2, 5), (1, 3)]
+    ys, fs = oracle_mod.forward_slices(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                       inp["D"], inp["initial_state"], 3, slices)
+    for i, (b, h) in enumerate(slices):
+        np.testing.assert_array_equal(ys[i], y[b, :, h])
+        np.testing.assert_array_equal(fs[i], fin[b, h])
+
+
+def test_oracle_rejects_bad_shapes(oracle_mod):
+    inp = _rand(b=1, L=4, H=3, P=2, N=2, G=1, seed=15)
+    with pytest.raises(ValueError):
+        oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], ngroups=2)
+
+
+# ---------------------------------------------------------------- planted mistakes
+
+def _mutant_serial(x, dt, A, B, C, D, S0, mistake):
+    """The recurrence with one deliberate mistake, for the sensitivity test."""
+    x, dt, A, B, C, D = (np.asarray(v, dtype=np.float64) for v in (x, dt, A, B, C, D))
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    S = np.zeros((b, H, P, N)) if S0 is None else np.array(S0, dtype=np.float64)
+    y = np.empty_like(x)
+    for t in range(L):
+        g = (np.arange(H) % G) if mistake == "group_mod" else np.arange(H) // (H // G)
+        al = np.exp((1.0 if mistake == "no_dt_in_decay" else dt[:, t]) * A[None, :]
+                    * (-1.0 if mistake == "decay_sign" else 1.0))
+        u = (x[:, t] if mistake == "no_dt_on_input" else dt[:, t, :, None] * x[:, t])
+        Sprev = S
+        S = al[..., None, None] * S + u[..., None] * B[:, t][:, g][:, :, None, :]
+        Sread = Sprev if mistake == "output_before_update" else S
+        Cg = C[:, t][:, g]
+        if mistake == "transposed_state":
+            yt = np.einsum("bhpn,bhp->bhn", Sread, Cg[..., :P]) if N == P else None
+        else:
+            yt = np.einsum("bhpn,bhn->bhp", Sread, Cg)
+        skip = 0.0 if mistake == "no_skip" else D[None, :, None] * x[:, t]
+        y[:, t] = yt + skip
+    return y, S
+
+
+@pytest.mark.parametrize("mistake", ["group_mod", "no_dt_in_decay", "decay_sign",
+                                     "no_dt_on_input", "output_before_update",
+                                     "transposed_state", "no_skip"])
+def test_pins_catch_planted_mistakes(oracle_mod, mistake):
+    """Each plausible mistake in the recurrence breaks at least one pin that
+    does not use the oracle itself: the quadratic brute-force form on a
+    random grouped problem, or the hand-derived golden values."""
+    from oracle.forms import quadratic
+    inp = _rand(b=1, L=9, H=4, P=3, N=3, G=2, seed=16)
+    ym, fm = _mutant_serial(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                            inp["initial_state"], mistake)
+    yq, fq = quadratic(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                       inp["initial_state"])
+    err = max(np.max(np.abs(ym - yq)), np.max(np.abs(fm - fq)))
+    assert err > 1e-6, mistake
