@@ -1,0 +1,382 @@
+"""Benchmark of the libssd chunked SSD forward on one MI355X.
+
+One step = one ``ssd_chunk_scan_fwd`` over the Mamba-2 2.7B-shape SSD layer
+(batch 4, seqlen 8192, 80 heads, headdim 64, d_state 128, 1 group, chunk 256;
+bf16 x/B/C, fp32 dt/A/D/state), every kernel of the chunked algorithm, on
+synthetic seeded inputs already resident in HBM.  Prints one JSON line.
+
+Also reported (not part of ``value``):
+  * per-kernel GPU time from HIP events recorded between the kernels of each
+    timed call (``ssd_chunk_scan_fwd_timed`` on the same stream);
+  * ``roofline`` for the dominant kernel and ``path_roofline`` for the whole
+    call against algorithmic bytes (x, B, C, dt, A, D read once; y and the
+    final state written once; no intermediates);
+  * the decode state update on the b256 / 80-head workload;
+  * ``cpu_baseline``: the fp64 serial oracle on the host cores over a bounded
+    sample of (batch, head) slices of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+BF16_PEAK_TFLOPS = 2500.0      # dense bf16 MFMA
+FP32_PEAK_TFLOPS = 157.3       # fp32 MFMA / vector
+METRIC = "SSD fwd tokens/sec per layer + achieved TFLOP/s & HBM GB/s vs MI355X peak"
+
+
+# ------------------------------------------------------------------ HIP events
+
+class HipEvents:
+    """Minimal ctypes access to hipEvent_* of the HIP runtime torch loaded."""
+
+    def __init__(self):
+        self.lib = ctypes.CDLL("libamdhip64.so")
+        self.lib.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.lib.hipEventCreate.restype = ctypes.c_int
+        self.lib.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventRecord.restype = ctypes.c_int
+        self.lib.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventSynchronize.restype = ctypes.c_int
+        self.lib.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float),
+                                                 ctypes.c_void_p, ctypes.c_void_p]
+        self.lib.hipEventElapsedTime.restype = ctypes.c_int
+        self.lib.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.lib.hipEventDestroy.restype = ctypes.c_int
+
+    def create(self):
+        e = ctypes.c_void_p()
+        rc = self.lib.hipEventCreate(ctypes.byref(e))
+        if rc != 0:
+            raise RuntimeError("hipEventCreate failed (%d)" % rc)
+        return e.value
+
+    def record(self, e, stream_handle):
+        rc = self.lib.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream_handle))
+        if rc != 0:
+            raise RuntimeError("hipEventRecord failed (%d)" % rc)
+
+    def ms(self, a, b):
+        out = ctypes.c_float()
+        rc = self.lib.hipEventElapsedTime(ctypes.byref(out), ctypes.c_void_p(a),
+                                          ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError("hipEventElapsedTime failed (%d)" % rc)
+        return float(out.value)
+
+    def destroy(self, e):
+        self.lib.hipEventDestroy(ctypes.c_void_p(e))
+
+
+# ------------------------------------------------------------------ accounting
+
+def alg_bytes_forward(w, es):
+    """Algorithmic HBM bytes of one forward: inputs read once, outputs once."""
+    b, L, H, P, N, G = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups
+    x = b * L * H * P * es
+    bc = 2 * b * L * G * N * es
+    dt = b * L * H * 4
+    small = 2 * H * 4
+    init = b * H * P * N * 4 if w.init_std > 0 else 0
+    final = b * H * P * N * 4
+    y = b * L * H * P * es
+    return x + bc + dt + small + init + final + y
+
+
+def alg_flops_forward(w):
+    """Chunked-SSD flops with causal triangles counted once."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    nc = -(-L // Q)
+    cb = 2 * (Q * (Q + 1) // 2) * N * b * nc * G
+    state = 2 * P * Q * N * b * nc * H
+    out = (2 * Q * N * P + Q * (Q + 1) * P) * b * nc * H
+    passing = 2 * P * N * b * nc * H
+    return cb + state + out + passing
+
+
+def kernel_alg_bytes(name, w, es):
+    """Algorithmic bytes of one launch of each kernel of the five-kernel split:
+    what that kernel must read and write given its own inputs and outputs."""
+    b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    nc = -(-L // Q)
+    per_chunk_vec = b * H * nc * Q * 4          # acum or dtT
+    states = b * nc * H * P * N * 4
+    ntl = Q // 16
+    cb = b * nc * G * (ntl * (ntl + 1) // 2) * 256 * 4
+    x = b * L * H * P * es
+    bc1 = b * L * G * N * es
+    if name == "k1_dA_cumsum":
+        return b * L * H * 4 + 2 * per_chunk_vec
+    if name == "k2_chunk_cb":
+        return 2 * bc1 + cb
+    if name == "k3_chunk_state":
+        return x + bc1 + 2 * per_chunk_vec + states
+    if name == "k4_state_passing":
+        init = b * H * P * N * 4 if w.init_std > 0 else 0
+        return 2 * states + b * H * nc * 4 + init + b * H * P * N * 4
+    if name == "k5_chunk_scan":
+        return x + bc1 + cb + states + 2 * per_chunk_vec + x
+    return None
+
+
+# ------------------------------------------------------------------ runs
+
+def setup(w, dev):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch, workload_inputs
+    inp = workload_inputs(w)
+    t = to_torch(inp, w.io_dtype, dev)
+    y = torch.empty_like(t["x"])
+    fin = torch.empty((w.batch, w.nheads, w.headdim, w.dstate), dtype=torch.float32,
+                      device=dev)
+    io = libssd.SSD_BF16 if w.io_dtype == "bf16" else libssd.SSD_F32
+    need = libssd.ssd_chunk_scan_fwd_workspace_size(w.batch, w.seqlen, w.nheads, w.headdim,
+                                                    w.dstate, w.ngroups, w.chunk_len, io)
+    ws = torch.empty(need, dtype=torch.uint8, device=dev)
+    return inp, t, y, fin, ws
+
+
+def time_forward(w, dev, steps, warmup, ev):
+    import torch
+    from state_space_sequence_amd import libssd
+    inp, t, y, fin, ws = setup(w, dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    kw = dict(chunk_len=w.chunk_len, y=y, final_state=fin, workspace=ws)
+    for _ in range(warmup):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+    nk = len(libssd.kernel_names())
+    events = [[ev.create() for _ in range(nk + 1)] for _ in range(steps)]
+    stream = torch.cuda.current_stream()
+    sh = stream.cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    h0 = time.perf_counter()
+    ev.record(e0, sh)
+    for k in range(steps):
+        libssd.ssd_chunk_scan_fwd_timed(events[k], *args, **kw)
+    ev.record(e1, sh)
+    torch.cuda.synchronize()
+    h1 = time.perf_counter()
+    total_ms = ev.ms(e0, e1)
+    per_kernel = [sum(ev.ms(events[k][i], events[k][i + 1]) for k in range(steps)) / steps
+                  for i in range(nk)]
+    for row in events:
+        for e in row:
+            ev.destroy(e)
+    ev.destroy(e0)
+    ev.destroy(e1)
+    del t, y, fin, ws
+    return dict(host_s=h1 - h0, gpu_ms=total_ms, per_kernel_ms=per_kernel,
+                names=libssd.kernel_names(), inputs=inp)
+
+
+def time_decode(w, dev, ev, reps=3):
+    """Steps of ssd_state_update over the decode workload, timed with events."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_inputs, to_torch
+    inp = make_inputs(w.batch, w.decode_steps, w.nheads, w.headdim, w.dstate, w.ngroups,
+                      io_dtype=w.io_dtype, init_std=w.init_std, seed=w.seed)
+    t = to_torch(inp, w.io_dtype, dev)
+    xs = [t["x"][:, s].contiguous() for s in range(w.decode_steps)]
+    dts = [t["dt"][:, s].contiguous() for s in range(w.decode_steps)]
+    Bs = [t["B"][:, s].contiguous() for s in range(w.decode_steps)]
+    Cs = [t["C"][:, s].contiguous() for s in range(w.decode_steps)]
+    state = t["initial_state"].clone()
+    ys = [torch.empty_like(xs[0]) for _ in range(w.decode_steps)]
+
+    def run_all():
+        for s in range(w.decode_steps):
+            libssd.ssd_state_update(state, xs[s], dts[s], t["A"], Bs[s], Cs[s], t["D"],
+                                    y=ys[s])
+    run_all()  # warm-up
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, sh)
+    for _ in range(reps):
+        run_all()
+    ev.record(e1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / (reps * w.decode_steps)
+    ev.destroy(e0)
+    ev.destroy(e1)
+    es = 2 if w.io_dtype == "bf16" else 4
+    b, H, P, N, G = w.batch, w.nheads, w.headdim, w.dstate, w.ngroups
+    alg = 2 * b * H * P * N * 4 + b * H * P * es * 2 + 2 * b * G * N * es + b * H * 4 + 2 * H * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    return {"workload": "decode b%d H%d P%d N%d G%d, %d steps, fp32 state, %s x/B/C"
+                        % (b, H, P, N, G, w.decode_steps, w.io_dtype),
+            "us_per_step": round(ms * 1e3, 2),
+            "tokens_per_s": round(b / (ms * 1e-3), 1),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": alg}}
+
+
+def cpu_baseline(w, inp, target_s=12.0):
+    """The fp64 serial oracle on the host cores, on a bounded sample of the
+    workload's (batch, head) slices over the full sequence; tokens/s scaled to
+    the whole workload by the fraction of slices computed."""
+    import numpy as np
+    import oracle
+    oracle.build(force=False)
+    threads = oracle.max_threads()
+    nsl = w.batch * w.nheads
+    order = [(b, h) for b in range(w.batch) for h in range(w.nheads)]
+
+    def run(k):
+        sl = order[:k]
+        t0 = time.perf_counter()
+        # slices are independent: one call per batch row keeps the arrays whole
+        done = 0
+        for b in sorted({s[0] for s in sl}):
+            hs = [h for bb, h in sl if bb == b]
+            x = inp["x"][b:b + 1][:, :, hs]
+            dt = inp["dt"][b:b + 1][:, :, hs]
+            g = np.array(hs) // (w.nheads // w.ngroups)
+            if w.ngroups == 1:
+                Bm, Cm = inp["B"][b:b + 1], inp["C"][b:b + 1]
+                init = None if inp["initial_state"] is None else inp["initial_state"][b:b + 1][:, hs]
+                oracle.forward(x, dt, inp["A"][hs], Bm, Cm, inp["D"][hs], init)
+            else:
+                oracle.forward_slices(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                      inp["D"], inp["initial_state"], w.ngroups,
+                                      [(b, h) for h in hs])
+            done += len(hs)
+            del g
+        return time.perf_counter() - t0, done
+
+    cal_k = min(nsl, max(4, threads))
+    t_cal, _ = run(cal_k)
+    per_slice = t_cal / cal_k
+    k = int(min(nsl, max(cal_k, target_s / max(per_slice, 1e-9))))
+    if k > cal_k:
+        t_run, k = run(k)
+    else:
+        t_run, k = t_cal, cal_k
+    tokens_equiv = w.batch * w.seqlen * (k / nsl)
+    return {"value": round(tokens_equiv / t_run, 1), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": "%d of %d (batch, head) slices, all %d tokens each, fp64 serial "
+                      "recurrence (C, OpenMP over slices), %.1f s; tokens/s scaled by the "
+                      "slice fraction" % (k, nsl, w.seqlen, t_run)}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="mamba2_2p7b")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the other workloads and the decode timing")
+    ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
+                    help="measured HBM traffic per launch of the dominant kernel "
+                         "(from rocprofv3 FETCH_SIZE/WRITE_SIZE runs), if present")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import WORKLOADS
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    libssd.load()
+    dev = torch.device("cuda:0")
+    ev = HipEvents()
+
+    w = WORKLOADS[args.workload]
+    es = 2 if w.io_dtype == "bf16" else 4
+    r = time_forward(w, dev, args.steps, args.warmup, ev)
+    ms_step = r["gpu_ms"] / args.steps
+    tokens = w.batch * w.seqlen
+    value = tokens / (ms_step * 1e-3)
+    flops = alg_flops_forward(w)
+    abytes = alg_bytes_forward(w, es)
+    per = dict(zip(r["names"], r["per_kernel_ms"]))
+    dom = max(per, key=per.get)
+    dom_ms = per[dom]
+    dom_bytes = kernel_alg_bytes(dom, w, es)
+    dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(args.traffic_json):
+        try:
+            tj = json.load(open(args.traffic_json))
+            if tj.get("kernel") == dom and tj.get("workload") == w.name:
+                traffic = tj.get("bytes_per_launch")
+        except (OSError, ValueError):
+            traffic = None
+    path_gbs = abytes / (ms_step * 1e-3) / 1e9
+    path_tflops = flops / (ms_step * 1e-3) / 1e12
+    out = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if w.io_dtype == "bf16" else "f32",
+        "data": "synthetic (seeded; distributions of the Mamba-2 layer initialisation)",
+        "config": {"workload": "Mamba-2 2.7B-shape SSD layer forward" if w.name == "mamba2_2p7b"
+                   else w.name,
+                   "batch": w.batch, "seqlen": w.seqlen, "nheads": w.nheads,
+                   "headdim": w.headdim, "dstate": w.dstate, "ngroups": w.ngroups,
+                   "chunk_len": w.chunk_len, "io_dtype": w.io_dtype,
+                   "state_dtype": "f32", "parallelism": "single GPU"},
+        "roofline": {"bound": "hbm", "kernel": dom, "achieved": round(dom_gbs, 1),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "alg_bytes_per_launch": dom_bytes, "avg_launch_ms": round(dom_ms, 4)},
+        "path_roofline": {"bound": "hbm", "alg_bytes": abytes, "alg_flops": flops,
+                          "achieved_gbs": round(path_gbs, 1),
+                          "achieved_tflops": round(path_tflops, 2),
+                          "frac_hbm": round(path_gbs / HBM_PEAK_GBS, 4),
+                          "frac_mfma_bf16": round(path_tflops / BF16_PEAK_TFLOPS, 4),
+                          "roofline_us": round(max(abytes / (HBM_PEAK_GBS * 1e9),
+                                                   flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6, 2)},
+        "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "host_wall_s": round(r["host_s"], 4),
+    }
+    if not args.no_extra:
+        extra = {}
+        for name in ("mamba2_130m", "grouped_g8"):
+            wx = WORKLOADS[name]
+            rx = time_forward(wx, dev, 10, 3, ev)
+            msx = rx["gpu_ms"] / 10
+            esx = 2 if wx.io_dtype == "bf16" else 4
+            gb = alg_bytes_forward(wx, esx) / (msx * 1e-3) / 1e9
+            extra[name] = {"ms_per_step": round(msx, 4),
+                           "tokens_per_s": round(wx.batch * wx.seqlen / (msx * 1e-3), 1),
+                           "path_frac_hbm": round(gb / HBM_PEAK_GBS, 4),
+                           "per_kernel_ms": {k: round(v, 4) for k, v in
+                                             zip(rx["names"], rx["per_kernel_ms"])}}
+            del rx
+        extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
+        out["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(w, r["inputs"])
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,171 @@
+/*
+ * ssd.h -- C ABI of libssd: the Mamba-2 SSD (state-space duality) chunked
+ * forward pass and the single-token decode state update, as hand-written
+ * HIP kernels for gfx950 (MI355X).
+ *
+ * The operation.  For every batch b and head h, with group g = h / (nheads /
+ * ngroups) and a state h_t of shape [headdim x dstate]:
+ *
+ *     h_t = exp(dt_t * A_h) * h_{t-1} + dt_t * x_t (outer) B_t
+ *     y_t = h_t C_t + D_h * x_t
+ *
+ * (fla `layers/mamba2.py`, `Mamba2.torch_forward`: the decode branch is one
+ * step of this recurrence and the naive branch computes the same thing chunk
+ * by chunk; burn-mamba `Mamba2SsdInput` rustdoc, `ssd_minimal`, Steps 1-4 and
+ * the D skip connection.)  `ssd_chunk_scan_fwd` evaluates it chunk by chunk:
+ * intra-chunk outputs (L o C B^T) X, per-chunk states, an inter-chunk
+ * state-passing scan and the state-to-output term, following the five
+ * kernels of burn-mamba `mamba2/ssd/serial.rs` (`k1_ssd_chunk_cumsum` ..
+ * `k5_ssd_chunk_scan`).  `ssd_state_update` is one token of the recurrence
+ * applied in place to a cached state (the `selective_state_update` call of
+ * the fla layer's decode path).
+ *
+ * Conventions shared by every entry point:
+ *  - All pointers except `stream` are DEVICE pointers to dense row-major
+ *    arrays; the library never dereferences them on the host.
+ *  - dt is the processed time step (already positive: bias, softplus and any
+ *    clamp are applied by the caller).  A is the per-head decay rate (the
+ *    method expects A < 0; any finite value is accepted).
+ *  - x, B, C and y share one element type, `io_dtype` (fp32 or bf16).
+ *    dt, A, D and every state are fp32.  Accumulation is fp32.
+ *  - The caller owns every buffer.  The library allocates no device memory,
+ *    keeps no state between calls and is reentrant.  Work is enqueued on
+ *    `stream` (a hipStream_t; NULL = the legacy default stream) and nothing
+ *    synchronises the host: results are ready when the stream is.
+ *  - Errors are reported as status codes, never by exceptions or aborts.
+ *    Argument validation happens before anything is enqueued, so a call that
+ *    returns SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED or
+ *    SSD_ERR_WORKSPACE has touched no device memory.  SSD_ERR_HIP means a
+ *    launch failed (hipGetLastError); earlier kernels of that call may have
+ *    run, so outputs are undefined.
+ *
+ * Supported shapes (anything else returns SSD_ERR_UNSUPPORTED):
+ *    chunk_len in {16, 32, 64, 128, 256};  headdim a multiple of 16, <= 128;
+ *    dstate a multiple of 16, <= 256.
+ */
+#ifndef LIBSSD_SSD_H
+#define LIBSSD_SSD_H
+
+#include <stddef.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSD_ABI_VERSION 1
+
+typedef enum ssd_status {
+    SSD_OK = 0,
+    SSD_ERR_INVALID_ARGUMENT = 1, /* NULL required pointer, size <= 0,
+                                     nheads % ngroups != 0, unknown dtype   */
+    SSD_ERR_UNSUPPORTED = 2,      /* valid but outside the supported shapes */
+    SSD_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than needed  */
+    SSD_ERR_HIP = 4               /* a kernel launch failed                 */
+} ssd_status;
+
+typedef enum ssd_dtype {
+    SSD_F32 = 0,
+    SSD_BF16 = 1
+} ssd_dtype;
+
+/* Version of this ABI (SSD_ABI_VERSION of the built library). */
+int ssd_abi_version(void);
+
+/* Static, NUL-terminated description of a status code. */
+const char *ssd_status_string(ssd_status status);
+
+/*
+ * Bytes of device workspace `ssd_chunk_scan_fwd` needs for this problem,
+ * written to *bytes.  The same validation as `ssd_chunk_scan_fwd` is applied
+ * (pointers aside); on error *bytes is left unchanged.  The workspace holds
+ * the per-chunk intermediates of the chunked algorithm (decay prefix sums,
+ * the C B^T blocks and the per-chunk fp32 states) and needs no
+ * initialisation.
+ */
+ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
+                                             int headdim, int dstate,
+                                             int ngroups, int chunk_len,
+                                             ssd_dtype io_dtype,
+                                             size_t *bytes);
+
+/*
+ * Chunked SSD forward.
+ *
+ *   x             [batch, seqlen, nheads, headdim]    io_dtype   in
+ *   dt            [batch, seqlen, nheads]             fp32       in
+ *   A             [nheads]                            fp32       in
+ *   B, C          [batch, seqlen, ngroups, dstate]    io_dtype   in
+ *   D             [nheads]                            fp32       in, NULL = 0
+ *   initial_state [batch, nheads, headdim, dstate]    fp32       in, NULL = 0
+ *   y             [batch, seqlen, nheads, headdim]    io_dtype   out
+ *   final_state   [batch, nheads, headdim, dstate]    fp32       out, NULL = skip
+ *   workspace     >= ssd_chunk_scan_fwd_workspace_size bytes, 256-byte aligned
+ *
+ * chunk_len is the chunk length Q of the chunked algorithm; the sequence is
+ * processed as ceil(seqlen / Q) chunks and a ragged last chunk behaves as if
+ * zero-padded (dt = x = B = C = 0 past seqlen), so the final state is that
+ * of token seqlen-1.  y is rounded to io_dtype (round to nearest even for
+ * bf16).  final_state may alias initial_state (a cache updated in place);
+ * no other buffers may overlap.
+ */
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              const float *initial_state, int chunk_len,
+                              int ngroups, int batch, int seqlen, int nheads,
+                              int headdim, int dstate, ssd_dtype io_dtype,
+                              void *y, float *final_state, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/*
+ * Kernels of one `ssd_chunk_scan_fwd` call, for timing.  The count is fixed
+ * for a given library build; names are static strings (NULL when i is out of
+ * range).
+ */
+int ssd_chunk_scan_fwd_kernel_count(void);
+const char *ssd_chunk_scan_fwd_kernel_name(int i);
+
+/*
+ * Diagnostic twin of `ssd_chunk_scan_fwd`: identical arguments, identical
+ * work and results, and in addition events[i] (caller-created hipEvent_t
+ * handles) is recorded on `stream` immediately before kernel i of the call
+ * and events[count] right after the last kernel, so the caller can read each
+ * kernel's GPU time with hipEventElapsedTime.  nevents must be at least
+ * ssd_chunk_scan_fwd_kernel_count() + 1 and every handle non-NULL, else
+ * SSD_ERR_INVALID_ARGUMENT.  A failed event record returns SSD_ERR_HIP.
+ */
+ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const float *initial_state, int chunk_len,
+                                    int ngroups, int batch, int seqlen, int nheads,
+                                    int headdim, int dstate, ssd_dtype io_dtype,
+                                    void *y, float *final_state, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t *events, int nevents);
+
+/*
+ * One decode step, in place.
+ *
+ *   state  [batch, nheads, headdim, dstate]  fp32      in/out
+ *   x      [batch, nheads, headdim]          io_dtype  in
+ *   dt     [batch, nheads]                   fp32      in
+ *   A      [nheads]                          fp32      in
+ *   B, C   [batch, ngroups, dstate]          io_dtype  in
+ *   D      [nheads]                          fp32      in, NULL = 0
+ *   y      [batch, nheads, headdim]          io_dtype  out
+ *
+ * state <- exp(dt A) state + dt x (outer) B, then y = state C + D x, read from
+ * the UPDATED state (the order of the fla decode branch).  y must not
+ * overlap state.  No workspace is needed.
+ */
+ssd_status ssd_state_update(float *state, const void *x, const float *dt,
+                            const float *A, const void *B, const void *C,
+                            const float *D, int ngroups, int batch, int nheads,
+                            int headdim, int dstate, ssd_dtype io_dtype,
+                            void *y, hipStream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LIBSSD_SSD_H */

@@ -1,0 +1,225 @@
+// ssd_api.hip -- the extern "C" entry points declared in include/ssd.h:
+// argument validation, workspace layout and kernel dispatch.  Validation is
+// plain host code that runs before anything is enqueued.
+#include "ssd.h"
+
+#include <stdint.h>
+
+#include "ssd_device.hpp"
+#include "ssd_kernels.hpp"
+
+namespace {
+
+constexpr size_t kAlign = 256;
+
+size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
+
+bool is_pow2_chunk(int q) {
+    return q == 16 || q == 32 || q == 64 || q == 128 || q == 256;
+}
+
+// Checks shared by the workspace query and the forward call.
+ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
+                               int dstate, int ngroups, int chunk_len,
+                               ssd_dtype io_dtype) {
+    if (batch <= 0 || seqlen <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 ||
+        ngroups <= 0 || chunk_len <= 0)
+        return SSD_ERR_INVALID_ARGUMENT;
+    if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (!is_pow2_chunk(chunk_len)) return SSD_ERR_UNSUPPORTED;
+    if (headdim % 16 != 0 || headdim > ssd::kMaxHeaddim) return SSD_ERR_UNSUPPORTED;
+    if (dstate % 16 != 0 || dstate > ssd::kMaxDstate) return SSD_ERR_UNSUPPORTED;
+    // Every element index must fit the 32-bit block/grid arithmetic used for
+    // per-(b,h) bases and the 64-bit offsets used for whole tensors.
+    const double elems = (double)batch * seqlen * nheads * headdim;
+    const double states = (double)batch * ((seqlen + chunk_len - 1) / chunk_len + 1) *
+                          nheads * headdim * dstate;
+    if (elems > 9.0e15 || states > 9.0e15 || (double)batch * nheads > 2.0e9)
+        return SSD_ERR_UNSUPPORTED;
+    // Launch grids put the batch, and (chunks x groups) / (heads x tile
+    // groups), on the y and z grid dimensions, which are limited to 65535.
+    const long nc = (seqlen + chunk_len - 1) / chunk_len;
+    if (batch > 65535 || nc * ngroups > 65535 || (long)nheads * 4 > 65535)
+        return SSD_ERR_UNSUPPORTED;
+    return SSD_OK;
+}
+
+struct Layout {
+    size_t acum, dtT, cb, S, total;
+};
+
+Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
+                      int ngroups, int chunk_len) {
+    const size_t nc = (size_t)(seqlen + chunk_len - 1) / chunk_len;
+    const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups,
+                 Q = chunk_len;
+    Layout l;
+    l.acum = 0;
+    l.dtT = l.acum + round_up(b * H * nc * Q * sizeof(float));
+    l.cb = l.dtT + round_up(b * H * nc * Q * sizeof(float));
+    l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
+    l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
+    return l;
+}
+
+}  // namespace
+
+extern "C" {
+
+int ssd_abi_version(void) { return SSD_ABI_VERSION; }
+
+const char *ssd_status_string(ssd_status status) {
+    switch (status) {
+    case SSD_OK: return "success";
+    case SSD_ERR_INVALID_ARGUMENT: return "invalid argument";
+    case SSD_ERR_UNSUPPORTED: return "unsupported shape";
+    case SSD_ERR_WORKSPACE: return "workspace missing or too small";
+    case SSD_ERR_HIP: return "HIP kernel launch failed";
+    }
+    return "unknown status";
+}
+
+ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
+                                             int headdim, int dstate, int ngroups,
+                                             int chunk_len, ssd_dtype io_dtype,
+                                             size_t *bytes) {
+    if (!bytes) return SSD_ERR_INVALID_ARGUMENT;
+    ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                        chunk_len, io_dtype);
+    if (st != SSD_OK) return st;
+    *bytes = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len).total;
+    return SSD_OK;
+}
+
+}  // extern "C"
+
+namespace {
+
+ssd_status forward_impl(const void *x, const float *dt, const float *A, const void *B,
+                        const void *C, const float *D, const float *initial_state,
+                        int chunk_len, int ngroups, int batch, int seqlen, int nheads,
+                        int headdim, int dstate, ssd_dtype io_dtype, void *y,
+                        float *final_state, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t *events) {
+    ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                        chunk_len, io_dtype);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+    // 16-byte vector accesses on x, B, C, y and the states.
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (initial_state && !aligned(initial_state, 16)) ||
+        (final_state && !aligned(final_state, 16)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                      chunk_len);
+    if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
+        return SSD_ERR_WORKSPACE;
+
+    ssd::SplitArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.init = initial_state;
+    a.y = y;
+    a.final_state = final_state;
+    a.batch = batch;
+    a.L = seqlen;
+    a.H = nheads;
+    a.G = ngroups;
+    a.P = headdim;
+    a.N = dstate;
+    a.Q = chunk_len;
+    a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
+    char *ws = static_cast<char *>(workspace);
+    a.acum = reinterpret_cast<float *>(ws + lay.acum);
+    a.dtT = reinterpret_cast<float *>(ws + lay.dtT);
+    a.cb = reinterpret_cast<float *>(ws + lay.cb);
+    a.S = reinterpret_cast<float *>(ws + lay.S);
+
+    hipError_t err = io_dtype == SSD_BF16
+                         ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
+                         : ssd::launch_split_forward<float>(a, stream, events);
+    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              const float *initial_state, int chunk_len, int ngroups,
+                              int batch, int seqlen, int nheads, int headdim,
+                              int dstate, ssd_dtype io_dtype, void *y,
+                              float *final_state, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream) {
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
+                        seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
+                        workspace, workspace_bytes, stream, nullptr);
+}
+
+int ssd_chunk_scan_fwd_kernel_count(void) { return ssd::kForwardKernels; }
+
+const char *ssd_chunk_scan_fwd_kernel_name(int i) {
+    return (i >= 0 && i < ssd::kForwardKernels) ? ssd::kForwardKernelNames[i] : nullptr;
+}
+
+ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const float *initial_state, int chunk_len,
+                                    int ngroups, int batch, int seqlen, int nheads,
+                                    int headdim, int dstate, ssd_dtype io_dtype, void *y,
+                                    float *final_state, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t *events, int nevents) {
+    if (!events || nevents < ssd::kForwardKernels + 1) return SSD_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i <= ssd::kForwardKernels; ++i)
+        if (!events[i]) return SSD_ERR_INVALID_ARGUMENT;
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
+                        seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
+                        workspace, workspace_bytes, stream, events);
+}
+
+ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,
+                            const void *B, const void *C, const float *D, int ngroups,
+                            int batch, int nheads, int headdim, int dstate,
+                            ssd_dtype io_dtype, void *y, hipStream_t stream) {
+    if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
+        return SSD_ERR_INVALID_ARGUMENT;
+    if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (!state || !x || !dt || !A || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+    if (headdim % 16 != 0 || headdim > ssd::kMaxHeaddim) return SSD_ERR_UNSUPPORTED;
+    if (dstate % 16 != 0 || dstate > ssd::kMaxDstate) return SSD_ERR_UNSUPPORTED;
+    if (batch > 65535 || (double)batch * nheads > 2.0e9) return SSD_ERR_UNSUPPORTED;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(state, 16) || !aligned(x, es) || !aligned(B, es) || !aligned(C, es) ||
+        !aligned(y, es) || !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    ssd::DecodeArgs a;
+    a.state = state;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.y = y;
+    a.batch = batch;
+    a.H = nheads;
+    a.G = ngroups;
+    a.P = headdim;
+    a.N = dstate;
+    hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_state_update<ssd::bf16>(a, stream)
+                                          : ssd::launch_state_update<float>(a, stream);
+    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+}  // extern "C"

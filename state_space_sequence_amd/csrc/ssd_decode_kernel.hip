@@ -1,0 +1,77 @@
+// ssd_decode_kernel.hip -- single-token SSM state update, in place.
+//
+// One token of the recurrence (fla `layers/mamba2.py`, decode branch of
+// `Mamba2.torch_forward`): decay the cached state by exp(dt*A), add
+// dt * x (outer) B, then read y = state . C + D x from the UPDATED state.
+//
+// The step moves 2 * P * N * 4 bytes of fp32 state per (batch, head) and does
+// ~5 flops per state element, so it is bound by HBM bandwidth.  A block owns
+// one (batch, head); each row p of the state is read and written as float4
+// vectors by a group of R lanes (R = the power of two >= N/4), so a wave
+// streams 64 / R whole rows per access with fully coalesced 16-byte lanes.
+// The row's dot product with C is reduced with xor shuffles inside the group.
+#include "ssd_device.hpp"
+#include "ssd_kernels.hpp"
+
+namespace ssd {
+
+template <typename T>
+__global__ void __launch_bounds__(256)
+k_state_update(float *__restrict__ state, const T *__restrict__ x,
+               const float *__restrict__ dt, const float *__restrict__ A,
+               const T *__restrict__ Bm, const T *__restrict__ Cm,
+               const float *__restrict__ D, T *__restrict__ y, int H, int G, int P,
+               int N, int R) {
+    const int h = blockIdx.x, b = blockIdx.y, g = h / (H / G);
+    const int tid = threadIdx.x;
+    const int rows_per_pass = 256 / R;
+    const int lr = tid & (R - 1);
+    const int n0 = lr * 4;
+    const bool nact = n0 < N;
+    const float dth = dt[(size_t)b * H + h];
+    const float alpha = fast_exp(dth * A[h]);
+    const float Dh = D ? D[h] : 0.f;
+    float Bv[4] = {0.f, 0.f, 0.f, 0.f}, Cv[4] = {0.f, 0.f, 0.f, 0.f};
+    if (nact) {
+        const T *bp = Bm + ((size_t)b * G + g) * N + n0;
+        const T *cp = Cm + ((size_t)b * G + g) * N + n0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            Bv[j] = to_f32(bp[j]);
+            Cv[j] = to_f32(cp[j]);
+        }
+    }
+    const size_t base = (size_t)(b * H + h) * P;
+    for (int p = tid / R; p < P; p += rows_per_pass) {
+        const float xv = to_f32(x[base + p]);
+        const float u = dth * xv;
+        float part = 0.f;
+        if (nact) {
+            float4 *sp = reinterpret_cast<float4 *>(state + (base + p) * N + n0);
+            float4 s = *sp;
+            s.x = alpha * s.x + u * Bv[0];
+            s.y = alpha * s.y + u * Bv[1];
+            s.z = alpha * s.z + u * Bv[2];
+            s.w = alpha * s.w + u * Bv[3];
+            *sp = s;
+            part = s.x * Cv[0] + s.y * Cv[1] + s.z * Cv[2] + s.w * Cv[3];
+        }
+        for (int off = R / 2; off > 0; off >>= 1) part += __shfl_xor(part, off, kWave);
+        if (lr == 0) y[base + p] = from_f32<T>(part + Dh * xv);
+    }
+}
+
+template <typename T>
+hipError_t launch_state_update(const DecodeArgs &a, hipStream_t stream) {
+    int R = 1;
+    while (R * 4 < a.N) R <<= 1;
+    hipLaunchKernelGGL(k_state_update<T>, dim3(a.H, a.batch), dim3(256), 0, stream, a.state,
+                       (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D,
+                       (T *)a.y, a.H, a.G, a.P, a.N, R);
+    return hipGetLastError();
+}
+
+template hipError_t launch_state_update<float>(const DecodeArgs &, hipStream_t);
+template hipError_t launch_state_update<bf16>(const DecodeArgs &, hipStream_t);
+
+}  // namespace ssd

@@ -1,0 +1,97 @@
+// ssd_device.hpp -- device-side building blocks shared by the libssd kernels
+// (gfx950 / CDNA4, wave64).
+//
+// MFMA fragment convention used everywhere in this library.  A "K-step" of a
+// 16x16 output tile contracts KS values of k.  For both operands, lane l of
+// the wave holds VEC consecutive k values of one row (A) or one column (B):
+//
+//      row/col = l % 16,     k = k0 + VEC * (l / 16) + j,   j = 0 .. VEC-1
+//
+//   bf16: VEC = 8, KS = 32, one v_mfma_f32_16x16x32_bf16 per K-step.
+//   fp32: VEC = 4, KS = 16, four v_mfma_f32_16x16x4_f32; instruction j takes
+//         element j of every lane, so lane group q supplies k = 4q + j.  The
+//         contraction covers all 16 k exactly once, and A and B agree on which
+//         k each (lane, element) slot carries, which is all a sum over k needs.
+//
+// The 16x16 fp32 result tile D is spread as: lane l holds
+//      D[4 * (l / 16) + i][l % 16],   i = 0 .. 3        (f32x4 element i).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ssd {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+// ----------------------------------------------------------------- conversions
+
+__device__ __forceinline__ float to_f32(float v) { return v; }
+__device__ __forceinline__ float to_f32(bf16 v) { return (float)v; }
+
+template <typename T> __device__ __forceinline__ T from_f32(float v);
+template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
+// fptrunc float -> bf16 rounds to nearest even.
+template <> __device__ __forceinline__ bf16 from_f32<bf16>(float v) { return (bf16)v; }
+
+// ----------------------------------------------------------------- MFMA traits
+
+template <typename T> struct Mma;
+
+template <> struct Mma<bf16> {
+    static constexpr int VEC = 8;
+    static constexpr int KS = 32;
+    typedef bf16x8 frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    }
+};
+
+template <> struct Mma<float> {
+    static constexpr int VEC = 4;
+    static constexpr int KS = 16;
+    typedef f32x4 frag;
+    static __device__ __forceinline__ f32x4 mma(frag a, frag b, f32x4 c) {
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[0], b[0], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[1], b[1], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[2], b[2], c, 0, 0, 0);
+        c = __builtin_amdgcn_mfma_f32_16x16x4f32(a[3], b[3], c, 0, 0, 0);
+        return c;
+    }
+};
+
+// Load VEC consecutive elements (one 16-byte vector) as a fragment.
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag load_frag(const T *p) {
+    return *reinterpret_cast<const typename Mma<T>::frag *>(p);
+}
+
+template <typename T>
+__device__ __forceinline__ typename Mma<T>::frag zero_frag() {
+    typename Mma<T>::frag f;
+#pragma unroll
+    for (int j = 0; j < Mma<T>::VEC; ++j) f[j] = from_f32<T>(0.f);
+    return f;
+}
+
+__device__ __forceinline__ f32x4 zero4() { return f32x4{0.f, 0.f, 0.f, 0.f}; }
+
+// ----------------------------------------------------------------- wave scan
+
+// Inclusive prefix sum of `v` over the 64 lanes of the wave.
+__device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        float o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
+__device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
+
+}  // namespace ssd

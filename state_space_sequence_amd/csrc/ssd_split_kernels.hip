@@ -1,0 +1,425 @@
+// ssd_split_kernels.hip -- the chunked SSD forward as five kernels, one per
+// step of the chunked algorithm (burn-mamba `mamba2/ssd/serial.rs`, kernels
+// 1-5; burn-mamba `Mamba2SsdInput` rustdoc, `ssd_minimal` Steps 1-4):
+//
+//   k1_dA_cumsum      per-chunk inclusive prefix sum of dt*A  (`k1_ssd_chunk_cumsum`)
+//   k2_chunk_cb       C B^T per chunk and group, causal blocks (`k2_ssd_bmm`)
+//   k3_chunk_state    zero-initial state of every chunk, Eq. 20 (`k3_ssd_chunk_state`)
+//   k4_state_passing  inter-chunk recurrence, Eq. 22            (`k4_ssd_state_passing`)
+//   k5_chunk_scan     y = state-to-output (Eq. 23) + masked intra-chunk
+//                     product + D skip                           (`k5_ssd_chunk_scan`)
+//
+// These kernels accept every supported shape.  Layouts of the workspace
+// intermediates (all fp32):
+//   acum [b][H][nc][Q]   prefix sums of dt*A inside each chunk (0 past seqlen)
+//   dtT  [b][H][nc][Q]   dt re-laid out per chunk (0 past seqlen)
+//   cb   [b][nc][G][Q][Q] C B^T of the chunk (only s-tiles <= l-tile written)
+//   S    [b][nc][H][P][N] chunk states, overwritten by k4 with the state
+//                         entering each chunk
+#include "ssd_device.hpp"
+#include "ssd_kernels.hpp"
+
+namespace ssd {
+
+// --------------------------------------------------------------------- k1
+// grid (nc, ceil(H/16), b), 256 threads.  A block stages dt for 16 heads of
+// one chunk through LDS (coalesced over heads), then every wave scans 4 heads:
+// each lane sums up to 4 consecutive tokens, the wave scans the lane totals.
+__global__ void __launch_bounds__(256)
+k1_dA_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
+             float *__restrict__ acum, float *__restrict__ dtT, int L, int H,
+             int nc, int Q) {
+    __shared__ float s_dt[16][257];
+    const int c = blockIdx.x, h0 = blockIdx.y * 16, b = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int j = tid & 15;
+    for (int r = tid >> 4; r < Q; r += 16) {
+        const int h = h0 + j, t = c * Q + r;
+        float v = 0.f;
+        if (h < H && t < L) v = dt[((size_t)b * L + t) * H + h];
+        s_dt[j][r] = v;
+    }
+    __syncthreads();
+    const int wave = tid >> 6, lane = tid & 63;
+    const int E = Q > 64 ? Q / 64 : 1;
+    for (int jj = 0; jj < 4; ++jj) {
+        const int hl = wave * 4 + jj, h = h0 + hl;
+        if (h >= H) break;
+        const float Ah = A[h];
+        float a[4], d[4];
+        float run = 0.f;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            a[e] = 0.f;
+            d[e] = 0.f;
+            const int idx = lane * E + e;
+            if (e < E && idx < Q) {
+                d[e] = s_dt[hl][idx];
+                run += d[e] * Ah;
+                a[e] = run;
+            }
+        }
+        const float incl = wave_inclusive_scan(run, lane);
+        float excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 0.f;
+        const size_t base = ((size_t)(b * H + h) * nc + c) * Q;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int idx = lane * E + e;
+            if (e < E && idx < Q) {
+                acum[base + idx] = excl + a[e];
+                dtT[base + idx] = d[e];
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------- k2
+// grid (npairs, nc*G, b), 256 threads.  Block `pair` covers an (l-block of 64,
+// s-block of 64) pair with s-block <= l-block; wave w takes the 16 rows
+// l0 = 64*lb + 16*w against four 16-column s-tiles.  Operands are read
+// straight from global memory: rows of C and B are contiguous in n, which is
+// the MFMA k dimension here.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k2_chunk_cb(const T *__restrict__ Bm, const T *__restrict__ Cm,
+            float *__restrict__ cb, int L, int G, int N, int nc, int Q) {
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    int pair = blockIdx.x, lb = 0;
+    while ((lb + 1) * (lb + 2) / 2 <= pair) ++lb;
+    const int sb = pair - lb * (lb + 1) / 2;
+    const int c = blockIdx.y / G, g = blockIdx.y % G, b = blockIdx.z;
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int l0 = lb * 64 + wave * 16;
+    if (l0 >= Q) return;
+    const int tl = c * Q + l0 + r;
+    const T *crow = Cm + (((size_t)b * L + tl) * G + g) * N;
+    int s0[4];
+    bool act[4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        s0[st] = sb * 64 + st * 16;
+        act[st] = s0[st] < Q && s0[st] <= l0 + 15;
+    }
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int k0 = 0; k0 < N; k0 += KS) {
+        const int k = k0 + VEC * q;
+        const bool kin = k < N;
+        typename Mma<T>::frag a = (tl < L && kin) ? load_frag(crow + k) : zero_frag<T>();
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            if (!act[st]) continue;
+            const int ts = c * Q + s0[st] + r;
+            typename Mma<T>::frag bb =
+                (ts < L && kin) ? load_frag(Bm + (((size_t)b * L + ts) * G + g) * N + k)
+                                : zero_frag<T>();
+            acc[st] = Mma<T>::mma(a, bb, acc[st]);
+        }
+    }
+    const size_t base = ((size_t)(b * nc + c) * G + g) * Q;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) {
+        if (!act[st]) continue;
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            cb[(base + l0 + 4 * q + i) * Q + s0[st] + r] = acc[st][i];
+    }
+}
+
+// --------------------------------------------------------------------- k3
+// grid (nc, H * ntile_groups, b), 256 threads, dynamic LDS.
+// S[p][n] = sum_s x[s][p] * w_s * B[s][n],  w_s = exp(acum_end - acum_s) dt_s.
+// The contraction runs over tokens s, which is the slow index of both x and
+// B in memory, so 32-token slabs of both are staged transposed in LDS
+// (XT[p][s], BT[n][s]) with w_s folded into x on the way in; fragments are
+// then 16-byte LDS reads.  Each wave owns up to kK3TilesPerWave 16x16 tiles.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
+               const float *__restrict__ acum, const float *__restrict__ dtT,
+               float *__restrict__ S, int L, int H, int G, int P, int N, int nc,
+               int Q) {
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    constexpr int KB = 32;
+    constexpr int PITCH = KB + 16 / (int)sizeof(T);
+    constexpr int TPW = kK3TilesPerWave;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *XT = reinterpret_cast<T *>(smem_raw);
+    T *BT = XT + (size_t)P * PITCH;
+
+    const int c = blockIdx.x, h = blockIdx.y % H, tg = blockIdx.y / H, b = blockIdx.z;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int ntn = N / 16, ntiles = (P / 16) * ntn;
+    const float *ac = acum + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
+    const float aend = ac[Q - 1];
+
+    f32x4 acc[TPW];
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) acc[i] = zero4();
+
+    for (int s0 = 0; s0 < Q; s0 += KB) {
+        __syncthreads();
+        const int pv = P / VEC;
+        for (int v = tid; v < KB * pv; v += 256) {
+            const int sl = v / pv, p0 = (v % pv) * VEC;
+            const int s = s0 + sl, t = c * Q + s;
+            const bool in = s < Q && t < L;
+            float w = 0.f;
+            typename Mma<T>::frag f = zero_frag<T>();
+            if (in) {
+                w = fast_exp(aend - ac[s]) * dc[s];
+                f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
+            }
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj)
+                XT[(p0 + jj) * PITCH + sl] = from_f32<T>(to_f32(f[jj]) * w);
+        }
+        const int nv = N / VEC;
+        for (int v = tid; v < KB * nv; v += 256) {
+            const int sl = v / nv, n0 = (v % nv) * VEC;
+            const int s = s0 + sl, t = c * Q + s;
+            typename Mma<T>::frag f = zero_frag<T>();
+            if (s < Q && t < L) f = load_frag(Bm + (((size_t)b * L + t) * G + g) * N + n0);
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj) BT[(n0 + jj) * PITCH + sl] = f[jj];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int kk = 0; kk < KB; kk += KS) {
+#pragma unroll
+            for (int i = 0; i < TPW; ++i) {
+                const int t = tg * 4 * TPW + wave + 4 * i;
+                if (t >= ntiles) continue;
+                const int pt = t / ntn, nt = t % ntn;
+                typename Mma<T>::frag a = load_frag(XT + (pt * 16 + r) * PITCH + kk + VEC * q);
+                typename Mma<T>::frag bb = load_frag(BT + (nt * 16 + r) * PITCH + kk + VEC * q);
+                acc[i] = Mma<T>::mma(a, bb, acc[i]);
+            }
+        }
+    }
+    float *Sc = S + ((size_t)(b * nc + c) * H + h) * P * N;
+#pragma unroll
+    for (int i = 0; i < TPW; ++i) {
+        const int t = tg * 4 * TPW + wave + 4 * i;
+        if (t >= ntiles) continue;
+        const int pt = t / ntn, nt = t % ntn;
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            Sc[(size_t)(pt * 16 + 4 * q + e) * N + nt * 16 + r] = acc[i][e];
+    }
+}
+
+// --------------------------------------------------------------------- k4
+// grid (ceil(P*N/1024), H, b), 256 threads, 4 consecutive state elements per
+// thread.  Serial over chunks; S[c] is replaced by the state entering chunk c
+// and the state after the last chunk is the final state.  Chunk states are
+// read kK4Prefetch chunks ahead so several loads are in flight per thread.
+__global__ void __launch_bounds__(256)
+k4_state_passing(float *__restrict__ S, const float *__restrict__ acum,
+                 const float *init, float *final_state, int H, int PN, int nc,
+                 int Q) {
+    const int h = blockIdx.y, b = blockIdx.z;
+    const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e0 >= PN) return;
+    const size_t soff = (size_t)(b * H + h) * PN + e0;
+    float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (init) run = *reinterpret_cast<const float4 *>(init + soff);
+    const float *ac = acum + (size_t)(b * H + h) * nc * Q;
+    constexpr int PF = kK4Prefetch;
+    for (int c0 = 0; c0 < nc; c0 += PF) {
+        float4 sv[PF];
+        float dec[PF];
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int c = c0 + k;
+            if (c < nc) {
+                sv[k] = *reinterpret_cast<const float4 *>(S + ((size_t)(b * nc + c) * H + h) * PN + e0);
+                dec[k] = fast_exp(ac[(size_t)c * Q + Q - 1]);
+            }
+        }
+#pragma unroll
+        for (int k = 0; k < PF; ++k) {
+            const int c = c0 + k;
+            if (c < nc) {
+                *reinterpret_cast<float4 *>(S + ((size_t)(b * nc + c) * H + h) * PN + e0) = run;
+                run.x = dec[k] * run.x + sv[k].x;
+                run.y = dec[k] * run.y + sv[k].y;
+                run.z = dec[k] * run.z + sv[k].z;
+                run.w = dec[k] * run.w + sv[k].w;
+            }
+        }
+    }
+    if (final_state) *reinterpret_cast<float4 *>(final_state + soff) = run;
+}
+
+// --------------------------------------------------------------------- k5
+// grid (nc * nlb, H, b), 256 threads, dynamic LDS; nlb = ceil(Q/64).
+// Block (c, lb) produces rows l in [64 lb, 64 lb + 64) of chunk c; wave w
+// owns the 16 rows l0 = 64 lb + 16 w and every 16-column p-tile.
+//   acc  = C[l] . h_in^T                 (state-to-output, Eq. 23)
+//   acc *= exp(acum_l)
+//   acc += sum_{s<=l} CB[l,s] exp(acum_l - acum_s) dt_s x[s]   (Step 1)
+//   y    = acc + D x[l]
+// The decay mask is applied with a select, so entries above the diagonal are
+// exactly 0 (the upper-triangle protection of the Kernel 5 page: the
+// exponent is never evaluated for s > l).  x is staged transposed in LDS,
+// 64 tokens at a time, as the B operand of the intra-chunk product.
+template <typename T>
+__global__ void __launch_bounds__(256)
+k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
+              const float *__restrict__ cb, const float *__restrict__ S,
+              const float *__restrict__ acum, const float *__restrict__ dtT,
+              const float *__restrict__ D, T *__restrict__ y, int L, int H, int G,
+              int P, int N, int nc, int Q) {
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    constexpr int SB = 64;
+    constexpr int PITCH = SB + 16 / (int)sizeof(T);
+    constexpr int MAXPT = kMaxHeaddim / 16;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *XT = reinterpret_cast<T *>(smem_raw);
+
+    const int nlb = (Q + 63) / 64;
+    const int c = blockIdx.x / nlb, lb = blockIdx.x % nlb;
+    const int h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int l0 = lb * 64 + wave * 16;
+    const bool active = l0 < Q;
+    const int row = l0 + r;
+    const int npt = P / 16;
+    const float *ac = acum + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
+
+    f32x4 acc[MAXPT];
+#pragma unroll
+    for (int i = 0; i < MAXPT; ++i) acc[i] = zero4();
+
+    if (active) {
+        const float *hin = S + ((size_t)(b * nc + c) * H + h) * P * N;
+        const int t = c * Q + row;
+        const T *crow = Cm + (((size_t)b * L + t) * G + g) * N;
+        for (int k0 = 0; k0 < N; k0 += KS) {
+            const int k = k0 + VEC * q;
+            const bool kin = k < N;
+            typename Mma<T>::frag a = (t < L && kin) ? load_frag(crow + k) : zero_frag<T>();
+#pragma unroll
+            for (int pt = 0; pt < MAXPT; ++pt) {
+                if (pt >= npt) continue;
+                typename Mma<T>::frag bb = zero_frag<T>();
+                if (kin) {
+                    const float *hp = hin + (size_t)(pt * 16 + r) * N + k;
+#pragma unroll
+                    for (int jj = 0; jj < VEC; ++jj) bb[jj] = from_f32<T>(hp[jj]);
+                }
+                acc[pt] = Mma<T>::mma(a, bb, acc[pt]);
+            }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float e = fast_exp(ac[l0 + 4 * q + i]);
+#pragma unroll
+            for (int pt = 0; pt < MAXPT; ++pt) acc[pt][i] *= e;
+        }
+    }
+
+    const float arow = active ? ac[row] : 0.f;
+    const float *cbrow = cb + (((size_t)(b * nc + c) * G + g) * Q + (active ? row : 0)) * Q;
+    const int pv = P / VEC;
+    for (int sb = 0; sb <= lb; ++sb) {
+        __syncthreads();
+        for (int v = tid; v < SB * pv; v += 256) {
+            const int sl = v / pv, p0 = (v % pv) * VEC;
+            const int s = sb * SB + sl, t = c * Q + s;
+            typename Mma<T>::frag f = zero_frag<T>();
+            if (s < Q && t < L) f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj) XT[(p0 + jj) * PITCH + sl] = f[jj];
+        }
+        __syncthreads();
+        if (!active) continue;
+        const int kend = min(min(sb * SB + SB, Q), l0 + 16);
+        for (int kk = sb * SB; kk < kend; kk += KS) {
+            const int sj0 = kk + VEC * q;
+            typename Mma<T>::frag m;
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj) {
+                const int s = sj0 + jj;
+                float v = 0.f;
+                if (s <= row && s < Q) v = cbrow[s] * fast_exp(arow - ac[s]) * dc[s];
+                m[jj] = from_f32<T>(v);
+            }
+#pragma unroll
+            for (int pt = 0; pt < MAXPT; ++pt) {
+                if (pt >= npt) continue;
+                typename Mma<T>::frag bb = load_frag(XT + (pt * 16 + r) * PITCH + (sj0 - sb * SB));
+                acc[pt] = Mma<T>::mma(m, bb, acc[pt]);
+            }
+        }
+    }
+
+    if (!active) return;
+    const float Dh = D ? D[h] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int l = l0 + 4 * q + i, t = c * Q + l;
+        if (l >= Q || t >= L) continue;
+        T *yrow = y + (((size_t)b * L + t) * H + h) * P;
+#pragma unroll
+        for (int pt = 0; pt < MAXPT; ++pt) {
+            if (pt >= npt) continue;
+            const int p = pt * 16 + r;
+            const float xv = to_f32(XT[p * PITCH + (l - lb * SB)]);
+            yrow[p] = from_f32<T>(acc[pt][i] + Dh * xv);
+        }
+    }
+}
+
+// --------------------------------------------------------------------- launch
+
+const char *const kForwardKernelNames[kForwardKernels] = {
+    "k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing", "k5_chunk_scan"};
+
+template <typename T>
+hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent_t *events) {
+    const int nc = a.nchunks, Q = a.Q;
+    int ev = 0;
+    auto mark = [&]() -> hipError_t {
+        return events ? hipEventRecord(events[ev++], stream) : hipSuccess;
+    };
+    hipError_t err;
+    if ((err = mark()) != hipSuccess) return err;
+    hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (a.H + 15) / 16, a.batch), dim3(256), 0,
+                       stream, a.dt, a.A, a.acum, a.dtT, a.L, a.H, nc, Q);
+    if ((err = mark()) != hipSuccess) return err;
+    const int nlb = (Q + 63) / 64;
+    hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
+                       dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, a.cb, a.L,
+                       a.G, a.N, nc, Q);
+    if ((err = mark()) != hipSuccess) return err;
+    const int ntiles = (a.P / 16) * (a.N / 16);
+    const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
+    const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
+    hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
+                       stream, (const T *)a.x, (const T *)a.B, a.acum, a.dtT, a.S, a.L,
+                       a.H, a.G, a.P, a.N, nc, Q);
+    if ((err = mark()) != hipSuccess) return err;
+    const int PN = a.P * a.N;
+    hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
+                       0, stream, a.S, a.acum, a.init, a.final_state, a.H, PN, nc, Q);
+    if ((err = mark()) != hipSuccess) return err;
+    const size_t k5_lds = (size_t)a.P * (64 + 16 / sizeof(T)) * sizeof(T);
+    hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
+                       stream, (const T *)a.x, (const T *)a.C, a.cb, a.S, a.acum, a.dtT,
+                       a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q);
+    if ((err = mark()) != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+template hipError_t launch_split_forward<float>(const SplitArgs &, hipStream_t, hipEvent_t *);
+template hipError_t launch_split_forward<bf16>(const SplitArgs &, hipStream_t, hipEvent_t *);
+
+}  // namespace ssd

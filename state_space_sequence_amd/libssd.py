@@ -1,0 +1,241 @@
+"""ctypes binding of libssd.so (C ABI in include/ssd.h).
+
+Argument marshalling only: every step of the SSD runs in the HIP kernels of
+libssd.so.  PyTorch supplies device memory and the current stream.  There is
+no fallback: if libssd.so is missing or cannot be loaded, every call raises.
+
+Python names mirror the C entry points:
+    ssd_chunk_scan_fwd_workspace_size(...)       -> int bytes
+    ssd_chunk_scan_fwd(x, dt, A, B, C, ...)      -> (y, final_state)
+    ssd_chunk_scan_fwd_timed(..., events)        -> (y, final_state)
+    ssd_state_update(state, x, dt, A, B, C, ...) -> y   (state updated in place)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "lib", "libssd.so")
+
+SSD_OK = 0
+SSD_ERR_INVALID_ARGUMENT = 1
+SSD_ERR_UNSUPPORTED = 2
+SSD_ERR_WORKSPACE = 3
+SSD_ERR_HIP = 4
+
+SSD_F32 = 0
+SSD_BF16 = 1
+
+_lock = threading.Lock()
+_lib = None
+
+
+class SsdError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        msg = load().ssd_status_string(status).decode()
+        super().__init__("%s failed: %s (status %d)" % (where, msg, status))
+
+
+_i = ctypes.c_int
+_p = ctypes.c_void_p
+_sz = ctypes.c_size_t
+
+_FWD_ARGS = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]
+
+
+def load():
+    """Load libssd.so (once).  Raises if it has not been built."""
+    global _lib
+    with _lock:
+        if _lib is not None:
+            return _lib
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                "libssd.so not found at %s; build it with "
+                "`python -m state_space_sequence_amd.build_lib`" % LIB_PATH)
+        lib = ctypes.CDLL(LIB_PATH)
+        lib.ssd_abi_version.restype = _i
+        lib.ssd_abi_version.argtypes = []
+        lib.ssd_status_string.restype = ctypes.c_char_p
+        lib.ssd_status_string.argtypes = [_i]
+        lib.ssd_chunk_scan_fwd_workspace_size.restype = _i
+        lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_i] * 8 + [ctypes.POINTER(_sz)]
+        lib.ssd_chunk_scan_fwd.restype = _i
+        lib.ssd_chunk_scan_fwd.argtypes = _FWD_ARGS
+        lib.ssd_chunk_scan_fwd_kernel_count.restype = _i
+        lib.ssd_chunk_scan_fwd_kernel_count.argtypes = []
+        lib.ssd_chunk_scan_fwd_kernel_name.restype = ctypes.c_char_p
+        lib.ssd_chunk_scan_fwd_kernel_name.argtypes = [_i]
+        lib.ssd_chunk_scan_fwd_timed.restype = _i
+        lib.ssd_chunk_scan_fwd_timed.argtypes = _FWD_ARGS + [ctypes.POINTER(_p), _i]
+        lib.ssd_state_update.restype = _i
+        lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
+        _lib = lib
+    return _lib
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return SSD_BF16
+    if t.dtype == torch.float32:
+        return SSD_F32
+    raise TypeError("x/B/C must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _check_dev(name, t, dtype=None, device=None):
+    import torch
+    if t is None:
+        return
+    if not isinstance(t, torch.Tensor):
+        raise TypeError("%s must be a torch.Tensor" % name)
+    if device is not None and t.device != device:
+        raise ValueError("%s is on %s, expected %s" % (name, t.device, device))
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def kernel_names():
+    lib = load()
+    return [lib.ssd_chunk_scan_fwd_kernel_name(i).decode()
+            for i in range(lib.ssd_chunk_scan_fwd_kernel_count())]
+
+
+def ssd_chunk_scan_fwd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                      chunk_len, io_dtype) -> int:
+    out = _sz(0)
+    st = load().ssd_chunk_scan_fwd_workspace_size(batch, seqlen, nheads, headdim, dstate,
+                                                  ngroups, chunk_len, io_dtype,
+                                                  ctypes.byref(out))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_chunk_scan_fwd_workspace_size")
+    return out.value
+
+
+def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
+             final_state, workspace, return_final_state, stream):
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    _check_dev("x", x, None, dev)
+    for n, t in (("B", B), ("C", C)):
+        _check_dev(n, t, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state)):
+        _check_dev(n, t, torch.float32, dev)
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b,L,H,P] and B/C [b,L,G,N]")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if ngroups is not None and ngroups != G:
+        raise ValueError("ngroups=%d but B has %d groups" % (ngroups, G))
+    if tuple(dt.shape) != (b, L, H) or tuple(A.shape) != (H,) or \
+            tuple(B.shape) != (b, L, G, N) or tuple(C.shape) != (b, L, G, N):
+        raise ValueError("inconsistent shapes x%s dt%s A%s B%s C%s" % (
+            tuple(x.shape), tuple(dt.shape), tuple(A.shape), tuple(B.shape), tuple(C.shape)))
+    if D is not None and tuple(D.shape) != (H,):
+        raise ValueError("D must be [H]")
+    if initial_state is not None and tuple(initial_state.shape) != (b, H, P, N):
+        raise ValueError("initial_state must be [b,H,P,N]")
+    if y is None:
+        y = torch.empty_like(x)
+    _check_dev("y", y, x.dtype, dev)
+    if tuple(y.shape) != tuple(x.shape):
+        raise ValueError("y must have x's shape")
+    if final_state is None and return_final_state:
+        final_state = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    _check_dev("final_state", final_state, torch.float32, dev)
+    need = ssd_chunk_scan_fwd_workspace_size(b, L, H, P, N, G, chunk_len, io)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_dev("workspace", workspace, torch.uint8, dev)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+            int(chunk_len), G, b, L, H, P, N, io, _ptr(y), _ptr(final_state),
+            _ptr(workspace), _sz(workspace.numel()), _stream_handle(stream))
+    if timed_events is None:
+        st = lib.ssd_chunk_scan_fwd(*args)
+        where = "ssd_chunk_scan_fwd"
+    else:
+        arr = (ctypes.c_void_p * len(timed_events))(*[ctypes.c_void_p(e) for e in timed_events])
+        st = lib.ssd_chunk_scan_fwd_timed(*args, arr, len(timed_events))
+        where = "ssd_chunk_scan_fwd_timed"
+    if st != SSD_OK:
+        raise SsdError(st, where)
+    return y, final_state
+
+
+def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256,
+                       ngroups=None, y=None, final_state=None, workspace=None,
+                       return_final_state=True, stream=None):
+    """Chunked SSD forward on the current (or given) torch stream.
+
+    x [b,L,H,P] (fp32|bf16), dt [b,L,H] fp32, A [H] fp32, B/C [b,L,G,N] (x's
+    dtype), D [H] fp32 or None, initial_state [b,H,P,N] fp32 or None.
+    Returns (y [b,L,H,P] in x's dtype, final_state [b,H,P,N] fp32 or None).
+    Outputs and workspace are allocated with torch when not supplied;
+    final_state may be the initial_state tensor itself."""
+    return _forward(None, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
+                    final_state, workspace, return_final_state, stream)
+
+
+def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
+                             chunk_len=256, ngroups=None, y=None, final_state=None,
+                             workspace=None, return_final_state=True, stream=None):
+    """``ssd_chunk_scan_fwd`` that also records the given hipEvent_t handles
+    (ints) around each kernel: events[i] before kernel i, events[-1] after."""
+    return _forward(list(events), x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
+                    y, final_state, workspace, return_final_state, stream)
+
+
+def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream=None):
+    """One decode token, in place on ``state``.
+
+    state [b,H,P,N] fp32, x [b,H,P] (fp32|bf16), dt [b,H] fp32, A [H],
+    B/C [b,G,N] (x's dtype), D [H] or None.  Returns y [b,H,P] in x's dtype."""
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    _check_dev("state", state, torch.float32, dev)
+    _check_dev("x", x, None, dev)
+    for n, t in (("B", B), ("C", C)):
+        _check_dev(n, t, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D)):
+        _check_dev(n, t, torch.float32, dev)
+    b, H, P, N = state.shape
+    G = B.shape[1]
+    if ngroups is not None and ngroups != G:
+        raise ValueError("ngroups=%d but B has %d groups" % (ngroups, G))
+    if tuple(x.shape) != (b, H, P) or tuple(dt.shape) != (b, H) or tuple(A.shape) != (H,) \
+            or tuple(B.shape) != (b, G, N) or tuple(C.shape) != (b, G, N):
+        raise ValueError("inconsistent decode shapes")
+    if D is not None and tuple(D.shape) != (H,):
+        raise ValueError("D must be [H]")
+    if y is None:
+        y = torch.empty_like(x)
+    _check_dev("y", y, x.dtype, dev)
+    st = lib.ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
+                              _ptr(D), G, b, H, P, N, io, _ptr(y), _stream_handle(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_state_update")
+    return y

@@ -1,0 +1,145 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header
+declares, and rejects bad arguments with the documented status codes before
+touching the GPU (every call below returns from host-side validation; no
+kernel is launched)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssd.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    from state_space_sequence_amd import libssd
+    if not os.path.exists(libssd.LIB_PATH):
+        from state_space_sequence_amd import build_lib
+        build_lib.build()
+    return libssd.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssd_[a-z0-9_]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for must in ("ssd_chunk_scan_fwd", "ssd_state_update",
+                 "ssd_chunk_scan_fwd_workspace_size", "ssd_status_string"):
+        assert must in names
+
+
+def test_every_declared_symbol_is_exported(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+
+
+def test_version_and_strings(lib):
+    assert lib.ssd_abi_version() == 1
+    for code in range(5):
+        assert lib.ssd_status_string(code)
+    assert lib.ssd_status_string(99) == b"unknown status"
+    assert lib.ssd_chunk_scan_fwd_kernel_count() >= 1
+    assert lib.ssd_chunk_scan_fwd_kernel_name(-1) is None
+
+
+FAKE = 0x10000  # 256-byte aligned, never dereferenced: validation fails first
+
+
+def ws_size(lib, *args):
+    out = ctypes.c_size_t(0)
+    st = lib.ssd_chunk_scan_fwd_workspace_size(*args, ctypes.byref(out))
+    return st, out.value
+
+
+def test_workspace_size(lib):
+    st, n = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
+    assert st == 0
+    nc = 32
+    expect = 2 * 4 * 80 * nc * 256 * 4 + 4 * nc * 1 * 256 * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4
+    assert n >= expect and n - expect < 4 * 256
+    st, _ = ws_size(lib, 4, 8192, 80, 64, 128, 3, 256, 1)
+    assert st == 1  # nheads % ngroups
+    st, _ = ws_size(lib, 4, 8192, 80, 64, 128, 1, 100, 1)
+    assert st == 2
+    assert lib.ssd_chunk_scan_fwd_workspace_size(1, 1, 1, 16, 16, 1, 16, 0, None) == 1
+
+
+def fwd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, init=None, Q=64, G=1,
+             b=1, L=100, H=2, P=16, N=16, io=0, y=FAKE, fin=None, ws=FAKE,
+             wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ssd_chunk_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"],
+                                  a["Q"], a["G"], a["b"], a["L"], a["H"], a["P"], a["N"],
+                                  a["io"], a["y"], a["fin"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=3, H=4), 1),
+    (dict(L=0), 1),
+    (dict(b=-1), 1),
+    (dict(io=7), 1),
+    (dict(x=None), 1),
+    (dict(C=None), 1),
+    (dict(y=None), 1),
+    (dict(x=FAKE + 2), 1),
+    (dict(init=FAKE + 4), 1),
+    (dict(Q=48), 2),
+    (dict(Q=512), 2),
+    (dict(P=24), 2),
+    (dict(P=256), 2),
+    (dict(N=8), 2),
+    (dict(N=512), 2),
+    (dict(wsb=16), 3),
+    (dict(ws=None), 3),
+    (dict(ws=FAKE + 16), 3),
+])
+def test_forward_validation(lib, kw, code):
+    assert fwd(lib, **kw) == code
+
+
+def test_timed_needs_enough_events(lib):
+    n = lib.ssd_chunk_scan_fwd_kernel_count()
+    arr = (ctypes.c_void_p * n)(*([FAKE] * n))
+    st = lib.ssd_chunk_scan_fwd_timed(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 64, 1, 1,
+                                      100, 2, 16, 16, 0, FAKE, None, FAKE, 1 << 40, None,
+                                      arr, n)
+    assert st == 1
+
+
+def upd(lib, **kw):
+    a = dict(state=FAKE, x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, G=1, b=2, H=4,
+             P=16, N=16, io=1, y=FAKE, stream=None)
+    a.update(kw)
+    return lib.ssd_state_update(a["state"], a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                a["G"], a["b"], a["H"], a["P"], a["N"], a["io"], a["y"],
+                                a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=3), 1),
+    (dict(b=0), 1),
+    (dict(state=None), 1),
+    (dict(y=None), 1),
+    (dict(io=5), 1),
+    (dict(state=FAKE + 8), 1),
+    (dict(P=20), 2),
+    (dict(N=300), 2),
+])
+def test_state_update_validation(lib, kw, code):
+    assert upd(lib, **kw) == code
+
+
+def test_binding_refuses_cpu_tensors():
+    import torch
+    from state_space_sequence_amd import libssd
+    x = torch.zeros(1, 4, 2, 16)
+    with pytest.raises(ValueError):
+        libssd.ssd_chunk_scan_fwd(x, torch.zeros(1, 4, 2), torch.zeros(2),
+                                  torch.zeros(1, 4, 1, 16), torch.zeros(1, 4, 1, 16))

@@ -1,0 +1,213 @@
+"""Parity of the HIP path (through the C ABI) with the fp64 oracle.
+
+Bar: fp32 inputs -> floored max relative error <= 1e-4; bf16 inputs ->
+normwise relative error <= 2e-2, on y and on the final state separately
+(oracle/metrics.py).  Small problems are compared element by element on
+every output; the full-size workloads on sampled (batch, head) slices, which
+the serial oracle computes exactly (slices are independent).
+"""
+import sys
+
+import numpy as np
+import pytest
+
+from oracle import metrics
+from state_space_sequence_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+
+pytestmark = pytest.mark.gpu
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+@pytest.fixture(scope="module")
+def dev():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    from state_space_sequence_amd import libssd
+    libssd.load()
+    return torch.device("cuda:0")
+
+
+def gpu_forward(inp, io, Q, dev, init=True, final=True, D=True):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    t = to_torch(inp, io, dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(
+        t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"] if D else None,
+        t["initial_state"] if init else None, chunk_len=Q, ngroups=t["B"].shape[2],
+        return_final_state=final)
+    torch.cuda.synchronize()
+    return y.float().cpu().numpy(), (None if fin is None else fin.cpu().numpy())
+
+
+def check(got, ref, io, what):
+    err = metrics.parity_error(got, ref, io)
+    tol = metrics.tolerance(io)
+    _say("  %-28s err=%.3e tol=%.0e" % (what, err, tol))
+    assert np.all(np.isfinite(got)), what + " has non-finite values"
+    assert err <= tol, "%s: error %.3e > %.0e" % (what, err, tol)
+
+
+SMALL = [
+    # b, L, H, P, N, G, Q, io, init
+    (1, 1, 2, 16, 16, 1, 16, "f32", False),
+    (2, 17, 4, 16, 32, 2, 16, "f32", True),
+    (1, 300, 4, 32, 64, 2, 64, "bf16", True),
+    (2, 513, 3, 48, 48, 3, 128, "f32", True),
+    (1, 256, 2, 128, 256, 1, 256, "bf16", False),
+    (1, 256, 2, 128, 256, 1, 256, "f32", True),
+    (2, 1000, 8, 64, 128, 8, 256, "bf16", True),
+    (1, 100, 2, 64, 128, 1, 32, "bf16", True),
+    (1, 64, 2, 16, 16, 2, 64, "f32", True),
+    (3, 700, 4, 64, 128, 1, 256, "f32", True),
+]
+
+
+@pytest.mark.parametrize("case", SMALL, ids=lambda c: "b%d_L%d_H%d_P%d_N%d_G%d_Q%d_%s%s" % (
+    c[:8] + ("_init" if c[8] else "",)))
+def test_small_problems_every_element(dev, oracle_mod, case):
+    b, L, H, P, N, G, Q, io, init = case
+    _say("case %s" % (case,))
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1 if init else 0.0,
+                      seed=100 + L)
+    y, fin = gpu_forward(inp, io, Q, dev)
+    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                  inp["D"], inp["initial_state"])
+    check(y, yr, io, "y")
+    check(fin, finr, io, "final_state")
+
+
+def test_tiny_workload(dev, oracle_mod):
+    w = WORKLOADS["tiny_f32"]
+    inp = workload_inputs(w)
+    y, fin = gpu_forward(inp, w.io_dtype, w.chunk_len, dev)
+    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                  inp["D"], inp["initial_state"])
+    check(y, yr, "f32", "tiny y")
+    check(fin, finr, "f32", "tiny final")
+
+
+def _sample_slices(b, H, n, seed):
+    rng = np.random.default_rng(seed)
+    sl = {(0, 0), (b - 1, H - 1), (0, H - 1), (b - 1, 0)}
+    while len(sl) < n:
+        sl.add((int(rng.integers(b)), int(rng.integers(H))))
+    return sorted(sl)
+
+
+@pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b", "grouped_g8"])
+def test_full_size_workloads_sampled(dev, oracle_mod, name):
+    w = WORKLOADS[name]
+    _say("workload %s" % name)
+    inp = workload_inputs(w)
+    y, fin = gpu_forward(inp, w.io_dtype, w.chunk_len, dev)
+    assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
+    slices = _sample_slices(w.batch, w.nheads, 12, seed=7)
+    ys, fs = oracle_mod.forward_slices(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                       inp["D"], inp["initial_state"], w.ngroups, slices)
+    gy = np.stack([y[b_, :, h_, :] for b_, h_ in slices])
+    gf = np.stack([fin[b_, h_] for b_, h_ in slices])
+    check(gy, ys, w.io_dtype, name + " y (sampled)")
+    check(gf, fs, w.io_dtype, name + " final (sampled)")
+    for i, (b_, h_) in enumerate(slices):
+        # every sampled slice on its own, not only their union
+        assert metrics.normwise_err(gy[i], ys[i]) <= metrics.BF16_NORMWISE, (b_, h_)
+
+
+def test_chunk_length_invariance_on_gpu(dev, oracle_mod):
+    inp = make_inputs(2, 777, 4, 64, 128, 2, io_dtype="f32", init_std=0.1, seed=5)
+    outs = {Q: gpu_forward(inp, "f32", Q, dev) for Q in (16, 64, 256)}
+    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                  inp["D"], inp["initial_state"])
+    for Q, (y, fin) in outs.items():
+        check(y, yr, "f32", "Q=%d y" % Q)
+        check(fin, finr, "f32", "Q=%d final" % Q)
+
+
+def test_optional_arguments(dev, oracle_mod):
+    inp = make_inputs(1, 200, 2, 32, 32, 1, io_dtype="f32", init_std=0.1, seed=6)
+    y, fin = gpu_forward(inp, "f32", 64, dev, init=False, final=False, D=False)
+    assert fin is None
+    yr, _ = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None)
+    check(y, yr, "f32", "no D / no init / no final")
+
+
+def test_final_state_may_alias_initial_state(dev, oracle_mod):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    inp = make_inputs(2, 300, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=8)
+    t = to_torch(inp, "bf16", dev)
+    cache = t["initial_state"].clone()
+    libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], cache,
+                              chunk_len=128, final_state=cache)
+    torch.cuda.synchronize()
+    _, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                 inp["D"], inp["initial_state"])
+    check(cache.cpu().numpy(), finr, "bf16", "aliased final")
+
+
+def test_deterministic(dev):
+    inp = make_inputs(2, 600, 8, 64, 128, 2, io_dtype="bf16", init_std=0.1, seed=9)
+    y1, f1 = gpu_forward(inp, "bf16", 256, dev)
+    y2, f2 = gpu_forward(inp, "bf16", 256, dev)
+    np.testing.assert_array_equal(y1, y2)
+    np.testing.assert_array_equal(f1, f2)
+
+
+# ------------------------------------------------------------------ decode
+
+def _decode_run(inp, io, dev, steps):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    t = to_torch(inp, io, dev)
+    state = t["initial_state"].clone()
+    ys = []
+    for s in range(steps):
+        y = libssd.ssd_state_update(state, t["x"][:, s].contiguous(), t["dt"][:, s].contiguous(),
+                                    t["A"], t["B"][:, s].contiguous(), t["C"][:, s].contiguous(),
+                                    t["D"])
+        ys.append(y)
+    torch.cuda.synchronize()
+    return torch.stack(ys, 1).float().cpu().numpy(), state.cpu().numpy(), t
+
+
+@pytest.mark.parametrize("case", [(3, 5, 4, 16, 16, 2, "f32"), (2, 9, 6, 48, 80, 3, "bf16"),
+                                  (2, 4, 2, 128, 256, 1, "f32")])
+def test_decode_small_every_element(dev, oracle_mod, case):
+    b, steps, H, P, N, G, io = case
+    inp = make_inputs(b, steps, H, P, N, G, io_dtype=io, init_std=0.1, seed=20 + P)
+    y, state, _ = _decode_run(inp, io, dev, steps)
+    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                  inp["D"], inp["initial_state"])
+    check(y, yr, io, "decode y")
+    check(state, finr, io, "decode state")
+
+
+def test_decode_workload_vs_serial_and_chunked(dev, oracle_mod):
+    """64 decode steps of the b256 workload: against the serial oracle on
+    sampled slices, and against the chunked forward over the same 64 tokens
+    started from the same state (final state and every output)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    w = WORKLOADS["decode_b256"]
+    _say("decode workload")
+    inp = make_inputs(w.batch, w.decode_steps, w.nheads, w.headdim, w.dstate, w.ngroups,
+                      io_dtype=w.io_dtype, init_std=w.init_std, seed=w.seed)
+    y, state, t = _decode_run(inp, w.io_dtype, dev, w.decode_steps)
+    slices = _sample_slices(w.batch, w.nheads, 16, seed=3)
+    ys, fs = oracle_mod.forward_slices(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
+                                       inp["D"], inp["initial_state"], w.ngroups, slices)
+    check(np.stack([y[b_, :, h_] for b_, h_ in slices]), ys, "bf16", "decode y vs serial")
+    check(np.stack([state[b_, h_] for b_, h_ in slices]), fs, "bf16", "decode state vs serial")
+    yc, fc = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                       t["initial_state"], chunk_len=w.chunk_len)
+    torch.cuda.synchronize()
+    check(state, fc.cpu().numpy(), "bf16", "decode state vs chunked")
+    check(y, yc.float().cpu().numpy(), "bf16", "decode y vs chunked")
