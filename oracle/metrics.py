@@ -2,12 +2,21 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-The pages fix no tolerance; these two readings are the ones the parity bar
-is written against:
+The pages fix no tolerance.  The bars are "max relative error 1e-4" for fp32
+inputs and "2e-2 normwise" for bf16 inputs, read as follows.
 
-* fp32 inputs: floored maximum relative error
-      max_i |g_i - o_i| / max(|o_i|, 1e-3 * max_j |o_j|)  <=  1e-4
-  The floor keeps entries that cancel to almost zero from dominating.
+* fp32 inputs: componentwise relative error against the magnitude of the
+  terms that are summed into each output,
+      max_i |g_i - o_i| / a_i  <=  1e-4,
+  where a = the oracle evaluated on |x|, |B|, |C|, |D|, |initial_state| (same
+  dt and A, so every decay factor is the same positive number).  a_i is then
+  exactly the sum of the absolute values of all products that make up o_i,
+  the quantity rounding errors of any summation order scale with.  Plain
+  fp32 evaluation of the recurrence scores ~1e-7 here; rounding any operand
+  to bf16 scores ~1e-3; a dropped or misplaced term scores O(1).
+  (A relative error floored at 1e-3 * max|o| was tried first and rejected:
+  the textbook fp32 serial recurrence itself scores 1.25e-4 under it for
+  headdim 128, dstate 256, so that reading would fail correct fp32 code.)
 * bf16 inputs: normwise relative error in fp64
       ||g - o||_2 / ||o||_2  <=  2e-2
   applied to y and to the final state separately.
@@ -20,7 +29,22 @@ FP32_MAX_REL = 1e-4
 BF16_NORMWISE = 2e-2
 
 
+def componentwise_err(got, ref, ref_abs) -> float:
+    """max_i |got_i - ref_i| / ref_abs_i (entries with ref_abs_i == 0 must be
+    exact; any error there counts as infinite)."""
+    g = np.asarray(got, dtype=np.float64)
+    o = np.asarray(ref, dtype=np.float64)
+    a = np.asarray(ref_abs, dtype=np.float64)
+    if o.size == 0:
+        return 0.0
+    d = np.abs(g - o)
+    with np.errstate(divide="ignore", invalid="ignore"):
+        r = np.where(a > 0, d / np.where(a > 0, a, 1.0), np.where(d > 0, np.inf, 0.0))
+    return float(np.max(r))
+
+
 def max_rel_err(got, ref, floor: float = 1e-3) -> float:
+    """Relative error floored at ``floor`` * max|ref| (informational only)."""
     g = np.asarray(got, dtype=np.float64)
     o = np.asarray(ref, dtype=np.float64)
     if o.size == 0:
@@ -40,10 +64,24 @@ def normwise_err(got, ref) -> float:
     return float(num / den)
 
 
-def parity_error(got, ref, io_dtype: str) -> float:
-    """Error in the measure that applies to ``io_dtype`` ('f32' or 'bf16')."""
-    return max_rel_err(got, ref) if io_dtype == "f32" else normwise_err(got, ref)
+def parity_error(got, ref, io_dtype: str, ref_abs=None) -> float:
+    """Error in the measure that applies to ``io_dtype`` ('f32' or 'bf16').
+    fp32 needs ``ref_abs`` (the oracle on absolute-valued inputs)."""
+    if io_dtype == "f32":
+        if ref_abs is None:
+            raise ValueError("the fp32 measure needs the magnitude reference")
+        return componentwise_err(got, ref, ref_abs)
+    return normwise_err(got, ref)
 
 
 def tolerance(io_dtype: str) -> float:
     return FP32_MAX_REL if io_dtype == "f32" else BF16_NORMWISE
+
+
+def abs_inputs(inp: dict) -> dict:
+    """Inputs whose oracle result is the magnitude reference of ``inp``."""
+    out = dict(inp)
+    for k in ("x", "B", "C", "D", "initial_state"):
+        if out.get(k) is not None:
+            out[k] = np.abs(out[k])
+    return out

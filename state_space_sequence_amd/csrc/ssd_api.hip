@@ -48,7 +48,7 @@ ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
 }
 
 struct Layout {
-    size_t acum, dtT, cb, S, total;
+    size_t acum_hi, acum_lo, dtT, cb, S, total;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -57,8 +57,9 @@ Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate
     const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups,
                  Q = chunk_len;
     Layout l;
-    l.acum = 0;
-    l.dtT = l.acum + round_up(b * H * nc * Q * sizeof(float));
+    l.acum_hi = 0;
+    l.acum_lo = l.acum_hi + round_up(b * H * nc * Q * sizeof(float));
+    l.dtT = l.acum_lo + round_up(b * H * nc * Q * sizeof(float));
     l.cb = l.dtT + round_up(b * H * nc * Q * sizeof(float));
     l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
     l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
@@ -138,7 +139,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.Q = chunk_len;
     a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
     char *ws = static_cast<char *>(workspace);
-    a.acum = reinterpret_cast<float *>(ws + lay.acum);
+    a.acum_hi = reinterpret_cast<float *>(ws + lay.acum_hi);
+    a.acum_lo = reinterpret_cast<float *>(ws + lay.acum_lo);
     a.dtT = reinterpret_cast<float *>(ws + lay.dtT);
     a.cb = reinterpret_cast<float *>(ws + lay.cb);
     a.S = reinterpret_cast<float *>(ws + lay.S);

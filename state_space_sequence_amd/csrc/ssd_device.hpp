@@ -92,6 +92,22 @@ __device__ __forceinline__ float wave_inclusive_scan(float v, int lane) {
     return v;
 }
 
+__device__ __forceinline__ double wave_inclusive_scan_f64(double v, int lane) {
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+        double o = __shfl_up(v, d, kWave);
+        if (lane >= d) v += o;
+    }
+    return v;
+}
+
 __device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
+
+// a - b for two prefix sums held as (hi, lo) float pairs.  When a and b are
+// close, hi_a - hi_b is exact (Sterbenz), so the result keeps the accuracy
+// of the small difference instead of the ulp of the large prefixes.
+__device__ __forceinline__ float prefix_diff(float a_hi, float a_lo, float b_hi, float b_lo) {
+    return (a_hi - b_hi) + (a_lo - b_lo);
+}
 
 }  // namespace ssd

@@ -25,8 +25,9 @@ struct SplitArgs {
     float *final_state;  // may be null
     int batch, L, H, G, P, N, Q, nchunks;
     // workspace regions
-    float *acum;  // [b][H][nc][Q]
-    float *dtT;   // [b][H][nc][Q]
+    float *acum_hi;  // [b][H][nc][Q]  fp32 part of the fp64 chunk prefix sums
+    float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
+    float *dtT;      // [b][H][nc][Q]
     float *cb;    // [b][nc][G][Q][Q]
     float *S;     // [b][nc][H][P][N]
 };

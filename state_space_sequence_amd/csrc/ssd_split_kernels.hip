@@ -11,7 +11,9 @@
 //
 // These kernels accept every supported shape.  Layouts of the workspace
 // intermediates (all fp32):
-//   acum [b][H][nc][Q]   prefix sums of dt*A inside each chunk (0 past seqlen)
+//   acum [b][H][nc][Q]   prefix sums of dt*A inside each chunk (0 past
+//                        seqlen), as a two-float pair: the fp64 prefix rounded
+//                        to fp32 (hi) and the rounding remainder (lo)
 //   dtT  [b][H][nc][Q]   dt re-laid out per chunk (0 past seqlen)
 //   cb   [b][nc][G][Q][Q] C B^T of the chunk (only s-tiles <= l-tile written)
 //   S    [b][nc][H][P][N] chunk states, overwritten by k4 with the state
@@ -25,10 +27,18 @@ namespace ssd {
 // grid (nc, ceil(H/16), b), 256 threads.  A block stages dt for 16 heads of
 // one chunk through LDS (coalesced over heads), then every wave scans 4 heads:
 // each lane sums up to 4 consecutive tokens, the wave scans the lane totals.
+//
+// The prefix is accumulated in fp64 (dt*A is exact in fp64) and stored as
+// hi = fp32(prefix), lo = fp32(prefix - hi).  Consumers need differences
+// acum_l - acum_s of two prefixes that can be large (hundreds) while their
+// difference is small; in plain fp32 that subtraction loses |acum| * 2^-24
+// absolutely, which is the instability the stable segment sum of the fla
+// layer (`segment_sum`) avoids.  (hi_l - hi_s) + (lo_l - lo_s) is accurate to
+// a few ulps of the difference itself.
 __global__ void __launch_bounds__(256)
 k1_dA_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
-             float *__restrict__ acum, float *__restrict__ dtT, int L, int H,
-             int nc, int Q) {
+             float *__restrict__ acum_hi, float *__restrict__ acum_lo,
+             float *__restrict__ dtT, int L, int H, int nc, int Q) {
     __shared__ float s_dt[16][257];
     const int c = blockIdx.x, h0 = blockIdx.y * 16, b = blockIdx.z;
     const int tid = threadIdx.x;
@@ -45,29 +55,33 @@ k1_dA_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
     for (int jj = 0; jj < 4; ++jj) {
         const int hl = wave * 4 + jj, h = h0 + hl;
         if (h >= H) break;
-        const float Ah = A[h];
-        float a[4], d[4];
-        float run = 0.f;
+        const double Ah = (double)A[h];
+        double a[4];
+        float d[4];
+        double run = 0.0;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            a[e] = 0.f;
+            a[e] = 0.0;
             d[e] = 0.f;
             const int idx = lane * E + e;
             if (e < E && idx < Q) {
                 d[e] = s_dt[hl][idx];
-                run += d[e] * Ah;
+                run += (double)d[e] * Ah;
                 a[e] = run;
             }
         }
-        const float incl = wave_inclusive_scan(run, lane);
-        float excl = __shfl_up(incl, 1, kWave);
-        if (lane == 0) excl = 0.f;
+        const double incl = wave_inclusive_scan_f64(run, lane);
+        double excl = __shfl_up(incl, 1, kWave);
+        if (lane == 0) excl = 0.0;
         const size_t base = ((size_t)(b * H + h) * nc + c) * Q;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = lane * E + e;
             if (e < E && idx < Q) {
-                acum[base + idx] = excl + a[e];
+                const double v = excl + a[e];
+                const float hi = (float)v;
+                acum_hi[base + idx] = hi;
+                acum_lo[base + idx] = (float)(v - (double)hi);
                 dtT[base + idx] = d[e];
             }
         }
@@ -137,9 +151,9 @@ k2_chunk_cb(const T *__restrict__ Bm, const T *__restrict__ Cm,
 template <typename T>
 __global__ void __launch_bounds__(256)
 k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
-               const float *__restrict__ acum, const float *__restrict__ dtT,
-               float *__restrict__ S, int L, int H, int G, int P, int N, int nc,
-               int Q) {
+               const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+               const float *__restrict__ dtT, float *__restrict__ S, int L, int H,
+               int G, int P, int N, int nc, int Q) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int KB = 32;
     constexpr int PITCH = KB + 16 / (int)sizeof(T);
@@ -153,9 +167,10 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
     const int ntn = N / 16, ntiles = (P / 16) * ntn;
-    const float *ac = acum + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
     const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
-    const float aend = ac[Q - 1];
+    const float end_hi = ah[Q - 1], end_lo = al[Q - 1];
 
     f32x4 acc[TPW];
 #pragma unroll
@@ -171,7 +186,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
             float w = 0.f;
             typename Mma<T>::frag f = zero_frag<T>();
             if (in) {
-                w = fast_exp(aend - ac[s]) * dc[s];
+                w = fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s];
                 f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
             }
 #pragma unroll
@@ -219,7 +234,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
 // and the state after the last chunk is the final state.  Chunk states are
 // read kK4Prefetch chunks ahead so several loads are in flight per thread.
 __global__ void __launch_bounds__(256)
-k4_state_passing(float *__restrict__ S, const float *__restrict__ acum,
+k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
                  const float *init, float *final_state, int H, int PN, int nc,
                  int Q) {
     const int h = blockIdx.y, b = blockIdx.z;
@@ -228,7 +243,7 @@ k4_state_passing(float *__restrict__ S, const float *__restrict__ acum,
     const size_t soff = (size_t)(b * H + h) * PN + e0;
     float4 run = make_float4(0.f, 0.f, 0.f, 0.f);
     if (init) run = *reinterpret_cast<const float4 *>(init + soff);
-    const float *ac = acum + (size_t)(b * H + h) * nc * Q;
+    const float *ac = acum_hi + (size_t)(b * H + h) * nc * Q;
     constexpr int PF = kK4Prefetch;
     for (int c0 = 0; c0 < nc; c0 += PF) {
         float4 sv[PF];
@@ -272,9 +287,9 @@ template <typename T>
 __global__ void __launch_bounds__(256)
 k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
               const float *__restrict__ cb, const float *__restrict__ S,
-              const float *__restrict__ acum, const float *__restrict__ dtT,
-              const float *__restrict__ D, T *__restrict__ y, int L, int H, int G,
-              int P, int N, int nc, int Q) {
+              const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+              const float *__restrict__ dtT, const float *__restrict__ D,
+              T *__restrict__ y, int L, int H, int G, int P, int N, int nc, int Q) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SB = 64;
     constexpr int PITCH = SB + 16 / (int)sizeof(T);
@@ -291,7 +306,8 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
     const bool active = l0 < Q;
     const int row = l0 + r;
     const int npt = P / 16;
-    const float *ac = acum + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
     const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
 
     f32x4 acc[MAXPT];
@@ -320,13 +336,13 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp(ac[l0 + 4 * q + i]);
+            const float e = fast_exp(ah[l0 + 4 * q + i]);
 #pragma unroll
             for (int pt = 0; pt < MAXPT; ++pt) acc[pt][i] *= e;
         }
     }
 
-    const float arow = active ? ac[row] : 0.f;
+    const float row_hi = active ? ah[row] : 0.f, row_lo = active ? al[row] : 0.f;
     const float *cbrow = cb + (((size_t)(b * nc + c) * G + g) * Q + (active ? row : 0)) * Q;
     const int pv = P / VEC;
     for (int sb = 0; sb <= lb; ++sb) {
@@ -349,7 +365,8 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
             for (int jj = 0; jj < VEC; ++jj) {
                 const int s = sj0 + jj;
                 float v = 0.f;
-                if (s <= row && s < Q) v = cbrow[s] * fast_exp(arow - ac[s]) * dc[s];
+                if (s <= row && s < Q)
+                    v = cbrow[s] * fast_exp(prefix_diff(row_hi, row_lo, ah[s], al[s])) * dc[s];
                 m[jj] = from_f32<T>(v);
             }
 #pragma unroll
@@ -393,7 +410,7 @@ hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
     hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (a.H + 15) / 16, a.batch), dim3(256), 0,
-                       stream, a.dt, a.A, a.acum, a.dtT, a.L, a.H, nc, Q);
+                       stream, a.dt, a.A, a.acum_hi, a.acum_lo, a.dtT, a.L, a.H, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     const int nlb = (Q + 63) / 64;
     hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
@@ -404,17 +421,17 @@ hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent
     const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
     const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
     hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
-                       stream, (const T *)a.x, (const T *)a.B, a.acum, a.dtT, a.S, a.L,
-                       a.H, a.G, a.P, a.N, nc, Q);
+                       stream, (const T *)a.x, (const T *)a.B, a.acum_hi, a.acum_lo, a.dtT,
+                       a.S, a.L, a.H, a.G, a.P, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     const int PN = a.P * a.N;
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
-                       0, stream, a.S, a.acum, a.init, a.final_state, a.H, PN, nc, Q);
+                       0, stream, a.S, a.acum_hi, a.init, a.final_state, a.H, PN, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     const size_t k5_lds = (size_t)a.P * (64 + 16 / sizeof(T)) * sizeof(T);
     hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
-                       stream, (const T *)a.x, (const T *)a.C, a.cb, a.S, a.acum, a.dtT,
-                       a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q);
+                       stream, (const T *)a.x, (const T *)a.C, a.cb, a.S, a.acum_hi,
+                       a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     return hipGetLastError();
 }

@@ -1,8 +1,9 @@
 """Parity of the HIP path (through the C ABI) with the fp64 oracle.
 
-Bar: fp32 inputs -> floored max relative error <= 1e-4; bf16 inputs ->
-normwise relative error <= 2e-2, on y and on the final state separately
-(oracle/metrics.py).  Small problems are compared element by element on
+Bar: fp32 inputs -> max componentwise relative error <= 1e-4, measured
+against the magnitude of the summed terms (the oracle on absolute-valued
+inputs); bf16 inputs -> normwise relative error <= 2e-2; on y and on the
+final state separately (oracle/metrics.py).  Small problems are compared element by element on
 every output; the full-size workloads on sampled (batch, head) slices, which
 the serial oracle computes exactly (slices are independent).
 """
@@ -12,6 +13,7 @@ import numpy as np
 import pytest
 
 from oracle import metrics
+from oracle.metrics import abs_inputs
 from state_space_sequence_amd.inputs import WORKLOADS, make_inputs, workload_inputs
 
 pytestmark = pytest.mark.gpu
@@ -45,8 +47,19 @@ def gpu_forward(inp, io, Q, dev, init=True, final=True, D=True):
     return y.float().cpu().numpy(), (None if fin is None else fin.cpu().numpy())
 
 
-def check(got, ref, io, what):
-    err = metrics.parity_error(got, ref, io)
+def reference(oracle_mod, inp, want_abs=True):
+    """(y, final, y_abs, final_abs) from the fp64 oracle."""
+    args = ("x", "dt", "A", "B", "C", "D", "initial_state")
+    yr, fr = oracle_mod.forward(*(inp[k] for k in args))
+    if not want_abs:
+        return yr, fr, None, None
+    ia = abs_inputs(inp)
+    ya, fa = oracle_mod.forward(*(ia[k] for k in args))
+    return yr, fr, ya, fa
+
+
+def check(got, ref, io, what, ref_abs=None):
+    err = metrics.parity_error(got, ref, io, ref_abs)
     tol = metrics.tolerance(io)
     _say("  %-28s err=%.3e tol=%.0e" % (what, err, tol))
     assert np.all(np.isfinite(got)), what + " has non-finite values"
@@ -76,20 +89,21 @@ def test_small_problems_every_element(dev, oracle_mod, case):
     inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1 if init else 0.0,
                       seed=100 + L)
     y, fin = gpu_forward(inp, io, Q, dev)
-    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
-                                  inp["D"], inp["initial_state"])
-    check(y, yr, io, "y")
-    check(fin, finr, io, "final_state")
+    yr, finr, ya, fa = reference(oracle_mod, inp)
+    check(y, yr, io, "y", ya)
+    check(fin, finr, io, "final_state", fa)
+    if io == "bf16":
+        # bf16 inputs are checked normwise; also report the componentwise score
+        _say("  componentwise y %.2e (informational)" % metrics.componentwise_err(y, yr, ya))
 
 
 def test_tiny_workload(dev, oracle_mod):
     w = WORKLOADS["tiny_f32"]
     inp = workload_inputs(w)
     y, fin = gpu_forward(inp, w.io_dtype, w.chunk_len, dev)
-    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
-                                  inp["D"], inp["initial_state"])
-    check(y, yr, "f32", "tiny y")
-    check(fin, finr, "f32", "tiny final")
+    yr, finr, ya, fa = reference(oracle_mod, inp)
+    check(y, yr, "f32", "tiny y", ya)
+    check(fin, finr, "f32", "tiny final", fa)
 
 
 def _sample_slices(b, H, n, seed):
@@ -122,19 +136,19 @@ def test_full_size_workloads_sampled(dev, oracle_mod, name):
 def test_chunk_length_invariance_on_gpu(dev, oracle_mod):
     inp = make_inputs(2, 777, 4, 64, 128, 2, io_dtype="f32", init_std=0.1, seed=5)
     outs = {Q: gpu_forward(inp, "f32", Q, dev) for Q in (16, 64, 256)}
-    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
-                                  inp["D"], inp["initial_state"])
+    yr, finr, ya, fa = reference(oracle_mod, inp)
     for Q, (y, fin) in outs.items():
-        check(y, yr, "f32", "Q=%d y" % Q)
-        check(fin, finr, "f32", "Q=%d final" % Q)
+        check(y, yr, "f32", "Q=%d y" % Q, ya)
+        check(fin, finr, "f32", "Q=%d final" % Q, fa)
 
 
 def test_optional_arguments(dev, oracle_mod):
     inp = make_inputs(1, 200, 2, 32, 32, 1, io_dtype="f32", init_std=0.1, seed=6)
     y, fin = gpu_forward(inp, "f32", 64, dev, init=False, final=False, D=False)
     assert fin is None
-    yr, _ = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None, None)
-    check(y, yr, "f32", "no D / no init / no final")
+    inp0 = dict(inp, D=None, initial_state=None)
+    yr, _, ya, _ = reference(oracle_mod, inp0)
+    check(y, yr, "f32", "no D / no init / no final", ya)
 
 
 def test_final_state_may_alias_initial_state(dev, oracle_mod):
@@ -184,10 +198,9 @@ def test_decode_small_every_element(dev, oracle_mod, case):
     b, steps, H, P, N, G, io = case
     inp = make_inputs(b, steps, H, P, N, G, io_dtype=io, init_std=0.1, seed=20 + P)
     y, state, _ = _decode_run(inp, io, dev, steps)
-    yr, finr = oracle_mod.forward(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"],
-                                  inp["D"], inp["initial_state"])
-    check(y, yr, io, "decode y")
-    check(state, finr, io, "decode state")
+    yr, finr, ya, fa = reference(oracle_mod, inp)
+    check(y, yr, io, "decode y", ya)
+    check(state, finr, io, "decode state", fa)
 
 
 def test_decode_workload_vs_serial_and_chunked(dev, oracle_mod):
