@@ -104,9 +104,24 @@ def alg_flops_forward(w):
 
 
 def kernel_alg_bytes(name, w, es):
-    """Algorithmic bytes of one launch of each kernel of the five-kernel split:
-    what that kernel must read and write given its own inputs and outputs."""
+    """Algorithmic bytes of one launch of a kernel.
+
+    k_fused_ssd performs the whole SSD forward except the prefix sums and
+    the C B^T diagonal blocks, so its algorithmic bytes are those of the
+    forward itself (inputs read once, outputs written once).  The helper
+    kernels and the five kernels of the split path count what each must
+    read and write given its own inputs and outputs."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
+    if name == "k_fused_ssd":
+        return alg_bytes_forward(w, es)
+    if name == "k2b_block_cb_bt":
+        nb = -(-L // 32)
+        return 2 * b * L * G * N * es + b * nb * G * (32 * 32 + N * 32) * es
+    if name == "k1_dA_cumsum":
+        # dt in; prefix hi, lo and dt per block out (the padded block length)
+        q1 = 32 if os.environ.get("SSD_FORWARD_PATH", "") != "split" and N == 128 \
+            and P % 32 == 0 else Q
+        return b * L * H * 4 + 3 * b * H * (-(-L // q1)) * q1 * 4
     nc = -(-L // Q)
     per_chunk_vec = b * H * nc * Q * 4          # acum or dtT
     states = b * nc * H * P * N * 4
@@ -114,8 +129,6 @@ def kernel_alg_bytes(name, w, es):
     cb = b * nc * G * (ntl * (ntl + 1) // 2) * 256 * 4
     x = b * L * H * P * es
     bc1 = b * L * G * N * es
-    if name == "k1_dA_cumsum":
-        return b * L * H * 4 + 2 * per_chunk_vec
     if name == "k2_chunk_cb":
         return 2 * bc1 + cb
     if name == "k3_chunk_state":
@@ -154,20 +167,22 @@ def time_forward(w, dev, steps, warmup, ev):
     kw = dict(chunk_len=w.chunk_len, y=y, final_state=fin, workspace=ws)
     for _ in range(warmup):
         libssd.ssd_chunk_scan_fwd(*args, **kw)
-    nk = len(libssd.kernel_names())
-    events = [[ev.create() for _ in range(nk + 1)] for _ in range(steps)]
+    nev = libssd.max_kernels() + 1
+    events = [[ev.create() for _ in range(nev)] for _ in range(steps)]
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     e0, e1 = ev.create(), ev.create()
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     ev.record(e0, sh)
+    names = None
     for k in range(steps):
-        libssd.ssd_chunk_scan_fwd_timed(events[k], *args, **kw)
+        _, _, names = libssd.ssd_chunk_scan_fwd_timed(events[k], *args, **kw)
     ev.record(e1, sh)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
     total_ms = ev.ms(e0, e1)
+    nk = len(names)
     per_kernel = [sum(ev.ms(events[k][i], events[k][i + 1]) for k in range(steps)) / steps
                   for i in range(nk)]
     for row in events:
@@ -177,7 +192,7 @@ def time_forward(w, dev, steps, warmup, ev):
     ev.destroy(e1)
     del t, y, fin, ws
     return dict(host_s=h1 - h0, gpu_ms=total_ms, per_kernel_ms=per_kernel,
-                names=libssd.kernel_names(), inputs=inp)
+                names=names, inputs=inp)
 
 
 def time_decode(w, dev, ev, reps=3):

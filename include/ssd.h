@@ -81,7 +81,10 @@ const char *ssd_status_string(ssd_status status);
  * (pointers aside); on error *bytes is left unchanged.  The workspace holds
  * the per-chunk intermediates of the chunked algorithm (decay prefix sums,
  * the C B^T blocks and the per-chunk fp32 states) and needs no
- * initialisation.
+ * initialisation.  It depends on the forward path (see
+ * ssd_chunk_scan_fwd_timed): the split path keeps every chunk state
+ * (batch * nchunks * nheads * headdim * dstate fp32), the fused path only
+ * per-token decay vectors and the diagonal blocks of C B^T.
  */
 ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
                                              int headdim, int dstate,
@@ -118,21 +121,36 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
- * Kernels of one `ssd_chunk_scan_fwd` call, for timing.  The count is fixed
- * for a given library build; names are static strings (NULL when i is out of
- * range).
+ * Upper bound on the number of kernels one `ssd_chunk_scan_fwd` call
+ * launches (fixed for a library build).
  */
-int ssd_chunk_scan_fwd_kernel_count(void);
-const char *ssd_chunk_scan_fwd_kernel_name(int i);
+int ssd_chunk_scan_fwd_max_kernels(void);
 
 /*
  * Diagnostic twin of `ssd_chunk_scan_fwd`: identical arguments, identical
- * work and results, and in addition events[i] (caller-created hipEvent_t
- * handles) is recorded on `stream` immediately before kernel i of the call
- * and events[count] right after the last kernel, so the caller can read each
- * kernel's GPU time with hipEventElapsedTime.  nevents must be at least
- * ssd_chunk_scan_fwd_kernel_count() + 1 and every handle non-NULL, else
+ * work and results.  In addition, with k the number of kernels this call
+ * launches, events[i] (caller-created hipEvent_t handles) is recorded on
+ * `stream` immediately before kernel i for i < k and events[k] right after
+ * the last kernel; events[k+1 .. max] are recorded after that, so every
+ * handle passed in is recorded.  The caller reads each kernel's GPU time
+ * with hipEventElapsedTime.  *nkernels receives k and kernel_names[0..k-1]
+ * static kernel names (both may be NULL; kernel_names must have room for
+ * ssd_chunk_scan_fwd_max_kernels() entries).  nevents must be at least
+ * ssd_chunk_scan_fwd_max_kernels() + 1 with every handle non-NULL, else
  * SSD_ERR_INVALID_ARGUMENT.  A failed event record returns SSD_ERR_HIP.
+ *
+ * Forward path.  bf16 shapes with dstate 128 and headdim a multiple of 32
+ * run the fused path: k1 (prefix sums per 32-token block), k2b (the
+ * diagonal 32x32 blocks of C B^T) and one kernel that walks the sequence in
+ * 32-token blocks with the fp32 state in registers and writes y; inside a
+ * chunk it contracts the off-diagonal blocks of L o C B^T through the
+ * running state (their rank-dstate factorisation), so its work and result
+ * do not depend on chunk_len.  Other shapes run the five-kernel split
+ * (k1 .. k5) with the given chunk_len as its chunk size.  The environment variable
+ * SSD_FORWARD_PATH=split|fused overrides the choice for diagnostics
+ * (forcing "fused" where it does not apply returns SSD_ERR_UNSUPPORTED);
+ * the workspace size depends on the path, so query it under the same
+ * setting.
  */
 ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float *A,
                                     const void *B, const void *C, const float *D,
@@ -141,7 +159,8 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
                                     int headdim, int dstate, ssd_dtype io_dtype,
                                     void *y, float *final_state, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream,
-                                    hipEvent_t *events, int nevents);
+                                    hipEvent_t *events, int nevents, int *nkernels,
+                                    const char **kernel_names);
 
 /*
  * One decode step, in place.

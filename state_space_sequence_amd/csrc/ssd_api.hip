@@ -1,9 +1,12 @@
 // ssd_api.hip -- the extern "C" entry points declared in include/ssd.h:
-// argument validation, workspace layout and kernel dispatch.  Validation is
-// plain host code that runs before anything is enqueued.
+// argument validation, forward-path choice, workspace layout and kernel
+// dispatch.  Validation is plain host code that runs before anything is
+// enqueued.
 #include "ssd.h"
 
 #include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
@@ -47,23 +50,126 @@ ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
     return SSD_OK;
 }
 
+// Forward path for a shape: the fused kernel where it applies, the split
+// kernels otherwise.  SSD_FORWARD_PATH=split|fused overrides the choice (a
+// diagnostic switch for comparing the two); forcing "fused" on a shape it
+// does not cover is reported as unsupported.
+ssd_status choose_path(int headdim, int dstate, int chunk_len, ssd_dtype io, ssd::Path *out) {
+    const bool fused_ok = io == SSD_BF16
+                              ? ssd::fused_supported<ssd::bf16>(headdim, dstate, chunk_len)
+                              : ssd::fused_supported<float>(headdim, dstate, chunk_len);
+    const char *env = getenv("SSD_FORWARD_PATH");
+    if (env && strcmp(env, "split") == 0) {
+        *out = ssd::Path::Split;
+    } else if (env && strcmp(env, "fused") == 0) {
+        if (!fused_ok) return SSD_ERR_UNSUPPORTED;
+        *out = ssd::Path::Fused;
+    } else {
+        *out = fused_ok ? ssd::Path::Fused : ssd::Path::Split;
+    }
+    return SSD_OK;
+}
+
 struct Layout {
-    size_t acum_hi, acum_lo, dtT, cb, S, total;
+    size_t acum_hi, acum_lo, dtT, cb, S, bt, total;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
-                      int ngroups, int chunk_len) {
-    const size_t nc = (size_t)(seqlen + chunk_len - 1) / chunk_len;
-    const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups,
-                 Q = chunk_len;
+                      int ngroups, int chunk_len, ssd_dtype io, ssd::Path path) {
+    // the fused path works in fixed blocks of kFusedBlock tokens
+    const size_t Q = path == ssd::Path::Split ? (size_t)chunk_len : (size_t)ssd::kFusedBlock;
+    const size_t nc = ((size_t)seqlen + Q - 1) / Q;
+    const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups;
+    const size_t es = io == SSD_BF16 ? 2 : 4;
+    const size_t vec = round_up(b * H * nc * Q * sizeof(float));
     Layout l;
     l.acum_hi = 0;
-    l.acum_lo = l.acum_hi + round_up(b * H * nc * Q * sizeof(float));
-    l.dtT = l.acum_lo + round_up(b * H * nc * Q * sizeof(float));
-    l.cb = l.dtT + round_up(b * H * nc * Q * sizeof(float));
-    l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
-    l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
+    l.acum_lo = l.acum_hi + vec;
+    l.dtT = l.acum_lo + vec;
+    l.cb = l.dtT + vec;
+    if (path == ssd::Path::Split) {
+        l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
+        l.bt = 0;
+        l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
+    } else {
+        l.S = 0;
+        l.bt = 0;
+        l.total = l.cb + round_up(b * nc * G * Q * Q * es);
+    }
     return l;
+}
+
+ssd_status forward_impl(const void *x, const float *dt, const float *A, const void *B,
+                        const void *C, const float *D, const float *initial_state,
+                        int chunk_len, int ngroups, int batch, int seqlen, int nheads,
+                        int headdim, int dstate, ssd_dtype io_dtype, void *y,
+                        float *final_state, void *workspace, size_t workspace_bytes,
+                        hipStream_t stream, hipEvent_t *events, int *nkernels,
+                        const char **names) {
+    ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                        chunk_len, io_dtype);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
+    // 16-byte vector accesses on x, B, C, y and the states.
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
+        !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
+        (initial_state && !aligned(initial_state, 16)) ||
+        (final_state && !aligned(final_state, 16)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    ssd::Path path;
+    if ((st = choose_path(headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
+    const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                      chunk_len, io_dtype, path);
+    if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
+        return SSD_ERR_WORKSPACE;
+
+    ssd::ForwardArgs a;
+    a.x = x;
+    a.dt = dt;
+    a.A = A;
+    a.B = B;
+    a.C = C;
+    a.D = D;
+    a.init = initial_state;
+    a.y = y;
+    a.final_state = final_state;
+    a.batch = batch;
+    a.L = seqlen;
+    a.H = nheads;
+    a.G = ngroups;
+    a.P = headdim;
+    a.N = dstate;
+    a.Q = chunk_len;
+    a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
+    char *ws = static_cast<char *>(workspace);
+    a.acum_hi = reinterpret_cast<float *>(ws + lay.acum_hi);
+    a.acum_lo = reinterpret_cast<float *>(ws + lay.acum_lo);
+    a.dtT = reinterpret_cast<float *>(ws + lay.dtT);
+    a.cb = ws + lay.cb;
+    a.S = path == ssd::Path::Split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
+    a.bt = nullptr;
+
+    const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::kFusedKernels;
+    const char *const *kn =
+        path == ssd::Path::Split ? ssd::kSplitKernelNames : ssd::kFusedKernelNames;
+    if (nkernels) *nkernels = nk;
+    if (names)
+        for (int i = 0; i < nk; ++i) names[i] = kn[i];
+
+    hipError_t err;
+    if (path == ssd::Path::Split)
+        err = io_dtype == SSD_BF16 ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
+                                   : ssd::launch_split_forward<float>(a, stream, events);
+    else
+        err = io_dtype == SSD_BF16 ? ssd::launch_fused_forward<ssd::bf16>(a, stream, events)
+                                   : ssd::launch_fused_forward<float>(a, stream, events);
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    if (events) {
+        // unused trailing events are recorded too, so every handle is valid
+        for (int i = nk + 1; i <= ssd::kMaxForwardKernels; ++i)
+            if (hipEventRecord(events[i], stream) != hipSuccess) return SSD_ERR_HIP;
+    }
+    return SSD_OK;
 }
 
 }  // namespace
@@ -91,69 +197,13 @@ ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
     ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
-    *bytes = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len).total;
+    ssd::Path path;
+    if ((st = choose_path(headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
+    *bytes = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len,
+                            io_dtype, path)
+                 .total;
     return SSD_OK;
 }
-
-}  // extern "C"
-
-namespace {
-
-ssd_status forward_impl(const void *x, const float *dt, const float *A, const void *B,
-                        const void *C, const float *D, const float *initial_state,
-                        int chunk_len, int ngroups, int batch, int seqlen, int nheads,
-                        int headdim, int dstate, ssd_dtype io_dtype, void *y,
-                        float *final_state, void *workspace, size_t workspace_bytes,
-                        hipStream_t stream, hipEvent_t *events) {
-    ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
-                                        chunk_len, io_dtype);
-    if (st != SSD_OK) return st;
-    if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
-    // 16-byte vector accesses on x, B, C, y and the states.
-    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
-        !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)) ||
-        (initial_state && !aligned(initial_state, 16)) ||
-        (final_state && !aligned(final_state, 16)))
-        return SSD_ERR_INVALID_ARGUMENT;
-    const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
-                                      chunk_len);
-    if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
-        return SSD_ERR_WORKSPACE;
-
-    ssd::SplitArgs a;
-    a.x = x;
-    a.dt = dt;
-    a.A = A;
-    a.B = B;
-    a.C = C;
-    a.D = D;
-    a.init = initial_state;
-    a.y = y;
-    a.final_state = final_state;
-    a.batch = batch;
-    a.L = seqlen;
-    a.H = nheads;
-    a.G = ngroups;
-    a.P = headdim;
-    a.N = dstate;
-    a.Q = chunk_len;
-    a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
-    char *ws = static_cast<char *>(workspace);
-    a.acum_hi = reinterpret_cast<float *>(ws + lay.acum_hi);
-    a.acum_lo = reinterpret_cast<float *>(ws + lay.acum_lo);
-    a.dtT = reinterpret_cast<float *>(ws + lay.dtT);
-    a.cb = reinterpret_cast<float *>(ws + lay.cb);
-    a.S = reinterpret_cast<float *>(ws + lay.S);
-
-    hipError_t err = io_dtype == SSD_BF16
-                         ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
-                         : ssd::launch_split_forward<float>(a, stream, events);
-    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
-}
-
-}  // namespace
-
-extern "C" {
 
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const void *B, const void *C, const float *D,
@@ -164,14 +214,10 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               size_t workspace_bytes, hipStream_t stream) {
     return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
-                        workspace, workspace_bytes, stream, nullptr);
+                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
 }
 
-int ssd_chunk_scan_fwd_kernel_count(void) { return ssd::kForwardKernels; }
-
-const char *ssd_chunk_scan_fwd_kernel_name(int i) {
-    return (i >= 0 && i < ssd::kForwardKernels) ? ssd::kForwardKernelNames[i] : nullptr;
-}
+int ssd_chunk_scan_fwd_max_kernels(void) { return ssd::kMaxForwardKernels; }
 
 ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float *A,
                                     const void *B, const void *C, const float *D,
@@ -180,13 +226,14 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
                                     int headdim, int dstate, ssd_dtype io_dtype, void *y,
                                     float *final_state, void *workspace,
                                     size_t workspace_bytes, hipStream_t stream,
-                                    hipEvent_t *events, int nevents) {
-    if (!events || nevents < ssd::kForwardKernels + 1) return SSD_ERR_INVALID_ARGUMENT;
-    for (int i = 0; i <= ssd::kForwardKernels; ++i)
+                                    hipEvent_t *events, int nevents, int *nkernels,
+                                    const char **kernel_names) {
+    if (!events || nevents < ssd::kMaxForwardKernels + 1) return SSD_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i <= ssd::kMaxForwardKernels; ++i)
         if (!events[i]) return SSD_ERR_INVALID_ARGUMENT;
     return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
-                        workspace, workspace_bytes, stream, events);
+                        workspace, workspace_bytes, stream, events, nkernels, kernel_names);
 }
 
 ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,

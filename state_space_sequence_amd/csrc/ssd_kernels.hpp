@@ -13,7 +13,7 @@ constexpr int kK3TilesPerWave = 8;
 constexpr int kK4Prefetch = 4;
 
 // Problem and workspace pointers of one chunked forward call.
-struct SplitArgs {
+struct ForwardArgs {
     const void *x;
     const float *dt;
     const float *A;
@@ -24,23 +24,47 @@ struct SplitArgs {
     void *y;
     float *final_state;  // may be null
     int batch, L, H, G, P, N, Q, nchunks;
-    // workspace regions
+    // workspace regions shared by both forward paths
     float *acum_hi;  // [b][H][nc][Q]  fp32 part of the fp64 chunk prefix sums
     float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
-    float *dtT;      // [b][H][nc][Q]
-    float *cb;    // [b][nc][G][Q][Q]
-    float *S;     // [b][nc][H][P][N]
+    float *dtT;      // [b][H][nc][Q]  dt per chunk, 0 past seqlen
+    void *cb;        // split path: C B^T per chunk and group, fp32 [b][nc][G][Q][Q]
+                     // fused path: diagonal 32x32 blocks, bf16 [b][nblk][G][32 * 32]
+                     // in MFMA fragment order
+    float *S;        // split path: chunk states [b][nc][H][P][N]
+    void *bt;        // unused
+    // (fused path: acum_hi/acum_lo/dtT hold 32-token blocks, [b][H][nblk][32])
 };
 
-// Kernels of one forward call, in launch order.
-constexpr int kForwardKernels = 5;
-extern const char *const kForwardKernelNames[kForwardKernels];
+// Forward paths.  The split path runs the five kernels of the chunked
+// algorithm one after the other with the caller's chunk length and accepts
+// every supported shape; the fused path (bf16, dstate 128, headdim a
+// multiple of 32) runs one pass over the sequence per (batch, head, headdim
+// block) in 32-token blocks with the state in registers.
+enum class Path { Split, Fused };
 
-// Enqueue the forward.  When `events` is non-null, events[i] is recorded on
-// `stream` right before kernel i and events[kForwardKernels] after the last.
+constexpr int kSplitKernels = 5;
+constexpr int kFusedKernels = 3;
+constexpr int kMaxForwardKernels = 5;
+extern const char *const kSplitKernelNames[kSplitKernels];
+extern const char *const kFusedKernelNames[kFusedKernels];
+
+// Enqueue a forward.  When `events` is non-null, events[i] is recorded on
+// `stream` right before kernel i and events[nkernels] after the last.
 template <typename T>
-hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream,
+hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream,
                                 hipEvent_t *events = nullptr);
+template <typename T>
+hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream,
+                                hipEvent_t *events = nullptr);
+template <typename T> bool fused_supported(int P, int N, int Q);
+// Tokens per block of the fused path and the number of blocks for L tokens.
+constexpr int kFusedBlock = 32;
+int fused_nblk(int L);
+
+// k1 (shared by both paths).
+void launch_dA_cumsum(const float *dt, const float *A, float *acum_hi, float *acum_lo,
+                      float *dtT, int batch, int L, int H, int nc, int Q, hipStream_t stream);
 
 struct DecodeArgs {
     float *state;

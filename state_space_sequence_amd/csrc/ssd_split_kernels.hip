@@ -397,11 +397,17 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
 
 // --------------------------------------------------------------------- launch
 
-const char *const kForwardKernelNames[kForwardKernels] = {
+const char *const kSplitKernelNames[kSplitKernels] = {
     "k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing", "k5_chunk_scan"};
 
+void launch_dA_cumsum(const float *dt, const float *A, float *acum_hi, float *acum_lo,
+                      float *dtT, int batch, int L, int H, int nc, int Q, hipStream_t stream) {
+    hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (H + 15) / 16, batch), dim3(256), 0, stream, dt,
+                       A, acum_hi, acum_lo, dtT, L, H, nc, Q);
+}
+
 template <typename T>
-hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent_t *events) {
+hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
     const int nc = a.nchunks, Q = a.Q;
     int ev = 0;
     auto mark = [&]() -> hipError_t {
@@ -409,12 +415,11 @@ hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent
     };
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (a.H + 15) / 16, a.batch), dim3(256), 0,
-                       stream, a.dt, a.A, a.acum_hi, a.acum_lo, a.dtT, a.L, a.H, nc, Q);
+    launch_dA_cumsum(a.dt, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q, stream);
     if ((err = mark()) != hipSuccess) return err;
     const int nlb = (Q + 63) / 64;
     hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
-                       dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, a.cb, a.L,
+                       dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, (float *)a.cb, a.L,
                        a.G, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     const int ntiles = (a.P / 16) * (a.N / 16);
@@ -430,13 +435,13 @@ hipError_t launch_split_forward(const SplitArgs &a, hipStream_t stream, hipEvent
     if ((err = mark()) != hipSuccess) return err;
     const size_t k5_lds = (size_t)a.P * (64 + 16 / sizeof(T)) * sizeof(T);
     hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
-                       stream, (const T *)a.x, (const T *)a.C, a.cb, a.S, a.acum_hi,
+                       stream, (const T *)a.x, (const T *)a.C, (const float *)a.cb, a.S, a.acum_hi,
                        a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
     return hipGetLastError();
 }
 
-template hipError_t launch_split_forward<float>(const SplitArgs &, hipStream_t, hipEvent_t *);
-template hipError_t launch_split_forward<bf16>(const SplitArgs &, hipStream_t, hipEvent_t *);
+template hipError_t launch_split_forward<float>(const ForwardArgs &, hipStream_t, hipEvent_t *);
+template hipError_t launch_split_forward<bf16>(const ForwardArgs &, hipStream_t, hipEvent_t *);
 
 }  // namespace ssd

@@ -7,7 +7,7 @@ no fallback: if libssd.so is missing or cannot be loaded, every call raises.
 Python names mirror the C entry points:
     ssd_chunk_scan_fwd_workspace_size(...)       -> int bytes
     ssd_chunk_scan_fwd(x, dt, A, B, C, ...)      -> (y, final_state)
-    ssd_chunk_scan_fwd_timed(..., events)        -> (y, final_state)
+    ssd_chunk_scan_fwd_timed(events, x, ...)     -> (y, final_state, kernel names)
     ssd_state_update(state, x, dt, A, B, C, ...) -> y   (state updated in place)
 """
 from __future__ import annotations
@@ -65,12 +65,11 @@ def load():
         lib.ssd_chunk_scan_fwd_workspace_size.argtypes = [_i] * 8 + [ctypes.POINTER(_sz)]
         lib.ssd_chunk_scan_fwd.restype = _i
         lib.ssd_chunk_scan_fwd.argtypes = _FWD_ARGS
-        lib.ssd_chunk_scan_fwd_kernel_count.restype = _i
-        lib.ssd_chunk_scan_fwd_kernel_count.argtypes = []
-        lib.ssd_chunk_scan_fwd_kernel_name.restype = ctypes.c_char_p
-        lib.ssd_chunk_scan_fwd_kernel_name.argtypes = [_i]
+        lib.ssd_chunk_scan_fwd_max_kernels.restype = _i
+        lib.ssd_chunk_scan_fwd_max_kernels.argtypes = []
         lib.ssd_chunk_scan_fwd_timed.restype = _i
-        lib.ssd_chunk_scan_fwd_timed.argtypes = _FWD_ARGS + [ctypes.POINTER(_p), _i]
+        lib.ssd_chunk_scan_fwd_timed.argtypes = _FWD_ARGS + [
+            ctypes.POINTER(_p), _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_char_p)]
         lib.ssd_state_update.restype = _i
         lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
         _lib = lib
@@ -111,10 +110,8 @@ def _stream_handle(stream):
     return ctypes.c_void_p(stream.cuda_stream)
 
 
-def kernel_names():
-    lib = load()
-    return [lib.ssd_chunk_scan_fwd_kernel_name(i).decode()
-            for i in range(lib.ssd_chunk_scan_fwd_kernel_count())]
+def max_kernels() -> int:
+    return load().ssd_chunk_scan_fwd_max_kernels()
 
 
 def ssd_chunk_scan_fwd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
@@ -175,8 +172,14 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
         where = "ssd_chunk_scan_fwd"
     else:
         arr = (ctypes.c_void_p * len(timed_events))(*[ctypes.c_void_p(e) for e in timed_events])
-        st = lib.ssd_chunk_scan_fwd_timed(*args, arr, len(timed_events))
+        nk = _i(0)
+        names = (ctypes.c_char_p * max_kernels())()
+        st = lib.ssd_chunk_scan_fwd_timed(*args, arr, len(timed_events), ctypes.byref(nk),
+                                          names)
         where = "ssd_chunk_scan_fwd_timed"
+        if st == SSD_OK:
+            timed_events_info = [names[i].decode() for i in range(nk.value)]
+            return y, final_state, timed_events_info
     if st != SSD_OK:
         raise SsdError(st, where)
     return y, final_state
@@ -200,7 +203,9 @@ def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
                              chunk_len=256, ngroups=None, y=None, final_state=None,
                              workspace=None, return_final_state=True, stream=None):
     """``ssd_chunk_scan_fwd`` that also records the given hipEvent_t handles
-    (ints) around each kernel: events[i] before kernel i, events[-1] after."""
+    (ints, at least max_kernels()+1 of them) around each kernel: events[i]
+    before kernel i, events[k] after the last of the k kernels.  Returns
+    (y, final_state, kernel_names)."""
     return _forward(list(events), x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
                     y, final_state, workspace, return_final_state, stream)
 

@@ -44,8 +44,7 @@ def test_version_and_strings(lib):
     for code in range(5):
         assert lib.ssd_status_string(code)
     assert lib.ssd_status_string(99) == b"unknown status"
-    assert lib.ssd_chunk_scan_fwd_kernel_count() >= 1
-    assert lib.ssd_chunk_scan_fwd_kernel_name(-1) is None
+    assert lib.ssd_chunk_scan_fwd_max_kernels() >= 3
 
 
 FAKE = 0x10000  # 256-byte aligned, never dereferenced: validation fails first
@@ -57,12 +56,25 @@ def ws_size(lib, *args):
     return st, out.value
 
 
-def test_workspace_size(lib):
+def test_workspace_size(lib, monkeypatch):
+    nc = 32
+    vec = 3 * 4 * 80 * nc * 256 * 4
+    monkeypatch.setenv("SSD_FORWARD_PATH", "split")
     st, n = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
     assert st == 0
-    nc = 32
-    expect = 3 * 4 * 80 * nc * 256 * 4 + 4 * nc * 1 * 256 * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4
-    assert n >= expect and n - expect < 5 * 256
+    expect = vec + 4 * nc * 1 * 256 * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4
+    assert n >= expect and n - expect < 6 * 256
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    st, n = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
+    assert st == 0
+    nb = 8192 // 32
+    expect = 3 * 4 * 80 * nb * 32 * 4 + 4 * nb * 32 * 32 * 2
+    assert n >= expect and n - expect < 6 * 256
+    st, _ = ws_size(lib, 4, 8192, 80, 48, 128, 1, 256, 1)   # headdim 48: no fused path
+    assert st == 2
+    monkeypatch.delenv("SSD_FORWARD_PATH")
+    st, n_auto = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
+    assert st == 0 and n_auto == n                          # fused is the default here
     st, _ = ws_size(lib, 4, 8192, 80, 64, 128, 3, 256, 1)
     assert st == 1  # nheads % ngroups
     st, _ = ws_size(lib, 4, 8192, 80, 64, 128, 1, 100, 1)
@@ -105,11 +117,11 @@ def test_forward_validation(lib, kw, code):
 
 
 def test_timed_needs_enough_events(lib):
-    n = lib.ssd_chunk_scan_fwd_kernel_count()
+    n = lib.ssd_chunk_scan_fwd_max_kernels()
     arr = (ctypes.c_void_p * n)(*([FAKE] * n))
     st = lib.ssd_chunk_scan_fwd_timed(FAKE, FAKE, FAKE, FAKE, FAKE, None, None, 64, 1, 1,
                                       100, 2, 16, 16, 0, FAKE, None, FAKE, 1 << 40, None,
-                                      arr, n)
+                                      arr, n, None, None)
     assert st == 1
 
 

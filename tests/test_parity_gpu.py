@@ -34,6 +34,27 @@ def dev():
     return torch.device("cuda:0")
 
 
+@pytest.fixture(params=["split", "fused"])
+def path(request, monkeypatch):
+    """Run the test through one forward path (the library reads
+    SSD_FORWARD_PATH on every call)."""
+    monkeypatch.setenv("SSD_FORWARD_PATH", request.param)
+    return request.param
+
+
+def skip_if_path_unsupported(inp, io, Q):
+    from state_space_sequence_amd import libssd
+    b, L, H, P = inp["x"].shape
+    G, N = inp["B"].shape[2], inp["B"].shape[3]
+    try:
+        libssd.ssd_chunk_scan_fwd_workspace_size(b, L, H, P, N, G, Q,
+                                                 libssd.SSD_BF16 if io == "bf16" else libssd.SSD_F32)
+    except libssd.SsdError as e:
+        if e.status == libssd.SSD_ERR_UNSUPPORTED:
+            pytest.skip("shape not covered by this forward path")
+        raise
+
+
 def gpu_forward(inp, io, Q, dev, init=True, final=True, D=True):
     import torch
     from state_space_sequence_amd import libssd
@@ -78,16 +99,24 @@ SMALL = [
     (1, 100, 2, 64, 128, 1, 32, "bf16", True),
     (1, 64, 2, 16, 16, 2, 64, "f32", True),
     (3, 700, 4, 64, 128, 1, 256, "f32", True),
+    (2, 300, 4, 64, 128, 2, 64, "bf16", True),
+    (1, 1000, 4, 32, 128, 1, 256, "bf16", True),
+    (2, 777, 4, 64, 128, 2, 128, "f32", True),
+    (1, 40, 2, 16, 128, 1, 32, "f32", True),
+    (1, 33, 2, 32, 128, 2, 32, "bf16", False),
+    (1, 512, 2, 128, 128, 1, 256, "bf16", True),
+    (2, 257, 4, 96, 128, 4, 128, "bf16", True),
 ]
 
 
 @pytest.mark.parametrize("case", SMALL, ids=lambda c: "b%d_L%d_H%d_P%d_N%d_G%d_Q%d_%s%s" % (
     c[:8] + ("_init" if c[8] else "",)))
-def test_small_problems_every_element(dev, oracle_mod, case):
+def test_small_problems_every_element(dev, oracle_mod, path, case):
     b, L, H, P, N, G, Q, io, init = case
-    _say("case %s" % (case,))
+    _say("case %s path %s" % (case, path))
     inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1 if init else 0.0,
                       seed=100 + L)
+    skip_if_path_unsupported(inp, io, Q)
     y, fin = gpu_forward(inp, io, Q, dev)
     yr, finr, ya, fa = reference(oracle_mod, inp)
     check(y, yr, io, "y", ya)
@@ -115,10 +144,11 @@ def _sample_slices(b, H, n, seed):
 
 
 @pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b", "grouped_g8"])
-def test_full_size_workloads_sampled(dev, oracle_mod, name):
+def test_full_size_workloads_sampled(dev, oracle_mod, path, name):
     w = WORKLOADS[name]
-    _say("workload %s" % name)
+    _say("workload %s path %s" % (name, path))
     inp = workload_inputs(w)
+    skip_if_path_unsupported(inp, w.io_dtype, w.chunk_len)
     y, fin = gpu_forward(inp, w.io_dtype, w.chunk_len, dev)
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
     slices = _sample_slices(w.batch, w.nheads, 12, seed=7)
@@ -135,15 +165,16 @@ def test_full_size_workloads_sampled(dev, oracle_mod, name):
 
 def test_chunk_length_invariance_on_gpu(dev, oracle_mod):
     inp = make_inputs(2, 777, 4, 64, 128, 2, io_dtype="f32", init_std=0.1, seed=5)
-    outs = {Q: gpu_forward(inp, "f32", Q, dev) for Q in (16, 64, 256)}
+    outs = {Q: gpu_forward(inp, "f32", Q, dev) for Q in (16, 32, 64, 128, 256)}
     yr, finr, ya, fa = reference(oracle_mod, inp)
     for Q, (y, fin) in outs.items():
         check(y, yr, "f32", "Q=%d y" % Q, ya)
         check(fin, finr, "f32", "Q=%d final" % Q, fa)
 
 
-def test_optional_arguments(dev, oracle_mod):
-    inp = make_inputs(1, 200, 2, 32, 32, 1, io_dtype="f32", init_std=0.1, seed=6)
+@pytest.mark.parametrize("N", [32, 128])
+def test_optional_arguments(dev, oracle_mod, N):
+    inp = make_inputs(1, 200, 2, 32, N, 1, io_dtype="f32", init_std=0.1, seed=6)
     y, fin = gpu_forward(inp, "f32", 64, dev, init=False, final=False, D=False)
     assert fin is None
     inp0 = dict(inp, D=None, initial_state=None)
@@ -151,7 +182,7 @@ def test_optional_arguments(dev, oracle_mod):
     check(y, yr, "f32", "no D / no init / no final", ya)
 
 
-def test_final_state_may_alias_initial_state(dev, oracle_mod):
+def test_final_state_may_alias_initial_state(dev, oracle_mod, path):
     import torch
     from state_space_sequence_amd import libssd
     from state_space_sequence_amd.inputs import to_torch
@@ -166,12 +197,37 @@ def test_final_state_may_alias_initial_state(dev, oracle_mod):
     check(cache.cpu().numpy(), finr, "bf16", "aliased final")
 
 
-def test_deterministic(dev):
+def test_deterministic(dev, path):
     inp = make_inputs(2, 600, 8, 64, 128, 2, io_dtype="bf16", init_std=0.1, seed=9)
     y1, f1 = gpu_forward(inp, "bf16", 256, dev)
     y2, f2 = gpu_forward(inp, "bf16", 256, dev)
     np.testing.assert_array_equal(y1, y2)
     np.testing.assert_array_equal(f1, f2)
+
+
+def test_timed_variant_matches_and_names_kernels(dev, path):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    inp = make_inputs(1, 300, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=10)
+    t = to_torch(inp, "bf16", dev)
+    hip = __import__("ctypes").CDLL("libamdhip64.so")
+    evs = []
+    for _ in range(libssd.max_kernels() + 1):
+        e = __import__("ctypes").c_void_p()
+        assert hip.hipEventCreate(__import__("ctypes").byref(e)) == 0
+        evs.append(e.value)
+    y1, f1 = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                       t["initial_state"], chunk_len=128)
+    y2, f2, names = libssd.ssd_chunk_scan_fwd_timed(evs, t["x"], t["dt"], t["A"], t["B"],
+                                                    t["C"], t["D"], t["initial_state"],
+                                                    chunk_len=128)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+    assert names[0] == "k1_dA_cumsum"
+    assert len(names) == (5 if path == "split" else 3)
+    for e in evs:
+        hip.hipEventDestroy(__import__("ctypes").c_void_p(e))
 
 
 # ------------------------------------------------------------------ decode
@@ -203,7 +259,7 @@ def test_decode_small_every_element(dev, oracle_mod, case):
     check(state, finr, io, "decode state", fa)
 
 
-def test_decode_workload_vs_serial_and_chunked(dev, oracle_mod):
+def test_decode_workload_vs_serial_and_chunked(dev, oracle_mod, path):
     """64 decode steps of the b256 workload: against the serial oracle on
     sampled slices, and against the chunked forward over the same 64 tokens
     started from the same state (final state and every output)."""
