@@ -114,9 +114,10 @@ def kernel_alg_bytes(name, w, es):
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     if name == "k_fused_ssd":
         return alg_bytes_forward(w, es)
-    if name == "k2b_block_cb_bt":
+    if name == "k2b_block_cb":
+        # C and B rows in, one 32 x 32 bf16 diagonal block per block and group out
         nb = -(-L // 32)
-        return 2 * b * L * G * N * es + b * nb * G * (32 * 32 + N * 32) * es
+        return 2 * b * L * G * N * es + b * nb * G * 32 * 32 * 2
     if name == "k1_dA_cumsum":
         # dt in; prefix hi, lo and dt per block out (the padded block length)
         q1 = 32 if os.environ.get("SSD_FORWARD_PATH", "") != "split" and N == 128 \

@@ -34,6 +34,9 @@ def compile_flags():
         "-I" + INCLUDE, "-I" + CSRC,
         # packed fp32 instructions stay off: plain float code only
         "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+        # MFMA accumulators in ordinary VGPRs: the kernels update them with
+        # vector ALU ops between MFMAs, which the AGPR form turns into copies
+        "-mllvm", "-amdgpu-mfma-vgpr-form",
         "-Wno-unused-command-line-argument",
     ]
 

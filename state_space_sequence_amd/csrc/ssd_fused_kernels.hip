@@ -21,43 +21,73 @@
 // result equals the chunked result for every chunk length up to rounding;
 // the work per token does not depend on the chunk length.
 //
-// Workgroup = NW waves, wave w owns headdim tile w (16 columns) of the block
-// of PB = 16 NW columns.  Per 32-token block:
-//   stage (next block, double-buffered LDS): C and B rows straight from
-//          global memory into LDS (global_load_lds), x raw and decay-scaled
-//          (x'_s = exp(lambda_e - lambda_s) dt_s x_s) through registers, the
-//          diagonal block of C B^T (precomputed, in fragment order);
-//          per-token decay vectors two blocks ahead;
-//   output 2 row tiles x the wave's headdim tile: C h^T with h^T taken
-//          straight from the state registers as the MFMA B operand, then the
-//          diagonal block, then D x;
-//   state  h <- exp(lambda_e) h + B^T x'.
-// Operands that the MFMA needs transposed (B^T, x^T) are read from row-major
-// LDS with ds_read_b64_tr_b16: within each 16-lane group, lane 4a+c receives
-// element c of the 8-byte reads of lanes a, a+4, a+8, a+12, so pointing lane
-// j at row kbase + j/4, columns 4 (j%4) .. +3 of a row-major [k][n] tile
-// hands lane n the column n for k = kbase .. kbase+3.
+// Scaled state.  The registers hold h~ with h = sigma h~ for a scalar sigma
+// that the kernel tracks, so the per-block decay exp(lambda_e) multiplies
+// sigma instead of the 128 x 16 state tile of every wave:
+//   x'_s  = exp(lambda_e - lambda_s) dt_s x_s / sigma_{k+1}     (staged, bf16)
+//   y_l   = exp(lambda_l - lambda_e) sigma_{k+1} (C_l h~^T + [C B^T]_l x') + D x_l
+//   h~   += B^T x'
+// with sigma_{k+1} = sigma_k exp(lambda_e).  When sigma_{k+1} would fall
+// below exp(-40) the state is rescaled once (h~ *= sigma_k, sigma_k = 1), so
+// 1/sigma stays below exp(40) and nothing approaches the fp32 range.
 //
-// The diagonal block normally runs as
-//   exp(lambda_l - lambda_e) * (exp(lambda_e) C h^T + mask(C B^T) x'),
-// so its mask is a select on C B^T.  When the block's total decay exceeds
-// exp(-40) that form could overflow, and the block is evaluated with the
-// exact per-element weights exp(lambda_l - lambda_s) dt_s (s > l exactly 0,
-// the upper-triangle protection of the Kernel 5 page) on raw x, with D on
-// the diagonal.
+// The diagonal block uses the factored weights exp(lambda_l - lambda_e) and
+// exp(lambda_e - lambda_s) only when the block's total decay is at most
+// exp(-40) away from 1; otherwise both could leave the fp32 range, and the
+// block is evaluated with the exact per-element weights
+// exp(lambda_l - lambda_s) dt_s (s > l exactly 0, the upper-triangle
+// protection of the Kernel 5 page) on raw x, with D on the diagonal, and the
+// state decays explicitly (h~ <- sigma_k exp(lambda_e) h~ + B^T x', sigma = 1).
+//
+// Workgroup = NW waves; wave w owns headdim tile w (16 columns) of the
+// block of PB = 16 NW columns.  Per 32-token block:
+//   stage (next block, double-buffered LDS): C and B rows straight from
+//          global memory into LDS (global_load_lds) in a swizzled layout,
+//          x raw and scaled through registers, the causal diagonal block of
+//          C B^T (precomputed, in fragment order); decay vectors two
+//          blocks ahead;
+//   output y^T = h~ C^T + x'^T [C B^T]^T for the wave's 16 headdim columns
+//          and both 16-token tiles, with h~ taken straight from the state
+//          registers as the MFMA A operand; each lane ends with 4
+//          consecutive headdim values of one token (one 8-byte store);
+//   state  h~ += B^T x'.
+//
+// Register state layout: st[m][e] = h~[n][p] for p = 16 wave + (lane % 16)
+// and n = 32 (m >> 1) + 8 (lane / 16) + 4 (m & 1) + e, so st[2ks], st[2ks+1]
+// are the 8 consecutive n = 32 ks + 8 q .. +7 that the bf16 MFMA fragment of
+// K-step ks holds in lane group q.
+//
+// Operands that the MFMA needs transposed (B^T, x'^T) are read from
+// row-major LDS with ds_read_b64_tr_b16: within each 16-lane group, lane 4a+c
+// receives element c of the 8-byte reads of lanes a, a+4, a+8, a+12, so
+// pointing lane a + 4 e at row kbase + e and 4 consecutive columns of a
+// row-major [k][n] tile hands those 4 columns to lanes 4a .. 4a+3.
+//
+// C / B rows (256 bytes) sit in LDS without padding; 16-byte chunk c of row t
+// is stored in slot c ^ swz(t), swz(t) = (t&1) | (t&2)<<1 | (t>>1)&2.  The
+// fragment reads of C (16 rows, one chunk) then hit 8 distinct 16-byte bank
+// groups per 8 lanes, and the transposed reads of B at most two lanes per
+// bank.
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
 
 namespace ssd {
 
-constexpr int kBlk = 32;            // tokens per block
-constexpr float kSafeDecay = 40.f;  // max -lambda_e for the factored diagonal
+constexpr int kBlk = 32;                  // tokens per block
+constexpr float kSafeDecay = 40.f;        // max -lambda_e for the factored diagonal
+constexpr float kRescale = 4.24835426e-18f;  // exp(-40): smallest sigma kept unrescaled
 // s_waitcnt immediate for "vmcnt(0)" alone on gfx9-family targets:
 // vmcnt = 0, expcnt = 7 and lgkmcnt = 15 (both at their no-wait maximum).
 constexpr int kWaitVmcnt0 = 0x0F70;
+// ... and for "vmcnt(n)" alone (n < 64; bits 5:4 of n go to bits 15:14)
+constexpr int wait_vmcnt_imm(int n) { return kWaitVmcnt0 | (n & 15) | ((n >> 4) << 14); }
+// ... and for "lgkmcnt(0)" alone: vmcnt = 63 (bits 3:0 and 15:14), expcnt = 7.
+constexpr int kWaitLgkmcnt0 = 0xC07F;
+// word 3 of a raw buffer resource on gfx9-family targets (32-bit data format)
+constexpr int kBufferWord3 = 0x00020000;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -65,8 +95,8 @@ __device__ __forceinline__ bf16x4 lds_tr(const unsigned char *base, int byte_off
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
         (lds_bf16x4 *)((lds_u8 *)(base) + byte_off));
 }
-__device__ __forceinline__ bf16x4 lds_b64(const unsigned char *base, int byte_off) {
-    return *reinterpret_cast<const bf16x4 *>(base + byte_off);
+__device__ __forceinline__ bf16x8 lds_b128(const unsigned char *base, int byte_off) {
+    return *reinterpret_cast<const bf16x8 *>(base + byte_off);
 }
 __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
@@ -76,34 +106,68 @@ __device__ __forceinline__ void dma16(const void *gsrc, unsigned char *lds_wave_
                                      (__attribute__((address_space(3))) void *)(lds_wave_base),
                                      16, 0, 0);
 }
+__device__ __forceinline__ float uniform(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
+}
+__device__ __forceinline__ unsigned pack2(float a, float b) {
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    return __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
+}
+// 16-byte chunk swizzle of a C / B row in LDS (depends on row & 7 only)
+__device__ __forceinline__ int cb_swz(int row) {
+    return (row & 1) | ((row & 2) << 1) | ((row >> 1) & 2);
+}
 
 template <int PB>
 struct Fused {
     static constexpr int NW = PB / 16;                 // waves
     static constexpr int NT = 64 * NW;                 // threads
     static constexpr int N = 128;                      // dstate
-    static constexpr int RC = N / 8 + 1;               // chunks per C/B row (+1 pad)
-    static constexpr int RB = RC * 16;                 // bytes per C/B row in LDS
-    static constexpr int CB_CHUNKS = kBlk * RC;        // 544
-    static constexpr int CB_DMA = (CB_CHUNKS + 63) / 64;   // wave DMAs per C (or B)
-    static constexpr int DPW = (CB_DMA + NW - 1) / NW; // of which per wave
-    static constexpr int XC = PB / 8;                  // chunks per x row
-    static constexpr int XPC = XC + 2;                 // LDS pitch (chunks)
-    static constexpr int XB = XPC * 16;                // bytes per x row in LDS
-    // one staging buffer
+    static constexpr int ROWB = 2 * N;                 // bytes per C / B row
+    static constexpr int MAT = kBlk * ROWB;            // 8 KB per matrix
+    static constexpr int NDMA = MAT / 1024;            // wave-wide 16-byte DMAs per matrix
+    static constexpr int DPW = NDMA / NW;              // of which per wave
+    static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
+    static constexpr int XSB = 2 * PB + 32;            // staged x row pitch: transposed reads
+    // one stage: C rows, B rows, C B^T fragments, staged x of one block
     static constexpr int CS = 0;
-    static constexpr int BS = CS + CB_DMA * 1024;
-    static constexpr int XR = BS + CB_DMA * 1024;
-    static constexpr int XS = XR + kBlk * XB;
-    static constexpr int CBF = XS + kBlk * XB;         // 2 x 1 KB of C B^T fragments
-    static constexpr int BUF = CBF + 2048;
-    // per-block vectors (floats), three of them in flight
+    static constexpr int BS = MAT;
+    static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
+    static constexpr int XS = CBF + 2048;
+    static constexpr int STG = XS + kBlk * XSB;
+    // per-block vectors (floats), three blocks in flight
     enum { LHI = 0, LLO = 32, DT = 64, CF = 96, RP = 128, EX = 160, DELTA = 192, FLAG = 193,
            VFLOATS = 196 };
-    static constexpr int LDS = 2 * BUF + 3 * VFLOATS * 4;
-    static_assert(BUF % 16 == 0, "alignment");
-    static_assert(LDS <= 65536, "static LDS");
+    static constexpr int LDS = 3 * STG + 3 * VFLOATS * 4;
+    // global memory instructions every wave issues in every block, in this
+    // order: C / B DMAs, one C B^T DMA, x, raw x of the skip term (2),
+    // decay vectors (3), y stores (2)
+    static constexpr int VM_BLOCK = 2 * DPW + 1 + 1 + 2 + 3 + 2;
+    static_assert(NDMA % NW == 0, "DMAs split evenly over the waves");
+    static_assert(STG % 16 == 0 && XSB % 16 == 0, "alignment");
+    static_assert(2 * LDS <= 160 * 1024, "two workgroups per compute unit");
     static_assert(XC * kBlk == NT, "one x chunk per thread");
+    static_assert(VM_BLOCK < 64, "vmcnt immediate");
+};
+
+// Workgroup barrier for LDS only: this wave's LDS reads and writes complete
+// (lgkmcnt(0)), then s_barrier; the asm "memory" clobber keeps the compiler
+// from moving memory accesses across it.  __syncthreads() (or an LDS-scope
+// fence) would also make the wave wait for every outstanding global load,
+// store and LDS DMA (vmcnt(0)) at each barrier, the prefetches included;
+// the LDS writes of global_load_lds are covered by explicit vmcnt waits.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
+    asm volatile("s_barrier" ::: "memory");
+}
+
+// Scale bookkeeping of one block (identical in every wave).
+struct Book {
+    float sig_in;   // sigma entering the block
+    float sig;      // sigma after the block
+    float delta;    // exp(lambda_e)
+    bool fac;       // factored diagonal
+    bool rescale;   // h~ *= sig_in before the block (factored blocks only)
 };
 
 template <int PB>
@@ -115,11 +179,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
-    // Two staging buffers and the vectors as separate LDS objects: the
-    // compiler can then see that the DMA filling one buffer never aliases the
-    // reads of the other, and does not wait for the DMA before those reads.
-    __shared__ __align__(16) unsigned char sbuf0[S::BUF];
-    __shared__ __align__(16) unsigned char sbuf1[S::BUF];
+    // Three stages and the vectors as separate LDS objects: the compiler can
+    // then see that the DMA filling one stage never aliases the reads of
+    // another, and does not wait for the DMA before those reads.
+    __shared__ __align__(16) unsigned char stg0[S::STG];
+    __shared__ __align__(16) unsigned char stg1[S::STG];
+    __shared__ __align__(16) unsigned char stg2[S::STG];
     __shared__ __align__(16) float svec[3 * S::VFLOATS];
 
     const int npb = P / PB;
@@ -131,138 +196,228 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     const int p0 = pb * PB, pt = wave;
     const size_t bh = (size_t)b * H + h;
     const float Dh = D ? D[h] : 0.f;
-    const size_t GN = (size_t)G * N, HP = (size_t)H * P;
+    const int GN = G * N, HP = H * P;
 
-    // ---- per-lane LDS byte offsets (relative to a staging buffer)
-    const int c_rd = (r * S::RC + (q >> 1)) * 16 + (q & 1) * 8;          // C rows, lt 0
-    const int b_tr = ((8 * q + (r >> 2)) * S::RC + ((r & 3) >> 1)) * 16 + (r & 1) * 8;
-    const int xs_tr = ((8 * q + (r >> 2)) * S::XPC + 2 * pt + ((r & 3) >> 1)) * 16 + (r & 1) * 8;
-    const int xr_skip = ((4 * q + (r >> 2)) * S::XPC + 2 * pt + ((r & 3) >> 1)) * 16 + (r & 1) * 8;
+    // ---- per-lane LDS byte offsets (relative to a stage)
+    // C fragment of token row 16 lt + r, chunk 4 ks + q:
+    //   CS + c_rd[ks & 1] + 128 (ks >> 1) + 4096 lt
+    int c_rd[2];
+    {
+        const int sw = cb_swz(r), s2 = (sw >> 2) & 1, s01 = sw & 3;
+#pragma unroll
+        for (int par = 0; par < 2; ++par)
+            c_rd[par] = r * S::ROWB + 16 * (q ^ s01) + 64 * (par ^ s2);
+    }
+    // B^T, tile m, token half s: BS + b_tr[s][(m >> 1) & 1] + 128 (m >> 2) + 8 (m & 1)
+    int b_tr[2][2];
+    {
+        const int a = r & 3, e = r >> 2, w0 = e & 1, w2 = (e >> 1) & 1;
+#pragma unroll
+        for (int s = 0; s < 2; ++s)
+#pragma unroll
+            for (int mb = 0; mb < 2; ++mb)
+                b_tr[s][mb] = (8 * q + e + 4 * s) * S::ROWB + 64 * (mb ^ w2) +
+                              16 * (a ^ (w0 | (s << 1)));
+    }
+    // staged-x fragment (tokens 8q .. 8q+7, column r of the wave's tile): two
+    // transposed reads at xs_tr and xs_tr + 4 XSB
+    const int xs_tr = (8 * q + (r >> 2)) * S::XSB + 32 * pt + 8 * (r & 3);
     const int cbf_rd = lane * 16;
-    // diagonal-block masks: fragment element j of lane (r, q) is column 8q+j
-    u32x4 mask[2];
-#pragma unroll
-    for (int lt = 0; lt < 2; ++lt)
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-            const int row = 16 * lt + r, s0 = 8 * q + 2 * d;
-            mask[lt][d] = (s0 <= row ? 0x0000FFFFu : 0u) | (s0 + 1 <= row ? 0xFFFF0000u : 0u);
-        }
     // x staging: one 16-byte chunk per thread
     const int xs_row = tid / S::XC, xs_chunk = tid % S::XC;
-    const int x_st = (xs_row * S::XPC + xs_chunk) * 16;
-    // C / B DMA: wave w issues DMAs w, w + NW, ... of the CB_DMA per matrix
-    int dma_row[S::DPW], dma_chunk[S::DPW];
-#pragma unroll
-    for (int i = 0; i < S::DPW; ++i) {
-        const int pos = 64 * (wave + NW * i) + lane;
-        dma_row[i] = pos / S::RC;
-        const int slot = pos % S::RC;
-        dma_chunk[i] = slot < N / 8 ? slot : 0;  // pad slot: any valid chunk of the row
-    }
+    const int xs_st = xs_row * S::XSB + 16 * xs_chunk;
+    const int x_off = xs_row * HP + 8 * xs_chunk;  // elements from the block's first row
+    // C / B DMA i of this wave covers LDS bytes 1024 (wave + NW i) + 16 lane:
+    // row dma_row + 4 NW i, slot lane & 15, holding global chunk dma_chunk
+    const int dma_row = 4 * wave + (lane >> 4);
+    const int dma_chunk = (lane & 15) ^ cb_swz(dma_row);
+    const int dma_off = dma_row * GN * 2 + 16 * dma_chunk;  // bytes
+    // y and the raw x of the skip term: token 16 lt + r, columns
+    // p0 + 16 pt + 4 q .. +3; element offset from the block's first row
+    const int y_off = r * HP + 16 * pt + 4 * q;
 
-    // ---- register-resident state: st[n] = S^T[16 n + 4 q + e][p0 + 16 pt + r]
+    // ---- register-resident scaled state
     f32x4 st[8];
 #pragma unroll
-    for (int n = 0; n < 8; ++n) {
-        st[n] = zero4();
+    for (int m = 0; m < 8; ++m) {
+        st[m] = zero4();
         if (init) {
             const float4 v = *reinterpret_cast<const float4 *>(
-                init + (bh * P + p0 + 16 * pt + r) * N + 16 * n + 4 * q);
-            st[n] = f32x4{v.x, v.y, v.z, v.w};
+                init + (bh * P + p0 + 16 * pt + r) * N + 32 * (m >> 1) + 8 * q + 4 * (m & 1));
+            st[m] = f32x4{v.x, v.y, v.z, v.w};
         }
     }
 
+    auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
     auto V = [&](int kb) -> float * { return svec + (kb % 3) * S::VFLOATS; };
-    auto vec_load = [&](int kb, float &lh, float &ll, float &dv) {
-        const size_t o = (bh * nblk + kb) * kBlk + lane;
-        lh = lam_hi[o];
-        ll = lam_lo[o];
-        dv = dtb[o];
+    // decay vectors of block kb; every lane loads (lanes 32-63 repeat 0-31)
+    auto vec_load = [&](int kb, f32x4 &vv) {
+        const size_t o = (bh * nblk + kb) * kBlk + (lane & (kBlk - 1));
+        vv = f32x4{lam_hi[o], lam_lo[o], dtb[o], 0.f};
     };
-    auto vec_store = [&](int kb, float lh, float ll, float dv) {
+    // derived per-token vectors of block kb into LDS (lanes 0-31 of one wave)
+    auto vec_store = [&](int kb, const f32x4 &vv) {
+        const float lh = vv[0], ll = vv[1], dv = vv[2];
         float *v = V(kb);
         const float eh = __shfl(lh, kBlk - 1, kWave), el = __shfl(ll, kBlk - 1, kWave);
-        const float neg_e = -(eh + el);
-        v[S::LHI + lane] = lh;
-        v[S::LLO + lane] = ll;
-        v[S::DT + lane] = dv;
-        v[S::CF + lane] = fast_exp(prefix_diff(eh, el, lh, ll)) * dv;
-        v[S::RP + lane] = neg_e <= kSafeDecay ? fast_exp(prefix_diff(lh, ll, eh, el)) : 0.f;
-        v[S::EX + lane] = fast_exp(lh + ll);
-        if (lane == kBlk - 1) {
-            v[S::DELTA] = fast_exp(eh + el);
-            v[S::FLAG] = neg_e <= kSafeDecay ? 1.f : 0.f;
-        }
-    };
-    // C, B rows and the C B^T fragments of block kb into the buffer at `buf`
-    auto dma_block = [&](int kb, unsigned char *buf) {
-        const int t0 = kb * kBlk;
-        const int lim = L - 1 - t0;
-        const bf16 *crow0 = Cm + ((size_t)b * L + t0) * GN + (size_t)g * N;
-        const bf16 *brow0 = Bm + ((size_t)b * L + t0) * GN + (size_t)g * N;
-#pragma unroll
-        for (int i = 0; i < S::DPW; ++i) {
-            const int d = wave + NW * i;
-            if (d < S::CB_DMA && 64 * d + lane < S::CB_CHUNKS) {
-                const size_t off = (size_t)min(dma_row[i], lim) * GN + 8 * dma_chunk[i];
-                dma16(crow0 + off, buf + S::CS + 1024 * d);
-                dma16(brow0 + off, buf + S::BS + 1024 * d);
+        if (lane < kBlk) {
+            const bool fac = -(eh + el) <= kSafeDecay;
+            v[S::LHI + lane] = lh;
+            v[S::LLO + lane] = ll;
+            v[S::DT + lane] = dv;
+            v[S::CF + lane] = fast_exp(prefix_diff(eh, el, lh, ll)) * dv;
+            v[S::RP + lane] = fac ? fast_exp(prefix_diff(lh, ll, eh, el)) : 0.f;
+            v[S::EX + lane] = fast_exp(lh + ll);
+            if (lane == kBlk - 1) {
+                v[S::DELTA] = fast_exp(eh + el);
+                v[S::FLAG] = fac ? 1.f : 0.f;
             }
         }
-        if (wave < 2)
-            dma16(cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk) + 8 * (64 * wave + lane),
-                  buf + S::CBF + 1024 * wave);
     };
-    auto x_load = [&](int kb) -> bf16x8 {
-        const int t = min(kb * kBlk + xs_row, L - 1);
-        return load_frag(x + ((size_t)b * L + t) * HP + h * P + p0 + 8 * xs_chunk);
+    auto book = [&](int kb, float sig_in) -> Book {
+        const float *v = V(kb);
+        Book bk;
+        bk.sig_in = sig_in;
+        bk.delta = uniform(v[S::DELTA]);
+        bk.fac = uniform(v[S::FLAG]) != 0.f;
+        bk.rescale = false;
+        if (bk.fac) {
+            bk.sig = sig_in * bk.delta;
+            if (bk.sig < kRescale) {
+                bk.rescale = true;
+                bk.sig = bk.delta;
+            }
+        } else {
+            bk.sig = 1.f;
+        }
+        return bk;
     };
-    auto x_store = [&](int kb, unsigned char *buf, bf16x8 xv) {
-        const float cf = V(kb)[S::CF + xs_row];
-        bf16x8 xsv;
+    // C, B rows and the C B^T fragments of block kb into stage `buf`: DPW
+    // DMAs per matrix and one C B^T DMA (waves 2w' and 2w'+1 both copy half
+    // w' of the 2 KB when NW = 4)
+    auto dma_block = [&](int kb, unsigned char *buf) {
+        const int t0 = kb * kBlk;
+        const unsigned char *crow =
+            reinterpret_cast<const unsigned char *>(Cm + ((size_t)b * L + t0) * GN + (size_t)g * N);
+        const unsigned char *brow =
+            reinterpret_cast<const unsigned char *>(Bm + ((size_t)b * L + t0) * GN + (size_t)g * N);
+        if (t0 + kBlk <= L) {
 #pragma unroll
-        for (int j = 0; j < 8; ++j) xsv[j] = (bf16)((float)xv[j] * cf);
-        *reinterpret_cast<bf16x8 *>(buf + S::XR + x_st) = xv;
-        *reinterpret_cast<bf16x8 *>(buf + S::XS + x_st) = xsv;
+            for (int i = 0; i < S::DPW; ++i) {
+                const int off = dma_off + i * (4 * NW * GN * 2);
+                dma16(crow + off, buf + S::CS + 1024 * (wave + NW * i));
+                dma16(brow + off, buf + S::BS + 1024 * (wave + NW * i));
+            }
+        } else {
+            // last, partial block: rows past the end repeat the last row
+            const int lim = L - 1 - t0;
+#pragma unroll
+            for (int i = 0; i < S::DPW; ++i) {
+                const int off = min(dma_row + 4 * NW * i, lim) * GN * 2 + 16 * dma_chunk;
+                dma16(crow + off, buf + S::CS + 1024 * (wave + NW * i));
+                dma16(brow + off, buf + S::BS + 1024 * (wave + NW * i));
+            }
+        }
+        const int half = NW == 4 ? wave >> 1 : wave;
+        dma16(cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk) + 8 * (64 * half + lane),
+              buf + S::CBF + 1024 * half);
+    };
+    // x of block kb: one 16-byte chunk per thread, and the raw x of the skip
+    // term (two 8-byte pieces per lane); rows past the end repeat the last row
+    auto x_load = [&](int kb, bf16x8 &xv, uint2 (&sk)[2]) {
+        const int t0 = kb * kBlk;
+        const bf16 *xb = x + ((size_t)b * L + t0) * HP + (size_t)h * P + p0;
+        if (t0 + kBlk <= L) {
+            xv = load_frag(xb + x_off);
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt)
+                sk[lt] = *reinterpret_cast<const uint2 *>(xb + y_off + lt * 16 * HP);
+        } else {
+            const int lim = L - 1 - t0;
+            xv = load_frag(xb + (size_t)min(xs_row, lim) * HP + 8 * xs_chunk);
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt)
+                sk[lt] = *reinterpret_cast<const uint2 *>(
+                    xb + (size_t)min(16 * lt + r, lim) * HP + 16 * pt + 4 * q);
+        }
+    };
+    // staged x of block kb (bookkeeping bkx): x'_s = x_s cf_s / sigma on
+    // factored blocks, raw x on exact blocks
+    auto x_store = [&](int kb, unsigned char *buf, bf16x8 xv, const Book &bkx) {
+        bf16x8 xsv = xv;
+        if (bkx.fac) {
+            const float cf = V(kb)[S::CF + xs_row] * __builtin_amdgcn_rcpf(bkx.sig);
+#pragma unroll
+            for (int j = 0; j < 8; ++j) xsv[j] = (bf16)((float)xv[j] * cf);
+        }
+        *reinterpret_cast<bf16x8 *>(buf + S::XS + xs_st) = xsv;
+    };
+    // y through a buffer resource over this batch's rows: the stores of
+    // tokens past the end fall outside it and are dropped by the hardware
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+    const int y_boff = (y_off + h * P + p0) * 2;
+    auto y_store = [&](int kb, const f32x4 (&acc)[2]) {
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+            const u32x2 v = {pack2(acc[lt][0], acc[lt][1]), pack2(acc[lt][2], acc[lt][3])};
+            __builtin_amdgcn_raw_buffer_store_b64(
+                v, y_rsrc, y_boff + (kb * kBlk + 16 * lt) * HP * 2, 0, 0);
+        }
     };
 
-    // ---- prologue
+    // ---- prologue.  Every global load runs ahead of its use: C / B rows and
+    // C B^T two blocks (three LDS stages), x and the skip-term x two blocks
+    // (registers xq / sk, set kb % 3), the decay vectors three blocks
+    // (registers vq, set kb % 3; block kb's are stored to LDS by wave
+    // kb % NW at the end of block kb - 2).  Past the last block the loads
+    // repeat it, so every block issues the same global memory instructions.
+    Book bk;
+    bf16x8 xq[3];
+    uint2 sk[3][2];
+    f32x4 vq[3];
     {
-        float lh, ll, dv;
-        if (wave == 0 && lane < kBlk) {
-            vec_load(0, lh, ll, dv);
-            vec_store(0, lh, ll, dv);
-        }
-        if (wave == (1 % NW) && lane < kBlk && nblk > 1) {
-            vec_load(1, lh, ll, dv);
-            vec_store(1, lh, ll, dv);
-        }
-        dma_block(0, sbuf0);
-        const bf16x8 xv = x_load(0);
-        __syncthreads();
-        x_store(0, sbuf0, xv);
+        const int last = nblk - 1;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) vec_load(min(j, last), vq[j]);
+        dma_block(0, stg0);
+        x_load(0, xq[0], sk[0]);
+        dma_block(min(1, last), stg1);
+        x_load(min(1, last), xq[1], sk[1]);
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
+        if (wave == 0) vec_store(0, vq[0]);
+        if (wave == 1 && nblk > 1) vec_store(1, vq[1]);
+        lds_barrier();
+        bk = book(0, 1.f);
+        x_store(0, stg0, xq[0], bk);
+        lds_barrier();
     }
+    float sig_out = 1.f;
 
-    auto block = [&](int kb, unsigned char *cur, unsigned char *nxt) {
-        const bool more1 = kb + 1 < nblk, more2 = kb + 2 < nblk;
-        const bool vec_wave = more2 && wave == (kb + 2) % NW && lane < kBlk;
-        bf16x8 xv_next = zero_frag<bf16>();
-        float nlh = 0.f, nll = 0.f, ndv = 0.f;
-        if (more1) {
-            dma_block(kb + 1, nxt);
-            xv_next = x_load(kb + 1);
-        }
-        if (vec_wave) vec_load(kb + 2, nlh, nll, ndv);
+    // block kb, si = kb % 3 (a literal in each unrolled copy)
+    auto block = [&](int kb, const int si) {
+        unsigned char *cur = stage(si);
+        const int last = nblk - 1;
+        const bool more1 = kb + 1 < nblk;
+        // ---- global memory issue: the same instructions in every block, in
+        // this order (the wait at the end of the block counts them)
+        dma_block(min(kb + 2, last), stage((si + 2) % 3));
+        __builtin_amdgcn_sched_barrier(0);
+        x_load(min(kb + 2, last), xq[(si + 2) % 3], sk[(si + 2) % 3]);
+        vec_load(min(kb + 3, last), vq[si]);
+        __builtin_amdgcn_sched_barrier(0);
+
+        Book bk1 = bk;
+        if (more1) bk1 = book(kb + 1, bk.sig);
 
         const float *v = V(kb);
-        const bool factored = v[S::FLAG] != 0.f;
-        const float delta = v[S::DELTA];
+        if (bk.rescale) {
+#pragma unroll
+            for (int m = 0; m < 8; ++m) st[m] *= bk.sig_in;
+        }
 
-        // -------- outputs: C h^T for both 16-row tiles
-        f32x4 acc0 = zero4(), acc1 = zero4();
+        // -------- y^T = h~ C^T for both 16-token tiles
+        f32x4 acc[2] = {zero4(), zero4()};
 #pragma unroll
         for (int ks = 0; ks < 4; ++ks) {
             bf16x8 hb;
@@ -271,115 +426,99 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                 hb[e] = (bf16)st[2 * ks][e];
                 hb[4 + e] = (bf16)st[2 * ks + 1][e];
             }
-            const bf16x8 a0 = join(lds_b64(cur, S::CS + c_rd + 64 * ks),
-                                   lds_b64(cur, S::CS + c_rd + 64 * ks + 32));
-            const bf16x8 a1 = join(lds_b64(cur, S::CS + c_rd + 16 * S::RB + 64 * ks),
-                                   lds_b64(cur, S::CS + c_rd + 16 * S::RB + 64 * ks + 32));
-            acc0 = Mma<bf16>::mma(a0, hb, acc0);
-            acc1 = Mma<bf16>::mma(a1, hb, acc1);
-        }
-        const bf16x8 xs = join(lds_tr(cur, S::XS + xs_tr), lds_tr(cur, S::XS + xs_tr + 4 * S::XB));
-        if (factored) {
-            acc0 *= delta;
-            acc1 *= delta;
-            bf16x8 m0 = *reinterpret_cast<const bf16x8 *>(cur + S::CBF + cbf_rd);
-            bf16x8 m1 = *reinterpret_cast<const bf16x8 *>(cur + S::CBF + 1024 + cbf_rd);
-            m0 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, m0) & mask[0]);
-            m1 = __builtin_bit_cast(bf16x8, __builtin_bit_cast(u32x4, m1) & mask[1]);
-            acc0 = Mma<bf16>::mma(m0, xs, acc0);
-            acc1 = Mma<bf16>::mma(m1, xs, acc1);
-            const f32x4 rp0 = *reinterpret_cast<const f32x4 *>(v + S::RP + 4 * q);
-            const f32x4 rp1 = *reinterpret_cast<const f32x4 *>(v + S::RP + 16 + 4 * q);
-            const bf16x4 x0 = lds_tr(cur, S::XR + xr_skip);
-            const bf16x4 x1 = lds_tr(cur, S::XR + xr_skip + 16 * S::XB);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                acc0[e] = acc0[e] * rp0[e] + Dh * (float)x0[e];
-                acc1[e] = acc1[e] * rp1[e] + Dh * (float)x1[e];
+            for (int lt = 0; lt < 2; ++lt) {
+                const bf16x8 cfr = lds_b128(cur, S::CS + c_rd[ks & 1] + 128 * (ks >> 1) + 4096 * lt);
+                acc[lt] = Mma<bf16>::mma(hb, cfr, acc[lt]);
+            }
+        }
+        bf16x8 xs = join(lds_tr(cur, S::XS + xs_tr), lds_tr(cur, S::XS + xs_tr + 4 * S::XSB));
+        if (bk.fac) {
+            // staged x is x' = exp(lambda_e - lambda_s) dt_s x_s / sigma
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt) {
+                acc[lt] = Mma<bf16>::mma(xs, lds_b128(cur, S::CBF + 1024 * lt + cbf_rd), acc[lt]);
+                const float f = v[S::RP + 16 * lt + r] * bk.sig;
+                const bf16x4 xr = __builtin_bit_cast(bf16x4, sk[si][lt]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) acc[lt][e] = acc[lt][e] * f + Dh * (float)xr[e];
             }
         } else {
-            const f32x4 ex0 = *reinterpret_cast<const f32x4 *>(v + S::EX + 4 * q);
-            const f32x4 ex1 = *reinterpret_cast<const f32x4 *>(v + S::EX + 16 + 4 * q);
-            acc0 *= ex0;
-            acc1 *= ex1;
-            const bf16x8 xb =
-                join(lds_tr(cur, S::XR + xs_tr), lds_tr(cur, S::XR + xs_tr + 4 * S::XB));
+            // staged x is raw x: exact weights exp(lambda_l - lambda_s) dt_s, D on the diagonal
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt) {
                 const int row = 16 * lt + r;
-                const bf16x8 cbv =
-                    *reinterpret_cast<const bf16x8 *>(cur + S::CBF + 1024 * lt + cbf_rd);
+                acc[lt] *= v[S::EX + row] * bk.sig_in;
+                const bf16x8 cbv = lds_b128(cur, S::CBF + 1024 * lt + cbf_rd);
                 const float lh = v[S::LHI + row], ll = v[S::LLO + row];
-                bf16x8 m;
+                bf16x8 wgt;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = 8 * q + j;
-                    float w = 0.f;
-                    if (s <= row) {
-                        w = (float)cbv[j] *
-                            fast_exp(prefix_diff(lh, ll, v[S::LHI + s], v[S::LLO + s])) *
-                            v[S::DT + s];
-                        if (s == row) w += Dh;
-                    }
-                    m[j] = (bf16)w;
+                    const float w = (float)cbv[j] *
+                                    fast_exp(fminf(prefix_diff(lh, ll, v[S::LHI + s], v[S::LLO + s]), 0.f)) *
+                                    v[S::DT + s] + (s == row ? Dh : 0.f);
+                    wgt[j] = (bf16)(s <= row ? w : 0.f);
                 }
-                if (lt == 0)
-                    acc0 = Mma<bf16>::mma(m, xb, acc0);
-                else
-                    acc1 = Mma<bf16>::mma(m, xb, acc1);
+                acc[lt] = Mma<bf16>::mma(xs, wgt, acc[lt]);
             }
-        }
-        {
-            const int t0 = kb * kBlk;
-            bf16 *yb = y + ((size_t)b * L + t0) * HP + h * P + p0 + 16 * pt + r;
-            if (t0 + kBlk <= L) {
+            // the state update takes x' = exp(lambda_e - lambda_s) dt_s x_s
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    yb[(size_t)(4 * q + e) * HP] = (bf16)acc0[e];
-                    yb[(size_t)(16 + 4 * q + e) * HP] = (bf16)acc1[e];
-                }
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    if (t0 + 4 * q + e < L) yb[(size_t)(4 * q + e) * HP] = (bf16)acc0[e];
-                    if (t0 + 16 + 4 * q + e < L) yb[(size_t)(16 + 4 * q + e) * HP] = (bf16)acc1[e];
-                }
-            }
+            for (int j = 0; j < 8; ++j) xs[j] = (bf16)((float)xs[j] * v[S::CF + 8 * q + j]);
         }
+        __builtin_amdgcn_sched_barrier(0);
+        y_store(kb, acc);
+        __builtin_amdgcn_sched_barrier(0);
 
-        // -------- state: h <- exp(lambda_e) h + B^T x'
+        // -------- state: h~ += B^T x'  (exact blocks: h~ <- sig_in delta h~ + B^T x')
+        if (!bk.fac) {
+            const float sd = bk.sig_in * bk.delta;
 #pragma unroll
-        for (int n = 0; n < 8; ++n) {
-            const bf16x8 a = join(lds_tr(cur, S::BS + b_tr + 32 * n),
-                                  lds_tr(cur, S::BS + b_tr + 4 * S::RB + 32 * n));
-            st[n] = Mma<bf16>::mma(a, xs, st[n] * delta);
+            for (int m = 0; m < 8; ++m) st[m] *= sd;
         }
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int o = 128 * (m >> 2) + 8 * (m & 1);
+            const bf16x8 a = join(lds_tr(cur, S::BS + b_tr[0][(m >> 1) & 1] + o),
+                                  lds_tr(cur, S::BS + b_tr[1][(m >> 1) & 1] + o));
+            st[m] = Mma<bf16>::mma(a, xs, st[m]);
+        }
+        sig_out = bk.sig;
 
-        // -------- stage the next block, vectors two ahead
-        if (more1) x_store(kb + 1, nxt, xv_next);
-        if (vec_wave) vec_store(kb + 2, nlh, nll, ndv);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        __syncthreads();
+        // -------- stage x of the next block, decay vectors two ahead
+        if (more1) x_store(kb + 1, stage((si + 1) % 3), xq[(si + 1) % 3], bk1);
+        if (kb + 2 < nblk && wave == (kb + 2) % NW) vec_store(kb + 2, vq[(si + 2) % 3]);
+        // The next block reads the stage whose DMA was issued in the previous
+        // block: all VM_BLOCK global memory instructions of this block may
+        // stay in flight, everything older has completed.
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_BLOCK));
+        lds_barrier();
+        bk = bk1;
     };
 
-    for (int kb = 0; kb < nblk; kb += 2) {
-        block(kb, sbuf0, sbuf1);
-        if (kb + 1 < nblk) block(kb + 1, sbuf1, sbuf0);
+    for (int kb = 0; kb < nblk; kb += 3) {
+        block(kb, 0);
+        if (kb + 1 < nblk) block(kb + 1, 1);
+        if (kb + 2 < nblk) block(kb + 2, 2);
     }
 
     if (final_state) {
 #pragma unroll
-        for (int n = 0; n < 8; ++n)
-            *reinterpret_cast<float4 *>(final_state + (bh * P + p0 + 16 * pt + r) * N + 16 * n +
-                                        4 * q) = make_float4(st[n][0], st[n][1], st[n][2], st[n][3]);
+        for (int m = 0; m < 8; ++m) {
+            const f32x4 hv = st[m] * sig_out;
+            *reinterpret_cast<float4 *>(final_state + (bh * P + p0 + 16 * pt + r) * N +
+                                        32 * (m >> 1) + 8 * q + 4 * (m & 1)) =
+                make_float4(hv[0], hv[1], hv[2], hv[3]);
+        }
     }
 }
 
 // Diagonal 32x32 block of C B^T for every 32-token block and group, bf16,
-// stored in the MFMA A-fragment order the fused kernel reads: for row tile
+// stored in the MFMA fragment order the fused kernel reads: for row tile
 // lt and lane (r, q), the 8 values C B^T[16 lt + r][8 q .. 8 q + 7] are the
-// 16 bytes at ((lt * 64) + q * 16 + r) * 16.  The tile above the diagonal
-// (rows 0-15, columns 16-31) is written as zeros.
+// 16 bytes at ((lt * 64) + q * 16 + r) * 16.  Entries with column > row
+// (the whole tile at rows 0-15, columns 16-31 included) are zero, so the
+// block is already causally masked.
 // grid (nblk * G, b), 256 threads; wave w < 3 computes tile (0,0), (1,0) or
 // (1,1) and scatters it, wave 3 writes the zero tile.
 __global__ void __launch_bounds__(256)
@@ -406,11 +545,13 @@ k2b_block_cb(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__r
             acc = Mma<bf16>::mma(a, bb, acc);
         }
     }
-    // D layout: lane (r, q) holds rows 16 lt + 4 q + e, column 16 ct + r
+    // D layout: lane (r, q) holds rows 16 lt + 4 q + e, column 16 ct + r;
+    // entries above the diagonal (s > l) are written as exact zeros
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
         const int rr = 4 * q + e, s = 16 * ct + r;
-        out[(lt * 64 + (s >> 3) * 16 + rr) * 8 + (s & 7)] = (bf16)acc[e];
+        out[(lt * 64 + (s >> 3) * 16 + rr) * 8 + (s & 7)] =
+            s <= 16 * lt + rr ? (bf16)acc[e] : (bf16)0.f;
     }
 }
 
