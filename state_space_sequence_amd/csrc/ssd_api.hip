@@ -57,7 +57,7 @@ ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
 ssd_status choose_path(int seqlen, int nheads, int headdim, int dstate, int chunk_len,
                        ssd_dtype io, ssd::Path *out) {
     // the fused kernel addresses one batch's y rows with 32-bit byte offsets
-    const bool fits = (size_t)seqlen * nheads * headdim * 2 < ((size_t)1 << 31);
+    const bool fits = ((size_t)seqlen + 32) * nheads * headdim * 2 < ((size_t)1 << 31);
     const bool fused_ok = fits && (io == SSD_BF16
                               ? ssd::fused_supported<ssd::bf16>(headdim, dstate, chunk_len)
                               : ssd::fused_supported<float>(headdim, dstate, chunk_len));

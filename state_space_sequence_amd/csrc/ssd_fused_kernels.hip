@@ -128,27 +128,39 @@ struct Fused {
     static constexpr int NDMA = MAT / 1024;            // wave-wide 16-byte DMAs per matrix
     static constexpr int DPW = NDMA / NW;              // of which per wave
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
-    static constexpr int XSB = 2 * PB + 32;            // staged x row pitch: transposed reads
-    // one stage: C rows, B rows, C B^T fragments, staged x of one block
+    static constexpr int XRB = 2 * PB;                 // raw x row bytes (swizzled chunks)
+    // one stage (three in flight), filled by DMA: C rows, B rows, C B^T
+    // fragments and raw x of block j, and the raw decay vectors (lam_hi,
+    // lam_lo, dt: 384 bytes of a 1 KB wave-wide DMA) of block j + 2
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
-    static constexpr int XS = CBF + 2048;
-    static constexpr int STG = XS + kBlk * XSB;
-    // per-block vectors (floats), three blocks in flight
+    static constexpr int XR = CBF + 2048;
+    static constexpr int RV = XR + kBlk * XRB;
+    static constexpr int STG = RV + 1024;
+    // derived per-block vectors (floats), three blocks in flight
     enum { LHI = 0, LLO = 32, DT = 64, CF = 96, RP = 128, EX = 160, DELTA = 192, FLAG = 193,
            VFLOATS = 196 };
     static constexpr int LDS = 3 * STG + 3 * VFLOATS * 4;
-    // global memory instructions every wave issues in every block, in this
-    // order: C / B DMAs, one C B^T DMA, x, raw x of the skip term (2),
-    // decay vectors (3), y stores (2)
-    static constexpr int VM_BLOCK = 2 * DPW + 1 + 1 + 2 + 3 + 2;
+    // DMAs every wave issues at the start of every block, all with every lane
+    // active: C / B, one C B^T, one x, one decay-vector DMA.  (The block's two
+    // y stores follow its end-of-block wait.)
+    static constexpr int VM_LOADS = 2 * DPW + 1 + 1 + 1;
     static_assert(NDMA % NW == 0, "DMAs split evenly over the waves");
-    static_assert(STG % 16 == 0 && XSB % 16 == 0, "alignment");
+    static_assert(XC * kBlk == NT, "one x chunk per thread: one x DMA per wave");
+    static_assert(STG % 16 == 0, "alignment");
     static_assert(2 * LDS <= 160 * 1024, "two workgroups per compute unit");
-    static_assert(XC * kBlk == NT, "one x chunk per thread");
-    static_assert(VM_BLOCK < 64, "vmcnt immediate");
+    static_assert(VM_LOADS < 64, "vmcnt immediate");
 };
+
+// Chunk swizzle of the raw x rows (16-byte chunks, XOR on the chunk index):
+// the transposed reads (4 rows x 32 bytes per 16 lanes) land in 4 distinct
+// 32-byte bank windows, and the 8-byte reads of the skip term (16 rows, one
+// column) at most two lanes per bank.
+template <int PB>
+__device__ __forceinline__ int x_swz(int row) {
+    return PB == 64 ? 2 * (row & 3) + ((row >> 2) & 1) : 2 * ((row >> 1) & 1) + ((row >> 2) & 1);
+}
 
 // Workgroup barrier for LDS only: this wave's LDS reads and writes complete
 // (lgkmcnt(0)), then s_barrier; the asm "memory" clobber keeps the compiler
@@ -179,9 +191,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
-    // Three stages and the vectors as separate LDS objects: the compiler can
-    // then see that the DMA filling one stage never aliases the reads of
-    // another, and does not wait for the DMA before those reads.
+    // Every LDS region that a DMA fills is its own object: the compiler can
+    // then see that a DMA in flight never aliases the reads of another
+    // region, and does not wait for it before those reads.
     __shared__ __align__(16) unsigned char stg0[S::STG];
     __shared__ __align__(16) unsigned char stg1[S::STG];
     __shared__ __align__(16) unsigned char stg2[S::STG];
@@ -198,7 +210,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     const float Dh = D ? D[h] : 0.f;
     const int GN = G * N, HP = H * P;
 
-    // ---- per-lane LDS byte offsets (relative to a stage)
+    // ---- per-lane LDS byte offsets
     // C fragment of token row 16 lt + r, chunk 4 ks + q:
     //   CS + c_rd[ks & 1] + 128 (ks >> 1) + 4096 lt
     int c_rd[2];
@@ -219,22 +231,33 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                 b_tr[s][mb] = (8 * q + e + 4 * s) * S::ROWB + 64 * (mb ^ w2) +
                               16 * (a ^ (w0 | (s << 1)));
     }
-    // staged-x fragment (tokens 8q .. 8q+7, column r of the wave's tile): two
-    // transposed reads at xs_tr and xs_tr + 4 XSB
-    const int xs_tr = (8 * q + (r >> 2)) * S::XSB + 32 * pt + 8 * (r & 3);
     const int cbf_rd = lane * 16;
-    // x staging: one 16-byte chunk per thread
-    const int xs_row = tid / S::XC, xs_chunk = tid % S::XC;
-    const int xs_st = xs_row * S::XSB + 16 * xs_chunk;
-    const int x_off = xs_row * HP + 8 * xs_chunk;  // elements from the block's first row
+    // raw x: chunk c of row t sits at XR + xr_off(t, c)
+    auto xr_off = [](int t, int c) { return t * S::XRB + 16 * (c ^ x_swz<PB>(t)); };
+    // x^T fragment (tokens 8q .. 8q+7, column r of the wave's tile): transposed
+    // reads at XR + xr_tr[0] (tokens 8q .. 8q+3) and XR + xr_tr[1] (8q+4 ..)
+    int xr_tr[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+        xr_tr[s] = xr_off(8 * q + (r >> 2) + 4 * s, 2 * pt + ((r & 3) >> 1)) + 8 * (r & 1);
+    // raw x of the skip term: token 16 lt + r, columns 16 pt + 4 q .. +3
+    //   XR + xr_skip + 16 XRB lt
+    const int xr_skip = xr_off(r, 2 * pt + (q >> 1)) + 8 * (q & 1);
+    // x DMA of this wave: LDS bytes 1024 wave + 16 lane of XR, i.e. row
+    // xd_row, slot xd_slot, holding global chunk xd_slot ^ x_swz(xd_row)
+    const int xd_row = (64 * wave + lane) / S::XC;
+    const int xd_chunk = ((64 * wave + lane) % S::XC) ^ x_swz<PB>(xd_row);
+    const int xd_off = xd_row * HP + 8 * xd_chunk;  // elements from the block's first row
     // C / B DMA i of this wave covers LDS bytes 1024 (wave + NW i) + 16 lane:
     // row dma_row + 4 NW i, slot lane & 15, holding global chunk dma_chunk
     const int dma_row = 4 * wave + (lane >> 4);
     const int dma_chunk = (lane & 15) ^ cb_swz(dma_row);
     const int dma_off = dma_row * GN * 2 + 16 * dma_chunk;  // bytes
-    // y and the raw x of the skip term: token 16 lt + r, columns
-    // p0 + 16 pt + 4 q .. +3; element offset from the block's first row
-    const int y_off = r * HP + 16 * pt + 4 * q;
+    // decay-vector DMA, 16 bytes per lane: lanes 0-23 copy lam_hi, lam_lo, dt
+    // of the block, lanes 24-63 repeat lanes 0-15 (bytes 384-1023 of the
+    // region are never read)
+    const int vd_arr = (lane < 24 ? lane : (lane & 15)) >> 3, vd_elt = 4 * (lane & 7);
+    const size_t vstride = (size_t)(lam_lo - lam_hi);
 
     // ---- register-resident scaled state
     f32x4 st[8];
@@ -250,17 +273,44 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 
     auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
     auto V = [&](int kb) -> float * { return svec + (kb % 3) * S::VFLOATS; };
-    // decay vectors of block kb; every lane loads (lanes 32-63 repeat 0-31)
-    auto vec_load = [&](int kb, f32x4 &vv) {
-        const size_t o = (bh * nblk + kb) * kBlk + (lane & (kBlk - 1));
-        vv = f32x4{lam_hi[o], lam_lo[o], dtb[o], 0.f};
+    // C, B rows, the C B^T fragments and raw x of block kb into stage `buf`:
+    // DPW DMAs per matrix, one C B^T DMA (waves 2w' and 2w'+1 both copy half
+    // w' of the 2 KB when NW = 4), one x DMA.  Rows past the end of the
+    // sequence repeat its last row.
+    auto dma_block = [&](int kb, unsigned char *buf) {
+        const int t0 = kb * kBlk;
+        const unsigned char *crow =
+            reinterpret_cast<const unsigned char *>(Cm + ((size_t)b * L + t0) * GN + (size_t)g * N);
+        const unsigned char *brow =
+            reinterpret_cast<const unsigned char *>(Bm + ((size_t)b * L + t0) * GN + (size_t)g * N);
+        const bf16 *xrow = x + ((size_t)b * L + t0) * HP + (size_t)h * P + p0;
+        const int half = NW == 4 ? wave >> 1 : wave;
+        const bf16 *cbsrc =
+            cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk) + 8 * (64 * half + lane);
+        // last row of the block inside the sequence (31 except in a partial
+        // last block).  One straight-line path: the compiler counts these
+        // DMAs exactly only when no branch splits them.
+        const int lim = min(L - 1 - t0, kBlk - 1);
+#pragma unroll
+        for (int i = 0; i < S::DPW; ++i) {
+            const int off = min(dma_row + 4 * NW * i, lim) * GN * 2 + 16 * dma_chunk;
+            dma16(crow + off, buf + S::CS + 1024 * (wave + NW * i));
+            dma16(brow + off, buf + S::BS + 1024 * (wave + NW * i));
+        }
+        dma16(cbsrc, buf + S::CBF + 1024 * half);
+        dma16(xrow + min(xd_row, lim) * HP + 8 * xd_chunk, buf + S::XR + 1024 * wave);
     };
-    // derived per-token vectors of block kb into LDS (lanes 0-31 of one wave)
-    auto vec_store = [&](int kb, const f32x4 &vv) {
-        const float lh = vv[0], ll = vv[1], dv = vv[2];
-        float *v = V(kb);
-        const float eh = __shfl(lh, kBlk - 1, kWave), el = __shfl(ll, kBlk - 1, kWave);
+    // raw decay vectors of block kb (lam_hi, lam_lo, dt) into `dst`
+    // (the three arrays are equal-size consecutive regions: lam_lo = lam_hi +
+    // vstride, dtb = lam_lo + vstride, which the launcher checks)
+    auto vec_dma = [&](int kb, unsigned char *buf) {
+        dma16(lam_hi + vd_arr * vstride + (bh * nblk + kb) * kBlk + vd_elt, buf + S::RV);
+    };
+    // derived per-token vectors of block kb (lanes 0-31: token lane; eh, el =
+    // the block's last prefix)
+    auto vec_derive = [&](int kb, float lh, float ll, float dv, float eh, float el) {
         if (lane < kBlk) {
+            float *v = V(kb);
             const bool fac = -(eh + el) <= kSafeDecay;
             v[S::LHI + lane] = lh;
             v[S::LLO + lane] = ll;
@@ -273,6 +323,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                 v[S::FLAG] = fac ? 1.f : 0.f;
             }
         }
+    };
+    // ... from the raw vectors in a stage
+    auto vec_store = [&](int kb, const unsigned char *buf) {
+        const float *raw = reinterpret_cast<const float *>(buf + S::RV);
+        const int t = lane & (kBlk - 1);
+        vec_derive(kb, raw[t], raw[kBlk + t], raw[2 * kBlk + t], raw[kBlk - 1], raw[2 * kBlk - 1]);
     };
     auto book = [&](int kb, float sig_in) -> Book {
         const float *v = V(kb);
@@ -292,71 +348,11 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         }
         return bk;
     };
-    // C, B rows and the C B^T fragments of block kb into stage `buf`: DPW
-    // DMAs per matrix and one C B^T DMA (waves 2w' and 2w'+1 both copy half
-    // w' of the 2 KB when NW = 4)
-    auto dma_block = [&](int kb, unsigned char *buf) {
-        const int t0 = kb * kBlk;
-        const unsigned char *crow =
-            reinterpret_cast<const unsigned char *>(Cm + ((size_t)b * L + t0) * GN + (size_t)g * N);
-        const unsigned char *brow =
-            reinterpret_cast<const unsigned char *>(Bm + ((size_t)b * L + t0) * GN + (size_t)g * N);
-        if (t0 + kBlk <= L) {
-#pragma unroll
-            for (int i = 0; i < S::DPW; ++i) {
-                const int off = dma_off + i * (4 * NW * GN * 2);
-                dma16(crow + off, buf + S::CS + 1024 * (wave + NW * i));
-                dma16(brow + off, buf + S::BS + 1024 * (wave + NW * i));
-            }
-        } else {
-            // last, partial block: rows past the end repeat the last row
-            const int lim = L - 1 - t0;
-#pragma unroll
-            for (int i = 0; i < S::DPW; ++i) {
-                const int off = min(dma_row + 4 * NW * i, lim) * GN * 2 + 16 * dma_chunk;
-                dma16(crow + off, buf + S::CS + 1024 * (wave + NW * i));
-                dma16(brow + off, buf + S::BS + 1024 * (wave + NW * i));
-            }
-        }
-        const int half = NW == 4 ? wave >> 1 : wave;
-        dma16(cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk) + 8 * (64 * half + lane),
-              buf + S::CBF + 1024 * half);
-    };
-    // x of block kb: one 16-byte chunk per thread, and the raw x of the skip
-    // term (two 8-byte pieces per lane); rows past the end repeat the last row
-    auto x_load = [&](int kb, bf16x8 &xv, uint2 (&sk)[2]) {
-        const int t0 = kb * kBlk;
-        const bf16 *xb = x + ((size_t)b * L + t0) * HP + (size_t)h * P + p0;
-        if (t0 + kBlk <= L) {
-            xv = load_frag(xb + x_off);
-#pragma unroll
-            for (int lt = 0; lt < 2; ++lt)
-                sk[lt] = *reinterpret_cast<const uint2 *>(xb + y_off + lt * 16 * HP);
-        } else {
-            const int lim = L - 1 - t0;
-            xv = load_frag(xb + (size_t)min(xs_row, lim) * HP + 8 * xs_chunk);
-#pragma unroll
-            for (int lt = 0; lt < 2; ++lt)
-                sk[lt] = *reinterpret_cast<const uint2 *>(
-                    xb + (size_t)min(16 * lt + r, lim) * HP + 16 * pt + 4 * q);
-        }
-    };
-    // staged x of block kb (bookkeeping bkx): x'_s = x_s cf_s / sigma on
-    // factored blocks, raw x on exact blocks
-    auto x_store = [&](int kb, unsigned char *buf, bf16x8 xv, const Book &bkx) {
-        bf16x8 xsv = xv;
-        if (bkx.fac) {
-            const float cf = V(kb)[S::CF + xs_row] * __builtin_amdgcn_rcpf(bkx.sig);
-#pragma unroll
-            for (int j = 0; j < 8; ++j) xsv[j] = (bf16)((float)xv[j] * cf);
-        }
-        *reinterpret_cast<bf16x8 *>(buf + S::XS + xs_st) = xsv;
-    };
     // y through a buffer resource over this batch's rows: the stores of
     // tokens past the end fall outside it and are dropped by the hardware
     const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
-    const int y_boff = (y_off + h * P + p0) * 2;
+    const int y_boff = (r * HP + h * P + p0 + 16 * pt + 4 * q) * 2;
     auto y_store = [&](int kb, const f32x4 (&acc)[2]) {
 #pragma unroll
         for (int lt = 0; lt < 2; ++lt) {
@@ -366,31 +362,29 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         }
     };
 
-    // ---- prologue.  Every global load runs ahead of its use: C / B rows and
-    // C B^T two blocks (three LDS stages), x and the skip-term x two blocks
-    // (registers xq / sk, set kb % 3), the decay vectors three blocks
-    // (registers vq, set kb % 3; block kb's are stored to LDS by wave
-    // kb % NW at the end of block kb - 2).  Past the last block the loads
-    // repeat it, so every block issues the same global memory instructions.
+    // ---- prologue.  Every global read in the loop is a DMA into LDS issued
+    // two blocks ahead of its use (three stages): C / B rows, C B^T and raw x
+    // of block j, and the raw decay vectors of block j + 2, which wave
+    // (j + 2) % NW turns into the derived vectors at the start of block j.
+    // Past the last block the DMAs repeat it, so every block issues the same
+    // global memory instructions.
     Book bk;
-    bf16x8 xq[3];
-    uint2 sk[3][2];
-    f32x4 vq[3];
     {
         const int last = nblk - 1;
-#pragma unroll
-        for (int j = 0; j < 3; ++j) vec_load(min(j, last), vq[j]);
         dma_block(0, stg0);
-        x_load(0, xq[0], sk[0]);
+        vec_dma(min(2, last), stg0);
         dma_block(min(1, last), stg1);
-        x_load(min(1, last), xq[1], sk[1]);
+        vec_dma(min(3, last), stg1);
+        if (wave < 2 && wave <= last) {
+            // the derived vectors of blocks 0 and 1 straight from global memory
+            const size_t o = (bh * nblk + wave) * kBlk;
+            const int t = lane & (kBlk - 1);
+            vec_derive(wave, lam_hi[o + t], lam_lo[o + t], dtb[o + t], lam_hi[o + kBlk - 1],
+                       lam_lo[o + kBlk - 1]);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        if (wave == 0) vec_store(0, vq[0]);
-        if (wave == 1 && nblk > 1) vec_store(1, vq[1]);
         lds_barrier();
         bk = book(0, 1.f);
-        x_store(0, stg0, xq[0], bk);
-        lds_barrier();
     }
     float sig_out = 1.f;
 
@@ -398,19 +392,43 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     auto block = [&](int kb, const int si) {
         unsigned char *cur = stage(si);
         const int last = nblk - 1;
-        const bool more1 = kb + 1 < nblk;
+        const float *v = V(kb);
         // ---- global memory issue: the same instructions in every block, in
         // this order (the wait at the end of the block counts them)
         dma_block(min(kb + 2, last), stage((si + 2) % 3));
-        __builtin_amdgcn_sched_barrier(0);
-        x_load(min(kb + 2, last), xq[(si + 2) % 3], sk[(si + 2) % 3]);
-        vec_load(min(kb + 3, last), vq[si]);
+        vec_dma(min(kb + 4, last), stage((si + 2) % 3));
         __builtin_amdgcn_sched_barrier(0);
 
-        Book bk1 = bk;
-        if (more1) bk1 = book(kb + 1, bk.sig);
+        // ---- every LDS operand of the block requested up front, so the
+        // reads overlap each other and the MFMAs instead of one round trip
+        // per step
+        bf16x8 cfr[4][2];  // C fragments of y^T = h~ C^T
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+            for (int lt = 0; lt < 2; ++lt)
+                cfr[ks][lt] = lds_b128(cur, S::CS + c_rd[ks & 1] + 128 * (ks >> 1) + 4096 * lt);
+        // x^T fragment of the block: raw x, tokens 8q .. 8q+7 of column r
+        bf16x8 xs = join(lds_tr(cur, S::XR + xr_tr[0]), lds_tr(cur, S::XR + xr_tr[1]));
+        const f32x4 cf0 = *reinterpret_cast<const f32x4 *>(v + S::CF + 8 * q);
+        const f32x4 cf1 = *reinterpret_cast<const f32x4 *>(v + S::CF + 8 * q + 4);
+        bf16x8 cbv[2];  // causal diagonal block of C B^T
+        float rpv[2];   // exp(lambda_l - lambda_e) of token 16 lt + r
+        bf16x4 xr[2];   // raw x of the skip term
+#pragma unroll
+        for (int lt = 0; lt < 2; ++lt) {
+            cbv[lt] = lds_b128(cur, S::CBF + 1024 * lt + cbf_rd);
+            rpv[lt] = v[S::RP + 16 * lt + r];
+            xr[lt] = *reinterpret_cast<const bf16x4 *>(cur + S::XR + xr_skip + 16 * S::XRB * lt);
+        }
+        bf16x8 bt[8];   // B^T fragments of the state update
+#pragma unroll
+        for (int m = 0; m < 8; ++m) {
+            const int o = 128 * (m >> 2) + 8 * (m & 1);
+            bt[m] = join(lds_tr(cur, S::BS + b_tr[0][(m >> 1) & 1] + o),
+                         lds_tr(cur, S::BS + b_tr[1][(m >> 1) & 1] + o));
+        }
 
-        const float *v = V(kb);
         if (bk.rescale) {
 #pragma unroll
             for (int m = 0; m < 8; ++m) st[m] *= bk.sig_in;
@@ -427,35 +445,35 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                 hb[4 + e] = (bf16)st[2 * ks + 1][e];
             }
 #pragma unroll
-            for (int lt = 0; lt < 2; ++lt) {
-                const bf16x8 cfr = lds_b128(cur, S::CS + c_rd[ks & 1] + 128 * (ks >> 1) + 4096 * lt);
-                acc[lt] = Mma<bf16>::mma(hb, cfr, acc[lt]);
-            }
+            for (int lt = 0; lt < 2; ++lt) acc[lt] = Mma<bf16>::mma(hb, cfr[ks][lt], acc[lt]);
         }
-        bf16x8 xs = join(lds_tr(cur, S::XS + xs_tr), lds_tr(cur, S::XS + xs_tr + 4 * S::XSB));
         if (bk.fac) {
-            // staged x is x' = exp(lambda_e - lambda_s) dt_s x_s / sigma
+            // x' = exp(lambda_e - lambda_s) dt_s x_s / sigma
+            const float inv = __builtin_amdgcn_rcpf(bk.sig);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                xs[j] = (bf16)((float)xs[j] * (cf0[j] * inv));
+                xs[4 + j] = (bf16)((float)xs[4 + j] * (cf1[j] * inv));
+            }
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt) {
-                acc[lt] = Mma<bf16>::mma(xs, lds_b128(cur, S::CBF + 1024 * lt + cbf_rd), acc[lt]);
-                const float f = v[S::RP + 16 * lt + r] * bk.sig;
-                const bf16x4 xr = __builtin_bit_cast(bf16x4, sk[si][lt]);
+                acc[lt] = Mma<bf16>::mma(xs, cbv[lt], acc[lt]);
+                const float f = rpv[lt] * bk.sig;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) acc[lt][e] = acc[lt][e] * f + Dh * (float)xr[e];
+                for (int e = 0; e < 4; ++e) acc[lt][e] = acc[lt][e] * f + Dh * (float)xr[lt][e];
             }
         } else {
-            // staged x is raw x: exact weights exp(lambda_l - lambda_s) dt_s, D on the diagonal
+            // exact weights exp(lambda_l - lambda_s) dt_s on raw x, D on the diagonal
 #pragma unroll
             for (int lt = 0; lt < 2; ++lt) {
                 const int row = 16 * lt + r;
                 acc[lt] *= v[S::EX + row] * bk.sig_in;
-                const bf16x8 cbv = lds_b128(cur, S::CBF + 1024 * lt + cbf_rd);
                 const float lh = v[S::LHI + row], ll = v[S::LLO + row];
                 bf16x8 wgt;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = 8 * q + j;
-                    const float w = (float)cbv[j] *
+                    const float w = (float)cbv[lt][j] *
                                     fast_exp(fminf(prefix_diff(lh, ll, v[S::LHI + s], v[S::LLO + s]), 0.f)) *
                                     v[S::DT + s] + (s == row ? Dh : 0.f);
                     wgt[j] = (bf16)(s <= row ? w : 0.f);
@@ -464,11 +482,11 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             }
             // the state update takes x' = exp(lambda_e - lambda_s) dt_s x_s
 #pragma unroll
-            for (int j = 0; j < 8; ++j) xs[j] = (bf16)((float)xs[j] * v[S::CF + 8 * q + j]);
+            for (int j = 0; j < 4; ++j) {
+                xs[j] = (bf16)((float)xs[j] * cf0[j]);
+                xs[4 + j] = (bf16)((float)xs[4 + j] * cf1[j]);
+            }
         }
-        __builtin_amdgcn_sched_barrier(0);
-        y_store(kb, acc);
-        __builtin_amdgcn_sched_barrier(0);
 
         // -------- state: h~ += B^T x'  (exact blocks: h~ <- sig_in delta h~ + B^T x')
         if (!bk.fac) {
@@ -477,30 +495,38 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             for (int m = 0; m < 8; ++m) st[m] *= sd;
         }
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int o = 128 * (m >> 2) + 8 * (m & 1);
-            const bf16x8 a = join(lds_tr(cur, S::BS + b_tr[0][(m >> 1) & 1] + o),
-                                  lds_tr(cur, S::BS + b_tr[1][(m >> 1) & 1] + o));
-            st[m] = Mma<bf16>::mma(a, xs, st[m]);
-        }
+        for (int m = 0; m < 8; ++m) st[m] = Mma<bf16>::mma(bt[m], xs, st[m]);
         sig_out = bk.sig;
+        __builtin_amdgcn_sched_barrier(0);
 
-        // -------- stage x of the next block, decay vectors two ahead
-        if (more1) x_store(kb + 1, stage((si + 1) % 3), xq[(si + 1) % 3], bk1);
-        if (kb + 2 < nblk && wave == (kb + 2) % NW) vec_store(kb + 2, vq[(si + 2) % 3]);
-        // The next block reads the stage whose DMA was issued in the previous
-        // block: all VM_BLOCK global memory instructions of this block may
-        // stay in flight, everything older has completed.
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_BLOCK));
+        // -------- while the MFMAs run: the derived decay vectors of block
+        // kb + 2 (one wave; visible after this block's barrier) and the
+        // bookkeeping of block kb + 1
+        if (kb + 2 < nblk && wave == (kb + 2) % NW) vec_store(kb + 2, cur);
+        Book bk1 = bk;
+        if (kb + 1 < nblk) bk1 = book(kb + 1, bk.sig);
+
+        // -------- the DMAs of the previous block have landed once at most
+        // this block's VM_LOADS DMAs are in flight (loads complete in issue
+        // order; a pending store only lengthens the wait); then this block's
+        // y stores
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS));
+        __builtin_amdgcn_sched_barrier(0);
+        y_store(kb, acc);
+        __builtin_amdgcn_sched_barrier(0);
         lds_barrier();
         bk = bk1;
     };
 
     for (int kb = 0; kb < nblk; kb += 3) {
         block(kb, 0);
-        if (kb + 1 < nblk) block(kb + 1, 1);
-        if (kb + 2 < nblk) block(kb + 2, 2);
+        if (kb + 1 < nblk) {
+            block(kb + 1, 1);
+            if (kb + 2 < nblk) block(kb + 2, 2);
+        }
     }
+    // no DMA may land in LDS after the workgroup ends
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     if (final_state) {
 #pragma unroll
@@ -574,6 +600,9 @@ template <int PB>
 static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
     const int nblk = fused_nblk(a.L);
+    // the kernel reaches acum_lo and dtT at fixed strides from acum_hi
+    if (a.acum_lo - a.acum_hi != a.dtT - a.acum_lo || a.acum_lo <= a.acum_hi)
+        return hipErrorInvalidValue;
     hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * (a.P / PB), a.batch), dim3(S::NT), 0,
                        stream, (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
                        (const bf16 *)a.cb, a.acum_hi, a.acum_lo, a.dtT, a.D, a.init,
