@@ -118,11 +118,12 @@ def kernel_alg_bytes(name, w, es):
         # C and B rows in, one 32 x 32 bf16 diagonal block per block and group out
         nb = -(-L // 32)
         return 2 * b * L * G * N * es + b * nb * G * 32 * 32 * 2
+    if name == "k1_block_vectors":
+        # dt in; one 132-float decay record per (batch, head, 32-token block) out
+        return b * L * H * 4 + b * H * (-(-L // 32)) * 132 * 4
     if name == "k1_dA_cumsum":
-        # dt in; prefix hi, lo and dt per block out (the padded block length)
-        q1 = 32 if os.environ.get("SSD_FORWARD_PATH", "") != "split" and N == 128 \
-            and P % 32 == 0 else Q
-        return b * L * H * 4 + 3 * b * H * (-(-L // q1)) * q1 * 4
+        # dt in; prefix hi, lo and dt per chunk out (the padded chunk length)
+        return b * L * H * 4 + 3 * b * H * (-(-L // Q)) * Q * 4
     nc = -(-L // Q)
     per_chunk_vec = b * H * nc * Q * 4          # acum or dtT
     states = b * nc * H * P * N * 4

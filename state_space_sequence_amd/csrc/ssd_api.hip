@@ -74,30 +74,36 @@ ssd_status choose_path(int seqlen, int nheads, int headdim, int dstate, int chun
 }
 
 struct Layout {
-    size_t acum_hi, acum_lo, dtT, cb, S, bt, total;
+    size_t acum_hi, acum_lo, dtT, vrec, cb, S, total;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                       int ngroups, int chunk_len, ssd_dtype io, ssd::Path path) {
-    // the fused path works in fixed blocks of kFusedBlock tokens
-    const size_t Q = path == ssd::Path::Split ? (size_t)chunk_len : (size_t)ssd::kFusedBlock;
-    const size_t nc = ((size_t)seqlen + Q - 1) / Q;
     const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups;
     const size_t es = io == SSD_BF16 ? 2 : 4;
-    const size_t vec = round_up(b * H * nc * Q * sizeof(float));
     Layout l;
-    l.acum_hi = 0;
-    l.acum_lo = l.acum_hi + vec;
-    l.dtT = l.acum_lo + vec;
-    l.cb = l.dtT + vec;
     if (path == ssd::Path::Split) {
+        const size_t Q = chunk_len;
+        const size_t nc = ((size_t)seqlen + Q - 1) / Q;
+        const size_t vec = round_up(b * H * nc * Q * sizeof(float));
+        l.acum_hi = 0;
+        l.acum_lo = l.acum_hi + vec;
+        l.dtT = l.acum_lo + vec;
+        l.vrec = 0;
+        l.cb = l.dtT + vec;
         l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
-        l.bt = 0;
         l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
     } else {
+        // the fused path works in fixed blocks of kFusedBlock tokens; its
+        // kernel copies 1 KB from the start of each decay record, so 1 KB of
+        // slack follows the last one
+        const size_t Q = ssd::kFusedBlock;
+        const size_t nb = ((size_t)seqlen + Q - 1) / Q;
+        l.acum_hi = l.acum_lo = l.dtT = 0;
+        l.vrec = 0;
+        l.cb = round_up(b * H * nb * ssd::kVecRec * sizeof(float) + 1024);
         l.S = 0;
-        l.bt = 0;
-        l.total = l.cb + round_up(b * nc * G * Q * Q * es);
+        l.total = l.cb + round_up(b * nb * G * Q * Q * es);
     }
     return l;
 }
@@ -145,12 +151,13 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.Q = chunk_len;
     a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
     char *ws = static_cast<char *>(workspace);
-    a.acum_hi = reinterpret_cast<float *>(ws + lay.acum_hi);
-    a.acum_lo = reinterpret_cast<float *>(ws + lay.acum_lo);
-    a.dtT = reinterpret_cast<float *>(ws + lay.dtT);
+    const bool split = path == ssd::Path::Split;
+    a.acum_hi = split ? reinterpret_cast<float *>(ws + lay.acum_hi) : nullptr;
+    a.acum_lo = split ? reinterpret_cast<float *>(ws + lay.acum_lo) : nullptr;
+    a.dtT = split ? reinterpret_cast<float *>(ws + lay.dtT) : nullptr;
+    a.vrec = split ? nullptr : reinterpret_cast<float *>(ws + lay.vrec);
     a.cb = ws + lay.cb;
-    a.S = path == ssd::Path::Split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
-    a.bt = nullptr;
+    a.S = split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
 
     const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::kFusedKernels;
     const char *const *kn =

@@ -32,9 +32,17 @@ struct ForwardArgs {
                      // fused path: diagonal 32x32 blocks, bf16 [b][nblk][G][32 * 32]
                      // in MFMA fragment order
     float *S;        // split path: chunk states [b][nc][H][P][N]
-    void *bt;        // unused
-    // (fused path: acum_hi/acum_lo/dtT hold 32-token blocks, [b][H][nblk][32])
+    float *vrec;     // fused path: per-block decay records [b][H][nblk][kVecRec]
+                     // (acum_hi / acum_lo / dtT unused there)
 };
+
+// Fused path: one record of floats per (batch, head, 32-token block) with the
+// per-token decay factors the block needs: [0, 32) cf_s = exp(lambda_e -
+// lambda_s) dt_s, [32, 64) rp_l = exp(lambda_l - lambda_e) (0 when the block
+// is not factored), [64, 96) lambda_l - lambda_e, [96, 128) dt_l, then
+// delta = exp(lambda_e), the factored flag (1 or 0) and lambda_e.  528 bytes,
+// a multiple of 16.
+constexpr int kVecRec = 132;
 
 // Forward paths.  The split path runs the five kernels of the chunked
 // algorithm one after the other with the caller's chunk length and accepts

@@ -126,6 +126,36 @@ def test_small_problems_every_element(dev, oracle_mod, path, case):
         _say("  componentwise y %.2e (informational)" % metrics.componentwise_err(y, yr, ya))
 
 
+def decay_regime_inputs(io, seed):
+    """Per-head decay profiles that cross every regime of the fused path in
+    one sequence: weak decay, repeated rescaling of the tracked state scale
+    (block decays of 20-40), blocks whose total decay exceeds exp(-60) (the
+    exact per-element weights, dt A summed over 32 tokens down to -300), and
+    factored blocks again after them; ragged length, initial state."""
+    L = 400
+    inp = make_inputs(2, L, 4, 64, 128, 1, io_dtype=io, init_std=0.1, seed=seed)
+    t = np.arange(L)
+    prof = np.where(t < 96, 0.01, np.where(t < 192, 0.25, np.where(t < 288, 0.08, 0.6)))
+    rng = np.random.default_rng(seed)
+    jitter = 1.0 + 0.2 * rng.standard_normal(size=(2, L, 4))
+    inp["A"] = np.array([-16.0, -8.0, -2.0, -0.5], dtype=np.float32)
+    inp["dt"] = (prof[None, :, None] * np.abs(jitter)).astype(np.float32)
+    return inp
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decay_regimes(dev, oracle_mod, path, io):
+    inp = decay_regime_inputs(io, seed=91)
+    lam = inp["dt"][0, : 384].reshape(12, 32, 4).sum(1) * inp["A"][None, :]
+    _say("block decays per head: min %.1f max %.1f" % (-lam.max(), -lam.min()))
+    assert (-lam > 60).any() and ((-lam > 20) & (-lam < 60)).any() and (-lam < 5).any()
+    skip_if_path_unsupported(inp, io, 64)
+    y, fin = gpu_forward(inp, io, 64, dev)
+    yr, finr, ya, fa = reference(oracle_mod, inp)
+    check(y, yr, io, "y", ya)
+    check(fin, finr, io, "final_state", fa)
+
+
 def test_tiny_workload(dev, oracle_mod):
     w = WORKLOADS["tiny_f32"]
     inp = workload_inputs(w)
@@ -224,8 +254,11 @@ def test_timed_variant_matches_and_names_kernels(dev, path):
                                                     chunk_len=128)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2) and torch.equal(f1, f2)
-    assert names[0] == "k1_dA_cumsum"
-    assert len(names) == (5 if path == "split" else 3)
+    if path == "split":
+        assert names == ["k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing",
+                         "k5_chunk_scan"]
+    else:
+        assert names == ["k1_block_vectors", "k2b_block_cb", "k_fused_ssd"]
     for e in evs:
         hip.hipEventDestroy(__import__("ctypes").c_void_p(e))
 
