@@ -290,6 +290,20 @@ def cpu_baseline(w, inp, target_s=12.0):
                       "slice fraction" % (k, nsl, w.seqlen, t_run)}
 
 
+COPY_CAL_BYTES = 256 << 20
+
+
+def kernel_source_hash():
+    """sha256 of the kernel sources the fused path is built from; a stored
+    traffic measurement is reported only while it matches."""
+    import hashlib
+    hsh = hashlib.sha256()
+    for name in ("ssd_fused_kernels.hip", "ssd_device.hpp", "ssd_kernels.hpp"):
+        with open(os.path.join(ROOT, "state_space_sequence_amd", "csrc", name), "rb") as f:
+            hsh.update(f.read())
+    return hsh.hexdigest()
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -302,6 +316,9 @@ def main():
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch of the dominant kernel "
                          "(from rocprofv3 FETCH_SIZE/WRITE_SIZE runs), if present")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run one device-to-device copy of 256 MiB, the known-size "
+                         "kernel the FETCH_SIZE / WRITE_SIZE counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -320,6 +337,12 @@ def main():
 
     w = WORKLOADS[args.workload]
     es = 2 if w.io_dtype == "bf16" else 4
+    if args.copy_calibration:
+        src = torch.empty(COPY_CAL_BYTES, dtype=torch.uint8, device=dev).fill_(1)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     r = time_forward(w, dev, args.steps, args.warmup, ev)
     ms_step = r["gpu_ms"] / args.steps
     tokens = w.batch * w.seqlen
@@ -335,7 +358,9 @@ def main():
     if os.path.exists(args.traffic_json):
         try:
             tj = json.load(open(args.traffic_json))
-            if tj.get("kernel") == dom and tj.get("workload") == w.name:
+            # counters taken on this kernel, this workload, this source only
+            if (tj.get("kernel") == dom and tj.get("workload") == w.name
+                    and tj.get("source_sha256") == kernel_source_hash()):
                 traffic = tj.get("bytes_per_launch")
         except (OSError, ValueError):
             traffic = None
