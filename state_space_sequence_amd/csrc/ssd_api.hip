@@ -54,10 +54,14 @@ ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
 // kernels otherwise.  SSD_FORWARD_PATH=split|fused overrides the choice (a
 // diagnostic switch for comparing the two); forcing "fused" on a shape it
 // does not cover is reported as unsupported.
-ssd_status choose_path(int seqlen, int nheads, int headdim, int dstate, int chunk_len,
-                       ssd_dtype io, ssd::Path *out) {
-    // the fused kernel addresses one batch's y rows with 32-bit byte offsets
-    const bool fits = ((size_t)seqlen + 32) * nheads * headdim * 2 < ((size_t)1 << 31);
+ssd_status choose_path(int seqlen, int nheads, int ngroups, int headdim, int dstate,
+                       int chunk_len, ssd_dtype io, ssd::Path *out) {
+    // the fused kernel addresses one batch's rows of x, y, B and C with 32-bit
+    // byte offsets, including the prefetches up to three blocks past the end
+    const size_t row = (size_t)nheads * headdim > (size_t)ngroups * dstate
+                           ? (size_t)nheads * headdim
+                           : (size_t)ngroups * dstate;
+    const bool fits = ((size_t)seqlen + 128) * row * 2 < ((size_t)1 << 31);
     const bool fused_ok = fits && (io == SSD_BF16
                               ? ssd::fused_supported<ssd::bf16>(headdim, dstate, chunk_len)
                               : ssd::fused_supported<float>(headdim, dstate, chunk_len));
@@ -126,7 +130,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
         (final_state && !aligned(final_state, 16)))
         return SSD_ERR_INVALID_ARGUMENT;
     ssd::Path path;
-    if ((st = choose_path(seqlen, nheads, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
+    if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
     const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
                                       chunk_len, io_dtype, path);
     if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
@@ -208,7 +212,7 @@ ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
     ssd::Path path;
-    if ((st = choose_path(seqlen, nheads, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
+    if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
     *bytes = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len,
                             io_dtype, path)
                  .total;

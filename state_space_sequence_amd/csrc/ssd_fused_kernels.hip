@@ -28,9 +28,9 @@
 //   y_l   = exp(lambda_l - lambda_e) sigma_{k+1} (C_l h~^T + [C B^T]_l x') + D x_l
 //   h~   += B^T x'
 // with sigma_{k+1} = sigma_k exp(lambda_e).  When sigma_{k+1} would fall
-// below exp(-40) the state is rescaled once before the block (h~ *= sigma_k,
-// sigma_k = 1), so 1/sigma stays below exp(60) and every intermediate stays
-// far inside the fp32 range.
+// below exp(-60) the scale restarts in that block (h~ *= sigma_k, sigma_k =
+// 1, so sigma_{k+1} = exp(lambda_e) >= exp(-60) in a factored block): 1/sigma
+// stays below exp(60) and every intermediate far inside the fp32 range.
 //
 // The diagonal block uses the factored weights exp(lambda_l - lambda_e) (up
 // to exp(60)) and exp(lambda_e - lambda_s) (down to exp(-60), so x' keeps
@@ -67,7 +67,7 @@ namespace ssd {
 
 constexpr int kBlk = 32;                  // tokens per block
 constexpr float kSafeDecay = 60.f;        // max -lambda_e for the factored diagonal
-constexpr float kRescale = 4.24835426e-18f;  // exp(-40): smallest sigma kept unrescaled
+constexpr float kRescale = 8.75651076e-27f;  // exp(-60): smallest sigma kept unrescaled
 // s_waitcnt immediate for "vmcnt(0)" alone on gfx9-family targets:
 // vmcnt = 0, expcnt = 7 and lgkmcnt = 15 (both at their no-wait maximum).
 constexpr int kWaitVmcnt0 = 0x0F70;
@@ -80,6 +80,7 @@ constexpr int kBufferWord3 = 0x00020000;
 
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
@@ -116,6 +117,11 @@ __device__ __forceinline__ int row_swz(int row) { return 2 * (row & 3) + ((row >
 // raw x rows of 64 bytes (4 chunks): the same two properties
 __device__ __forceinline__ int row_swz4(int row) { return 2 * ((row >> 1) & 1) + ((row >> 2) & 1); }
 
+// Workgroup layout.  A workgroup covers PB consecutive columns of one
+// batch's flattened (head, headdim) columns h P + p (x and y rows are
+// contiguous over them): NW = PB / 32 waves of 32 columns each.  With
+// PB > P the workgroup spans NH = PB / P heads of one B/C group, which then
+// share the staged C and B rows.
 template <int PB>
 struct Fused {
     static constexpr int NW = PB / 32;                 // waves: 32 headdim columns each
@@ -126,32 +132,36 @@ struct Fused {
     static constexpr int CBD = MAT / 1024 / NW;        // wave-wide DMAs per matrix and wave
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
     static constexpr int XRB = 2 * PB;                 // raw x row bytes
-    static constexpr int XD = kBlk * XRB / 1024 / NW;  // x DMAs per wave
-    static constexpr int CBFD = 2 / NW;                // C B^T DMAs per wave
+    static constexpr int XD = kBlk * XRB / 1024 / NW;  // x DMAs per wave (two)
+    static constexpr int NRS = PB == 128 ? 2 : 1;      // decay-record slots (heads)
+    // the other DMAs of a block, 1 KB each: the two halves of the C B^T
+    // block, then one decay record per head; wave w issues pieces
+    // w, w + NW, ... (past the last piece: a repeat of a record)
+    static constexpr int MISC = (2 + NRS + NW - 1) / NW;
     // one stage (three in flight), filled by DMA: C rows, B rows, C B^T
-    // fragments, raw x and the decay record (kVecRec floats of a 1 KB
-    // wave-wide DMA) of one block
+    // fragments, raw x and the decay records (kVecRec floats in 1 KB slots)
+    // of one block
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
     static constexpr int XR = CBF + 2048;
     static constexpr int VR = XR + kBlk * XRB;
-    static constexpr int STG = VR + 1024;
+    static constexpr int STG = VR + 1024 * NRS;
     // floats of the decay record
     enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
     static constexpr int LDS = 3 * STG;
-    // DMAs every wave issues at the start of every block, all with every lane
-    // active: C and B, C B^T, x, one decay-record DMA.  (The block's four y
-    // stores follow its end-of-block wait.)
-    static constexpr int VM_LOADS = 2 * CBD + CBFD + XD + 1;
-    static_assert(PB == 32 || PB == 64, "one or two waves");
+    // DMAs every wave issues in every block, all with every lane active
+    static constexpr int VM_LOADS = 2 * CBD + XD + MISC;
+    static constexpr int Y_STORES = 2;                 // y stores per wave and block
+    static_assert(PB == 32 || PB == 64 || PB == 128, "one, two or four waves");
+    static_assert(XD == 2, "x DMAs");
     static_assert(STG % 16 == 0, "alignment");
-    static_assert(2 * LDS <= 160 * 1024, "two workgroups per compute unit");
-    static_assert(VM_LOADS < 64, "vmcnt immediate");
+    static_assert(PB == 128 ? LDS <= 160 * 1024 : 2 * LDS <= 160 * 1024, "LDS per compute unit");
+    static_assert(VM_LOADS + Y_STORES < 64, "vmcnt immediate");
 };
 
 template <int PB>
-__device__ __forceinline__ int x_swz(int row) { return PB == 64 ? row_swz(row) : row_swz4(row); }
+__device__ __forceinline__ int x_swz(int row) { return PB >= 64 ? row_swz(row) : row_swz4(row); }
 
 // Workgroup barrier for LDS only: this wave's LDS reads and writes complete
 // (lgkmcnt(0)), then s_barrier; the asm "memory" clobber keeps the compiler
@@ -163,18 +173,22 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_s_waitcnt(kWaitLgkmcnt0);
     asm volatile("s_barrier" ::: "memory");
 }
+// The barrier at the end of a block: every LDS read of the block has been
+// consumed by then (the compiler's waits precede each use), so no LDS wait
+// is needed before it; an lgkmcnt(0) here would also wait for this block's
+// DMAs into LDS still in flight (they count on that counter as well).
+__device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
 
-// Scale bookkeeping of one block (identical in every wave).
+// Scale bookkeeping of one block (identical in every wave of a head).
 struct Book {
     float sig_in;   // sigma entering the block
     float sig;      // sigma after the block
     float delta;    // exp(lambda_e)
     bool fac;       // factored diagonal
-    bool rescale;   // h~ *= sig_in before the block (factored blocks only)
+    bool rescale;   // restart the scale: h~ *= sig_in, sigma_in = 1 (factored blocks only)
 };
 
-// Bookkeeping of a block from its decay record and the sigma entering it
-// (selects only: no branch waits for the record).
+// Bookkeeping of a block from its decay record and the sigma entering it.
 __device__ __forceinline__ Book book_of(const float *rec, float sig_in) {
     Book bk;
     bk.sig_in = sig_in;
@@ -193,16 +207,29 @@ __device__ __forceinline__ f32x16 mma32(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-// Per wave: headdim columns p = p0 + 32 wave + (0..31).  With lane l,
-// r = l % 32, hi = l / 32:
-//   state     st[m][v] = h~[n][p0 + 32 wave + r],  i = v / 4, c = v % 4,
+// Column of MFMA row / column q (0..31) within a wave's 32 headdim columns.
+// Output row q = 8 i + 4 hi + c of y^T lands in result register 4 i + c of
+// the lanes with l / 32 = hi; with this order those registers hold, in
+// order, 16 columns that form two runs of 8: 8 hi + (0..7) and
+// 16 + 8 hi + (0..7).  A lane then stores 16 contiguous bytes per run, and
+// one store instruction covers 32 contiguous bytes of each token.
+__device__ __forceinline__ int col_of(int q) {
+    return 8 * ((q >> 2) & 1) + 4 * ((q >> 3) & 1) + 16 * (q >> 4) + (q & 3);
+}
+
+// Per wave: flattened columns c0 + 32 wave + (0..31) of head hw, headdim
+// columns pw + (0..31).  With lane l, r = l % 32, hi = l / 32, and
+// pr = pw + col_of(r):
+//   state     st[m][v] = h~[n][pr],  i = v / 4, c = v % 4,
 //             n = 32 m + 16 (i / 2) + 8 hi + 4 (i % 2) + c
 //             so st[m][8u .. 8u+7] are n = 32 m + 16 u + 8 hi + 0..7, the A
 //             fragment of K-step (m, u) of y^T = h~ C^T;
-//   output    acc[v] = y[token r][p0 + 32 wave + 8 i + 4 hi + c];
-//   x'        xs[kk] = x'[token 16 kk + 8 hi + j][p0 + 32 wave + r] (the A
-//             fragment of the diagonal block and the B fragment of the state
-//             update, K-step kk).
+//   output    acc[v] = y[token r][pw + col_of(8 i + 4 hi + c)]: acc[0..7]
+//             are columns pw + 8 hi + (0..7), acc[8..15] are columns
+//             pw + 16 + 8 hi + (0..7);
+//   x'        xs[kk] = x'[token 16 kk + 8 hi + j][pr] (the A fragment of
+//             the diagonal block and the B fragment of the state update,
+//             K-step kk).
 template <int PB>
 __global__ void __launch_bounds__(64 * (PB / 32))
 k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
@@ -218,16 +245,17 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     __shared__ __align__(16) unsigned char stg1[S::STG];
     __shared__ __align__(16) unsigned char stg2[S::STG];
 
-    const int npb = P / PB;
-    const int pb = blockIdx.x % npb, h = blockIdx.x / npb, b = blockIdx.y;
-    const int g = h / (H / G);
+    const int HP = H * P, GN = G * N;
+    const int c0 = blockIdx.x * PB, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
     const int r = lane & 31, hi = lane >> 5;
-    const int p0 = pb * PB, pt = wave;
-    const size_t bh = (size_t)b * H + h;
-    const float Dh = D ? D[h] : 0.f;
-    const int GN = G * N, HP = H * P;
+    const int cw = c0 + 32 * wave;             // this wave's first flattened column
+    const int hw = cw / P, pw = cw - hw * P;   // its head and headdim column
+    const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
+    const int slot = (cw - c0) / (PB > P ? P : PB);  // its decay-record slot
+    const size_t bh = (size_t)b * H + hw;
+    const float Dh = D ? D[hw] : 0.f;
 
     // ---- per-lane LDS byte offsets (lane = 16 grp + a + 4 e for the
     // transposed reads, which act within each 16-lane group)
@@ -258,16 +286,21 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     // raw x: chunk c of token row t sits at XR + xr_off(t, c)
     auto xr_off = [](int t, int c) { return t * S::XRB + 16 * (c ^ x_swz<PB>(t)); };
     // x^T fragment of K-step kk, token half s: token 16 kk + 8 hi + 4 s + e4,
-    // columns 32 wave + 16 g1 + 4 a4 .. +3:  XR + xs_tr[s] + 16 XRB kk
+    // for lanes 16 g1 + 4 a4 + (0..3) (MFMA columns q = 16 g1 + 4 a4 + c)
+    // the wave's columns 16 g1 + 8 (a4 & 1) + 4 (a4 >> 1) + (0..3) =
+    // col_of(q):  XR + xs_tr[s] + 16 XRB kk
     int xs_tr[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        xs_tr[s] = xr_off(8 * hi + 4 * s + e4, 4 * pt + 2 * g1 + (a4 >> 1)) + 8 * (a4 & 1);
-    // raw x of the skip term: token r, columns 32 wave + 8 i + 4 hi .. +3
-    int xr_skip[4];
+        xs_tr[s] = xr_off(8 * hi + 4 * s + e4, 4 * wave + 2 * g1 + (a4 & 1)) + 8 * (a4 >> 1);
+    // raw x of the skip term: token r, the wave's columns 8 hi + (0..7) and
+    // 16 + 8 hi + (0..7)
+    int xr_skip[2];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) xr_skip[i] = xr_off(r, 4 * pt + i) + 8 * hi;
+    for (int i = 0; i < 2; ++i) xr_skip[i] = xr_off(r, 4 * wave + 2 * i + hi);
+    const int pr = pw + col_of(r);
     const int cbf_rd = lane * 16;
+    const int rec_off = S::VR + 1024 * slot;
 
     // ---- register-resident scaled state
     f32x16 st[4];
@@ -279,8 +312,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 32 * m + 16 * (i >> 1) + 8 * hi + 4 * (i & 1);
-                const float4 q4 = *reinterpret_cast<const float4 *>(
-                    init + (bh * P + p0 + 32 * pt + r) * N + n);
+                const float4 q4 = *reinterpret_cast<const float4 *>(init + (bh * P + pr) * N + n);
                 st[m][4 * i] = q4.x;
                 st[m][4 * i + 1] = q4.y;
                 st[m][4 * i + 2] = q4.z;
@@ -290,12 +322,29 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     }
 
     auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
-    // C, B rows, the C B^T fragments, raw x and the decay record of block kb
-    // into stage `buf`.  Buffer-resource DMAs: the block's offset lives in
-    // the resource (scalar), the per-lane offsets are fixed, and rows past
-    // the end of the sequence fall outside the resource's range (the
-    // hardware returns zeros for them).
-    int dma_cb[S::CBD], dma_x[S::XD];
+    // Buffer resources over this workgroup's slices of C, B, x, the C B^T
+    // blocks and the decay records, built once.  The DMAs of a block add the
+    // block's byte offset to fixed per-lane offsets; rows past the end of the
+    // sequence (the ragged tail, and the prefetches past the last block) fall
+    // outside a resource's range, and the hardware reads them as zeros.
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
+        (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
+    // the records of the workgroup's heads (consecutive (batch, head) rows)
+    const int h0 = c0 / P;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
+        kBufferWord3);
+    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
+    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
+    // per-lane byte offsets of the C / B rows and of the raw x rows (block 0)
+    unsigned dma_cb[S::CBD], dma_x[S::XD];
 #pragma unroll
     for (int i = 0; i < S::CBD; ++i) {
         const int row = 4 * (wave + NW * i) + (lane >> 4);
@@ -310,61 +359,62 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
     };
-    auto dma_block = [&](int kb, unsigned char *buf) {
-        const int t0 = kb * kBlk;
-        const int rows = L - t0;  // >= 1
-        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Cm + ((size_t)b * L + t0) * GN + (size_t)g * N), 0,
-            rows * GN * 2 - g * N * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Bm + ((size_t)b * L + t0) * GN + (size_t)g * N), 0,
-            rows * GN * 2 - g * N * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(x + ((size_t)b * L + t0) * HP + (size_t)h * P + p0), 0,
-            rows * HP * 2 - (h * P + p0) * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk)), 0,
-            kBlk * kBlk * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vrec + (bh * nblk + kb) * kVecRec), 0, 1024, kBufferWord3);
-#pragma unroll
-        for (int i = 0; i < S::CBD; ++i) {
-            bdma(rc, dma_cb[i], buf + S::CS + 1024 * (wave + NW * i));
-            bdma(rb, dma_cb[i], buf + S::BS + 1024 * (wave + NW * i));
+    // DMA j (0 <= j < VM_LOADS) of block kb into stage `buf`: C and B rows
+    // (alternating), raw x, then this wave's share of the C B^T halves and
+    // the decay records
+    auto dma_piece = [&](int kb, unsigned char *buf, int j) {
+        if (j < 2 * S::CBD) {
+            const int i = j >> 1;
+            const unsigned o = dma_cb[i] + kb * cb_step;
+            if (j & 1)
+                bdma(rb, o, buf + S::BS + 1024 * (wave + NW * i));
+            else
+                bdma(rc, o, buf + S::CS + 1024 * (wave + NW * i));
+        } else if (j < 2 * S::CBD + S::XD) {
+            const int i = j - 2 * S::CBD;
+            bdma(rx, dma_x[i] + kb * x_step, buf + S::XR + 1024 * (wave + NW * i));
+        } else {
+            // piece pc (wave-uniform): selects, not a branch, so every wave
+            // runs the same instruction stream
+            int pc = wave + NW * (j - 2 * S::CBD - S::XD);
+            if (pc >= 2 + S::NRS) pc = 2 + (pc - 2) % S::NRS;
+            const bool half = pc < 2;
+            const int rsl = half ? 0 : pc - 2;
+            // a C B^T half, or 1 KB from a record start (the record and
+            // slack after it)
+            bdma(half ? rcb : rv,
+                 half ? 16 * (64 * pc + lane) + kb * cbf_step
+                      : 16 * lane + (rsl * nblk + kb) * v_step,
+                 buf + (half ? S::CBF + 1024 * pc : S::VR + 1024 * rsl));
         }
+    };
+    auto dma_block = [&](int kb, unsigned char *buf) {
 #pragma unroll
-        for (int i = 0; i < S::CBFD; ++i)
-            bdma(rcb, 16 * (64 * (wave + NW * i) + lane), buf + S::CBF + 1024 * (wave + NW * i));
-#pragma unroll
-        for (int i = 0; i < S::XD; ++i) bdma(rx, dma_x[i], buf + S::XR + 1024 * (wave + NW * i));
-        // 1 KB from the record start: the record and slack after it
-        bdma(rv, 16 * lane, buf + S::VR);
+        for (int j = 0; j < S::VM_LOADS; ++j) dma_piece(kb, buf, j);
     };
     // y through a buffer resource over this batch's rows: the stores of
     // tokens past the end fall outside it and are dropped by the hardware
     const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
         y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
-    const int y_boff = (r * HP + h * P + p0 + 32 * pt + 4 * hi) * 2;
+    const int y_boff = (r * HP + cw + 8 * hi) * 2;
     auto y_store = [&](int kb, const f32x16 &acc) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const u32x2 v = {pack2(acc[4 * i], acc[4 * i + 1]), pack2(acc[4 * i + 2], acc[4 * i + 3])};
-            __builtin_amdgcn_raw_buffer_store_b64(v, y_rsrc, y_boff + kb * kBlk * HP * 2 + 16 * i,
-                                                  0, 0);
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = {pack2(acc[8 * i], acc[8 * i + 1]), pack2(acc[8 * i + 2], acc[8 * i + 3]),
+                             pack2(acc[8 * i + 4], acc[8 * i + 5]), pack2(acc[8 * i + 6], acc[8 * i + 7])};
+            __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, y_boff + kb * kBlk * HP * 2 + 32 * i,
+                                                   0, 0);
         }
     };
 
     // ---- prologue.  Every global read in the loop is a DMA into LDS issued
     // two blocks ahead of its use (three stages): C / B rows, C B^T, raw x
-    // and the decay record of a block.  Past the last block the DMAs repeat
-    // it, so every block issues the same global memory instructions.
-    {
-        const int last = nblk - 1;
-        dma_block(0, stg0);
-        dma_block(min(1, last), stg1);
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        lds_barrier();
-    }
+    // and the decay records of a block.  Every block issues the same global
+    // memory instructions (those past the last block read zeros).
+    dma_block(0, stg0);
+    dma_block(1, stg1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
     float sig_out = 1.f;  // sigma after the previous block
 
     // The operands of block kb from stage `cur` (requested before any use)
@@ -376,7 +426,13 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         bf16x8 bt[4][2];   // B^T fragments of the state update, tile m, K-step kk
     };
     auto load_ops = [&](const unsigned char *cur, Ops &o) {
-        const float *v = reinterpret_cast<const float *>(cur + S::VR);
+        const float *v = reinterpret_cast<const float *>(cur + rec_off);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+            for (int w4 = 0; w4 < 2; ++w4)
+                o.cfv[2 * kk + w4] =
+                    *reinterpret_cast<const f32x4 *>(v + S::CF + 16 * kk + 8 * hi + 4 * w4);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -387,93 +443,83 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             o.xs[kk] = join(lds_tr(cur, S::XR + xs_tr[0] + 16 * S::XRB * kk),
                             lds_tr(cur, S::XR + xs_tr[1] + 16 * S::XRB * kk));
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int w4 = 0; w4 < 2; ++w4)
-                o.cfv[2 * kk + w4] =
-                    *reinterpret_cast<const f32x4 *>(v + S::CF + 16 * kk + 8 * hi + 4 * w4);
-#pragma unroll
         for (int kk = 0; kk < 2; ++kk) o.cbv[kk] = lds_b128(cur, S::CBF + 1024 * kk + cbf_rd);
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) {
-                const int off = 128 * (m >> 1) + 4096 * kk;
-                o.bt[m][kk] = join(lds_tr(cur, S::BS + b_tr[0][m & 1] + off),
-                                   lds_tr(cur, S::BS + b_tr[1][m & 1] + off));
-            }
     };
-    // y^T = h~ C^T (state entering the block)
-    auto y_off = [&](const Ops &o) -> f32x16 {
+    // B^T fragment q = 2 m + kk of the state update (read during y^T = h~ C^T)
+    auto load_bt = [&](const unsigned char *cur, Ops &o, int q) {
+        const int m = q >> 1, kk = q & 1;
+        const int off = 128 * (m >> 1) + 4096 * kk;
+        o.bt[m][kk] = join(lds_tr(cur, S::BS + b_tr[0][m & 1] + off),
+                           lds_tr(cur, S::BS + b_tr[1][m & 1] + off));
+    };
+
+    // block kb, si = kb % 3 (a literal in each unrolled copy)
+    auto block = [&](int kb, const int si) {
+        unsigned char *cur = stage(si);
+        const float *v = reinterpret_cast<const float *>(cur + rec_off);
+        // The block is written as a sequence of chunks fenced by scheduling
+        // barriers: each chunk starts one MFMA and then issues vector work
+        // that does not depend on it (the next state conversion and x'
+        // during y^T = h~ C^T; the epilogue and the DMAs of block kb + 2
+        // during the state update), so ALU and memory issue overlap the
+        // matrix pipeline.  A rescaled or exact block edits the operands of
+        // the common path in place between the two phases.
+        const Book bk = book_of(v, sig_out);
+        Ops o;
+        load_ops(cur, o);
+        const float rpv = v[S::RP + r];  // exp(lambda_r - lambda_e)
+        bf16x8 xr[2];                     // raw x of the skip term
+#pragma unroll
+        for (int i = 0; i < 2; ++i) xr[i] = lds_b128(cur, S::XR + xr_skip[i]);
+        const float xscale = bk.fac ? __builtin_amdgcn_rcpf(bk.sig) : 1.f;
+        auto hb_of = [&](int q) {  // bf16 A fragment of K-step q = 2 m + u
+            bf16x8 hb;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) hb[j] = (bf16)st[q >> 1][8 * (q & 1) + j];
+            return hb;
+        };
+        // x' / sigma (the state update operand; also the diagonal operand
+        // in a factored block), two values per chunk
+        bf16x8 xp[2];
+        auto xp_part = [&](int q) {
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int kk = q >> 2, j = 2 * (q & 3) + e;
+                xp[kk][j] = (bf16)((float)o.xs[kk][j] * (o.cfv[2 * kk + (j >> 2)][j & 3] * xscale));
+            }
+        };
         f32x16 acc;
 #pragma unroll
         for (int v16 = 0; v16 < 16; ++v16) acc[v16] = 0.f;
+        bf16x8 hb = hb_of(0);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int q = 0; q < 8; ++q) {
+            acc = mma32(hb, o.cfr[q >> 1][q & 1], acc);
+            __builtin_amdgcn_sched_barrier(0);
+            if (q < 7) hb = hb_of(q + 1);
+            xp_part(q);
+            load_bt(cur, o, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // (the empty asm consumes x' here, so no pass sinks its arithmetic
+        // out of the chunks above)
+        asm volatile("" : "+v"(xp[0]), "+v"(xp[1]));
+        float f = rpv * bk.sig, dco = Dh;
+        if (bk.rescale) {
+            // restart of the scale (sigma would fall below exp(-60)): the
+            // state and its output so far move to sigma_in = 1
+            __builtin_amdgcn_sched_barrier(0);
+            acc *= bk.sig_in;
 #pragma unroll
-            for (int u = 0; u < 2; ++u) {
-                bf16x8 hb;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) hb[j] = (bf16)st[m][8 * u + j];
-                acc = mma32(hb, o.cfr[m][u], acc);
-            }
-        return acc;
-    };
-    // x' = exp(lambda_e - lambda_s) dt_s x_s * scale
-    auto x_prime = [&](const Ops &o, float scale, bf16x8 (&xp)[2]) {
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                xp[kk][j] = (bf16)((float)o.xs[kk][j] * (o.cfv[2 * kk + (j >> 2)][j & 3] * scale));
-    };
-    auto state_update = [&](const Ops &o, const bf16x8 (&xp)[2]) {
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
-    };
-
-    // block kb, si = kb % 3 (a literal in each unrolled copy); bk = its
-    // bookkeeping (decided at the end of the previous block)
-    Book bk = book_of(reinterpret_cast<const float *>(stg0 + S::VR), 1.f);
-    auto block = [&](int kb, const int si) {
-        unsigned char *cur = stage(si);
-        const int last = nblk - 1;
-        const float *v = reinterpret_cast<const float *>(cur + S::VR);
-        f32x16 acc;
-        if (bk.fac) {
-            // ---- common path: one straight-line region.  Global memory
-            // issue first (the same instructions in every block, counted by
-            // the wait at the end), then every LDS operand, then the MFMAs.
-            dma_block(min(kb + 2, last), stage((si + 2) % 3));
-            Ops o;
-            load_ops(cur, o);
-            const float rpv = v[S::RP + r];  // exp(lambda_r - lambda_e)
-            bf16x4 xr[4];                     // raw x of the skip term
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                xr[i] = *reinterpret_cast<const bf16x4 *>(cur + S::XR + xr_skip[i]);
-            acc = y_off(o);
-            // x' / sigma: the operand of both the diagonal block and the state
-            bf16x8 xp[2];
-            x_prime(o, __builtin_amdgcn_rcpf(bk.sig), xp);
-#pragma unroll
-            for (int kk = 0; kk < 2; ++kk) acc = mma32(xp[kk], o.cbv[kk], acc);
-            state_update(o, xp);
-            const float f = rpv * bk.sig;
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-#pragma unroll
-                for (int c = 0; c < 4; ++c)
-                    acc[4 * i + c] = acc[4 * i + c] * f + Dh * (float)xr[i][c];
-        } else {
-            // ---- exact block: weights exp(lambda_l - lambda_s) dt_s on raw
-            // x with D on the diagonal; h~ <- sigma_in delta h~ + B^T x', sigma = 1
-            dma_block(min(kb + 2, last), stage((si + 2) % 3));
-            Ops o;
-            load_ops(cur, o);
-            acc = y_off(o);
+            for (int m = 0; m < 4; ++m) st[m] *= bk.sig_in;
+        }
+        if (!bk.fac) {
+            // (a side effect keeps the compiler from evaluating this rare
+            // branch unconditionally with selects)
+            __builtin_amdgcn_sched_barrier(0);
+            // exact block: weights exp(lambda_l - lambda_s) dt_s on raw x with
+            // D on the diagonal; h~ <- sigma_in delta h~ + B^T x', sigma = 1.
             // exp(lambda_r) sigma_in (<= 1: the exponent is formed before exp)
             acc *= fast_exp(v[S::LR + r] + v[S::LE]) * bk.sig_in;
             const float lr = v[S::LR + r];
@@ -488,36 +534,58 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                     wgt[j] = (bf16)(s <= r ? w : 0.f);
                 }
                 acc = mma32(o.xs[kk], wgt, acc);
+                // the common diagonal product below then adds zeros
+                o.cbv[kk] = zero_frag<bf16>();
             }
+            f = 1.f;
+            dco = 0.f;
             const float sd = bk.sig_in * bk.delta;
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[m] *= sd;
-            bf16x8 xp[2];
-            x_prime(o, 1.f, xp);
-            state_update(o, xp);
         }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) acc = mma32(xp[kk], o.cbv[kk], acc);
+        __builtin_amdgcn_sched_barrier(0);
+        // state update h~ += B^T x' (K-step 0 of every tile, then K-step 1),
+        // with the epilogue (from the third chunk on, once the diagonal
+        // product has landed) and the DMAs of block kb + 2
+        {
+            unsigned char *nbuf = stage((si + 2) % 3);
+            int j = 0;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int kk = q >> 2, m = q & 3;
+                st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int jn = (S::VM_LOADS * (q + 1)) / 8;
+                for (; j < jn; ++j) dma_piece(kb + 2, nbuf, j);
+                if (q >= 2) {
+                    // acc[vv] for the vv with vv * 6 / 16 == q - 2 (the
+                    // empty asm keeps them in this chunk)
+#pragma unroll
+                    for (int vv = 0; vv < 16; ++vv)
+                        if (vv * 6 / 16 == q - 2)
+                            acc[vv] = acc[vv] * f + dco * (float)xr[vv >> 3][vv & 7];
+                    asm volatile("" : "+v"(acc));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("" : "+v"(acc));
         sig_out = bk.sig;
         __builtin_amdgcn_sched_barrier(0);
 
-        // -------- the DMAs of the previous block have landed once at most
-        // this block's VM_LOADS DMAs are in flight (loads complete in issue
-        // order; a pending store only lengthens the wait); then this block's
-        // y stores
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS));
+        // -------- the DMAs of the next block have landed once at most this
+        // block's DMAs and the previous block's y stores are in flight
+        // (vector memory operations complete in issue order); then this
+        // block's y stores, and the barrier after which every wave's DMAs
+        // of the next block are visible and this stage may be refilled
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS + S::Y_STORES));
         __builtin_amdgcn_sched_barrier(0);
         y_store(kb, acc);
         __builtin_amdgcn_sched_barrier(0);
-        // bookkeeping of the next block from its decay record (landed), and
-        // the rare restart of the scale before it: h~ <- sigma h~, sigma = 1
-        if (kb + 1 < nblk) {
-            bk = book_of(reinterpret_cast<const float *>(stage((si + 1) % 3) + S::VR), sig_out);
-            if (bk.rescale) {
-#pragma unroll
-                for (int m = 0; m < 4; ++m) st[m] *= bk.sig_in;
-                bk.sig_in = 1.f;
-            }
-        }
-        lds_barrier();
+        block_barrier();
     };
 
     for (int kb = 0; kb < nblk; kb += 3) {
@@ -536,7 +604,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int n = 32 * m + 16 * (i >> 1) + 8 * hi + 4 * (i & 1);
-                *reinterpret_cast<float4 *>(final_state + (bh * P + p0 + 32 * pt + r) * N + n) =
+                *reinterpret_cast<float4 *>(final_state + (bh * P + pr) * N + n) =
                     make_float4(st[m][4 * i] * sig_out, st[m][4 * i + 1] * sig_out,
                                 st[m][4 * i + 2] * sig_out, st[m][4 * i + 3] * sig_out);
             }
@@ -640,18 +708,23 @@ template <int PB>
 static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
     const int nblk = fused_nblk(a.L);
-    hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * (a.P / PB), a.batch), dim3(S::NT), 0,
-                       stream, (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
+    hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
+                       (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
                        (const bf16 *)a.cb, a.vrec, a.D, a.init, a.final_state, (bf16 *)a.y,
                        a.L, a.H, a.G, a.P, nblk);
     return hipSuccess;
 }
 
-// Headdim block per workgroup: 64 columns (2 waves) when that still gives at
-// least one workgroup per compute unit, else 32 (1 wave) for more of them.
+// Columns per workgroup.  One workgroup per compute unit is the target:
+// 128 columns (four waves over two heads of one B/C group, which share the
+// staged C and B rows) once 64-column workgroups would outnumber the 256
+// compute units; 64 (two waves) while those still cover them; else 32 (one
+// wave) for more workgroups.
 static int pick_pb(const ForwardArgs &a) {
-    const long wg64 = (a.P % 64 == 0) ? (long)a.batch * a.H * (a.P / 64) : 0;
-    return wg64 >= 256 ? 64 : 32;
+    const long cols = (long)a.batch * a.H * a.P;
+    if (a.P == 64 && a.H % 2 == 0 && (a.H / a.G) % 2 == 0 && cols / 64 > 256) return 128;
+    if (a.P % 64 == 0 && cols / 64 >= 256) return 64;
+    return 32;
 }
 
 template <typename T>
@@ -670,7 +743,11 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     hipLaunchKernelGGL(k2b_block_cb, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
                        (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
     if ((err = mark()) != hipSuccess) return err;
-    err = pick_pb(a) == 64 ? launch_fused_main<64>(a, stream) : launch_fused_main<32>(a, stream);
+    switch (pick_pb(a)) {
+        case 128: err = launch_fused_main<128>(a, stream); break;
+        case 64: err = launch_fused_main<64>(a, stream); break;
+        default: err = launch_fused_main<32>(a, stream); break;
+    }
     if (err != hipSuccess) return err;
     if ((err = mark()) != hipSuccess) return err;
     return hipGetLastError();

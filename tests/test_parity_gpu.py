@@ -106,6 +106,9 @@ SMALL = [
     (1, 33, 2, 32, 128, 2, 32, "bf16", False),
     (1, 512, 2, 128, 128, 1, 256, "bf16", True),
     (2, 257, 4, 96, 128, 4, 128, "bf16", True),
+    # more 64-column workgroups than compute units: the fused path's
+    # four-wave layout over two heads of one group (ragged tail)
+    (2, 200, 132, 64, 128, 2, 64, "bf16", True),
 ]
 
 
@@ -126,27 +129,28 @@ def test_small_problems_every_element(dev, oracle_mod, path, case):
         _say("  componentwise y %.2e (informational)" % metrics.componentwise_err(y, yr, ya))
 
 
-def decay_regime_inputs(io, seed):
+def decay_regime_inputs(io, seed, H=4):
     """Per-head decay profiles that cross every regime of the fused path in
     one sequence: weak decay, repeated rescaling of the tracked state scale
     (block decays of 20-40), blocks whose total decay exceeds exp(-60) (the
     exact per-element weights, dt A summed over 32 tokens down to -300), and
-    factored blocks again after them; ragged length, initial state."""
+    factored blocks again after them; ragged length, initial state.  The
+    four decay rates repeat over the heads."""
     L = 400
-    inp = make_inputs(2, L, 4, 64, 128, 1, io_dtype=io, init_std=0.1, seed=seed)
+    inp = make_inputs(2, L, H, 64, 128, 1, io_dtype=io, init_std=0.1, seed=seed)
     t = np.arange(L)
     prof = np.where(t < 96, 0.01, np.where(t < 192, 0.25, np.where(t < 288, 0.08, 0.6)))
     rng = np.random.default_rng(seed)
-    jitter = 1.0 + 0.2 * rng.standard_normal(size=(2, L, 4))
-    inp["A"] = np.array([-16.0, -8.0, -2.0, -0.5], dtype=np.float32)
+    jitter = 1.0 + 0.2 * rng.standard_normal(size=(2, L, H))
+    inp["A"] = np.resize(np.array([-16.0, -8.0, -2.0, -0.5], dtype=np.float32), H)
     inp["dt"] = (prof[None, :, None] * np.abs(jitter)).astype(np.float32)
     return inp
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_decay_regimes(dev, oracle_mod, path, io):
-    inp = decay_regime_inputs(io, seed=91)
-    lam = inp["dt"][0, : 384].reshape(12, 32, 4).sum(1) * inp["A"][None, :]
+@pytest.mark.parametrize("io,H", [("bf16", 4), ("f32", 4), ("bf16", 132)])
+def test_decay_regimes(dev, oracle_mod, path, io, H):
+    inp = decay_regime_inputs(io, seed=91, H=H)
+    lam = inp["dt"][0, : 384].reshape(12, 32, H).sum(1) * inp["A"][None, :]
     _say("block decays per head: min %.1f max %.1f" % (-lam.max(), -lam.min()))
     assert (-lam > 60).any() and ((-lam > 20) & (-lam < 60)).any() and (-lam < 5).any()
     skip_if_path_unsupported(inp, io, 64)
