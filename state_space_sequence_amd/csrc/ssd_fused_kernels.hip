@@ -60,6 +60,9 @@
 // receives element c of the 8-byte reads of lanes a, a+4, a+8, a+12, so
 // pointing lane a + 4 e at row kbase + e and 4 consecutive columns of a
 // row-major [k][n] tile hands those 4 columns to lanes 4a .. 4a+3.
+#include <stdlib.h>
+#include <string.h>
+
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
 
@@ -124,8 +127,13 @@ __device__ __forceinline__ int row_swz4(int row) { return 2 * ((row >> 1) & 1) +
 // share the staged C and B rows.
 template <int PB>
 struct Fused {
-    static constexpr int NW = PB / 32;                 // waves: 32 headdim columns each
-    static constexpr int NT = 64 * NW;                 // threads
+    static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
+    // With 128 columns a fifth wave (the producer) issues every global
+    // memory operation of the workgroup: the DMAs of the stages and the y
+    // stores, which the compute waves hand over through LDS.  The compute
+    // waves then never wait on the vector memory pipeline.
+    static constexpr bool PROD = PB == 128;
+    static constexpr int NT = 64 * (NW + (PROD ? 1 : 0));  // threads
     static constexpr int N = 128;                      // dstate
     static constexpr int ROWB = 2 * N;                 // bytes per C / B row
     static constexpr int MAT = kBlk * ROWB;            // 8 KB per matrix
@@ -146,10 +154,16 @@ struct Fused {
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
     static constexpr int XR = CBF + 2048;
     static constexpr int VR = XR + kBlk * XRB;
-    static constexpr int STG = VR + 1024 * NRS;
+    // y of the block for the producer: 32 rows of XRB bytes, 16-byte chunk
+    // c of row t in slot c ^ (t & 15)
+    static constexpr int YS = VR + 1024 * NRS;
+    static constexpr int STG = YS + (PROD ? kBlk * XRB : 0);
     // floats of the decay record
     enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
-    static constexpr int LDS = 3 * STG;
+    // stages in flight: the DMAs of a block go out NST - 1 blocks ahead of
+    // its use
+    static constexpr int NST = 3;
+    static constexpr int LDS = NST * STG;
     // DMAs every wave issues in every block, all with every lane active
     static constexpr int VM_LOADS = 2 * CBD + XD + MISC;
     static constexpr int Y_STORES = 2;                 // y stores per wave and block
@@ -157,7 +171,18 @@ struct Fused {
     static_assert(XD == 2, "x DMAs");
     static_assert(STG % 16 == 0, "alignment");
     static_assert(PB == 128 ? LDS <= 160 * 1024 : 2 * LDS <= 160 * 1024, "LDS per compute unit");
-    static_assert(VM_LOADS + Y_STORES < 64, "vmcnt immediate");
+    // the end-of-block wait: younger than the DMAs of the next block are the
+    // DMAs of the NST - 2 blocks after it and the y stores of NST - 2 blocks
+    static constexpr int VM_WAIT = (NST - 2) * (VM_LOADS + Y_STORES);
+    static_assert(VM_WAIT < 64, "vmcnt immediate");
+    // the producer's DMAs of a block (C and B, x, C B^T halves, records) and
+    // y stores, and its end-of-block wait: younger than the DMAs of the next
+    // block are the y stores issued after them, the DMAs of the block after
+    // and this block's y stores
+    static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 2 + NRS;
+    static constexpr int P_STORES = kBlk * XRB / 1024;
+    static constexpr int P_WAIT = P_STORES + (NST - 2) * (P_LOADS + P_STORES);
+    static_assert(!PROD || P_WAIT < 64, "vmcnt immediate");
 };
 
 template <int PB>
@@ -231,7 +256,7 @@ __device__ __forceinline__ int col_of(int q) {
 //             the diagonal block and the B fragment of the state update,
 //             K-step kk).
 template <int PB>
-__global__ void __launch_bounds__(64 * (PB / 32))
+__global__ void __launch_bounds__(Fused<PB>::NT)
 k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const bf16 *__restrict__ cbf, const float *__restrict__ vrec,
             const float *__restrict__ D, const float *init, float *final_state,
@@ -244,15 +269,118 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     __shared__ __align__(16) unsigned char stg0[S::STG];
     __shared__ __align__(16) unsigned char stg1[S::STG];
     __shared__ __align__(16) unsigned char stg2[S::STG];
+    __shared__ __align__(16) unsigned char stg3[S::NST > 3 ? S::STG : 16];
 
     const int HP = H * P, GN = G * N;
     const int c0 = blockIdx.x * PB, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = (NW == 1 && !S::PROD) ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
+
+    auto stage = [&](int i) -> unsigned char * {
+        return i == 0 ? stg0 : (i == 1 ? stg1 : (i == 2 ? stg2 : stg3));
+    };
+    // Buffer resources over this workgroup's slices of C, B, x, the C B^T
+    // blocks and the decay records, built once.  The DMAs of a block add the
+    // block's byte offset to fixed per-lane offsets; rows past the end of the
+    // sequence (the ragged tail, and the prefetches past the last block) fall
+    // outside a resource's range, and the hardware reads them as zeros.
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
+        (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
+    // the records of the workgroup's heads (consecutive (batch, head) rows)
+    const int h0 = c0 / P;
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
+        kBufferWord3);
+    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
+    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
+    };
+    // y through a buffer resource over this batch's rows: the stores of
+    // tokens past the end fall outside it and are dropped by the hardware
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+
+    if constexpr (S::PROD) {
+        if (wave == NW) {
+            // ---- the producer wave: every DMA of the stages and every y
+            // store.  Per-lane offsets: C / B rows 4 i + lane / 16 and x rows
+            // (64 i + lane) / XC of DMA i; y rows 4 i + lane / 16, chunk
+            // lane % 16 of store i.
+            constexpr int NCB = S::MAT / 1024, NXD = kBlk * S::XRB / 1024;
+            unsigned pcb[NCB], px[NXD];
+#pragma unroll
+            for (int i = 0; i < NCB; ++i) {
+                const int row = 4 * i + (lane >> 4);
+                pcb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
+            }
+#pragma unroll
+            for (int i = 0; i < NXD; ++i) {
+                const int pos = 64 * i + lane, row = pos / S::XC;
+                px[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
+            }
+            auto pdma = [&](int kb, unsigned char *buf) {
+#pragma unroll
+                for (int i = 0; i < NCB; ++i) {
+                    bdma(rc, pcb[i] + kb * cb_step, buf + S::CS + 1024 * i);
+                    bdma(rb, pcb[i] + kb * cb_step, buf + S::BS + 1024 * i);
+                }
+#pragma unroll
+                for (int i = 0; i < NXD; ++i) bdma(rx, px[i] + kb * x_step, buf + S::XR + 1024 * i);
+#pragma unroll
+                for (int pc = 0; pc < 2; ++pc)
+                    bdma(rcb, 16 * (64 * pc + lane) + kb * cbf_step, buf + S::CBF + 1024 * pc);
+#pragma unroll
+                for (int q = 0; q < S::NRS; ++q)
+                    bdma(rv, 16 * lane + (q * nblk + kb) * v_step, buf + S::VR + 1024 * q);
+            };
+            auto pstore = [&](int kb, const unsigned char *buf) {
+#pragma unroll
+                for (int i = 0; i < S::P_STORES; ++i) {
+                    const int t = 4 * i + (lane >> 4), c = lane & 15;
+                    const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
+                                                                     16 * (c ^ (t & 15)));
+                    __builtin_amdgcn_raw_buffer_store_b128(
+                        v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
+                }
+            };
+#pragma unroll
+            for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i));
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            lds_barrier();
+            // block kb: refill the stage block kb - 1 used, store its y, then
+            // wait for the DMAs of block kb + 1 before the end-of-block barrier
+            auto pblock = [&](int kb, const int si) {
+                pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
+                if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+                __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
+                lds_barrier();
+            };
+            for (int kb = 0; kb < nblk; kb += 3) {
+                pblock(kb, 0);
+                if (kb + 1 < nblk) {
+                    pblock(kb + 1, 1);
+                    if (kb + 2 < nblk) pblock(kb + 2, 2);
+                }
+            }
+            pstore(nblk - 1, stage((nblk - 1) % S::NST));
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+            return;
+        }
+    }
+
     const int r = lane & 31, hi = lane >> 5;
     const int cw = c0 + 32 * wave;             // this wave's first flattened column
     const int hw = cw / P, pw = cw - hw * P;   // its head and headdim column
-    const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
     const int slot = (cw - c0) / (PB > P ? P : PB);  // its decay-record slot
     const size_t bh = (size_t)b * H + hw;
     const float Dh = D ? D[hw] : 0.f;
@@ -321,28 +449,6 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         }
     }
 
-    auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
-    // Buffer resources over this workgroup's slices of C, B, x, the C B^T
-    // blocks and the decay records, built once.  The DMAs of a block add the
-    // block's byte offset to fixed per-lane offsets; rows past the end of the
-    // sequence (the ragged tail, and the prefetches past the last block) fall
-    // outside a resource's range, and the hardware reads them as zeros.
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
-        (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
-    // the records of the workgroup's heads (consecutive (batch, head) rows)
-    const int h0 = c0 / P;
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
-        kBufferWord3);
-    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
-    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
     // per-lane byte offsets of the C / B rows and of the raw x rows (block 0)
     unsigned dma_cb[S::CBD], dma_x[S::XD];
 #pragma unroll
@@ -355,10 +461,6 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         const int pos = 64 * (wave + NW * i) + lane, row = pos / S::XC;
         dma_x[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
     }
-    typedef __attribute__((address_space(3))) void lds_void;
-    auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
-    };
     // DMA j (0 <= j < VM_LOADS) of block kb into stage `buf`: C and B rows
     // (alternating), raw x, then this wave's share of the C B^T halves and
     // the decay records
@@ -392,11 +494,20 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
         for (int j = 0; j < S::VM_LOADS; ++j) dma_piece(kb, buf, j);
     };
-    // y through a buffer resource over this batch's rows: the stores of
-    // tokens past the end fall outside it and are dropped by the hardware
-    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
     const int y_boff = (r * HP + cw + 8 * hi) * 2;
+    // staging slots of this lane's two 16-byte runs (row r, chunks
+    // 4 wave + 2 i + hi of the workgroup's row)
+    int ys_off[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) ys_off[i] = S::YS + r * S::XRB + 16 * ((4 * wave + 2 * i + hi) ^ (r & 15));
+    auto y_stage = [&](unsigned char *cur, const f32x16 &acc) {
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const u32x4 v = {pack2(acc[8 * i], acc[8 * i + 1]), pack2(acc[8 * i + 2], acc[8 * i + 3]),
+                             pack2(acc[8 * i + 4], acc[8 * i + 5]), pack2(acc[8 * i + 6], acc[8 * i + 7])};
+            *reinterpret_cast<u32x4 *>(cur + ys_off[i]) = v;
+        }
+    };
     auto y_store = [&](int kb, const f32x16 &acc) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -408,11 +519,13 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     };
 
     // ---- prologue.  Every global read in the loop is a DMA into LDS issued
-    // two blocks ahead of its use (three stages): C / B rows, C B^T, raw x
+    // NST - 1 blocks ahead of its use (NST stages): C / B rows, C B^T, raw x
     // and the decay records of a block.  Every block issues the same global
     // memory instructions (those past the last block read zeros).
-    dma_block(0, stg0);
-    dma_block(1, stg1);
+    if constexpr (!S::PROD) {
+#pragma unroll
+        for (int i = 0; i < S::NST - 1; ++i) dma_block(i, stage(i));
+    }
     __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
     lds_barrier();
     float sig_out = 1.f;  // sigma after the previous block
@@ -460,7 +573,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         // The block is written as a sequence of chunks fenced by scheduling
         // barriers: each chunk starts one MFMA and then issues vector work
         // that does not depend on it (the next state conversion and x'
-        // during y^T = h~ C^T; the epilogue and the DMAs of block kb + 2
+        // during y^T = h~ C^T; the epilogue and the DMAs of block kb + NST - 1
         // during the state update), so ALU and memory issue overlap the
         // matrix pipeline.  A rescaled or exact block edits the operands of
         // the common path in place between the two phases.
@@ -549,17 +662,19 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         __builtin_amdgcn_sched_barrier(0);
         // state update h~ += B^T x' (K-step 0 of every tile, then K-step 1),
         // with the epilogue (from the third chunk on, once the diagonal
-        // product has landed) and the DMAs of block kb + 2
+        // product has landed) and the DMAs of block kb + NST - 1
         {
-            unsigned char *nbuf = stage((si + 2) % 3);
+            unsigned char *nbuf = stage((si + S::NST - 1) % S::NST);
             int j = 0;
 #pragma unroll
             for (int q = 0; q < 8; ++q) {
                 const int kk = q >> 2, m = q & 3;
                 st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
                 __builtin_amdgcn_sched_barrier(0);
-                const int jn = (S::VM_LOADS * (q + 1)) / 8;
-                for (; j < jn; ++j) dma_piece(kb + 2, nbuf, j);
+                if constexpr (!S::PROD) {
+                    const int jn = (S::VM_LOADS * (q + 1)) / 8;
+                    for (; j < jn; ++j) dma_piece(kb + S::NST - 1, nbuf, j);
+                }
                 if (q >= 2) {
                     // acc[vv] for the vv with vv * 6 / 16 == q - 2 (the
                     // empty asm keeps them in this chunk)
@@ -576,23 +691,38 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         sig_out = bk.sig;
         __builtin_amdgcn_sched_barrier(0);
 
-        // -------- the DMAs of the next block have landed once at most this
-        // block's DMAs and the previous block's y stores are in flight
-        // (vector memory operations complete in issue order); then this
-        // block's y stores, and the barrier after which every wave's DMAs
-        // of the next block are visible and this stage may be refilled
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS + S::Y_STORES));
-        __builtin_amdgcn_sched_barrier(0);
-        y_store(kb, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        block_barrier();
+        if constexpr (S::PROD) {
+            // y of the block to the producer through this stage's staging
+            // rows; the barrier then also publishes it
+            y_stage(cur, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            lds_barrier();
+        } else {
+            // -------- the DMAs of the next block have landed once at most
+            // this block's DMAs and the previous block's y stores are in
+            // flight (vector memory operations complete in issue order);
+            // then this block's y stores, and the barrier after which every
+            // wave's DMAs of the next block are visible and this stage may
+            // be refilled
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_WAIT));
+            __builtin_amdgcn_sched_barrier(0);
+            y_store(kb, acc);
+            __builtin_amdgcn_sched_barrier(0);
+            block_barrier();
+        }
     };
 
-    for (int kb = 0; kb < nblk; kb += 3) {
+    // unrolled by the stage count, so that every stage address is a literal
+    for (int kb = 0; kb < nblk; kb += S::NST) {
         block(kb, 0);
         if (kb + 1 < nblk) {
             block(kb + 1, 1);
-            if (kb + 2 < nblk) block(kb + 2, 2);
+            if (kb + 2 < nblk) {
+                block(kb + 2, 2);
+                if constexpr (S::NST > 3) {
+                    if (kb + 3 < nblk) block(kb + 3, 3);
+                }
+            }
         }
     }
     // no DMA may land in LDS after the workgroup ends
@@ -613,11 +743,15 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 
 // Diagonal 32x32 block of C B^T for every 32-token block and group, bf16,
 // causally masked (entries with s > l are exact zeros), stored in the MFMA
-// B-fragment order the fused kernel reads: K-step kk, lane L hold the 8
-// values C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at
-// (64 kk + L) * 16.  One wave per (block, group, batch) computes E = B C^T
-// with v_mfma_f32_32x32x16_bf16: lane (l = L % 32, hi) ends with
+// B-fragment order the fused kernel reads.  W16 = 0 (waves of 32 columns,
+// v_mfma_f32_32x32x16_bf16): K-step kk, lane L hold the 8 values
+// C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at (64 kk + L) * 16.
+// W16 = 1 (waves of 16 columns, v_mfma_f32_16x16x32_bf16): token tile tt,
+// lane L hold C B^T[16 tt + L % 16][8 (L / 16) .. +7] at (64 tt + L) * 16.
+// One wave per (block, group, batch) computes E = B C^T with
+// v_mfma_f32_32x32x16_bf16: lane (l = L % 32, hi) ends with
 // E[s][l] = C_l . B_s for s = 8 i + 4 hi + c, four runs of 4 consecutive s.
+template <int W16>
 __global__ void __launch_bounds__(64)
 k2b_block_cb(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__restrict__ cbf,
              int L, int G, int nblk) {
@@ -639,11 +773,384 @@ k2b_block_cb(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__r
     // lane (l = r, hi): E[s][l] for s = 8 i + 4 hi + c
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-        const int s0 = 8 * i + 4 * hi, kk = s0 >> 4, hs = (s0 >> 3) & 1;
+        const int s0 = 8 * i + 4 * hi;
         bf16x4 v4;
 #pragma unroll
         for (int c = 0; c < 4; ++c) v4[c] = s0 + c <= r ? (bf16)acc[4 * i + c] : (bf16)0.f;
-        *reinterpret_cast<bf16x4 *>(out + (64 * kk + r + 32 * hs) * 8 + (s0 & 7)) = v4;
+        size_t dst;
+        if (W16) {
+            // t-tile r / 16, lane (r % 16) + 16 (s0 / 8), values s0 % 8 .. +3
+            dst = (64 * (r >> 4) + (r & 15) + 16 * (s0 >> 3)) * 8 + (s0 & 7);
+        } else {
+            const int kk = s0 >> 4, hs = (s0 >> 3) & 1;
+            dst = (64 * kk + r + 32 * hs) * 8 + (s0 & 7);
+        }
+        *reinterpret_cast<bf16x4 *>(out + dst) = v4;
+    }
+}
+
+// ------------------------------------------------------------------------
+// The same pass with 16 headdim columns per wave on v_mfma_f32_16x16x32_bf16
+// (operands: lane l holds row (A) / column (B) l % 16 and k = 8 (l / 16) + j,
+// j = 0..7; result register v of lane l is D[4 (l / 16) + v][l % 16]).  A
+// workgroup of NW = PB / 16 waves covers PB columns of one head, so twice as
+// many waves share the work of a head: with two of them on a SIMD, one
+// wave's vector ALU work issues while the other waits, which a single wave
+// per SIMD cannot do.
+//
+// Per wave: headdim columns pw + (0..15), pw = p0 + 16 wave.  With lane l,
+// r = l % 16, g = l / 16:
+//   state     st[mt][v] = h~[n][pw + r], n = 32 (mt / 2) + 8 g + 4 (mt % 2) + v
+//             (the state update's row order), so st[2 kk] and st[2 kk + 1]
+//             together hold n = 32 kk + 8 g + (0..7): the A fragment of
+//             K-step kk of y^T = h~ C^T;
+//   output    acc[tt][v] = y[token 16 tt + r][pw + 4 g + v];
+//   x'        xs = x'[token 8 g + j][pw + r] (the A fragment of the diagonal
+//             block and the B fragment of the state update).
+template <int PB>
+struct Fused16 {
+    static constexpr int NW = PB / 16;                 // waves: 16 headdim columns each
+    static constexpr int NT = 64 * NW;
+    static constexpr int N = 128;
+    static constexpr int ROWB = 2 * N;
+    static constexpr int MAT = kBlk * ROWB;
+    static constexpr int CBD = MAT / 1024 / NW;        // DMAs per matrix and wave
+    static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
+    static constexpr int XRB = 2 * PB;
+    static constexpr int XD = kBlk * XRB / 1024 / NW;  // x DMAs per wave (one)
+    static constexpr int MISC = (3 + NW - 1) / NW;     // C B^T halves and the record
+    static constexpr int CS = 0;
+    static constexpr int BS = MAT;
+    static constexpr int CBF = 2 * MAT;
+    static constexpr int XR = CBF + 2048;
+    static constexpr int VR = XR + kBlk * XRB;
+    static constexpr int STG = VR + 1024;
+    enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
+    static constexpr int LDS = 3 * STG;
+    static constexpr int VM_LOADS = 2 * CBD + XD + MISC;
+    static constexpr int Y_STORES = 2;
+    static_assert(PB == 32 || PB == 64, "two or four waves");
+    static_assert(XD == 1, "x DMAs");
+    static_assert(2 * LDS <= 160 * 1024, "two workgroups per compute unit");
+    static_assert(VM_LOADS + Y_STORES < 64, "vmcnt immediate");
+};
+
+__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int PB>
+__global__ void __launch_bounds__(64 * (PB / 16))
+k_fused16_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
+              const bf16 *__restrict__ Cm, const bf16 *__restrict__ cbf,
+              const float *__restrict__ vrec, const float *__restrict__ D, const float *init,
+              float *final_state, bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
+    typedef Fused16<PB> S;
+    constexpr int NW = S::NW, N = S::N;
+    __shared__ __align__(16) unsigned char stg0[S::STG];
+    __shared__ __align__(16) unsigned char stg1[S::STG];
+    __shared__ __align__(16) unsigned char stg2[S::STG];
+
+    const int HP = H * P, GN = G * N;
+    const int npb = P / PB;
+    const int pb = blockIdx.x % npb, h = blockIdx.x / npb, b = blockIdx.y;
+    const int g_grp = h / (H / G);
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int r = lane & 15, g = lane >> 4;
+    const int p0 = pb * PB, pw = p0 + 16 * wave;
+    const size_t bh = (size_t)b * H + h;
+    const float Dh = D ? D[h] : 0.f;
+
+    // ---- per-lane LDS byte offsets (transposed reads: within each 16-lane
+    // group, lane 4 a + c receives element c of the 8-byte reads of lanes a,
+    // a + 4, a + 8, a + 12; here a = lane & 3, e = (lane >> 2) & 3 is the
+    // reading lane's k offset)
+    const int a4 = lane & 3, e4 = (lane >> 2) & 3;
+    // C fragment (tt, kk): token 16 tt + r, chunk 4 kk + g:
+    //   CS + c_rd[kk & 1] + 4096 tt + 128 (kk >> 1)
+    int c_rd[2];
+    {
+        const int sw = row_swz(r);
+#pragma unroll
+        for (int k1 = 0; k1 < 2; ++k1) c_rd[k1] = r * S::ROWB + 16 * ((4 * k1 + g) ^ sw);
+    }
+    // B^T fragment of state tile mt (rows n = 32 (mt / 2) + 8 a + 4 (mt % 2)
+    // + c for the lanes 4 a + c), read half hh: token 8 g + 4 hh + e4:
+    //   BS + b_tr[hh][(mt >> 1) & 1] + 128 (mt >> 2) + 8 (mt & 1)
+    int b_tr[2][2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int q1 = 0; q1 < 2; ++q1) {
+            const int t = 8 * g + 4 * hh + e4;
+            b_tr[hh][q1] = t * S::ROWB + 16 * ((4 * q1 + a4) ^ row_swz(t));
+        }
+    auto xr_off = [](int t, int c) { return t * S::XRB + 16 * (c ^ x_swz<PB>(t)); };
+    // x^T fragment, read half hh: token 8 g + 4 hh + e4, columns
+    // 16 wave + 4 a4 .. +3:  XR + xs_tr[hh]
+    int xs_tr[2];
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+        xs_tr[hh] = xr_off(8 * g + 4 * hh + e4, 2 * wave + (a4 >> 1)) + 8 * (a4 & 1);
+    // raw x of the skip term: token 16 tt + r, columns 16 wave + 4 g .. +3
+    int xr_skip[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) xr_skip[tt] = xr_off(16 * tt + r, 2 * wave + (g >> 1)) + 8 * (g & 1);
+    const int cbf_rd = lane * 16;
+
+    // ---- register-resident scaled state
+    f32x4 st[8];
+#pragma unroll
+    for (int mt = 0; mt < 8; ++mt) {
+        st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (init) {
+            const int n = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1);
+            const float4 q4 = *reinterpret_cast<const float4 *>(init + (bh * P + pw + r) * N + n);
+            st[mt] = f32x4{q4.x, q4.y, q4.z, q4.w};
+        }
+    }
+
+    auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
+    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Cm + (size_t)b * L * GN + (size_t)g_grp * N), 0, (L * GN - g_grp * N) * 2,
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(Bm + (size_t)b * L * GN + (size_t)g_grp * N), 0, (L * GN - g_grp * N) * 2,
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(x + (size_t)b * L * HP + (size_t)h * P + p0), 0, (L * HP - h * P - p0) * 2,
+        kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(cbf + ((size_t)b * nblk * G + g_grp) * (kBlk * kBlk)), 0,
+        (nblk * G - g_grp) * (kBlk * kBlk * 2), kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+        (void *)(vrec + bh * nblk * kVecRec), 0, nblk * kVecRec * 4, kBufferWord3);
+    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
+    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
+    unsigned dma_cb[S::CBD], dma_x;
+#pragma unroll
+    for (int i = 0; i < S::CBD; ++i) {
+        const int row = 4 * (wave + NW * i) + (lane >> 4);
+        dma_cb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
+    }
+    {
+        const int pos = 64 * wave + lane, row = pos / S::XC;
+        dma_x = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
+    }
+    typedef __attribute__((address_space(3))) void lds_void;
+    auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
+    };
+    // DMA j (0 <= j < VM_LOADS) of block kb into stage `buf`: C and B rows
+    // (alternating), raw x, then this wave's share of the C B^T halves and
+    // the record (past the last piece: the record again)
+    auto dma_piece = [&](int kb, unsigned char *buf, int j) {
+        if (j < 2 * S::CBD) {
+            const int i = j >> 1;
+            const unsigned o = dma_cb[i] + kb * cb_step;
+            if (j & 1)
+                bdma(rb, o, buf + S::BS + 1024 * (wave + NW * i));
+            else
+                bdma(rc, o, buf + S::CS + 1024 * (wave + NW * i));
+        } else if (j < 2 * S::CBD + S::XD) {
+            bdma(rx, dma_x + kb * x_step, buf + S::XR + 1024 * wave);
+        } else {
+            int pc = wave + NW * (j - 2 * S::CBD - S::XD);
+            if (pc > 2) pc = 2;
+            const bool half = pc < 2;
+            bdma(half ? rcb : rv,
+                 half ? 16 * (64 * pc + lane) + kb * cbf_step : 16 * lane + kb * v_step,
+                 buf + (half ? S::CBF + 1024 * pc : S::VR));
+        }
+    };
+    auto dma_block = [&](int kb, unsigned char *buf) {
+#pragma unroll
+        for (int j = 0; j < S::VM_LOADS; ++j) dma_piece(kb, buf, j);
+    };
+    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+    const int y_boff = (r * HP + h * P + pw + 4 * g) * 2;
+    auto y_store = [&](int kb, const f32x4 (&acc)[2]) {
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) {
+            const u32x2 v = {pack2(acc[tt][0], acc[tt][1]), pack2(acc[tt][2], acc[tt][3])};
+            __builtin_amdgcn_raw_buffer_store_b64(v, y_rsrc,
+                                                  y_boff + (kb * kBlk + 16 * tt) * HP * 2, 0, 0);
+        }
+    };
+
+    dma_block(0, stg0);
+    dma_block(1, stg1);
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    lds_barrier();
+    float sig_out = 1.f;
+
+    struct Ops {
+        bf16x8 cfr[2][4];  // C fragments (tt, kk)
+        bf16x8 xs;         // raw x^T
+        f32x4 cfv[2];      // cf of tokens 8 g + 0..7
+        bf16x8 cbv[2];     // causal diagonal block of C B^T, t-tiles 0 and 1
+        bf16x8 bt[8];      // B^T fragments of the state tiles
+    };
+    auto load_ops = [&](const unsigned char *cur, Ops &o) {
+        const float *v = reinterpret_cast<const float *>(cur + S::VR);
+#pragma unroll
+        for (int w4 = 0; w4 < 2; ++w4)
+            o.cfv[w4] = *reinterpret_cast<const f32x4 *>(v + S::CF + 8 * g + 4 * w4);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt)
+                o.cfr[tt][kk] = lds_b128(cur, S::CS + c_rd[kk & 1] + 4096 * tt + 128 * (kk >> 1));
+        o.xs = join(lds_tr(cur, S::XR + xs_tr[0]), lds_tr(cur, S::XR + xs_tr[1]));
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) o.cbv[tt] = lds_b128(cur, S::CBF + 1024 * tt + cbf_rd);
+    };
+    auto load_bt = [&](const unsigned char *cur, Ops &o, int mt) {
+        const int off = 128 * (mt >> 2) + 8 * (mt & 1);
+        o.bt[mt] = join(lds_tr(cur, S::BS + b_tr[0][(mt >> 1) & 1] + off),
+                        lds_tr(cur, S::BS + b_tr[1][(mt >> 1) & 1] + off));
+    };
+
+    auto block = [&](int kb, const int si) {
+        unsigned char *cur = stage(si);
+        const float *v = reinterpret_cast<const float *>(cur + S::VR);
+        const Book bk = book_of(v, sig_out);
+        Ops o;
+        load_ops(cur, o);
+        float rpv[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) rpv[tt] = v[S::RP + 16 * tt + r];
+        bf16x4 xr[2];
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt)
+            xr[tt] = *reinterpret_cast<const bf16x4 *>(cur + S::XR + xr_skip[tt]);
+        const float xscale = bk.fac ? __builtin_amdgcn_rcpf(bk.sig) : 1.f;
+        auto hb_of = [&](int kk) {
+            bf16x8 hb;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                hb[j] = (bf16)st[2 * kk][j];
+                hb[4 + j] = (bf16)st[2 * kk + 1][j];
+            }
+            return hb;
+        };
+        bf16x8 xp;
+        f32x4 acc[2];
+        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
+        acc[1] = acc[0];
+        bf16x8 hb = hb_of(0);
+        __builtin_amdgcn_sched_barrier(0);
+        // y^T = h~ C^T: eight MFMAs (K-step kk, t-tile tt), each followed by
+        // the next state conversion, one x' value and a B^T fragment
+#pragma unroll
+        for (int q = 0; q < 8; ++q) {
+            const int kk = q >> 1, tt = q & 1;
+            acc[tt] = mma16(hb, o.cfr[tt][kk], acc[tt]);
+            __builtin_amdgcn_sched_barrier(0);
+            if (tt == 1 && kk < 3) hb = hb_of(kk + 1);
+            if (q & 1) {
+                // x' values q - 1 and q (tokens 8 g + q - 1, 8 g + q)
+#pragma unroll
+                for (int e = 0; e < 2; ++e) {
+                    const int j = q - 1 + e;
+                    xp[j] = (bf16)((float)o.xs[j] * (o.cfv[j >> 2][j & 3] * xscale));
+                }
+            }
+            load_bt(cur, o, q);
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        asm volatile("" : "+v"(xp));
+        float f[2] = {rpv[0] * bk.sig, rpv[1] * bk.sig};
+        float dco = Dh;
+        if (bk.rescale) {
+            __builtin_amdgcn_sched_barrier(0);
+            acc[0] *= bk.sig_in;
+            acc[1] *= bk.sig_in;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) st[mt] *= bk.sig_in;
+        }
+        if (!bk.fac) {
+            __builtin_amdgcn_sched_barrier(0);
+            // exact block (see the wave-of-32 kernel): per-element weights
+            // exp(lambda_t - lambda_s) dt_s on raw x, D on the diagonal
+#pragma unroll
+            for (int tt = 0; tt < 2; ++tt) {
+                const int t = 16 * tt + r;
+                const float lr = v[S::LR + t];
+                acc[tt] *= fast_exp(lr + v[S::LE]) * bk.sig_in;
+                bf16x8 wgt;
+#pragma unroll
+                for (int j = 0; j < 8; ++j) {
+                    const int s = 8 * g + j;
+                    const float w = (float)o.cbv[tt][j] * fast_exp(fminf(lr - v[S::LR + s], 0.f)) *
+                                        v[S::DT + s] + (s == t ? Dh : 0.f);
+                    wgt[j] = (bf16)(s <= t ? w : 0.f);
+                }
+                acc[tt] = mma16(o.xs, wgt, acc[tt]);
+                o.cbv[tt] = zero_frag<bf16>();
+            }
+            f[0] = f[1] = 1.f;
+            dco = 0.f;
+            const float sd = bk.sig_in * bk.delta;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) st[mt] *= sd;
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int tt = 0; tt < 2; ++tt) acc[tt] = mma16(xp, o.cbv[tt], acc[tt]);
+        __builtin_amdgcn_sched_barrier(0);
+        // state update h~ += B^T x' (eight tiles), with the epilogue and the
+        // DMAs of block kb + 2 issued between the MFMAs
+        {
+            unsigned char *nbuf = stage((si + 2) % 3);
+            int j = 0;
+#pragma unroll
+            for (int mt = 0; mt < 8; ++mt) {
+                st[mt] = mma16(o.bt[mt], xp, st[mt]);
+                __builtin_amdgcn_sched_barrier(0);
+                const int jn = (S::VM_LOADS * (mt + 1)) / 8;
+                for (; j < jn; ++j) dma_piece(kb + 2, nbuf, j);
+                if (mt >= 2 && mt < 6) {
+                    // output values 2 (mt - 2), 2 (mt - 2) + 1 of both t-tiles
+#pragma unroll
+                    for (int e = 0; e < 2; ++e) {
+                        const int vv = 2 * (mt - 2) + e, tt = vv >> 2, c = vv & 3;
+                        acc[tt][c] = acc[tt][c] * f[tt] + dco * (float)xr[tt][c];
+                    }
+                    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+                }
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
+        sig_out = bk.sig;
+        __builtin_amdgcn_sched_barrier(0);
+        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS + S::Y_STORES));
+        __builtin_amdgcn_sched_barrier(0);
+        y_store(kb, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        block_barrier();
+    };
+
+    for (int kb = 0; kb < nblk; kb += 3) {
+        block(kb, 0);
+        if (kb + 1 < nblk) {
+            block(kb + 1, 1);
+            if (kb + 2 < nblk) block(kb + 2, 2);
+        }
+    }
+    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+
+    if (final_state) {
+#pragma unroll
+        for (int mt = 0; mt < 8; ++mt) {
+            const int n = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1);
+            *reinterpret_cast<float4 *>(final_state + (bh * P + pw + r) * N + n) =
+                make_float4(st[mt][0] * sig_out, st[mt][1] * sig_out, st[mt][2] * sig_out,
+                            st[mt][3] * sig_out);
+        }
     }
 }
 
@@ -679,8 +1186,11 @@ k1_block_vectors(const float *__restrict__ dt, const float *__restrict__ A,
     float *rec = vrec + (((size_t)b * H + h) * nblk + kb) * kVecRec;
     rec[tt] = fast_exp((float)(lam_e - lam)) * d;
     rec[kBlk + tt] = fac ? fast_exp((float)(lam - lam_e)) : 0.f;
-    rec[2 * kBlk + tt] = (float)(lam - lam_e);
-    rec[3 * kBlk + tt] = d;
+    // the per-element exponents and steps are read by exact blocks only
+    if (!fac) {
+        rec[2 * kBlk + tt] = (float)(lam - lam_e);
+        rec[3 * kBlk + tt] = d;
+    }
     if (tt == kBlk - 1) {
         rec[4 * kBlk] = fast_exp(le);
         rec[4 * kBlk + 1] = fac ? 1.f : 0.f;
@@ -715,6 +1225,25 @@ static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     return hipSuccess;
 }
 
+template <int PB>
+static hipError_t launch_fused16_main(const ForwardArgs &a, hipStream_t stream) {
+    typedef Fused16<PB> S;
+    const int nblk = fused_nblk(a.L);
+    hipLaunchKernelGGL((k_fused16_ssd<PB>), dim3(a.H * (a.P / PB), a.batch), dim3(S::NT), 0,
+                       stream, (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
+                       (const bf16 *)a.cb, a.vrec, a.D, a.init, a.final_state, (bf16 *)a.y,
+                       a.L, a.H, a.G, a.P, nblk);
+    return hipSuccess;
+}
+
+// Waves of 32 columns unless SSD_FUSED_WAVE=16 asks for waves of 16 (a
+// diagnostic switch for comparing the two layouts).
+static bool use_wave16(const ForwardArgs &a) {
+    (void)a;
+    const char *env = getenv("SSD_FUSED_WAVE");
+    return env && strcmp(env, "16") == 0;
+}
+
 // Columns per workgroup.  One workgroup per compute unit is the target:
 // 128 columns (four waves over two heads of one B/C group, which share the
 // staged C and B rows) once 64-column workgroups would outnumber the 256
@@ -740,13 +1269,22 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     hipLaunchKernelGGL(k1_block_vectors, dim3(nblk, (a.H + 7) / 8, a.batch), dim3(256), 0, stream,
                        a.dt, a.A, a.vrec, a.L, a.H, nblk);
     if ((err = mark()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k2b_block_cb, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
-                       (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
+    const bool w16 = use_wave16(a);
+    if (w16)
+        hipLaunchKernelGGL(k2b_block_cb<1>, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
+                           (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
+    else
+        hipLaunchKernelGGL(k2b_block_cb<0>, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
+                           (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
     if ((err = mark()) != hipSuccess) return err;
-    switch (pick_pb(a)) {
-        case 128: err = launch_fused_main<128>(a, stream); break;
-        case 64: err = launch_fused_main<64>(a, stream); break;
-        default: err = launch_fused_main<32>(a, stream); break;
+    if (w16) {
+        err = a.P % 64 == 0 ? launch_fused16_main<64>(a, stream) : launch_fused16_main<32>(a, stream);
+    } else {
+        switch (pick_pb(a)) {
+            case 128: err = launch_fused_main<128>(a, stream); break;
+            case 64: err = launch_fused_main<64>(a, stream); break;
+            default: err = launch_fused_main<32>(a, stream); break;
+        }
     }
     if (err != hipSuccess) return err;
     if ((err = mark()) != hipSuccess) return err;

@@ -34,11 +34,14 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.fixture(params=["split", "fused"])
+@pytest.fixture(params=["split", "fused", "fused16"])
 def path(request, monkeypatch):
     """Run the test through one forward path (the library reads
-    SSD_FORWARD_PATH on every call)."""
-    monkeypatch.setenv("SSD_FORWARD_PATH", request.param)
+    SSD_FORWARD_PATH and SSD_FUSED_WAVE on every call): the split kernels,
+    the fused pass with waves of 32 headdim columns (the default), or the
+    fused pass with waves of 16."""
+    monkeypatch.setenv("SSD_FORWARD_PATH", "split" if request.param == "split" else "fused")
+    monkeypatch.setenv("SSD_FUSED_WAVE", "16" if request.param == "fused16" else "32")
     return request.param
 
 
