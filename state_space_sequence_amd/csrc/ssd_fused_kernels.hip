@@ -128,11 +128,11 @@ __device__ __forceinline__ int row_swz4(int row) { return 2 * ((row >> 1) & 1) +
 template <int PB>
 struct Fused {
     static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
-    // With 128 columns a fifth wave (the producer) issues every global
-    // memory operation of the workgroup: the DMAs of the stages and the y
-    // stores, which the compute waves hand over through LDS.  The compute
-    // waves then never wait on the vector memory pipeline.
-    static constexpr bool PROD = PB == 128;
+    // One more wave (the producer) issues every global memory operation of
+    // the workgroup: the DMAs of the stages and the y stores, which the
+    // compute waves hand over through LDS.  The compute waves then never
+    // wait on the vector memory pipeline.
+    static constexpr bool PROD = true;
     static constexpr int NT = 64 * (NW + (PROD ? 1 : 0));  // threads
     static constexpr int N = 128;                      // dstate
     static constexpr int ROWB = 2 * N;                 // bytes per C / B row
@@ -155,7 +155,7 @@ struct Fused {
     static constexpr int XR = CBF + 2048;
     static constexpr int VR = XR + kBlk * XRB;
     // y of the block for the producer: 32 rows of XRB bytes, 16-byte chunk
-    // c of row t in slot c ^ (t & 15)
+    // c of row t in slot c ^ (t & (XC - 1))
     static constexpr int YS = VR + 1024 * NRS;
     static constexpr int STG = YS + (PROD ? kBlk * XRB : 0);
     // floats of the decay record
@@ -170,7 +170,9 @@ struct Fused {
     static_assert(PB == 32 || PB == 64 || PB == 128, "one, two or four waves");
     static_assert(XD == 2, "x DMAs");
     static_assert(STG % 16 == 0, "alignment");
-    static_assert(PB == 128 ? LDS <= 160 * 1024 : 2 * LDS <= 160 * 1024, "LDS per compute unit");
+    // (two 32-column workgroups fit a compute unit; wider ones run one per
+    // compute unit, which the column choice arranges)
+    static_assert(PB == 32 ? 2 * LDS <= 160 * 1024 : LDS <= 160 * 1024, "LDS per compute unit");
     // the end-of-block wait: younger than the DMAs of the next block are the
     // DMAs of the NST - 2 blocks after it and the y stores of NST - 2 blocks
     static constexpr int VM_WAIT = (NST - 2) * (VM_LOADS + Y_STORES);
@@ -314,8 +316,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         if (wave == NW) {
             // ---- the producer wave: every DMA of the stages and every y
             // store.  Per-lane offsets: C / B rows 4 i + lane / 16 and x rows
-            // (64 i + lane) / XC of DMA i; y rows 4 i + lane / 16, chunk
-            // lane % 16 of store i.
+            // (64 i + lane) / XC of DMA i; y row (64 i + lane) / XC, chunk
+            // (64 i + lane) % XC of store i.
             constexpr int NCB = S::MAT / 1024, NXD = kBlk * S::XRB / 1024;
             unsigned pcb[NCB], px[NXD];
 #pragma unroll
@@ -346,9 +348,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             auto pstore = [&](int kb, const unsigned char *buf) {
 #pragma unroll
                 for (int i = 0; i < S::P_STORES; ++i) {
-                    const int t = 4 * i + (lane >> 4), c = lane & 15;
+                    const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
                     const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
-                                                                     16 * (c ^ (t & 15)));
+                                                                     16 * (c ^ (t & (S::XC - 1))));
                     __builtin_amdgcn_raw_buffer_store_b128(
                         v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
                 }
@@ -499,7 +501,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     // 4 wave + 2 i + hi of the workgroup's row)
     int ys_off[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) ys_off[i] = S::YS + r * S::XRB + 16 * ((4 * wave + 2 * i + hi) ^ (r & 15));
+    for (int i = 0; i < 2; ++i)
+        ys_off[i] = S::YS + r * S::XRB + 16 * ((4 * wave + 2 * i + hi) ^ (r & (S::XC - 1)));
     auto y_stage = [&](unsigned char *cur, const f32x16 &acc) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
