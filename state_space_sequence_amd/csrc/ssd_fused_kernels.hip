@@ -130,61 +130,52 @@ struct Fused {
     static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
     // One more wave (the producer) issues every global memory operation of
     // the workgroup: the DMAs of the stages and the y stores, which the
-    // compute waves hand over through LDS.  The compute waves then never
-    // wait on the vector memory pipeline.
-    static constexpr bool PROD = true;
-    static constexpr int NT = 64 * (NW + (PROD ? 1 : 0));  // threads
+    // compute waves hand over through LDS.  The compute waves never wait on
+    // the vector memory pipeline.
+    static constexpr int NT = 64 * (NW + 1);           // threads
     static constexpr int N = 128;                      // dstate
     static constexpr int ROWB = 2 * N;                 // bytes per C / B row
     static constexpr int MAT = kBlk * ROWB;            // 8 KB per matrix
-    static constexpr int CBD = MAT / 1024 / NW;        // wave-wide DMAs per matrix and wave
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
     static constexpr int XRB = 2 * PB;                 // raw x row bytes
-    static constexpr int XD = kBlk * XRB / 1024 / NW;  // x DMAs per wave (two)
     static constexpr int NRS = PB == 128 ? 2 : 1;      // decay-record slots (heads)
-    // the other DMAs of a block, 1 KB each: the two halves of the C B^T
-    // block, then one decay record per head; wave w issues pieces
-    // w, w + NW, ... (past the last piece: a repeat of a record)
-    static constexpr int MISC = (2 + NRS + NW - 1) / NW;
-    // one stage (three in flight), filled by DMA: C rows, B rows, C B^T
-    // fragments, raw x and the decay records (kVecRec floats in 1 KB slots)
-    // of one block
+    // one stage, filled by DMA: C rows, B rows, C B^T fragments, raw x and
+    // the decay records (kVecRec floats in 1 KB slots) of one block; then
+    // the block's y for the producer: 32 rows of XRB bytes, 16-byte chunk c
+    // of row t in slot c ^ (t & (XC - 1))
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
     static constexpr int XR = CBF + 2048;
     static constexpr int VR = XR + kBlk * XRB;
-    // y of the block for the producer: 32 rows of XRB bytes, 16-byte chunk
-    // c of row t in slot c ^ (t & (XC - 1))
     static constexpr int YS = VR + 1024 * NRS;
-    static constexpr int STG = YS + (PROD ? kBlk * XRB : 0);
+    static constexpr int STG = YS + kBlk * XRB;
     // floats of the decay record
     enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
-    // stages in flight: the DMAs of a block go out NST - 1 blocks ahead of
-    // its use
-    static constexpr int NST = 3;
+    // stages: the DMAs of a block go out NST - 1 blocks ahead of its use.
+    // With four stages (64 and 128 columns) a block's stage is complete one
+    // block early, and the operands that open a block are read during the
+    // block before it (PF).
+    static constexpr int NST = PB >= 64 ? 4 : 3;
+    static constexpr bool PF = NST == 4;
+    // K-step rows m of the C fragments among the opening operands (within
+    // the 256 registers per lane that two waves on a SIMD leave each)
+    static constexpr int ECF = PB == 128 ? 1 : 2;
     static constexpr int LDS = NST * STG;
-    // DMAs every wave issues in every block, all with every lane active
-    static constexpr int VM_LOADS = 2 * CBD + XD + MISC;
-    static constexpr int Y_STORES = 2;                 // y stores per wave and block
     static_assert(PB == 32 || PB == 64 || PB == 128, "one, two or four waves");
-    static_assert(XD == 2, "x DMAs");
     static_assert(STG % 16 == 0, "alignment");
     // (two 32-column workgroups fit a compute unit; wider ones run one per
     // compute unit, which the column choice arranges)
     static_assert(PB == 32 ? 2 * LDS <= 160 * 1024 : LDS <= 160 * 1024, "LDS per compute unit");
-    // the end-of-block wait: younger than the DMAs of the next block are the
-    // DMAs of the NST - 2 blocks after it and the y stores of NST - 2 blocks
-    static constexpr int VM_WAIT = (NST - 2) * (VM_LOADS + Y_STORES);
-    static_assert(VM_WAIT < 64, "vmcnt immediate");
     // the producer's DMAs of a block (C and B, x, C B^T halves, records) and
-    // y stores, and its end-of-block wait: younger than the DMAs of the next
-    // block are the y stores issued after them, the DMAs of the block after
-    // and this block's y stores
+    // y stores.  At the end of block kb it waits for the DMAs of block
+    // kb + 1 (kb + 2 with PF); younger than those are the y stores issued
+    // right after them and the DMAs and y stores of the NST - 2 - PF blocks
+    // after
     static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 2 + NRS;
     static constexpr int P_STORES = kBlk * XRB / 1024;
-    static constexpr int P_WAIT = P_STORES + (NST - 2) * (P_LOADS + P_STORES);
-    static_assert(!PROD || P_WAIT < 64, "vmcnt immediate");
+    static constexpr int P_WAIT = P_STORES + (NST - 2 - (PF ? 1 : 0)) * (P_LOADS + P_STORES);
+    static_assert(P_WAIT < 64, "vmcnt immediate");
 };
 
 template <int PB>
@@ -215,16 +206,20 @@ struct Book {
     bool rescale;   // restart the scale: h~ *= sig_in, sigma_in = 1 (factored blocks only)
 };
 
-// Bookkeeping of a block from its decay record and the sigma entering it.
-__device__ __forceinline__ Book book_of(const float *rec, float sig_in) {
+// Bookkeeping of a block from its decay record's delta and factored flag
+// (the same in every lane) and the sigma entering it.
+__device__ __forceinline__ Book book_of(float dl, float fc, float sig_in) {
     Book bk;
     bk.sig_in = sig_in;
-    bk.delta = uniform(rec[kVecRec - 4]);
-    bk.fac = uniform(rec[kVecRec - 3]) != 0.f;
+    bk.delta = uniform(dl);
+    bk.fac = uniform(fc) != 0.f;
     const float p = sig_in * bk.delta;
     bk.rescale = bk.fac && p < kRescale;
     bk.sig = bk.fac ? (bk.rescale ? bk.delta : p) : 1.f;
     return bk;
+}
+__device__ __forceinline__ Book book_of(const float *rec, float sig_in) {
+    return book_of(rec[kVecRec - 4], rec[kVecRec - 3], sig_in);
 }
 
 // MFMA operands of v_mfma_f32_32x32x16_bf16: lane l holds row (A) / column
@@ -276,108 +271,112 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     const int HP = H * P, GN = G * N;
     const int c0 = blockIdx.x * PB, b = blockIdx.y;
     const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = (NW == 1 && !S::PROD) ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
 
     auto stage = [&](int i) -> unsigned char * {
         return i == 0 ? stg0 : (i == 1 ? stg1 : (i == 2 ? stg2 : stg3));
     };
-    // Buffer resources over this workgroup's slices of C, B, x, the C B^T
-    // blocks and the decay records, built once.  The DMAs of a block add the
-    // block's byte offset to fixed per-lane offsets; rows past the end of the
-    // sequence (the ragged tail, and the prefetches past the last block) fall
-    // outside a resource's range, and the hardware reads them as zeros.
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
-        (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
-    // the records of the workgroup's heads (consecutive (batch, head) rows)
-    const int h0 = c0 / P;
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
-        kBufferWord3);
-    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
-    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
-    typedef __attribute__((address_space(3))) void lds_void;
-    auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
-    };
-    // y through a buffer resource over this batch's rows: the stores of
-    // tokens past the end fall outside it and are dropped by the hardware
-    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
 
-    if constexpr (S::PROD) {
-        if (wave == NW) {
-            // ---- the producer wave: every DMA of the stages and every y
-            // store.  Per-lane offsets: C / B rows 4 i + lane / 16 and x rows
-            // (64 i + lane) / XC of DMA i; y row (64 i + lane) / XC, chunk
-            // (64 i + lane) % XC of store i.
-            constexpr int NCB = S::MAT / 1024, NXD = kBlk * S::XRB / 1024;
-            unsigned pcb[NCB], px[NXD];
+    if (wave == NW) {
+        // ---- the producer wave: every DMA of the stages and every y store.
+        // Buffer resources over the workgroup's slices of C, B, x, the C B^T
+        // blocks, the decay records and y, built once; a block adds its byte
+        // offset to fixed per-lane offsets.  Rows past the end of the
+        // sequence (the ragged tail, and the prefetches past the last block)
+        // fall outside a resource's range: the hardware reads them as zeros
+        // and drops such stores.
+        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
+            (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
+        // the records of the workgroup's heads (consecutive (batch, head) rows)
+        const int h0 = c0 / P;
+        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
+            kBufferWord3);
+        const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
+            y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+        const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
+        const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
+        typedef __attribute__((address_space(3))) void lds_void;
+        auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
+        };
+        // Per-lane offsets: C / B rows 4 i + lane / 16 and x rows
+        // (64 i + lane) / XC of DMA i; y row (64 i + lane) / XC, chunk
+        // (64 i + lane) % XC of store i.
+        constexpr int NCB = S::MAT / 1024, NXD = kBlk * S::XRB / 1024;
+        unsigned pcb[NCB], px[NXD];
+#pragma unroll
+        for (int i = 0; i < NCB; ++i) {
+            const int row = 4 * i + (lane >> 4);
+            pcb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
+        }
+#pragma unroll
+        for (int i = 0; i < NXD; ++i) {
+            const int pos = 64 * i + lane, row = pos / S::XC;
+            px[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
+        }
+        auto pdma = [&](int kb, unsigned char *buf) {
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
-                const int row = 4 * i + (lane >> 4);
-                pcb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
+                bdma(rc, pcb[i] + kb * cb_step, buf + S::CS + 1024 * i);
+                bdma(rb, pcb[i] + kb * cb_step, buf + S::BS + 1024 * i);
             }
 #pragma unroll
-            for (int i = 0; i < NXD; ++i) {
-                const int pos = 64 * i + lane, row = pos / S::XC;
-                px[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
+            for (int i = 0; i < NXD; ++i) bdma(rx, px[i] + kb * x_step, buf + S::XR + 1024 * i);
+#pragma unroll
+            for (int pc = 0; pc < 2; ++pc)
+                bdma(rcb, 16 * (64 * pc + lane) + kb * cbf_step, buf + S::CBF + 1024 * pc);
+#pragma unroll
+            for (int q = 0; q < S::NRS; ++q)
+                bdma(rv, 16 * lane + (q * nblk + kb) * v_step, buf + S::VR + 1024 * q);
+        };
+        auto pstore = [&](int kb, const unsigned char *buf) {
+#pragma unroll
+            for (int i = 0; i < S::P_STORES; ++i) {
+                const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
+                                                                 16 * (c ^ (t & (S::XC - 1))));
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
             }
-            auto pdma = [&](int kb, unsigned char *buf) {
+        };
 #pragma unroll
-                for (int i = 0; i < NCB; ++i) {
-                    bdma(rc, pcb[i] + kb * cb_step, buf + S::CS + 1024 * i);
-                    bdma(rb, pcb[i] + kb * cb_step, buf + S::BS + 1024 * i);
-                }
-#pragma unroll
-                for (int i = 0; i < NXD; ++i) bdma(rx, px[i] + kb * x_step, buf + S::XR + 1024 * i);
-#pragma unroll
-                for (int pc = 0; pc < 2; ++pc)
-                    bdma(rcb, 16 * (64 * pc + lane) + kb * cbf_step, buf + S::CBF + 1024 * pc);
-#pragma unroll
-                for (int q = 0; q < S::NRS; ++q)
-                    bdma(rv, 16 * lane + (q * nblk + kb) * v_step, buf + S::VR + 1024 * q);
-            };
-            auto pstore = [&](int kb, const unsigned char *buf) {
-#pragma unroll
-                for (int i = 0; i < S::P_STORES; ++i) {
-                    const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
-                    const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
-                                                                     16 * (c ^ (t & (S::XC - 1))));
-                    __builtin_amdgcn_raw_buffer_store_b128(
-                        v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
-                }
-            };
-#pragma unroll
-            for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i));
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i));
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        lds_barrier();
+        // block kb: refill the stage block kb - 1 used, store its y, then
+        // wait for the DMAs of block kb + 1 (kb + 2 with PF) before the
+        // end-of-block barrier
+        auto pblock = [&](int kb, const int si) {
+            pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
+            if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+            __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
             lds_barrier();
-            // block kb: refill the stage block kb - 1 used, store its y, then
-            // wait for the DMAs of block kb + 1 before the end-of-block barrier
-            auto pblock = [&](int kb, const int si) {
-                pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
-                if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
-                __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
-                lds_barrier();
-            };
-            for (int kb = 0; kb < nblk; kb += 3) {
-                pblock(kb, 0);
-                if (kb + 1 < nblk) {
-                    pblock(kb + 1, 1);
-                    if (kb + 2 < nblk) pblock(kb + 2, 2);
+        };
+        for (int kb = 0; kb < nblk; kb += S::NST) {
+            pblock(kb, 0);
+            if (kb + 1 < nblk) {
+                pblock(kb + 1, 1);
+                if (kb + 2 < nblk) {
+                    pblock(kb + 2, 2);
+                    if constexpr (S::NST > 3) {
+                        if (kb + 3 < nblk) pblock(kb + 3, 3);
+                    }
                 }
             }
-            pstore(nblk - 1, stage((nblk - 1) % S::NST));
-            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-            return;
         }
+        pstore(nblk - 1, stage((nblk - 1) % S::NST));
+        // no DMA may land in LDS after the workgroup ends
+        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        return;
     }
 
     const int r = lane & 31, hi = lane >> 5;
@@ -451,53 +450,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         }
     }
 
-    // per-lane byte offsets of the C / B rows and of the raw x rows (block 0)
-    unsigned dma_cb[S::CBD], dma_x[S::XD];
-#pragma unroll
-    for (int i = 0; i < S::CBD; ++i) {
-        const int row = 4 * (wave + NW * i) + (lane >> 4);
-        dma_cb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
-    }
-#pragma unroll
-    for (int i = 0; i < S::XD; ++i) {
-        const int pos = 64 * (wave + NW * i) + lane, row = pos / S::XC;
-        dma_x[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
-    }
-    // DMA j (0 <= j < VM_LOADS) of block kb into stage `buf`: C and B rows
-    // (alternating), raw x, then this wave's share of the C B^T halves and
-    // the decay records
-    auto dma_piece = [&](int kb, unsigned char *buf, int j) {
-        if (j < 2 * S::CBD) {
-            const int i = j >> 1;
-            const unsigned o = dma_cb[i] + kb * cb_step;
-            if (j & 1)
-                bdma(rb, o, buf + S::BS + 1024 * (wave + NW * i));
-            else
-                bdma(rc, o, buf + S::CS + 1024 * (wave + NW * i));
-        } else if (j < 2 * S::CBD + S::XD) {
-            const int i = j - 2 * S::CBD;
-            bdma(rx, dma_x[i] + kb * x_step, buf + S::XR + 1024 * (wave + NW * i));
-        } else {
-            // piece pc (wave-uniform): selects, not a branch, so every wave
-            // runs the same instruction stream
-            int pc = wave + NW * (j - 2 * S::CBD - S::XD);
-            if (pc >= 2 + S::NRS) pc = 2 + (pc - 2) % S::NRS;
-            const bool half = pc < 2;
-            const int rsl = half ? 0 : pc - 2;
-            // a C B^T half, or 1 KB from a record start (the record and
-            // slack after it)
-            bdma(half ? rcb : rv,
-                 half ? 16 * (64 * pc + lane) + kb * cbf_step
-                      : 16 * lane + (rsl * nblk + kb) * v_step,
-                 buf + (half ? S::CBF + 1024 * pc : S::VR + 1024 * rsl));
-        }
-    };
-    auto dma_block = [&](int kb, unsigned char *buf) {
-#pragma unroll
-        for (int j = 0; j < S::VM_LOADS; ++j) dma_piece(kb, buf, j);
-    };
-    const int y_boff = (r * HP + cw + 8 * hi) * 2;
-    // staging slots of this lane's two 16-byte runs (row r, chunks
+    // staging slots of this lane's two 16-byte runs of y (row r, chunks
     // 4 wave + 2 i + hi of the workgroup's row)
     int ys_off[2];
 #pragma unroll
@@ -511,53 +464,57 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             *reinterpret_cast<u32x4 *>(cur + ys_off[i]) = v;
         }
     };
-    auto y_store = [&](int kb, const f32x16 &acc) {
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-            const u32x4 v = {pack2(acc[8 * i], acc[8 * i + 1]), pack2(acc[8 * i + 2], acc[8 * i + 3]),
-                             pack2(acc[8 * i + 4], acc[8 * i + 5]), pack2(acc[8 * i + 6], acc[8 * i + 7])};
-            __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, y_boff + kb * kBlk * HP * 2 + 32 * i,
-                                                   0, 0);
-        }
-    };
 
-    // ---- prologue.  Every global read in the loop is a DMA into LDS issued
-    // NST - 1 blocks ahead of its use (NST stages): C / B rows, C B^T, raw x
-    // and the decay records of a block.  Every block issues the same global
-    // memory instructions (those past the last block read zeros).
-    if constexpr (!S::PROD) {
-#pragma unroll
-        for (int i = 0; i < S::NST - 1; ++i) dma_block(i, stage(i));
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+    // ---- prologue: the producer's DMAs of the first blocks have landed
     lds_barrier();
     float sig_out = 1.f;  // sigma after the previous block
 
-    // The operands of block kb from stage `cur` (requested before any use)
+    // The operands that open a block (with PF read from its stage during the
+    // block before): the decay-record fields of the bookkeeping, cf and
+    // exp(lambda_r - lambda_e), raw x^T and the C fragments of the first
+    // 2 ECF K-steps.
+    constexpr int ECF = S::ECF;
+    struct Early {
+        f32x4 cfv[4];        // cf of tokens 16 kk + 8 hi + 0..7
+        bf16x8 xs[2];        // raw x^T, K-steps 0 and 1
+        bf16x8 cfr[ECF][2];  // C fragments of y^T = h~ C^T, K-steps (m, u), m < ECF
+        float rpv;           // exp(lambda_r - lambda_e)
+        float dl, fc;        // the record's delta and factored flag (uniform)
+    };
+    // The rest of a block's operands, read from its stage during the block.
     struct Ops {
-        bf16x8 cfr[4][2];  // C fragments of y^T = h~ C^T, K-step (m, u)
-        bf16x8 xs[2];      // raw x^T, K-steps 0 and 1
-        f32x4 cfv[4];      // cf of tokens 16 kk + 8 hi + 0..7
+        bf16x8 cfr[4 - ECF][2];  // C fragments, K-steps (m, u), m >= ECF
         bf16x8 cbv[2];     // causal diagonal block of C B^T, K-steps 0 and 1
         bf16x8 bt[4][2];   // B^T fragments of the state update, tile m, K-step kk
+        bf16x8 xr[2];      // raw x of the skip term (read for the epilogue)
     };
-    auto load_ops = [&](const unsigned char *cur, Ops &o) {
-        const float *v = reinterpret_cast<const float *>(cur + rec_off);
+    auto load_early = [&](const unsigned char *buf, Early &e) {
+        const float *v = reinterpret_cast<const float *>(buf + rec_off);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
             for (int w4 = 0; w4 < 2; ++w4)
-                o.cfv[2 * kk + w4] =
+                e.cfv[2 * kk + w4] =
                     *reinterpret_cast<const f32x4 *>(v + S::CF + 16 * kk + 8 * hi + 4 * w4);
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+        for (int kk = 0; kk < 2; ++kk)
+            e.xs[kk] = join(lds_tr(buf, S::XR + xs_tr[0] + 16 * S::XRB * kk),
+                            lds_tr(buf, S::XR + xs_tr[1] + 16 * S::XRB * kk));
+#pragma unroll
+        for (int m = 0; m < ECF; ++m)
 #pragma unroll
             for (int u = 0; u < 2; ++u)
-                o.cfr[m][u] = lds_b128(cur, S::CS + c_rd[m & 1][u] + 128 * (m >> 1));
+                e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[m & 1][u] + 128 * (m >> 1));
+        e.rpv = v[S::RP + r];
+        e.dl = v[S::DELTA];
+        e.fc = v[S::FLAG];
+    };
+    auto load_late = [&](const unsigned char *cur, Ops &o) {
 #pragma unroll
-        for (int kk = 0; kk < 2; ++kk)
-            o.xs[kk] = join(lds_tr(cur, S::XR + xs_tr[0] + 16 * S::XRB * kk),
-                            lds_tr(cur, S::XR + xs_tr[1] + 16 * S::XRB * kk));
+        for (int m = ECF; m < 4; ++m)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+                o.cfr[m - ECF][u] = lds_b128(cur, S::CS + c_rd[m & 1][u] + 128 * (m >> 1));
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) o.cbv[kk] = lds_b128(cur, S::CBF + 1024 * kk + cbf_rd);
     };
@@ -569,24 +526,22 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                            lds_tr(cur, S::BS + b_tr[1][m & 1] + off));
     };
 
-    // block kb, si = kb % 3 (a literal in each unrolled copy)
-    auto block = [&](int kb, const int si) {
+    // block kb from stage si = kb % NST (a literal in each unrolled copy);
+    // e holds its opening operands, nx receives those of block kb + 1 (PF)
+    auto block = [&](int kb, const int si, Early &e, Early &nx) {
         unsigned char *cur = stage(si);
         const float *v = reinterpret_cast<const float *>(cur + rec_off);
         // The block is written as a sequence of chunks fenced by scheduling
         // barriers: each chunk starts one MFMA and then issues vector work
         // that does not depend on it (the next state conversion and x'
-        // during y^T = h~ C^T; the epilogue and the DMAs of block kb + NST - 1
-        // during the state update), so ALU and memory issue overlap the
-        // matrix pipeline.  A rescaled or exact block edits the operands of
-        // the common path in place between the two phases.
-        const Book bk = book_of(v, sig_out);
+        // during y^T = h~ C^T; the epilogue and the reads of the next
+        // block's opening operands during the state update), so ALU and LDS
+        // issue overlap the matrix pipeline.  A rescaled or exact block edits
+        // the operands of the common path in place between the two phases.
+        if constexpr (!S::PF) load_early(cur, e);
         Ops o;
-        load_ops(cur, o);
-        const float rpv = v[S::RP + r];  // exp(lambda_r - lambda_e)
-        bf16x8 xr[2];                     // raw x of the skip term
-#pragma unroll
-        for (int i = 0; i < 2; ++i) xr[i] = lds_b128(cur, S::XR + xr_skip[i]);
+        load_late(cur, o);
+        const Book bk = book_of(e.dl, e.fc, sig_out);
         const float xscale = bk.fac ? __builtin_amdgcn_rcpf(bk.sig) : 1.f;
         auto hb_of = [&](int q) {  // bf16 A fragment of K-step q = 2 m + u
             bf16x8 hb;
@@ -599,9 +554,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         bf16x8 xp[2];
         auto xp_part = [&](int q) {
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const int kk = q >> 2, j = 2 * (q & 3) + e;
-                xp[kk][j] = (bf16)((float)o.xs[kk][j] * (o.cfv[2 * kk + (j >> 2)][j & 3] * xscale));
+            for (int ee = 0; ee < 2; ++ee) {
+                const int kk = q >> 2, j = 2 * (q & 3) + ee;
+                xp[kk][j] = (bf16)((float)e.xs[kk][j] * (e.cfv[2 * kk + (j >> 2)][j & 3] * xscale));
             }
         };
         f32x16 acc;
@@ -611,7 +566,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
-            acc = mma32(hb, o.cfr[q >> 1][q & 1], acc);
+            acc = mma32(hb, (q >> 1) < ECF ? e.cfr[(q >> 1) % ECF][q & 1]
+                                           : o.cfr[((q >> 1) - ECF) & 3][q & 1], acc);
             __builtin_amdgcn_sched_barrier(0);
             if (q < 7) hb = hb_of(q + 1);
             xp_part(q);
@@ -621,7 +577,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         // (the empty asm consumes x' here, so no pass sinks its arithmetic
         // out of the chunks above)
         asm volatile("" : "+v"(xp[0]), "+v"(xp[1]));
-        float f = rpv * bk.sig, dco = Dh;
+        float f = e.rpv * bk.sig, dco = Dh;
         if (bk.rescale) {
             // restart of the scale (sigma would fall below exp(-60)): the
             // state and its output so far move to sigma_in = 1
@@ -649,7 +605,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                                         v[S::DT + s] + (s == r ? Dh : 0.f);
                     wgt[j] = (bf16)(s <= r ? w : 0.f);
                 }
-                acc = mma32(o.xs[kk], wgt, acc);
+                acc = mma32(e.xs[kk], wgt, acc);
                 // the common diagonal product below then adds zeros
                 o.cbv[kk] = zero_frag<bf16>();
             }
@@ -660,76 +616,61 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             for (int m = 0; m < 4; ++m) st[m] *= sd;
         }
         __builtin_amdgcn_sched_barrier(0);
+        // (raw x of the skip term, read here for the epilogue)
+#pragma unroll
+        for (int i = 0; i < 2; ++i) o.xr[i] = lds_b128(cur, S::XR + xr_skip[i]);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) acc = mma32(xp[kk], o.cbv[kk], acc);
         __builtin_amdgcn_sched_barrier(0);
         // state update h~ += B^T x' (K-step 0 of every tile, then K-step 1),
-        // with the epilogue (from the third chunk on, once the diagonal
-        // product has landed) and the DMAs of block kb + NST - 1
-        {
-            unsigned char *nbuf = stage((si + S::NST - 1) % S::NST);
-            int j = 0;
+        // with the reads of the next block's opening operands (PF) and the
+        // epilogue (from the third chunk on, once the diagonal product has
+        // landed)
 #pragma unroll
-            for (int q = 0; q < 8; ++q) {
-                const int kk = q >> 2, m = q & 3;
-                st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
-                __builtin_amdgcn_sched_barrier(0);
-                if constexpr (!S::PROD) {
-                    const int jn = (S::VM_LOADS * (q + 1)) / 8;
-                    for (; j < jn; ++j) dma_piece(kb + S::NST - 1, nbuf, j);
-                }
-                if (q >= 2) {
-                    // acc[vv] for the vv with vv * 6 / 16 == q - 2 (the
-                    // empty asm keeps them in this chunk)
-#pragma unroll
-                    for (int vv = 0; vv < 16; ++vv)
-                        if (vv * 6 / 16 == q - 2)
-                            acc[vv] = acc[vv] * f + dco * (float)xr[vv >> 3][vv & 7];
-                    asm volatile("" : "+v"(acc));
-                }
-                __builtin_amdgcn_sched_barrier(0);
+        for (int q = 0; q < 8; ++q) {
+            const int kk = q >> 2, m = q & 3;
+            st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
+            __builtin_amdgcn_sched_barrier(0);
+            if constexpr (S::PF) {
+                if (q == 0) load_early(stage((si + 1) % S::NST), nx);
             }
+            if (q >= 2) {
+                // acc[vv] for the vv with vv * 6 / 16 == q - 2 (the
+                // empty asm keeps them in this chunk)
+#pragma unroll
+                for (int vv = 0; vv < 16; ++vv)
+                    if (vv * 6 / 16 == q - 2)
+                        acc[vv] = acc[vv] * f + dco * (float)o.xr[vv >> 3][vv & 7];
+                asm volatile("" : "+v"(acc));
+            }
+            __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("" : "+v"(acc));
         sig_out = bk.sig;
         __builtin_amdgcn_sched_barrier(0);
-
-        if constexpr (S::PROD) {
-            // y of the block to the producer through this stage's staging
-            // rows; the barrier then also publishes it
-            y_stage(cur, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            lds_barrier();
-        } else {
-            // -------- the DMAs of the next block have landed once at most
-            // this block's DMAs and the previous block's y stores are in
-            // flight (vector memory operations complete in issue order);
-            // then this block's y stores, and the barrier after which every
-            // wave's DMAs of the next block are visible and this stage may
-            // be refilled
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_WAIT));
-            __builtin_amdgcn_sched_barrier(0);
-            y_store(kb, acc);
-            __builtin_amdgcn_sched_barrier(0);
-            block_barrier();
-        }
+        // y of the block to the producer through this stage's staging rows;
+        // the barrier then also publishes it
+        y_stage(cur, acc);
+        __builtin_amdgcn_sched_barrier(0);
+        lds_barrier();
     };
 
     // unrolled by the stage count, so that every stage address is a literal
+    // (and with PF the two sets of opening operands alternate)
+    Early ea, eb;
+    if constexpr (S::PF) load_early(stage(0), ea);
     for (int kb = 0; kb < nblk; kb += S::NST) {
-        block(kb, 0);
+        block(kb, 0, ea, eb);
         if (kb + 1 < nblk) {
-            block(kb + 1, 1);
+            block(kb + 1, 1, eb, ea);
             if (kb + 2 < nblk) {
-                block(kb + 2, 2);
+                block(kb + 2, 2, ea, eb);
                 if constexpr (S::NST > 3) {
-                    if (kb + 3 < nblk) block(kb + 3, 3);
+                    if (kb + 3 < nblk) block(kb + 3, 3, eb, ea);
                 }
             }
         }
     }
-    // no DMA may land in LDS after the workgroup ends
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
 
     if (final_state) {
 #pragma unroll
@@ -1247,15 +1188,16 @@ static bool use_wave16(const ForwardArgs &a) {
     return env && strcmp(env, "16") == 0;
 }
 
-// Columns per workgroup.  One workgroup per compute unit is the target:
-// 128 columns (four waves over two heads of one B/C group, which share the
-// staged C and B rows) once 64-column workgroups would outnumber the 256
-// compute units; 64 (two waves) while those still cover them; else 32 (one
-// wave) for more workgroups.
+// Columns per workgroup.  One workgroup per compute unit is the target
+// (two 32-column workgroups on one compute unit slow each other down more
+// than one 64-column workgroup's two waves do): 128 columns (four waves over
+// two heads of one B/C group, which share the staged C and B rows) once
+// 64-column workgroups would outnumber the 256 compute units; 64 (two
+// waves) once 32-column ones would; else 32 (one wave).
 static int pick_pb(const ForwardArgs &a) {
     const long cols = (long)a.batch * a.H * a.P;
     if (a.P == 64 && a.H % 2 == 0 && (a.H / a.G) % 2 == 0 && cols / 64 > 256) return 128;
-    if (a.P % 64 == 0 && cols / 64 >= 256) return 64;
+    if (a.P % 64 == 0 && cols / 32 > 256) return 64;
     return 32;
 }
 

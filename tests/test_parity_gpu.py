@@ -112,6 +112,10 @@ SMALL = [
     # more 64-column workgroups than compute units: the fused path's
     # four-wave layout over two heads of one group (ragged tail)
     (2, 200, 132, 64, 128, 2, 64, "bf16", True),
+    # more 32-column workgroups than compute units: the two-wave layout,
+    # also with an odd head count
+    (2, 300, 66, 64, 128, 1, 64, "bf16", True),
+    (1, 130, 129, 64, 128, 1, 64, "bf16", False),
 ]
 
 
@@ -150,7 +154,7 @@ def decay_regime_inputs(io, seed, H=4):
     return inp
 
 
-@pytest.mark.parametrize("io,H", [("bf16", 4), ("f32", 4), ("bf16", 132)])
+@pytest.mark.parametrize("io,H", [("bf16", 4), ("f32", 4), ("bf16", 66), ("bf16", 132)])
 def test_decay_regimes(dev, oracle_mod, path, io, H):
     inp = decay_regime_inputs(io, seed=91, H=H)
     lam = inp["dt"][0, : 384].reshape(12, 32, H).sum(1) * inp["A"][None, :]
