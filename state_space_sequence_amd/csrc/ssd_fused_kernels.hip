@@ -139,10 +139,11 @@ struct Fused {
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
     static constexpr int XRB = 2 * PB;                 // raw x row bytes
     static constexpr int NRS = PB == 128 ? 2 : 1;      // decay-record slots (heads)
-    // one stage, filled by DMA: C rows, B rows, C B^T fragments, raw x and
-    // the decay records (kVecRec floats in 1 KB slots) of one block; then
-    // the block's y for the producer: 32 rows of XRB bytes, 16-byte chunk c
-    // of row t in slot c ^ (t & (XC - 1))
+    // one stage, filled by DMA: C rows, B rows (column-blocked, blk_off),
+    // C B^T fragments, raw x (column-blocked) and the decay records (kVecRec
+    // floats in 1 KB slots) of one block; then the block's y for the
+    // producer: 32 rows of XRB bytes, 16-byte chunk c of row t in slot
+    // c ^ ys_swz(t)
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
@@ -180,6 +181,23 @@ struct Fused {
 
 template <int PB>
 __device__ __forceinline__ int x_swz(int row) { return PB >= 64 ? row_swz(row) : row_swz4(row); }
+
+// Column-blocked LDS layout of the staged C, B and x tiles (32 rows): the
+// 16-byte chunk c of row t sits at byte blk_off(t, c), so each block of four
+// chunks (32 bf16 columns) is a 2 KB region of 32 rows x 64 bytes, and the
+// chunks of a row are rotated by an XOR with (t / 4) % 4.  Over the 64-bank
+// LDS (256 bytes per cycle) the fragment reads (16 consecutive rows, one
+// chunk each) then hit 16 distinct 16-byte bank groups, the transposed reads
+// (4 consecutive rows from a multiple of 4, the same 2 or 4 chunks each) hit
+// distinct ones too, and moving to another column block or 16 rows further
+// is a constant offset (2048 and 1024 bytes).
+__device__ __forceinline__ int blk_off(int t, int c) {
+    return 2048 * (c >> 2) + 64 * t + 16 * ((c & 3) ^ ((t >> 2) & 3));
+}
+// Staging slot of chunk c of y row t (XC chunks per row, rows contiguous):
+// c ^ ys_swz(t) spreads 16 consecutive rows over distinct bank groups.
+template <int XC>
+__device__ __forceinline__ int ys_swz(int t) { return (t / (16 / XC)) & (XC - 1); }
 
 // Workgroup barrier for LDS only: this wave's LDS reads and writes complete
 // (lgkmcnt(0)), then s_barrier; the asm "memory" clobber keeps the compiler
@@ -308,20 +326,22 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
         };
-        // Per-lane offsets: C / B rows 4 i + lane / 16 and x rows
-        // (64 i + lane) / XC of DMA i; y row (64 i + lane) / XC, chunk
-        // (64 i + lane) % XC of store i.
+        // Per-lane offsets.  DMA i fills the 1 KB at 1024 i of a
+        // column-blocked tile: column block i / 2, rows 16 (i % 2) + lane / 4,
+        // slot lane % 4 (so chunk 4 (i / 2) + ((lane % 4) ^ ((t / 4) % 4)) of
+        // row t).  Store i takes y row (64 i + lane) / XC, chunk
+        // (64 i + lane) % XC.
         constexpr int NCB = S::MAT / 1024, NXD = kBlk * S::XRB / 1024;
         unsigned pcb[NCB], px[NXD];
 #pragma unroll
         for (int i = 0; i < NCB; ++i) {
-            const int row = 4 * i + (lane >> 4);
-            pcb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
+            const int t = 16 * (i & 1) + (lane >> 2);
+            pcb[i] = t * GN * 2 + 16 * (4 * (i >> 1) + ((lane & 3) ^ ((t >> 2) & 3)));
         }
 #pragma unroll
         for (int i = 0; i < NXD; ++i) {
-            const int pos = 64 * i + lane, row = pos / S::XC;
-            px[i] = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
+            const int t = 16 * (i & 1) + (lane >> 2);
+            px[i] = t * HP * 2 + 16 * (4 * (i >> 1) + ((lane & 3) ^ ((t >> 2) & 3)));
         }
         auto pdma = [&](int kb, unsigned char *buf) {
 #pragma unroll
@@ -343,7 +363,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             for (int i = 0; i < S::P_STORES; ++i) {
                 const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
-                                                                 16 * (c ^ (t & (S::XC - 1))));
+                                                                 16 * (c ^ ys_swz<S::XC>(t)));
                 __builtin_amdgcn_raw_buffer_store_b128(
                     v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
             }
@@ -390,43 +410,30 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     // transposed reads, which act within each 16-lane group)
     const int a4 = lane & 3, e4 = (lane >> 2) & 3, g1 = (lane >> 4) & 1;
     // C fragment of K-step (m, u): token r, chunk 4 m + 2 u + hi:
-    //   CS + c_rd[m & 1][u] + 128 (m >> 1)
-    int c_rd[2][2];
-    {
-        const int sw = row_swz(r);
+    //   CS + c_rd[u] + 2048 m
+    int c_rd[2];
 #pragma unroll
-        for (int mb = 0; mb < 2; ++mb)
-#pragma unroll
-            for (int u = 0; u < 2; ++u)
-                c_rd[mb][u] = r * S::ROWB + 16 * ((4 * mb + 2 * u + hi) ^ sw);
-    }
+    for (int u = 0; u < 2; ++u) c_rd[u] = blk_off(r, 2 * u + hi);
     // B^T, state tile m, K-step kk, token half s: token 16 kk + 8 hi + 4 s + e4,
     // n-quad 8 m + 4 g1 + 2 (a4 & 1) + (a4 >> 1):
-    //   BS + b_tr[s][m & 1] + 128 (m >> 1) + 4096 kk
-    int b_tr[2][2];
+    //   BS + b_tr[s] + 2048 m + 1024 kk
+    int b_tr[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-#pragma unroll
-        for (int mb = 0; mb < 2; ++mb) {
-            const int t = 8 * hi + 4 * s + e4;
-            b_tr[s][mb] = t * S::ROWB + 16 * ((4 * mb + 2 * g1 + (a4 & 1)) ^ row_swz(t)) +
-                          8 * (a4 >> 1);
-        }
-    // raw x: chunk c of token row t sits at XR + xr_off(t, c)
-    auto xr_off = [](int t, int c) { return t * S::XRB + 16 * (c ^ x_swz<PB>(t)); };
+        b_tr[s] = blk_off(8 * hi + 4 * s + e4, 2 * g1 + (a4 & 1)) + 8 * (a4 >> 1);
     // x^T fragment of K-step kk, token half s: token 16 kk + 8 hi + 4 s + e4,
     // for lanes 16 g1 + 4 a4 + (0..3) (MFMA columns q = 16 g1 + 4 a4 + c)
     // the wave's columns 16 g1 + 8 (a4 & 1) + 4 (a4 >> 1) + (0..3) =
-    // col_of(q):  XR + xs_tr[s] + 16 XRB kk
+    // col_of(q):  XR + xs_tr[s] + 1024 kk
     int xs_tr[2];
 #pragma unroll
     for (int s = 0; s < 2; ++s)
-        xs_tr[s] = xr_off(8 * hi + 4 * s + e4, 4 * wave + 2 * g1 + (a4 & 1)) + 8 * (a4 >> 1);
+        xs_tr[s] = blk_off(8 * hi + 4 * s + e4, 4 * wave + 2 * g1 + (a4 & 1)) + 8 * (a4 >> 1);
     // raw x of the skip term: token r, the wave's columns 8 hi + (0..7) and
     // 16 + 8 hi + (0..7)
     int xr_skip[2];
 #pragma unroll
-    for (int i = 0; i < 2; ++i) xr_skip[i] = xr_off(r, 4 * wave + 2 * i + hi);
+    for (int i = 0; i < 2; ++i) xr_skip[i] = blk_off(r, 4 * wave + 2 * i + hi);
     const int pr = pw + col_of(r);
     const int cbf_rd = lane * 16;
     const int rec_off = S::VR + 1024 * slot;
@@ -455,7 +462,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     int ys_off[2];
 #pragma unroll
     for (int i = 0; i < 2; ++i)
-        ys_off[i] = S::YS + r * S::XRB + 16 * ((4 * wave + 2 * i + hi) ^ (r & (S::XC - 1)));
+        ys_off[i] = S::YS + r * S::XRB + 16 * ((4 * wave + 2 * i + hi) ^ ys_swz<S::XC>(r));
     auto y_stage = [&](unsigned char *cur, const f32x16 &acc) {
 #pragma unroll
         for (int i = 0; i < 2; ++i) {
@@ -498,13 +505,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                     *reinterpret_cast<const f32x4 *>(v + S::CF + 16 * kk + 8 * hi + 4 * w4);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
-            e.xs[kk] = join(lds_tr(buf, S::XR + xs_tr[0] + 16 * S::XRB * kk),
-                            lds_tr(buf, S::XR + xs_tr[1] + 16 * S::XRB * kk));
+            e.xs[kk] = join(lds_tr(buf, S::XR + xs_tr[0] + 1024 * kk),
+                            lds_tr(buf, S::XR + xs_tr[1] + 1024 * kk));
 #pragma unroll
         for (int m = 0; m < ECF; ++m)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[m & 1][u] + 128 * (m >> 1));
+            for (int u = 0; u < 2; ++u) e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[u] + 2048 * m);
         e.rpv = v[S::RP + r];
         e.dl = v[S::DELTA];
         e.fc = v[S::FLAG];
@@ -513,17 +519,15 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
         for (int m = ECF; m < 4; ++m)
 #pragma unroll
-            for (int u = 0; u < 2; ++u)
-                o.cfr[m - ECF][u] = lds_b128(cur, S::CS + c_rd[m & 1][u] + 128 * (m >> 1));
+            for (int u = 0; u < 2; ++u) o.cfr[m - ECF][u] = lds_b128(cur, S::CS + c_rd[u] + 2048 * m);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) o.cbv[kk] = lds_b128(cur, S::CBF + 1024 * kk + cbf_rd);
     };
     // B^T fragment q = 2 m + kk of the state update (read during y^T = h~ C^T)
     auto load_bt = [&](const unsigned char *cur, Ops &o, int q) {
         const int m = q >> 1, kk = q & 1;
-        const int off = 128 * (m >> 1) + 4096 * kk;
-        o.bt[m][kk] = join(lds_tr(cur, S::BS + b_tr[0][m & 1] + off),
-                           lds_tr(cur, S::BS + b_tr[1][m & 1] + off));
+        const int off = 2048 * m + 1024 * kk;
+        o.bt[m][kk] = join(lds_tr(cur, S::BS + b_tr[0] + off), lds_tr(cur, S::BS + b_tr[1] + off));
     };
 
     // block kb from stage si = kb % NST (a literal in each unrolled copy);
