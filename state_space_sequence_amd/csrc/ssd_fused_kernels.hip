@@ -323,8 +323,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
         const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
         typedef __attribute__((address_space(3))) void lds_void;
-        auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
+        // (the block's byte offset goes in the scalar offset, so a DMA
+        // costs no vector instruction)
+        auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, unsigned char *dst) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
         };
         // Per-lane offsets.  DMA i fills the 1 KB at 1024 i of a
         // column-blocked tile: column block i / 2, rows 16 (i % 2) + lane / 4,
@@ -344,28 +346,37 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             px[i] = t * HP * 2 + 16 * (4 * (i >> 1) + ((lane & 3) ^ ((t >> 2) & 3)));
         }
         auto pdma = [&](int kb, unsigned char *buf) {
+            const unsigned cbo = kb * cb_step, xo = kb * x_step, cbfo = kb * cbf_step,
+                           vo = kb * v_step;
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
-                bdma(rc, pcb[i] + kb * cb_step, buf + S::CS + 1024 * i);
-                bdma(rb, pcb[i] + kb * cb_step, buf + S::BS + 1024 * i);
+                bdma(rc, pcb[i], cbo, buf + S::CS + 1024 * i);
+                bdma(rb, pcb[i], cbo, buf + S::BS + 1024 * i);
             }
 #pragma unroll
-            for (int i = 0; i < NXD; ++i) bdma(rx, px[i] + kb * x_step, buf + S::XR + 1024 * i);
+            for (int i = 0; i < NXD; ++i) bdma(rx, px[i], xo, buf + S::XR + 1024 * i);
 #pragma unroll
             for (int pc = 0; pc < 2; ++pc)
-                bdma(rcb, 16 * (64 * pc + lane) + kb * cbf_step, buf + S::CBF + 1024 * pc);
+                bdma(rcb, 16 * (64 * pc + lane), cbfo, buf + S::CBF + 1024 * pc);
 #pragma unroll
             for (int q = 0; q < S::NRS; ++q)
-                bdma(rv, 16 * lane + (q * nblk + kb) * v_step, buf + S::VR + 1024 * q);
+                bdma(rv, 16 * lane + q * nblk * v_step, vo, buf + S::VR + 1024 * q);
         };
+        // per-lane y offsets and LDS staging slots of the stores
+        unsigned py[S::P_STORES];
+        int pys[S::P_STORES];
+#pragma unroll
+        for (int i = 0; i < S::P_STORES; ++i) {
+            const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
+            py[i] = (t * HP + c0 + 8 * c) * 2;
+            pys[i] = S::YS + t * S::XRB + 16 * (c ^ ys_swz<S::XC>(t));
+        }
         auto pstore = [&](int kb, const unsigned char *buf) {
+            const unsigned yo = kb * kBlk * HP * 2;
 #pragma unroll
             for (int i = 0; i < S::P_STORES; ++i) {
-                const int pos = 64 * i + lane, t = pos / S::XC, c = pos % S::XC;
-                const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + S::YS + t * S::XRB +
-                                                                 16 * (c ^ ys_swz<S::XC>(t)));
-                __builtin_amdgcn_raw_buffer_store_b128(
-                    v, y_rsrc, (t * HP + c0 + 8 * c) * 2 + kb * kBlk * HP * 2, 0, 0);
+                const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + pys[i]);
+                __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, py[i], yo, 0);
             }
         };
 #pragma unroll
