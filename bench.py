@@ -114,13 +114,13 @@ def kernel_alg_bytes(name, w, es):
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     if name == "k_fused_ssd":
         return alg_bytes_forward(w, es)
-    if name == "k2b_block_cb":
-        # C and B rows in, one 32 x 32 bf16 diagonal block per block and group out
+    if name == "k_prep":
+        # dt in, one decay record per (batch, head, 32-token block) out (the
+        # 68 floats a factored block's record needs); C and B rows in, one
+        # 32 x 32 bf16 diagonal block per block and group out
         nb = -(-L // 32)
-        return 2 * b * L * G * N * es + b * nb * G * 32 * 32 * 2
-    if name == "k1_block_vectors":
-        # dt in; one 132-float decay record per (batch, head, 32-token block) out
-        return b * L * H * 4 + b * H * (-(-L // 32)) * 132 * 4
+        return (b * L * H * 4 + b * H * nb * 68 * 4 +
+                2 * b * L * G * N * es + b * nb * G * 32 * 32 * 2)
     if name == "k1_dA_cumsum":
         # dt in; prefix hi, lo and dt per chunk out (the padded chunk length)
         return b * L * H * 4 + 3 * b * H * (-(-L // Q)) * Q * 4
@@ -174,16 +174,22 @@ def time_forward(w, dev, steps, warmup, ev):
     stream = torch.cuda.current_stream()
     sh = stream.cuda_stream
     e0, e1 = ev.create(), ev.create()
+    # the timed steps: plain calls, events only around the whole region
     torch.cuda.synchronize()
     h0 = time.perf_counter()
     ev.record(e0, sh)
-    names = None
     for k in range(steps):
-        _, _, names = libssd.ssd_chunk_scan_fwd_timed(events[k], *args, **kw)
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
     ev.record(e1, sh)
     torch.cuda.synchronize()
     h1 = time.perf_counter()
     total_ms = ev.ms(e0, e1)
+    # the same steps again with an event between every two kernels, for the
+    # per-kernel split
+    names = None
+    for k in range(steps):
+        _, _, names = libssd.ssd_chunk_scan_fwd_timed(events[k], *args, **kw)
+    torch.cuda.synchronize()
     nk = len(names)
     per_kernel = [sum(ev.ms(events[k][i], events[k][i + 1]) for k in range(steps)) / steps
                   for i in range(nk)]
@@ -307,8 +313,10 @@ def kernel_source_hash():
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # (the GPU clocks take some tens of milliseconds of back-to-back work to
+    # settle; 100 warmup steps of the 2.7B-shape layer are about 30 ms)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--workload", default="mamba2_2p7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
@@ -403,8 +411,8 @@ def main():
         extra = {}
         for name in ("mamba2_130m", "grouped_g8"):
             wx = WORKLOADS[name]
-            rx = time_forward(wx, dev, 10, 3, ev)
-            msx = rx["gpu_ms"] / 10
+            rx = time_forward(wx, dev, 100, 50, ev)
+            msx = rx["gpu_ms"] / 100
             esx = 2 if wx.io_dtype == "bf16" else 4
             gb = alg_bytes_forward(wx, esx) / (msx * 1e-3) / 1e9
             extra[name] = {"ms_per_step": round(msx, 4),

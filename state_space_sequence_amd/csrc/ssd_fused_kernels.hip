@@ -40,7 +40,7 @@
 // (s > l exactly 0, the upper-triangle protection of the Kernel 5 page) on
 // raw x, with D on the diagonal, and the state decays explicitly
 // (h~ <- sigma_k exp(lambda_e) h~ + B^T x', sigma = 1).  The per-token
-// factors come precomputed per block (k1_block_vectors, from fp64 prefixes).
+// factors come precomputed per block (k_prep, from fp64 prefixes).
 //
 // Workgroup = NW = PB / 32 waves; wave w owns headdim columns 32 w .. 32 w +
 // 31 of the workgroup's PB columns and computes with
@@ -700,54 +700,6 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     }
 }
 
-// Diagonal 32x32 block of C B^T for every 32-token block and group, bf16,
-// causally masked (entries with s > l are exact zeros), stored in the MFMA
-// B-fragment order the fused kernel reads.  W16 = 0 (waves of 32 columns,
-// v_mfma_f32_32x32x16_bf16): K-step kk, lane L hold the 8 values
-// C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at (64 kk + L) * 16.
-// W16 = 1 (waves of 16 columns, v_mfma_f32_16x16x32_bf16): token tile tt,
-// lane L hold C B^T[16 tt + L % 16][8 (L / 16) .. +7] at (64 tt + L) * 16.
-// One wave per (block, group, batch) computes E = B C^T with
-// v_mfma_f32_32x32x16_bf16: lane (l = L % 32, hi) ends with
-// E[s][l] = C_l . B_s for s = 8 i + 4 hi + c, four runs of 4 consecutive s.
-template <int W16>
-__global__ void __launch_bounds__(64)
-k2b_block_cb(const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__restrict__ cbf,
-             int L, int G, int nblk) {
-    constexpr int N = 128;
-    const int kb = blockIdx.x / G, g = blockIdx.x % G, b = blockIdx.y;
-    const int lane = threadIdx.x, r = lane & 31, hi = lane >> 5;
-    const int t = kb * kBlk + r;
-    bf16 *out = cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk);
-    f32x16 acc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) {
-        const size_t o = (((size_t)b * L + t) * G + g) * N + 16 * ks + 8 * hi;
-        const bf16x8 bs = t < L ? load_frag(Bm + o) : zero_frag<bf16>();  // A: row s = r
-        const bf16x8 cl = t < L ? load_frag(Cm + o) : zero_frag<bf16>();  // B: column l = r
-        acc = mma32(bs, cl, acc);
-    }
-    // lane (l = r, hi): E[s][l] for s = 8 i + 4 hi + c
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s0 = 8 * i + 4 * hi;
-        bf16x4 v4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = s0 + c <= r ? (bf16)acc[4 * i + c] : (bf16)0.f;
-        size_t dst;
-        if (W16) {
-            // t-tile r / 16, lane (r % 16) + 16 (s0 / 8), values s0 % 8 .. +3
-            dst = (64 * (r >> 4) + (r & 15) + 16 * (s0 >> 3)) * 8 + (s0 & 7);
-        } else {
-            const int kk = s0 >> 4, hs = (s0 >> 3) & 1;
-            dst = (64 * kk + r + 32 * hs) * 8 + (s0 & 7);
-        }
-        *reinterpret_cast<bf16x4 *>(out + dst) = v4;
-    }
-}
-
 // ------------------------------------------------------------------------
 // The same pass with 16 headdim columns per wave on v_mfma_f32_16x16x32_bf16
 // (operands: lane l holds row (A) / column (B) l % 16 and k = 8 (l / 16) + j,
@@ -1113,55 +1065,166 @@ k_fused16_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
     }
 }
 
-// Per-block decay records of the fused path (one per batch, head and
-// 32-token block; layout at kVecRec).  grid (nblk, ceil(H / 8), b), 256
-// threads: the block's dt for 8 heads is staged through LDS (32-byte runs
-// over heads), then each half-wave scans one head's 32 tokens in fp64 (dt A
-// is exact in fp64), so lambda_l - lambda_s is the difference of two fp64
-// prefixes rounded once.
+// Inclusive prefix sum of an fp64 value over each 32-lane half of the wave,
+// without LDS round trips: DPP shifts by 1, 2, 4 and 8 within each 16-lane
+// row (lanes shifted in from outside the row read 0), then lanes 16..31
+// (48..63) add the row total of lane 15 (47), read with v_readlane.
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ double dpp_f64(double v) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xF, true);
+    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xF, true);
+    return __builtin_bit_cast(double, (unsigned long long)(unsigned)lo |
+                                          ((unsigned long long)(unsigned)hi << 32));
+}
+__device__ __forceinline__ double lane_f64(double v, int src) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, src);
+    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), src);
+    return __builtin_bit_cast(double, (unsigned long long)lo | ((unsigned long long)hi << 32));
+}
+__device__ __forceinline__ double scan32_f64(double v, int lane) {
+    v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
+    v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
+    v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
+    v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
+    const double r0 = lane_f64(v, 15), r2 = lane_f64(v, 47);
+    return v + ((lane & 16) ? (lane >= 32 ? r2 : r0) : 0.0);
+}
+// the value of lane 31 in lanes 0..31 and of lane 63 in lanes 32..63
+__device__ __forceinline__ double last_of_half(double v, int lane) {
+    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
+    const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
+    const unsigned lo0 = __builtin_amdgcn_readlane(lo, 31), hi0 = __builtin_amdgcn_readlane(hi, 31);
+    const unsigned lo1 = __builtin_amdgcn_readlane(lo, 63), hi1 = __builtin_amdgcn_readlane(hi, 63);
+    const bool up = lane >= 32;
+    return __builtin_bit_cast(double, (unsigned long long)(up ? lo1 : lo0) |
+                                          ((unsigned long long)(up ? hi1 : hi0) << 32));
+}
+
+// Per-block preparation of the fused pass, in one launch.  grid (n_rec +
+// n_cb, batch), 256 threads.
+//
+// Workgroups [0, n_rec): the decay records (one per batch, head and 32-token
+// block; layout at kVecRec) of kPrepBlocks consecutive blocks of 8 heads.
+// All their dt values are staged through LDS first (32-byte runs over
+// heads), then each half-wave takes one head and block at a time: the fp64
+// prefix sum of dt A over the block's 32 tokens (dt A is exact in fp64), so
+// lambda_l - lambda_s is the difference of two fp64 prefixes rounded once.
+//
+// Workgroups [n_rec, n_rec + n_cb): the causal diagonal 32x32 block of C B^T
+// for four (block, group) pairs, one per wave, bf16, in the MFMA B-fragment
+// order the fused kernel reads.  W16 = 0 (waves of 32 columns,
+// v_mfma_f32_32x32x16_bf16): K-step kk, lane L hold the 8 values
+// C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at (64 kk + L) * 16.
+// W16 = 1 (waves of 16 columns, v_mfma_f32_16x16x32_bf16): token tile tt,
+// lane L hold C B^T[16 tt + L % 16][8 (L / 16) .. +7] at (64 tt + L) * 16.
+// A wave computes E = B C^T with v_mfma_f32_32x32x16_bf16 (all its row loads
+// issued first; rows past the sequence end read as zeros through the buffer
+// resource's range): lane (l = L % 32, hi) ends with E[s][l] = C_l . B_s for
+// s = 8 i + 4 hi + c, four runs of 4 consecutive s.
+constexpr int kPrepBlocks = 8;
+template <int W16>
 __global__ void __launch_bounds__(256)
-k1_block_vectors(const float *__restrict__ dt, const float *__restrict__ A,
-                 float *__restrict__ vrec, int L, int H, int nblk) {
-    __shared__ float s_dt[kBlk][9];
-    const int kb = blockIdx.x, h0 = blockIdx.y * 8, b = blockIdx.z;
-    const int tid = threadIdx.x;
-    {
-        const int tt = tid >> 3, hh = tid & 7, t = kb * kBlk + tt, h = h0 + hh;
-        s_dt[tt][hh] = (t < L && h < H) ? dt[((size_t)b * L + t) * H + h] : 0.f;
-    }
-    __syncthreads();
-    const int hh = tid >> 5, tt = tid & 31, h = h0 + hh;
-    if (h >= H) return;  // whole half-waves
-    const float d = s_dt[tt][hh];
-    double lam = (double)d * (double)A[h];
+k_prep(const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ vrec,
+       const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__restrict__ cbf, int L,
+       int H, int G, int nblk, int n_rec) {
+    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
+    if ((int)blockIdx.x < n_rec) {
+        __shared__ float s_dt[kPrepBlocks][kBlk][9];
+        const int nbg = (nblk + kPrepBlocks - 1) / kPrepBlocks;
+        const int kb0 = (blockIdx.x % nbg) * kPrepBlocks, h0 = (blockIdx.x / nbg) * 8;
+        const int hh = tid >> 5, tt = tid & 31, h = h0 + hh;
+        float af = A[h < H ? h : H - 1];
+        {
+            // (loads through a buffer resource over this batch's dt: tokens
+            // past the end read as zeros, and all loads issue before any
+            // wait; heads past H feed only half-waves that return below)
+            const __amdgpu_buffer_rsrc_t rdt = __builtin_amdgcn_make_buffer_rsrc(
+                (void *)(dt + (size_t)b * L * H), 0, (unsigned)((size_t)L * H * 4), kBufferWord3);
+            const int lt = tid >> 3, lh = tid & 7;
+            float v[kPrepBlocks];
 #pragma unroll
-    for (int o = 1; o < kBlk; o <<= 1) {
-        const double u = __shfl_up(lam, o, kBlk);
-        if (tt >= o) lam += u;
+            for (int i = 0; i < kPrepBlocks; ++i)
+                v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
+                    rdt, (unsigned)(((kb0 + i) * kBlk + lt) * H + h0 + lh) * 4, 0, 0));
+#pragma unroll
+            for (int i = 0; i < kPrepBlocks; ++i) s_dt[i][lt][lh] = v[i];
+            // (A is read here, with the dt loads in flight, not after the
+            // barrier)
+            asm volatile("" : "+v"(af));
+        }
+        const double a = (double)af;
+        __syncthreads();
+        if (h >= H) return;  // whole half-waves, after the only barrier
+#pragma unroll
+        for (int i = 0; i < kPrepBlocks; ++i) {
+            const int kb = kb0 + i;
+            if (kb >= nblk) break;
+            const float d = s_dt[i][tt][hh];
+            const double lam = scan32_f64((double)d * a, lane);
+            const double lam_e = last_of_half(lam, lane);
+            const float le = (float)lam_e;
+            const bool fac = -le <= kSafeDecay;
+            float *rec = vrec + (((size_t)b * H + h) * nblk + kb) * kVecRec;
+            rec[tt] = fast_exp((float)(lam_e - lam)) * d;
+            rec[kBlk + tt] = fac ? fast_exp((float)(lam - lam_e)) : 0.f;
+            // the per-element exponents and steps are read by exact blocks only
+            if (!fac) {
+                rec[2 * kBlk + tt] = (float)(lam - lam_e);
+                rec[3 * kBlk + tt] = d;
+            }
+            if (tt == kBlk - 1)
+                *reinterpret_cast<float4 *>(rec + 4 * kBlk) =
+                    make_float4(fast_exp(le), fac ? 1.f : 0.f, le, 0.f);
+        }
+        return;
     }
-    const double lam_e = __shfl(lam, kBlk - 1, kBlk);
-    const float le = (float)lam_e;
-    const bool fac = -le <= kSafeDecay;
-    float *rec = vrec + (((size_t)b * H + h) * nblk + kb) * kVecRec;
-    rec[tt] = fast_exp((float)(lam_e - lam)) * d;
-    rec[kBlk + tt] = fac ? fast_exp((float)(lam - lam_e)) : 0.f;
-    // the per-element exponents and steps are read by exact blocks only
-    if (!fac) {
-        rec[2 * kBlk + tt] = (float)(lam - lam_e);
-        rec[3 * kBlk + tt] = d;
+    constexpr int N = 128;
+    const int pair = (blockIdx.x - n_rec) * 4 + (tid >> 6);
+    if (pair >= nblk * G) return;
+    const int kb = pair / G, g = pair % G;
+    const int r = lane & 31, hi = lane >> 5;
+    const size_t base = ((size_t)b * L * G + g) * N;
+    const unsigned range = (unsigned)(((size_t)L * G * N - (size_t)g * N) * 2);
+    const __amdgpu_buffer_rsrc_t rbr = __builtin_amdgcn_make_buffer_rsrc((void *)(Bm + base), 0, range, kBufferWord3);
+    const __amdgpu_buffer_rsrc_t rcr = __builtin_amdgcn_make_buffer_rsrc((void *)(Cm + base), 0, range, kBufferWord3);
+    const unsigned roff = (unsigned)((kb * kBlk + r) * G * N + 8 * hi) * 2;
+    u32x4 bs[N / 16], cl[N / 16];
+#pragma unroll
+    for (int ks = 0; ks < N / 16; ++ks) {
+        bs[ks] = __builtin_amdgcn_raw_buffer_load_b128(rbr, roff + 32 * ks, 0, 0);  // A: row s = r
+        cl[ks] = __builtin_amdgcn_raw_buffer_load_b128(rcr, roff + 32 * ks, 0, 0);  // B: column l = r
     }
-    if (tt == kBlk - 1) {
-        rec[4 * kBlk] = fast_exp(le);
-        rec[4 * kBlk + 1] = fac ? 1.f : 0.f;
-        rec[4 * kBlk + 2] = le;
-        rec[4 * kBlk + 3] = 0.f;
+    f32x16 acc;
+#pragma unroll
+    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
+#pragma unroll
+    for (int ks = 0; ks < N / 16; ++ks)
+        acc = mma32(__builtin_bit_cast(bf16x8, bs[ks]), __builtin_bit_cast(bf16x8, cl[ks]), acc);
+    bf16 *out = cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk);
+    // lane (l = r, hi): E[s][l] for s = 8 i + 4 hi + c
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int s0 = 8 * i + 4 * hi;
+        bf16x4 v4;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) v4[c] = s0 + c <= r ? (bf16)acc[4 * i + c] : (bf16)0.f;
+        size_t dst;
+        if (W16) {
+            // t-tile r / 16, lane (r % 16) + 16 (s0 / 8), values s0 % 8 .. +3
+            dst = (64 * (r >> 4) + (r & 15) + 16 * (s0 >> 3)) * 8 + (s0 & 7);
+        } else {
+            const int kk = s0 >> 4, hs = (s0 >> 3) & 1;
+            dst = (64 * kk + r + 32 * hs) * 8 + (s0 & 7);
+        }
+        *reinterpret_cast<bf16x4 *>(out + dst) = v4;
     }
 }
 
 // --------------------------------------------------------------------- launch
 
-const char *const kFusedKernelNames[kFusedKernels] = {"k1_block_vectors", "k2b_block_cb",
-                                                      "k_fused_ssd"};
+const char *const kFusedKernelNames[kFusedKernels] = {"k_prep", "k_fused_ssd"};
 
 template <typename T>
 bool fused_supported(int P, int N, int Q) {
@@ -1226,16 +1289,17 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     const int nblk = fused_nblk(a.L);
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
-    hipLaunchKernelGGL(k1_block_vectors, dim3(nblk, (a.H + 7) / 8, a.batch), dim3(256), 0, stream,
-                       a.dt, a.A, a.vrec, a.L, a.H, nblk);
-    if ((err = mark()) != hipSuccess) return err;
     const bool w16 = use_wave16(a);
+    const int n_rec = (nblk + kPrepBlocks - 1) / kPrepBlocks * ((a.H + 7) / 8);
+    const int n_cb = (nblk * a.G + 3) / 4;
     if (w16)
-        hipLaunchKernelGGL(k2b_block_cb<1>, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
-                           (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
+        hipLaunchKernelGGL(k_prep<1>, dim3(n_rec + n_cb, a.batch), dim3(256), 0, stream, a.dt, a.A,
+                           a.vrec, (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.H,
+                           a.G, nblk, n_rec);
     else
-        hipLaunchKernelGGL(k2b_block_cb<0>, dim3(nblk * a.G, a.batch), dim3(64), 0, stream,
-                           (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.G, nblk);
+        hipLaunchKernelGGL(k_prep<0>, dim3(n_rec + n_cb, a.batch), dim3(256), 0, stream, a.dt, a.A,
+                           a.vrec, (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.H,
+                           a.G, nblk, n_rec);
     if ((err = mark()) != hipSuccess) return err;
     if (w16) {
         err = a.P % 64 == 0 ? launch_fused16_main<64>(a, stream) : launch_fused16_main<32>(a, stream);

@@ -52,7 +52,7 @@ constexpr int kVecRec = 132;
 enum class Path { Split, Fused };
 
 constexpr int kSplitKernels = 5;
-constexpr int kFusedKernels = 3;
+constexpr int kFusedKernels = 2;
 constexpr int kMaxForwardKernels = 5;
 extern const char *const kSplitKernelNames[kSplitKernels];
 extern const char *const kFusedKernelNames[kFusedKernels];

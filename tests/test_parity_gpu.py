@@ -269,7 +269,7 @@ def test_timed_variant_matches_and_names_kernels(dev, path):
         assert names == ["k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing",
                          "k5_chunk_scan"]
     else:
-        assert names == ["k1_block_vectors", "k2b_block_cb", "k_fused_ssd"]
+        assert names == ["k_prep", "k_fused_ssd"]
     for e in evs:
         hip.hipEventDestroy(__import__("ctypes").c_void_p(e))
 
