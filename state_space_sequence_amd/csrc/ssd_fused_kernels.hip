@@ -139,11 +139,12 @@ struct Fused {
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
     static constexpr int XRB = 2 * PB;                 // raw x row bytes
     static constexpr int NRS = PB == 128 ? 2 : 1;      // decay-record slots (heads)
-    // one stage, filled by DMA: C rows, B rows (column-blocked, blk_off),
-    // C B^T fragments, raw x (column-blocked) and the decay records (kVecRec
-    // floats in 1 KB slots) of one block; then the block's y for the
-    // producer: 32 rows of XRB bytes, 16-byte chunk c of row t in slot
-    // c ^ ys_swz(t)
+    // one stage: C rows, B rows (column-blocked, blk_off), raw x
+    // (column-blocked) and the decay records (kVecRec floats in 1 KB slots)
+    // of one block, filled by DMA; the causal diagonal block of C B^T in the
+    // MFMA B-fragment order, formed by the producer from the stage's C and B
+    // rows; then the block's y for the producer: 32 rows of XRB bytes,
+    // 16-byte chunk c of row t in slot c ^ ys_swz(t)
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
@@ -153,29 +154,26 @@ struct Fused {
     static constexpr int STG = YS + kBlk * XRB;
     // floats of the decay record
     enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
-    // stages: the DMAs of a block go out NST - 1 blocks ahead of its use.
-    // With four stages (64 and 128 columns) a block's stage is complete one
-    // block early, and the operands that open a block are read during the
-    // block before it (PF).
-    static constexpr int NST = PB >= 64 ? 4 : 3;
-    static constexpr bool PF = NST == 4;
+    // four stages: the DMAs of a block go out three blocks ahead of its
+    // use, and a block's stage is complete one block early: the producer
+    // forms its C B^T block and the compute waves read its opening operands
+    // during the block before it
+    static constexpr int NST = 4;
     // K-step rows m of the C fragments among the opening operands (within
     // the 256 registers per lane that two waves on a SIMD leave each)
     static constexpr int ECF = PB == 128 ? 1 : 2;
     static constexpr int LDS = NST * STG;
     static_assert(PB == 32 || PB == 64 || PB == 128, "one, two or four waves");
     static_assert(STG % 16 == 0, "alignment");
-    // (two 32-column workgroups fit a compute unit; wider ones run one per
-    // compute unit, which the column choice arranges)
-    static_assert(PB == 32 ? 2 * LDS <= 160 * 1024 : LDS <= 160 * 1024, "LDS per compute unit");
-    // the producer's DMAs of a block (C and B, x, C B^T halves, records) and
-    // y stores.  At the end of block kb it waits for the DMAs of block
-    // kb + 1 (kb + 2 with PF); younger than those are the y stores issued
-    // right after them and the DMAs and y stores of the NST - 2 - PF blocks
-    // after
-    static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 2 + NRS;
+    // (one workgroup per compute unit, which the column choice arranges)
+    static_assert(LDS <= 160 * 1024, "LDS per compute unit");
+    // the producer's DMAs of a block (C and B, x, records) and y stores.  At
+    // the end of block kb it waits for the DMAs of block kb + 2; younger
+    // than those are the y stores issued right after them and the DMAs and
+    // y stores of block kb + 3
+    static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + NRS;
     static constexpr int P_STORES = kBlk * XRB / 1024;
-    static constexpr int P_WAIT = P_STORES + (NST - 2 - (PF ? 1 : 0)) * (P_LOADS + P_STORES);
+    static constexpr int P_WAIT = P_STORES + (NST - 3) * (P_LOADS + P_STORES);
     static_assert(P_WAIT < 64, "vmcnt immediate");
 };
 
@@ -273,7 +271,7 @@ __device__ __forceinline__ int col_of(int q) {
 template <int PB>
 __global__ void __launch_bounds__(Fused<PB>::NT)
 k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-            const bf16 *__restrict__ cbf, const float *__restrict__ vrec,
+            const float *__restrict__ vrec,
             const float *__restrict__ D, const float *init, float *final_state,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
     typedef Fused<PB> S;
@@ -310,9 +308,6 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(cbf + ((size_t)b * nblk * G + g) * (kBlk * kBlk)), 0,
-            (nblk * G - g) * (kBlk * kBlk * 2), kBufferWord3);
         // the records of the workgroup's heads (consecutive (batch, head) rows)
         const int h0 = c0 / P;
         const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
@@ -321,7 +316,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
         const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
-        const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
+        const unsigned v_step = kVecRec * 4;
         typedef __attribute__((address_space(3))) void lds_void;
         // (the block's byte offset goes in the scalar offset, so a DMA
         // costs no vector instruction)
@@ -346,8 +341,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             px[i] = t * HP * 2 + 16 * (4 * (i >> 1) + ((lane & 3) ^ ((t >> 2) & 3)));
         }
         auto pdma = [&](int kb, unsigned char *buf) {
-            const unsigned cbo = kb * cb_step, xo = kb * x_step, cbfo = kb * cbf_step,
-                           vo = kb * v_step;
+            const unsigned cbo = kb * cb_step, xo = kb * x_step, vo = kb * v_step;
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
                 bdma(rc, pcb[i], cbo, buf + S::CS + 1024 * i);
@@ -356,11 +350,42 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
             for (int i = 0; i < NXD; ++i) bdma(rx, px[i], xo, buf + S::XR + 1024 * i);
 #pragma unroll
-            for (int pc = 0; pc < 2; ++pc)
-                bdma(rcb, 16 * (64 * pc + lane), cbfo, buf + S::CBF + 1024 * pc);
-#pragma unroll
             for (int q = 0; q < S::NRS; ++q)
                 bdma(rv, 16 * lane + q * nblk * v_step, vo, buf + S::VR + 1024 * q);
+        };
+        // The causal diagonal block of C B^T of the block staged in `buf`,
+        // from its C and B rows: E = B C^T on MFMA (A: B row s = lane % 32,
+        // B: C row l = lane % 32, K-step ks over dstate 16 ks .. 16 ks + 15),
+        // so lane (r, hi) ends with E[s][r] = C_r . B_s for s = 8 i + 4 hi + c;
+        // entries with s > r are exact zeros.  Written in the fragment order
+        // of the diagonal product: K-step kk, lane L hold the 8 values
+        // C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at
+        // CBF + (64 kk + L) * 16.
+        const int pr_ = lane & 31, phi = lane >> 5;
+        int pc_rd[2];
+#pragma unroll
+        for (int u = 0; u < 2; ++u) pc_rd[u] = blk_off(pr_, 2 * u + phi);
+        auto pcbt = [&](unsigned char *buf) {
+            f32x16 e;
+#pragma unroll
+            for (int v = 0; v < 16; ++v) e[v] = 0.f;
+            bf16x8 fb[8], fc[8];
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) {
+                fb[ks] = lds_b128(buf, S::BS + pc_rd[ks & 1] + 2048 * (ks >> 1));
+                fc[ks] = lds_b128(buf, S::CS + pc_rd[ks & 1] + 2048 * (ks >> 1));
+            }
+#pragma unroll
+            for (int ks = 0; ks < 8; ++ks) e = mma32(fb[ks], fc[ks], e);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int s0 = 8 * i + 4 * phi;
+                bf16x4 v4;
+#pragma unroll
+                for (int c = 0; c < 4; ++c) v4[c] = s0 + c <= pr_ ? (bf16)e[4 * i + c] : (bf16)0.f;
+                const int kk = s0 >> 4, hs = (s0 >> 3) & 1;
+                *reinterpret_cast<bf16x4 *>(buf + S::CBF + ((64 * kk + pr_ + 32 * hs) * 8 + (s0 & 7)) * 2) = v4;
+            }
         };
         // per-lane y offsets and LDS staging slots of the stores
         unsigned py[S::P_STORES];
@@ -382,13 +407,15 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
 #pragma unroll
         for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        pcbt(stage(0));
         lds_barrier();
-        // block kb: refill the stage block kb - 1 used, store its y, then
-        // wait for the DMAs of block kb + 1 (kb + 2 with PF) before the
-        // end-of-block barrier
+        // block kb: refill the stage block kb - 1 used, store its y, form
+        // the C B^T block of block kb + 1, then wait for the DMAs of block
+        // kb + 2 before the end-of-block barrier
         auto pblock = [&](int kb, const int si) {
             pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
             if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+            pcbt(stage((si + 1) % S::NST));
             __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
             lds_barrier();
         };
@@ -487,8 +514,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     lds_barrier();
     float sig_out = 1.f;  // sigma after the previous block
 
-    // The operands that open a block (with PF read from its stage during the
-    // block before): the decay-record fields of the bookkeeping, cf and
+    // The operands that open a block (read from its stage during the block
+    // before): the decay-record fields of the bookkeeping, cf and
     // exp(lambda_r - lambda_e), raw x^T and the C fragments of the first
     // 2 ECF K-steps.
     constexpr int ECF = S::ECF;
@@ -542,7 +569,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     };
 
     // block kb from stage si = kb % NST (a literal in each unrolled copy);
-    // e holds its opening operands, nx receives those of block kb + 1 (PF)
+    // e holds its opening operands, nx receives those of block kb + 1
     auto block = [&](int kb, const int si, Early &e, Early &nx) {
         unsigned char *cur = stage(si);
         const float *v = reinterpret_cast<const float *>(cur + rec_off);
@@ -553,7 +580,6 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         // block's opening operands during the state update), so ALU and LDS
         // issue overlap the matrix pipeline.  A rescaled or exact block edits
         // the operands of the common path in place between the two phases.
-        if constexpr (!S::PF) load_early(cur, e);
         Ops o;
         load_late(cur, o);
         const Book bk = book_of(e.dl, e.fc, sig_out);
@@ -638,7 +664,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
         for (int kk = 0; kk < 2; ++kk) acc = mma32(xp[kk], o.cbv[kk], acc);
         __builtin_amdgcn_sched_barrier(0);
         // state update h~ += B^T x' (K-step 0 of every tile, then K-step 1),
-        // with the reads of the next block's opening operands (PF) and the
+        // with the reads of the next block's opening operands and the
         // epilogue (from the third chunk on, once the diagonal product has
         // landed)
 #pragma unroll
@@ -646,9 +672,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             const int kk = q >> 2, m = q & 3;
             st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
             __builtin_amdgcn_sched_barrier(0);
-            if constexpr (S::PF) {
-                if (q == 0) load_early(stage((si + 1) % S::NST), nx);
-            }
+            if (q == 0) load_early(stage((si + 1) % S::NST), nx);
             if (q >= 2) {
                 // acc[vv] for the vv with vv * 6 / 16 == q - 2 (the
                 // empty asm keeps them in this chunk)
@@ -671,9 +695,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     };
 
     // unrolled by the stage count, so that every stage address is a literal
-    // (and with PF the two sets of opening operands alternate)
+    // (and the two sets of opening operands alternate)
     Early ea, eb;
-    if constexpr (S::PF) load_early(stage(0), ea);
+    load_early(stage(0), ea);
     for (int kb = 0; kb < nblk; kb += S::NST) {
         block(kb, 0, ea, eb);
         if (kb + 1 < nblk) {
@@ -1112,9 +1136,10 @@ __device__ __forceinline__ double last_of_half(double v, int lane) {
 // prefix sum of dt A over the block's 32 tokens (dt A is exact in fp64), so
 // lambda_l - lambda_s is the difference of two fp64 prefixes rounded once.
 //
-// Workgroups [n_rec, n_rec + n_cb): the causal diagonal 32x32 block of C B^T
-// for four (block, group) pairs, one per wave, bf16, in the MFMA B-fragment
-// order the fused kernel reads.  W16 = 0 (waves of 32 columns,
+// Workgroups [n_rec, n_rec + n_cb) (launched for the 16-column kernel; the
+// 32-column kernel forms these blocks itself from its staged C and B rows):
+// the causal diagonal 32x32 block of C B^T for four (block, group) pairs,
+// one per wave, bf16, in the MFMA B-fragment order the fused kernel reads.  W16 = 0 (waves of 32 columns,
 // v_mfma_f32_32x32x16_bf16): K-step kk, lane L hold the 8 values
 // C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at (64 kk + L) * 16.
 // W16 = 1 (waves of 16 columns, v_mfma_f32_16x16x32_bf16): token tile tt,
@@ -1157,16 +1182,16 @@ k_prep(const float *__restrict__ dt, const float *__restrict__ A, float *__restr
         const double a = (double)af;
         __syncthreads();
         if (h >= H) return;  // whole half-waves, after the only barrier
+        float *const rec0 = vrec + (((size_t)b * H + h) * nblk + kb0) * kVecRec;
 #pragma unroll
         for (int i = 0; i < kPrepBlocks; ++i) {
-            const int kb = kb0 + i;
-            if (kb >= nblk) break;
+            if (kb0 + i >= nblk) break;
             const float d = s_dt[i][tt][hh];
             const double lam = scan32_f64((double)d * a, lane);
             const double lam_e = last_of_half(lam, lane);
             const float le = (float)lam_e;
             const bool fac = -le <= kSafeDecay;
-            float *rec = vrec + (((size_t)b * H + h) * nblk + kb) * kVecRec;
+            float *const rec = rec0 + i * kVecRec;
             rec[tt] = fast_exp((float)(lam_e - lam)) * d;
             rec[kBlk + tt] = fac ? fast_exp((float)(lam - lam_e)) : 0.f;
             // the per-element exponents and steps are read by exact blocks only
@@ -1181,7 +1206,9 @@ k_prep(const float *__restrict__ dt, const float *__restrict__ A, float *__restr
         return;
     }
     constexpr int N = 128;
-    const int pair = (blockIdx.x - n_rec) * 4 + (tid >> 6);
+    // (the wave index read as uniform, so that the buffer resources below
+    // stay in scalar registers)
+    const int pair = (blockIdx.x - n_rec) * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
     if (pair >= nblk * G) return;
     const int kb = pair / G, g = pair % G;
     const int r = lane & 31, hi = lane >> 5;
@@ -1241,9 +1268,8 @@ static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
     const int nblk = fused_nblk(a.L);
     hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
-                       (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
-                       (const bf16 *)a.cb, a.vrec, a.D, a.init, a.final_state, (bf16 *)a.y,
-                       a.L, a.H, a.G, a.P, nblk);
+                       (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C, a.vrec, a.D,
+                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, nblk);
     return hipSuccess;
 }
 
@@ -1291,7 +1317,8 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     if ((err = mark()) != hipSuccess) return err;
     const bool w16 = use_wave16(a);
     const int n_rec = (nblk + kPrepBlocks - 1) / kPrepBlocks * ((a.H + 7) / 8);
-    const int n_cb = (nblk * a.G + 3) / 4;
+    // (the 32-column kernel forms its C B^T blocks itself)
+    const int n_cb = w16 ? (nblk * a.G + 3) / 4 : 0;
     if (w16)
         hipLaunchKernelGGL(k_prep<1>, dim3(n_rec + n_cb, a.batch), dim3(256), 0, stream, a.dt, a.A,
                            a.vrec, (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.H,
