@@ -114,13 +114,6 @@ def kernel_alg_bytes(name, w, es):
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     if name == "k_fused_ssd":
         return alg_bytes_forward(w, es)
-    if name == "k_prep":
-        # dt in, one decay record per (batch, head, 32-token block) out (the
-        # 68 floats a factored block's record needs); C and B rows in, one
-        # 32 x 32 bf16 diagonal block per block and group out
-        nb = -(-L // 32)
-        return (b * L * H * 4 + b * H * nb * 68 * 4 +
-                2 * b * L * G * N * es + b * nb * G * 32 * 32 * 2)
     if name == "k1_dA_cumsum":
         # dt in; prefix hi, lo and dt per chunk out (the padded chunk length)
         return b * L * H * 4 + 3 * b * H * (-(-L // Q)) * Q * 4

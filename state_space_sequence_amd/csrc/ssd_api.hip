@@ -78,13 +78,13 @@ ssd_status choose_path(int seqlen, int nheads, int ngroups, int headdim, int dst
 }
 
 struct Layout {
-    size_t acum_hi, acum_lo, dtT, vrec, cb, S, total;
+    size_t acum_hi, acum_lo, dtT, cb, S, total;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
                       int ngroups, int chunk_len, ssd_dtype io, ssd::Path path) {
     const size_t b = batch, H = nheads, P = headdim, N = dstate, G = ngroups;
-    const size_t es = io == SSD_BF16 ? 2 : 4;
+    (void)io;
     Layout l;
     if (path == ssd::Path::Split) {
         const size_t Q = chunk_len;
@@ -93,21 +93,13 @@ Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate
         l.acum_hi = 0;
         l.acum_lo = l.acum_hi + vec;
         l.dtT = l.acum_lo + vec;
-        l.vrec = 0;
         l.cb = l.dtT + vec;
         l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
         l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
     } else {
-        // the fused path works in fixed blocks of kFusedBlock tokens; its
-        // kernel copies 1 KB from the start of each decay record, so 1 KB of
-        // slack follows the last one
-        const size_t Q = ssd::kFusedBlock;
-        const size_t nb = ((size_t)seqlen + Q - 1) / Q;
-        l.acum_hi = l.acum_lo = l.dtT = 0;
-        l.vrec = 0;
-        l.cb = round_up(b * H * nb * ssd::kVecRec * sizeof(float) + 1024);
-        l.S = 0;
-        l.total = l.cb + round_up(b * nb * G * Q * Q * es);
+        // the fused kernel keeps every intermediate on chip
+        l.acum_hi = l.acum_lo = l.dtT = l.cb = l.S = 0;
+        l.total = 0;
     }
     return l;
 }
@@ -133,7 +125,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
     const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
                                       chunk_len, io_dtype, path);
-    if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
+    if (lay.total > 0 &&
+        (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign)))
         return SSD_ERR_WORKSPACE;
 
     ssd::ForwardArgs a;
@@ -159,8 +152,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.acum_hi = split ? reinterpret_cast<float *>(ws + lay.acum_hi) : nullptr;
     a.acum_lo = split ? reinterpret_cast<float *>(ws + lay.acum_lo) : nullptr;
     a.dtT = split ? reinterpret_cast<float *>(ws + lay.dtT) : nullptr;
-    a.vrec = split ? nullptr : reinterpret_cast<float *>(ws + lay.vrec);
-    a.cb = ws + lay.cb;
+    a.cb = split ? ws + lay.cb : nullptr;
     a.S = split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
 
     const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::kFusedKernels;

@@ -40,7 +40,7 @@
 // (s > l exactly 0, the upper-triangle protection of the Kernel 5 page) on
 // raw x, with D on the diagonal, and the state decays explicitly
 // (h~ <- sigma_k exp(lambda_e) h~ + B^T x', sigma = 1).  The per-token
-// factors come precomputed per block (k_prep, from fp64 prefixes).
+// factors come precomputed per block (k_prep, from fp32 prefixes).
 //
 // Workgroup = NW = PB / 32 waves; wave w owns headdim columns 32 w .. 32 w +
 // 31 of the workgroup's PB columns and computes with
@@ -98,11 +98,6 @@ __device__ __forceinline__ bf16x8 lds_b128(const unsigned char *base, int byte_o
 __device__ __forceinline__ bf16x8 join(bf16x4 lo, bf16x4 hi) {
     return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
 }
-__device__ __forceinline__ void dma16(const void *gsrc, unsigned char *lds_wave_base) {
-    __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void *)gsrc,
-                                     (__attribute__((address_space(3))) void *)(lds_wave_base),
-                                     16, 0, 0);
-}
 __device__ __forceinline__ float uniform(float v) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readfirstlane(__builtin_bit_cast(int, v)));
 }
@@ -110,15 +105,31 @@ __device__ __forceinline__ unsigned pack2(float a, float b) {
     typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
     return __builtin_bit_cast(unsigned, bf16x2{(bf16)a, (bf16)b});
 }
-// 16-byte chunk swizzle of the C / B rows and of the raw x rows in LDS (XOR
-// on the chunk index; depends on row & 7 only).  It is a bijection on
-// row & 7, so the fragment reads of 8 consecutive rows (one chunk each) hit 8
-// distinct bank groups, and its bits 1-2 are row & 3, so the transposed reads
-// (4 consecutive rows x one aligned 32-byte window each) land in 4 distinct
-// 32-byte bank windows.
-__device__ __forceinline__ int row_swz(int row) { return 2 * (row & 3) + ((row >> 2) & 1); }
-// raw x rows of 64 bytes (4 chunks): the same two properties
-__device__ __forceinline__ int row_swz4(int row) { return 2 * ((row >> 1) & 1) + ((row >> 2) & 1); }
+// Inclusive prefix sum over each 32-lane half of the wave, without LDS
+// round trips: DPP shifts by 1, 2, 4 and 8 within each 16-lane row (lanes
+// shifted in from outside the row read 0), then lanes 16..31 (48..63) add
+// the row total of lane 15 (47), read with v_readlane.
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v),
+                                                                 CTRL, 0xF, 0xF, true));
+}
+__device__ __forceinline__ float lane_f32(float v, int src) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
+}
+__device__ __forceinline__ float scan32(float v, int lane) {
+    v += dpp_f32<0x111>(v);  // row_shr:1
+    v += dpp_f32<0x112>(v);  // row_shr:2
+    v += dpp_f32<0x114>(v);  // row_shr:4
+    v += dpp_f32<0x118>(v);  // row_shr:8
+    const float r0 = lane_f32(v, 15), r2 = lane_f32(v, 47);
+    return v + ((lane & 16) ? (lane >= 32 ? r2 : r0) : 0.f);
+}
+// the value of lane 31 in lanes 0..31 and of lane 63 in lanes 32..63
+__device__ __forceinline__ float last_of_half(float v, int lane) {
+    const float a = lane_f32(v, 31), c = lane_f32(v, 63);
+    return lane >= 32 ? c : a;
+}
 
 // Workgroup layout.  A workgroup covers PB consecutive columns of one
 // batch's flattened (head, headdim) columns h P + p (x and y rows are
@@ -139,25 +150,28 @@ struct Fused {
     static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
     static constexpr int XRB = 2 * PB;                 // raw x row bytes
     static constexpr int NRS = PB == 128 ? 2 : 1;      // decay-record slots (heads)
-    // one stage: C rows, B rows (column-blocked, blk_off), raw x
-    // (column-blocked) and the decay records (kVecRec floats in 1 KB slots)
-    // of one block, filled by DMA; the causal diagonal block of C B^T in the
-    // MFMA B-fragment order, formed by the producer from the stage's C and B
-    // rows; then the block's y for the producer: 32 rows of XRB bytes,
-    // 16-byte chunk c of row t in slot c ^ ys_swz(t)
+    // one stage: C rows, B rows (column-blocked, blk_off) and raw x
+    // (column-blocked) of one block, filled by DMA, and its dt (token t of
+    // head slot q at DTR + 4 (32 q + t)), filled by the DMAs of the block
+    // before; the causal diagonal block of C B^T in the
+    // MFMA B-fragment order and the decay records (kVecRec floats in 1 KB
+    // slots), formed by the producer from the stage's C and B rows and dt;
+    // then the block's y for the producer: 32 rows of XRB bytes, 16-byte
+    // chunk c of row t in slot c ^ ys_swz(t)
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
     static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
     static constexpr int XR = CBF + 2048;
     static constexpr int VR = XR + kBlk * XRB;
     static constexpr int YS = VR + 1024 * NRS;
-    static constexpr int STG = YS + kBlk * XRB;
+    static constexpr int DTR = YS + kBlk * XRB;
+    static constexpr int STG = DTR + 256;
     // floats of the decay record
     enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
     // four stages: the DMAs of a block go out three blocks ahead of its
-    // use, and a block's stage is complete one block early: the producer
-    // forms its C B^T block and the compute waves read its opening operands
-    // during the block before it
+    // use; the producer forms a block's decay records two blocks ahead and
+    // its C B^T block one block ahead, and the compute waves read its
+    // opening operands during the block before it
     static constexpr int NST = 4;
     // K-step rows m of the C fragments among the opening operands (within
     // the 256 registers per lane that two waves on a SIMD leave each)
@@ -167,18 +181,15 @@ struct Fused {
     static_assert(STG % 16 == 0, "alignment");
     // (one workgroup per compute unit, which the column choice arranges)
     static_assert(LDS <= 160 * 1024, "LDS per compute unit");
-    // the producer's DMAs of a block (C and B, x, records) and y stores.  At
-    // the end of block kb it waits for the DMAs of block kb + 2; younger
-    // than those are the y stores issued right after them and the DMAs and
-    // y stores of block kb + 3
-    static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + NRS;
+    // the producer's DMAs of a block (C and B, x, and the next block's dt)
+    // and y stores.  At the end of block kb it waits for the DMAs of block
+    // kb + 2; younger than those are the y stores issued right after them
+    // and the DMAs and y stores of block kb + 3
+    static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 1;
     static constexpr int P_STORES = kBlk * XRB / 1024;
     static constexpr int P_WAIT = P_STORES + (NST - 3) * (P_LOADS + P_STORES);
     static_assert(P_WAIT < 64, "vmcnt immediate");
 };
-
-template <int PB>
-__device__ __forceinline__ int x_swz(int row) { return PB >= 64 ? row_swz(row) : row_swz4(row); }
 
 // Column-blocked LDS layout of the staged C, B and x tiles (32 rows): the
 // 16-byte chunk c of row t sits at byte blk_off(t, c), so each block of four
@@ -270,8 +281,8 @@ __device__ __forceinline__ int col_of(int q) {
 //             K-step kk).
 template <int PB>
 __global__ void __launch_bounds__(Fused<PB>::NT)
-k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-            const float *__restrict__ vrec,
+k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
+            const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const float *__restrict__ D, const float *init, float *final_state,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
     typedef Fused<PB> S;
@@ -308,21 +319,21 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
         const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
             (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
-        // the records of the workgroup's heads (consecutive (batch, head) rows)
+        // dt of this batch; lane l of the dt DMA reads token l % 32 of head
+        // h0 + l / 32 (heads past the workgroup's are read and not used)
         const int h0 = c0 / P;
-        const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(vrec + ((size_t)b * H + h0) * nblk * kVecRec), 0, S::NRS * nblk * kVecRec * 4,
-            kBufferWord3);
+        const __amdgpu_buffer_rsrc_t rdt = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(dt + (size_t)b * L * H), 0, (unsigned)((size_t)L * H * 4), kBufferWord3);
         const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
-        const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
-        const unsigned v_step = kVecRec * 4;
+        const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2, dt_step = kBlk * H * 4;
         typedef __attribute__((address_space(3))) void lds_void;
         // (the block's byte offset goes in the scalar offset, so a DMA
         // costs no vector instruction)
         auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned soff, unsigned char *dst) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, 0);
         };
+        const unsigned pdt = ((lane & 31) * H + h0 + (lane >> 5)) * 4;
         // Per-lane offsets.  DMA i fills the 1 KB at 1024 i of a
         // column-blocked tile: column block i / 2, rows 16 (i % 2) + lane / 4,
         // slot lane % 4 (so chunk 4 (i / 2) + ((lane % 4) ^ ((t / 4) % 4)) of
@@ -340,8 +351,15 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             const int t = 16 * (i & 1) + (lane >> 2);
             px[i] = t * HP * 2 + 16 * (4 * (i >> 1) + ((lane & 3) ^ ((t >> 2) & 3)));
         }
-        auto pdma = [&](int kb, unsigned char *buf) {
-            const unsigned cbo = kb * cb_step, xo = kb * x_step, vo = kb * v_step;
+        // dt of block kb into `buf` (the stage of block kb)
+        auto pdt_dma = [&](int kb, unsigned char *buf) {
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_void *)(buf + S::DTR), 4, pdt,
+                                                     kb * dt_step, 0, 0);
+        };
+        // the DMAs of block kb into `buf`, and the dt of block kb + 1 into
+        // `nbuf` (the stage of block kb + 1)
+        auto pdma = [&](int kb, unsigned char *buf, unsigned char *nbuf) {
+            const unsigned cbo = kb * cb_step, xo = kb * x_step;
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
                 bdma(rc, pcb[i], cbo, buf + S::CS + 1024 * i);
@@ -349,9 +367,34 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
             }
 #pragma unroll
             for (int i = 0; i < NXD; ++i) bdma(rx, px[i], xo, buf + S::XR + 1024 * i);
-#pragma unroll
-            for (int q = 0; q < S::NRS; ++q)
-                bdma(rv, 16 * lane + q * nblk * v_step, vo, buf + S::VR + 1024 * q);
+            pdt_dma(kb + 1, nbuf);
+        };
+        // The decay record of head slot q = lane / 32 of the block staged in
+        // `buf`, from its dt: lambda_t = sum_{j <= t} dt_j A (fp32, the block's
+        // 32 tokens), lambda_e = lambda_31, and per token
+        //   CF = exp(lambda_e - lambda_t) dt_t, RP = exp(lambda_t - lambda_e)
+        //   (0 when the block is not factored), LR = lambda_t - lambda_e,
+        //   DT = dt_t, then DELTA = exp(lambda_e), FLAG = factored
+        //   (-lambda_e <= 60) and LE = lambda_e.  lambda_e - lambda_t carries
+        // an absolute error of a few units of |lambda_e| 2^-24 (below 1e-4
+        // while the block is factored), the relative error it puts on the
+        // exp factors.
+        const float pa = A[(h0 + (lane >> 5)) < H ? h0 + (lane >> 5) : H - 1];
+        auto prec = [&](unsigned char *buf) {
+            const int t = lane & 31, q = lane >> 5;
+            const float d = *reinterpret_cast<const float *>(buf + S::DTR + 4 * lane);
+            const float lam = scan32(d * pa, lane);
+            const float le = last_of_half(lam, lane);
+            const bool fac = -le <= kSafeDecay;
+            if (q < S::NRS) {
+                float *rec = reinterpret_cast<float *>(buf + S::VR + 1024 * q);
+                rec[S::CF + t] = fast_exp(le - lam) * d;
+                rec[S::RP + t] = fac ? fast_exp(lam - le) : 0.f;
+                rec[S::LR + t] = lam - le;
+                rec[S::DT + t] = d;
+                if (t == kBlk - 1)
+                    *reinterpret_cast<f32x4 *>(rec + S::DELTA) = f32x4{fast_exp(le), fac ? 1.f : 0.f, le, 0.f};
+            }
         };
         // The causal diagonal block of C B^T of the block staged in `buf`,
         // from its C and B rows: E = B C^T on MFMA (A: B row s = lane % 32,
@@ -404,18 +447,25 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
                 __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, py[i], yo, 0);
             }
         };
+        pdt_dma(0, stage(0));
 #pragma unroll
-        for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i));
+        for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i), stage(i + 1));
         __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         pcbt(stage(0));
+        prec(stage(0));
+        prec(stage(1));
         lds_barrier();
-        // block kb: refill the stage block kb - 1 used, store its y, form
-        // the C B^T block of block kb + 1, then wait for the DMAs of block
-        // kb + 2 before the end-of-block barrier
+        // block kb: refill the stage block kb - 1 used (and the dt slot of
+        // block kb + 4 in this block's stage: its records were formed two
+        // blocks ago) and store block kb - 1's y; form the C B^T block of
+        // block kb + 1 and the records of block kb + 2 (whose dt came with
+        // the DMAs of block kb + 1, landed before the last barrier); then
+        // wait for the DMAs of block kb + 2 and the end-of-block barrier
         auto pblock = [&](int kb, const int si) {
-            pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
+            pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
             if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
             pcbt(stage((si + 1) % S::NST));
+            prec(stage((si + 2) % S::NST));
             __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
             lds_barrier();
         };
@@ -724,534 +774,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm, const bf16 
     }
 }
 
-// ------------------------------------------------------------------------
-// The same pass with 16 headdim columns per wave on v_mfma_f32_16x16x32_bf16
-// (operands: lane l holds row (A) / column (B) l % 16 and k = 8 (l / 16) + j,
-// j = 0..7; result register v of lane l is D[4 (l / 16) + v][l % 16]).  A
-// workgroup of NW = PB / 16 waves covers PB columns of one head, so twice as
-// many waves share the work of a head: with two of them on a SIMD, one
-// wave's vector ALU work issues while the other waits, which a single wave
-// per SIMD cannot do.
-//
-// Per wave: headdim columns pw + (0..15), pw = p0 + 16 wave.  With lane l,
-// r = l % 16, g = l / 16:
-//   state     st[mt][v] = h~[n][pw + r], n = 32 (mt / 2) + 8 g + 4 (mt % 2) + v
-//             (the state update's row order), so st[2 kk] and st[2 kk + 1]
-//             together hold n = 32 kk + 8 g + (0..7): the A fragment of
-//             K-step kk of y^T = h~ C^T;
-//   output    acc[tt][v] = y[token 16 tt + r][pw + 4 g + v];
-//   x'        xs = x'[token 8 g + j][pw + r] (the A fragment of the diagonal
-//             block and the B fragment of the state update).
-template <int PB>
-struct Fused16 {
-    static constexpr int NW = PB / 16;                 // waves: 16 headdim columns each
-    static constexpr int NT = 64 * NW;
-    static constexpr int N = 128;
-    static constexpr int ROWB = 2 * N;
-    static constexpr int MAT = kBlk * ROWB;
-    static constexpr int CBD = MAT / 1024 / NW;        // DMAs per matrix and wave
-    static constexpr int XC = PB / 8;                  // 16-byte chunks per x row
-    static constexpr int XRB = 2 * PB;
-    static constexpr int XD = kBlk * XRB / 1024 / NW;  // x DMAs per wave (one)
-    static constexpr int MISC = (3 + NW - 1) / NW;     // C B^T halves and the record
-    static constexpr int CS = 0;
-    static constexpr int BS = MAT;
-    static constexpr int CBF = 2 * MAT;
-    static constexpr int XR = CBF + 2048;
-    static constexpr int VR = XR + kBlk * XRB;
-    static constexpr int STG = VR + 1024;
-    enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
-    static constexpr int LDS = 3 * STG;
-    static constexpr int VM_LOADS = 2 * CBD + XD + MISC;
-    static constexpr int Y_STORES = 2;
-    static_assert(PB == 32 || PB == 64, "two or four waves");
-    static_assert(XD == 1, "x DMAs");
-    static_assert(2 * LDS <= 160 * 1024, "two workgroups per compute unit");
-    static_assert(VM_LOADS + Y_STORES < 64, "vmcnt immediate");
-};
-
-__device__ __forceinline__ f32x4 mma16(bf16x8 a, bf16x8 b, f32x4 c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-}
-
-template <int PB>
-__global__ void __launch_bounds__(64 * (PB / 16))
-k_fused16_ssd(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
-              const bf16 *__restrict__ Cm, const bf16 *__restrict__ cbf,
-              const float *__restrict__ vrec, const float *__restrict__ D, const float *init,
-              float *final_state, bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
-    typedef Fused16<PB> S;
-    constexpr int NW = S::NW, N = S::N;
-    __shared__ __align__(16) unsigned char stg0[S::STG];
-    __shared__ __align__(16) unsigned char stg1[S::STG];
-    __shared__ __align__(16) unsigned char stg2[S::STG];
-
-    const int HP = H * P, GN = G * N;
-    const int npb = P / PB;
-    const int pb = blockIdx.x % npb, h = blockIdx.x / npb, b = blockIdx.y;
-    const int g_grp = h / (H / G);
-    const int tid = threadIdx.x, lane = tid & 63;
-    const int wave = NW == 1 ? 0 : __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int r = lane & 15, g = lane >> 4;
-    const int p0 = pb * PB, pw = p0 + 16 * wave;
-    const size_t bh = (size_t)b * H + h;
-    const float Dh = D ? D[h] : 0.f;
-
-    // ---- per-lane LDS byte offsets (transposed reads: within each 16-lane
-    // group, lane 4 a + c receives element c of the 8-byte reads of lanes a,
-    // a + 4, a + 8, a + 12; here a = lane & 3, e = (lane >> 2) & 3 is the
-    // reading lane's k offset)
-    const int a4 = lane & 3, e4 = (lane >> 2) & 3;
-    // C fragment (tt, kk): token 16 tt + r, chunk 4 kk + g:
-    //   CS + c_rd[kk & 1] + 4096 tt + 128 (kk >> 1)
-    int c_rd[2];
-    {
-        const int sw = row_swz(r);
-#pragma unroll
-        for (int k1 = 0; k1 < 2; ++k1) c_rd[k1] = r * S::ROWB + 16 * ((4 * k1 + g) ^ sw);
-    }
-    // B^T fragment of state tile mt (rows n = 32 (mt / 2) + 8 a + 4 (mt % 2)
-    // + c for the lanes 4 a + c), read half hh: token 8 g + 4 hh + e4:
-    //   BS + b_tr[hh][(mt >> 1) & 1] + 128 (mt >> 2) + 8 (mt & 1)
-    int b_tr[2][2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-#pragma unroll
-        for (int q1 = 0; q1 < 2; ++q1) {
-            const int t = 8 * g + 4 * hh + e4;
-            b_tr[hh][q1] = t * S::ROWB + 16 * ((4 * q1 + a4) ^ row_swz(t));
-        }
-    auto xr_off = [](int t, int c) { return t * S::XRB + 16 * (c ^ x_swz<PB>(t)); };
-    // x^T fragment, read half hh: token 8 g + 4 hh + e4, columns
-    // 16 wave + 4 a4 .. +3:  XR + xs_tr[hh]
-    int xs_tr[2];
-#pragma unroll
-    for (int hh = 0; hh < 2; ++hh)
-        xs_tr[hh] = xr_off(8 * g + 4 * hh + e4, 2 * wave + (a4 >> 1)) + 8 * (a4 & 1);
-    // raw x of the skip term: token 16 tt + r, columns 16 wave + 4 g .. +3
-    int xr_skip[2];
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt) xr_skip[tt] = xr_off(16 * tt + r, 2 * wave + (g >> 1)) + 8 * (g & 1);
-    const int cbf_rd = lane * 16;
-
-    // ---- register-resident scaled state
-    f32x4 st[8];
-#pragma unroll
-    for (int mt = 0; mt < 8; ++mt) {
-        st[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (init) {
-            const int n = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1);
-            const float4 q4 = *reinterpret_cast<const float4 *>(init + (bh * P + pw + r) * N + n);
-            st[mt] = f32x4{q4.x, q4.y, q4.z, q4.w};
-        }
-    }
-
-    auto stage = [&](int i) -> unsigned char * { return i == 0 ? stg0 : (i == 1 ? stg1 : stg2); };
-    const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Cm + (size_t)b * L * GN + (size_t)g_grp * N), 0, (L * GN - g_grp * N) * 2,
-        kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(Bm + (size_t)b * L * GN + (size_t)g_grp * N), 0, (L * GN - g_grp * N) * 2,
-        kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(x + (size_t)b * L * HP + (size_t)h * P + p0), 0, (L * HP - h * P - p0) * 2,
-        kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rcb = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(cbf + ((size_t)b * nblk * G + g_grp) * (kBlk * kBlk)), 0,
-        (nblk * G - g_grp) * (kBlk * kBlk * 2), kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
-        (void *)(vrec + bh * nblk * kVecRec), 0, nblk * kVecRec * 4, kBufferWord3);
-    const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2;
-    const unsigned cbf_step = G * kBlk * kBlk * 2, v_step = kVecRec * 4;
-    unsigned dma_cb[S::CBD], dma_x;
-#pragma unroll
-    for (int i = 0; i < S::CBD; ++i) {
-        const int row = 4 * (wave + NW * i) + (lane >> 4);
-        dma_cb[i] = row * GN * 2 + 16 * ((lane & 15) ^ row_swz(row));
-    }
-    {
-        const int pos = 64 * wave + lane, row = pos / S::XC;
-        dma_x = row * HP * 2 + 16 * ((pos % S::XC) ^ x_swz<PB>(row));
-    }
-    typedef __attribute__((address_space(3))) void lds_void;
-    auto bdma = [](__amdgpu_buffer_rsrc_t rs, unsigned voff, unsigned char *dst) {
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, 0, 0, 0);
-    };
-    // DMA j (0 <= j < VM_LOADS) of block kb into stage `buf`: C and B rows
-    // (alternating), raw x, then this wave's share of the C B^T halves and
-    // the record (past the last piece: the record again)
-    auto dma_piece = [&](int kb, unsigned char *buf, int j) {
-        if (j < 2 * S::CBD) {
-            const int i = j >> 1;
-            const unsigned o = dma_cb[i] + kb * cb_step;
-            if (j & 1)
-                bdma(rb, o, buf + S::BS + 1024 * (wave + NW * i));
-            else
-                bdma(rc, o, buf + S::CS + 1024 * (wave + NW * i));
-        } else if (j < 2 * S::CBD + S::XD) {
-            bdma(rx, dma_x + kb * x_step, buf + S::XR + 1024 * wave);
-        } else {
-            int pc = wave + NW * (j - 2 * S::CBD - S::XD);
-            if (pc > 2) pc = 2;
-            const bool half = pc < 2;
-            bdma(half ? rcb : rv,
-                 half ? 16 * (64 * pc + lane) + kb * cbf_step : 16 * lane + kb * v_step,
-                 buf + (half ? S::CBF + 1024 * pc : S::VR));
-        }
-    };
-    auto dma_block = [&](int kb, unsigned char *buf) {
-#pragma unroll
-        for (int j = 0; j < S::VM_LOADS; ++j) dma_piece(kb, buf, j);
-    };
-    const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-        y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
-    const int y_boff = (r * HP + h * P + pw + 4 * g) * 2;
-    auto y_store = [&](int kb, const f32x4 (&acc)[2]) {
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) {
-            const u32x2 v = {pack2(acc[tt][0], acc[tt][1]), pack2(acc[tt][2], acc[tt][3])};
-            __builtin_amdgcn_raw_buffer_store_b64(v, y_rsrc,
-                                                  y_boff + (kb * kBlk + 16 * tt) * HP * 2, 0, 0);
-        }
-    };
-
-    dma_block(0, stg0);
-    dma_block(1, stg1);
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-    lds_barrier();
-    float sig_out = 1.f;
-
-    struct Ops {
-        bf16x8 cfr[2][4];  // C fragments (tt, kk)
-        bf16x8 xs;         // raw x^T
-        f32x4 cfv[2];      // cf of tokens 8 g + 0..7
-        bf16x8 cbv[2];     // causal diagonal block of C B^T, t-tiles 0 and 1
-        bf16x8 bt[8];      // B^T fragments of the state tiles
-    };
-    auto load_ops = [&](const unsigned char *cur, Ops &o) {
-        const float *v = reinterpret_cast<const float *>(cur + S::VR);
-#pragma unroll
-        for (int w4 = 0; w4 < 2; ++w4)
-            o.cfv[w4] = *reinterpret_cast<const f32x4 *>(v + S::CF + 8 * g + 4 * w4);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt)
-                o.cfr[tt][kk] = lds_b128(cur, S::CS + c_rd[kk & 1] + 4096 * tt + 128 * (kk >> 1));
-        o.xs = join(lds_tr(cur, S::XR + xs_tr[0]), lds_tr(cur, S::XR + xs_tr[1]));
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) o.cbv[tt] = lds_b128(cur, S::CBF + 1024 * tt + cbf_rd);
-    };
-    auto load_bt = [&](const unsigned char *cur, Ops &o, int mt) {
-        const int off = 128 * (mt >> 2) + 8 * (mt & 1);
-        o.bt[mt] = join(lds_tr(cur, S::BS + b_tr[0][(mt >> 1) & 1] + off),
-                        lds_tr(cur, S::BS + b_tr[1][(mt >> 1) & 1] + off));
-    };
-
-    auto block = [&](int kb, const int si) {
-        unsigned char *cur = stage(si);
-        const float *v = reinterpret_cast<const float *>(cur + S::VR);
-        const Book bk = book_of(v, sig_out);
-        Ops o;
-        load_ops(cur, o);
-        float rpv[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) rpv[tt] = v[S::RP + 16 * tt + r];
-        bf16x4 xr[2];
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt)
-            xr[tt] = *reinterpret_cast<const bf16x4 *>(cur + S::XR + xr_skip[tt]);
-        const float xscale = bk.fac ? __builtin_amdgcn_rcpf(bk.sig) : 1.f;
-        auto hb_of = [&](int kk) {
-            bf16x8 hb;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                hb[j] = (bf16)st[2 * kk][j];
-                hb[4 + j] = (bf16)st[2 * kk + 1][j];
-            }
-            return hb;
-        };
-        bf16x8 xp;
-        f32x4 acc[2];
-        acc[0] = f32x4{0.f, 0.f, 0.f, 0.f};
-        acc[1] = acc[0];
-        bf16x8 hb = hb_of(0);
-        __builtin_amdgcn_sched_barrier(0);
-        // y^T = h~ C^T: eight MFMAs (K-step kk, t-tile tt), each followed by
-        // the next state conversion, one x' value and a B^T fragment
-#pragma unroll
-        for (int q = 0; q < 8; ++q) {
-            const int kk = q >> 1, tt = q & 1;
-            acc[tt] = mma16(hb, o.cfr[tt][kk], acc[tt]);
-            __builtin_amdgcn_sched_barrier(0);
-            if (tt == 1 && kk < 3) hb = hb_of(kk + 1);
-            if (q & 1) {
-                // x' values q - 1 and q (tokens 8 g + q - 1, 8 g + q)
-#pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const int j = q - 1 + e;
-                    xp[j] = (bf16)((float)o.xs[j] * (o.cfv[j >> 2][j & 3] * xscale));
-                }
-            }
-            load_bt(cur, o, q);
-            __builtin_amdgcn_sched_barrier(0);
-        }
-        asm volatile("" : "+v"(xp));
-        float f[2] = {rpv[0] * bk.sig, rpv[1] * bk.sig};
-        float dco = Dh;
-        if (bk.rescale) {
-            __builtin_amdgcn_sched_barrier(0);
-            acc[0] *= bk.sig_in;
-            acc[1] *= bk.sig_in;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) st[mt] *= bk.sig_in;
-        }
-        if (!bk.fac) {
-            __builtin_amdgcn_sched_barrier(0);
-            // exact block (see the wave-of-32 kernel): per-element weights
-            // exp(lambda_t - lambda_s) dt_s on raw x, D on the diagonal
-#pragma unroll
-            for (int tt = 0; tt < 2; ++tt) {
-                const int t = 16 * tt + r;
-                const float lr = v[S::LR + t];
-                acc[tt] *= fast_exp(lr + v[S::LE]) * bk.sig_in;
-                bf16x8 wgt;
-#pragma unroll
-                for (int j = 0; j < 8; ++j) {
-                    const int s = 8 * g + j;
-                    const float w = (float)o.cbv[tt][j] * fast_exp(fminf(lr - v[S::LR + s], 0.f)) *
-                                        v[S::DT + s] + (s == t ? Dh : 0.f);
-                    wgt[j] = (bf16)(s <= t ? w : 0.f);
-                }
-                acc[tt] = mma16(o.xs, wgt, acc[tt]);
-                o.cbv[tt] = zero_frag<bf16>();
-            }
-            f[0] = f[1] = 1.f;
-            dco = 0.f;
-            const float sd = bk.sig_in * bk.delta;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) st[mt] *= sd;
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int tt = 0; tt < 2; ++tt) acc[tt] = mma16(xp, o.cbv[tt], acc[tt]);
-        __builtin_amdgcn_sched_barrier(0);
-        // state update h~ += B^T x' (eight tiles), with the epilogue and the
-        // DMAs of block kb + 2 issued between the MFMAs
-        {
-            unsigned char *nbuf = stage((si + 2) % 3);
-            int j = 0;
-#pragma unroll
-            for (int mt = 0; mt < 8; ++mt) {
-                st[mt] = mma16(o.bt[mt], xp, st[mt]);
-                __builtin_amdgcn_sched_barrier(0);
-                const int jn = (S::VM_LOADS * (mt + 1)) / 8;
-                for (; j < jn; ++j) dma_piece(kb + 2, nbuf, j);
-                if (mt >= 2 && mt < 6) {
-                    // output values 2 (mt - 2), 2 (mt - 2) + 1 of both t-tiles
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        const int vv = 2 * (mt - 2) + e, tt = vv >> 2, c = vv & 3;
-                        acc[tt][c] = acc[tt][c] * f[tt] + dco * (float)xr[tt][c];
-                    }
-                    asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
-                }
-                __builtin_amdgcn_sched_barrier(0);
-            }
-        }
-        asm volatile("" : "+v"(acc[0]), "+v"(acc[1]));
-        sig_out = bk.sig;
-        __builtin_amdgcn_sched_barrier(0);
-        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::VM_LOADS + S::Y_STORES));
-        __builtin_amdgcn_sched_barrier(0);
-        y_store(kb, acc);
-        __builtin_amdgcn_sched_barrier(0);
-        block_barrier();
-    };
-
-    for (int kb = 0; kb < nblk; kb += 3) {
-        block(kb, 0);
-        if (kb + 1 < nblk) {
-            block(kb + 1, 1);
-            if (kb + 2 < nblk) block(kb + 2, 2);
-        }
-    }
-    __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-
-    if (final_state) {
-#pragma unroll
-        for (int mt = 0; mt < 8; ++mt) {
-            const int n = 32 * (mt >> 1) + 8 * g + 4 * (mt & 1);
-            *reinterpret_cast<float4 *>(final_state + (bh * P + pw + r) * N + n) =
-                make_float4(st[mt][0] * sig_out, st[mt][1] * sig_out, st[mt][2] * sig_out,
-                            st[mt][3] * sig_out);
-        }
-    }
-}
-
-// Inclusive prefix sum of an fp64 value over each 32-lane half of the wave,
-// without LDS round trips: DPP shifts by 1, 2, 4 and 8 within each 16-lane
-// row (lanes shifted in from outside the row read 0), then lanes 16..31
-// (48..63) add the row total of lane 15 (47), read with v_readlane.
-template <int CTRL, int ROW_MASK>
-__device__ __forceinline__ double dpp_f64(double v) {
-    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-    const int lo = __builtin_amdgcn_update_dpp(0, (int)(unsigned)u, CTRL, ROW_MASK, 0xF, true);
-    const int hi = __builtin_amdgcn_update_dpp(0, (int)(unsigned)(u >> 32), CTRL, ROW_MASK, 0xF, true);
-    return __builtin_bit_cast(double, (unsigned long long)(unsigned)lo |
-                                          ((unsigned long long)(unsigned)hi << 32));
-}
-__device__ __forceinline__ double lane_f64(double v, int src) {
-    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-    const unsigned lo = __builtin_amdgcn_readlane((unsigned)u, src);
-    const unsigned hi = __builtin_amdgcn_readlane((unsigned)(u >> 32), src);
-    return __builtin_bit_cast(double, (unsigned long long)lo | ((unsigned long long)hi << 32));
-}
-__device__ __forceinline__ double scan32_f64(double v, int lane) {
-    v += dpp_f64<0x111, 0xF>(v);  // row_shr:1
-    v += dpp_f64<0x112, 0xF>(v);  // row_shr:2
-    v += dpp_f64<0x114, 0xF>(v);  // row_shr:4
-    v += dpp_f64<0x118, 0xF>(v);  // row_shr:8
-    const double r0 = lane_f64(v, 15), r2 = lane_f64(v, 47);
-    return v + ((lane & 16) ? (lane >= 32 ? r2 : r0) : 0.0);
-}
-// the value of lane 31 in lanes 0..31 and of lane 63 in lanes 32..63
-__device__ __forceinline__ double last_of_half(double v, int lane) {
-    const unsigned long long u = __builtin_bit_cast(unsigned long long, v);
-    const unsigned lo = (unsigned)u, hi = (unsigned)(u >> 32);
-    const unsigned lo0 = __builtin_amdgcn_readlane(lo, 31), hi0 = __builtin_amdgcn_readlane(hi, 31);
-    const unsigned lo1 = __builtin_amdgcn_readlane(lo, 63), hi1 = __builtin_amdgcn_readlane(hi, 63);
-    const bool up = lane >= 32;
-    return __builtin_bit_cast(double, (unsigned long long)(up ? lo1 : lo0) |
-                                          ((unsigned long long)(up ? hi1 : hi0) << 32));
-}
-
-// Per-block preparation of the fused pass, in one launch.  grid (n_rec +
-// n_cb, batch), 256 threads.
-//
-// Workgroups [0, n_rec): the decay records (one per batch, head and 32-token
-// block; layout at kVecRec) of kPrepBlocks consecutive blocks of 8 heads.
-// All their dt values are staged through LDS first (32-byte runs over
-// heads), then each half-wave takes one head and block at a time: the fp64
-// prefix sum of dt A over the block's 32 tokens (dt A is exact in fp64), so
-// lambda_l - lambda_s is the difference of two fp64 prefixes rounded once.
-//
-// Workgroups [n_rec, n_rec + n_cb) (launched for the 16-column kernel; the
-// 32-column kernel forms these blocks itself from its staged C and B rows):
-// the causal diagonal 32x32 block of C B^T for four (block, group) pairs,
-// one per wave, bf16, in the MFMA B-fragment order the fused kernel reads.  W16 = 0 (waves of 32 columns,
-// v_mfma_f32_32x32x16_bf16): K-step kk, lane L hold the 8 values
-// C B^T[L % 32][16 kk + 8 (L / 32) .. +7] as the 16 bytes at (64 kk + L) * 16.
-// W16 = 1 (waves of 16 columns, v_mfma_f32_16x16x32_bf16): token tile tt,
-// lane L hold C B^T[16 tt + L % 16][8 (L / 16) .. +7] at (64 tt + L) * 16.
-// A wave computes E = B C^T with v_mfma_f32_32x32x16_bf16 (all its row loads
-// issued first; rows past the sequence end read as zeros through the buffer
-// resource's range): lane (l = L % 32, hi) ends with E[s][l] = C_l . B_s for
-// s = 8 i + 4 hi + c, four runs of 4 consecutive s.
-constexpr int kPrepBlocks = 8;
-template <int W16>
-__global__ void __launch_bounds__(256)
-k_prep(const float *__restrict__ dt, const float *__restrict__ A, float *__restrict__ vrec,
-       const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm, bf16 *__restrict__ cbf, int L,
-       int H, int G, int nblk, int n_rec) {
-    const int b = blockIdx.y, tid = threadIdx.x, lane = tid & 63;
-    if ((int)blockIdx.x < n_rec) {
-        __shared__ float s_dt[kPrepBlocks][kBlk][9];
-        const int nbg = (nblk + kPrepBlocks - 1) / kPrepBlocks;
-        const int kb0 = (blockIdx.x % nbg) * kPrepBlocks, h0 = (blockIdx.x / nbg) * 8;
-        const int hh = tid >> 5, tt = tid & 31, h = h0 + hh;
-        float af = A[h < H ? h : H - 1];
-        {
-            // (loads through a buffer resource over this batch's dt: tokens
-            // past the end read as zeros, and all loads issue before any
-            // wait; heads past H feed only half-waves that return below)
-            const __amdgpu_buffer_rsrc_t rdt = __builtin_amdgcn_make_buffer_rsrc(
-                (void *)(dt + (size_t)b * L * H), 0, (unsigned)((size_t)L * H * 4), kBufferWord3);
-            const int lt = tid >> 3, lh = tid & 7;
-            float v[kPrepBlocks];
-#pragma unroll
-            for (int i = 0; i < kPrepBlocks; ++i)
-                v[i] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(
-                    rdt, (unsigned)(((kb0 + i) * kBlk + lt) * H + h0 + lh) * 4, 0, 0));
-#pragma unroll
-            for (int i = 0; i < kPrepBlocks; ++i) s_dt[i][lt][lh] = v[i];
-            // (A is read here, with the dt loads in flight, not after the
-            // barrier)
-            asm volatile("" : "+v"(af));
-        }
-        const double a = (double)af;
-        __syncthreads();
-        if (h >= H) return;  // whole half-waves, after the only barrier
-        float *const rec0 = vrec + (((size_t)b * H + h) * nblk + kb0) * kVecRec;
-#pragma unroll
-        for (int i = 0; i < kPrepBlocks; ++i) {
-            if (kb0 + i >= nblk) break;
-            const float d = s_dt[i][tt][hh];
-            const double lam = scan32_f64((double)d * a, lane);
-            const double lam_e = last_of_half(lam, lane);
-            const float le = (float)lam_e;
-            const bool fac = -le <= kSafeDecay;
-            float *const rec = rec0 + i * kVecRec;
-            rec[tt] = fast_exp((float)(lam_e - lam)) * d;
-            rec[kBlk + tt] = fac ? fast_exp((float)(lam - lam_e)) : 0.f;
-            // the per-element exponents and steps are read by exact blocks only
-            if (!fac) {
-                rec[2 * kBlk + tt] = (float)(lam - lam_e);
-                rec[3 * kBlk + tt] = d;
-            }
-            if (tt == kBlk - 1)
-                *reinterpret_cast<float4 *>(rec + 4 * kBlk) =
-                    make_float4(fast_exp(le), fac ? 1.f : 0.f, le, 0.f);
-        }
-        return;
-    }
-    constexpr int N = 128;
-    // (the wave index read as uniform, so that the buffer resources below
-    // stay in scalar registers)
-    const int pair = (blockIdx.x - n_rec) * 4 + __builtin_amdgcn_readfirstlane(tid >> 6);
-    if (pair >= nblk * G) return;
-    const int kb = pair / G, g = pair % G;
-    const int r = lane & 31, hi = lane >> 5;
-    const size_t base = ((size_t)b * L * G + g) * N;
-    const unsigned range = (unsigned)(((size_t)L * G * N - (size_t)g * N) * 2);
-    const __amdgpu_buffer_rsrc_t rbr = __builtin_amdgcn_make_buffer_rsrc((void *)(Bm + base), 0, range, kBufferWord3);
-    const __amdgpu_buffer_rsrc_t rcr = __builtin_amdgcn_make_buffer_rsrc((void *)(Cm + base), 0, range, kBufferWord3);
-    const unsigned roff = (unsigned)((kb * kBlk + r) * G * N + 8 * hi) * 2;
-    u32x4 bs[N / 16], cl[N / 16];
-#pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks) {
-        bs[ks] = __builtin_amdgcn_raw_buffer_load_b128(rbr, roff + 32 * ks, 0, 0);  // A: row s = r
-        cl[ks] = __builtin_amdgcn_raw_buffer_load_b128(rcr, roff + 32 * ks, 0, 0);  // B: column l = r
-    }
-    f32x16 acc;
-#pragma unroll
-    for (int v = 0; v < 16; ++v) acc[v] = 0.f;
-#pragma unroll
-    for (int ks = 0; ks < N / 16; ++ks)
-        acc = mma32(__builtin_bit_cast(bf16x8, bs[ks]), __builtin_bit_cast(bf16x8, cl[ks]), acc);
-    bf16 *out = cbf + (((size_t)b * nblk + kb) * G + g) * (kBlk * kBlk);
-    // lane (l = r, hi): E[s][l] for s = 8 i + 4 hi + c
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s0 = 8 * i + 4 * hi;
-        bf16x4 v4;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) v4[c] = s0 + c <= r ? (bf16)acc[4 * i + c] : (bf16)0.f;
-        size_t dst;
-        if (W16) {
-            // t-tile r / 16, lane (r % 16) + 16 (s0 / 8), values s0 % 8 .. +3
-            dst = (64 * (r >> 4) + (r & 15) + 16 * (s0 >> 3)) * 8 + (s0 & 7);
-        } else {
-            const int kk = s0 >> 4, hs = (s0 >> 3) & 1;
-            dst = (64 * kk + r + 32 * hs) * 8 + (s0 & 7);
-        }
-        *reinterpret_cast<bf16x4 *>(out + dst) = v4;
-    }
-}
-
 // --------------------------------------------------------------------- launch
 
-const char *const kFusedKernelNames[kFusedKernels] = {"k_prep", "k_fused_ssd"};
+const char *const kFusedKernelNames[kFusedKernels] = {"k_fused_ssd"};
 
 template <typename T>
 bool fused_supported(int P, int N, int Q) {
@@ -1264,32 +789,11 @@ template bool fused_supported<bf16>(int, int, int);
 int fused_nblk(int L) { return (L + kBlk - 1) / kBlk; }
 
 template <int PB>
-static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
+static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
-    const int nblk = fused_nblk(a.L);
     hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
-                       (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C, a.vrec, a.D,
-                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, nblk);
-    return hipSuccess;
-}
-
-template <int PB>
-static hipError_t launch_fused16_main(const ForwardArgs &a, hipStream_t stream) {
-    typedef Fused16<PB> S;
-    const int nblk = fused_nblk(a.L);
-    hipLaunchKernelGGL((k_fused16_ssd<PB>), dim3(a.H * (a.P / PB), a.batch), dim3(S::NT), 0,
-                       stream, (const bf16 *)a.x, (const bf16 *)a.B, (const bf16 *)a.C,
-                       (const bf16 *)a.cb, a.vrec, a.D, a.init, a.final_state, (bf16 *)a.y,
-                       a.L, a.H, a.G, a.P, nblk);
-    return hipSuccess;
-}
-
-// Waves of 32 columns unless SSD_FUSED_WAVE=16 asks for waves of 16 (a
-// diagnostic switch for comparing the two layouts).
-static bool use_wave16(const ForwardArgs &a) {
-    (void)a;
-    const char *env = getenv("SSD_FUSED_WAVE");
-    return env && strcmp(env, "16") == 0;
+                       (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C, a.D,
+                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, fused_nblk(a.L));
 }
 
 // Columns per workgroup.  One workgroup per compute unit is the target
@@ -1305,41 +809,20 @@ static int pick_pb(const ForwardArgs &a) {
     return 32;
 }
 
+// The fused forward is one launch.
 template <typename T>
 hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
     if (sizeof(T) != 2) return hipErrorInvalidValue;  // bf16 only (fused_supported)
-    int ev = 0;
-    auto mark = [&]() -> hipError_t {
-        return events ? hipEventRecord(events[ev++], stream) : hipSuccess;
-    };
-    const int nblk = fused_nblk(a.L);
     hipError_t err;
-    if ((err = mark()) != hipSuccess) return err;
-    const bool w16 = use_wave16(a);
-    const int n_rec = (nblk + kPrepBlocks - 1) / kPrepBlocks * ((a.H + 7) / 8);
-    // (the 32-column kernel forms its C B^T blocks itself)
-    const int n_cb = w16 ? (nblk * a.G + 3) / 4 : 0;
-    if (w16)
-        hipLaunchKernelGGL(k_prep<1>, dim3(n_rec + n_cb, a.batch), dim3(256), 0, stream, a.dt, a.A,
-                           a.vrec, (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.H,
-                           a.G, nblk, n_rec);
-    else
-        hipLaunchKernelGGL(k_prep<0>, dim3(n_rec + n_cb, a.batch), dim3(256), 0, stream, a.dt, a.A,
-                           a.vrec, (const bf16 *)a.B, (const bf16 *)a.C, (bf16 *)a.cb, a.L, a.H,
-                           a.G, nblk, n_rec);
-    if ((err = mark()) != hipSuccess) return err;
-    if (w16) {
-        err = a.P % 64 == 0 ? launch_fused16_main<64>(a, stream) : launch_fused16_main<32>(a, stream);
-    } else {
-        switch (pick_pb(a)) {
-            case 128: err = launch_fused_main<128>(a, stream); break;
-            case 64: err = launch_fused_main<64>(a, stream); break;
-            default: err = launch_fused_main<32>(a, stream); break;
-        }
+    if (events && (err = hipEventRecord(events[0], stream)) != hipSuccess) return err;
+    switch (pick_pb(a)) {
+        case 128: launch_fused_main<128>(a, stream); break;
+        case 64: launch_fused_main<64>(a, stream); break;
+        default: launch_fused_main<32>(a, stream); break;
     }
-    if (err != hipSuccess) return err;
-    if ((err = mark()) != hipSuccess) return err;
-    return hipGetLastError();
+    if ((err = hipGetLastError()) != hipSuccess) return err;
+    if (events && (err = hipEventRecord(events[1], stream)) != hipSuccess) return err;
+    return hipSuccess;
 }
 
 template hipError_t launch_fused_forward<float>(const ForwardArgs &, hipStream_t, hipEvent_t *);

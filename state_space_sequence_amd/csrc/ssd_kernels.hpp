@@ -29,15 +29,12 @@ struct ForwardArgs {
     float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
     float *dtT;      // [b][H][nc][Q]  dt per chunk, 0 past seqlen
     void *cb;        // split path: C B^T per chunk and group, fp32 [b][nc][G][Q][Q]
-                     // fused path: diagonal 32x32 blocks, bf16 [b][nblk][G][32 * 32]
-                     // in MFMA fragment order
     float *S;        // split path: chunk states [b][nc][H][P][N]
-    float *vrec;     // fused path: per-block decay records [b][H][nblk][kVecRec]
                      // (acum_hi / acum_lo / dtT unused there)
 };
 
-// Fused path: one record of floats per (batch, head, 32-token block) with the
-// per-token decay factors the block needs: [0, 32) cf_s = exp(lambda_e -
+// Fused path: the decay record of one (batch, head, 32-token block), as the
+// fused kernel keeps it in LDS, floats: [0, 32) cf_s = exp(lambda_e -
 // lambda_s) dt_s, [32, 64) rp_l = exp(lambda_l - lambda_e) (0 when the block
 // is not factored), [64, 96) lambda_l - lambda_e, [96, 128) dt_l, then
 // delta = exp(lambda_e), the factored flag (1 or 0) and lambda_e.  528 bytes,
@@ -52,7 +49,7 @@ constexpr int kVecRec = 132;
 enum class Path { Split, Fused };
 
 constexpr int kSplitKernels = 5;
-constexpr int kFusedKernels = 2;
+constexpr int kFusedKernels = 1;
 constexpr int kMaxForwardKernels = 5;
 extern const char *const kSplitKernelNames[kSplitKernels];
 extern const char *const kFusedKernelNames[kFusedKernels];
@@ -66,11 +63,10 @@ template <typename T>
 hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream,
                                 hipEvent_t *events = nullptr);
 template <typename T> bool fused_supported(int P, int N, int Q);
-// Tokens per block of the fused path and the number of blocks for L tokens.
-constexpr int kFusedBlock = 32;
+// The number of 32-token blocks of the fused path for L tokens.
 int fused_nblk(int L);
 
-// k1 (shared by both paths).
+// k1 of the split path.
 void launch_dA_cumsum(const float *dt, const float *A, float *acum_hi, float *acum_lo,
                       float *dtT, int batch, int L, int H, int nc, int Q, hipStream_t stream);
 

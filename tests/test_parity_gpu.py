@@ -34,14 +34,11 @@ def dev():
     return torch.device("cuda:0")
 
 
-@pytest.fixture(params=["split", "fused", "fused16"])
+@pytest.fixture(params=["split", "fused"])
 def path(request, monkeypatch):
     """Run the test through one forward path (the library reads
-    SSD_FORWARD_PATH and SSD_FUSED_WAVE on every call): the split kernels,
-    the fused pass with waves of 32 headdim columns (the default), or the
-    fused pass with waves of 16."""
-    monkeypatch.setenv("SSD_FORWARD_PATH", "split" if request.param == "split" else "fused")
-    monkeypatch.setenv("SSD_FUSED_WAVE", "16" if request.param == "fused16" else "32")
+    SSD_FORWARD_PATH on every call): the split kernels or the fused pass."""
+    monkeypatch.setenv("SSD_FORWARD_PATH", request.param)
     return request.param
 
 
@@ -269,7 +266,7 @@ def test_timed_variant_matches_and_names_kernels(dev, path):
         assert names == ["k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing",
                          "k5_chunk_scan"]
     else:
-        assert names == ["k_prep", "k_fused_ssd"]
+        assert names == ["k_fused_ssd"]
     for e in evs:
         hip.hipEventDestroy(__import__("ctypes").c_void_p(e))
 
