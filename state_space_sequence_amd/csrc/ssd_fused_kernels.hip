@@ -296,7 +296,19 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     __shared__ __align__(16) unsigned char stg3[S::NST > 3 ? S::STG : 16];
 
     const int HP = H * P, GN = G * N;
-    const int c0 = blockIdx.x * PB, b = blockIdx.y;
+    // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8),
+    // each XCD with its own L2.  With a multiple of 8 workgroups, XCD x gets
+    // the consecutive range x * n / 8 .. of (batch, column block) pairs, so
+    // a batch's workgroups share few L2s and fetch its C, B and dt rows a few
+    // times instead of once per XCD.
+    int c0, b;
+    {
+        const int nc = H * P / PB, n = nc * gridDim.y;
+        const int i = blockIdx.y * nc + blockIdx.x;
+        const int v = (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+        c0 = (v % nc) * PB;
+        b = v / nc;
+    }
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
