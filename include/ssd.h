@@ -79,12 +79,12 @@ const char *ssd_status_string(ssd_status status);
  * Bytes of device workspace `ssd_chunk_scan_fwd` needs for this problem,
  * written to *bytes.  The same validation as `ssd_chunk_scan_fwd` is applied
  * (pointers aside); on error *bytes is left unchanged.  The workspace holds
- * the per-chunk intermediates of the chunked algorithm (decay prefix sums,
- * the C B^T blocks and the per-chunk fp32 states) and needs no
+ * the per-chunk intermediates of the chunked algorithm and needs no
  * initialisation.  It depends on the forward path (see
- * ssd_chunk_scan_fwd_timed): the split path keeps every chunk state
- * (batch * nchunks * nheads * headdim * dstate fp32), the fused path only
- * per-token decay vectors and the diagonal blocks of C B^T.
+ * ssd_chunk_scan_fwd_timed): the split path keeps the decay prefix sums,
+ * the C B^T blocks and every chunk state (batch * nchunks * nheads *
+ * headdim * dstate fp32); the fused path keeps every intermediate on chip
+ * and needs none (0 bytes).
  */
 ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
                                              int headdim, int dstate,
@@ -104,6 +104,7 @@ ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
  *   y             [batch, seqlen, nheads, headdim]    io_dtype   out
  *   final_state   [batch, nheads, headdim, dstate]    fp32       out, NULL = skip
  *   workspace     >= ssd_chunk_scan_fwd_workspace_size bytes, 256-byte aligned
+ *                 (ignored, and may be NULL, when that size is 0)
  *
  * chunk_len is the chunk length Q of the chunked algorithm; the sequence is
  * processed as ceil(seqlen / Q) chunks and a ragged last chunk behaves as if
@@ -140,12 +141,12 @@ int ssd_chunk_scan_fwd_max_kernels(void);
  * SSD_ERR_INVALID_ARGUMENT.  A failed event record returns SSD_ERR_HIP.
  *
  * Forward path.  bf16 shapes with dstate 128 and headdim a multiple of 32
- * run the fused path: k1 (prefix sums per 32-token block), k2b (the
- * diagonal 32x32 blocks of C B^T) and one kernel that walks the sequence in
- * 32-token blocks with the fp32 state in registers and writes y; inside a
- * chunk it contracts the off-diagonal blocks of L o C B^T through the
- * running state (their rank-dstate factorisation), so its work and result
- * do not depend on chunk_len.  Other shapes run the five-kernel split
+ * run the fused path: one kernel that walks the sequence in 32-token
+ * blocks with the fp32 state in registers, forms each block's decay
+ * prefix sums and diagonal 32x32 block of C B^T on chip, and writes y;
+ * inside a chunk it contracts the off-diagonal blocks of L o C B^T through
+ * the running state (their rank-dstate factorisation), so its work and
+ * result do not depend on chunk_len.  Other shapes run the five-kernel split
  * (k1 .. k5) with the given chunk_len as its chunk size.  The environment variable
  * SSD_FORWARD_PATH=split|fused overrides the choice for diagnostics
  * (forcing "fused" where it does not apply returns SSD_ERR_UNSUPPORTED);
