@@ -85,6 +85,7 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 typedef __attribute__((address_space(3))) unsigned char lds_u8;
 
@@ -139,11 +140,12 @@ __device__ __forceinline__ float last_of_half(float v, int lane) {
 template <int PB>
 struct Fused {
     static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
-    // One more wave (the producer) issues every global memory operation of
-    // the workgroup: the DMAs of the stages and the y stores, which the
-    // compute waves hand over through LDS.  The compute waves never wait on
-    // the vector memory pipeline.
-    static constexpr int NT = 64 * (NW + 1);           // threads
+    // Two more waves.  The first (the loader) issues every global memory
+    // operation of the workgroup: the DMAs of the stages and the y stores,
+    // which the compute waves hand over through LDS; the compute waves never
+    // wait on the vector memory pipeline.  The second (the former) forms each
+    // block's decay records and C B^T block in LDS.
+    static constexpr int NT = 64 * (NW + 2);           // threads
     static constexpr int N = 128;                      // dstate
     static constexpr int ROWB = 2 * N;                 // bytes per C / B row
     static constexpr int MAT = kBlk * ROWB;            // 8 KB per matrix
@@ -155,8 +157,8 @@ struct Fused {
     // head slot q at DTR + 4 (32 q + t)), filled by the DMAs of the block
     // before; the causal diagonal block of C B^T in the
     // MFMA B-fragment order and the decay records (kVecRec floats in 1 KB
-    // slots), formed by the producer from the stage's C and B rows and dt;
-    // then the block's y for the producer: 32 rows of XRB bytes, 16-byte
+    // slots), formed by the former from the stage's C and B rows and dt;
+    // then the block's y for the loader: 32 rows of XRB bytes, 16-byte
     // chunk c of row t in slot c ^ ys_swz(t)
     static constexpr int CS = 0;
     static constexpr int BS = MAT;
@@ -167,9 +169,10 @@ struct Fused {
     static constexpr int DTR = YS + kBlk * XRB;
     static constexpr int STG = DTR + 256;
     // floats of the decay record
-    enum { CF = 0, RP = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130 };
+    enum { W = 0, F = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130, SIGIN = 131,
+           SIGOUT = 132, RESC = 133 };
     // four stages: the DMAs of a block go out three blocks ahead of its
-    // use; the producer forms a block's decay records two blocks ahead and
+    // use; the former forms a block's decay records two blocks ahead and
     // its C B^T block one block ahead, and the compute waves read its
     // opening operands during the block before it
     static constexpr int NST = 4;
@@ -181,7 +184,7 @@ struct Fused {
     static_assert(STG % 16 == 0, "alignment");
     // (one workgroup per compute unit, which the column choice arranges)
     static_assert(LDS <= 160 * 1024, "LDS per compute unit");
-    // the producer's DMAs of a block (C and B, x, and the next block's dt)
+    // the loader's DMAs of a block (C and B, x, and the next block's dt)
     // and y stores.  At the end of block kb it waits for the DMAs of block
     // kb + 2; younger than those are the y stores issued right after them
     // and the DMAs and y stores of block kb + 3
@@ -223,31 +226,6 @@ __device__ __forceinline__ void lds_barrier() {
 // is needed before it; an lgkmcnt(0) here would also wait for this block's
 // DMAs into LDS still in flight (they count on that counter as well).
 __device__ __forceinline__ void block_barrier() { asm volatile("s_barrier" ::: "memory"); }
-
-// Scale bookkeeping of one block (identical in every wave of a head).
-struct Book {
-    float sig_in;   // sigma entering the block
-    float sig;      // sigma after the block
-    float delta;    // exp(lambda_e)
-    bool fac;       // factored diagonal
-    bool rescale;   // restart the scale: h~ *= sig_in, sigma_in = 1 (factored blocks only)
-};
-
-// Bookkeeping of a block from its decay record's delta and factored flag
-// (the same in every lane) and the sigma entering it.
-__device__ __forceinline__ Book book_of(float dl, float fc, float sig_in) {
-    Book bk;
-    bk.sig_in = sig_in;
-    bk.delta = uniform(dl);
-    bk.fac = uniform(fc) != 0.f;
-    const float p = sig_in * bk.delta;
-    bk.rescale = bk.fac && p < kRescale;
-    bk.sig = bk.fac ? (bk.rescale ? bk.delta : p) : 1.f;
-    return bk;
-}
-__device__ __forceinline__ Book book_of(const float *rec, float sig_in) {
-    return book_of(rec[kVecRec - 4], rec[kVecRec - 3], sig_in);
-}
 
 // MFMA operands of v_mfma_f32_32x32x16_bf16: lane l holds row (A) / column
 // (B) l % 32 and k = 8 (l / 32) + j, j = 0..7; result register v of lane l
@@ -317,8 +295,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         return i == 0 ? stg0 : (i == 1 ? stg1 : (i == 2 ? stg2 : stg3));
     };
 
-    if (wave == NW) {
-        // ---- the producer wave: every DMA of the stages and every y store.
+    if (wave >= NW) {
+        // ---- the loader (wave NW): every DMA of the stages and every y
+        // store; the former (wave NW + 1): the records and C B^T blocks.
         // Buffer resources over the workgroup's slices of C, B, x, the C B^T
         // blocks, the decay records and y, built once; a block adds its byte
         // offset to fixed per-lane offsets.  Rows past the end of the
@@ -382,30 +361,44 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             pdt_dma(kb + 1, nbuf);
         };
         // The decay record of head slot q = lane / 32 of the block staged in
-        // `buf`, from its dt: lambda_t = sum_{j <= t} dt_j A (fp32, the block's
-        // 32 tokens), lambda_e = lambda_31, and per token
-        //   CF = exp(lambda_e - lambda_t) dt_t, RP = exp(lambda_t - lambda_e)
-        //   (0 when the block is not factored), LR = lambda_t - lambda_e,
-        //   DT = dt_t, then DELTA = exp(lambda_e), FLAG = factored
-        //   (-lambda_e <= 60) and LE = lambda_e.  lambda_e - lambda_t carries
-        // an absolute error of a few units of |lambda_e| 2^-24 (below 1e-4
-        // while the block is factored), the relative error it puts on the
-        // exp factors.
+        // `buf`, from its dt, blocks taken in order: lambda_t = sum_{j <= t}
+        // dt_j A (fp32, the block's 32 tokens), lambda_e = lambda_31, delta =
+        // exp(lambda_e), factored = (-lambda_e <= 60).  The scale sigma of the
+        // head's state (h = sigma h~) is tracked here: sigma_out = sigma_in
+        // delta, restarted to delta when that would fall below exp(-60)
+        // (RESC), and 1 after an exact block.  Per token
+        //   W = exp(lambda_e - lambda_t) dt_t / sigma_out   (x' = W x; 1 for
+        //       sigma_out in an exact block),
+        //   F = exp(lambda_t - lambda_e) sigma_out          (0 in an exact block),
+        //   LR = lambda_t - lambda_e, DT = dt_t,
+        // then DELTA, FLAG, LE = lambda_e, SIGIN, SIGOUT, RESC.
+        // lambda_e - lambda_t carries an absolute error of a few units of
+        // |lambda_e| 2^-24 (below 1e-4 while the block is factored), the
+        // relative error it puts on the exp factors.
         const float pa = A[(h0 + (lane >> 5)) < H ? h0 + (lane >> 5) : H - 1];
+        float psig = 1.f;  // sigma of this lane's head after the last record formed
         auto prec = [&](unsigned char *buf) {
             const int t = lane & 31, q = lane >> 5;
             const float d = *reinterpret_cast<const float *>(buf + S::DTR + 4 * lane);
             const float lam = scan32(d * pa, lane);
             const float le = last_of_half(lam, lane);
             const bool fac = -le <= kSafeDecay;
+            const float delta = fast_exp(le);
+            const float sig_in = psig, p = sig_in * delta;
+            const bool resc = fac && p < kRescale;
+            const float sig_out = fac ? (resc ? delta : p) : 1.f;
+            const float xsc = fac ? __builtin_amdgcn_rcpf(sig_out) : 1.f;
+            psig = sig_out;
             if (q < S::NRS) {
                 float *rec = reinterpret_cast<float *>(buf + S::VR + 1024 * q);
-                rec[S::CF + t] = fast_exp(le - lam) * d;
-                rec[S::RP + t] = fac ? fast_exp(lam - le) : 0.f;
+                rec[S::W + t] = fast_exp(le - lam) * d * xsc;
+                rec[S::F + t] = fac ? fast_exp(lam - le) * sig_out : 0.f;
                 rec[S::LR + t] = lam - le;
                 rec[S::DT + t] = d;
-                if (t == kBlk - 1)
-                    *reinterpret_cast<f32x4 *>(rec + S::DELTA) = f32x4{fast_exp(le), fac ? 1.f : 0.f, le, 0.f};
+                if (t == kBlk - 1) {
+                    *reinterpret_cast<f32x4 *>(rec + S::DELTA) = f32x4{delta, fac ? 1.f : 0.f, le, sig_in};
+                    *reinterpret_cast<f32x2 *>(rec + S::SIGOUT) = f32x2{sig_out, resc ? 1.f : 0.f};
+                }
             }
         };
         // The causal diagonal block of C B^T of the block staged in `buf`,
@@ -459,43 +452,66 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, py[i], yo, 0);
             }
         };
-        pdt_dma(0, stage(0));
+        // Every wave takes the same barriers: two in the prologue (the DMAs
+        // of blocks 0..2 landed; then the C B^T block of block 0 and the
+        // records of blocks 0 and 1 formed), then one at the end of every
+        // block.
+        if (wave == NW) {
+            pdt_dma(0, stage(0));
 #pragma unroll
-        for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i), stage(i + 1));
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
-        pcbt(stage(0));
-        prec(stage(0));
-        prec(stage(1));
-        lds_barrier();
-        // block kb: refill the stage block kb - 1 used (and the dt slot of
-        // block kb + 4 in this block's stage: its records were formed two
-        // blocks ago) and store block kb - 1's y; form the C B^T block of
-        // block kb + 1 and the records of block kb + 2 (whose dt came with
-        // the DMAs of block kb + 1, landed before the last barrier); then
-        // wait for the DMAs of block kb + 2 and the end-of-block barrier
-        auto pblock = [&](int kb, const int si) {
-            pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
-            if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
-            pcbt(stage((si + 1) % S::NST));
-            prec(stage((si + 2) % S::NST));
-            __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
+            for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i), stage(i + 1));
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             lds_barrier();
-        };
-        for (int kb = 0; kb < nblk; kb += S::NST) {
-            pblock(kb, 0);
-            if (kb + 1 < nblk) {
-                pblock(kb + 1, 1);
-                if (kb + 2 < nblk) {
-                    pblock(kb + 2, 2);
-                    if constexpr (S::NST > 3) {
+            lds_barrier();
+            // block kb: refill the stage block kb - 1 used (and the dt slot of
+            // block kb + 4 in this block's stage: its records were formed two
+            // blocks ago), store block kb - 1's y, then wait for the DMAs of
+            // block kb + 2 and the end-of-block barrier
+            auto pblock = [&](int kb, const int si) {
+                pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
+                if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+                __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
+                lds_barrier();
+            };
+            for (int kb = 0; kb < nblk; kb += S::NST) {
+                pblock(kb, 0);
+                if (kb + 1 < nblk) {
+                    pblock(kb + 1, 1);
+                    if (kb + 2 < nblk) {
+                        pblock(kb + 2, 2);
                         if (kb + 3 < nblk) pblock(kb + 3, 3);
                     }
                 }
             }
+            pstore(nblk - 1, stage((nblk - 1) % S::NST));
+            // no DMA may land in LDS after the workgroup ends
+            __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
+        } else {
+            lds_barrier();
+            pcbt(stage(0));
+            prec(stage(0));
+            prec(stage(1));
+            lds_barrier();
+            // block kb: the C B^T block of block kb + 1 and the records of
+            // block kb + 2 (whose data landed before the last barrier: the
+            // dt of block kb + 2 comes with the DMAs of block kb + 1), then
+            // the end-of-block barrier
+            auto fblock = [&](const int si) {
+                pcbt(stage((si + 1) % S::NST));
+                prec(stage((si + 2) % S::NST));
+                lds_barrier();
+            };
+            for (int kb = 0; kb < nblk; kb += S::NST) {
+                fblock(0);
+                if (kb + 1 < nblk) {
+                    fblock(1);
+                    if (kb + 2 < nblk) {
+                        fblock(2);
+                        if (kb + 3 < nblk) fblock(3);
+                    }
+                }
+            }
         }
-        pstore(nblk - 1, stage((nblk - 1) % S::NST));
-        // no DMA may land in LDS after the workgroup ends
-        __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         return;
     }
 
@@ -572,9 +588,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         }
     };
 
-    // ---- prologue: the producer's DMAs of the first blocks have landed
+    // ---- prologue: the first blocks' data, then their records and C B^T
+    // blocks
     lds_barrier();
-    float sig_out = 1.f;  // sigma after the previous block
+    lds_barrier();
 
     // The operands that open a block (read from its stage during the block
     // before): the decay-record fields of the bookkeeping, cf and
@@ -582,11 +599,11 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     // 2 ECF K-steps.
     constexpr int ECF = S::ECF;
     struct Early {
-        f32x4 cfv[4];        // cf of tokens 16 kk + 8 hi + 0..7
+        f32x4 cfv[4];        // W (x' weights) of tokens 16 kk + 8 hi + 0..7
         bf16x8 xs[2];        // raw x^T, K-steps 0 and 1
         bf16x8 cfr[ECF][2];  // C fragments of y^T = h~ C^T, K-steps (m, u), m < ECF
-        float rpv;           // exp(lambda_r - lambda_e)
-        float dl, fc;        // the record's delta and factored flag (uniform)
+        float rpv;           // F of token r (the output factor)
+        float fc, rs;        // the record's factored and restart flags (uniform)
     };
     // The rest of a block's operands, read from its stage during the block.
     struct Ops {
@@ -602,7 +619,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
 #pragma unroll
             for (int w4 = 0; w4 < 2; ++w4)
                 e.cfv[2 * kk + w4] =
-                    *reinterpret_cast<const f32x4 *>(v + S::CF + 16 * kk + 8 * hi + 4 * w4);
+                    *reinterpret_cast<const f32x4 *>(v + S::W + 16 * kk + 8 * hi + 4 * w4);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk)
             e.xs[kk] = join(lds_tr(buf, S::XR + xs_tr[0] + 1024 * kk),
@@ -611,9 +628,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         for (int m = 0; m < ECF; ++m)
 #pragma unroll
             for (int u = 0; u < 2; ++u) e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[u] + 2048 * m);
-        e.rpv = v[S::RP + r];
-        e.dl = v[S::DELTA];
+        e.rpv = v[S::F + r];
         e.fc = v[S::FLAG];
+        e.rs = v[S::RESC];
     };
     auto load_late = [&](const unsigned char *cur, Ops &o) {
 #pragma unroll
@@ -644,8 +661,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // the operands of the common path in place between the two phases.
         Ops o;
         load_late(cur, o);
-        const Book bk = book_of(e.dl, e.fc, sig_out);
-        const float xscale = bk.fac ? __builtin_amdgcn_rcpf(bk.sig) : 1.f;
+        const bool fac = uniform(e.fc) != 0.f, rescale = uniform(e.rs) != 0.f;
         auto hb_of = [&](int q) {  // bf16 A fragment of K-step q = 2 m + u
             bf16x8 hb;
 #pragma unroll
@@ -659,7 +675,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
 #pragma unroll
             for (int ee = 0; ee < 2; ++ee) {
                 const int kk = q >> 2, j = 2 * (q & 3) + ee;
-                xp[kk][j] = (bf16)((float)e.xs[kk][j] * (e.cfv[2 * kk + (j >> 2)][j & 3] * xscale));
+                xp[kk][j] = (bf16)((float)e.xs[kk][j] * e.cfv[2 * kk + (j >> 2)][j & 3]);
             }
         };
         f32x16 acc;
@@ -680,23 +696,25 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // (the empty asm consumes x' here, so no pass sinks its arithmetic
         // out of the chunks above)
         asm volatile("" : "+v"(xp[0]), "+v"(xp[1]));
-        float f = e.rpv * bk.sig, dco = Dh;
-        if (bk.rescale) {
+        float f = e.rpv, dco = Dh;
+        if (rescale) {
             // restart of the scale (sigma would fall below exp(-60)): the
             // state and its output so far move to sigma_in = 1
             __builtin_amdgcn_sched_barrier(0);
-            acc *= bk.sig_in;
+            const float sig_in = uniform(v[S::SIGIN]);
+            acc *= sig_in;
 #pragma unroll
-            for (int m = 0; m < 4; ++m) st[m] *= bk.sig_in;
+            for (int m = 0; m < 4; ++m) st[m] *= sig_in;
         }
-        if (!bk.fac) {
+        if (!fac) {
             // (a side effect keeps the compiler from evaluating this rare
             // branch unconditionally with selects)
             __builtin_amdgcn_sched_barrier(0);
             // exact block: weights exp(lambda_l - lambda_s) dt_s on raw x with
             // D on the diagonal; h~ <- sigma_in delta h~ + B^T x', sigma = 1.
             // exp(lambda_r) sigma_in (<= 1: the exponent is formed before exp)
-            acc *= fast_exp(v[S::LR + r] + v[S::LE]) * bk.sig_in;
+            const float sig_in = uniform(v[S::SIGIN]);
+            acc *= fast_exp(v[S::LR + r] + v[S::LE]) * sig_in;
             const float lr = v[S::LR + r];
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
@@ -714,7 +732,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             }
             f = 1.f;
             dco = 0.f;
-            const float sd = bk.sig_in * bk.delta;
+            const float sd = sig_in * uniform(v[S::DELTA]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[m] *= sd;
         }
@@ -747,9 +765,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("" : "+v"(acc));
-        sig_out = bk.sig;
         __builtin_amdgcn_sched_barrier(0);
-        // y of the block to the producer through this stage's staging rows;
+        // y of the block to the loader through this stage's staging rows;
         // the barrier then also publishes it
         y_stage(cur, acc);
         __builtin_amdgcn_sched_barrier(0);
@@ -774,6 +791,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     }
 
     if (final_state) {
+        // h = sigma h~ with the last block's sigma (its record is still staged)
+        const float sig_out =
+            uniform(reinterpret_cast<const float *>(stage((nblk - 1) % S::NST) + rec_off)[S::SIGOUT]);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll

@@ -34,12 +34,14 @@ struct ForwardArgs {
 };
 
 // Fused path: the decay record of one (batch, head, 32-token block), as the
-// fused kernel keeps it in LDS, floats: [0, 32) cf_s = exp(lambda_e -
-// lambda_s) dt_s, [32, 64) rp_l = exp(lambda_l - lambda_e) (0 when the block
-// is not factored), [64, 96) lambda_l - lambda_e, [96, 128) dt_l, then
-// delta = exp(lambda_e), the factored flag (1 or 0) and lambda_e.  528 bytes,
-// a multiple of 16.
-constexpr int kVecRec = 132;
+// fused kernel keeps it in LDS, floats: [0, 32) the x' weights
+// exp(lambda_e - lambda_s) dt_s / sigma_out, [32, 64) the output factors
+// exp(lambda_l - lambda_e) sigma_out (0 when the block is not factored),
+// [64, 96) lambda_l - lambda_e, [96, 128) dt_l, then delta = exp(lambda_e),
+// the factored flag (1 or 0), lambda_e, sigma_in, sigma_out and the restart
+// flag (sigma the scale of the state, h = sigma h~), 2 floats of padding.
+// 544 bytes, a multiple of 16.
+constexpr int kVecRec = 136;
 
 // Forward paths.  The split path runs the five kernels of the chunked
 // algorithm one after the other with the caller's chunk length and accepts
