@@ -23,9 +23,11 @@
  * Conventions shared by every entry point:
  *  - All pointers except `stream` are DEVICE pointers to dense row-major
  *    arrays; the library never dereferences them on the host.
- *  - dt is the processed time step (already positive: bias, softplus and any
- *    clamp are applied by the caller).  A is the per-head decay rate (the
- *    method expects A < 0; any finite value is accepted).
+ *  - dt is the processed time step (already non-negative: bias, softplus
+ *    and any clamp are applied by the caller), except in the `_ex` entry
+ *    points, which apply that processing themselves (see ssd_dt_proc).  A is
+ *    the per-head decay rate (the method expects A < 0; any finite value is
+ *    accepted).
  *  - x, B, C and y share one element type, `io_dtype` (fp32 or bf16).
  *    dt, A, D and every state are fp32.  Accumulation is fp32.
  *  - The caller owns every buffer.  The library allocates no device memory,
@@ -183,6 +185,63 @@ ssd_status ssd_state_update(float *state, const void *x, const float *dt,
                             const float *D, int ngroups, int batch, int nheads,
                             int headdim, int dstate, ssd_dtype io_dtype,
                             void *y, hipStream_t stream);
+
+/*
+ * Time-step preprocessing inside the kernels.  The Mamba-2 layer does not
+ * feed its projected time step to the recurrence directly: it passes
+ * `dt_bias`, `dt_softplus` and `dt_limit` to `mamba_chunk_scan_combined`
+ * and `selective_state_update`, and its reference branches compute
+ * dt = clamp(softplus(dt + dt_bias), time_step_limit) (fla
+ * `layers/mamba2.py`, `Mamba2.forward` and `Mamba2.torch_forward`).  With
+ * this struct the library does the same, per element of dt, in fp32:
+ *
+ *     dt_used = min(max(f(dt + dt_bias_h), dt_min), dt_max)
+ *     f(v)    = log(1 + e^v) when dt_softplus != 0 (v itself above 20),
+ *               else v
+ *
+ *   dt_bias      [nheads] fp32 device pointer, 4-byte aligned; NULL = 0
+ *   dt_softplus  0 or nonzero
+ *   dt_min       lower bound, >= 0 (so dt_used >= 0); the layer's default 0
+ *   dt_max       upper bound, >= dt_min; +INFINITY for none (the default)
+ *
+ * Tokens past seqlen (the ragged last chunk) keep dt_used = 0, as in the
+ * entry points without preprocessing.  Any bound that is NaN, dt_min < 0 or
+ * dt_min > dt_max returns SSD_ERR_INVALID_ARGUMENT.
+ */
+typedef struct ssd_dt_proc {
+    const float *dt_bias;
+    int dt_softplus;
+    float dt_min;
+    float dt_max;
+} ssd_dt_proc;
+
+/*
+ * ssd_chunk_scan_fwd with dt the raw time step [batch, seqlen, nheads],
+ * processed as *dt_proc says.  A NULL dt_proc makes it exactly
+ * ssd_chunk_scan_fwd.  Same arguments, workspace (size and path) and errors
+ * otherwise.
+ */
+ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
+                                 const void *B, const void *C, const float *D,
+                                 const float *initial_state, int chunk_len,
+                                 int ngroups, int batch, int seqlen, int nheads,
+                                 int headdim, int dstate, ssd_dtype io_dtype,
+                                 void *y, float *final_state, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 const ssd_dt_proc *dt_proc);
+
+/*
+ * ssd_state_update with dt the raw time step [batch, nheads], processed as
+ * *dt_proc says (the `dt_bias` and `dt_softplus` arguments of the layer's
+ * `selective_state_update` call).  A NULL dt_proc makes it exactly
+ * ssd_state_update.
+ */
+ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt,
+                               const float *A, const void *B, const void *C,
+                               const float *D, int ngroups, int batch, int nheads,
+                               int headdim, int dstate, ssd_dtype io_dtype,
+                               void *y, hipStream_t stream,
+                               const ssd_dt_proc *dt_proc);
 
 #ifdef __cplusplus
 }

@@ -15,6 +15,8 @@ Contents
              a NumPy serial loop, the quadratic (masked semiseparable-matrix)
              form and the four-step chunked form.
 ``metrics``  the two error measures that the parity tolerances are stated in.
+``dt``       the layer's time-step preprocessing (bias, softplus, clamp) in
+             fp64, for the library's fused preprocessing.
 """
 from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
-from . import forms, metrics  # noqa: F401
+from . import dt, forms, metrics  # noqa: F401

@@ -50,6 +50,21 @@ ssd_status check_forward_shape(int batch, int seqlen, int nheads, int headdim,
     return SSD_OK;
 }
 
+// The time-step preprocessing options of the `_ex` entry points (NULL: off).
+ssd_status check_dt_proc(const ssd_dt_proc *p, ssd::DtProc *out) {
+    *out = ssd::DtProc();
+    if (!p) return SSD_OK;
+    // (a NaN bound fails every comparison below)
+    if (!(p->dt_min >= 0.f) || !(p->dt_max >= p->dt_min)) return SSD_ERR_INVALID_ARGUMENT;
+    if (p->dt_bias && !aligned(p->dt_bias, 4)) return SSD_ERR_INVALID_ARGUMENT;
+    out->on = true;
+    out->bias = p->dt_bias;
+    out->softplus = p->dt_softplus != 0;
+    out->lo = p->dt_min;
+    out->hi = p->dt_max;
+    return SSD_OK;
+}
+
 // Forward path for a shape: the fused kernel where it applies, the split
 // kernels otherwise.  SSD_FORWARD_PATH=split|fused overrides the choice (a
 // diagnostic switch for comparing the two); forcing "fused" on a shape it
@@ -110,10 +125,12 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
                         int headdim, int dstate, ssd_dtype io_dtype, void *y,
                         float *final_state, void *workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t *events, int *nkernels,
-                        const char **names) {
+                        const char **names, const ssd_dt_proc *dt_proc) {
     ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
+    ssd::DtProc dtp;
+    if ((st = check_dt_proc(dt_proc, &dtp)) != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !y) return SSD_ERR_INVALID_ARGUMENT;
     // 16-byte vector accesses on x, B, C, y and the states.
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(y, 16) ||
@@ -147,6 +164,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.N = dstate;
     a.Q = chunk_len;
     a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
+    a.dtp = dtp;
     char *ws = static_cast<char *>(workspace);
     const bool split = path == ssd::Path::Split;
     a.acum_hi = split ? reinterpret_cast<float *>(ws + lay.acum_hi) : nullptr;
@@ -220,7 +238,22 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               size_t workspace_bytes, hipStream_t stream) {
     return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
-                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr);
+                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
+                        nullptr);
+}
+
+ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
+                                 const void *B, const void *C, const float *D,
+                                 const float *initial_state, int chunk_len, int ngroups,
+                                 int batch, int seqlen, int nheads, int headdim,
+                                 int dstate, ssd_dtype io_dtype, void *y,
+                                 float *final_state, void *workspace,
+                                 size_t workspace_bytes, hipStream_t stream,
+                                 const ssd_dt_proc *dt_proc) {
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
+                        seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
+                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
+                        dt_proc);
 }
 
 int ssd_chunk_scan_fwd_max_kernels(void) { return ssd::kMaxForwardKernels; }
@@ -239,13 +272,15 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
         if (!events[i]) return SSD_ERR_INVALID_ARGUMENT;
     return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
-                        workspace, workspace_bytes, stream, events, nkernels, kernel_names);
+                        workspace, workspace_bytes, stream, events, nkernels, kernel_names,
+                        nullptr);
 }
 
-ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,
-                            const void *B, const void *C, const float *D, int ngroups,
-                            int batch, int nheads, int headdim, int dstate,
-                            ssd_dtype io_dtype, void *y, hipStream_t stream) {
+ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, const float *A,
+                               const void *B, const void *C, const float *D, int ngroups,
+                               int batch, int nheads, int headdim, int dstate,
+                               ssd_dtype io_dtype, void *y, hipStream_t stream,
+                               const ssd_dt_proc *dt_proc) {
     if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
         return SSD_ERR_INVALID_ARGUMENT;
     if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
@@ -258,6 +293,9 @@ ssd_status ssd_state_update(float *state, const void *x, const float *dt, const 
     if (!aligned(state, 16) || !aligned(x, es) || !aligned(B, es) || !aligned(C, es) ||
         !aligned(y, es) || !aligned(dt, 4) || !aligned(A, 4) || (D && !aligned(D, 4)))
         return SSD_ERR_INVALID_ARGUMENT;
+    ssd::DtProc dtp;
+    const ssd_status st = check_dt_proc(dt_proc, &dtp);
+    if (st != SSD_OK) return st;
     ssd::DecodeArgs a;
     a.state = state;
     a.x = x;
@@ -272,9 +310,18 @@ ssd_status ssd_state_update(float *state, const void *x, const float *dt, const 
     a.G = ngroups;
     a.P = headdim;
     a.N = dstate;
+    a.dtp = dtp;
     hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_state_update<ssd::bf16>(a, stream)
                                           : ssd::launch_state_update<float>(a, stream);
     return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,
+                            const void *B, const void *C, const float *D, int ngroups,
+                            int batch, int nheads, int headdim, int dstate,
+                            ssd_dtype io_dtype, void *y, hipStream_t stream) {
+    return ssd_state_update_ex(state, x, dt, A, B, C, D, ngroups, batch, nheads, headdim,
+                               dstate, io_dtype, y, stream, nullptr);
 }
 
 }  // extern "C"

@@ -25,7 +25,8 @@ template <typename T, int R>
 __global__ void __launch_bounds__(256)
 k_state_update(float *__restrict__ state, const T *__restrict__ x, const float *__restrict__ dt,
                const float *__restrict__ A, const T *__restrict__ Bm, const T *__restrict__ Cm,
-               const float *__restrict__ D, T *__restrict__ y, int H, int G, int P, int N) {
+               const float *__restrict__ D, T *__restrict__ y, int H, int G, int P, int N,
+               const DtProc dtp) {
     constexpr int RP = 256 / R;  // rows per pass of the workgroup
     constexpr int U = 8;         // passes whose loads are in flight together
     const int h = blockIdx.x, b = blockIdx.y, g = h / (H / G);
@@ -33,7 +34,8 @@ k_state_update(float *__restrict__ state, const T *__restrict__ x, const float *
     const int lr = tid & (R - 1);
     const int n0 = lr * 4;
     const bool nact = n0 < N;
-    const float dth = dt[(size_t)b * H + h];
+    float dth = dt[(size_t)b * H + h];
+    if (dtp.on) dth = dt_process(dth, dtp.bias ? dtp.bias[h] : 0.f, dtp.softplus, dtp.lo, dtp.hi);
     const float alpha = fast_exp(dth * A[h]);
     const float Dh = D ? D[h] : 0.f;
     float Bv[4] = {0.f, 0.f, 0.f, 0.f}, Cv[4] = {0.f, 0.f, 0.f, 0.f};
@@ -95,7 +97,7 @@ hipError_t launch_state_update(const DecodeArgs &a, hipStream_t stream) {
     case RR:                                                                                   \
         hipLaunchKernelGGL((k_state_update<T, RR>), grid, block, 0, stream, a.state,          \
                            (const T *)a.x, a.dt, a.A, (const T *)a.B, (const T *)a.C, a.D,    \
-                           (T *)a.y, a.H, a.G, a.P, a.N);                                      \
+                           (T *)a.y, a.H, a.G, a.P, a.N, a.dtp);                               \
         break;
     switch (R) {
         SSD_DECODE_CASE(4)

@@ -103,6 +103,16 @@ __device__ __forceinline__ double wave_inclusive_scan_f64(double v, int lane) {
 
 __device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
 
+// The layer's time-step preprocessing (the `_ex` entry points): bias, then
+// softplus log(1 + e^v) (v itself above 20, where the two agree in fp32),
+// then the clamp to [lo, hi].
+__device__ __forceinline__ float dt_process(float v, float bias, bool softplus, float lo,
+                                            float hi) {
+    v += bias;
+    if (softplus) v = v > 20.f ? v : log1pf(__expf(v));
+    return fminf(fmaxf(v, lo), hi);
+}
+
 // a - b for two prefix sums held as (hi, lo) float pairs.  When a and b are
 // close, hi_a - hi_b is exact (Sterbenz), so the result keeps the accuracy
 // of the small difference instead of the ulp of the large prefixes.

@@ -265,7 +265,7 @@ __global__ void __launch_bounds__(Fused<PB>::NT)
 k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
             const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const float *__restrict__ D, const float *init, float *final_state,
-            bf16 *__restrict__ y, int L, int H, int G, int P, int nblk) {
+            bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
     // Every LDS region that a DMA fills is its own object: the compiler can
@@ -378,8 +378,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             }
             pdt_dma(kb + 1, nbuf);
         };
-        // The decay record of head slot q = lane / 32 of the block staged in
-        // `buf`, from its dt, blocks taken in order: lambda_t = sum_{j <= t}
+        // The decay record of head slot q = lane / 32 of block kblk, staged
+        // in `buf`, from its dt (run through the time-step preprocessing when
+        // that is on, tokens past seqlen kept at 0), blocks taken in order:
+        // lambda_t = sum_{j <= t}
         // dt_j A (fp32, the block's 32 tokens), lambda_e = lambda_31, delta =
         // exp(lambda_e), factored = (-lambda_e <= 60).  The scale sigma of the
         // head's state (h = sigma h~) is tracked here: sigma_out = sigma_in
@@ -393,11 +395,15 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // lambda_e - lambda_t carries an absolute error of a few units of
         // |lambda_e| 2^-24 (below 1e-4 while the block is factored), the
         // relative error it puts on the exp factors.
-        const float pa = A[(h0 + (lane >> 5)) < H ? h0 + (lane >> 5) : H - 1];
+        const int ph = (h0 + (lane >> 5)) < H ? h0 + (lane >> 5) : H - 1;
+        const float pa = A[ph];
+        const float pbias = dtp.on && dtp.bias ? dtp.bias[ph] : 0.f;
         float psig = 1.f;  // sigma of this lane's head after the last record formed
-        auto prec = [&](unsigned char *buf) {
+        auto prec = [&](unsigned char *buf, int kblk) {
             const int t = lane & 31, q = lane >> 5;
-            const float d = *reinterpret_cast<const float *>(buf + S::DTR + 4 * lane);
+            float d = *reinterpret_cast<const float *>(buf + S::DTR + 4 * lane);
+            if (dtp.on)
+                d = kBlk * kblk + t < L ? dt_process(d, pbias, dtp.softplus, dtp.lo, dtp.hi) : 0.f;
             const float lam = scan32(d * pa, lane);
             const float le = last_of_half(lam, lane);
             const bool fac = -le <= kSafeDecay;
@@ -507,25 +513,25 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         } else {
             lds_barrier();
             pcbt(stage(0));
-            prec(stage(0));
-            prec(stage(1));
+            prec(stage(0), 0);
+            prec(stage(1), 1);
             lds_barrier();
             // block kb: the C B^T block of block kb + 1 and the records of
             // block kb + 2 (whose data landed before the last barrier: the
             // dt of block kb + 2 comes with the DMAs of block kb + 1), then
             // the end-of-block barrier
-            auto fblock = [&](const int si) {
+            auto fblock = [&](const int si, int kb) {
                 pcbt(stage((si + 1) % S::NST));
-                prec(stage((si + 2) % S::NST));
+                prec(stage((si + 2) % S::NST), kb + 2);
                 lds_barrier();
             };
             for (int kb = 0; kb < nblk; kb += S::NST) {
-                fblock(0);
+                fblock(0, kb);
                 if (kb + 1 < nblk) {
-                    fblock(1);
+                    fblock(1, kb + 1);
                     if (kb + 2 < nblk) {
-                        fblock(2);
-                        if (kb + 3 < nblk) fblock(3);
+                        fblock(2, kb + 2);
+                        if (kb + 3 < nblk) fblock(3, kb + 3);
                     }
                 }
             }
@@ -843,7 +849,8 @@ static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
     hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
                        (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C, a.D,
-                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, fused_nblk(a.L));
+                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, fused_nblk(a.L),
+                       a.dtp);
 }
 
 // Columns per workgroup.  One workgroup per compute unit is the target

@@ -12,6 +12,16 @@ constexpr int kMaxDstate = 256;
 constexpr int kK3TilesPerWave = 8;
 constexpr int kK4Prefetch = 4;
 
+// Time-step preprocessing of the `_ex` entry points: when `on`, the kernels
+// use min(max(f(dt + bias_h), lo), hi) with f = softplus if `softplus`,
+// else the identity (bias may be null: 0).  Tokens past seqlen keep dt = 0.
+struct DtProc {
+    bool on = false;
+    const float *bias = nullptr;
+    bool softplus = false;
+    float lo = 0.f, hi = 0.f;
+};
+
 // Problem and workspace pointers of one chunked forward call.
 struct ForwardArgs {
     const void *x;
@@ -24,6 +34,7 @@ struct ForwardArgs {
     void *y;
     float *final_state;  // may be null
     int batch, L, H, G, P, N, Q, nchunks;
+    DtProc dtp;      // dt preprocessing (off: dt is used as given)
     // workspace regions shared by both forward paths
     float *acum_hi;  // [b][H][nc][Q]  fp32 part of the fp64 chunk prefix sums
     float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
@@ -69,8 +80,9 @@ template <typename T> bool fused_supported(int P, int N, int Q);
 int fused_nblk(int L);
 
 // k1 of the split path.
-void launch_dA_cumsum(const float *dt, const float *A, float *acum_hi, float *acum_lo,
-                      float *dtT, int batch, int L, int H, int nc, int Q, hipStream_t stream);
+void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float *acum_hi,
+                      float *acum_lo, float *dtT, int batch, int L, int H, int nc, int Q,
+                      hipStream_t stream);
 
 struct DecodeArgs {
     float *state;
@@ -82,6 +94,7 @@ struct DecodeArgs {
     const float *D;  // may be null
     void *y;
     int batch, H, G, P, N;
+    DtProc dtp;      // dt preprocessing (off: dt is used as given)
 };
 
 template <typename T>

@@ -14,7 +14,9 @@
 //   acum [b][H][nc][Q]   prefix sums of dt*A inside each chunk (0 past
 //                        seqlen), as a two-float pair: the fp64 prefix rounded
 //                        to fp32 (hi) and the rounding remainder (lo)
-//   dtT  [b][H][nc][Q]   dt re-laid out per chunk (0 past seqlen)
+//   dtT  [b][H][nc][Q]   dt re-laid out per chunk (0 past seqlen), after the
+//                        time-step preprocessing when it is on; every later
+//                        kernel reads dt from here
 //   cb   [b][nc][G][Q][Q] C B^T of the chunk (only s-tiles <= l-tile written)
 //   S    [b][nc][H][P][N] chunk states, overwritten by k4 with the state
 //                         entering each chunk
@@ -36,7 +38,7 @@ namespace ssd {
 // layer (`segment_sum`) avoids.  (hi_l - hi_s) + (lo_l - lo_s) is accurate to
 // a few ulps of the difference itself.
 __global__ void __launch_bounds__(256)
-k1_dA_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
+k1_dA_cumsum(const float *__restrict__ dt, const DtProc dtp, const float *__restrict__ A,
              float *__restrict__ acum_hi, float *__restrict__ acum_lo,
              float *__restrict__ dtT, int L, int H, int nc, int Q) {
     __shared__ float s_dt[16][257];
@@ -46,7 +48,10 @@ k1_dA_cumsum(const float *__restrict__ dt, const float *__restrict__ A,
     for (int r = tid >> 4; r < Q; r += 16) {
         const int h = h0 + j, t = c * Q + r;
         float v = 0.f;
-        if (h < H && t < L) v = dt[((size_t)b * L + t) * H + h];
+        if (h < H && t < L) {
+            v = dt[((size_t)b * L + t) * H + h];
+            if (dtp.on) v = dt_process(v, dtp.bias ? dtp.bias[h] : 0.f, dtp.softplus, dtp.lo, dtp.hi);
+        }
         s_dt[j][r] = v;
     }
     __syncthreads();
@@ -400,10 +405,11 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
 const char *const kSplitKernelNames[kSplitKernels] = {
     "k1_dA_cumsum", "k2_chunk_cb", "k3_chunk_state", "k4_state_passing", "k5_chunk_scan"};
 
-void launch_dA_cumsum(const float *dt, const float *A, float *acum_hi, float *acum_lo,
-                      float *dtT, int batch, int L, int H, int nc, int Q, hipStream_t stream) {
+void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float *acum_hi,
+                      float *acum_lo, float *dtT, int batch, int L, int H, int nc, int Q,
+                      hipStream_t stream) {
     hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (H + 15) / 16, batch), dim3(256), 0, stream, dt,
-                       A, acum_hi, acum_lo, dtT, L, H, nc, Q);
+                       dtp, A, acum_hi, acum_lo, dtT, L, H, nc, Q);
 }
 
 template <typename T>
@@ -415,7 +421,8 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     };
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
-    launch_dA_cumsum(a.dt, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q, stream);
+    launch_dA_cumsum(a.dt, a.dtp, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q,
+                     stream);
     if ((err = mark()) != hipSuccess) return err;
     const int nlb = (Q + 63) / 64;
     hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),

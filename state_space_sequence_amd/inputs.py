@@ -22,6 +22,12 @@ Draw order: A, dt_bias, D, x, dt-noise, B, C, init, from
 ``numpy.random.Generator(PCG64(seed))``.  x, B and C are rounded to bf16
 (round to nearest even) when the workload is bf16; every array is returned
 as float32 holding exactly the values the GPU receives.
+
+The same draw also yields the layer's raw time step, for callers that let
+the library apply the time-step preprocessing itself:
+
+    dt_raw    = 0.5 * N(0, 1)  (the same noise)            fp32 [b,L,H]
+    dt_bias   = dt_bias_h                                  fp32 [H]
 """
 from __future__ import annotations
 
@@ -85,7 +91,8 @@ def _softplus(v):
 def make_inputs(batch, seqlen, nheads, headdim, dstate, ngroups,
                 io_dtype="bf16", init_std=0.0, seed=1234):
     """Draw one problem.  Returns a dict of float32 numpy arrays
-    x, dt, A, B, C, D, initial_state (None when init_std == 0)."""
+    x, dt, A, B, C, D, initial_state (None when init_std == 0), and the raw
+    time step dt_raw with its per-head bias dt_bias."""
     rng = np.random.Generator(np.random.PCG64(seed))
     H, P, N, G = nheads, headdim, dstate, ngroups
     A = -np.exp(rng.uniform(0.0, np.log(16.0), size=H))
@@ -113,6 +120,8 @@ def make_inputs(batch, seqlen, nheads, headdim, dstate, ngroups,
         "C": np.ascontiguousarray(Cm, dtype=np.float32),
         "D": D.astype(np.float32),
         "initial_state": init,
+        "dt_raw": (0.5 * noise.astype(np.float64)).astype(np.float32),
+        "dt_bias": dt_bias.astype(np.float32),
     }
 
 

@@ -46,6 +46,13 @@ _sz = ctypes.c_size_t
 _FWD_ARGS = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]
 
 
+class DtProc(ctypes.Structure):
+    """``ssd_dt_proc`` of include/ssd.h: the time-step preprocessing the
+    ``_ex`` entry points apply, min(max(f(dt + dt_bias), dt_min), dt_max)."""
+    _fields_ = [("dt_bias", ctypes.c_void_p), ("dt_softplus", ctypes.c_int),
+                ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
+
+
 def load():
     """Load libssd.so (once).  Raises if it has not been built."""
     global _lib
@@ -72,6 +79,10 @@ def load():
             ctypes.POINTER(_p), _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_char_p)]
         lib.ssd_state_update.restype = _i
         lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
+        lib.ssd_chunk_scan_fwd_ex.restype = _i
+        lib.ssd_chunk_scan_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(DtProc)]
+        lib.ssd_state_update_ex.restype = _i
+        lib.ssd_state_update_ex.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p, ctypes.POINTER(DtProc)]
         _lib = lib
     return _lib
 
@@ -125,8 +136,23 @@ def ssd_chunk_scan_fwd_workspace_size(batch, seqlen, nheads, headdim, dstate, ng
     return out.value
 
 
+def _dt_proc(dt_bias, dt_softplus, dt_limit, H, dev):
+    """The ssd_dt_proc struct for these options, or None when none is set
+    (then dt is used as given)."""
+    import torch
+    if dt_bias is None and not dt_softplus and dt_limit is None:
+        return None
+    if dt_bias is not None:
+        _check_dev("dt_bias", dt_bias, torch.float32, dev)
+        if tuple(dt_bias.shape) != (H,):
+            raise ValueError("dt_bias must be [H]")
+    lo, hi = (0.0, float("inf")) if dt_limit is None else (float(dt_limit[0]), float(dt_limit[1]))
+    return DtProc(None if dt_bias is None else dt_bias.data_ptr(), 1 if dt_softplus else 0,
+                  lo, hi)
+
+
 def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-             final_state, workspace, return_final_state, stream):
+             final_state, workspace, return_final_state, stream, dtp=None):
     import torch
     lib = load()
     dev = x.device
@@ -167,7 +193,12 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
             int(chunk_len), G, b, L, H, P, N, io, _ptr(y), _ptr(final_state),
             _ptr(workspace), _sz(workspace.numel()), _stream_handle(stream))
-    if timed_events is None:
+    if dtp is not None:
+        if timed_events is not None:
+            raise ValueError("the timed forward takes processed dt only")
+        st = lib.ssd_chunk_scan_fwd_ex(*args, ctypes.byref(dtp))
+        where = "ssd_chunk_scan_fwd_ex"
+    elif timed_events is None:
         st = lib.ssd_chunk_scan_fwd(*args)
         where = "ssd_chunk_scan_fwd"
     else:
@@ -187,16 +218,23 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
 
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256,
                        ngroups=None, y=None, final_state=None, workspace=None,
-                       return_final_state=True, stream=None):
+                       return_final_state=True, stream=None, dt_bias=None,
+                       dt_softplus=False, dt_limit=None):
     """Chunked SSD forward on the current (or given) torch stream.
 
     x [b,L,H,P] (fp32|bf16), dt [b,L,H] fp32, A [H] fp32, B/C [b,L,G,N] (x's
     dtype), D [H] fp32 or None, initial_state [b,H,P,N] fp32 or None.
     Returns (y [b,L,H,P] in x's dtype, final_state [b,H,P,N] fp32 or None).
     Outputs and workspace are allocated with torch when not supplied;
-    final_state may be the initial_state tensor itself."""
+    final_state may be the initial_state tensor itself.
+
+    With dt_bias ([H] fp32), dt_softplus or dt_limit ((min, max)) given, dt
+    is the raw time step and the kernels use min(max(f(dt + dt_bias), min),
+    max), f = softplus when dt_softplus (the layer's `dt_bias`,
+    `dt_softplus`, `dt_limit` arguments; ssd_chunk_scan_fwd_ex)."""
+    dtp = _dt_proc(dt_bias, dt_softplus, dt_limit, A.shape[0], x.device)
     return _forward(None, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-                    final_state, workspace, return_final_state, stream)
+                    final_state, workspace, return_final_state, stream, dtp)
 
 
 def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
@@ -210,11 +248,14 @@ def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
                     y, final_state, workspace, return_final_state, stream)
 
 
-def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream=None):
+def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream=None,
+                     dt_bias=None, dt_softplus=False, dt_limit=None):
     """One decode token, in place on ``state``.
 
     state [b,H,P,N] fp32, x [b,H,P] (fp32|bf16), dt [b,H] fp32, A [H],
-    B/C [b,G,N] (x's dtype), D [H] or None.  Returns y [b,H,P] in x's dtype."""
+    B/C [b,G,N] (x's dtype), D [H] or None.  Returns y [b,H,P] in x's dtype.
+    dt_bias / dt_softplus / dt_limit: as in ssd_chunk_scan_fwd
+    (ssd_state_update_ex)."""
     import torch
     lib = load()
     dev = x.device
@@ -239,8 +280,13 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream
     if y is None:
         y = torch.empty_like(x)
     _check_dev("y", y, x.dtype, dev)
-    st = lib.ssd_state_update(_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C),
-                              _ptr(D), G, b, H, P, N, io, _ptr(y), _stream_handle(stream))
+    args = (_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), G, b, H, P,
+            N, io, _ptr(y), _stream_handle(stream))
+    dtp = _dt_proc(dt_bias, dt_softplus, dt_limit, H, dev)
+    if dtp is None:
+        st, where = lib.ssd_state_update(*args), "ssd_state_update"
+    else:
+        st, where = lib.ssd_state_update_ex(*args, ctypes.byref(dtp)), "ssd_state_update_ex"
     if st != SSD_OK:
-        raise SsdError(st, "ssd_state_update")
+        raise SsdError(st, where)
     return y

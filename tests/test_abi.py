@@ -152,3 +152,27 @@ def test_binding_refuses_cpu_tensors():
     with pytest.raises(ValueError):
         libssd.ssd_chunk_scan_fwd(x, torch.zeros(1, 4, 2), torch.zeros(2),
                                   torch.zeros(1, 4, 1, 16), torch.zeros(1, 4, 1, 16))
+
+
+@pytest.mark.parametrize("bias,lo,hi", [
+    (None, -0.1, 1.0),                   # dt_min < 0
+    (None, 0.5, 0.1),                    # dt_min > dt_max
+    (None, float("nan"), 1.0),           # NaN bound
+    (None, 0.0, float("nan")),
+    (FAKE + 2, 0.0, float("inf")),       # misaligned dt_bias
+])
+def test_dt_proc_validation(lib, bias, lo, hi):
+    """Invalid preprocessing options are rejected before anything launches
+    (every other argument here is valid)."""
+    from state_space_sequence_amd.libssd import DtProc  # the ssd_dt_proc layout
+    p = DtProc(bias, 1, lo, hi)
+    st = lib.ssd_chunk_scan_fwd_ex(
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, None, 64, 1, 1, 100, 2, 64, 128,
+        1, ctypes.c_void_p(FAKE), None, None, ctypes.c_size_t(0), None, ctypes.byref(p))
+    assert st == 1
+    st = lib.ssd_state_update_ex(
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE),
+        ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, 1, 2, 4,
+        16, 16, 1, ctypes.c_void_p(FAKE), None, ctypes.byref(p))
+    assert st == 1

@@ -305,3 +305,47 @@ def test_pins_catch_planted_mistakes(oracle_mod, mistake):
                        inp["initial_state"])
     err = max(np.max(np.abs(ym - yq)), np.max(np.abs(fm - fq)))
     assert err > 1e-6, mistake
+
+
+# ------------------------------------------------------ time-step preprocessing
+
+def test_softplus_closed_forms():
+    """softplus(v) = log(1 + e^v): softplus(0) = ln 2; softplus(v) -
+    softplus(-v) = v (since 1 + e^v = e^v (1 + e^-v)); its inverse is
+    u + log(1 - e^-u), the form the input generator uses for dt_bias, so
+    softplus of that is u again; no overflow or loss at the extremes."""
+    from oracle.dt import softplus
+    assert softplus(0.0) == np.log(2.0)
+    v = np.linspace(-30.0, 30.0, 121)
+    np.testing.assert_allclose(softplus(v) - softplus(-v), v, rtol=0, atol=1e-13)
+    u = np.array([1e-3, 3e-3, 1e-2, 0.05, 0.1, 1.0, 5.0])
+    np.testing.assert_allclose(softplus(u + np.log(-np.expm1(-u))), u, rtol=1e-12)
+    assert softplus(800.0) == 800.0
+    np.testing.assert_allclose(softplus(-40.0), np.exp(-40.0), rtol=1e-15)
+
+
+def test_process_dt_order_of_steps():
+    """bias, then softplus, then the clamp (fla ``Mamba2.torch_forward``)."""
+    from oracle.dt import process_dt, softplus
+    raw = np.array([[-5.0, 0.0, 3.0]])
+    bias = np.array([0.5, -1.0, 0.25])
+    np.testing.assert_array_equal(process_dt(raw, bias, True), softplus(raw + bias))
+    # the clamp acts on the softplus output, not on its argument
+    got = process_dt(raw, bias, True, dt_min=0.05, dt_max=1.0)
+    np.testing.assert_array_equal(got, np.clip(softplus(raw + bias), 0.05, 1.0))
+    assert got[0, 0] == 0.05 and got[0, 2] == 1.0
+    # without softplus the biased value is clamped directly (0 floor)
+    np.testing.assert_array_equal(process_dt(raw, bias, False), np.maximum(raw + bias, 0.0))
+    # no bias, no softplus, default limits: the identity on non-negative dt
+    d = np.array([0.0, 1e-3, 0.7])
+    np.testing.assert_array_equal(process_dt(d), d)
+
+
+def test_process_dt_matches_generator():
+    """The generator's processed dt is softplus(0.5 noise + dt_bias) rounded
+    to fp32; processing its raw dt and bias (both fp32) gives the same values
+    to fp32 rounding."""
+    from oracle.dt import process_dt
+    inp = make_inputs(2, 40, 3, 4, 8, 1, io_dtype="f32", seed=5)
+    got = process_dt(inp["dt_raw"], inp["dt_bias"], True)
+    np.testing.assert_allclose(got, inp["dt"], rtol=2e-6)

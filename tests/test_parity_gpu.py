@@ -325,3 +325,97 @@ def test_decode_workload_vs_serial_and_chunked(dev, oracle_mod, path):
     torch.cuda.synchronize()
     check(state, fc.cpu().numpy(), "bf16", "decode state vs chunked")
     check(y, yc.float().cpu().numpy(), "bf16", "decode y vs chunked")
+
+
+# ------------------------------------------------------ time-step preprocessing
+
+# (b, L, H, P, N, G, Q, io, softplus, dt_limit, bias shift or None for no bias)
+DT_PROC = [
+    # the layer's call: softplus(dt + dt_bias), limits (0, inf)
+    (2, 300, 4, 64, 128, 1, 64, "bf16", True, None, 0.0),
+    (2, 300, 4, 64, 128, 2, 64, "f32", True, None, 0.0),
+    # both clamp bounds active
+    (2, 333, 4, 64, 128, 2, 128, "bf16", True, (0.002, 0.05), 0.0),
+    (1, 200, 3, 32, 128, 1, 32, "f32", True, (0.002, 0.05), 0.0),
+    # no softplus: the biased value floored at 0 (bias shifted so that both
+    # signs occur; large dt drives the exact per-element blocks)
+    (1, 257, 4, 64, 128, 1, 64, "bf16", False, None, 5.0),
+    # softplus of the raw value alone
+    (1, 130, 2, 16, 32, 1, 64, "f32", True, None, None),
+]
+
+
+@pytest.mark.parametrize("case", DT_PROC, ids=lambda c: "b%d_L%d_H%d_P%d_N%d_G%d_Q%d_%s" % c[:8]
+                         + ("_sp" if c[8] else "") + ("_lim" if c[9] else "")
+                         + ("_nobias" if c[10] is None else ""))
+def test_dt_preprocessing(dev, oracle_mod, path, case):
+    """The `_ex` forward on the raw time step against the oracle run on the
+    oracle's own preprocessing of it (oracle/dt.py)."""
+    import torch
+    from oracle.dt import process_dt
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    b, L, H, P, N, G, Q, io, sp, lim, shift = case
+    _say("dt preprocessing case %s path %s" % (case, path))
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=300 + L)
+    skip_if_path_unsupported(inp, io, Q)
+    bias = None if shift is None else (inp["dt_bias"] + np.float32(shift)).astype(np.float32)
+    dtp = process_dt(inp["dt_raw"], bias, sp, *(lim or (0.0, np.inf)))
+    if lim:
+        assert (dtp == lim[0]).any() and (dtp == lim[1]).any()
+    if not sp:
+        assert (dtp == 0).any() and (dtp > 1).any()
+    t = to_torch(inp, io, dev)
+    tb = None if bias is None else torch.from_numpy(bias).to(dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt_raw"], t["A"], t["B"], t["C"], t["D"],
+                                       t["initial_state"], chunk_len=Q, ngroups=G, dt_bias=tb,
+                                       dt_softplus=sp, dt_limit=lim)
+    torch.cuda.synchronize()
+    yr, finr, ya, fa = reference(oracle_mod, dict(inp, dt=dtp))
+    check(y.float().cpu().numpy(), yr, io, "y", ya)
+    check(fin.cpu().numpy(), finr, io, "final_state", fa)
+
+
+def test_dt_preprocessing_identity_is_bit_exact(dev, path):
+    """Preprocessing that is the identity on the (non-negative) processed dt:
+    no bias, no softplus, limits (0, inf).  Same bits as the plain call."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    inp = make_inputs(2, 300, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=17)
+    skip_if_path_unsupported(inp, "bf16", 64)
+    t = to_torch(inp, "bf16", dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    y1, f1 = libssd.ssd_chunk_scan_fwd(*args, chunk_len=64)
+    y2, f2 = libssd.ssd_chunk_scan_fwd(*args, chunk_len=64, dt_limit=(0.0, float("inf")))
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2) and torch.equal(f1, f2)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_decode_dt_preprocessing(dev, oracle_mod, io):
+    """`ssd_state_update_ex` steps on the raw time step (bias, softplus, an
+    active upper bound) against the serial oracle on the processed one."""
+    import torch
+    from oracle.dt import process_dt
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    b, steps, H, P, N, G = 3, 7, 4, 64, 128, 2
+    inp = make_inputs(b, steps, H, P, N, G, io_dtype=io, init_std=0.1, seed=41)
+    lim = (0.0, 0.08)
+    dtp = process_dt(inp["dt_raw"], inp["dt_bias"], True, *lim)
+    assert (dtp == lim[1]).any() and (dtp < lim[1]).any()
+    t = to_torch(inp, io, dev)
+    state = t["initial_state"].clone()
+    ys = []
+    for s in range(steps):
+        ys.append(libssd.ssd_state_update(state, t["x"][:, s].contiguous(),
+                                          t["dt_raw"][:, s].contiguous(), t["A"],
+                                          t["B"][:, s].contiguous(), t["C"][:, s].contiguous(),
+                                          t["D"], dt_bias=t["dt_bias"], dt_softplus=True,
+                                          dt_limit=lim))
+    torch.cuda.synchronize()
+    y = torch.stack(ys, 1).float().cpu().numpy()
+    yr, finr, ya, fa = reference(oracle_mod, dict(inp, dt=dtp))
+    check(y, yr, io, "decode y", ya)
+    check(state.cpu().numpy(), finr, io, "decode state", fa)
