@@ -11,6 +11,8 @@ Also reported (not part of ``value``):
   * ``roofline`` for the dominant kernel and ``path_roofline`` for the whole
     call against algorithmic bytes (x, B, C, dt, A, D read once; y and the
     final state written once; no intermediates);
+  * the other forward workloads, and the headline forward again on the raw
+    time step with the preprocessing (bias, softplus) inside the kernels;
   * the decode state update on the b256 / 80-head workload;
   * ``cpu_baseline``: the fp64 serial oracle on the host cores over a bounded
     sample of (batch, head) slices of the same workload.
@@ -194,6 +196,33 @@ def time_forward(w, dev, steps, warmup, ev):
     del t, y, fin, ws
     return dict(host_s=h1 - h0, gpu_ms=total_ms, per_kernel_ms=per_kernel,
                 names=names, inputs=inp)
+
+
+def time_forward_dt_proc(w, dev, ev, steps=100, warmup=50):
+    """ms per forward with the time-step preprocessing inside the kernels:
+    the raw dt with the per-head bias and softplus, limits (0, inf), as the
+    Mamba-2 layer calls the scan (ssd_chunk_scan_fwd_ex)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    inp, t, y, fin, ws = setup(w, dev)
+    args = (t["x"], t["dt_raw"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    kw = dict(chunk_len=w.chunk_len, y=y, final_state=fin, workspace=ws,
+              dt_bias=t["dt_bias"], dt_softplus=True)
+    for _ in range(warmup):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, sh)
+    for _ in range(steps):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+    ev.record(e1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    del t, y, fin, ws
+    return ms
 
 
 def time_decode(w, dev, ev, reps=3):
@@ -414,6 +443,11 @@ def main():
                            "per_kernel_ms": {k: round(v, 4) for k, v in
                                              zip(rx["names"], rx["per_kernel_ms"])}}
             del rx
+        msd = time_forward_dt_proc(w, dev, ev)
+        extra[w.name + "_dt_proc"] = {
+            "what": "the same forward on the raw time step: softplus(dt + dt_bias) in the kernels",
+            "ms_per_step": round(msd, 4),
+            "tokens_per_s": round(w.batch * w.seqlen / (msd * 1e-3), 1)}
         extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
         out["other_workloads"] = extra
     if not args.no_cpu_baseline:
