@@ -143,12 +143,22 @@ __device__ __forceinline__ float last_of_half(float v, int lane) {
 template <int PB>
 struct Fused {
     static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
-    // Two more waves.  The first (the loader) issues every global memory
+    // Helper waves.  The loader (wave NW) issues every global memory
     // operation of the workgroup: the DMAs of the stages and the y stores,
     // which the compute waves hand over through LDS; the compute waves never
-    // wait on the vector memory pipeline.  The second (the former) forms each
-    // block's decay records and C B^T block in LDS.
-    static constexpr int NT = 64 * (NW + 2);           // threads
+    // wait on the vector memory pipeline.  The former forms each block's
+    // decay records and C B^T block in LDS.  Waves go to the four SIMDs in
+    // turn (wave w to SIMD w % 4), and a helper slows the compute wave whose
+    // SIMD it shares by about its own issue time.  With four compute waves
+    // the former's two jobs are split over waves NW + 2 (C B^T blocks, on
+    // SIMD 2) and NW + 3 (records, on SIMD 3), and wave NW + 1 only takes
+    // the barriers, so that no SIMD carries two helpers (the loader shares
+    // SIMD 0) and the records wave has time to spare (the time-step
+    // preprocessing of the raw dt runs there).  With fewer compute waves
+    // every helper has a SIMD of its own.
+    static constexpr int NHELP = NW == 4 ? 4 : 2;
+    static constexpr bool SPLIT_FORMER = NHELP == 4;
+    static constexpr int NT = 64 * (NW + NHELP);       // threads
     static constexpr int N = 128;                      // dstate
     static constexpr int ROWB = 2 * N;                 // bytes per C / B row
     static constexpr int MAT = kBlk * ROWB;            // 8 KB per matrix
@@ -511,18 +521,24 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             // no DMA may land in LDS after the workgroup ends
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         } else {
+            // the former's jobs: C B^T blocks (do_cbt) and records (do_rec)
+            const bool do_cbt = !S::SPLIT_FORMER || wave == NW + 2;
+            const bool do_rec = !S::SPLIT_FORMER || wave == NW + 3;
             lds_barrier();
-            pcbt(stage(0));
-            prec(stage(0), 0);
-            prec(stage(1), 1);
+            if (do_cbt) pcbt(stage(0));
+            if (do_rec) {
+                prec(stage(0), 0);
+                prec(stage(1), 1);
+            }
             lds_barrier();
             // block kb: the C B^T block of block kb + 1 and the records of
             // block kb + 2 (whose data landed before the last barrier: the
             // dt of block kb + 2 comes with the DMAs of block kb + 1), then
-            // the end-of-block barrier
+            // the end-of-block barrier (unrolled by the stage count, so that
+            // every stage address is a literal)
             auto fblock = [&](const int si, int kb) {
-                pcbt(stage((si + 1) % S::NST));
-                prec(stage((si + 2) % S::NST), kb + 2);
+                if (do_cbt) pcbt(stage((si + 1) % S::NST));
+                if (do_rec) prec(stage((si + 2) % S::NST), kb + 2);
                 lds_barrier();
             };
             for (int kb = 0; kb < nblk; kb += S::NST) {
