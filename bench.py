@@ -321,14 +321,29 @@ def cpu_baseline(w, inp, target_s=12.0):
 COPY_CAL_BYTES = 256 << 20
 
 
-def kernel_source_hash():
-    """sha256 of the kernel sources the fused path is built from; a stored
-    traffic measurement is reported only while it matches."""
+def _code_only(text):
+    """C++ source with comments removed and whitespace collapsed (string
+    literals in these files hold no comment markers)."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def kernel_source_hash(read=None):
+    """sha256 of the code (comments and layout aside) of the kernel sources
+    the fused path is built from; a stored traffic measurement is reported
+    only while it matches."""
     import hashlib
     hsh = hashlib.sha256()
     for name in ("ssd_fused_kernels.hip", "ssd_device.hpp", "ssd_kernels.hpp"):
-        with open(os.path.join(ROOT, "state_space_sequence_amd", "csrc", name), "rb") as f:
-            hsh.update(f.read())
+        path = os.path.join("state_space_sequence_amd", "csrc", name)
+        if read is None:
+            with open(os.path.join(ROOT, path)) as f:
+                text = f.read()
+        else:
+            text = read(path)
+        hsh.update(_code_only(text).encode())
     return hsh.hexdigest()
 
 

@@ -40,19 +40,18 @@
 // (s > l exactly 0, the upper-triangle protection of the Kernel 5 page) on
 // raw x, with D on the diagonal, and the state decays explicitly
 // (h~ <- sigma_k exp(lambda_e) h~ + B^T x', sigma = 1).  The per-token
-// factors come precomputed per block (k_prep, from fp32 prefixes).
+// factors come in each block's decay record (fp32 prefixes), formed by a
+// helper wave two blocks ahead.
 //
-// Workgroup = NW = PB / 32 waves; wave w owns headdim columns 32 w .. 32 w +
-// 31 of the workgroup's PB columns and computes with
-// v_mfma_f32_32x32x16_bf16.  Per 32-token block:
-//   stage  three LDS stages filled by buffer-resource DMA two blocks ahead:
-//          C and B rows (swizzled), the causal diagonal block of C B^T
-//          (precomputed, in fragment order), raw x (swizzled) and the
-//          block's decay record;
-//   output y^T = h~ C^T + x'^T [C B^T]^T for the wave's 32 columns and the
-//          block's 32 tokens, with h~ taken straight from the state
-//          registers as the MFMA A operand; each lane ends with 4 runs of 4
-//          consecutive headdim values of one token (four 8-byte stores);
+// Workgroup (the Fused struct below): PB / 32 compute waves, wave w owning
+// headdim columns 32 w .. 32 w + 31 of the workgroup's PB columns and
+// computing with v_mfma_f32_32x32x16_bf16, plus helper waves: a loader that
+// issues every DMA into LDS and every y store, and a former that forms the
+// decay records and the causal C B^T blocks.  Four LDS stages rotate; per
+// 32-token block a compute wave computes
+//   output y^T = h~ C^T + x'^T [C B^T]^T for its 32 columns and the block's
+//          32 tokens, with h~ taken straight from the state registers as the
+//          MFMA A operand, and hands y to the loader through LDS;
 //   state  h~ += B^T x'.
 //
 // Operands that the MFMA needs transposed (B^T, x'^T) are read from
