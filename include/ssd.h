@@ -243,6 +243,59 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt,
                                void *y, hipStream_t stream,
                                const ssd_dt_proc *dt_proc);
 
+/*
+ * The causal depthwise convolution that precedes the scan in the Mamba-2
+ * layer (fla `layers/mamba2.py`, `Mamba2.torch_forward`: the x | B | C
+ * channels go through `nn.Conv1d(conv_dim, conv_dim, kernel_size=width,
+ * groups=conv_dim, padding=width-1)`, truncated to the first seqlen outputs,
+ * then SiLU).  Per channel c, with x_t = 0 for t < 0:
+ *
+ *     out_t[c] = act(bias[c] + sum_{k<width} weight[c][k] * x_{t-width+1+k}[c])
+ *
+ * act is the identity (SSD_ACT_NONE) or SiLU, v / (1 + e^-v) (SSD_ACT_SILU).
+ */
+typedef enum ssd_activation {
+    SSD_ACT_NONE = 0,
+    SSD_ACT_SILU = 1
+} ssd_activation;
+
+/*
+ * Convolution over a sequence, starting from an empty (zero) cache.
+ *
+ *   x           [batch, seqlen, dim]    io_dtype   in, 16-byte aligned
+ *   weight      [dim, width]            fp32       in (the conv1d weight with
+ *                                                  its singleton axis dropped)
+ *   bias        [dim]                   fp32       in, NULL = 0
+ *   out         [batch, seqlen, dim]    io_dtype   out, 16-byte aligned; may
+ *                                                  not overlap x
+ *   conv_state  [batch, dim, width]     io_dtype   out, NULL = skip: the cache
+ *               the decode path continues from, the last `width` inputs of
+ *               every channel, zeros before the first token (the layer's
+ *               cache initialisation, a left pad of the transposed inputs)
+ *
+ * width is 2, 3 or 4 and dim a multiple of 8 (else SSD_ERR_UNSUPPORTED).
+ * Accumulation is fp32; out is rounded to io_dtype.
+ */
+ssd_status ssd_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
+                                 int batch, int seqlen, int dim, int width, int activation,
+                                 ssd_dtype io_dtype, void *out, void *conv_state,
+                                 hipStream_t stream);
+
+/*
+ * One decode token, the cache updated in place (the layer's single-token
+ * branch: `update_conv_state` rolls the cache left by one and appends the
+ * new input; the output is the same dot product, bias and activation).
+ *
+ *   conv_state  [batch, dim, width]  io_dtype  in/out
+ *   x           [batch, dim]         io_dtype  in
+ *   weight, bias                     as above
+ *   out         [batch, dim]         io_dtype  out, may not overlap the cache
+ */
+ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
+                                    const float *bias, int batch, int dim, int width,
+                                    int activation, ssd_dtype io_dtype, void *out,
+                                    hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -17,6 +17,8 @@ Contents
 ``metrics``  the two error measures that the parity tolerances are stated in.
 ``dt``       the layer's time-step preprocessing (bias, softplus, clamp) in
              fp64, for the library's fused preprocessing.
+``conv``     the layer's causal depthwise convolution (+ SiLU) and its decode
+             update, in fp64.
 """
 from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
-from . import dt, forms, metrics  # noqa: F401
+from . import conv, dt, forms, metrics  # noqa: F401

@@ -324,4 +324,57 @@ ssd_status ssd_state_update(float *state, const void *x, const float *dt, const 
                                dstate, io_dtype, y, stream, nullptr);
 }
 
+namespace {
+
+ssd_status check_conv(const void *x, const float *weight, const float *bias, int batch,
+                      int seqlen, int dim, int width, int activation, ssd_dtype io_dtype,
+                      const void *out) {
+    if (batch <= 0 || seqlen <= 0 || dim <= 0 || width <= 0) return SSD_ERR_INVALID_ARGUMENT;
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (activation != SSD_ACT_NONE && activation != SSD_ACT_SILU) return SSD_ERR_INVALID_ARGUMENT;
+    if (!x || !weight || !out) return SSD_ERR_INVALID_ARGUMENT;
+    if (width < 2 || width > 4 || dim % 8 != 0) return SSD_ERR_UNSUPPORTED;
+    if (batch > 65535 || (seqlen + 63) / 64 > 65535 || (double)batch * seqlen * dim > 9.0e15)
+        return SSD_ERR_UNSUPPORTED;
+    if (!aligned(weight, 4) || (bias && !aligned(bias, 4))) return SSD_ERR_INVALID_ARGUMENT;
+    return SSD_OK;
+}
+
+}  // namespace
+
+ssd_status ssd_causal_conv1d_fwd(const void *x, const float *weight, const float *bias,
+                                 int batch, int seqlen, int dim, int width, int activation,
+                                 ssd_dtype io_dtype, void *out, void *conv_state,
+                                 hipStream_t stream) {
+    ssd_status st = check_conv(x, weight, bias, batch, seqlen, dim, width, activation, io_dtype,
+                               out);
+    if (st != SSD_OK) return st;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    // 16-byte vectors of 8 channels (bf16) or two of 4 (fp32)
+    if (!aligned(x, 16) || !aligned(out, 16) || (conv_state && !aligned(conv_state, es)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    ssd::ConvArgs a{x, weight, bias, out, conv_state, batch, seqlen, dim, width,
+                    activation == SSD_ACT_SILU ? 1 : 0};
+    const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_conv1d_fwd<ssd::bf16>(a, stream)
+                                                : ssd::launch_conv1d_fwd<float>(a, stream);
+    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
+ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
+                                    const float *bias, int batch, int dim, int width,
+                                    int activation, ssd_dtype io_dtype, void *out,
+                                    hipStream_t stream) {
+    ssd_status st = check_conv(x, weight, bias, batch, 1, dim, width, activation, io_dtype, out);
+    if (st != SSD_OK) return st;
+    if (!conv_state) return SSD_ERR_INVALID_ARGUMENT;
+    const size_t es = io_dtype == SSD_BF16 ? 2 : 4;
+    if (!aligned(x, es) || !aligned(out, es) || !aligned(conv_state, es))
+        return SSD_ERR_INVALID_ARGUMENT;
+    ssd::ConvArgs a{x, weight, bias, out, conv_state, batch, 1, dim, width,
+                    activation == SSD_ACT_SILU ? 1 : 0};
+    const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_conv1d_update<ssd::bf16>(a, stream)
+                                                : ssd::launch_conv1d_update<float>(a, stream);
+    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // extern "C"

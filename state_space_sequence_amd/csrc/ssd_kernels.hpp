@@ -100,4 +100,22 @@ struct DecodeArgs {
 template <typename T>
 hipError_t launch_state_update(const DecodeArgs &a, hipStream_t stream);
 
+// The causal depthwise convolution before the scan (ssd_conv_kernels.hip):
+// x, out [batch][L][D] (forward) or [batch][D] (update); w [D][W] and bias
+// [D] fp32; state the cache [batch][D][W] (forward: written when non-null;
+// update: in and out).
+struct ConvArgs {
+    const void *x;
+    const float *w;
+    const float *bias;  // may be null
+    void *out;
+    void *state;        // forward: may be null
+    int batch, L, D, W, silu;
+};
+
+template <typename T>
+hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
+template <typename T>
+hipError_t launch_conv1d_update(const ConvArgs &a, hipStream_t stream);
+
 }  // namespace ssd

@@ -147,3 +147,26 @@ def to_torch(inp: dict, io_dtype: str, device):
             t = t.to(tdt)
         out[k] = t.to(device).contiguous()
     return out
+
+
+def make_conv_inputs(batch, seqlen, dim, width, io_dtype="bf16", seed=1234, decode_steps=0):
+    """Inputs of the causal depthwise convolution before the scan.
+
+    x ~ N(0, 1) [batch, seqlen, dim] (the projected x | B | C channels),
+    rounded to bf16 for a bf16 problem; weight [dim, width] and bias [dim]
+    ~ U(-1/sqrt(width), 1/sqrt(width)), the default initialisation of a
+    depthwise ``nn.Conv1d`` (fan-in = width); fp32.  With decode_steps > 0,
+    also x_dec [decode_steps, batch, dim], the tokens that follow.  Draw
+    order: weight, bias, x, x_dec."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    bound = 1.0 / np.sqrt(width)
+    w = rng.uniform(-bound, bound, size=(dim, width)).astype(np.float32)
+    bias = rng.uniform(-bound, bound, size=dim).astype(np.float32)
+    x = rng.standard_normal(size=(batch, seqlen, dim), dtype=np.float32)
+    xd = rng.standard_normal(size=(decode_steps, batch, dim), dtype=np.float32)
+    if io_dtype == "bf16":
+        x, xd = round_to_bf16(x), round_to_bf16(xd)
+    elif io_dtype != "f32":
+        raise ValueError("io_dtype must be 'f32' or 'bf16'")
+    return {"x": np.ascontiguousarray(x), "weight": w, "bias": bias,
+            "x_dec": np.ascontiguousarray(xd)}

@@ -83,6 +83,10 @@ def load():
         lib.ssd_chunk_scan_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(DtProc)]
         lib.ssd_state_update_ex.restype = _i
         lib.ssd_state_update_ex.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p, ctypes.POINTER(DtProc)]
+        lib.ssd_causal_conv1d_fwd.restype = _i
+        lib.ssd_causal_conv1d_fwd.argtypes = [_p, _p, _p] + [_i] * 6 + [_p, _p, _p]
+        lib.ssd_causal_conv1d_update.restype = _i
+        lib.ssd_causal_conv1d_update.argtypes = [_p, _p, _p, _p] + [_i] * 5 + [_p, _p]
         _lib = lib
     return _lib
 
@@ -290,3 +294,82 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream
     if st != SSD_OK:
         raise SsdError(st, where)
     return y
+
+
+_ACT = {None: 0, "none": 0, "silu": 1, "swish": 1}
+
+
+def _conv_params(x, weight, bias, activation, dev):
+    import torch
+    if activation not in _ACT:
+        raise ValueError("activation must be None or 'silu'")
+    _check_dev("weight", weight, torch.float32, dev)
+    _check_dev("bias", bias, torch.float32, dev)
+    D = x.shape[-1]
+    if weight.dim() != 2 or weight.shape[0] != D:
+        raise ValueError("weight must be [dim, width]")
+    if bias is not None and tuple(bias.shape) != (D,):
+        raise ValueError("bias must be [dim]")
+    return D, weight.shape[1], _ACT[activation]
+
+
+def ssd_causal_conv1d_fwd(x, weight, bias=None, activation="silu", out=None, conv_state=None,
+                          return_conv_state=True, stream=None):
+    """Causal depthwise convolution (+ SiLU) over a sequence, from an empty
+    cache: x [b, L, dim] (fp32|bf16), weight [dim, width] fp32, bias [dim]
+    fp32 or None.  Returns (out [b, L, dim] in x's dtype, conv_state
+    [b, dim, width] in x's dtype, the cache for the decode path, or None)."""
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    _check_dev("x", x, None, dev)
+    if x.dim() != 3:
+        raise ValueError("x must be [b, L, dim]")
+    D, W, act = _conv_params(x, weight, bias, activation, dev)
+    b, L = x.shape[0], x.shape[1]
+    if out is None:
+        out = torch.empty_like(x)
+    _check_dev("out", out, x.dtype, dev)
+    if tuple(out.shape) != tuple(x.shape):
+        raise ValueError("out must have x's shape")
+    if conv_state is None and return_conv_state:
+        conv_state = torch.empty((b, D, W), dtype=x.dtype, device=dev)
+    _check_dev("conv_state", conv_state, x.dtype, dev)
+    if conv_state is not None and tuple(conv_state.shape) != (b, D, W):
+        raise ValueError("conv_state must be [b, dim, width]")
+    st = lib.ssd_causal_conv1d_fwd(_ptr(x), _ptr(weight), _ptr(bias), b, L, D, W, act, io,
+                                   _ptr(out), _ptr(conv_state), _stream_handle(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_causal_conv1d_fwd")
+    return out, conv_state
+
+
+def ssd_causal_conv1d_update(conv_state, x, weight, bias=None, activation="silu", out=None,
+                             stream=None):
+    """One decode token: conv_state [b, dim, width] (x's dtype) is rolled
+    left and x [b, dim] appended, in place; returns out [b, dim]."""
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    _check_dev("x", x, None, dev)
+    _check_dev("conv_state", conv_state, x.dtype, dev)
+    if x.dim() != 2:
+        raise ValueError("x must be [b, dim]")
+    D, W, act = _conv_params(x, weight, bias, activation, dev)
+    b = x.shape[0]
+    if tuple(conv_state.shape) != (b, D, W):
+        raise ValueError("conv_state must be [b, dim, width]")
+    if out is None:
+        out = torch.empty_like(x)
+    _check_dev("out", out, x.dtype, dev)
+    st = lib.ssd_causal_conv1d_update(_ptr(conv_state), _ptr(x), _ptr(weight), _ptr(bias), b,
+                                      D, W, act, io, _ptr(out), _stream_handle(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_causal_conv1d_update")
+    return out

@@ -176,3 +176,39 @@ def test_dt_proc_validation(lib, bias, lo, hi):
         ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), None, 1, 2, 4,
         16, 16, 1, ctypes.c_void_p(FAKE), None, ctypes.byref(p))
     assert st == 1
+
+
+def conv(lib, **kw):
+    a = dict(x=FAKE, w=FAKE, bias=None, b=2, L=100, D=64, W=4, act=1, io=1, out=FAKE,
+             state=None)
+    a.update(kw)
+    return lib.ssd_causal_conv1d_fwd(a["x"], a["w"], a["bias"], a["b"], a["L"], a["D"],
+                                     a["W"], a["act"], a["io"], a["out"], a["state"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(b=0), 1),
+    (dict(L=0), 1),
+    (dict(act=2), 1),
+    (dict(io=4), 1),
+    (dict(x=None), 1),
+    (dict(w=None), 1),
+    (dict(out=None), 1),
+    (dict(x=FAKE + 2), 1),
+    (dict(w=FAKE + 2), 1),
+    (dict(D=12), 2),
+    (dict(W=5), 2),
+    (dict(W=1), 2),
+])
+def test_conv_validation(lib, kw, code):
+    assert conv(lib, **kw) == code
+
+
+def test_conv_update_validation(lib):
+    args = [FAKE, FAKE, FAKE, None, 2, 64, 4, 1, 1, FAKE, None]
+    bad_state = list(args)
+    bad_state[0] = None
+    assert lib.ssd_causal_conv1d_update(*bad_state) == 1
+    bad_w = list(args)
+    bad_w[6] = 7
+    assert lib.ssd_causal_conv1d_update(*bad_w) == 2

@@ -349,3 +349,80 @@ def test_process_dt_matches_generator():
     inp = make_inputs(2, 40, 3, 4, 8, 1, io_dtype="f32", seed=5)
     got = process_dt(inp["dt_raw"], inp["dt_bias"], True)
     np.testing.assert_allclose(got, inp["dt"], rtol=2e-6)
+
+
+# ------------------------------------------------------ causal depthwise conv
+
+def _conv_inputs(b=2, L=23, D=5, W=4, seed=3):
+    rng = np.random.default_rng(seed)
+    return (rng.standard_normal((b, L, D)), rng.standard_normal((D, W)),
+            rng.standard_normal(D))
+
+
+@pytest.mark.parametrize("W", [2, 3, 4])
+def test_conv_matches_numpy_convolve(W):
+    """Per channel, the causal convolution is the head of the full
+    convolution with the reversed kernel (numpy.convolve)."""
+    from oracle.conv import causal_conv1d
+    x, w, bias = _conv_inputs(W=W)
+    out = causal_conv1d(x, w, bias, activation=None)
+    L = x.shape[1]
+    for b in range(x.shape[0]):
+        for c in range(x.shape[2]):
+            ref = np.convolve(x[b, :, c], w[c, ::-1])[:L] + bias[c]
+            np.testing.assert_allclose(out[b, :, c], ref, rtol=1e-13, atol=1e-13)
+
+
+def test_conv_matches_the_layers_conv1d_module():
+    """The layer's own construction, run by plain PyTorch on the CPU in fp64:
+    Conv1d(groups=D, padding=W-1) on [b, D, L], cut to the first L outputs,
+    then SiLU."""
+    import torch
+    from oracle.conv import causal_conv1d
+    x, w, bias = _conv_inputs(b=2, L=30, D=6, W=4, seed=8)
+    conv = torch.nn.Conv1d(6, 6, kernel_size=4, groups=6, padding=3, bias=True).double()
+    with torch.no_grad():
+        conv.weight.copy_(torch.from_numpy(w)[:, None, :])
+        conv.bias.copy_(torch.from_numpy(bias))
+        ref = torch.nn.functional.silu(conv(torch.from_numpy(x).transpose(1, 2))[..., :30])
+    np.testing.assert_allclose(causal_conv1d(x, w, bias, "silu"),
+                               ref.transpose(1, 2).numpy(), rtol=1e-12, atol=1e-13)
+
+
+def test_conv_impulse_response():
+    """A unit impulse at t0 comes out as the reversed kernel from t0 on."""
+    from oracle.conv import causal_conv1d
+    W, L, t0 = 4, 12, 5
+    x = np.zeros((1, L, 1))
+    x[0, t0, 0] = 1.0
+    w = np.array([[2.0, -3.0, 5.0, 7.0]])
+    out = causal_conv1d(x, w, None, activation=None)[0, :, 0]
+    expect = np.zeros(L)
+    expect[t0:t0 + W] = w[0, ::-1]
+    np.testing.assert_array_equal(out, expect)
+
+
+def test_silu_closed_forms():
+    """silu(0) = 0, silu(v) - silu(-v) = v, and silu = v * expit(v)."""
+    from scipy.special import expit
+    from oracle.conv import silu
+    assert silu(0.0) == 0.0
+    v = np.linspace(-40.0, 40.0, 161)
+    np.testing.assert_allclose(silu(v) - silu(-v), v, rtol=0, atol=1e-12)
+    np.testing.assert_allclose(silu(v), v * expit(v), rtol=1e-14, atol=1e-300)
+
+
+@pytest.mark.parametrize("L", [2, 4, 9])
+def test_conv_decode_steps_match_forward(L):
+    """L decode steps from an empty cache give the forward's outputs, and the
+    cache then equals the forward's final cache (also for L < W)."""
+    from oracle.conv import causal_conv1d, conv_state_after, conv_update
+    x, w, bias = _conv_inputs(b=2, L=L, D=5, W=4, seed=11)
+    out = causal_conv1d(x, w, bias, "silu")
+    state = np.zeros((2, 5, 4))
+    for t in range(L):
+        o, state = conv_update(state, x[:, t], w, bias, "silu")
+        np.testing.assert_allclose(o, out[:, t], rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(state, conv_state_after(x, 4))
+    if L < 4:
+        assert np.all(state[:, :, :4 - L] == 0)

@@ -419,3 +419,72 @@ def test_decode_dt_preprocessing(dev, oracle_mod, io):
     yr, finr, ya, fa = reference(oracle_mod, dict(inp, dt=dtp))
     check(y, yr, io, "decode y", ya)
     check(state.cpu().numpy(), finr, io, "decode state", fa)
+
+
+# ------------------------------------------------------ causal depthwise conv
+
+# (b, L, dim, width, io, bias, activation)
+CONV = [
+    (2, 300, 96, 4, "bf16", True, "silu"),
+    (1, 70, 40, 4, "f32", True, "silu"),        # ragged 64-token run
+    (3, 3, 16, 4, "bf16", False, None),          # seqlen < width
+    (2, 129, 2056, 3, "f32", True, "silu"),      # two 256-lane channel blocks, the second partial
+    (1, 65, 8, 2, "bf16", True, "silu"),         # width 2, one channel group
+    (2, 1, 24, 4, "f32", True, None),            # a single token
+]
+
+
+def _conv_ref(x, w, bias, act):
+    from oracle.conv import causal_conv1d
+    ref = causal_conv1d(x, w, bias, act)
+    mag = causal_conv1d(np.abs(x), np.abs(w), None if bias is None else np.abs(bias), None)
+    return ref, mag
+
+
+@pytest.mark.parametrize("case", CONV, ids=lambda c: "b%d_L%d_D%d_W%d_%s" % c[:5]
+                         + ("_bias" if c[5] else "") + ("_" + c[6] if c[6] else ""))
+def test_causal_conv1d_every_element(dev, case):
+    import torch
+    from oracle.conv import conv_state_after
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs
+    b, L, D, W, io, use_bias, act = case
+    _say("conv case %s" % (case,))
+    inp = make_conv_inputs(b, L, D, W, io_dtype=io, seed=500 + L + D)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    x = torch.from_numpy(inp["x"]).to(tdt).to(dev)
+    w = torch.from_numpy(inp["weight"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev) if use_bias else None
+    out, state = libssd.ssd_causal_conv1d_fwd(x, w, bias, activation=act)
+    torch.cuda.synchronize()
+    ref, mag = _conv_ref(inp["x"], inp["weight"], inp["bias"] if use_bias else None, act)
+    check(out.float().cpu().numpy(), ref, io, "conv out", mag)
+    # the cache holds inputs (exact copies)
+    np.testing.assert_array_equal(state.float().cpu().numpy(), conv_state_after(inp["x"], W))
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_causal_conv1d_prefill_then_decode(dev, io):
+    """The layer's sequence: a prefill over L tokens leaves the cache, then
+    single-token updates continue from it; outputs against the oracle over
+    the whole L + steps tokens."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs
+    b, L, D, W, steps = 3, 37, 264, 4, 6
+    inp = make_conv_inputs(b, L, D, W, io_dtype=io, seed=77, decode_steps=steps)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    x = torch.from_numpy(inp["x"]).to(tdt).to(dev)
+    w = torch.from_numpy(inp["weight"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    out, state = libssd.ssd_causal_conv1d_fwd(x, w, bias, activation="silu")
+    outs = []
+    for s in range(steps):
+        xs = torch.from_numpy(inp["x_dec"][s]).to(tdt).to(dev).contiguous()
+        outs.append(libssd.ssd_causal_conv1d_update(state, xs, w, bias, activation="silu"))
+    torch.cuda.synchronize()
+    xall = np.concatenate([inp["x"], inp["x_dec"].transpose(1, 0, 2)], axis=1)
+    ref, mag = _conv_ref(xall, inp["weight"], inp["bias"], "silu")
+    check(out.float().cpu().numpy(), ref[:, :L], io, "prefill out", mag[:, :L])
+    got = torch.stack(outs, 1).float().cpu().numpy()
+    check(got, ref[:, L:], io, "decode out", mag[:, L:])
