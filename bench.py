@@ -14,6 +14,8 @@ Also reported (not part of ``value``):
   * the other forward workloads, and the headline forward again on the raw
     time step with the preprocessing (bias, softplus) inside the kernels;
   * the decode state update on the b256 / 80-head workload;
+  * the causal depthwise conv before the scan on the same layer's channels,
+    and its single-token update at batch 256;
   * ``cpu_baseline``: the fp64 serial oracle on the host cores over a bounded
     sample of (batch, head) slices of the same workload.
 """
@@ -223,6 +225,69 @@ def time_forward_dt_proc(w, dev, ev, steps=100, warmup=50):
     ev.destroy(e1)
     del t, y, fin, ws
     return ms
+
+
+def time_conv(w, dev, ev, steps=50, warmup=20, decode_batch=256):
+    """The causal depthwise conv that precedes the scan, on this layer's
+    x | B | C channels (dim = H P + 2 G N, width 4, SiLU, bias): the
+    sequence forward and the single-token update at batch decode_batch,
+    each against the HBM roofline of its algorithmic bytes."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs
+    D, W = w.nheads * w.headdim + 2 * w.ngroups * w.dstate, 4
+    es = 2 if w.io_dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    inp = make_conv_inputs(w.batch, w.seqlen, D, W, io_dtype=w.io_dtype, seed=w.seed)
+    x = torch.from_numpy(inp["x"]).to(tdt).to(dev)
+    wt = torch.from_numpy(inp["weight"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    out = torch.empty_like(x)
+    state = torch.empty((w.batch, D, W), dtype=tdt, device=dev)
+    sh = torch.cuda.current_stream().cuda_stream
+
+    def timed(fn, n):
+        for _ in range(warmup):
+            fn()
+        e0, e1 = ev.create(), ev.create()
+        torch.cuda.synchronize()
+        ev.record(e0, sh)
+        for _ in range(n):
+            fn()
+        ev.record(e1, sh)
+        torch.cuda.synchronize()
+        ms = ev.ms(e0, e1) / n
+        ev.destroy(e0)
+        ev.destroy(e1)
+        return ms
+
+    ms = timed(lambda: libssd.ssd_causal_conv1d_fwd(x, wt, bias, "silu", out=out,
+                                                    conv_state=state), steps)
+    alg = 2 * w.batch * w.seqlen * D * es + D * (W + 1) * 4 + w.batch * D * W * es
+    gbs = alg / (ms * 1e-3) / 1e9
+    res = {"workload": "causal conv1d b%d L%d dim %d width %d, SiLU, %s"
+                       % (w.batch, w.seqlen, D, W, w.io_dtype),
+           "ms_per_step": round(ms, 4),
+           "tokens_per_s": round(w.batch * w.seqlen / (ms * 1e-3), 1),
+           "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                        "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                        "alg_bytes_per_launch": alg}}
+    bd = decode_batch
+    cs = torch.zeros((bd, D, W), dtype=tdt, device=dev)
+    xd = torch.randn((bd, D), device=dev).to(tdt)
+    od = torch.empty_like(xd)
+    msd = timed(lambda: libssd.ssd_causal_conv1d_update(cs, xd, wt, bias, "silu", out=od),
+                steps * 4)
+    algd = 2 * bd * D * W * es + 2 * bd * D * es + D * (W + 1) * 4
+    gbd = algd / (msd * 1e-3) / 1e9
+    res_d = {"workload": "causal conv1d update b%d dim %d width %d, SiLU, %s"
+                         % (bd, D, W, w.io_dtype),
+             "us_per_step": round(msd * 1e3, 2),
+             "roofline": {"bound": "hbm", "achieved": round(gbd, 1), "peak": HBM_PEAK_GBS,
+                          "unit": "GB/s", "frac": round(gbd / HBM_PEAK_GBS, 4),
+                          "alg_bytes_per_launch": algd}}
+    del x, out, state, cs, xd, od
+    return res, res_d
 
 
 def time_decode(w, dev, ev, reps=3):
@@ -464,6 +529,7 @@ def main():
             "ms_per_step": round(msd, 4),
             "tokens_per_s": round(w.batch * w.seqlen / (msd * 1e-3), 1)}
         extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
+        extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(w, dev, ev)
         out["other_workloads"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["inputs"])

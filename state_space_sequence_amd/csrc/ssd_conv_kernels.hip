@@ -20,6 +20,9 @@
 // issues the loads of 8 tokens before using them; consecutive lanes take
 // consecutive channel groups, so a wave reads 1 KB of each token row.
 // Update: a thread owns one channel; its W-element cache row is contiguous.
+// The forward's outputs are written once and carry the non-temporal hint
+// (measured: 5% shorter on the 2.7B layer's channels; the same hint on the
+// loads costs a third more time on a cache-resident 130M-size input).
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
 
@@ -50,11 +53,11 @@ __device__ __forceinline__ void store8(bf16 *p, const float (&v)[8]) {
     bf16x8 q;
 #pragma unroll
     for (int j = 0; j < 8; ++j) q[j] = (bf16)v[j];
-    *reinterpret_cast<bf16x8 *>(p) = q;
+    __builtin_nontemporal_store(q, reinterpret_cast<bf16x8 *>(p));
 }
 __device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
-    *reinterpret_cast<f32x4 *>(p) = f32x4{v[0], v[1], v[2], v[3]};
-    *reinterpret_cast<f32x4 *>(p + 4) = f32x4{v[4], v[5], v[6], v[7]};
+    __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
+    __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(p + 4));
 }
 
 // SiLU v sigmoid(v) = v / (1 + e^-v) (the layer's activation)
