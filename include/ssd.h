@@ -296,6 +296,32 @@ ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float
                                     int activation, ssd_dtype io_dtype, void *out,
                                     hipStream_t stream);
 
+/*
+ * The gated RMS normalisation that follows the scan in the Mamba-2 layer
+ * (fla `layers/mamba2.py`: `RMSNormGated(intermediate_size, eps=norm_eps,
+ * norm_before_gate=False)`, applied as `norm(y, gate)` to the scan output).
+ * Per row of dim values, with silu(v) = v / (1 + e^-v):
+ *
+ *   norm_before_gate == 0 (the layer's):  g = y * silu(z),
+ *                                        out = g / sqrt(mean(g^2) + eps) * weight
+ *   norm_before_gate != 0:               out = y / sqrt(mean(y^2) + eps) * weight * silu(z)
+ *   z == NULL:                           out = y / sqrt(mean(y^2) + eps) * weight
+ *
+ * The mean runs over the whole row (the module as the layer builds it has
+ * no group size).
+ *
+ *   y, z    [rows, dim]  io_dtype  in, 16-byte aligned (z may be NULL)
+ *   weight  [dim]        fp32      in, 16-byte aligned
+ *   out     [rows, dim]  io_dtype  out, 16-byte aligned; may alias y
+ *   eps     >= 0 (the layer's norm_eps, 1e-5 by default)
+ *
+ * dim must be a multiple of 8 and at most 8192 (else SSD_ERR_UNSUPPORTED).
+ * Sums and scaling are fp32; out is rounded to io_dtype.
+ */
+ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weight, int rows,
+                                 int dim, float eps, int norm_before_gate, ssd_dtype io_dtype,
+                                 void *out, hipStream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -19,6 +19,7 @@ Contents
              fp64, for the library's fused preprocessing.
 ``conv``     the layer's causal depthwise convolution (+ SiLU) and its decode
              update, in fp64.
+``norm``     the layer's gated RMS normalisation after the scan, in fp64.
 """
 from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
-from . import conv, dt, forms, metrics  # noqa: F401
+from . import conv, dt, forms, metrics, norm  # noqa: F401

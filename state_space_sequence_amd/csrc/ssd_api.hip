@@ -377,4 +377,28 @@ ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float
     return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
 }
 
+ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weight, int rows,
+                                 int dim, float eps, int norm_before_gate, ssd_dtype io_dtype,
+                                 void *out, hipStream_t stream) {
+    if (rows <= 0 || dim <= 0 || !(eps >= 0.f) || eps > 3.0e38f) return SSD_ERR_INVALID_ARGUMENT;
+    if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
+    if (!y || !weight || !out) return SSD_ERR_INVALID_ARGUMENT;
+    if (dim % 8 != 0 || dim > ssd::kMaxNormDim) return SSD_ERR_UNSUPPORTED;
+    if ((double)rows * dim > 9.0e15 || (rows + 3) / 4 > 2147483647) return SSD_ERR_UNSUPPORTED;
+    if (!aligned(y, 16) || !aligned(out, 16) || !aligned(weight, 16) || (z && !aligned(z, 16)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    ssd::NormArgs a;
+    a.y = y;
+    a.z = z;
+    a.w = weight;
+    a.out = out;
+    a.rows = rows;
+    a.dim = dim;
+    a.gate = z ? (norm_before_gate ? 2 : 1) : 0;
+    a.eps = eps;
+    const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_gated_rmsnorm<ssd::bf16>(a, stream)
+                                                : ssd::launch_gated_rmsnorm<float>(a, stream);
+    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+}
+
 }  // extern "C"

@@ -118,4 +118,20 @@ hipError_t launch_conv1d_fwd(const ConvArgs &a, hipStream_t stream);
 template <typename T>
 hipError_t launch_conv1d_update(const ConvArgs &a, hipStream_t stream);
 
+// The gated RMS normalisation after the scan (ssd_norm_kernels.hip): y, z,
+// out [rows][dim]; w [dim] fp32; gate 0 none, 1 before the normalisation
+// (the layer's), 2 after it.
+struct NormArgs {
+    const void *y;
+    const void *z;  // may be null when gate == 0
+    const float *w;
+    void *out;
+    int rows, dim, gate;
+    float eps;
+};
+constexpr int kMaxNormDim = 8192;
+
+template <typename T>
+hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream);
+
 }  // namespace ssd

@@ -170,3 +170,20 @@ def make_conv_inputs(batch, seqlen, dim, width, io_dtype="bf16", seed=1234, deco
         raise ValueError("io_dtype must be 'f32' or 'bf16'")
     return {"x": np.ascontiguousarray(x), "weight": w, "bias": bias,
             "x_dec": np.ascontiguousarray(xd)}
+
+
+def make_norm_inputs(rows, dim, io_dtype="bf16", seed=1234):
+    """Inputs of the gated RMS normalisation after the scan: y, z ~ N(0, 1)
+    [rows, dim] (the scan output and the gate channels), rounded to bf16 for
+    a bf16 problem; weight [dim] fp32 = 1 + 0.1 N(0, 1) (the module starts at
+    ones; a spread exercises the per-channel scale).  Draw order: y, z,
+    weight."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    y = rng.standard_normal(size=(rows, dim), dtype=np.float32)
+    z = rng.standard_normal(size=(rows, dim), dtype=np.float32)
+    w = (1.0 + 0.1 * rng.standard_normal(size=dim)).astype(np.float32)
+    if io_dtype == "bf16":
+        y, z = round_to_bf16(y), round_to_bf16(z)
+    elif io_dtype != "f32":
+        raise ValueError("io_dtype must be 'f32' or 'bf16'")
+    return {"y": np.ascontiguousarray(y), "z": np.ascontiguousarray(z), "weight": w}

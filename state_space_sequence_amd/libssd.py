@@ -87,6 +87,8 @@ def load():
         lib.ssd_causal_conv1d_fwd.argtypes = [_p, _p, _p] + [_i] * 6 + [_p, _p, _p]
         lib.ssd_causal_conv1d_update.restype = _i
         lib.ssd_causal_conv1d_update.argtypes = [_p, _p, _p, _p] + [_i] * 5 + [_p, _p]
+        lib.ssd_gated_rmsnorm_fwd.restype = _i
+        lib.ssd_gated_rmsnorm_fwd.argtypes = [_p, _p, _p, _i, _i, ctypes.c_float, _i, _i, _p, _p]
         _lib = lib
     return _lib
 
@@ -372,4 +374,36 @@ def ssd_causal_conv1d_update(conv_state, x, weight, bias=None, activation="silu"
                                       D, W, act, io, _ptr(out), _stream_handle(stream))
     if st != SSD_OK:
         raise SsdError(st, "ssd_causal_conv1d_update")
+    return out
+
+
+def ssd_gated_rmsnorm_fwd(y, z, weight, eps=1e-5, norm_before_gate=False, out=None, stream=None):
+    """Gated RMS normalisation over the last axis: y, z [..., dim] (fp32|bf16;
+    z may be None), weight [dim] fp32.  Returns out (y's shape and dtype);
+    out may be y itself."""
+    import torch
+    lib = load()
+    dev = y.device
+    if dev.type != "cuda":
+        raise ValueError("y must be a GPU tensor")
+    io = _dtype_code(y)
+    _check_dev("y", y, None, dev)
+    _check_dev("z", z, y.dtype, dev)
+    _check_dev("weight", weight, torch.float32, dev)
+    dim = y.shape[-1]
+    if z is not None and tuple(z.shape) != tuple(y.shape):
+        raise ValueError("z must have y's shape")
+    if tuple(weight.shape) != (dim,):
+        raise ValueError("weight must be [dim]")
+    rows = y.numel() // dim
+    if out is None:
+        out = torch.empty_like(y)
+    _check_dev("out", out, y.dtype, dev)
+    if tuple(out.shape) != tuple(y.shape):
+        raise ValueError("out must have y's shape")
+    st = lib.ssd_gated_rmsnorm_fwd(_ptr(y), _ptr(z), _ptr(weight), rows, dim, float(eps),
+                                   1 if norm_before_gate else 0, io, _ptr(out),
+                                   _stream_handle(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_gated_rmsnorm_fwd")
     return out

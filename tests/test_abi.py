@@ -212,3 +212,28 @@ def test_conv_update_validation(lib):
     bad_w = list(args)
     bad_w[6] = 7
     assert lib.ssd_causal_conv1d_update(*bad_w) == 2
+
+
+def norm(lib, **kw):
+    a = dict(y=FAKE, z=None, w=FAKE, rows=4, dim=64, eps=1e-5, nbg=0, io=1, out=FAKE)
+    a.update(kw)
+    return lib.ssd_gated_rmsnorm_fwd(a["y"], a["z"], a["w"], a["rows"], a["dim"], a["eps"],
+                                     a["nbg"], a["io"], a["out"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(rows=0), 1),
+    (dict(dim=0), 1),
+    (dict(eps=-1.0), 1),
+    (dict(eps=float("nan")), 1),
+    (dict(io=3), 1),
+    (dict(y=None), 1),
+    (dict(w=None), 1),
+    (dict(out=None), 1),
+    (dict(y=FAKE + 8), 1),
+    (dict(z=FAKE + 4), 1),
+    (dict(dim=12), 2),
+    (dict(dim=8200), 2),
+])
+def test_norm_validation(lib, kw, code):
+    assert norm(lib, **kw) == code

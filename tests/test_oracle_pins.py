@@ -426,3 +426,38 @@ def test_conv_decode_steps_match_forward(L):
     np.testing.assert_array_equal(state, conv_state_after(x, 4))
     if L < 4:
         assert np.all(state[:, :, :4 - L] == 0)
+
+
+# ------------------------------------------------------ gated RMS normalisation
+
+def test_rmsnorm_matches_torch():
+    """Without a gate, and with the gate applied first, against plain
+    PyTorch's rms_norm on the CPU in fp64 (the gate product formed with
+    torch's own SiLU)."""
+    import torch
+    from oracle.norm import gated_rmsnorm
+    rng = np.random.default_rng(21)
+    y, z = rng.standard_normal((5, 48)), rng.standard_normal((5, 48))
+    w = rng.uniform(0.5, 1.5, 48)
+    ty, tz, tw = (torch.from_numpy(a) for a in (y, z, w))
+    ref = torch.nn.functional.rms_norm(ty, (48,), tw, eps=1e-5).numpy()
+    np.testing.assert_allclose(gated_rmsnorm(y, None, w, 1e-5), ref, rtol=1e-13, atol=1e-14)
+    refg = torch.nn.functional.rms_norm(ty * torch.nn.functional.silu(tz), (48,), tw, eps=1e-5)
+    np.testing.assert_allclose(gated_rmsnorm(y, z, w, 1e-5), refg.numpy(), rtol=1e-13, atol=1e-14)
+    refa = torch.nn.functional.rms_norm(ty, (48,), tw, eps=1e-5) * torch.nn.functional.silu(tz)
+    np.testing.assert_allclose(gated_rmsnorm(y, z, w, 1e-5, norm_before_gate=True), refa.numpy(),
+                               rtol=1e-13, atol=1e-14)
+
+
+def test_rmsnorm_closed_forms():
+    """With eps = 0 and unit weights every output row has RMS 1 and the
+    result is invariant under scaling a row; a constant row c gives sign(c)."""
+    from oracle.norm import gated_rmsnorm
+    rng = np.random.default_rng(22)
+    y = rng.standard_normal((4, 40))
+    out = gated_rmsnorm(y, None, np.ones(40), eps=0.0)
+    np.testing.assert_allclose(np.sqrt(np.mean(out ** 2, axis=-1)), 1.0, rtol=1e-14)
+    np.testing.assert_allclose(gated_rmsnorm(7.5 * y, None, np.ones(40), eps=0.0), out,
+                               rtol=1e-14, atol=1e-15)
+    np.testing.assert_array_equal(gated_rmsnorm(np.full((1, 8), -3.0), None, np.ones(8), 0.0),
+                                  -np.ones((1, 8)))

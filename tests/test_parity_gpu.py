@@ -488,3 +488,53 @@ def test_causal_conv1d_prefill_then_decode(dev, io):
     check(out.float().cpu().numpy(), ref[:, :L], io, "prefill out", mag[:, :L])
     got = torch.stack(outs, 1).float().cpu().numpy()
     check(got, ref[:, L:], io, "decode out", mag[:, L:])
+
+
+# ------------------------------------------------------ gated RMS normalisation
+
+# (rows, dim, io, gate: "before" | "after" | None)
+NORM = [
+    (300, 512, "bf16", "before"),      # the layer's order, one vector per lane
+    (37, 5120, "bf16", "before"),      # the 2.7B layer's row (10 vectors per lane)
+    (64, 1536, "f32", "before"),       # the 130M layer's row
+    (5, 8192, "f32", "after"),         # the largest row
+    (9, 40, "bf16", None),             # a row shorter than a wave's vector
+    (130, 2056, "f32", None),          # a ragged last vector group
+]
+
+
+@pytest.mark.parametrize("case", NORM, ids=lambda c: "rows%d_dim%d_%s_%s" % c)
+def test_gated_rmsnorm_every_element(dev, case):
+    import torch
+    from oracle.norm import gated_rmsnorm
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_norm_inputs
+    rows, dim, io, gate = case
+    _say("norm case %s" % (case,))
+    inp = make_norm_inputs(rows, dim, io_dtype=io, seed=600 + dim)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    y = torch.from_numpy(inp["y"]).to(tdt).to(dev)
+    z = torch.from_numpy(inp["z"]).to(tdt).to(dev) if gate else None
+    w = torch.from_numpy(inp["weight"]).to(dev)
+    out = libssd.ssd_gated_rmsnorm_fwd(y, z, w, eps=1e-5, norm_before_gate=gate == "after")
+    torch.cuda.synchronize()
+    ref = gated_rmsnorm(inp["y"], inp["z"] if gate else None, inp["weight"], 1e-5,
+                        norm_before_gate=gate == "after")
+    # each output is a product of its inputs and the row's scale: no
+    # cancellation, so the magnitude reference is the output itself
+    check(out.float().cpu().numpy(), ref, io, "norm out", np.abs(ref))
+
+
+def test_gated_rmsnorm_in_place(dev):
+    import torch
+    from oracle.norm import gated_rmsnorm
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_norm_inputs
+    inp = make_norm_inputs(20, 1024, io_dtype="bf16", seed=9)
+    y = torch.from_numpy(inp["y"]).to(torch.bfloat16).to(dev)
+    z = torch.from_numpy(inp["z"]).to(torch.bfloat16).to(dev)
+    w = torch.from_numpy(inp["weight"]).to(dev)
+    libssd.ssd_gated_rmsnorm_fwd(y, z, w, out=y)
+    torch.cuda.synchronize()
+    check(y.float().cpu().numpy(), gated_rmsnorm(inp["y"], inp["z"], inp["weight"]), "bf16",
+          "norm in place")
