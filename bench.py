@@ -16,6 +16,7 @@ Also reported (not part of ``value``):
   * the decode state update on the b256 / 80-head workload;
   * the causal depthwise conv before the scan on the same layer's channels,
     and its single-token update at batch 256;
+  * the gated RMS normalisation after the scan on the same layer's output;
   * ``cpu_baseline``: the fp64 serial oracle on the host cores over a bounded
     sample of (batch, head) slices of the same workload.
 """
@@ -290,6 +291,44 @@ def time_conv(w, dev, ev, steps=50, warmup=20, decode_batch=256):
     return res, res_d
 
 
+def time_norm(w, dev, ev, steps=50, warmup=20):
+    """The gated RMS normalisation after the scan on this layer's output
+    (rows = b L, dim = H P, gate before the norm, eps 1e-5), against the HBM
+    roofline of its algorithmic bytes (y and z read, out written once)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_norm_inputs
+    rows, dim = w.batch * w.seqlen, w.nheads * w.headdim
+    es = 2 if w.io_dtype == "bf16" else 4
+    tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    inp = make_norm_inputs(rows, dim, io_dtype=w.io_dtype, seed=w.seed)
+    y = torch.from_numpy(inp["y"]).to(tdt).to(dev)
+    z = torch.from_numpy(inp["z"]).to(tdt).to(dev)
+    wt = torch.from_numpy(inp["weight"]).to(dev)
+    out = torch.empty_like(y)
+    sh = torch.cuda.current_stream().cuda_stream
+    for _ in range(warmup):
+        libssd.ssd_gated_rmsnorm_fwd(y, z, wt, out=out)
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, sh)
+    for _ in range(steps):
+        libssd.ssd_gated_rmsnorm_fwd(y, z, wt, out=out)
+    ev.record(e1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    alg = 3 * rows * dim * es + dim * 4
+    gbs = alg / (ms * 1e-3) / 1e9
+    del y, z, out
+    return {"workload": "gated RMSNorm rows %d dim %d, %s" % (rows, dim, w.io_dtype),
+            "ms_per_step": round(ms, 4),
+            "roofline": {"bound": "hbm", "achieved": round(gbs, 1), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "alg_bytes_per_launch": alg}}
+
+
 def time_decode(w, dev, ev, reps=3):
     """Steps of ssd_state_update over the decode workload, timed with events."""
     import torch
@@ -530,6 +569,7 @@ def main():
             "tokens_per_s": round(w.batch * w.seqlen / (msd * 1e-3), 1)}
         extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
         extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(w, dev, ev)
+        extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev)
         out["other_workloads"] = extra
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(w, r["inputs"])

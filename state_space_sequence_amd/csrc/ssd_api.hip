@@ -384,7 +384,7 @@ ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weig
     if (io_dtype != SSD_F32 && io_dtype != SSD_BF16) return SSD_ERR_INVALID_ARGUMENT;
     if (!y || !weight || !out) return SSD_ERR_INVALID_ARGUMENT;
     if (dim % 8 != 0 || dim > ssd::kMaxNormDim) return SSD_ERR_UNSUPPORTED;
-    if ((double)rows * dim > 9.0e15 || (rows + 3) / 4 > 2147483647) return SSD_ERR_UNSUPPORTED;
+    if ((double)rows * dim > 9.0e15) return SSD_ERR_UNSUPPORTED;
     if (!aligned(y, 16) || !aligned(out, 16) || !aligned(weight, 16) || (z && !aligned(z, 16)))
         return SSD_ERR_INVALID_ARGUMENT;
     ssd::NormArgs a;

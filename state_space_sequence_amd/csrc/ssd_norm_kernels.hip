@@ -12,11 +12,13 @@
 // and with it after (norm_before_gate): out = y / sqrt(mean(y^2) + eps) * w *
 // silu(z).  Without a gate it is the plain RMS normalisation.
 //
-// One wave per row: lane l holds the 16-byte vectors l, l + 64, ... of the
-// row (8 values each) in registers, the sum of squares is reduced across the
-// wave, and the row is scaled and stored.  It reads y and z and writes out
-// once, so it is bound by HBM bandwidth; the output stores carry the
-// non-temporal hint.
+// One 256-thread workgroup per row: thread i holds the 16-byte vectors i,
+// i + 256, ... of the row (8 values each) in registers, the sum of squares
+// is reduced within each wave and then across the four through LDS, and the
+// row is scaled and stored.  The loads of y and z are unconditional (from a
+// clamped vector where a thread has none), so a thread's loads all issue
+// before it waits.  It reads y and z and writes out once, so it is bound by
+// HBM bandwidth; the output stores carry the non-temporal hint.
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
 
@@ -54,49 +56,50 @@ __device__ __forceinline__ float nsilu(float v) {
 
 }  // namespace
 
-// grid (ceil(rows / 4)), 256 threads (4 rows per workgroup); NV 16-byte
-// vectors per lane cover up to 512 NV values of a row; dim % 8 == 0.
-// gate: 0 none, 1 gate before the normalisation, 2 after it.
-template <typename T, int NV>
+// grid (rows), 256 threads; NV 16-byte vectors per thread cover up to
+// 2048 NV values of a row; dim % 8 == 0.  GATE: 0 none, 1 gate before the
+// normalisation, 2 after it.
+template <typename T, int NV, int GATE>
 __global__ void __launch_bounds__(256)
 k_gated_rmsnorm(const T *__restrict__ y, const T *__restrict__ z, const float *__restrict__ w,
-                T *__restrict__ out, int rows, int dim, float eps, int gate) {
-    const int row = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-    if (row >= rows) return;
-    const size_t base = (size_t)row * dim;
-    float g[NV][8];
+                T *__restrict__ out, int dim, float eps) {
+    __shared__ float s_part[4];
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const size_t base = (size_t)blockIdx.x * dim;
+    float g[NV][8], zv[GATE ? NV : 1][8];
+#pragma unroll
+    for (int i = 0; i < NV; ++i) {
+        const int c = min(8 * (tid + 256 * i), dim - 8);
+        nload8(y + base + c, g[i]);
+        if (GATE) nload8(z + base + c, zv[GATE ? i : 0]);
+    }
     float ss = 0.f;
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int c = 8 * (lane + 64 * i);
-        if (c < dim) {
-            nload8(y + base + c, g[i]);
-            if (gate == 1) {
-                float zv[8];
-                nload8(z + base + c, zv);
+        const bool valid = 8 * (tid + 256 * i) < dim;
 #pragma unroll
-                for (int j = 0; j < 8; ++j) g[i][j] *= nsilu(zv[j]);
-            }
-#pragma unroll
-            for (int j = 0; j < 8; ++j) ss += g[i][j] * g[i][j];
+        for (int j = 0; j < 8; ++j) {
+            if (GATE == 1) g[i][j] *= nsilu(zv[GATE ? i : 0][j]);
+            if (!valid) g[i][j] = 0.f;
+            ss += g[i][j] * g[i][j];
         }
     }
 #pragma unroll
     for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, kWave);
+    if (lane == 0) s_part[wave] = ss;
+    __syncthreads();
+    ss = (s_part[0] + s_part[1]) + (s_part[2] + s_part[3]);
     const float rstd = __builtin_amdgcn_rsqf(ss / (float)dim + eps);
 #pragma unroll
     for (int i = 0; i < NV; ++i) {
-        const int c = 8 * (lane + 64 * i);
+        const int c = 8 * (tid + 256 * i);
         if (c < dim) {
             float wv[8], o[8];
             nload8(w + c, wv);
 #pragma unroll
-            for (int j = 0; j < 8; ++j) o[j] = g[i][j] * rstd * wv[j];
-            if (gate == 2) {
-                float zv[8];
-                nload8(z + base + c, zv);
-#pragma unroll
-                for (int j = 0; j < 8; ++j) o[j] *= nsilu(zv[j]);
+            for (int j = 0; j < 8; ++j) {
+                o[j] = g[i][j] * rstd * wv[j];
+                if (GATE == 2) o[j] *= nsilu(zv[GATE ? i : 0][j]);
             }
             nstore8(out + base + c, o);
         }
@@ -105,19 +108,18 @@ k_gated_rmsnorm(const T *__restrict__ y, const T *__restrict__ z, const float *_
 
 template <typename T>
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream) {
-    const dim3 grid((a.rows + 3) / 4);
-    const int nv = (a.dim / 8 + 63) / 64;  // 16-byte vectors per lane
-#define SSD_NORM_CASE(NN)                                                                     \
-    if (nv <= NN) {                                                                           \
-        hipLaunchKernelGGL((k_gated_rmsnorm<T, NN>), grid, dim3(256), 0, stream,             \
-                           (const T *)a.y, (const T *)a.z, a.w, (T *)a.out, a.rows, a.dim, a.eps, \
-                           a.gate);                                                           \
+    const int nv = (a.dim / 8 + 255) / 256;  // 16-byte vectors per thread
+#define SSD_NORM_CASE(NN, GG)                                                                 \
+    if (nv <= NN && a.gate == GG) {                                                           \
+        hipLaunchKernelGGL((k_gated_rmsnorm<T, NN, GG>), dim3(a.rows), dim3(256), 0, stream, \
+                           (const T *)a.y, (const T *)a.z, a.w, (T *)a.out, a.dim, a.eps);   \
         return hipGetLastError();                                                             \
     }
-    SSD_NORM_CASE(2)
-    SSD_NORM_CASE(4)
-    SSD_NORM_CASE(8)
-    SSD_NORM_CASE(16)
+#define SSD_NORM_GATES(NN) SSD_NORM_CASE(NN, 0) SSD_NORM_CASE(NN, 1) SSD_NORM_CASE(NN, 2)
+    SSD_NORM_GATES(1)
+    SSD_NORM_GATES(2)
+    SSD_NORM_GATES(4)
+#undef SSD_NORM_GATES
 #undef SSD_NORM_CASE
     return hipErrorInvalidValue;
 }
