@@ -231,6 +231,28 @@ ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
                                  const ssd_dt_proc *dt_proc);
 
 /*
+ * Packed variable-length sequences: each batch row holds several sequences
+ * one after the other, told apart by seq_idx [batch, seqlen] (int32 device
+ * pointer, 4-byte aligned), the `seq_idx` argument of the pages'
+ * `mamba_chunk_scan_combined`.  Token t > 0 whose seq_idx differs from token
+ * t-1's starts a new sequence: the state entering it is zero, so no output
+ * or state depends on an earlier sequence.  initial_state enters the row's
+ * first sequence; final_state is that of the row's last token.  Otherwise
+ * as ssd_chunk_scan_fwd_ex (dt_proc may be NULL).  Only the fused pass
+ * handles it (bf16 io, dstate 128, headdim a multiple of 32); other shapes,
+ * and the split path when forced, return SSD_ERR_UNSUPPORTED; a NULL seq_idx
+ * is SSD_ERR_INVALID_ARGUMENT.
+ */
+ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const float *initial_state, int chunk_len, int ngroups,
+                                     int batch, int seqlen, int nheads, int headdim,
+                                     int dstate, ssd_dtype io_dtype, void *y,
+                                     float *final_state, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream,
+                                     const int *seq_idx, const ssd_dt_proc *dt_proc);
+
+/*
  * ssd_state_update with dt the raw time step [batch, nheads], processed as
  * *dt_proc says (the `dt_bias` and `dt_softplus` arguments of the layer's
  * `selective_state_update` call).  A NULL dt_proc makes it exactly

@@ -20,6 +20,8 @@ Contents
 ``conv``     the layer's causal depthwise convolution (+ SiLU) and its decode
              update, in fp64.
 ``norm``     the layer's gated RMS normalisation after the scan, in fp64.
+``varlen``   packed variable-length sequences: the serial oracle run on every
+             sequence of a row separately.
 """
 from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
-from . import conv, dt, forms, metrics, norm  # noqa: F401
+from . import conv, dt, forms, metrics, norm, varlen  # noqa: F401

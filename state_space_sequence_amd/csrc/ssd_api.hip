@@ -125,7 +125,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
                         int headdim, int dstate, ssd_dtype io_dtype, void *y,
                         float *final_state, void *workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t *events, int *nkernels,
-                        const char **names, const ssd_dt_proc *dt_proc) {
+                        const char **names, const ssd_dt_proc *dt_proc,
+                        const int *seq_idx = nullptr) {
     ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
@@ -140,6 +141,9 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
         return SSD_ERR_INVALID_ARGUMENT;
     ssd::Path path;
     if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
+    // packed sequences are handled by the fused pass only
+    if (seq_idx && (path != ssd::Path::Fused || !aligned(seq_idx, 4)))
+        return path != ssd::Path::Fused ? SSD_ERR_UNSUPPORTED : SSD_ERR_INVALID_ARGUMENT;
     const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
                                       chunk_len, io_dtype, path);
     if (lay.total > 0 &&
@@ -165,6 +169,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.Q = chunk_len;
     a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
     a.dtp = dtp;
+    a.seq_idx = seq_idx;
     char *ws = static_cast<char *>(workspace);
     const bool split = path == ssd::Path::Split;
     a.acum_hi = split ? reinterpret_cast<float *>(ws + lay.acum_hi) : nullptr;
@@ -254,6 +259,21 @@ ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
                         workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
                         dt_proc);
+}
+
+ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float *A,
+                                     const void *B, const void *C, const float *D,
+                                     const float *initial_state, int chunk_len, int ngroups,
+                                     int batch, int seqlen, int nheads, int headdim,
+                                     int dstate, ssd_dtype io_dtype, void *y,
+                                     float *final_state, void *workspace,
+                                     size_t workspace_bytes, hipStream_t stream,
+                                     const int *seq_idx, const ssd_dt_proc *dt_proc) {
+    if (!seq_idx) return SSD_ERR_INVALID_ARGUMENT;
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch,
+                        seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
+                        workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
+                        dt_proc, seq_idx);
 }
 
 int ssd_chunk_scan_fwd_max_kernels(void) { return ssd::kMaxForwardKernels; }

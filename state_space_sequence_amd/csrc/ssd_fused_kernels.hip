@@ -120,6 +120,19 @@ __device__ __forceinline__ float dpp_f32(float v) {
 __device__ __forceinline__ float lane_f32(float v, int src) {
     return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), src));
 }
+// A compile-time flag passed to generic lambdas.
+template <bool V> struct BoolTag { static constexpr bool value = V; };
+
+// Inclusive running maximum over each half-wave of values >= 0 (the DPP
+// shifts bring in 0 past the row start, the identity for such values).
+__device__ __forceinline__ float scanmax32(float v, int lane) {
+    v = fmaxf(v, dpp_f32<0x111>(v));  // row_shr:1
+    v = fmaxf(v, dpp_f32<0x112>(v));  // row_shr:2
+    v = fmaxf(v, dpp_f32<0x114>(v));  // row_shr:4
+    v = fmaxf(v, dpp_f32<0x118>(v));  // row_shr:8
+    const float r0 = lane_f32(v, 15), r2 = lane_f32(v, 47);
+    return (lane & 16) ? fmaxf(v, lane >= 32 ? r2 : r0) : v;
+}
 __device__ __forceinline__ float scan32(float v, int lane) {
     v += dpp_f32<0x111>(v);  // row_shr:1
     v += dpp_f32<0x112>(v);  // row_shr:2
@@ -179,10 +192,11 @@ struct Fused {
     static constexpr int VR = XR + kBlk * XRB;
     static constexpr int YS = VR + 1024 * NRS;
     static constexpr int DTR = YS + kBlk * XRB;
-    static constexpr int STG = DTR + 256;
+    static constexpr int SEQ = DTR + 256;              // seq_idx of the block (varlen), 2 x 32
+    static constexpr int STG = SEQ + 256;
     // floats of the decay record
     enum { W = 0, F = 32, LR = 64, DT = 96, DELTA = 128, FLAG = 129, LE = 130, SIGIN = 131,
-           SIGOUT = 132, RESC = 133 };
+           SIGOUT = 132, RESC = 133, SEG = 136 };
     // four stages: the DMAs of a block go out three blocks ahead of its
     // use; the former forms a block's decay records two blocks ahead and
     // its C B^T block one block ahead, and the compute waves read its
@@ -203,7 +217,9 @@ struct Fused {
     static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 1;
     static constexpr int P_STORES = kBlk * XRB / 1024;
     static constexpr int P_WAIT = P_STORES + (NST - 3) * (P_LOADS + P_STORES);
-    static_assert(P_WAIT < 64, "vmcnt immediate");
+    // ... with the seq_idx DMA of packed sequences, one more load per block
+    static constexpr int P_WAIT_V = P_STORES + (NST - 3) * (P_LOADS + 1 + P_STORES);
+    static_assert(P_WAIT_V < 64, "vmcnt immediate");
 };
 
 // Column-blocked LDS layout of the staged C, B and x tiles (32 rows): the
@@ -274,7 +290,8 @@ __global__ void __launch_bounds__(Fused<PB>::NT)
 k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
             const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const float *__restrict__ D, const float *init, float *final_state,
-            bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp) {
+            bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp,
+            const int *__restrict__ seq_idx) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
     // Every LDS region that a DMA fills is its own object: the compiler can
@@ -347,6 +364,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void *)dst, 16, voff, soff, 0, kNonTemporal);
         };
         const unsigned pdt = ((lane & 31) * H + h0 + (lane >> 5)) * 4;
+        // packed sequences: seq_idx of this batch, token lane % 32 into both
+        // halves of the stage's SEQ region
+        const bool varlen = seq_idx != nullptr;
+        const __amdgpu_buffer_rsrc_t rseq = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(varlen ? seq_idx + (size_t)b * L : nullptr), 0, varlen ? L * 4 : 0,
+            kBufferWord3);
         // Per-lane offsets.  DMA i fills the 1 KB at 1024 i of a
         // column-blocked tile: column block i / 2, rows 16 (i % 2) + lane / 4,
         // slot lane % 4 (so chunk 4 (i / 2) + ((lane % 4) ^ ((t / 4) % 4)) of
@@ -368,6 +391,9 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         auto pdt_dma = [&](int kb, unsigned char *buf) {
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_void *)(buf + S::DTR), 4, pdt,
                                                      kb * dt_step, 0, 0);
+            if (varlen)
+                __builtin_amdgcn_raw_ptr_buffer_load_lds(rseq, (lds_void *)(buf + S::SEQ), 4,
+                                                         (lane & 31) * 4, kb * kBlk * 4, 0, 0);
         };
         // the DMAs of block kb into `buf`, and the dt of block kb + 1 into
         // `nbuf` (the stage of block kb + 1)
@@ -408,15 +434,40 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         const float pa = A[ph];
         const float pbias = dtp.on && dtp.bias ? dtp.bias[ph] : 0.f;
         float psig = 1.f;  // sigma of this lane's head after the last record formed
-        auto prec = [&](unsigned char *buf, int kblk) {
+        // Packed sequences: token t (> 0, < seqlen) whose seq_idx differs from
+        // token t - 1's starts a new sequence, and the state entering it is 0.
+        // pseq is the seq_idx of the last token of the previous block.
+        int pseq = 0;
+        bool pfirst = true;
+        // VL: the packed-sequence variant (a compile-time tag, so that the
+        // plain one is the code without any of it)
+        auto prec_v = [&](unsigned char *buf, int kblk, auto vl_tag) {
+            constexpr bool VL = decltype(vl_tag)::value;
             const int t = lane & 31, q = lane >> 5;
+            const int tok = kBlk * kblk + t;
             float d = *reinterpret_cast<const float *>(buf + S::DTR + 4 * lane);
-            if (dtp.on)
-                d = kBlk * kblk + t < L ? dt_process(d, pbias, dtp.softplus, dtp.lo, dtp.hi) : 0.f;
+            if (dtp.on) d = tok < L ? dt_process(d, pbias, dtp.softplus, dtp.lo, dtp.hi) : 0.f;
+            // s0 = the last sequence start at or before t in this block (-1:
+            // none), s0e the last one in the block
+            float s0 = -1.f, s0e = -1.f;
+            if constexpr (VL) {
+                const int sq = *reinterpret_cast<const int *>(buf + S::SEQ + 4 * lane);
+                const int up = __builtin_amdgcn_update_dpp(0, sq, 0x138, 0xF, 0xF, false);  // wave_shr:1
+                const int prev = t == 0 ? (pfirst ? sq : pseq) : up;
+                const bool start = tok < L && sq != prev;
+                s0 = scanmax32(start ? (float)(t + 1) : 0.f, lane) - 1.f;
+                s0e = last_of_half(s0, lane);
+                pseq = __builtin_amdgcn_readlane(sq, kBlk - 1);
+                pfirst = false;
+            }
             const float lam = scan32(d * pa, lane);
             const float le = last_of_half(lam, lane);
-            const bool fac = -le <= kSafeDecay;
-            const float delta = fast_exp(le);
+            // a block with a sequence start takes the exact path: the state
+            // entering it does not reach past the start (delta = 0), the
+            // state-in factor applies before it only, and the state leaving
+            // it collects the last sequence only
+            const bool fac = (!VL || s0e < 0.f) && -le <= kSafeDecay;
+            const float delta = (!VL || s0e < 0.f) ? fast_exp(le) : 0.f;
             const float sig_in = psig, p = sig_in * delta;
             const bool resc = fac && p < kRescale;
             const float sig_out = fac ? (resc ? delta : p) : 1.f;
@@ -424,8 +475,17 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             psig = sig_out;
             if (q < S::NRS) {
                 float *rec = reinterpret_cast<float *>(buf + S::VR + 1024 * q);
-                rec[S::W + t] = fast_exp(le - lam) * d * xsc;
-                rec[S::F + t] = fac ? fast_exp(lam - le) * sig_out : 0.f;
+                if constexpr (VL) {
+                    rec[S::W + t] = (float)t >= s0e ? fast_exp(le - lam) * d * xsc : 0.f;
+                    // (exact blocks: the state-in factor exp(lambda_t), before
+                    // the block's first sequence start)
+                    rec[S::F + t] = fast_exp(fac ? lam - le : lam) *
+                                    (fac ? sig_out : (s0 < 0.f ? 1.f : 0.f));
+                    rec[S::SEG + t] = s0;
+                } else {
+                    rec[S::W + t] = fast_exp(le - lam) * d * xsc;
+                    rec[S::F + t] = fac ? fast_exp(lam - le) * sig_out : 0.f;
+                }
                 rec[S::LR + t] = lam - le;
                 rec[S::DT + t] = d;
                 if (t == kBlk - 1) {
@@ -433,6 +493,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                     *reinterpret_cast<f32x2 *>(rec + S::SIGOUT) = f32x2{sig_out, resc ? 1.f : 0.f};
                 }
             }
+        };
+        auto prec = [&](unsigned char *buf, int kblk) {
+            if (varlen)
+                prec_v(buf, kblk, BoolTag<true>{});
+            else
+                prec_v(buf, kblk, BoolTag<false>{});
         };
         // The causal diagonal block of C B^T of the block staged in `buf`,
         // from its C and B rows: E = B C^T on MFMA (A: B row s = lane % 32,
@@ -503,7 +569,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             auto pblock = [&](int kb, const int si) {
                 pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
                 if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
-                __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
+                if (varlen)
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT_V));
+                else
+                    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
                 lds_barrier();
             };
             for (int kb = 0; kb < nblk; kb += S::NST) {
@@ -750,20 +819,26 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             // branch unconditionally with selects)
             __builtin_amdgcn_sched_barrier(0);
             // exact block: weights exp(lambda_l - lambda_s) dt_s on raw x with
-            // D on the diagonal; h~ <- sigma_in delta h~ + B^T x', sigma = 1.
-            // exp(lambda_r) sigma_in (<= 1: the exponent is formed before exp)
+            // D on the diagonal, within token r's sequence (s >= its start);
+            // h~ <- sigma_in delta h~ + B^T x', sigma = 1.  The state-in
+            // factor exp(lambda_r) sigma_in (<= 1: the exponent is formed
+            // before exp); with packed sequences the record holds exp(lambda_r),
+            // 0 past a sequence start.
             const float sig_in = uniform(v[S::SIGIN]);
-            acc *= fast_exp(v[S::LR + r] + v[S::LE]) * sig_in;
+            acc *= (seq_idx ? e.rpv : fast_exp(v[S::LR + r] + v[S::LE])) * sig_in;
             const float lr = v[S::LR + r];
+            // s = 16 kk + 8 hi + j is kept when seg_r <= s <= r: compared as
+            // 16 kk + j against per-lane bounds (immediates in the compares)
+            const int rlo = (seq_idx ? (int)v[S::SEG + r] : -1) - 8 * hi, rhi = r - 8 * hi;
 #pragma unroll
             for (int kk = 0; kk < 2; ++kk) {
                 bf16x8 wgt;
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
-                    const int s = 16 * kk + 8 * hi + j;
+                    const int s = 16 * kk + 8 * hi + j, sj = 16 * kk + j;
                     const float w = (float)o.cbv[kk][j] * fast_exp(fminf(lr - v[S::LR + s], 0.f)) *
-                                        v[S::DT + s] + (s == r ? Dh : 0.f);
-                    wgt[j] = (bf16)(s <= r ? w : 0.f);
+                                        v[S::DT + s] + (sj == rhi ? Dh : 0.f);
+                    wgt[j] = (bf16)(sj <= rhi && sj >= rlo ? w : 0.f);
                 }
                 acc = mma32(e.xs[kk], wgt, acc);
                 // the common diagonal product below then adds zeros
@@ -865,7 +940,7 @@ static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
                        (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C, a.D,
                        a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, fused_nblk(a.L),
-                       a.dtp);
+                       a.dtp, a.seq_idx);
 }
 
 // Columns per workgroup.  One workgroup per compute unit is the target

@@ -35,6 +35,7 @@ struct ForwardArgs {
     float *final_state;  // may be null
     int batch, L, H, G, P, N, Q, nchunks;
     DtProc dtp;      // dt preprocessing (off: dt is used as given)
+    const int *seq_idx = nullptr;  // packed sequences [b][L] (fused path only), or null
     // workspace regions shared by both forward paths
     float *acum_hi;  // [b][H][nc][Q]  fp32 part of the fp64 chunk prefix sums
     float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
@@ -50,9 +51,12 @@ struct ForwardArgs {
 // exp(lambda_l - lambda_e) sigma_out (0 when the block is not factored),
 // [64, 96) lambda_l - lambda_e, [96, 128) dt_l, then delta = exp(lambda_e),
 // the factored flag (1 or 0), lambda_e, sigma_in, sigma_out and the restart
-// flag (sigma the scale of the state, h = sigma h~), 2 floats of padding.
-// 544 bytes, a multiple of 16.
-constexpr int kVecRec = 136;
+// flag (sigma the scale of the state, h = sigma h~), 2 floats of padding,
+// then [136, 168) the start of each token's packed sequence within the block
+// (-1: none).  In a block that takes the exact path, [32, 64) holds the
+// state-in factor exp(lambda_l) instead (0 past a sequence start).  672
+// bytes, a multiple of 16.
+constexpr int kVecRec = 168;
 
 // Forward paths.  The split path runs the five kernels of the chunked
 // algorithm one after the other with the caller's chunk length and accepts

@@ -187,3 +187,18 @@ def make_norm_inputs(rows, dim, io_dtype="bf16", seed=1234):
     elif io_dtype != "f32":
         raise ValueError("io_dtype must be 'f32' or 'bf16'")
     return {"y": np.ascontiguousarray(y), "z": np.ascontiguousarray(z), "weight": w}
+
+
+def make_seq_idx(batch, seqlen, seed=1234, max_len=96):
+    """Packed-sequence labels [batch, seqlen] int32: each row is cut into
+    sequences of lengths drawn uniformly from 1 .. max_len, labelled 0, 1, 2,
+    ... in order."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    out = np.zeros((batch, seqlen), dtype=np.int32)
+    for r in range(batch):
+        t, k = 0, 0
+        while t < seqlen:
+            n = int(rng.integers(1, max_len + 1))
+            out[r, t:t + n] = k
+            t, k = t + n, k + 1
+    return out

@@ -81,6 +81,8 @@ def load():
         lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
         lib.ssd_chunk_scan_fwd_ex.restype = _i
         lib.ssd_chunk_scan_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(DtProc)]
+        lib.ssd_chunk_scan_fwd_varlen.restype = _i
+        lib.ssd_chunk_scan_fwd_varlen.argtypes = _FWD_ARGS + [_p, ctypes.POINTER(DtProc)]
         lib.ssd_state_update_ex.restype = _i
         lib.ssd_state_update_ex.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p, ctypes.POINTER(DtProc)]
         lib.ssd_causal_conv1d_fwd.restype = _i
@@ -158,7 +160,7 @@ def _dt_proc(dt_bias, dt_softplus, dt_limit, H, dev):
 
 
 def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-             final_state, workspace, return_final_state, stream, dtp=None):
+             final_state, workspace, return_final_state, stream, dtp=None, seq_idx=None):
     import torch
     lib = load()
     dev = x.device
@@ -199,7 +201,16 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
             int(chunk_len), G, b, L, H, P, N, io, _ptr(y), _ptr(final_state),
             _ptr(workspace), _sz(workspace.numel()), _stream_handle(stream))
-    if dtp is not None:
+    if seq_idx is not None:
+        if timed_events is not None:
+            raise ValueError("the timed forward takes unpacked rows only")
+        _check_dev("seq_idx", seq_idx, torch.int32, dev)
+        if tuple(seq_idx.shape) != (b, L):
+            raise ValueError("seq_idx must be [b, L] int32")
+        st = lib.ssd_chunk_scan_fwd_varlen(*args, _ptr(seq_idx),
+                                           None if dtp is None else ctypes.byref(dtp))
+        where = "ssd_chunk_scan_fwd_varlen"
+    elif dtp is not None:
         if timed_events is not None:
             raise ValueError("the timed forward takes processed dt only")
         st = lib.ssd_chunk_scan_fwd_ex(*args, ctypes.byref(dtp))
@@ -225,7 +236,7 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256,
                        ngroups=None, y=None, final_state=None, workspace=None,
                        return_final_state=True, stream=None, dt_bias=None,
-                       dt_softplus=False, dt_limit=None):
+                       dt_softplus=False, dt_limit=None, seq_idx=None):
     """Chunked SSD forward on the current (or given) torch stream.
 
     x [b,L,H,P] (fp32|bf16), dt [b,L,H] fp32, A [H] fp32, B/C [b,L,G,N] (x's
@@ -237,10 +248,13 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256
     With dt_bias ([H] fp32), dt_softplus or dt_limit ((min, max)) given, dt
     is the raw time step and the kernels use min(max(f(dt + dt_bias), min),
     max), f = softplus when dt_softplus (the layer's `dt_bias`,
-    `dt_softplus`, `dt_limit` arguments; ssd_chunk_scan_fwd_ex)."""
+    `dt_softplus`, `dt_limit` arguments; ssd_chunk_scan_fwd_ex).
+
+    seq_idx ([b, L] int32) packs several sequences per row: the state is
+    reset where it changes (ssd_chunk_scan_fwd_varlen)."""
     dtp = _dt_proc(dt_bias, dt_softplus, dt_limit, A.shape[0], x.device)
     return _forward(None, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-                    final_state, workspace, return_final_state, stream, dtp)
+                    final_state, workspace, return_final_state, stream, dtp, seq_idx)
 
 
 def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,

@@ -461,3 +461,46 @@ def test_rmsnorm_closed_forms():
                                rtol=1e-14, atol=1e-15)
     np.testing.assert_array_equal(gated_rmsnorm(np.full((1, 8), -3.0), None, np.ones(8), 0.0),
                                   -np.ones((1, 8)))
+
+
+# ------------------------------------------------------ packed sequences
+
+def test_varlen_single_token_sequences_closed_form(oracle_mod):
+    """Every token its own sequence: h_t = dt_t x_t (outer) B_t, so y_t =
+    dt_t (B_t . C_t) x_t + D x_t, except token 0, which also sees the decayed
+    initial state."""
+    from oracle.varlen import forward_varlen
+    inp = _rand(b=2, L=9, H=2, P=3, N=4, G=1, seed=31)
+    seq = np.tile(np.arange(9, dtype=np.int32), (2, 1))
+    y, fin = forward_varlen(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], inp["D"],
+                            inp["initial_state"], seq)
+    x, dt, Bm, Cm, D, A = (inp[k].astype(np.float64) for k in ("x", "dt", "B", "C", "D", "A"))
+    bc = np.einsum("bln,bln->bl", Bm[:, :, 0], Cm[:, :, 0])
+    expect = dt[..., None] * bc[:, :, None, None] * x + D[None, None, :, None] * x
+    init = inp["initial_state"].astype(np.float64)
+    expect[:, 0] += np.exp(dt[:, 0, :, None] * A[None, :, None]) * np.einsum(
+        "bhpn,bn->bhp", init, Cm[:, 0, 0])
+    np.testing.assert_allclose(y, expect, rtol=1e-12, atol=1e-13)
+    last = dt[:, -1, :, None, None] * x[:, -1, :, :, None] * Bm[:, -1, 0][:, None, None, :]
+    np.testing.assert_allclose(fin, last, rtol=1e-12, atol=1e-14)
+
+
+def test_varlen_sequences_do_not_interact(oracle_mod):
+    """Changing the inputs of one packed sequence leaves the outputs of the
+    others unchanged; one label for the whole row is the plain forward."""
+    from oracle.varlen import forward_varlen
+    inp = _rand(b=1, L=40, H=2, P=3, N=4, G=1, seed=32)
+    seq = np.array([[0] * 13 + [1] * 20 + [2] * 7], dtype=np.int32)
+    args = [inp[k] for k in ("x", "dt", "A", "B", "C", "D", "initial_state")]
+    y, fin = forward_varlen(*args, seq)
+    x2 = inp["x"].copy()
+    x2[:, 13:33] *= -3.0
+    y2, fin2 = forward_varlen(x2, *args[1:], seq)
+    np.testing.assert_array_equal(y2[:, :13], y[:, :13])
+    np.testing.assert_array_equal(y2[:, 33:], y[:, 33:])
+    np.testing.assert_array_equal(fin2, fin)
+    assert not np.allclose(y2[:, 13:33], y[:, 13:33])
+    yp, finp = forward_varlen(*args, np.zeros((1, 40), dtype=np.int32))
+    yr, finr = oracle_mod.forward(*args)
+    np.testing.assert_array_equal(yp, yr)
+    np.testing.assert_array_equal(finp, finr)

@@ -538,3 +538,88 @@ def test_gated_rmsnorm_in_place(dev):
     torch.cuda.synchronize()
     check(y.float().cpu().numpy(), gated_rmsnorm(inp["y"], inp["z"], inp["weight"]), "bf16",
           "norm in place")
+
+
+# ------------------------------------------------------ packed sequences
+
+# (b, L, H, P, G, max sequence length, initial state, dt preprocessing);
+# the head counts select the fused pass's three layouts (32, 64 and
+# 128-column workgroups)
+VARLEN = [
+    (2, 300, 4, 64, 1, 96, True, False),
+    (2, 333, 4, 64, 2, 8, True, False),        # several sequence starts per block
+    (2, 200, 132, 64, 2, 70, True, False),     # four-wave workgroups, two heads each
+    (2, 300, 66, 64, 1, 40, False, False),     # two-wave workgroups
+    (1, 257, 4, 64, 1, 96, True, True),        # with the time-step preprocessing
+]
+
+
+def _varlen_check(oracle_mod, dev, inp, seq, dtp=False):
+    import torch
+    from oracle.dt import process_dt
+    from oracle.varlen import forward_varlen
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    t = to_torch(inp, "bf16", dev)
+    ts = torch.from_numpy(seq).to(dev)
+    if dtp:
+        y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt_raw"], t["A"], t["B"], t["C"], t["D"],
+                                           t["initial_state"], chunk_len=64, seq_idx=ts,
+                                           dt_bias=t["dt_bias"], dt_softplus=True)
+        dt_used = process_dt(inp["dt_raw"], inp["dt_bias"], True)
+    else:
+        y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                           t["initial_state"], chunk_len=64, seq_idx=ts)
+        dt_used = inp["dt"]
+    torch.cuda.synchronize()
+    yr, fr = forward_varlen(inp["x"], dt_used, inp["A"], inp["B"], inp["C"], inp["D"],
+                            inp["initial_state"], seq)
+    check(y.float().cpu().numpy(), yr, "bf16", "varlen y")
+    check(fin.cpu().numpy(), fr, "bf16", "varlen final")
+    # and every packed sequence on its own (a short one must not drown in the
+    # norm of the others)
+    from oracle.varlen import segments
+    yg = y.float().cpu().numpy()
+    for r in range(seq.shape[0]):
+        for s0, s1 in segments(seq[r]):
+            assert metrics.normwise_err(yg[r, s0:s1], yr[r, s0:s1]) <= metrics.BF16_NORMWISE, (r, s0)
+
+
+@pytest.mark.parametrize("case", VARLEN, ids=lambda c: "b%d_L%d_H%d_P%d_G%d_max%d" % c[:6]
+                         + ("_init" if c[6] else "") + ("_dtproc" if c[7] else ""))
+def test_varlen_packed_sequences(dev, oracle_mod, case):
+    from state_space_sequence_amd.inputs import make_seq_idx
+    b, L, H, P, G, mx, init, dtp = case
+    _say("varlen case %s" % (case,))
+    inp = make_inputs(b, L, H, P, 128, G, io_dtype="bf16", init_std=0.1 if init else 0.0,
+                      seed=700 + L + H)
+    skip_if_path_unsupported(inp, "bf16", 64)
+    seq = make_seq_idx(b, L, seed=800 + L, max_len=mx)
+    _varlen_check(oracle_mod, dev, inp, seq, dtp)
+
+
+def test_varlen_placed_boundaries(dev, oracle_mod):
+    """Sequence starts at block starts (32, 64), a run of one-token sequences
+    (100, 101, 102), at the last token, and none in the first block's tail."""
+    L = 230
+    inp = make_inputs(2, L, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=61)
+    seq = np.zeros((2, L), dtype=np.int32)
+    for k, start in enumerate([32, 33, 64, 100, 101, 102, L - 1]):
+        seq[:, start:] = k + 1
+    seq[1, :] = np.minimum(seq[1], 3)      # row 1: starts at 32, 33 and 64 only
+    _varlen_check(oracle_mod, dev, inp, seq)
+
+
+def test_varlen_unsupported_paths(dev, monkeypatch):
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    seq = torch.zeros((1, 100), dtype=torch.int32, device=dev)
+    for io, path in (("f32", None), ("bf16", "split")):
+        if path:
+            monkeypatch.setenv("SSD_FORWARD_PATH", path)
+        inp = make_inputs(1, 100, 2, 64, 128, 1, io_dtype=io, seed=3)
+        t = to_torch(inp, io, dev)
+        with pytest.raises(libssd.SsdError) as ei:
+            libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], seq_idx=seq)
+        assert ei.value.status == libssd.SSD_ERR_UNSUPPORTED
