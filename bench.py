@@ -12,7 +12,8 @@ Also reported (not part of ``value``):
     call against algorithmic bytes (x, B, C, dt, A, D read once; y and the
     final state written once; no intermediates);
   * the other forward workloads, and the headline forward again on the raw
-    time step with the preprocessing (bias, softplus) inside the kernels;
+    time step with the preprocessing (bias, softplus) inside the kernels, and
+    with packed variable-length sequences;
   * the decode state update on the b256 / 80-head workload;
   * the causal depthwise conv before the scan on the same layer's channels,
     and its single-token update at batch 256;
@@ -199,6 +200,35 @@ def time_forward(w, dev, steps, warmup, ev):
     del t, y, fin, ws
     return dict(host_s=h1 - h0, gpu_ms=total_ms, per_kernel_ms=per_kernel,
                 names=names, inputs=inp)
+
+
+def time_forward_varlen(w, dev, ev, steps=100, warmup=50, max_len=2048):
+    """ms per forward with each row packed with sequences of lengths drawn
+    from 1 .. max_len (ssd_chunk_scan_fwd_varlen)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_seq_idx
+    inp, t, y, fin, ws = setup(w, dev)
+    seq = make_seq_idx(w.batch, w.seqlen, seed=w.seed, max_len=max_len)
+    nseq = int(sum(len(set(r.tolist())) for r in seq))
+    ts = torch.from_numpy(seq).to(dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    kw = dict(chunk_len=w.chunk_len, y=y, final_state=fin, workspace=ws, seq_idx=ts)
+    for _ in range(warmup):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+    sh = torch.cuda.current_stream().cuda_stream
+    e0, e1 = ev.create(), ev.create()
+    torch.cuda.synchronize()
+    ev.record(e0, sh)
+    for _ in range(steps):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+    ev.record(e1, sh)
+    torch.cuda.synchronize()
+    ms = ev.ms(e0, e1) / steps
+    ev.destroy(e0)
+    ev.destroy(e1)
+    del t, y, fin, ws
+    return ms, nseq
 
 
 def time_forward_dt_proc(w, dev, ev, steps=100, warmup=50):
@@ -567,6 +597,12 @@ def main():
             "what": "the same forward on the raw time step: softplus(dt + dt_bias) in the kernels",
             "ms_per_step": round(msd, 4),
             "tokens_per_s": round(w.batch * w.seqlen / (msd * 1e-3), 1)}
+        msv, nseq = time_forward_varlen(w, dev, ev)
+        extra[w.name + "_varlen"] = {
+            "what": "the same forward with %d packed sequences (lengths 1..2048) in its %d rows"
+                    % (nseq, w.batch),
+            "ms_per_step": round(msv, 4),
+            "tokens_per_s": round(w.batch * w.seqlen / (msv * 1e-3), 1)}
         extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
         extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(w, dev, ev)
         extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev)
