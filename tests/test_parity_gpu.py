@@ -623,3 +623,79 @@ def test_varlen_unsupported_paths(dev, monkeypatch):
         with pytest.raises(libssd.SsdError) as ei:
             libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], seq_idx=seq)
         assert ei.value.status == libssd.SSD_ERR_UNSUPPORTED
+
+
+# ------------------------------------------ full-size checks of the layer steps
+
+def test_causal_conv1d_full_size_sampled(dev):
+    """The conv at the size bench.py times (the 2.7B layer's 5376 x | B | C
+    channels, b4 L8192, width 4, SiLU), checked on sampled channels over
+    every token, and the cache of all channels."""
+    import torch
+    from oracle.conv import causal_conv1d, conv_state_after
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs
+    w = WORKLOADS["mamba2_2p7b"]
+    D = w.nheads * w.headdim + 2 * w.ngroups * w.dstate
+    inp = make_conv_inputs(w.batch, w.seqlen, D, 4, io_dtype="bf16", seed=w.seed)
+    x = torch.from_numpy(inp["x"]).to(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(inp["weight"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev)
+    out, state = libssd.ssd_causal_conv1d_fwd(x, wt, bias, "silu")
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(5)
+    ch = np.unique(np.concatenate([[0, 7, 8, D - 8, D - 1], rng.integers(0, D, 59)]))
+    ref = causal_conv1d(inp["x"][:, :, ch], inp["weight"][ch], inp["bias"][ch], "silu")
+    got = out[:, :, torch.from_numpy(ch).to(dev)].float().cpu().numpy()
+    check(got, ref, "bf16", "conv full size (sampled channels)")
+    np.testing.assert_array_equal(state.float().cpu().numpy(), conv_state_after(inp["x"], 4))
+
+
+def test_gated_rmsnorm_full_size_sampled(dev):
+    """The gated norm at the size bench.py times (32768 rows x 5120), on
+    sampled rows."""
+    import torch
+    from oracle.norm import gated_rmsnorm
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_norm_inputs
+    w = WORKLOADS["mamba2_2p7b"]
+    rows, dim = w.batch * w.seqlen, w.nheads * w.headdim
+    inp = make_norm_inputs(rows, dim, io_dtype="bf16", seed=w.seed)
+    y = torch.from_numpy(inp["y"]).to(torch.bfloat16).to(dev)
+    z = torch.from_numpy(inp["z"]).to(torch.bfloat16).to(dev)
+    wt = torch.from_numpy(inp["weight"]).to(dev)
+    out = libssd.ssd_gated_rmsnorm_fwd(y, z, wt)
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(6)
+    rs = np.unique(np.concatenate([[0, rows - 1], rng.integers(0, rows, 254)]))
+    ref = gated_rmsnorm(inp["y"][rs], inp["z"][rs], inp["weight"])
+    got = out[torch.from_numpy(rs).to(dev)].float().cpu().numpy()
+    check(got, ref, "bf16", "norm full size (sampled rows)")
+    for i in range(len(rs)):
+        assert metrics.normwise_err(got[i], ref[i]) <= metrics.BF16_NORMWISE, rs[i]
+
+
+def test_varlen_full_size_sampled(dev, oracle_mod):
+    """The 2.7B-shape forward with packed sequences as bench.py times it,
+    checked on sampled heads of every row against the per-sequence oracle."""
+    import torch
+    from oracle.varlen import forward_varlen
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_seq_idx, to_torch
+    w = WORKLOADS["mamba2_2p7b"]
+    inp = workload_inputs(w)
+    seq = make_seq_idx(w.batch, w.seqlen, seed=w.seed, max_len=2048)
+    t = to_torch(inp, w.io_dtype, dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                       t["initial_state"], chunk_len=w.chunk_len,
+                                       seq_idx=torch.from_numpy(seq).to(dev))
+    torch.cuda.synchronize()
+    heads = [0, 37, w.nheads - 1]
+    sub = {k: (v[:, :, heads] if k in ("x", "dt") else v) for k, v in inp.items()
+           if k in ("x", "dt", "B", "C")}
+    yr, fr = forward_varlen(sub["x"], sub["dt"], inp["A"][heads], sub["B"], sub["C"],
+                            inp["D"][heads], None if inp["initial_state"] is None
+                            else inp["initial_state"][:, heads], seq)
+    gy = y[:, :, heads].float().cpu().numpy()
+    check(gy, yr, "bf16", "varlen full size (sampled heads)")
+    check(fin[:, heads].cpu().numpy(), fr, "bf16", "varlen final (sampled heads)")
