@@ -192,6 +192,10 @@ def time_forward(w, dev, steps, warmup, ev):
     nk = len(names)
     per_kernel = [sum(ev.ms(events[k][i], events[k][i + 1]) for k in range(steps)) / steps
                   for i in range(nk)]
+    # the spread of one forward's time over the event-bracketed steps
+    step_ms = sorted(ev.ms(events[k][0], events[k][nk]) for k in range(steps))
+    dist = {q: step_ms[min(len(step_ms) - 1, int(round(f * (len(step_ms) - 1))))]
+            for q, f in (("p10", 0.1), ("p50", 0.5), ("p90", 0.9))}
     for row in events:
         for e in row:
             ev.destroy(e)
@@ -199,7 +203,7 @@ def time_forward(w, dev, steps, warmup, ev):
     ev.destroy(e1)
     del t, y, fin, ws
     return dict(host_s=h1 - h0, gpu_ms=total_ms, per_kernel_ms=per_kernel,
-                names=names, inputs=inp)
+                names=names, inputs=inp, step_dist_ms=dist)
 
 
 def time_forward_varlen(w, dev, ev, steps=100, warmup=50, max_len=2048):
@@ -576,6 +580,7 @@ def main():
                           "roofline_us": round(max(abytes / (HBM_PEAK_GBS * 1e9),
                                                    flops / (BF16_PEAK_TFLOPS * 1e12)) * 1e6, 2)},
         "per_kernel_ms": {k: round(v, 4) for k, v in per.items()},
+        "step_ms_dist": {k: round(v, 4) for k, v in r["step_dist_ms"].items()},
         "host_wall_s": round(r["host_s"], 4),
     }
     if not args.no_extra:
