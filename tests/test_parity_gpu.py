@@ -494,12 +494,13 @@ def test_causal_conv1d_prefill_then_decode(dev, io):
 
 # (rows, dim, io, gate: "before" | "after" | None)
 NORM = [
-    (300, 512, "bf16", "before"),      # the layer's order, one vector per lane
-    (37, 5120, "bf16", "before"),      # the 2.7B layer's row (10 vectors per lane)
-    (64, 1536, "f32", "before"),       # the 130M layer's row
-    (5, 8192, "f32", "after"),         # the largest row
-    (9, 40, "bf16", None),             # a row shorter than a wave's vector
-    (130, 2056, "f32", None),          # a ragged last vector group
+    # (8-value vectors per row -> threads x vectors per thread)
+    (300, 512, "bf16", "before"),      # the layer's order; 64 -> 64 x 1
+    (37, 5120, "bf16", "before"),      # the 2.7B layer's row; 640 -> 320 x 2
+    (64, 1536, "f32", "before"),       # the 130M layer's row; 192 -> 192 x 1
+    (5, 8192, "f32", "after"),         # the largest row; 1024 -> 512 x 2
+    (9, 40, "bf16", None),             # shorter than a wave; 5 -> 64 x 1
+    (130, 2056, "f32", None),          # 257 -> 192 x 2, the second partly clamped
 ]
 
 
