@@ -12,8 +12,8 @@
 // and with it after (norm_before_gate): out = y / sqrt(mean(y^2) + eps) * w *
 // silu(z).  Without a gate it is the plain RMS normalisation.
 //
-// One workgroup per row, of as many whole waves as the row's 16-byte vectors
-// need at one vector per thread (rows of up to 256 vectors) or two: thread i
+// One workgroup per row, of as many whole waves as the row's 8-value vectors
+// (16 bytes in bf16) need at one vector per thread (rows of up to 256 vectors) or two: thread i
 // holds vectors i and i + nt of the row (8 values each) in registers, the sum
 // of squares is reduced within each wave and then across the waves through
 // LDS, and the row is scaled and stored.  (At 5120 values, 320 threads with
@@ -59,7 +59,7 @@ __device__ __forceinline__ float nsilu(float v) {
 
 }  // namespace
 
-// grid (rows), nt threads (a multiple of 64, at most 512) with NV 16-byte
+// grid (rows), nt threads (a multiple of 64, at most 512) with NV 8-value
 // vectors per thread covering the row: 8 NV nt >= dim; dim % 8 == 0.  GATE: 0
 // none, 1 gate before the normalisation, 2 after it.
 template <typename T, int NV, int GATE>
@@ -112,7 +112,7 @@ k_gated_rmsnorm(const T *__restrict__ y, const T *__restrict__ z, const float *_
 
 template <typename T>
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream) {
-    // 16-byte vectors of a row, per thread (1 up to 256 of them, else 2), and
+    // 8-value vectors of a row, per thread (1 up to 256 of them, else 2), and
     // the threads: whole waves, at most 512 (dim <= kMaxNormDim = 8192)
     const int vecs = a.dim / 8, nv = vecs <= 256 ? 1 : 2;
     const int nt = ((vecs + nv - 1) / nv + 63) / 64 * 64;
