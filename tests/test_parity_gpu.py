@@ -490,6 +490,51 @@ def test_causal_conv1d_prefill_then_decode(dev, io):
     check(got, ref[:, L:], io, "decode out", mag[:, L:])
 
 
+# (batch, dim, width, io, bias, activation, misalign): misalign shifts x and
+# the cache by one element off their 16-byte alignment
+CONV_UPD = [
+    (256, 5376, 4, "bf16", True, "silu", False),  # the 2.7B layer's channels, b256
+    (3, 264, 4, "f32", True, "silu", False),      # four channels per thread, fp32
+    (1, 1032, 4, "f32", False, None, False),      # 258 threads: a partial second workgroup
+    (2, 8, 4, "bf16", True, "silu", False),       # the smallest dim: two threads
+    (2, 40, 3, "f32", False, None, False),        # width 3
+    (5, 1032, 2, "bf16", True, "silu", False),    # width 2, a partial last workgroup
+    (2, 264, 4, "bf16", True, "silu", True),      # misaligned x and cache: one channel per thread
+]
+
+
+@pytest.mark.parametrize("case", CONV_UPD, ids=lambda c: "b%d_dim%d_w%d_%s_%s_%s_%s" % c)
+def test_causal_conv1d_update_every_element(dev, case):
+    """One decode token of the conv from a full cache: out and the rolled
+    cache against the oracle's update (the cache bit for bit: it holds
+    inputs)."""
+    import torch
+    from oracle.conv import conv_state_after, conv_update
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs
+    b, D, W, io, use_bias, act, mis = case
+    _say("conv update case %s" % (case,))
+    inp = make_conv_inputs(b, W, D, W, io_dtype=io, seed=700 + D + W, decode_steps=1)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    st0 = conv_state_after(inp["x"], W)           # [b, D, W], every slot filled
+    x1 = inp["x_dec"][0]
+    off = 1 if mis else 0
+
+    def place(a):
+        flat = torch.zeros(a.size + off, dtype=tdt, device=dev)
+        flat[off:] = torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32).ravel()).to(tdt).to(dev)
+        return flat[off:].view(*a.shape)
+    state = place(st0)
+    xs = place(x1)
+    w = torch.from_numpy(inp["weight"]).to(dev)
+    bias = torch.from_numpy(inp["bias"]).to(dev) if use_bias else None
+    out = libssd.ssd_causal_conv1d_update(state, xs, w, bias, activation=act)
+    torch.cuda.synchronize()
+    ref, ref_state = conv_update(st0, x1, inp["weight"], inp["bias"] if use_bias else None, act)
+    assert np.array_equal(state.float().cpu().numpy(), ref_state.astype(np.float32))
+    check(out.float().cpu().numpy(), ref, io, "update out", np.abs(ref))
+
+
 # ------------------------------------------------------ gated RMS normalisation
 
 # (rows, dim, io, gate: "before" | "after" | None)
