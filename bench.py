@@ -99,7 +99,13 @@ def alg_bytes_forward(w, es):
 
 
 def alg_flops_forward(w):
-    """Chunked-SSD flops with causal triangles counted once."""
+    """Flops of the chunked SSD forward (the pages' four steps), with each
+    causal triangle counted once: the C B^T blocks (Q(Q+1)/2 entries of N
+    products per chunk and group), the chunk states (P Q N per chunk and
+    head), the output (the off-diagonal P Q N and the diagonal Q(Q+1)/2 P per
+    chunk and head) and the passing of the states (P N per chunk and head),
+    two flops per multiply-add.  The serial recurrence's 4 P N per token and
+    head, and the dense L x L quadratic form, are not counted."""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     nc = -(-L // Q)
     cb = 2 * (Q * (Q + 1) // 2) * N * b * nc * G
