@@ -745,3 +745,28 @@ def test_varlen_full_size_sampled(dev, oracle_mod):
     gy = y[:, :, heads].float().cpu().numpy()
     check(gy, yr, "bf16", "varlen full size (sampled heads)")
     check(fin[:, heads].cpu().numpy(), fr, "bf16", "varlen final (sampled heads)")
+
+
+def test_dt_preprocessing_full_size_sampled(dev, oracle_mod):
+    """The 2.7B-shape forward on the raw time step (softplus(dt + dt_bias) in
+    the kernels) as bench.py times it, checked on sampled heads of every row
+    against the oracle run on the processed time step."""
+    import torch
+    from oracle.dt import process_dt
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    w = WORKLOADS["mamba2_2p7b"]
+    inp = workload_inputs(w)
+    t = to_torch(inp, w.io_dtype, dev)
+    _say("dt preprocessing full size %s" % w.name)
+    y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt_raw"], t["A"], t["B"], t["C"], t["D"],
+                                       t["initial_state"], chunk_len=w.chunk_len,
+                                       dt_bias=t["dt_bias"], dt_softplus=True)
+    torch.cuda.synchronize()
+    heads = [1, 40, w.nheads - 2]
+    dt_used = process_dt(inp["dt_raw"][:, :, heads], inp["dt_bias"][heads], True)
+    init = None if inp["initial_state"] is None else inp["initial_state"][:, heads]
+    yr, fr = oracle_mod.forward(np.ascontiguousarray(inp["x"][:, :, heads]), dt_used,
+                                inp["A"][heads], inp["B"], inp["C"], inp["D"][heads], init)
+    check(y[:, :, heads].float().cpu().numpy(), yr, "bf16", "dt_proc full size (sampled heads)")
+    check(fin[:, heads].cpu().numpy(), fr, "bf16", "dt_proc final (sampled heads)")
