@@ -770,3 +770,56 @@ def test_dt_preprocessing_full_size_sampled(dev, oracle_mod):
                                 inp["A"][heads], inp["B"], inp["C"], inp["D"][heads], init)
     check(y[:, :, heads].float().cpu().numpy(), yr, "bf16", "dt_proc full size (sampled heads)")
     check(fin[:, heads].cpu().numpy(), fr, "bf16", "dt_proc final (sampled heads)")
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_forward_and_decode_replay_in_a_graph(dev, io):
+    """The library allocates nothing and sets no memory from the host, so a
+    forward and a decode step can be captured in one HIP graph.  Each replay
+    (after eager resets and synchronisations) equals the eager calls bit for
+    bit.  bf16 runs the fused kernel, fp32 the split kernels."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    b, L, H, P, N, G, Q = 2, 1000, 8, 64, 128, 2, 256
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=31)
+    t = to_torch(inp, io, dev)
+    code = libssd.SSD_BF16 if io == "bf16" else libssd.SSD_F32
+    y = torch.empty_like(t["x"])
+    fin = torch.empty((b, H, P, N), dtype=torch.float32, device=dev)
+    ws = torch.empty(max(libssd.ssd_chunk_scan_fwd_workspace_size(b, L, H, P, N, G, Q, code), 1),
+                     dtype=torch.uint8, device=dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    kw = dict(chunk_len=Q, y=y, final_state=fin, workspace=ws)
+    xd, dtd = t["x"][:, 0].contiguous(), t["dt"][:, 0].contiguous()
+    Bd, Cd = t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous()
+    yd = torch.empty_like(xd)
+    _say("graph replay case %s" % io)
+    libssd.ssd_chunk_scan_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    y_ref, fin_ref = y.clone(), fin.clone()
+    state0 = fin_ref.clone()
+    state = state0.clone()
+    libssd.ssd_state_update(state, xd, dtd, t["A"], Bd, Cd, t["D"], y=yd)
+    torch.cuda.synchronize()
+    yd_ref, st_ref = yd.clone(), state.clone()
+
+    state.copy_(state0)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        libssd.ssd_chunk_scan_fwd(*args, **kw)
+        libssd.ssd_state_update(state, xd, dtd, t["A"], Bd, Cd, t["D"], y=yd)
+    for rep in range(3):
+        y.zero_()
+        fin.zero_()
+        yd.zero_()
+        state.copy_(state0)
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), rep
+        assert torch.equal(fin, fin_ref), rep
+        assert torch.equal(yd, yd_ref), rep
+        assert torch.equal(state, st_ref), rep
+    del graph
