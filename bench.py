@@ -537,7 +537,7 @@ def main():
                          "kernel the FETCH_SIZE / WRITE_SIZE counters are scaled by")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU only: this build has no multi-GPU path "
+        print("bench.py measures one GPU only: libssd has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
