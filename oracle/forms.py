@@ -5,6 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 Three ways of computing the same (y, final_state), all in float64:
 
 ``serial_numpy``  the per-token recurrence again, in NumPy instead of C.
+``serial_fp32``   the same loop with every operation rounded to float32: what
+                  plain fp32 arithmetic scores under an error measure.
 ``quadratic``     the quadratic "attention" form of the semiseparable matrix
                   (burn-mamba ``Mamba2SsdInput`` rustdoc, Step 1 applied with
                   one chunk covering the whole sequence), with every decay a
@@ -12,11 +14,10 @@ Three ways of computing the same (y, final_state), all in float64:
                   initial-state term written out explicitly.
 ``chunked``       the four-step chunked algorithm of the same rustdoc (Step 1
                   intra-chunk outputs, Step 2 chunk states (Eq. 20), Step 3
-                  inter-chunk state passing (Eq. 22) done as one matrix product
-                  with the segment-sum decay over chunks, Step 4 state-to-output
-                  (Eq. 23), plus the D skip term), in the order and with the
-                  zero padding of the naive branch of fla ``Mamba2.torch_forward``
-                  and its ``segment_sum`` helper.
+                  inter-chunk state passing (Eq. 22), Step 4 state-to-output
+                  (Eq. 23), plus the D skip term), chunk after chunk, with each
+                  decay a product of per-token factors and the passing a
+                  sequential loop over the chunks.
 
 Shapes: x [b,L,H,P], dt [b,L,H] (already positive, i.e. after softplus),
 A [H], B/C [b,L,G,N], D [H] or None, initial_state [b,H,P,N] or None.
@@ -59,6 +60,33 @@ def serial_numpy(x, dt, A, B, C, D=None, initial_state=None):
         u = dt[:, t, :, None] * x[:, t]                             # [b,H,P]
         S = alpha[:, :, None, None] * S + u[:, :, :, None] * Bh[:, t, :, None, :]
         y[:, t] = np.einsum("bhpn,bhn->bhp", S, Ch[:, t]) + D[None, :, None] * x[:, t]
+    return y, S
+
+
+def serial_fp32(x, dt, A, B, C, D=None, initial_state=None):
+    """The textbook evaluation of the recurrence in fp32: every operation of
+    ``serial_numpy`` rounded to float32 (numpy float32 arithmetic), token by
+    token.  Not a reference: it shows what plain fp32 arithmetic scores under
+    an error measure, which sets the fp32 bars of the parity tests."""
+    f = np.float32
+    x = np.asarray(x, dtype=f)
+    dt = np.asarray(dt, dtype=f)
+    A = np.asarray(A, dtype=f)
+    b, L, H, P = x.shape
+    G = np.asarray(B).shape[2]
+    Bh = np.repeat(np.asarray(B, dtype=f), H // G, axis=2)
+    Ch = np.repeat(np.asarray(C, dtype=f), H // G, axis=2)
+    D = np.zeros(H, dtype=f) if D is None else np.asarray(D, dtype=f)
+    N = Bh.shape[3]
+    S = np.zeros((b, H, P, N), dtype=f) if initial_state is None else \
+        np.array(initial_state, dtype=f)
+    y = np.empty_like(x)
+    for t in range(L):
+        al = np.exp(dt[:, t] * A[None, :]).astype(f)
+        S = (al[:, :, None, None] * S + (dt[:, t, :, None] * x[:, t])[..., None]
+             * Bh[:, t, :, None, :]).astype(f)
+        y[:, t] = (np.einsum("bhpn,bhn->bhp", S, Ch[:, t]).astype(f)
+                   + D[None, :, None] * x[:, t]).astype(f)
     return y, S
 
 
@@ -120,63 +148,62 @@ def quadratic(x, dt, A, B, C, D=None, initial_state=None):
     return y, final
 
 
-def segment_sum(a):
-    """Stable segment sum over the last axis, as fla's ``segment_sum``:
-    out[..., i, j] = sum_{k=j+1..i} a[..., k] for i >= j, -inf above the
-    diagonal.  Built with a masked cumulative sum, never by subtracting two
-    cumulative sums."""
-    T = a.shape[-1]
-    rep = np.repeat(a[..., None], T, axis=-1)          # rep[..., k, j] = a[..., k]
-    strict = np.tril(np.ones((T, T), dtype=bool), k=-1)  # k > j
-    rep = np.where(strict, rep, 0.0)
-    seg = np.cumsum(rep, axis=-2)
-    incl = np.tril(np.ones((T, T), dtype=bool), k=0)
-    return np.where(incl, seg, -np.inf)
-
-
 def chunked(x, dt, A, B, C, D=None, initial_state=None, chunk_len=64):
-    """Four-step chunked SSD in float64 (zero-padded to a multiple of chunk_len)."""
-    x, dt, A, Bh, Ch, D, S0 = _prep(x, dt, A, B, C, D, initial_state)
+    """The four steps of the burn-mamba ``Mamba2SsdInput`` rustdoc, one chunk
+    after the other, in float64.
+
+    The sequence is cut into chunks of ``chunk_len`` tokens; a ragged last
+    chunk is simply shorter (the zero padding of the rustdoc's layout adds
+    nothing to any sum).  With alpha_k = exp(dt_k A) and h the state entering
+    chunk [c0, c1), for tokens c0 <= s <= t < c1:
+
+      decay(t, s) = alpha_{s+1} * ... * alpha_t          (1 when s = t)
+      Step 1, intra-chunk output (L o C B^T) X:
+          y_t  = sum_{s <= t} (C_t . B_s) decay(t, s) dt_s x_s
+      Step 4, state to output (Eq. 23):
+          y_t += (alpha_{c0} * ... * alpha_t) (h C_t)
+      Step 2, the chunk's own state (Eq. 20):
+          S    = sum_s decay(c1 - 1, s) dt_s x_s (outer) B_s
+      Step 3, state passing (Eq. 22):
+          h   <- (alpha_{c0} * ... * alpha_{c1-1}) h + S
+
+    plus D x_t.  Every decay is a product accumulated one factor at a time,
+    and the passing is a sequential loop over chunks, so this shares neither
+    the per-token loop of the serial oracle nor the cumulative sums of the
+    fused kernel."""
+    x, dt, A, Bh, Ch, D, h = _prep(x, dt, A, B, C, D, initial_state)
     b, L, H, P = x.shape
-    N = Bh.shape[3]
     Q = int(chunk_len)
-    pad = (Q - L % Q) % Q
-    nc = (L + pad) // Q
-
-    def padL(t):
-        widths = [(0, 0)] * t.ndim
-        widths[1] = (0, pad)
-        return np.pad(t, widths)
-
-    D_res = D[None, None, :, None] * padL(x)
-    xdt = padL(x * dt[..., None])                                   # dt-weighted input
-    a = padL(dt * A[None, None, :])                                  # [b,Lp,H]
-    Bc = padL(Bh).reshape(b, nc, Q, H, N)
-    Cc = padL(Ch).reshape(b, nc, Q, H, N)
-    Xc = xdt.reshape(b, nc, Q, H, P)
-    ac = a.reshape(b, nc, Q, H).transpose(0, 3, 1, 2)                # [b,H,c,Q]
-    acum = np.cumsum(ac, axis=-1)
-
-    # Step 1: intra-chunk outputs with zero incoming state.
-    Lmask = np.exp(segment_sum(ac))                                  # [b,H,c,Q,Q]
-    G = np.einsum("bclhn,bcshn->bclsh", Cc, Bc)
-    Mm = G * Lmask.transpose(0, 2, 3, 4, 1)
-    Y_diag = np.einsum("bclsh,bcshp->bclhp", Mm, Xc)
-
-    # Step 2: state of every chunk from its own tokens only (Eq. 20).
-    decay_states = np.exp(acum[..., -1:] - acum)                     # [b,H,c,Q]
-    states = np.einsum("bclhn,bhcl,bclhp->bchpn", Bc, decay_states, Xc)
-
-    # Step 3: inter-chunk recurrence (Eq. 22) as one product with the
-    # segment-sum decay over chunk boundaries.
-    states = np.concatenate([S0[:, None], states], axis=1)           # [b,c+1,H,P,N]
-    chunk_ends = np.pad(acum[..., -1], [(0, 0), (0, 0), (1, 0)])     # [b,H,c+1]
-    decay_chunk = np.exp(segment_sum(chunk_ends))                    # [b,H,c+1,c+1]
-    new_states = np.einsum("bhzc,bchpn->bzhpn", decay_chunk, states)
-    h_in, final = new_states[:, :-1], new_states[:, -1]
-
-    # Step 4: contribution of each chunk's incoming state (Eq. 23).
-    Y_off = np.einsum("bclhn,bchpn,bhcl->bclhp", Cc, h_in, np.exp(acum))
-
-    y = (Y_diag + Y_off).reshape(b, nc * Q, H, P) + D_res
-    return y[:, :L], final
+    y = np.empty_like(x)
+    h = h.copy()
+    for c0 in range(0, L, Q):
+        c1 = min(c0 + Q, L)
+        n = c1 - c0
+        alpha = np.exp(dt[:, c0:c1] * A[None, None, :])            # [b,n,H]
+        # decay[..., t, s] within the chunk, zero above the diagonal
+        decay = np.zeros((b, H, n, n))
+        for t in range(n):
+            run = np.ones((b, H))
+            for s in range(t, -1, -1):
+                decay[:, :, t, s] = run
+                run = run * alpha[:, s, :]
+        # into[..., t] = alpha_{c0} * ... * alpha_t: the entering state's decay
+        into = np.empty((b, H, n))
+        run = np.ones((b, H))
+        for t in range(n):
+            run = run * alpha[:, t, :]
+            into[:, :, t] = run
+        xc, dtc = x[:, c0:c1], dt[:, c0:c1]                          # [b,n,H,P], [b,n,H]
+        Bc, Cc = Bh[:, c0:c1], Ch[:, c0:c1]                          # [b,n,H,N]
+        u = xc * dtc[..., None]                                       # dt_s x_s
+        # Step 1
+        cb = np.einsum("bthn,bshn->bhts", Cc, Bc)
+        y_diag = np.einsum("bhts,bshp->bthp", cb * decay, u)
+        # Step 4
+        y_off = np.einsum("bht,bhpn,bthn->bthp", into, h, Cc)
+        y[:, c0:c1] = y_diag + y_off + D[None, None, :, None] * xc
+        # Step 2
+        S = np.einsum("bhs,bshp,bshn->bhpn", decay[:, :, n - 1, :], u, Bc)
+        # Step 3
+        h = into[:, :, n - 1, None, None] * h + S
+    return y, h

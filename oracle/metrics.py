@@ -17,9 +17,16 @@ inputs and "2e-2 normwise" for bf16 inputs, read as follows.
   (A relative error floored at 1e-3 * max|o| was tried first and rejected:
   the textbook fp32 serial recurrence itself scores 1.25e-4 under it for
   headdim 128, dstate 256, so that reading would fail correct fp32 code.)
+  Because a_i can be tens of times |o_i|, the fp32 checks also bound the
+  floored relative error below (``fp32_floored_bar``): no worse than twice
+  what the textbook fp32 recurrence scores on the same inputs, and never
+  above the 1e-4 bar where that recurrence meets it.  A change of 1e-3 |o|
+  on typical outputs passes the componentwise measure alone but fails the
+  pair.
 * bf16 inputs: normwise relative error in fp64
       ||g - o||_2 / ||o||_2  <=  2e-2
-  applied to y and to the final state separately.
+  applied to y and to the final state separately, and to y also over every
+  32-token block of every slice (``block_normwise_err``).
 """
 from __future__ import annotations
 
@@ -54,6 +61,13 @@ def max_rel_err(got, ref, floor: float = 1e-3) -> float:
     return float(np.max(np.abs(g - o) / scale))
 
 
+def fp32_floored_bar(textbook_err: float) -> float:
+    """Bar on ``max_rel_err`` for an fp32 result, given the score of the
+    textbook fp32 recurrence (``forms.serial_fp32``) on the same inputs:
+    1e-4 where that recurrence meets 1e-4, else twice its score."""
+    return max(FP32_MAX_REL, 2.0 * textbook_err)
+
+
 def normwise_err(got, ref) -> float:
     g = np.asarray(got, dtype=np.float64)
     o = np.asarray(ref, dtype=np.float64)
@@ -62,6 +76,40 @@ def normwise_err(got, ref) -> float:
     if den == 0.0:
         return float(num)
     return float(num / den)
+
+
+BLOCK = 32
+
+
+def block_normwise_err(got, ref, tok_axis: int, block: int = BLOCK):
+    """Largest normwise error over blocks of ``block`` tokens of every slice,
+    and where it occurs.  The token axis is cut into blocks (the last one
+    ragged); every other axis except the last (the feature axis) indexes a
+    slice.  With every block under the bar, so is every slice and the whole
+    array (squared norms add), but one wrong token row cannot hide in the
+    norm of a long sequence."""
+    worst, where = 0.0, None
+    g_all = np.moveaxis(np.asarray(got), tok_axis, -2)
+    o_all = np.moveaxis(np.asarray(ref), tok_axis, -2)
+    # one leading index at a time keeps the float64 temporaries small
+    lead = g_all.shape[0] if g_all.ndim > 2 else 1
+    for i in range(lead):
+        g = np.asarray(g_all[i] if g_all.ndim > 2 else g_all, dtype=np.float64)
+        o = np.asarray(o_all[i] if o_all.ndim > 2 else o_all, dtype=np.float64)
+        L, F = g.shape[-2], g.shape[-1]
+        pad = (-L) % block
+        if pad:
+            widths = [(0, 0)] * (g.ndim - 2) + [(0, pad), (0, 0)]
+            g, o = np.pad(g, widths), np.pad(o, widths)
+        shp = g.shape[:-2] + ((L + pad) // block, block, F)
+        d2 = ((g - o) ** 2).reshape(shp).sum(axis=(-2, -1))
+        o2 = (o ** 2).reshape(shp).sum(axis=(-2, -1))
+        r = np.sqrt(np.where(o2 > 0, d2 / np.where(o2 > 0, o2, 1.0), d2))
+        k = int(np.argmax(r))
+        if r.ravel()[k] > worst or where is None:
+            worst = float(r.ravel()[k])
+            where = ((i,) if g_all.ndim > 2 else ()) + tuple(int(v) for v in np.unravel_index(k, r.shape))
+    return worst, where
 
 
 def parity_error(got, ref, io_dtype: str, ref_abs=None) -> float:

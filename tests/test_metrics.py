@@ -47,3 +47,80 @@ def test_componentwise_measure_scores(oracle_mod):
 def test_componentwise_zero_reference_must_be_exact():
     assert metrics.componentwise_err([0.0, 1.0], [0.0, 1.0], [0.0, 2.0]) == 0.0
     assert metrics.componentwise_err([1e-30, 1.0], [0.0, 1.0], [0.0, 2.0]) == np.inf
+
+
+def _refs(oracle_mod, inp):
+    args = ("x", "dt", "A", "B", "C", "D", "initial_state")
+    yr, fr = oracle_mod.forward(*(inp[k] for k in args))
+    ya, fa = oracle_mod.forward(*(metrics.abs_inputs(inp)[k] for k in args))
+    return yr, fr, ya, fa
+
+
+def test_fp32_reading_floored_measure_fails_textbook_fp32(oracle_mod):
+    """Pins the reading of the fp32 bar.  At headdim 128, dstate 256 (seed
+    356) the textbook fp32 recurrence, correct fp32 code, scores above 1e-4
+    under the relative error floored at 1e-3 max|o|, so that measure cannot be
+    the bar; the componentwise measure passes it by three orders of
+    magnitude."""
+    from oracle.forms import serial_fp32
+    inp = make_inputs(1, 256, 2, 128, 256, 1, io_dtype="f32", init_std=0.1, seed=356)
+    yr, fr, ya, fa = _refs(oracle_mod, inp)
+    y32, f32 = serial_fp32(*(inp[k] for k in ("x", "dt", "A", "B", "C", "D", "initial_state")))
+    assert metrics.max_rel_err(y32, yr) >= 1e-4
+    assert metrics.componentwise_err(y32, yr, ya) <= 1e-6
+    assert metrics.componentwise_err(f32, fr, fa) <= 1e-5
+    # the floored bar that the GPU checks add adapts to it
+    assert metrics.max_rel_err(y32, yr) <= metrics.fp32_floored_bar(metrics.max_rel_err(y32, yr))
+
+
+def test_fp32_pair_rejects_a_small_error_on_typical_outputs(oracle_mod):
+    """A 1e-3 |o| change on the outputs whose magnitude reference is at least
+    20 |o| (typical ones) passes the componentwise measure alone (<= 5e-5),
+    which is why the fp32 checks also bound the floored error: the pair
+    rejects it."""
+    from oracle.forms import serial_fp32
+    inp = make_inputs(1, 256, 2, 64, 128, 1, io_dtype="f32", init_std=0.1, seed=21)
+    yr, fr, ya, fa = _refs(oracle_mod, inp)
+    y32, _ = serial_fp32(*(inp[k] for k in ("x", "dt", "A", "B", "C", "D", "initial_state")))
+    typical = ya >= 20 * np.abs(yr)
+    assert typical.mean() > 0.3
+    yp = np.where(typical, yr * (1 + 1e-3), yr)
+    assert metrics.componentwise_err(yp, yr, ya) <= 1e-4
+    bar = metrics.fp32_floored_bar(metrics.max_rel_err(y32, yr))
+    assert bar < 5e-4
+    assert metrics.max_rel_err(yp, yr) > bar
+    # and the textbook fp32 run itself passes both
+    assert metrics.componentwise_err(y32, yr, ya) <= 1e-6 and metrics.max_rel_err(y32, yr) <= bar
+
+
+def test_textbook_fp32_form_is_fp32(oracle_mod):
+    """serial_fp32 really rounds: it differs from the fp64 oracle by more than
+    fp64 rounding and by less than fp32 rounding allows."""
+    from oracle.forms import serial_fp32
+    inp = make_inputs(1, 64, 2, 16, 16, 1, io_dtype="f32", seed=3)
+    yr, _, ya, _ = _refs(oracle_mod, inp)
+    y32, _ = serial_fp32(*(inp[k] for k in ("x", "dt", "A", "B", "C", "D", "initial_state")))
+    assert y32.dtype == np.float32
+    err = metrics.componentwise_err(y32, yr, ya)
+    assert 1e-9 < err < 1e-6
+
+
+def test_block_measure_catches_one_wrong_token_row():
+    """At full size one completely wrong 64-value token row moves a slice's
+    normwise error by about sqrt(64 / 524288) ~ 0.011, under the 2e-2 bar;
+    the per-32-token-block measure sees it in full."""
+    rng = np.random.default_rng(4)
+    ref = rng.standard_normal((1, 8192, 2, 64))            # [b, L, H, P]
+    got = round_to_bf16(ref.astype(np.float32)).astype(np.float64)
+    got[0, 5000, 1] = rng.standard_normal(64)               # one wrong token row
+    slice_err = metrics.normwise_err(got[0, :, 1], ref[0, :, 1])
+    assert slice_err < metrics.BF16_NORMWISE
+    blk, where = metrics.block_normwise_err(got, ref, tok_axis=1)
+    assert blk > metrics.BF16_NORMWISE
+    assert where == (0, 1, 5000 // 32)
+    # bf16 rounding alone passes every block
+    ok = round_to_bf16(ref.astype(np.float32))
+    assert metrics.block_normwise_err(ok, ref, tok_axis=1)[0] < 1e-2
+    # a ragged tail and a 3-d layout [n, L, P]
+    blk3, where3 = metrics.block_normwise_err(got[:, :4001, 1], ref[:, :4001, 1], tok_axis=1)
+    assert blk3 < 1e-2 and where3[0] == 0
