@@ -39,7 +39,8 @@
  *    returns SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED or
  *    SSD_ERR_WORKSPACE has touched no device memory.  SSD_ERR_HIP means a
  *    launch failed (hipGetLastError); earlier kernels of that call may have
- *    run, so outputs are undefined.
+ *    run, so outputs are undefined.  SSD_ERR_NONFINITE comes only from the
+ *    opt-in check described below (SSD_CHECK_FINITE).
  *
  * Supported shapes (anything else returns SSD_ERR_UNSUPPORTED):
  *    chunk_len in {16, 32, 64, 128, 256};  headdim a multiple of 16, <= 128;
@@ -63,13 +64,33 @@ typedef enum ssd_status {
                                      nheads % ngroups != 0, unknown dtype   */
     SSD_ERR_UNSUPPORTED = 2,      /* valid but outside the supported shapes */
     SSD_ERR_WORKSPACE = 3,        /* workspace NULL or smaller than needed  */
-    SSD_ERR_HIP = 4               /* a kernel launch failed                 */
+    SSD_ERR_HIP = 4,              /* a kernel launch failed                 */
+    SSD_ERR_NONFINITE = 5         /* opt-in check (SSD_CHECK_FINITE): a NaN
+                                     or infinity in an input or an output  */
 } ssd_status;
 
 typedef enum ssd_dtype {
     SSD_F32 = 0,
     SSD_BF16 = 1
 } ssd_dtype;
+
+/*
+ * The opt-in non-finite check.  burn-mamba's `ssd_serial`
+ * (`mamba2/ssd/serial.rs`) guards every intermediate of its five kernels
+ * against NaN and infinity (its `san` calls), and the `Mamba2SsdInput`
+ * rustdoc gives the input a `sanity()` check; libssd offers the same guard
+ * on the values that cross its boundary.  With the environment variable
+ * SSD_CHECK_FINITE set to anything but "" or "0", every entry point below
+ * (forward, decode, convolution, normalisation) also scans its
+ * floating-point inputs before its work and its outputs after it, on
+ * `stream`, and returns SSD_ERR_NONFINITE if any value is a NaN or an
+ * infinity (exponent bits all ones).  The outputs are still written.  In
+ * that mode the call waits for `stream` (it reads the result back), so it
+ * cannot be captured in a graph, and checked calls on one device share one
+ * result word: they must not run concurrently.  With the variable unset or
+ * "0" the call reads it and nothing else changes: no extra kernel runs and
+ * nothing synchronises.  The variable is read on every call.
+ */
 
 /* Version of this ABI (SSD_ABI_VERSION of the built library). */
 int ssd_abi_version(void);

@@ -92,6 +92,43 @@ ssd_status choose_path(int seqlen, int nheads, int ngroups, int headdim, int dst
     return SSD_OK;
 }
 
+// The opt-in non-finite check: SSD_CHECK_FINITE set to anything but "" or
+// "0".  Read on every call, like SSD_FORWARD_PATH.
+bool finite_check_requested() {
+    const char *e = getenv("SSD_CHECK_FINITE");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
+// One call's non-finite check: created once the arguments are validated
+// (a rejected call launches nothing), it clears the device flag, scans the
+// buffers it is shown, and turns the flag into the call's status.  Off, it
+// does nothing.
+class FiniteCheck {
+  public:
+    explicit FiniteCheck(hipStream_t s) : s_(s), on_(finite_check_requested()) {
+        if (on_) err_ = ssd::launch_nonfinite_reset(s_);
+    }
+    void input(const void *p, size_t n, int es) { scan(p, n, es, ssd::kNonfiniteInput); }
+    void output(const void *p, size_t n, int es) { scan(p, n, es, ssd::kNonfiniteOutput); }
+    // `st`, the status of the call's own launches, unless a check launch
+    // failed or a value was not finite (reads the flag back: synchronises)
+    ssd_status finish(ssd_status st) {
+        if (!on_ || st != SSD_OK) return st;
+        if (err_ != hipSuccess) return SSD_ERR_HIP;
+        unsigned flag = 0;
+        if (ssd::read_nonfinite(&flag, s_) != hipSuccess) return SSD_ERR_HIP;
+        return flag ? SSD_ERR_NONFINITE : SSD_OK;
+    }
+
+  private:
+    void scan(const void *p, size_t n, int es, unsigned bit) {
+        if (on_ && err_ == hipSuccess) err_ = ssd::launch_nonfinite_scan(p, n, es, bit, s_);
+    }
+    hipStream_t s_;
+    bool on_;
+    hipError_t err_ = hipSuccess;
+};
+
 struct Layout {
     size_t acum_hi, acum_lo, dtT, cb, S, total;
 };
@@ -185,6 +222,20 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     if (names)
         for (int i = 0; i < nk; ++i) names[i] = kn[i];
 
+    const int es = io_dtype == SSD_BF16 ? 2 : 4;
+    const size_t nx = (size_t)batch * seqlen * nheads * headdim;
+    const size_t nbc = (size_t)batch * seqlen * ngroups * dstate;
+    const size_t nst = (size_t)batch * nheads * headdim * dstate;
+    FiniteCheck fc(stream);
+    fc.input(x, nx, es);
+    fc.input(dt, (size_t)batch * seqlen * nheads, 4);
+    fc.input(A, nheads, 4);
+    fc.input(B, nbc, es);
+    fc.input(C, nbc, es);
+    fc.input(D, D ? nheads : 0, 4);
+    fc.input(initial_state, initial_state ? nst : 0, 4);
+    fc.input(dtp.bias, dtp.bias ? nheads : 0, 4);
+
     hipError_t err;
     if (path == ssd::Path::Split)
         err = io_dtype == SSD_BF16 ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
@@ -198,7 +249,9 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
         for (int i = nk + 1; i <= ssd::kMaxForwardKernels; ++i)
             if (hipEventRecord(events[i], stream) != hipSuccess) return SSD_ERR_HIP;
     }
-    return SSD_OK;
+    fc.output(y, nx, es);
+    fc.output(final_state, final_state ? nst : 0, 4);
+    return fc.finish(SSD_OK);
 }
 
 }  // namespace
@@ -214,6 +267,7 @@ const char *ssd_status_string(ssd_status status) {
     case SSD_ERR_UNSUPPORTED: return "unsupported shape";
     case SSD_ERR_WORKSPACE: return "workspace missing or too small";
     case SSD_ERR_HIP: return "HIP kernel launch failed";
+    case SSD_ERR_NONFINITE: return "non-finite value (NaN or infinity) in an input or output";
     }
     return "unknown status";
 }
@@ -331,9 +385,24 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, con
     a.P = headdim;
     a.N = dstate;
     a.dtp = dtp;
+    const size_t nst = (size_t)batch * nheads * headdim * dstate;
+    const size_t nxh = (size_t)batch * nheads * headdim;
+    const size_t nbc = (size_t)batch * ngroups * dstate;
+    FiniteCheck fc(stream);
+    fc.input(state, nst, 4);
+    fc.input(x, nxh, (int)es);
+    fc.input(dt, (size_t)batch * nheads, 4);
+    fc.input(A, nheads, 4);
+    fc.input(B, nbc, (int)es);
+    fc.input(C, nbc, (int)es);
+    fc.input(D, D ? nheads : 0, 4);
+    fc.input(dtp.bias, dtp.bias ? nheads : 0, 4);
     hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_state_update<ssd::bf16>(a, stream)
                                           : ssd::launch_state_update<float>(a, stream);
-    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    fc.output(y, nxh, (int)es);
+    fc.output(state, nst, 4);
+    return fc.finish(SSD_OK);
 }
 
 ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,
@@ -375,9 +444,17 @@ ssd_status ssd_causal_conv1d_fwd(const void *x, const float *weight, const float
         return SSD_ERR_INVALID_ARGUMENT;
     ssd::ConvArgs a{x, weight, bias, out, conv_state, batch, seqlen, dim, width,
                     activation == SSD_ACT_SILU ? 1 : 0};
+    const size_t n = (size_t)batch * seqlen * dim;
+    FiniteCheck fc(stream);
+    fc.input(x, n, (int)es);
+    fc.input(weight, (size_t)dim * width, 4);
+    fc.input(bias, bias ? dim : 0, 4);
     const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_conv1d_fwd<ssd::bf16>(a, stream)
                                                 : ssd::launch_conv1d_fwd<float>(a, stream);
-    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    fc.output(out, n, (int)es);
+    fc.output(conv_state, conv_state ? (size_t)batch * dim * width : 0, (int)es);
+    return fc.finish(SSD_OK);
 }
 
 ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float *weight,
@@ -392,9 +469,18 @@ ssd_status ssd_causal_conv1d_update(void *conv_state, const void *x, const float
         return SSD_ERR_INVALID_ARGUMENT;
     ssd::ConvArgs a{x, weight, bias, out, conv_state, batch, 1, dim, width,
                     activation == SSD_ACT_SILU ? 1 : 0};
+    const size_t ncache = (size_t)batch * dim * width;
+    FiniteCheck fc(stream);
+    fc.input(conv_state, ncache, (int)es);
+    fc.input(x, (size_t)batch * dim, (int)es);
+    fc.input(weight, (size_t)dim * width, 4);
+    fc.input(bias, bias ? dim : 0, 4);
     const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_conv1d_update<ssd::bf16>(a, stream)
                                                 : ssd::launch_conv1d_update<float>(a, stream);
-    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    fc.output(out, (size_t)batch * dim, (int)es);
+    fc.output(conv_state, ncache, (int)es);
+    return fc.finish(SSD_OK);
 }
 
 ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weight, int rows,
@@ -416,9 +502,17 @@ ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weig
     a.dim = dim;
     a.gate = z ? (norm_before_gate ? 2 : 1) : 0;
     a.eps = eps;
+    const int es = io_dtype == SSD_BF16 ? 2 : 4;
+    const size_t n = (size_t)rows * dim;
+    FiniteCheck fc(stream);
+    fc.input(y, n, es);
+    fc.input(z, z ? n : 0, es);
+    fc.input(weight, dim, 4);
     const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_gated_rmsnorm<ssd::bf16>(a, stream)
                                                 : ssd::launch_gated_rmsnorm<float>(a, stream);
-    return err == hipSuccess ? SSD_OK : SSD_ERR_HIP;
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    fc.output(out, n, es);
+    return fc.finish(SSD_OK);
 }
 
 }  // extern "C"

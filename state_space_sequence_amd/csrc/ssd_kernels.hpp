@@ -138,4 +138,14 @@ constexpr int kMaxNormDim = 8192;
 template <typename T>
 hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream);
 
+// The opt-in non-finite check (ssd_check_kernels.hip): clear the device's
+// flag word, scan a buffer of `nelems` fp32 (elem_bytes 4) or bf16 (2)
+// values OR-ing `bit` into the flag when one is a NaN or an infinity, and
+// read the flag back (synchronises `stream`).
+constexpr unsigned kNonfiniteInput = 1u, kNonfiniteOutput = 2u;
+hipError_t launch_nonfinite_reset(hipStream_t stream);
+hipError_t launch_nonfinite_scan(const void *p, size_t nelems, int elem_bytes, unsigned bit,
+                                 hipStream_t stream);
+hipError_t read_nonfinite(unsigned *out, hipStream_t stream);
+
 }  // namespace ssd

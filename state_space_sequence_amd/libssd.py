@@ -24,6 +24,7 @@ SSD_ERR_INVALID_ARGUMENT = 1
 SSD_ERR_UNSUPPORTED = 2
 SSD_ERR_WORKSPACE = 3
 SSD_ERR_HIP = 4
+SSD_ERR_NONFINITE = 5  # opt-in check: SSD_CHECK_FINITE set in the environment
 
 SSD_F32 = 0
 SSD_BF16 = 1

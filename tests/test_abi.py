@@ -41,8 +41,9 @@ def test_every_declared_symbol_is_exported(lib):
 
 def test_version_and_strings(lib):
     assert lib.ssd_abi_version() == 1
-    for code in range(5):
+    for code in range(6):
         assert lib.ssd_status_string(code)
+    assert b"non-finite" in lib.ssd_status_string(5)
     assert lib.ssd_status_string(99) == b"unknown status"
     assert lib.ssd_chunk_scan_fwd_max_kernels() >= 3
 
@@ -237,3 +238,38 @@ def norm(lib, **kw):
 ])
 def test_norm_validation(lib, kw, code):
     assert norm(lib, **kw) == code
+
+
+def test_header_status_codes():
+    """The status values the header documents, SSD_ERR_NONFINITE among them."""
+    text = open(HEADER).read()
+    for name, value in (("SSD_OK", 0), ("SSD_ERR_INVALID_ARGUMENT", 1), ("SSD_ERR_UNSUPPORTED", 2),
+                        ("SSD_ERR_WORKSPACE", 3), ("SSD_ERR_HIP", 4), ("SSD_ERR_NONFINITE", 5)):
+        assert re.search(r"\b%s = %d\b" % (name, value), text), name
+    from state_space_sequence_amd import libssd
+    assert libssd.SSD_ERR_NONFINITE == 5
+
+
+def test_finite_check_keeps_validation_first(lib, monkeypatch):
+    """With the non-finite check requested, a call with bad arguments still
+    returns its validation status before anything is enqueued (no kernel,
+    no read-back: this runs without a GPU)."""
+    monkeypatch.setenv("SSD_CHECK_FINITE", "1")
+    p = ctypes.c_void_p(FAKE)
+    # forward: nheads not a multiple of ngroups
+    st = lib.ssd_chunk_scan_fwd(p, p, p, p, p, None, None, 64, 3, 1, 64, 4, 16, 16, 0, p, None,
+                                None, 0, None)
+    assert st == 1
+    # forward: unsupported chunk length
+    st = lib.ssd_chunk_scan_fwd(p, p, p, p, p, None, None, 100, 1, 1, 64, 4, 16, 16, 0, p, None,
+                                None, 0, None)
+    assert st == 2
+    # decode: missing state
+    st = lib.ssd_state_update(None, p, p, p, p, p, None, 1, 2, 4, 16, 16, 0, p, None)
+    assert st == 1
+    # convolution: width 5
+    st = lib.ssd_causal_conv1d_fwd(p, p, None, 1, 10, 16, 5, 1, 1, p, None, None)
+    assert st == 2
+    # normalisation: dim not a multiple of 8
+    st = lib.ssd_gated_rmsnorm_fwd(p, None, p, 4, 12, ctypes.c_float(1e-5), 0, 1, p, None)
+    assert st == 2

@@ -878,3 +878,96 @@ def test_forward_and_decode_replay_in_a_graph(dev, io):
         assert torch.equal(yd, yd_ref), rep
         assert torch.equal(state, st_ref), rep
     del graph
+
+
+# ------------------------------------------------------ opt-in non-finite check
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_nonfinite_check_forward(dev, monkeypatch, path, io):
+    """With SSD_CHECK_FINITE set: clean inputs pass, a NaN in x, an infinity
+    in dt or in the initial state, and an output that overflows each return
+    SSD_ERR_NONFINITE; with the check off the same NaN goes through silently
+    (the status is OK and y holds NaNs)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    inp = make_inputs(2, 300, 4, 64, 128, 2, io_dtype=io, init_std=0.1, seed=51)
+    skip_if_path_unsupported(inp, io, 64)
+    t = to_torch(inp, io, dev)
+
+    def run(**over):
+        a = dict(t, **over)
+        return libssd.ssd_chunk_scan_fwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"],
+                                         a["initial_state"], chunk_len=64)
+
+    monkeypatch.setenv("SSD_CHECK_FINITE", "1")
+    y, fin = run()
+    torch.cuda.synchronize()
+    assert torch.isfinite(y).all() and torch.isfinite(fin).all()
+    xn = t["x"].clone()
+    xn[1, 123, 2, 7] = float("nan")
+    dtn = t["dt"].clone()
+    dtn[0, 299, 3] = float("inf")
+    sn = t["initial_state"].clone()
+    sn[1, 0, 5, 100] = float("-inf")
+    big = torch.full_like(t["x"], 3.0e38 if io == "f32" else 3.0e38)
+    for what, over in (("x NaN", dict(x=xn)), ("dt inf", dict(dt=dtn)),
+                       ("initial state -inf", dict(initial_state=sn)),
+                       ("y overflow", dict(x=big))):
+        with pytest.raises(libssd.SsdError) as ei:
+            run(**over)
+        assert ei.value.status == libssd.SSD_ERR_NONFINITE, what
+        _say("  %s -> SSD_ERR_NONFINITE" % what)
+    monkeypatch.setenv("SSD_CHECK_FINITE", "0")
+    y, _ = run(x=xn)
+    torch.cuda.synchronize()
+    assert torch.isnan(y).any()
+
+
+def test_nonfinite_check_decode_conv_norm(dev, monkeypatch):
+    """The check on the decode step (a NaN in the cached state), the
+    convolution (an infinity in x, misaligned by one element in the update)
+    and the gated norm (a NaN in the gate)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_conv_inputs, make_norm_inputs, to_torch
+    monkeypatch.setenv("SSD_CHECK_FINITE", "1")
+    inp = make_inputs(2, 1, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=52)
+    t = to_torch(inp, "bf16", dev)
+    state = t["initial_state"].clone()
+    args = (t["x"][:, 0].contiguous(), t["dt"][:, 0].contiguous(), t["A"],
+            t["B"][:, 0].contiguous(), t["C"][:, 0].contiguous(), t["D"])
+    libssd.ssd_state_update(state, *args)
+    state[0, 3, 63, 127] = float("nan")
+    with pytest.raises(libssd.SsdError) as ei:
+        libssd.ssd_state_update(state, *args)
+    assert ei.value.status == libssd.SSD_ERR_NONFINITE
+
+    cin = make_conv_inputs(2, 40, 64, 4, io_dtype="bf16", seed=53, decode_steps=1)
+    x = torch.from_numpy(cin["x"]).to(torch.bfloat16).to(dev)
+    w = torch.from_numpy(cin["weight"]).to(dev)
+    out, cs = libssd.ssd_causal_conv1d_fwd(x, w, None, "silu")
+    x[1, 39, 63] = float("inf")
+    with pytest.raises(libssd.SsdError) as ei:
+        libssd.ssd_causal_conv1d_fwd(x, w, None, "silu")
+    assert ei.value.status == libssd.SSD_ERR_NONFINITE
+    # the update on 2-byte aligned operands: the odd first element checked on its own
+    flat = torch.zeros(2 * 64 + 1, dtype=torch.bfloat16, device=dev)
+    xd = flat[1:].view(2, 64)
+    xd.copy_(torch.from_numpy(cin["x_dec"][0]).to(torch.bfloat16))
+    libssd.ssd_causal_conv1d_update(cs, xd, w, None, "silu")
+    xd[0, 0] = float("nan")
+    with pytest.raises(libssd.SsdError) as ei:
+        libssd.ssd_causal_conv1d_update(cs, xd, w, None, "silu")
+    assert ei.value.status == libssd.SSD_ERR_NONFINITE
+
+    nin = make_norm_inputs(8, 256, io_dtype="bf16", seed=54)
+    y = torch.from_numpy(nin["y"]).to(torch.bfloat16).to(dev)
+    z = torch.from_numpy(nin["z"]).to(torch.bfloat16).to(dev)
+    wn = torch.from_numpy(nin["weight"]).to(dev)
+    libssd.ssd_gated_rmsnorm_fwd(y, z, wn)
+    z[7, 255] = float("nan")
+    with pytest.raises(libssd.SsdError) as ei:
+        libssd.ssd_gated_rmsnorm_fwd(y, z, wn)
+    assert ei.value.status == libssd.SSD_ERR_NONFINITE
+    torch.cuda.synchronize()
