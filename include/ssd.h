@@ -145,6 +145,31 @@ ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               size_t workspace_bytes, hipStream_t stream);
 
 /*
+ * ssd_chunk_scan_fwd for callers that cannot allocate device memory: code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments without the workspace; the call itself
+ * allocates nothing.  Where the forward path needs a workspace (the split
+ * path, see ssd_chunk_scan_fwd_timed) it uses a scratch array of
+ * SSD_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on,
+ * from the library's load until the process ends; a problem whose workspace
+ * (ssd_chunk_scan_fwd_workspace_size) exceeds it returns SSD_ERR_WORKSPACE
+ * before anything is enqueued.  Every call on one GPU shares that GPU's
+ * array and it keeps the last call's contents (the forward needs none of
+ * them: no kernel reads workspace that the same call has not written), so
+ * calls that overlap on one GPU, from several streams or host threads, race
+ * and must be serialised by the caller.  The first call on a device looks
+ * the array's address up once (SSD_ERR_HIP if that fails).
+ */
+#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const float *initial_state, int chunk_len,
+                                      int ngroups, int batch, int seqlen, int nheads,
+                                      int headdim, int dstate, ssd_dtype io_dtype,
+                                      void *y, float *final_state, hipStream_t stream);
+
+/*
  * Upper bound on the number of kernels one `ssd_chunk_scan_fwd` call
  * launches (fixed for a library build).
  */

@@ -8,12 +8,53 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
+
+// Scratch of the no-allocation forward (ssd_chunk_scan_fwd_noalloc): every
+// GPU that the library runs on holds one copy of this array until the
+// process ends.  In host code `scratch` names a host-side stand-in, not the
+// device array: the device address of the current GPU's copy comes from
+// hipGetSymbolAddress (scratch_address below) and only that address is
+// handed to kernels.
+static __device__ __align__(256) unsigned char scratch[SSD_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
 constexpr size_t kAlign = 256;
+
+// The device address of `scratch` on the device that runs `stream` (the
+// current device for the null stream), looked up once per device with that
+// device current and kept.
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];
+
+hipError_t scratch_address(hipStream_t stream, void **out) {
+    int cur = 0, dev = 0;
+    hipError_t err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    dev = cur;
+    if (stream && (err = hipStreamGetDevice(stream, &dev)) != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        void *p = nullptr;
+        err = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        if (!p || (uintptr_t)p % kAlign != 0) return hipErrorInvalidSymbol;
+        g_scratch_ptr[dev] = p;
+    }
+    *out = g_scratch_ptr[dev];
+    return hipSuccess;
+}
 
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
@@ -163,7 +204,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
                         float *final_state, void *workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t *events, int *nkernels,
                         const char **names, const ssd_dt_proc *dt_proc,
-                        const int *seq_idx = nullptr) {
+                        const int *seq_idx = nullptr, bool noalloc = false) {
     ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
@@ -183,9 +224,19 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
         return path != ssd::Path::Fused ? SSD_ERR_UNSUPPORTED : SSD_ERR_INVALID_ARGUMENT;
     const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
                                       chunk_len, io_dtype, path);
-    if (lay.total > 0 &&
-        (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign)))
+    if (noalloc) {
+        // the library's scratch array stands in for the workspace
+        if (lay.total > SSD_NOALLOC_SCRATCH_BYTES) return SSD_ERR_WORKSPACE;
+        workspace = nullptr;
+        workspace_bytes = 0;
+        if (lay.total > 0) {
+            if (scratch_address(stream, &workspace) != hipSuccess) return SSD_ERR_HIP;
+            workspace_bytes = SSD_NOALLOC_SCRATCH_BYTES;
+        }
+    } else if (lay.total > 0 &&
+               (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))) {
         return SSD_ERR_WORKSPACE;
+    }
 
     ssd::ForwardArgs a;
     a.x = x;
@@ -328,6 +379,17 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
                         seqlen, nheads, headdim, dstate, io_dtype, y, final_state,
                         workspace, workspace_bytes, stream, nullptr, nullptr, nullptr,
                         dt_proc, seq_idx);
+}
+
+ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const float *A,
+                                      const void *B, const void *C, const float *D,
+                                      const float *initial_state, int chunk_len, int ngroups,
+                                      int batch, int seqlen, int nheads, int headdim,
+                                      int dstate, ssd_dtype io_dtype, void *y,
+                                      float *final_state, hipStream_t stream) {
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch, seqlen,
+                        nheads, headdim, dstate, io_dtype, y, final_state, nullptr, 0, stream,
+                        nullptr, nullptr, nullptr, nullptr, nullptr, true);
 }
 
 int ssd_chunk_scan_fwd_max_kernels(void) { return ssd::kMaxForwardKernels; }

@@ -80,6 +80,8 @@ def load():
             ctypes.POINTER(_p), _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_char_p)]
         lib.ssd_state_update.restype = _i
         lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
+        lib.ssd_chunk_scan_fwd_noalloc.restype = _i
+        lib.ssd_chunk_scan_fwd_noalloc.argtypes = _FWD_ARGS[:17] + [_p]
         lib.ssd_chunk_scan_fwd_ex.restype = _i
         lib.ssd_chunk_scan_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(DtProc)]
         lib.ssd_chunk_scan_fwd_varlen.restype = _i
@@ -267,6 +269,42 @@ def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
     (y, final_state, kernel_names)."""
     return _forward(list(events), x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
                     y, final_state, workspace, return_final_state, stream)
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20   # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
+
+
+def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D, initial_state, chunk_len, y, final_state,
+                               stream=None):
+    """``ssd_chunk_scan_fwd_noalloc``: the forward with no workspace argument
+    and no allocation anywhere, neither in the library nor here, so y (and
+    final_state, unless None) must be given.  The split path uses the
+    library's per-GPU scratch array; calls that overlap on one GPU race."""
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    for n, t in (("x", x), ("B", B), ("C", C), ("y", y)):
+        _check_dev(n, t, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
+                 ("final_state", final_state)):
+        _check_dev(n, t, torch.float32, dev)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if tuple(y.shape) != tuple(x.shape) or tuple(dt.shape) != (b, L, H) or \
+            tuple(B.shape) != (b, L, G, N) or tuple(C.shape) != (b, L, G, N):
+        raise ValueError("inconsistent shapes")
+    for n, t in (("initial_state", initial_state), ("final_state", final_state)):
+        if t is not None and tuple(t.shape) != (b, H, P, N):
+            raise ValueError("%s must be [b,H,P,N]" % n)
+    st = lib.ssd_chunk_scan_fwd_noalloc(_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D),
+                                        _ptr(initial_state), int(chunk_len), G, b, L, H, P, N,
+                                        io, _ptr(y), _ptr(final_state), _stream_handle(stream))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_chunk_scan_fwd_noalloc")
+    return y, final_state
 
 
 def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream=None,

@@ -273,3 +273,26 @@ def test_finite_check_keeps_validation_first(lib, monkeypatch):
     # normalisation: dim not a multiple of 8
     st = lib.ssd_gated_rmsnorm_fwd(p, None, p, 4, 12, ctypes.c_float(1e-5), 0, 1, p, None)
     assert st == 2
+
+
+def test_noalloc_rejects_oversized_problems_before_the_gpu(lib):
+    """ssd_chunk_scan_fwd_noalloc: a problem whose workspace exceeds the
+    scratch array returns SSD_ERR_WORKSPACE from host validation, and bad
+    arguments keep their own status (no GPU needed: nothing is enqueued)."""
+    from state_space_sequence_amd import libssd
+    p = ctypes.c_void_p(FAKE)
+    need = ctypes.c_size_t(0)
+    assert lib.ssd_chunk_scan_fwd_workspace_size(1, 8192, 80, 64, 128, 1, 256, 0,
+                                                 ctypes.byref(need)) == 0
+    assert need.value > libssd.NOALLOC_SCRATCH_BYTES
+    st = lib.ssd_chunk_scan_fwd_noalloc(p, p, p, p, p, None, None, 256, 1, 1, 8192, 80, 64, 128,
+                                        0, p, None, None)
+    assert st == 3
+    st = lib.ssd_chunk_scan_fwd_noalloc(p, p, p, p, p, None, None, 256, 3, 1, 64, 80, 64, 128,
+                                        0, p, None, None)
+    assert st == 1   # nheads % ngroups
+    st = lib.ssd_chunk_scan_fwd_noalloc(None, p, p, p, p, None, None, 256, 1, 1, 64, 8, 64, 128,
+                                        0, p, None, None)
+    assert st == 1   # x missing
+    assert "#define SSD_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in open(HEADER).read()
+    assert libssd.NOALLOC_SCRATCH_BYTES == 64 << 20
