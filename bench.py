@@ -22,7 +22,8 @@ Also reported (not part of ``value``):
   * the other workloads, timed before the headline: the tiny fp32, 130M and
     8-group forwards, the decode state update (b256 / 80 heads), the
     headline forward on the raw time step with the preprocessing (bias,
-    softplus) inside the kernels and with packed variable-length sequences,
+    softplus) inside the kernels, with packed variable-length sequences, and
+    with the output gate and a per-column D,
     the causal depthwise conv before the scan and its single-token update,
     and the gated RMS normalisation after it;
   * ``per_workload``: for each of the five workloads, tokens/s, TFLOP/s, GB/s
@@ -343,6 +344,25 @@ def time_forward_dt_proc(w, dev, ev, steps=100, warmup=20):
               dt_bias=t["dt_bias"], dt_softplus=True)
     ms = time_plain(lambda: libssd.ssd_chunk_scan_fwd(*args, **kw), ev, steps, warmup)
     del t, y, fin, ws
+    return ms
+
+
+def time_forward_gated(w, dev, ev, steps=100, warmup=20):
+    """ms per forward with the output gate and a per-(head, column) D, y =
+    (C h + D (*) x) silu(z) (ssd_chunk_scan_fwd_full)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_gate_inputs
+    inp, t, y, fin, ws = setup(w, dev)
+    g = make_gate_inputs(w.batch, w.seqlen, w.nheads, w.headdim, io_dtype=w.io_dtype,
+                         seed=w.seed)
+    tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    z = torch.from_numpy(g["z"]).to(tdt).to(dev)
+    Dhp = torch.from_numpy(g["D_hp"]).to(dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], Dhp, t["initial_state"])
+    kw = dict(chunk_len=w.chunk_len, y=y, final_state=fin, workspace=ws, z=z)
+    ms = time_plain(lambda: libssd.ssd_chunk_scan_fwd(*args, **kw), ev, steps, warmup)
+    del t, y, fin, ws, z
     return ms
 
 
@@ -723,6 +743,15 @@ def main():
                     % (nseq, w.batch),
             "ms_per_step": round(msv, 4),
             "tokens_per_s": round(w.batch * w.seqlen / (msv * 1e-3), 1)}
+        msg = time_forward_gated(w, dev, ev)
+        extra[w.name + "_gated"] = {
+            "what": "the same forward with the output gate and a per-(head, column) D: "
+                    "y = (C h + D x) silu(z), z read like x",
+            "ms_per_step": round(msg, 4),
+            "tokens_per_s": round(w.batch * w.seqlen / (msg * 1e-3), 1),
+            "alg_bytes": alg_bytes_forward(w, es) + w.batch * w.seqlen * w.nheads * w.headdim * es,
+            "frac_hbm": round((alg_bytes_forward(w, es) + w.batch * w.seqlen * w.nheads * w.headdim
+                               * es) / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(w, dev, ev)
         extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev)
 

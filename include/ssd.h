@@ -299,6 +299,67 @@ ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float
                                      const int *seq_idx, const ssd_dt_proc *dt_proc);
 
 /*
+ * The output gate and the shape of the skip term.  The pages' scan and
+ * decode kernels take `D` and `z` (`mamba_chunk_scan_combined(x, dt, A, B,
+ * C, chunk_size, D, z, seq_idx, ...)`, `selective_state_update(state, x, dt,
+ * A, B, C, D, z, dt_bias, dt_softplus)` in fla `layers/mamba2.py`), and the
+ * lrnnx scan spells out what they do to the output (`selective_scan_ref`,
+ * "Final Output Processing"): the skip term is added, then the sum is
+ * multiplied by SiLU of the gate,
+ *
+ *     y_t = (h_t C_t + D (*) x_t) * silu(z_t),    silu(v) = v / (1 + e^-v),
+ *
+ * per element, with D either one value per head or one per head and
+ * headdim column (the fla decode branch passes D expanded to [nheads,
+ * headdim]).
+ *
+ *   z              like x: [batch, seqlen, nheads, headdim] for the forward,
+ *                  [batch, nheads, headdim] for the decode step; io_dtype,
+ *                  aligned like x (16 bytes for the forward); NULL = no gate
+ *   D_per_channel  0: D is [nheads] (as in the plain calls); nonzero: D is
+ *                  [nheads, headdim] fp32 (ignored when D is NULL)
+ *
+ * The state and final_state are not gated.  A misaligned z returns
+ * SSD_ERR_INVALID_ARGUMENT.
+ */
+typedef struct ssd_gate {
+    const void *z;
+    int D_per_channel;
+} ssd_gate;
+
+/*
+ * The forward with every optional argument of the pages' scan call: packed
+ * sequences (seq_idx, as ssd_chunk_scan_fwd_varlen; NULL = one sequence per
+ * row), the time-step preprocessing (dt_proc, as ssd_chunk_scan_fwd_ex; NULL =
+ * dt as given) and the gate and per-channel D (gate; NULL = neither).  With
+ * all three NULL it is ssd_chunk_scan_fwd.  Both forward paths take the gate
+ * and per-channel D; packed sequences need the fused pass (see
+ * ssd_chunk_scan_fwd_varlen).
+ */
+ssd_status ssd_chunk_scan_fwd_full(const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   const float *initial_state, int chunk_len, int ngroups,
+                                   int batch, int seqlen, int nheads, int headdim,
+                                   int dstate, ssd_dtype io_dtype, void *y,
+                                   float *final_state, void *workspace,
+                                   size_t workspace_bytes, hipStream_t stream,
+                                   const int *seq_idx, const ssd_dt_proc *dt_proc,
+                                   const ssd_gate *gate);
+
+/*
+ * The decode step with every optional argument of the pages' decode call:
+ * the time-step preprocessing (dt_proc) and the gate and per-channel D
+ * (gate), both nullable.  With both NULL it is ssd_state_update.  y is the
+ * gated output; the state is updated as in ssd_state_update.
+ */
+ssd_status ssd_state_update_full(float *state, const void *x, const float *dt,
+                                 const float *A, const void *B, const void *C,
+                                 const float *D, int ngroups, int batch, int nheads,
+                                 int headdim, int dstate, ssd_dtype io_dtype,
+                                 void *y, hipStream_t stream,
+                                 const ssd_dt_proc *dt_proc, const ssd_gate *gate);
+
+/*
  * ssd_state_update with dt the raw time step [batch, nheads], processed as
  * *dt_proc says (the `dt_bias` and `dt_softplus` arguments of the layer's
  * `selective_state_update` call).  A NULL dt_proc makes it exactly

@@ -22,6 +22,8 @@ Contents
 ``norm``     the layer's gated RMS normalisation after the scan, in fp64.
 ``varlen``   packed variable-length sequences: the serial oracle run on every
              sequence of a row separately.
+``gate``     the output gate y * silu(z) and a per-(head, column) D on top of
+             the serial oracle, in fp64.
 """
 from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
-from . import conv, dt, forms, metrics, norm, varlen  # noqa: F401
+from . import conv, dt, forms, gate, metrics, norm, varlen  # noqa: F401

@@ -204,7 +204,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
                         float *final_state, void *workspace, size_t workspace_bytes,
                         hipStream_t stream, hipEvent_t *events, int *nkernels,
                         const char **names, const ssd_dt_proc *dt_proc,
-                        const int *seq_idx = nullptr, bool noalloc = false) {
+                        const int *seq_idx = nullptr, bool noalloc = false,
+                        const ssd_gate *gate = nullptr) {
     ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
                                         chunk_len, io_dtype);
     if (st != SSD_OK) return st;
@@ -217,6 +218,9 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
         (initial_state && !aligned(initial_state, 16)) ||
         (final_state && !aligned(final_state, 16)))
         return SSD_ERR_INVALID_ARGUMENT;
+    const void *z = gate ? gate->z : nullptr;
+    const bool D_hdim = gate && gate->D_per_channel && D;
+    if (z && !aligned(z, 16)) return SSD_ERR_INVALID_ARGUMENT;
     ssd::Path path;
     if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
     // packed sequences are handled by the fused pass only
@@ -258,6 +262,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.nchunks = (seqlen + chunk_len - 1) / chunk_len;
     a.dtp = dtp;
     a.seq_idx = seq_idx;
+    a.z = z;
+    a.D_hdim = D_hdim;
     char *ws = static_cast<char *>(workspace);
     const bool split = path == ssd::Path::Split;
     a.acum_hi = split ? reinterpret_cast<float *>(ws + lay.acum_hi) : nullptr;
@@ -283,9 +289,10 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     fc.input(A, nheads, 4);
     fc.input(B, nbc, es);
     fc.input(C, nbc, es);
-    fc.input(D, D ? nheads : 0, 4);
+    fc.input(D, D ? (D_hdim ? (size_t)nheads * headdim : (size_t)nheads) : 0, 4);
     fc.input(initial_state, initial_state ? nst : 0, 4);
     fc.input(dtp.bias, dtp.bias ? nheads : 0, 4);
+    fc.input(z, z ? nx : 0, es);
 
     hipError_t err;
     if (path == ssd::Path::Split)
@@ -392,6 +399,20 @@ ssd_status ssd_chunk_scan_fwd_noalloc(const void *x, const float *dt, const floa
                         nullptr, nullptr, nullptr, nullptr, nullptr, true);
 }
 
+ssd_status ssd_chunk_scan_fwd_full(const void *x, const float *dt, const float *A,
+                                   const void *B, const void *C, const float *D,
+                                   const float *initial_state, int chunk_len, int ngroups,
+                                   int batch, int seqlen, int nheads, int headdim, int dstate,
+                                   ssd_dtype io_dtype, void *y, float *final_state,
+                                   void *workspace, size_t workspace_bytes, hipStream_t stream,
+                                   const int *seq_idx, const ssd_dt_proc *dt_proc,
+                                   const ssd_gate *gate) {
+    return forward_impl(x, dt, A, B, C, D, initial_state, chunk_len, ngroups, batch, seqlen,
+                        nheads, headdim, dstate, io_dtype, y, final_state, workspace,
+                        workspace_bytes, stream, nullptr, nullptr, nullptr, dt_proc, seq_idx,
+                        false, gate);
+}
+
 int ssd_chunk_scan_fwd_max_kernels(void) { return ssd::kMaxForwardKernels; }
 
 ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float *A,
@@ -412,11 +433,11 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
                         nullptr);
 }
 
-ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, const float *A,
-                               const void *B, const void *C, const float *D, int ngroups,
-                               int batch, int nheads, int headdim, int dstate,
-                               ssd_dtype io_dtype, void *y, hipStream_t stream,
-                               const ssd_dt_proc *dt_proc) {
+ssd_status ssd_state_update_full(float *state, const void *x, const float *dt,
+                                 const float *A, const void *B, const void *C, const float *D,
+                                 int ngroups, int batch, int nheads, int headdim, int dstate,
+                                 ssd_dtype io_dtype, void *y, hipStream_t stream,
+                                 const ssd_dt_proc *dt_proc, const ssd_gate *gate) {
     if (batch <= 0 || nheads <= 0 || headdim <= 0 || dstate <= 0 || ngroups <= 0)
         return SSD_ERR_INVALID_ARGUMENT;
     if (nheads % ngroups != 0) return SSD_ERR_INVALID_ARGUMENT;
@@ -432,6 +453,9 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, con
     ssd::DtProc dtp;
     const ssd_status st = check_dt_proc(dt_proc, &dtp);
     if (st != SSD_OK) return st;
+    const void *z = gate ? gate->z : nullptr;
+    const bool D_hdim = gate && gate->D_per_channel && D;
+    if (z && !aligned(z, es)) return SSD_ERR_INVALID_ARGUMENT;
     ssd::DecodeArgs a;
     a.state = state;
     a.x = x;
@@ -447,6 +471,8 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, con
     a.P = headdim;
     a.N = dstate;
     a.dtp = dtp;
+    a.z = z;
+    a.D_hdim = D_hdim;
     const size_t nst = (size_t)batch * nheads * headdim * dstate;
     const size_t nxh = (size_t)batch * nheads * headdim;
     const size_t nbc = (size_t)batch * ngroups * dstate;
@@ -457,8 +483,9 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, con
     fc.input(A, nheads, 4);
     fc.input(B, nbc, (int)es);
     fc.input(C, nbc, (int)es);
-    fc.input(D, D ? nheads : 0, 4);
+    fc.input(D, D ? (D_hdim ? (size_t)nheads * headdim : (size_t)nheads) : 0, 4);
     fc.input(dtp.bias, dtp.bias ? nheads : 0, 4);
+    fc.input(z, z ? nxh : 0, (int)es);
     hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_state_update<ssd::bf16>(a, stream)
                                           : ssd::launch_state_update<float>(a, stream);
     if (err != hipSuccess) return SSD_ERR_HIP;
@@ -467,12 +494,21 @@ ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, con
     return fc.finish(SSD_OK);
 }
 
+ssd_status ssd_state_update_ex(float *state, const void *x, const float *dt, const float *A,
+                               const void *B, const void *C, const float *D, int ngroups,
+                               int batch, int nheads, int headdim, int dstate,
+                               ssd_dtype io_dtype, void *y, hipStream_t stream,
+                               const ssd_dt_proc *dt_proc) {
+    return ssd_state_update_full(state, x, dt, A, B, C, D, ngroups, batch, nheads, headdim,
+                                 dstate, io_dtype, y, stream, dt_proc, nullptr);
+}
+
 ssd_status ssd_state_update(float *state, const void *x, const float *dt, const float *A,
                             const void *B, const void *C, const float *D, int ngroups,
                             int batch, int nheads, int headdim, int dstate,
                             ssd_dtype io_dtype, void *y, hipStream_t stream) {
-    return ssd_state_update_ex(state, x, dt, A, B, C, D, ngroups, batch, nheads, headdim,
-                               dstate, io_dtype, y, stream, nullptr);
+    return ssd_state_update_full(state, x, dt, A, B, C, D, ngroups, batch, nheads, headdim,
+                                 dstate, io_dtype, y, stream, nullptr, nullptr);
 }
 
 namespace {

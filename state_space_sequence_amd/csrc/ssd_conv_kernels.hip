@@ -61,9 +61,7 @@ __device__ __forceinline__ void store8(float *p, const float (&v)[8]) {
 }
 
 // SiLU v sigmoid(v) = v / (1 + e^-v) (the layer's activation)
-__device__ __forceinline__ float silu(float v) {
-    return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
-}
+__device__ __forceinline__ float silu(float v) { return silu_f32(v); }
 
 }  // namespace
 

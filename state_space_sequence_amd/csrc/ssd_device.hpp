@@ -103,6 +103,14 @@ __device__ __forceinline__ double wave_inclusive_scan_f64(double v, int lane) {
 
 __device__ __forceinline__ float fast_exp(float v) { return __expf(v); }
 
+// SiLU, v / (1 + e^-v), from the hardware exp and reciprocal (for large
+// negative v, e^-v overflows to infinity and the result is 0, the limit).
+// The layer's activation after the conv, its gate in the norm, and the
+// output gate of the scan and decode calls.
+__device__ __forceinline__ float silu_f32(float v) {
+    return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
+}
+
 // softplus(v) = log(1 + e^v) in fp32, as max(v, 0) + log1p(t) with
 // t = e^-|v| in (0, 1].  log1p(t) is evaluated from the hardware log as
 // log(u) * t / (u - 1), u = 1 + t (t itself when u rounds to 1): the

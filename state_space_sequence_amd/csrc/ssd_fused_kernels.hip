@@ -210,16 +210,24 @@ struct Fused {
     static_assert(STG % 16 == 0, "alignment");
     // (one workgroup per compute unit, which the column choice arranges)
     static_assert(LDS <= 160 * 1024, "LDS per compute unit");
-    // the loader's DMAs of a block (C and B, x, and the next block's dt)
-    // and y stores.  At the end of block kb it waits for the DMAs of block
-    // kb + 2; younger than those are the y stores issued right after them
-    // and the DMAs and y stores of block kb + 3
+    // The loader's vector-memory operations per block: DMAs (C and B, x,
+    // and the next block's dt; one more, seq_idx, with packed sequences),
+    // y stores, and with the output gate the DMAs of the block's z into its
+    // y staging slots.  In block kb it issues the DMAs of block kb + 3, the
+    // y stores of block kb - 1, then the z DMAs of block kb + 3, and at its
+    // end waits until the DMAs of block kb + 2 have landed (everything older
+    // has landed too, the z of block kb + 1 among them).  Younger than the
+    // DMAs of block kb + 2 are the stores and z DMAs issued after them in
+    // block kb - 1 and all of block kb's operations.  Block 0 stores no y,
+    // so in block 1 the count is P_STORES smaller.
     static constexpr int P_LOADS = 2 * (MAT / 1024) + kBlk * XRB / 1024 + 1;
     static constexpr int P_STORES = kBlk * XRB / 1024;
-    static constexpr int P_WAIT = P_STORES + (NST - 3) * (P_LOADS + P_STORES);
-    // ... with the seq_idx DMA of packed sequences, one more load per block
-    static constexpr int P_WAIT_V = P_STORES + (NST - 3) * (P_LOADS + 1 + P_STORES);
-    static_assert(P_WAIT_V < 64, "vmcnt immediate");
+    static_assert(NST == 4, "the wait counts assume four stages");
+    static constexpr int wait_count(bool gate, bool varlen, bool block1) {
+        return 2 * P_STORES + (gate ? 2 * P_STORES : 0) + P_LOADS + (varlen ? 1 : 0) -
+               (block1 ? P_STORES : 0);
+    }
+    static_assert(wait_count(true, true, false) < 64, "vmcnt immediate");
 };
 
 // Column-blocked LDS layout of the staged C, B and x tiles (32 rows): the
@@ -285,15 +293,20 @@ __device__ __forceinline__ int col_of(int q) {
 //   x'        xs[kk] = x'[token 16 kk + 8 hi + j][pr] (the A fragment of
 //             the diagonal block and the B fragment of the state update,
 //             K-step kk).
-template <int PB>
+// Output variants (EPI): bit 0, D per (head, headdim column) instead of per
+// head; bit 1, the output gate y * silu(z).  EPI = 0 is the plain forward.
+constexpr int kEpiDhp = 1, kEpiGate = 2;
+
+template <int PB, int EPI>
 __global__ void __launch_bounds__(Fused<PB>::NT)
 k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
             const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const float *__restrict__ D, const float *init, float *final_state,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp,
-            const int *__restrict__ seq_idx) {
+            const int *__restrict__ seq_idx, const bf16 *__restrict__ z) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
+    constexpr bool DHP = (EPI & kEpiDhp) != 0, GATE = (EPI & kEpiGate) != 0;
     // Every LDS region that a DMA fills is its own object: the compiler can
     // then see that a DMA in flight never aliases the reads of another
     // region, and does not wait for it before those reads.
@@ -301,6 +314,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     __shared__ __align__(16) unsigned char stg1[S::STG];
     __shared__ __align__(16) unsigned char stg2[S::STG];
     __shared__ __align__(16) unsigned char stg3[S::NST > 3 ? S::STG : 16];
+    // D of the workgroup's columns when it is per (head, headdim column)
+    __shared__ __align__(16) float dsh[DHP ? PB : 4];
 
     const int HP = H * P, GN = G * N;
     // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8),
@@ -346,6 +361,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             (void *)(dt + (size_t)b * L * H), 0, (unsigned)((size_t)L * H * 4), kBufferWord3);
         const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
             y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+        // the gate z, like y (read once: non-temporal)
+        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
+            (void *)(GATE ? z + (size_t)b * L * HP : nullptr), 0, GATE ? L * HP * 2 : 0,
+            kBufferWord3);
         const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2, dt_step = kBlk * H * 4;
         typedef __attribute__((address_space(3))) void lds_void;
         // (the block's byte offset goes in the scalar offset, so a DMA
@@ -551,6 +570,27 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 __builtin_amdgcn_raw_buffer_store_b128(v, y_rsrc, py[i], yo, kNonTemporal);
             }
         };
+        // The gate's DMAs: z of block kb into the y staging rows of its stage,
+        // each 16-byte chunk in the slot that its y chunk will take (DMA i,
+        // lane l fills slot 64 i + l: row t = slot / XC and slot column
+        // slot % XC, which holds chunk (slot % XC) ^ ys_swz(t)).  Issued after
+        // the y stores that read those rows for block kb - 4.
+        unsigned pz[GATE ? S::P_STORES : 1];
+        if constexpr (GATE) {
+#pragma unroll
+            for (int i = 0; i < S::P_STORES; ++i) {
+                const int pos = 64 * i + lane, t = pos / S::XC;
+                const int c = (pos % S::XC) ^ ys_swz<S::XC>(t);
+                pz[i] = (t * HP + c0 + 8 * c) * 2;
+            }
+        }
+        auto zdma = [&](int kb, unsigned char *buf) {
+            if constexpr (GATE) {
+                const unsigned zo = kb * kBlk * HP * 2;
+#pragma unroll
+                for (int i = 0; i < S::P_STORES; ++i) bdma_nt(rz, pz[i], zo, buf + S::YS + 1024 * i);
+            }
+        };
         // Every wave takes the same barriers: two in the prologue (the DMAs
         // of blocks 0..2 landed; then the C B^T block of block 0 and the
         // records of blocks 0 and 1 formed), then one at the end of every
@@ -559,6 +599,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             pdt_dma(0, stage(0));
 #pragma unroll
             for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i), stage(i + 1));
+#pragma unroll
+            for (int i = 0; i < S::NST - 1; ++i) zdma(i, stage(i));
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             lds_barrier();
             lds_barrier();
@@ -569,10 +611,24 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             auto pblock = [&](int kb, const int si) {
                 pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
                 if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
-                if (varlen)
-                    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT_V));
-                else
-                    __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::P_WAIT));
+                // The z DMAs refill the staging rows that the y stores above
+                // read.  Each store waits for its LDS read, so DMAs issued after
+                // the stores cannot land first; nothing may be scheduled across
+                // this point (a DMA past the end returns zeros at once, and an
+                // early one would zero the y not yet read).
+                if constexpr (GATE) __builtin_amdgcn_sched_barrier(0);
+                zdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
+                if (kb == 1) {
+                    if (varlen)
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count(GATE, true, true)));
+                    else
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count(GATE, false, true)));
+                } else {
+                    if (varlen)
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count(GATE, true, false)));
+                    else
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count(GATE, false, false)));
+                }
                 lds_barrier();
             };
             for (int kb = 0; kb < nblk; kb += S::NST) {
@@ -628,7 +684,11 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     const int hw = cw / P, pw = cw - hw * P;   // its head and headdim column
     const int slot = (cw - c0) / (PB > P ? P : PB);  // its decay-record slot
     const size_t bh = (size_t)b * H + hw;
-    const float Dh = D ? D[hw] : 0.f;
+    const float Dh = !DHP && D ? D[hw] : 0.f;
+    if constexpr (DHP) {
+        // (published to the other waves by the prologue barriers)
+        if (lane < 32) dsh[32 * wave + lane] = D[cw + lane];
+    }
 
     // ---- per-lane LDS byte offsets (lane = 16 grp + a + 4 e for the
     // transposed reads, which act within each 16-lane group)
@@ -837,7 +897,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 for (int j = 0; j < 8; ++j) {
                     const int s = 16 * kk + 8 * hi + j, sj = 16 * kk + j;
                     const float w = (float)o.cbv[kk][j] * fast_exp(fminf(lr - v[S::LR + s], 0.f)) *
-                                        v[S::DT + s] + (sj == rhi ? Dh : 0.f);
+                                        v[S::DT + s] + (!DHP && sj == rhi ? Dh : 0.f);
                     wgt[j] = (bf16)(sj <= rhi && sj >= rlo ? w : 0.f);
                 }
                 acc = mma32(e.xs[kk], wgt, acc);
@@ -845,7 +905,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 o.cbv[kk] = zero_frag<bf16>();
             }
             f = 1.f;
-            dco = 0.f;
+            dco = 0.f;  // (per-head D went onto the diagonal; per-channel D stays)
             const float sd = sig_in * uniform(v[S::DELTA]);
 #pragma unroll
             for (int m = 0; m < 4; ++m) st[m] *= sd;
@@ -861,6 +921,14 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // with the reads of the next block's opening operands and the
         // epilogue (from the third chunk on, once the diagonal product has
         // landed)
+        f32x4 dcol[DHP ? 4 : 1];
+        if constexpr (DHP) {
+            // D of this lane's columns 8 hi + (0..7) and 16 + 8 hi + (0..7)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                dcol[i] = *reinterpret_cast<const f32x4 *>(dsh + 32 * wave + 16 * (i >> 1) +
+                                                           8 * hi + 4 * (i & 1));
+        }
 #pragma unroll
         for (int q = 0; q < 8; ++q) {
             const int kk = q >> 2, m = q & 3;
@@ -872,14 +940,27 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 // empty asm keeps them in this chunk)
 #pragma unroll
                 for (int vv = 0; vv < 16; ++vv)
-                    if (vv * 6 / 16 == q - 2)
-                        acc[vv] = acc[vv] * f + dco * (float)o.xr[vv >> 3][vv & 7];
+                    if (vv * 6 / 16 == q - 2) {
+                        const float dv = DHP ? dcol[vv >> 2][vv & 3] : dco;
+                        acc[vv] = acc[vv] * f + dv * (float)o.xr[vv >> 3][vv & 7];
+                    }
                 asm volatile("" : "+v"(acc));
             }
             __builtin_amdgcn_sched_barrier(0);
         }
         asm volatile("" : "+v"(acc));
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (GATE) {
+            // the gate: this lane's z chunks sit in the staging slots its y
+            // chunks will take (DMA'd by the loader three blocks ahead)
+#pragma unroll
+            for (int i = 0; i < 2; ++i) {
+                const bf16x8 zv = lds_b128(cur, ys_off[i]);
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[8 * i + j] *= silu_f32((float)zv[j]);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
         // y of the block to the loader through this stage's staging rows;
         // the barrier then also publishes it
         y_stage(cur, acc);
@@ -934,13 +1015,24 @@ template bool fused_supported<bf16>(int, int, int);
 
 int fused_nblk(int L) { return (L + kBlk - 1) / kBlk; }
 
+template <int PB, int EPI>
+static void launch_fused_epi(const ForwardArgs &a, hipStream_t stream) {
+    typedef Fused<PB> S;
+    hipLaunchKernelGGL((k_fused_ssd<PB, EPI>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0,
+                       stream, (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C,
+                       a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P,
+                       fused_nblk(a.L), a.dtp, a.seq_idx, (const bf16 *)a.z);
+}
+
 template <int PB>
 static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
-    typedef Fused<PB> S;
-    hipLaunchKernelGGL((k_fused_ssd<PB>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0, stream,
-                       (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C, a.D,
-                       a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, fused_nblk(a.L),
-                       a.dtp, a.seq_idx);
+    const int epi = (a.D_hdim && a.D ? kEpiDhp : 0) | (a.z ? kEpiGate : 0);
+    switch (epi) {
+        case kEpiDhp: launch_fused_epi<PB, kEpiDhp>(a, stream); break;
+        case kEpiGate: launch_fused_epi<PB, kEpiGate>(a, stream); break;
+        case kEpiDhp | kEpiGate: launch_fused_epi<PB, kEpiDhp | kEpiGate>(a, stream); break;
+        default: launch_fused_epi<PB, 0>(a, stream); break;
+    }
 }
 
 // Columns per workgroup.  One workgroup per compute unit is the target

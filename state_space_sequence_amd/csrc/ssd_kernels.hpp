@@ -36,6 +36,8 @@ struct ForwardArgs {
     int batch, L, H, G, P, N, Q, nchunks;
     DtProc dtp;      // dt preprocessing (off: dt is used as given)
     const int *seq_idx = nullptr;  // packed sequences [b][L] (fused path only), or null
+    const void *z = nullptr;       // output gate [b][L][H][P] (x's type), or null
+    bool D_hdim = false;           // D is [H][P] (else [H])
     // workspace regions shared by both forward paths
     float *acum_hi;  // [b][H][nc][Q]  fp32 part of the fp64 chunk prefix sums
     float *acum_lo;  // [b][H][nc][Q]  remainder: prefix = hi + lo
@@ -99,6 +101,8 @@ struct DecodeArgs {
     void *y;
     int batch, H, G, P, N;
     DtProc dtp;      // dt preprocessing (off: dt is used as given)
+    const void *z = nullptr;  // output gate [b][H][P] (x's type), or null
+    bool D_hdim = false;      // D is [H][P] (else [H])
 };
 
 template <typename T>

@@ -53,9 +53,7 @@ __device__ __forceinline__ void nstore8(float *p, const float (&v)[8]) {
     __builtin_nontemporal_store(f32x4{v[0], v[1], v[2], v[3]}, reinterpret_cast<f32x4 *>(p));
     __builtin_nontemporal_store(f32x4{v[4], v[5], v[6], v[7]}, reinterpret_cast<f32x4 *>(p + 4));
 }
-__device__ __forceinline__ float nsilu(float v) {
-    return v * __builtin_amdgcn_rcpf(1.f + __expf(-v));
-}
+__device__ __forceinline__ float nsilu(float v) { return silu_f32(v); }
 
 }  // namespace
 

@@ -283,7 +283,8 @@ k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
 //   acc  = C[l] . h_in^T                 (state-to-output, Eq. 23)
 //   acc *= exp(acum_l)
 //   acc += sum_{s<=l} CB[l,s] exp(acum_l - acum_s) dt_s x[s]   (Step 1)
-//   y    = acc + D x[l]
+//   y    = acc + D x[l]               (D per head, or per head and column)
+//   y   *= silu(z[l])                 (when gated)
 // The decay mask is applied with a select, so entries above the diagonal are
 // exactly 0 (the upper-triangle protection of the Kernel 5 page: the
 // exponent is never evaluated for s > l).  x is staged transposed in LDS,
@@ -294,7 +295,8 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
               const float *__restrict__ cb, const float *__restrict__ S,
               const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
               const float *__restrict__ dtT, const float *__restrict__ D,
-              T *__restrict__ y, int L, int H, int G, int P, int N, int nc, int Q) {
+              T *__restrict__ y, int L, int H, int G, int P, int N, int nc, int Q,
+              const T *__restrict__ z, int D_hdim) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SB = 64;
     constexpr int PITCH = SB + 16 / (int)sizeof(T);
@@ -389,13 +391,16 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
     for (int i = 0; i < 4; ++i) {
         const int l = l0 + 4 * q + i, t = c * Q + l;
         if (l >= Q || t >= L) continue;
-        T *yrow = y + (((size_t)b * L + t) * H + h) * P;
+        const size_t ro = (((size_t)b * L + t) * H + h) * P;
 #pragma unroll
         for (int pt = 0; pt < MAXPT; ++pt) {
             if (pt >= npt) continue;
             const int p = pt * 16 + r;
             const float xv = to_f32(XT[p * PITCH + (l - lb * SB)]);
-            yrow[p] = from_f32<T>(acc[pt][i] + Dh * xv);
+            const float dp = D_hdim && D ? D[(size_t)h * P + p] : Dh;
+            float o = acc[pt][i] + dp * xv;
+            if (z) o *= silu_f32(to_f32(z[ro + p]));
+            y[ro + p] = from_f32<T>(o);
         }
     }
 }
@@ -443,7 +448,8 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     const size_t k5_lds = (size_t)a.P * (64 + 16 / sizeof(T)) * sizeof(T);
     hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
                        stream, (const T *)a.x, (const T *)a.C, (const float *)a.cb, a.S, a.acum_hi,
-                       a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q);
+                       a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q,
+                       (const T *)a.z, a.D_hdim ? 1 : 0);
     if ((err = mark()) != hipSuccess) return err;
     return hipGetLastError();
 }

@@ -202,3 +202,16 @@ def make_seq_idx(batch, seqlen, seed=1234, max_len=96):
             out[r, t:t + n] = k
             t, k = t + n, k + 1
     return out
+
+
+def make_gate_inputs(batch, seqlen, nheads, headdim, io_dtype="bf16", seed=0):
+    """The output gate z ~ N(0, 1) ([b, L, H, P], rounded to the I/O dtype;
+    seqlen 0 gives the decode shape [b, H, P]) and a per-(head, column) D ~
+    U(0, 1) ([H, P] fp32), drawn in that order from PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    shape = (batch, nheads, headdim) if seqlen == 0 else (batch, seqlen, nheads, headdim)
+    z = rng.standard_normal(size=shape).astype(np.float32)
+    if io_dtype == "bf16":
+        z = round_to_bf16(z)
+    Dhp = rng.uniform(0.0, 1.0, size=(nheads, headdim)).astype(np.float32)
+    return {"z": z, "D_hp": Dhp}

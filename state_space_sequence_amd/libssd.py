@@ -54,6 +54,12 @@ class DtProc(ctypes.Structure):
                 ("dt_min", ctypes.c_float), ("dt_max", ctypes.c_float)]
 
 
+class Gate(ctypes.Structure):
+    """``ssd_gate`` of include/ssd.h: the output gate z (nullable) and
+    whether D is per (head, headdim column)."""
+    _fields_ = [("z", ctypes.c_void_p), ("D_per_channel", ctypes.c_int)]
+
+
 def load():
     """Load libssd.so (once).  Raises if it has not been built."""
     global _lib
@@ -86,6 +92,12 @@ def load():
         lib.ssd_chunk_scan_fwd_ex.argtypes = _FWD_ARGS + [ctypes.POINTER(DtProc)]
         lib.ssd_chunk_scan_fwd_varlen.restype = _i
         lib.ssd_chunk_scan_fwd_varlen.argtypes = _FWD_ARGS + [_p, ctypes.POINTER(DtProc)]
+        lib.ssd_chunk_scan_fwd_full.restype = _i
+        lib.ssd_chunk_scan_fwd_full.argtypes = _FWD_ARGS + [_p, ctypes.POINTER(DtProc),
+                                                             ctypes.POINTER(Gate)]
+        lib.ssd_state_update_full.restype = _i
+        lib.ssd_state_update_full.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p, ctypes.POINTER(DtProc),
+                                                                    ctypes.POINTER(Gate)]
         lib.ssd_state_update_ex.restype = _i
         lib.ssd_state_update_ex.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p, ctypes.POINTER(DtProc)]
         lib.ssd_causal_conv1d_fwd.restype = _i
@@ -162,8 +174,24 @@ def _dt_proc(dt_bias, dt_softplus, dt_limit, H, dev):
                   lo, hi)
 
 
+def _gate(z, D, like, H, P, dev):
+    """The ssd_gate struct for a gate z (shaped like ``like``) and a D of
+    shape [H] or [H, P], or None when neither is used."""
+    d2 = D is not None and D.dim() == 2
+    if D is not None and tuple(D.shape) not in ((H,), (H, P)):
+        raise ValueError("D must be [H] or [H, P]")
+    if z is None and not d2:
+        return None
+    if z is not None:
+        _check_dev("z", z, like.dtype, dev)
+        if tuple(z.shape) != tuple(like.shape):
+            raise ValueError("z must have x's shape")
+    return Gate(None if z is None else z.data_ptr(), 1 if d2 else 0)
+
+
 def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-             final_state, workspace, return_final_state, stream, dtp=None, seq_idx=None):
+             final_state, workspace, return_final_state, stream, dtp=None, seq_idx=None,
+             z=None):
     import torch
     lib = load()
     dev = x.device
@@ -185,8 +213,7 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
             tuple(B.shape) != (b, L, G, N) or tuple(C.shape) != (b, L, G, N):
         raise ValueError("inconsistent shapes x%s dt%s A%s B%s C%s" % (
             tuple(x.shape), tuple(dt.shape), tuple(A.shape), tuple(B.shape), tuple(C.shape)))
-    if D is not None and tuple(D.shape) != (H,):
-        raise ValueError("D must be [H]")
+    gate = _gate(z, D, x, H, P, dev)
     if initial_state is not None and tuple(initial_state.shape) != (b, H, P, N):
         raise ValueError("initial_state must be [b,H,P,N]")
     if y is None:
@@ -204,7 +231,18 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
     args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
             int(chunk_len), G, b, L, H, P, N, io, _ptr(y), _ptr(final_state),
             _ptr(workspace), _sz(workspace.numel()), _stream_handle(stream))
-    if seq_idx is not None:
+    if gate is not None:
+        if timed_events is not None:
+            raise ValueError("the timed forward takes no gate")
+        if seq_idx is not None:
+            _check_dev("seq_idx", seq_idx, torch.int32, dev)
+            if tuple(seq_idx.shape) != (b, L):
+                raise ValueError("seq_idx must be [b, L] int32")
+        st = lib.ssd_chunk_scan_fwd_full(*args, _ptr(seq_idx),
+                                         None if dtp is None else ctypes.byref(dtp),
+                                         ctypes.byref(gate))
+        where = "ssd_chunk_scan_fwd_full"
+    elif seq_idx is not None:
         if timed_events is not None:
             raise ValueError("the timed forward takes unpacked rows only")
         _check_dev("seq_idx", seq_idx, torch.int32, dev)
@@ -239,7 +277,7 @@ def _forward(timed_events, x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
 def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256,
                        ngroups=None, y=None, final_state=None, workspace=None,
                        return_final_state=True, stream=None, dt_bias=None,
-                       dt_softplus=False, dt_limit=None, seq_idx=None):
+                       dt_softplus=False, dt_limit=None, seq_idx=None, z=None):
     """Chunked SSD forward on the current (or given) torch stream.
 
     x [b,L,H,P] (fp32|bf16), dt [b,L,H] fp32, A [H] fp32, B/C [b,L,G,N] (x's
@@ -254,10 +292,14 @@ def ssd_chunk_scan_fwd(x, dt, A, B, C, D=None, initial_state=None, chunk_len=256
     `dt_softplus`, `dt_limit` arguments; ssd_chunk_scan_fwd_ex).
 
     seq_idx ([b, L] int32) packs several sequences per row: the state is
-    reset where it changes (ssd_chunk_scan_fwd_varlen)."""
+    reset where it changes (ssd_chunk_scan_fwd_varlen).
+
+    z (x's shape and dtype) gates the output, y = (C h + D x) silu(z), and D
+    may be [H, P] (per headdim column) as well as [H]
+    (ssd_chunk_scan_fwd_full)."""
     dtp = _dt_proc(dt_bias, dt_softplus, dt_limit, A.shape[0], x.device)
     return _forward(None, x, dt, A, B, C, D, initial_state, chunk_len, ngroups, y,
-                    final_state, workspace, return_final_state, stream, dtp, seq_idx)
+                    final_state, workspace, return_final_state, stream, dtp, seq_idx, z)
 
 
 def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
@@ -308,13 +350,14 @@ def ssd_chunk_scan_fwd_noalloc(x, dt, A, B, C, D, initial_state, chunk_len, y, f
 
 
 def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream=None,
-                     dt_bias=None, dt_softplus=False, dt_limit=None):
+                     dt_bias=None, dt_softplus=False, dt_limit=None, z=None):
     """One decode token, in place on ``state``.
 
     state [b,H,P,N] fp32, x [b,H,P] (fp32|bf16), dt [b,H] fp32, A [H],
-    B/C [b,G,N] (x's dtype), D [H] or None.  Returns y [b,H,P] in x's dtype.
-    dt_bias / dt_softplus / dt_limit: as in ssd_chunk_scan_fwd
-    (ssd_state_update_ex)."""
+    B/C [b,G,N] (x's dtype), D [H], [H, P] or None.  Returns y [b,H,P] in
+    x's dtype.  dt_bias / dt_softplus / dt_limit: as in ssd_chunk_scan_fwd
+    (ssd_state_update_ex); z (x's shape) gates the output
+    (ssd_state_update_full)."""
     import torch
     lib = load()
     dev = x.device
@@ -334,15 +377,18 @@ def ssd_state_update(state, x, dt, A, B, C, D=None, ngroups=None, y=None, stream
     if tuple(x.shape) != (b, H, P) or tuple(dt.shape) != (b, H) or tuple(A.shape) != (H,) \
             or tuple(B.shape) != (b, G, N) or tuple(C.shape) != (b, G, N):
         raise ValueError("inconsistent decode shapes")
-    if D is not None and tuple(D.shape) != (H,):
-        raise ValueError("D must be [H]")
+    gate = _gate(z, D, x, H, P, dev)
     if y is None:
         y = torch.empty_like(x)
     _check_dev("y", y, x.dtype, dev)
     args = (_ptr(state), _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), G, b, H, P,
             N, io, _ptr(y), _stream_handle(stream))
     dtp = _dt_proc(dt_bias, dt_softplus, dt_limit, H, dev)
-    if dtp is None:
+    if gate is not None:
+        st = lib.ssd_state_update_full(*args, None if dtp is None else ctypes.byref(dtp),
+                                       ctypes.byref(gate))
+        where = "ssd_state_update_full"
+    elif dtp is None:
         st, where = lib.ssd_state_update(*args), "ssd_state_update"
     else:
         st, where = lib.ssd_state_update_ex(*args, ctypes.byref(dtp)), "ssd_state_update_ex"

@@ -504,3 +504,84 @@ def test_varlen_sequences_do_not_interact(oracle_mod):
     yr, finr = oracle_mod.forward(*args)
     np.testing.assert_array_equal(yp, yr)
     np.testing.assert_array_equal(finp, finr)
+
+
+# ------------------------------------------------ output gate, per-channel D
+
+def test_silu_against_torch_and_identities():
+    """SiLU of the gate oracle against PyTorch's silu in fp64 on the CPU,
+    silu(0) = 0 and silu(v) - silu(-v) = v."""
+    import torch
+    from oracle.gate import silu
+    v = np.concatenate([np.linspace(-40, 40, 801), [-700.0, 700.0, 0.0]])
+    ref = torch.nn.functional.silu(torch.from_numpy(v)).numpy()
+    np.testing.assert_allclose(silu(v), ref, rtol=1e-15, atol=1e-300)
+    assert silu(0.0) == 0.0
+    np.testing.assert_allclose(silu(v) - silu(-v), v, rtol=1e-14, atol=1e-12)
+
+
+def test_per_channel_D_constant_over_columns_is_per_head_D(oracle_mod):
+    """A [H, P] D that repeats D_h over the columns gives exactly the plain
+    oracle, which applies the per-head D inside its C loop."""
+    from oracle.gate import forward_gated
+    inp = _rand(b=2, L=37, H=4, P=3, N=5, G=2, init=True, seed=71)
+    y, fin = _fwd(oracle_mod, inp)
+    Dhp = np.repeat(inp["D"][:, None], 3, axis=1)
+    yg, fing = forward_gated(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], Dhp, None,
+                             inp["initial_state"])
+    np.testing.assert_allclose(yg, y, rtol=1e-13, atol=1e-14)
+    np.testing.assert_array_equal(fing, fin)
+
+
+def test_gate_multiplies_the_whole_output(oracle_mod):
+    """z = 50 everywhere: silu(50) = 50 (1 - 2e-22), so the gated output is 50
+    times the plain one, the skip term included; z = 0 gives exactly 0.  The
+    gate applied before the skip term (a plausible mistake) fails it."""
+    from oracle.gate import forward_gated, skip
+    inp = _rand(b=1, L=29, H=2, P=4, N=3, G=1, init=True, seed=72)
+    y, fin = _fwd(oracle_mod, inp)
+    args = (inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"])
+    z50 = np.full(inp["x"].shape, 50.0)
+    yg, fing = forward_gated(*args, inp["D"], z50, inp["initial_state"])
+    np.testing.assert_allclose(yg, 50.0 * y, rtol=1e-14)
+    np.testing.assert_array_equal(fing, fin)
+    y0, _ = forward_gated(*args, inp["D"], np.zeros_like(z50), inp["initial_state"])
+    assert np.all(y0 == 0.0)
+    core, _ = forward_gated(*args, None, None, inp["initial_state"])
+    wrong = 50.0 * core + skip(inp["D"], inp["x"])
+    assert np.max(np.abs(wrong - yg)) > 1e-3 * np.max(np.abs(yg))
+
+
+def test_gated_decode_against_the_numpy_decode_step():
+    """One gated decode token with a per-channel D against the NumPy decode
+    step of the fla decode branch (per-head D = 0 there), plus D x, times
+    silu(z) from PyTorch."""
+    import torch
+    from oracle.forms import decode_step_numpy
+    from oracle.gate import state_update_gated
+    rng = np.random.default_rng(73)
+    b, H, P, N, G = 2, 4, 8, 16, 2
+    state = 0.1 * rng.standard_normal((b, H, P, N))
+    x = rng.standard_normal((b, H, P))
+    dt = rng.uniform(0.01, 0.2, (b, H))
+    A = -rng.uniform(1, 8, H)
+    B, C = rng.standard_normal((b, G, N)), rng.standard_normal((b, G, N))
+    Dhp = rng.uniform(0, 1, (H, P))
+    z = rng.standard_normal((b, H, P))
+    st, yg = state_update_gated(state, x, dt, A, B, C, Dhp, z)
+    st_ref, y_ref = decode_step_numpy(state, x, dt, A, B, C, None)
+    gate = torch.nn.functional.silu(torch.from_numpy(z)).numpy()
+    np.testing.assert_allclose(st, st_ref, rtol=1e-13, atol=1e-15)
+    np.testing.assert_allclose(yg, (y_ref + Dhp[None] * x) * gate, rtol=1e-12, atol=1e-14)
+
+
+def test_gate_magnitude_reference_bounds_the_output(oracle_mod):
+    from oracle.gate import forward_gated, forward_gated_abs
+    from state_space_sequence_amd.inputs import make_gate_inputs
+    inp = make_inputs(1, 64, 2, 16, 16, 1, io_dtype="f32", init_std=0.1, seed=74)
+    g = make_gate_inputs(1, 64, 2, 16, io_dtype="f32", seed=75)
+    args = (inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], g["D_hp"], g["z"],
+            inp["initial_state"])
+    y, _ = forward_gated(*args)
+    ya = forward_gated_abs(*args)
+    assert np.all(np.abs(y) <= ya * (1 + 1e-12))

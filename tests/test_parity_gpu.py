@@ -971,3 +971,138 @@ def test_nonfinite_check_decode_conv_norm(dev, monkeypatch):
         libssd.ssd_gated_rmsnorm_fwd(y, z, wn)
     assert ei.value.status == libssd.SSD_ERR_NONFINITE
     torch.cuda.synchronize()
+
+
+# ------------------------------------------------ output gate, per-channel D
+
+# (b, L, H, P, N, G, Q, io, z, per-channel D, extra); the head counts select
+# the fused pass's three workgroup layouts (32, 64, 128 columns)
+GATED = [
+    (2, 300, 4, 64, 128, 2, 64, "bf16", True, True, None),
+    (2, 300, 4, 64, 128, 2, 64, "f32", True, True, None),
+    (2, 333, 4, 64, 128, 1, 128, "bf16", True, False, None),
+    (2, 333, 4, 64, 128, 1, 128, "f32", False, True, None),
+    (2, 200, 132, 64, 128, 2, 64, "bf16", True, True, None),
+    (2, 300, 66, 64, 128, 1, 64, "bf16", True, False, None),
+    (2, 257, 3, 32, 64, 1, 64, "f32", True, True, None),
+    (1, 257, 4, 64, 128, 1, 64, "bf16", True, True, "dtproc"),
+    (2, 300, 4, 64, 128, 1, 64, "bf16", True, True, "varlen"),
+    (2, 200, 132, 64, 128, 2, 64, "bf16", True, True, "varlen"),
+    (2, 400, 4, 64, 128, 1, 64, "bf16", True, True, "decay"),
+    (2, 400, 4, 64, 128, 1, 64, "f32", False, True, "decay"),
+    (2, 400, 132, 64, 128, 1, 64, "bf16", False, True, "decay"),
+    (2, 400, 66, 64, 128, 1, 64, "bf16", True, True, "decay"),
+]
+
+
+@pytest.mark.parametrize("case", GATED, ids=lambda c: "b%d_L%d_H%d_P%d_N%d_G%d_Q%d_%s" % c[:8]
+                         + ("_z" if c[8] else "") + ("_Dhp" if c[9] else "")
+                         + ("_" + c[10] if c[10] else ""))
+def test_gate_and_per_channel_D(dev, oracle_mod, path, case):
+    """y = (C h + D (*) x) silu(z) with D per head or per (head, column),
+    against the gate oracle (oracle/gate.py): the gate alone, the per-column
+    D alone and both, with the time-step preprocessing, with packed
+    sequences (the fused pass), and through the exact and rescaled blocks of
+    the decay-regime inputs (where a per-head D rides on the diagonal
+    weights and a per-column one cannot)."""
+    import torch
+    from oracle.dt import process_dt
+    from oracle.gate import forward_gated, forward_gated_abs, silu, skip
+    from oracle.varlen import forward_varlen
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_gate_inputs, make_seq_idx, to_torch
+    b, L, H, P, N, G, Q, io, use_z, dhp, extra = case
+    _say("gate case %s path %s" % (case, path))
+    if extra == "decay":
+        inp = decay_regime_inputs(io, seed=95, H=H)
+    else:
+        inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=900 + L + H)
+    skip_if_path_unsupported(inp, io, Q)
+    if extra == "varlen" and path == "split":
+        pytest.skip("packed sequences run on the fused pass only")
+    g = make_gate_inputs(b, L, H, P, io_dtype=io, seed=901 + L)
+    z = g["z"] if use_z else None
+    D = g["D_hp"] if dhp else inp["D"]
+    t = to_torch(inp, io, dev)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    tz = None if z is None else torch.from_numpy(z).to(tdt).to(dev)
+    tD = torch.from_numpy(D).to(dev)
+    kw = dict(chunk_len=Q, z=tz)
+    dt_used, dt_arg = inp["dt"], t["dt"]
+    if extra == "dtproc":
+        kw.update(dt_bias=t["dt_bias"], dt_softplus=True)
+        dt_used, dt_arg = process_dt(inp["dt_raw"], inp["dt_bias"], True), t["dt_raw"]
+    seq = None
+    if extra == "varlen":
+        seq = make_seq_idx(b, L, seed=902 + L, max_len=60)
+        kw["seq_idx"] = torch.from_numpy(seq).to(dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(t["x"], dt_arg, t["A"], t["B"], t["C"], tD,
+                                       t["initial_state"], **kw)
+    torch.cuda.synchronize()
+    args = (inp["x"], dt_used, inp["A"], inp["B"], inp["C"], D, z, inp["initial_state"])
+    if seq is not None:
+        core, fr = forward_varlen(inp["x"], dt_used, inp["A"], inp["B"], inp["C"], None,
+                                  inp["initial_state"], seq)
+        yr = core + skip(D, inp["x"])
+        if z is not None:
+            yr = yr * silu(z)
+    else:
+        yr, fr = forward_gated(*args)
+    ya = forward_gated_abs(*args) if io == "f32" else None
+    check(y.float().cpu().numpy(), yr, io, "gated y", ya, tok_axis=1)
+    # the state is not gated: the plain bar on the final state
+    _, _, _, fa = reference(oracle_mod, dict(inp, dt=dt_used)) if io == "f32" else (0, 0, 0, None)
+    check(fin.cpu().numpy(), fr, io, "final_state", fa)
+
+
+@pytest.mark.parametrize("io", ["bf16", "f32"])
+def test_gated_decode_every_element(dev, oracle_mod, io):
+    """ssd_state_update with the gate and a per-column D, step by step,
+    against the gate oracle's decode step."""
+    import torch
+    from oracle.gate import state_update_gated
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_gate_inputs, to_torch
+    b, steps, H, P, N, G = 3, 5, 4, 64, 128, 2
+    inp = make_inputs(b, steps, H, P, N, G, io_dtype=io, init_std=0.1, seed=81)
+    t = to_torch(inp, io, dev)
+    tdt = torch.bfloat16 if io == "bf16" else torch.float32
+    Dhp = make_gate_inputs(b, 0, H, P, io_dtype=io, seed=82)["D_hp"]
+    zs = [make_gate_inputs(b, 0, H, P, io_dtype=io, seed=83 + s)["z"] for s in range(steps)]
+    tD = torch.from_numpy(Dhp).to(dev)
+    state = t["initial_state"].clone()
+    st_ref = inp["initial_state"].astype(np.float64)
+    for s in range(steps):
+        tz = torch.from_numpy(zs[s]).to(tdt).to(dev)
+        y = libssd.ssd_state_update(state, t["x"][:, s].contiguous(), t["dt"][:, s].contiguous(),
+                                    t["A"], t["B"][:, s].contiguous(), t["C"][:, s].contiguous(),
+                                    tD, z=tz)
+        torch.cuda.synchronize()
+        st_ref, yr = state_update_gated(st_ref, inp["x"][:, s], inp["dt"][:, s], inp["A"],
+                                        inp["B"][:, s], inp["C"][:, s], Dhp, zs[s])
+        err = metrics.normwise_err(y.float().cpu().numpy(), yr)
+        _say("  step %d gated y normwise %.3e" % (s, err))
+        assert err <= (2e-5 if io == "f32" else metrics.BF16_NORMWISE)
+    assert metrics.normwise_err(state.cpu().numpy(), st_ref) <= (2e-6 if io == "f32" else 2e-2)
+
+
+def test_gated_full_size_every_slice(dev, oracle_mod):
+    """The 2.7B-shape forward with the gate and a per-column D, on every
+    (batch, head) slice."""
+    import torch
+    from oracle.gate import forward_gated
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_gate_inputs, to_torch
+    w = WORKLOADS["mamba2_2p7b"]
+    inp = workload_inputs(w)
+    g = make_gate_inputs(w.batch, w.seqlen, w.nheads, w.headdim, io_dtype="bf16", seed=w.seed)
+    t = to_torch(inp, "bf16", dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"],
+                                       torch.from_numpy(g["D_hp"]).to(dev), t["initial_state"],
+                                       chunk_len=w.chunk_len,
+                                       z=torch.from_numpy(g["z"]).to(torch.bfloat16).to(dev))
+    torch.cuda.synchronize()
+    yr, fr = forward_gated(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], g["D_hp"], g["z"],
+                           inp["initial_state"])
+    check_every_slice(y.float().cpu().numpy(), fin.cpu().numpy(), yr, fr, "bf16",
+                      "gated full size")
