@@ -26,8 +26,11 @@
  *  - dt is the processed time step (already non-negative: bias, softplus
  *    and any clamp are applied by the caller), except in the `_ex` entry
  *    points, which apply that processing themselves (see ssd_dt_proc).  A is
- *    the per-head decay rate (the method expects A < 0; any finite value is
- *    accepted).
+ *    the per-head decay rate and must be <= 0: the layer stores it as
+ *    A = -exp(A_log) (fla Mamba2 page, the mixer's A_log parameter), so every
+ *    factor exp(dt A) is a decay in (0, 1].  A > 0 is outside the method; the
+ *    forward's factored decays then overflow, and its outputs are undefined
+ *    (no error is reported: A stays on the device, unread by the host).
  *  - x, B, C and y share one element type, `io_dtype` (fp32 or bf16).
  *    dt, A, D and every state are fp32.  Accumulation is fp32.
  *  - The caller owns every buffer.  The library allocates no device memory,

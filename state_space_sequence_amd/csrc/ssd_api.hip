@@ -110,14 +110,17 @@ ssd_status check_dt_proc(const ssd_dt_proc *p, ssd::DtProc *out) {
 // kernels otherwise.  SSD_FORWARD_PATH=split|fused overrides the choice (a
 // diagnostic switch for comparing the two); forcing "fused" on a shape it
 // does not cover is reported as unsupported.
-ssd_status choose_path(int seqlen, int nheads, int ngroups, int headdim, int dstate,
+ssd_status choose_path(int /*seqlen*/, int nheads, int ngroups, int headdim, int dstate,
                        int chunk_len, ssd_dtype io, ssd::Path *out) {
-    // the fused kernel addresses one batch's rows of x, y, B and C with 32-bit
-    // byte offsets, including the prefetches up to three blocks past the end
-    const size_t row = (size_t)nheads * headdim > (size_t)ngroups * dstate
-                           ? (size_t)nheads * headdim
-                           : (size_t)ngroups * dstate;
-    const bool fits = ((size_t)seqlen + 128) * row * 2 < ((size_t)1 << 31);
+    // the fused kernel addresses a batch row with 32-bit offsets from
+    // resources rebased every window of blocks: any length fits as long as a
+    // window holds a few blocks of the widest stream
+    size_t row = (size_t)nheads * headdim > (size_t)ngroups * dstate
+                     ? (size_t)nheads * headdim
+                     : (size_t)ngroups * dstate;
+    row *= 2;
+    if ((size_t)nheads * 4 > row) row = (size_t)nheads * 4;
+    const bool fits = ssd::fused_row_fits(row);
     const bool fused_ok = fits && (io == SSD_BF16
                               ? ssd::fused_supported<ssd::bf16>(headdim, dstate, chunk_len)
                               : ssd::fused_supported<float>(headdim, dstate, chunk_len));

@@ -247,6 +247,41 @@ __device__ __forceinline__ int blk_off(int t, int c) {
 template <int XC>
 __device__ __forceinline__ int ys_swz(int t) { return (t / (16 / XC)) & (XC - 1); }
 
+// A buffer resource over one stream of a batch row (x, y, z, C, B, dt,
+// seq_idx), rebased every 2^shift blocks: buffer offsets are 32 bits, and a
+// long sequence at a wide row has more than 2^31 bytes.  The resource covers
+// the bytes from the start of block k's window to the end of the stream
+// (clamped to 2^32 - 1), so rows past the end still read as zeros and their
+// stores are dropped; at(k) rebuilds it only when k enters another window
+// (a compare and a branch otherwise) and gives block k's offset in it.
+struct WinRsrc {
+    const char *row0;
+    size_t total;
+    unsigned blk_bytes;
+    int shift, w;
+    __amdgpu_buffer_rsrc_t r;
+    __device__ void init(const void *p, size_t total_bytes, unsigned blk, int sh) {
+        row0 = static_cast<const char *>(p);
+        total = total_bytes;
+        blk_bytes = blk;
+        shift = sh;
+        w = -1;
+    }
+    __device__ __forceinline__ const __amdgpu_buffer_rsrc_t &at(int k, unsigned &soff) {
+        const int kw = k >> shift;
+        if (kw != w) {
+            w = kw;
+            const size_t base = ((size_t)kw << shift) * blk_bytes;
+            const size_t rem = total > base ? total - base : 0;
+            r = __builtin_amdgcn_make_buffer_rsrc((void *)(row0 + base), 0,
+                                                  (unsigned)(rem < 0xFFFFFFFFull ? rem : 0xFFFFFFFFull),
+                                                  kBufferWord3);
+        }
+        soff = (unsigned)(k - (kw << shift)) * blk_bytes;
+        return r;
+    }
+};
+
 // Workgroup barrier for LDS only: this wave's LDS reads and writes complete
 // (lgkmcnt(0)), then s_barrier; the asm "memory" clobber keeps the compiler
 // from moving memory accesses across it.  __syncthreads() (or an LDS-scope
@@ -303,7 +338,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
             const float *__restrict__ D, const float *init, float *final_state,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp,
-            const int *__restrict__ seq_idx, const bf16 *__restrict__ z) {
+            const int *__restrict__ seq_idx, const bf16 *__restrict__ z, int win_shift) {
     typedef Fused<PB> S;
     constexpr int NW = S::NW, N = S::N;
     constexpr bool DHP = (EPI & kEpiDhp) != 0, GATE = (EPI & kEpiGate) != 0;
@@ -342,30 +377,29 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     if (wave >= NW) {
         // ---- the loader (wave NW): every DMA of the stages and every y
         // store; the former (wave NW + 1): the records and C B^T blocks.
-        // Buffer resources over the workgroup's slices of C, B, x, the C B^T
-        // blocks, the decay records and y, built once; a block adds its byte
-        // offset to fixed per-lane offsets.  Rows past the end of the
-        // sequence (the ragged tail, and the prefetches past the last block)
-        // fall outside a resource's range: the hardware reads them as zeros
-        // and drops such stores.
-        const __amdgpu_buffer_rsrc_t rc = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Cm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(Bm + (size_t)b * L * GN + (size_t)g * N), 0, (L * GN - g * N) * 2, kBufferWord3);
-        const __amdgpu_buffer_rsrc_t rx = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(x + (size_t)b * L * HP + c0), 0, (L * HP - c0) * 2, kBufferWord3);
+        // Buffer resources over the workgroup's slices of C, B, x, dt, y and
+        // z (WinRsrc: rebased every 2^win_shift blocks, once per window in
+        // practice); a block adds its byte offset to fixed per-lane offsets.
+        // Rows past the end of the sequence (the ragged tail, and the
+        // prefetches past the last block) fall outside a resource's range:
+        // the hardware reads them as zeros and drops such stores.  The DMAs
+        // of a block, its dt and its y stores are issued at different times,
+        // so each has its own resource.
+        const size_t Lz = (size_t)L;
+        WinRsrc wc, wb, wx, wdt, wy, wz, wseq;
+        wc.init(Cm + (size_t)b * Lz * GN + (size_t)g * N, (Lz * GN - g * N) * 2, kBlk * GN * 2,
+                win_shift);
+        wb.init(Bm + (size_t)b * Lz * GN + (size_t)g * N, (Lz * GN - g * N) * 2, kBlk * GN * 2,
+                win_shift);
+        wx.init(x + (size_t)b * Lz * HP + c0, (Lz * HP - c0) * 2, kBlk * HP * 2, win_shift);
         // dt of this batch; lane l of the dt DMA reads token l % 32 of head
         // h0 + l / 32 (heads past the workgroup's are read and not used)
         const int h0 = c0 / P;
-        const __amdgpu_buffer_rsrc_t rdt = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(dt + (size_t)b * L * H), 0, (unsigned)((size_t)L * H * 4), kBufferWord3);
-        const __amdgpu_buffer_rsrc_t y_rsrc = __builtin_amdgcn_make_buffer_rsrc(
-            y + (size_t)b * L * HP, 0, L * HP * 2, kBufferWord3);
+        wdt.init(dt + (size_t)b * Lz * H, Lz * H * 4, kBlk * H * 4, win_shift);
+        wy.init(y + (size_t)b * Lz * HP, Lz * HP * 2, kBlk * HP * 2, win_shift);
         // the gate z, like y (read once: non-temporal)
-        const __amdgpu_buffer_rsrc_t rz = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(GATE ? z + (size_t)b * L * HP : nullptr), 0, GATE ? L * HP * 2 : 0,
-            kBufferWord3);
-        const unsigned cb_step = kBlk * GN * 2, x_step = kBlk * HP * 2, dt_step = kBlk * H * 4;
+        wz.init(GATE ? z + (size_t)b * Lz * HP : nullptr, GATE ? Lz * HP * 2 : 0, kBlk * HP * 2,
+                win_shift);
         typedef __attribute__((address_space(3))) void lds_void;
         // (the block's byte offset goes in the scalar offset, so a DMA
         // costs no vector instruction).  y is written once and never read
@@ -386,9 +420,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // packed sequences: seq_idx of this batch, token lane % 32 into both
         // halves of the stage's SEQ region
         const bool varlen = seq_idx != nullptr;
-        const __amdgpu_buffer_rsrc_t rseq = __builtin_amdgcn_make_buffer_rsrc(
-            (void *)(varlen ? seq_idx + (size_t)b * L : nullptr), 0, varlen ? L * 4 : 0,
-            kBufferWord3);
+        wseq.init(varlen ? seq_idx + (size_t)b * Lz : nullptr, varlen ? Lz * 4 : 0, kBlk * 4,
+                  win_shift);
         // Per-lane offsets.  DMA i fills the 1 KB at 1024 i of a
         // column-blocked tile: column block i / 2, rows 16 (i % 2) + lane / 4,
         // slot lane % 4 (so chunk 4 (i / 2) + ((lane % 4) ^ ((t / 4) % 4)) of
@@ -408,20 +441,27 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         }
         // dt of block kb into `buf` (the stage of block kb)
         auto pdt_dma = [&](int kb, unsigned char *buf) {
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_void *)(buf + S::DTR), 4, pdt,
-                                                     kb * dt_step, 0, 0);
-            if (varlen)
+            unsigned so;
+            const __amdgpu_buffer_rsrc_t &rdt = wdt.at(kb, so);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rdt, (lds_void *)(buf + S::DTR), 4, pdt, so,
+                                                     0, 0);
+            if (varlen) {
+                const __amdgpu_buffer_rsrc_t &rseq = wseq.at(kb, so);
                 __builtin_amdgcn_raw_ptr_buffer_load_lds(rseq, (lds_void *)(buf + S::SEQ), 4,
-                                                         (lane & 31) * 4, kb * kBlk * 4, 0, 0);
+                                                         (lane & 31) * 4, so, 0, 0);
+            }
         };
         // the DMAs of block kb into `buf`, and the dt of block kb + 1 into
         // `nbuf` (the stage of block kb + 1)
         auto pdma = [&](int kb, unsigned char *buf, unsigned char *nbuf) {
-            const unsigned cbo = kb * cb_step, xo = kb * x_step;
+            unsigned cbo, bo, xo;
+            const __amdgpu_buffer_rsrc_t &rc = wc.at(kb, cbo);
+            const __amdgpu_buffer_rsrc_t &rb = wb.at(kb, bo);
+            const __amdgpu_buffer_rsrc_t &rx = wx.at(kb, xo);
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
                 bdma(rc, pcb[i], cbo, buf + S::CS + 1024 * i);
-                bdma(rb, pcb[i], cbo, buf + S::BS + 1024 * i);
+                bdma(rb, pcb[i], bo, buf + S::BS + 1024 * i);
             }
             if (x_nt) {
 #pragma unroll
@@ -563,7 +603,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             pys[i] = S::YS + t * S::XRB + 16 * (c ^ ys_swz<S::XC>(t));
         }
         auto pstore = [&](int kb, const unsigned char *buf) {
-            const unsigned yo = kb * kBlk * HP * 2;
+            unsigned yo;
+            const __amdgpu_buffer_rsrc_t &y_rsrc = wy.at(kb, yo);
 #pragma unroll
             for (int i = 0; i < S::P_STORES; ++i) {
                 const u32x4 v = *reinterpret_cast<const u32x4 *>(buf + pys[i]);
@@ -586,7 +627,8 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         }
         auto zdma = [&](int kb, unsigned char *buf) {
             if constexpr (GATE) {
-                const unsigned zo = kb * kBlk * HP * 2;
+                unsigned zo;
+                const __amdgpu_buffer_rsrc_t &rz = wz.at(kb, zo);
 #pragma unroll
                 for (int i = 0; i < S::P_STORES; ++i) bdma_nt(rz, pz[i], zo, buf + S::YS + 1024 * i);
             }
@@ -1015,13 +1057,36 @@ template bool fused_supported<bf16>(int, int, int);
 
 int fused_nblk(int L) { return (L + kBlk - 1) / kBlk; }
 
+// The loader's buffer resources are rebased every 2^shift blocks: the
+// largest window whose offsets (block offset + a block's rows) stay under
+// 2^31 bytes on the widest stream.  SSD_FUSED_WINDOW_SHIFT forces a smaller
+// window (a diagnostic: the tests cross many window boundaries with it).
+static int window_shift_for(size_t row_bytes) {
+    int s = 0;
+    while (s < 24 && (((size_t)1 << (s + 1)) + 1) * kBlk * row_bytes < ((size_t)1 << 31)) ++s;
+    return s;
+}
+int fused_window_shift(const ForwardArgs &a) {
+    size_t row = (size_t)a.H * a.P * 2;
+    row = row > (size_t)a.G * a.N * 2 ? row : (size_t)a.G * a.N * 2;
+    row = row > (size_t)a.H * 4 ? row : (size_t)a.H * 4;
+    int s = window_shift_for(row);
+    if (const char *e = getenv("SSD_FUSED_WINDOW_SHIFT")) {
+        const int f = atoi(e);
+        if (f >= 2 && f < s) s = f;
+    }
+    return s;
+}
+bool fused_row_fits(size_t row_bytes) { return window_shift_for(row_bytes) >= 3; }
+
 template <int PB, int EPI>
 static void launch_fused_epi(const ForwardArgs &a, hipStream_t stream) {
     typedef Fused<PB> S;
     hipLaunchKernelGGL((k_fused_ssd<PB, EPI>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0,
                        stream, (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C,
                        a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P,
-                       fused_nblk(a.L), a.dtp, a.seq_idx, (const bf16 *)a.z);
+                       fused_nblk(a.L), a.dtp, a.seq_idx, (const bf16 *)a.z,
+                       fused_window_shift(a));
 }
 
 template <int PB>

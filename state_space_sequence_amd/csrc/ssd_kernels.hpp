@@ -84,6 +84,11 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream,
 template <typename T> bool fused_supported(int P, int N, int Q);
 // The number of 32-token blocks of the fused path for L tokens.
 int fused_nblk(int L);
+// log2 of the blocks per rebasing window of the fused loader's resources,
+// and whether a row of `row_bytes` (the widest stream) leaves a window of
+// at least 8 blocks.
+int fused_window_shift(const ForwardArgs &a);
+bool fused_row_fits(size_t row_bytes);
 
 // k1 of the split path.
 void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float *acum_hi,

@@ -1106,3 +1106,108 @@ def test_gated_full_size_every_slice(dev, oracle_mod):
                            inp["initial_state"])
     check_every_slice(y.float().cpu().numpy(), fin.cpu().numpy(), yr, fr, "bf16",
                       "gated full size")
+
+
+# bf16 cases of the gate test (the fused pass is bf16) that cross the
+# windows below: plain, gated, per-column D, two- and four-wave workgroups,
+# packed sequences, the time-step preprocessing and the decay regimes
+WINDOW_CASES = [c for i, c in enumerate(GATED) if i in (0, 2, 4, 5, 7, 8, 9, 10, 12)]
+
+
+@pytest.mark.parametrize("case", WINDOW_CASES, ids=lambda c: "b%d_L%d_H%d_Q%d" % (c[0], c[1], c[2], c[6])
+                         + ("_z" if c[8] else "") + ("_Dhp" if c[9] else "")
+                         + ("_" + c[10] if c[10] else ""))
+def test_fused_resources_rebased_every_four_blocks(dev, oracle_mod, monkeypatch, case):
+    """The fused pass's loader addresses each stream (x, B, C, dt, y, z,
+    sequence labels) with 32-bit offsets from a buffer resource that it moves
+    forward every window of blocks.  Forcing the window down to 4 blocks
+    (128 tokens) makes these 200-400-token problems cross one to three window
+    boundaries, with the prefetches three blocks ahead and the y stores one
+    behind in different windows; every element against the oracle."""
+    monkeypatch.setenv("SSD_FUSED_WINDOW_SHIFT", "2")
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    test_gate_and_per_channel_D(dev, oracle_mod, "fused", case)
+
+
+def test_long_sequence_fused_sampled_heads(dev, oracle_mod, monkeypatch):
+    """One 262,144-token sequence at the 2.7B layer shape (80 heads of 64
+    columns, one group of 128 states, chunk 256, bf16, an initial state).
+    A row of x is 2.7 GB, past what a 32-bit buffer offset reaches, so the
+    fused pass's loader moves its resources forward three times along the
+    row (every 2048 blocks).  Sixteen head slices, the first and last heads
+    among them, against the serial oracle: every 32-token block of y and the
+    final states."""
+    import torch
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    L, H, P, N = 262144, 80, 64, 128
+    _say("long sequence b1 L%d H%d: drawing inputs" % (L, H))
+    inp = make_inputs(1, L, H, P, N, 1, io_dtype="bf16", init_std=0.1, seed=1239)
+    assert L * H * P * 2 > 2 ** 31
+    _say("  forward on the fused pass")
+    y, fin = gpu_forward(inp, "bf16", 256, dev)
+    rng = np.random.default_rng(1240)
+    hs = sorted({0, 1, 39, 40, H - 2, H - 1} | set(int(v) for v in rng.choice(H, 10, replace=False)))
+    while len(hs) < 16:
+        hs = sorted(set(hs) | {int(rng.integers(H))})
+    _say("  oracle on heads %s" % hs)
+    yr, fr = oracle_mod.forward(inp["x"][:, :, hs], inp["dt"][:, :, hs], inp["A"][hs],
+                                inp["B"], inp["C"], inp["D"][hs], inp["initial_state"][:, hs])
+    yg = np.ascontiguousarray(y[:, :, hs])
+    del y
+    check(yg, yr, "bf16", "long y (16 heads)", tok_axis=1)
+    check(fin[:, hs], fr, "bf16", "long final (16 heads)")
+    # the last window's blocks and the tail on their own
+    check(yg[:, -2048:], yr[:, -2048:], "bf16", "long y, last 2048 tokens", tok_axis=1)
+
+
+@pytest.mark.parametrize("shift", [None, "2"], ids=["natural_window", "four_block_window"])
+def test_fused_reads_and_writes_nothing_past_the_end(dev, oracle_mod, monkeypatch, shift):
+    """A ragged one-row problem (300 tokens: 9 blocks and 12 tokens) whose
+    inputs x, dt, B, C, z and the sequence labels are each the head of a
+    buffer 256 tokens longer, the rest NaN (labels: a new sequence on every
+    token), and whose y is the head of one whose rest holds a sentinel.  The
+    fused pass's loader prefetches up to three blocks past the last one and
+    stores the last block whole: the resources' ranges must turn those rows
+    into zeros and dropped stores.  A NaN read would reach the final state;
+    a stray store would change the sentinel."""
+    import torch
+    from oracle.gate import silu, skip
+    from oracle.varlen import forward_varlen
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_gate_inputs, make_seq_idx, to_torch
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    if shift:
+        monkeypatch.setenv("SSD_FUSED_WINDOW_SHIFT", shift)
+    L, H, P, N, pad = 300, 4, 64, 128, 256
+    inp = make_inputs(1, L, H, P, N, 1, io_dtype="bf16", init_std=0.1, seed=1301)
+    g = make_gate_inputs(1, L, H, P, io_dtype="bf16", seed=1302)
+    seq = make_seq_idx(1, L, seed=1303, max_len=90)
+    t = to_torch(inp, "bf16", dev)
+
+    def guarded(v, fill):
+        full = torch.full((v.shape[0], L + pad) + tuple(v.shape[2:]), fill, dtype=v.dtype,
+                          device=dev)
+        full[:, :L] = v
+        view = full[:, :L]
+        assert view.is_contiguous()
+        return full, view
+
+    _, xv = guarded(t["x"], float("nan"))
+    _, dtv = guarded(t["dt"], float("nan"))
+    _, bv = guarded(t["B"], float("nan"))
+    _, cv = guarded(t["C"], float("nan"))
+    _, zv = guarded(torch.from_numpy(g["z"]).to(torch.bfloat16).to(dev), float("nan"))
+    sfull = torch.arange(L + pad, dtype=torch.int32, device=dev)[None] + 1000
+    sfull[:, :L] = torch.from_numpy(seq).to(dev)
+    sv = sfull[:, :L]
+    yfull = torch.full((1, L + pad, H, P), 7.0, dtype=torch.bfloat16, device=dev)
+    y, fin = libssd.ssd_chunk_scan_fwd(xv, dtv, t["A"], bv, cv, t["D"], t["initial_state"],
+                                       chunk_len=64, y=yfull[:, :L], seq_idx=sv, z=zv)
+    torch.cuda.synchronize()
+    assert y.data_ptr() == yfull.data_ptr()
+    assert bool((yfull[:, L:] == 7.0).all()), "a store landed past the end of y"
+    core, fr = forward_varlen(inp["x"], inp["dt"], inp["A"], inp["B"], inp["C"], None,
+                              inp["initial_state"], seq)
+    yr = (core + skip(inp["D"], inp["x"])) * silu(g["z"])
+    check(y.float().cpu().numpy(), yr, "bf16", "guarded y", tok_axis=1)
+    check(fin.cpu().numpy(), fr, "bf16", "guarded final state")
