@@ -716,7 +716,7 @@ def main():
     peaks = measure_peaks(dev, ev)
     extra, fwd_ms = {}, {}
     if not args.no_extra:
-        for name in ("tiny_f32", "mamba2_130m", "grouped_g8"):
+        for name in ("tiny_f32", "mamba2_130m", "mamba2_130m_f32", "grouped_g8"):
             wx = WORKLOADS[name]
             # the tiny forward takes microseconds: 50 per captured graph
             reps, per_graph = (20, 50) if name == "tiny_f32" else (100, 1)
@@ -829,7 +829,8 @@ def main():
         out["cpu_baseline"] = cpu_baseline(w, r["inputs"])
     # per-workload table (every workload timed in this run)
     table = {}
-    for name in ("tiny_f32", "mamba2_130m", "mamba2_2p7b", "grouped_g8", "decode_b256"):
+    for name in ("tiny_f32", "mamba2_130m", "mamba2_130m_f32", "mamba2_2p7b", "grouped_g8",
+                 "decode_b256"):
         if name not in fwd_ms:
             continue
         wx = WORKLOADS[name]

@@ -287,10 +287,10 @@ ssd_status ssd_chunk_scan_fwd_ex(const void *x, const float *dt, const float *A,
  * t-1's starts a new sequence: the state entering it is zero, so no output
  * or state depends on an earlier sequence.  initial_state enters the row's
  * first sequence; final_state is that of the row's last token.  Otherwise
- * as ssd_chunk_scan_fwd_ex (dt_proc may be NULL).  Only the fused pass
- * handles it (bf16 io, dstate 128, headdim a multiple of 32); other shapes,
- * and the split path when forced, return SSD_ERR_UNSUPPORTED; a NULL seq_idx
- * is SSD_ERR_INVALID_ARGUMENT.
+ * as ssd_chunk_scan_fwd_ex (dt_proc may be NULL).  Both forward paths take
+ * it, every io type and supported shape; the workspace is the same as for
+ * ssd_chunk_scan_fwd.  A NULL or misaligned seq_idx is
+ * SSD_ERR_INVALID_ARGUMENT.
  */
 ssd_status ssd_chunk_scan_fwd_varlen(const void *x, const float *dt, const float *A,
                                      const void *B, const void *C, const float *D,
@@ -335,9 +335,8 @@ typedef struct ssd_gate {
  * sequences (seq_idx, as ssd_chunk_scan_fwd_varlen; NULL = one sequence per
  * row), the time-step preprocessing (dt_proc, as ssd_chunk_scan_fwd_ex; NULL =
  * dt as given) and the gate and per-channel D (gate; NULL = neither).  With
- * all three NULL it is ssd_chunk_scan_fwd.  Both forward paths take the gate
- * and per-channel D; packed sequences need the fused pass (see
- * ssd_chunk_scan_fwd_varlen).
+ * all three NULL it is ssd_chunk_scan_fwd.  Both forward paths take all
+ * three.
  */
 ssd_status ssd_chunk_scan_fwd_full(const void *x, const float *dt, const float *A,
                                    const void *B, const void *C, const float *D,

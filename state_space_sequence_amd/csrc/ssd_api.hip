@@ -174,7 +174,7 @@ class FiniteCheck {
 };
 
 struct Layout {
-    size_t acum_hi, acum_lo, dtT, cb, S, total;
+    size_t acum_hi, acum_lo, dtT, cb, S, segst, total;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -191,10 +191,13 @@ Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate
         l.dtT = l.acum_lo + vec;
         l.cb = l.dtT + vec;
         l.S = l.cb + round_up(b * nc * G * Q * Q * sizeof(float));
-        l.total = l.S + round_up(b * nc * H * P * N * sizeof(float));
+        // (the packed-sequence starts: always reserved, so the size does
+        // not depend on whether a call passes seq_idx)
+        l.segst = l.S + round_up(b * nc * H * P * N * sizeof(float));
+        l.total = l.segst + round_up(b * nc * Q * sizeof(int));
     } else {
         // the fused kernel keeps every intermediate on chip
-        l.acum_hi = l.acum_lo = l.dtT = l.cb = l.S = 0;
+        l.acum_hi = l.acum_lo = l.dtT = l.cb = l.S = l.segst = 0;
         l.total = 0;
     }
     return l;
@@ -226,9 +229,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     if (z && !aligned(z, 16)) return SSD_ERR_INVALID_ARGUMENT;
     ssd::Path path;
     if ((st = choose_path(seqlen, nheads, ngroups, headdim, dstate, chunk_len, io_dtype, &path)) != SSD_OK) return st;
-    // packed sequences are handled by the fused pass only
-    if (seq_idx && (path != ssd::Path::Fused || !aligned(seq_idx, 4)))
-        return path != ssd::Path::Fused ? SSD_ERR_UNSUPPORTED : SSD_ERR_INVALID_ARGUMENT;
+    if (seq_idx && !aligned(seq_idx, 4)) return SSD_ERR_INVALID_ARGUMENT;
     const Layout lay = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
                                       chunk_len, io_dtype, path);
     if (noalloc) {
@@ -274,6 +275,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.dtT = split ? reinterpret_cast<float *>(ws + lay.dtT) : nullptr;
     a.cb = split ? ws + lay.cb : nullptr;
     a.S = split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
+    a.segst = split ? reinterpret_cast<int *>(ws + lay.segst) : nullptr;
 
     const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::kFusedKernels;
     const char *const *kn =

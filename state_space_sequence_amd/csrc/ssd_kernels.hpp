@@ -35,7 +35,7 @@ struct ForwardArgs {
     float *final_state;  // may be null
     int batch, L, H, G, P, N, Q, nchunks;
     DtProc dtp;      // dt preprocessing (off: dt is used as given)
-    const int *seq_idx = nullptr;  // packed sequences [b][L] (fused path only), or null
+    const int *seq_idx = nullptr;  // packed sequences [b][L], or null
     const void *z = nullptr;       // output gate [b][L][H][P] (x's type), or null
     bool D_hdim = false;           // D is [H][P] (else [H])
     // workspace regions shared by both forward paths
@@ -44,6 +44,7 @@ struct ForwardArgs {
     float *dtT;      // [b][H][nc][Q]  dt per chunk, 0 past seqlen
     void *cb;        // split path: C B^T per chunk and group, fp32 [b][nc][G][Q][Q]
     float *S;        // split path: chunk states [b][nc][H][P][N]
+    int *segst;      // split path, packed sequences: last start per token [b][nc][Q]
                      // (acum_hi / acum_lo / dtT unused there)
 };
 
@@ -93,7 +94,7 @@ bool fused_row_fits(size_t row_bytes);
 // k1 of the split path.
 void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float *acum_hi,
                       float *acum_lo, float *dtT, int batch, int L, int H, int nc, int Q,
-                      hipStream_t stream);
+                      hipStream_t stream, const int *seq_idx = nullptr, int *segst = nullptr);
 
 struct DecodeArgs {
     float *state;

@@ -20,6 +20,18 @@
 //   cb   [b][nc][G][Q][Q] C B^T of the chunk (only s-tiles <= l-tile written)
 //   S    [b][nc][H][P][N] chunk states, overwritten by k4 with the state
 //                         entering each chunk
+//   segst [b][nc][Q] int32 packed sequences only: for each token, its
+//                         position in the chunk of the last sequence start at
+//                         or before it in that chunk (-1: none)
+//
+// Packed sequences (seq_idx, as the fla layer's `mamba_chunk_scan_combined`
+// takes it): token t > 0 whose label differs from token t - 1's starts a new
+// sequence, and the state entering it is zero.  In the chunked form a start
+// at position st of a chunk cuts every decay path that crosses it: the
+// intra-chunk weights keep sources s >= segst[l] only, the entering state
+// reaches only the rows before the chunk's first start, the chunk's own state
+// collects only its last sequence (s >= segst[Q - 1]), and a chunk with a
+// start passes nothing of the state entering it on (decay 0 in k4).
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
 
@@ -37,13 +49,33 @@ namespace ssd {
 // absolutely, which is the instability the stable segment sum of the fla
 // layer (`segment_sum`) avoids.  (hi_l - hi_s) + (lo_l - lo_s) is accurate to
 // a few ulps of the difference itself.
+//
+// With packed sequences the blocks of the first head group also write the
+// chunk's segst row: the start flags, then an inclusive max-scan of their
+// positions over the chunk (Q <= 256 tokens, one per thread).
 __global__ void __launch_bounds__(256)
 k1_dA_cumsum(const float *__restrict__ dt, const DtProc dtp, const float *__restrict__ A,
              float *__restrict__ acum_hi, float *__restrict__ acum_lo,
-             float *__restrict__ dtT, int L, int H, int nc, int Q) {
+             float *__restrict__ dtT, int L, int H, int nc, int Q,
+             const int *__restrict__ seq_idx, int *__restrict__ segst) {
     __shared__ float s_dt[16][257];
     const int c = blockIdx.x, h0 = blockIdx.y * 16, b = blockIdx.z;
     const int tid = threadIdx.x;
+    if (seq_idx && blockIdx.y == 0) {
+        __shared__ int s_st[256];
+        const int t = c * Q + tid;
+        const bool start = tid < Q && t > 0 && t < L &&
+                           seq_idx[(size_t)b * L + t] != seq_idx[(size_t)b * L + t - 1];
+        s_st[tid] = start ? tid : -1;
+        __syncthreads();
+        for (int d = 1; d < Q; d <<= 1) {
+            const int o = tid >= d ? s_st[tid - d] : -1;
+            __syncthreads();
+            s_st[tid] = max(s_st[tid], o);
+            __syncthreads();
+        }
+        if (tid < Q) segst[((size_t)b * nc + c) * Q + tid] = s_st[tid];
+    }
     const int j = tid & 15;
     for (int r = tid >> 4; r < Q; r += 16) {
         const int h = h0 + j, t = c * Q + r;
@@ -158,7 +190,7 @@ __global__ void __launch_bounds__(256)
 k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
                const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
                const float *__restrict__ dtT, float *__restrict__ S, int L, int H,
-               int G, int P, int N, int nc, int Q) {
+               int G, int P, int N, int nc, int Q, const int *__restrict__ segst) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int KB = 32;
     constexpr int PITCH = KB + 16 / (int)sizeof(T);
@@ -176,6 +208,8 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
     const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
     const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
     const float end_hi = ah[Q - 1], end_lo = al[Q - 1];
+    // packed sequences: only the chunk's last sequence reaches its end state
+    const int s_first = segst ? segst[((size_t)b * nc + c) * Q + Q - 1] : -1;
 
     f32x4 acc[TPW];
 #pragma unroll
@@ -187,7 +221,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
         for (int v = tid; v < KB * pv; v += 256) {
             const int sl = v / pv, p0 = (v % pv) * VEC;
             const int s = s0 + sl, t = c * Q + s;
-            const bool in = s < Q && t < L;
+            const bool in = s < Q && t < L && s >= s_first;
             float w = 0.f;
             typename Mma<T>::frag f = zero_frag<T>();
             if (in) {
@@ -241,7 +275,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
 __global__ void __launch_bounds__(256)
 k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
                  const float *init, float *final_state, int H, int PN, int nc,
-                 int Q) {
+                 int Q, const int *__restrict__ segst) {
     const int h = blockIdx.y, b = blockIdx.z;
     const int e0 = (blockIdx.x * 256 + threadIdx.x) * 4;
     if (e0 >= PN) return;
@@ -258,7 +292,10 @@ k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
             const int c = c0 + k;
             if (c < nc) {
                 sv[k] = *reinterpret_cast<const float4 *>(S + ((size_t)(b * nc + c) * H + h) * PN + e0);
-                dec[k] = fast_exp(ac[(size_t)c * Q + Q - 1]);
+                // (a chunk with a sequence start passes nothing on)
+                dec[k] = segst && segst[((size_t)b * nc + c) * Q + Q - 1] >= 0
+                             ? 0.f
+                             : fast_exp(ac[(size_t)c * Q + Q - 1]);
             }
         }
 #pragma unroll
@@ -281,14 +318,18 @@ k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
 // Block (c, lb) produces rows l in [64 lb, 64 lb + 64) of chunk c; wave w
 // owns the 16 rows l0 = 64 lb + 16 w and every 16-column p-tile.
 //   acc  = C[l] . h_in^T                 (state-to-output, Eq. 23)
-//   acc *= exp(acum_l)
-//   acc += sum_{s<=l} CB[l,s] exp(acum_l - acum_s) dt_s x[s]   (Step 1)
+//   acc *= exp(acum_l)                   (0 past a sequence start in the chunk)
+//   acc += sum_{s<=l} M[l][s] x[s],  M[l][s] = CB[l,s] exp(acum_l - acum_s) dt_s
+//                                        (Step 1; s >= segst[l] with packed sequences)
 //   y    = acc + D x[l]               (D per head, or per head and column)
 //   y   *= silu(z[l])                 (when gated)
-// The decay mask is applied with a select, so entries above the diagonal are
-// exactly 0 (the upper-triangle protection of the Kernel 5 page: the
-// exponent is never evaluated for s > l).  x is staged transposed in LDS,
-// 64 tokens at a time, as the B operand of the intra-chunk product.
+// For each 64-token s-block at or before the l-block the workgroup stages x^T
+// of the s-block and builds the 64 x 64 tile of M in LDS, in the MFMA operand
+// type: each thread forms 16 entries from coalesced reads of the C B^T rows
+// and the staged prefix sums and dt, so the product loop is LDS reads and
+// MFMAs only.  The mask is a select, so entries above the diagonal are
+// exactly 0 (the upper-triangle protection of the Kernel 5 page: no exponent
+// of s > l reaches the tile).
 template <typename T>
 __global__ void __launch_bounds__(256)
 k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
@@ -296,13 +337,20 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
               const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
               const float *__restrict__ dtT, const float *__restrict__ D,
               T *__restrict__ y, int L, int H, int G, int P, int N, int nc, int Q,
-              const T *__restrict__ z, int D_hdim) {
+              const T *__restrict__ z, int D_hdim, const int *__restrict__ segst) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SB = 64;
     constexpr int PITCH = SB + 16 / (int)sizeof(T);
     constexpr int MAXPT = kMaxHeaddim / 16;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    T *XT = reinterpret_cast<T *>(smem_raw);
+    T *XT = reinterpret_cast<T *>(smem_raw);                 // [P][PITCH]: x^T of the s-block
+    T *MT = XT + (size_t)P * PITCH;                           // [64][PITCH]: M of (l-block, s-block)
+    float *s_hi = reinterpret_cast<float *>(MT + SB * PITCH);  // the s-block's prefix sums, dt
+    float *s_lo = s_hi + SB;
+    float *s_dt = s_lo + SB;
+    float *r_hi = s_dt + SB;                                  // the l-block's prefix sums
+    float *r_lo = r_hi + SB;
+    int *r_st = reinterpret_cast<int *>(r_lo + SB);           // and sequence starts
 
     const int nlb = (Q + 63) / 64;
     const int c = blockIdx.x / nlb, lb = blockIdx.x % nlb;
@@ -311,11 +359,19 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
     const int r = lane & 15, q = lane >> 4;
     const int l0 = lb * 64 + wave * 16;
     const bool active = l0 < Q;
-    const int row = l0 + r;
     const int npt = P / 16;
     const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
     const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
     const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
+    const int *sg = segst ? segst + ((size_t)b * nc + c) * Q : nullptr;
+
+    if (tid < SB) {
+        const int l = lb * SB + tid;
+        r_hi[tid] = l < Q ? ah[l] : 0.f;
+        r_lo[tid] = l < Q ? al[l] : 0.f;
+        r_st[tid] = sg && l < Q ? sg[l] : -1;
+    }
+    __syncthreads();
 
     f32x4 acc[MAXPT];
 #pragma unroll
@@ -323,7 +379,7 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
 
     if (active) {
         const float *hin = S + ((size_t)(b * nc + c) * H + h) * P * N;
-        const int t = c * Q + row;
+        const int t = c * Q + l0 + r;
         const T *crow = Cm + (((size_t)b * L + t) * G + g) * N;
         for (int k0 = 0; k0 < N; k0 += KS) {
             const int k = k0 + VEC * q;
@@ -343,14 +399,14 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const float e = fast_exp(ah[l0 + 4 * q + i]);
+            const int li = wave * 16 + 4 * q + i;
+            const float e = r_st[li] < 0 ? fast_exp(r_hi[li]) : 0.f;
 #pragma unroll
             for (int pt = 0; pt < MAXPT; ++pt) acc[pt][i] *= e;
         }
     }
 
-    const float row_hi = active ? ah[row] : 0.f, row_lo = active ? al[row] : 0.f;
-    const float *cbrow = cb + (((size_t)(b * nc + c) * G + g) * Q + (active ? row : 0)) * Q;
+    const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
     const int pv = P / VEC;
     for (int sb = 0; sb <= lb; ++sb) {
         __syncthreads();
@@ -362,24 +418,38 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
 #pragma unroll
             for (int jj = 0; jj < VEC; ++jj) XT[(p0 + jj) * PITCH + sl] = f[jj];
         }
+        if (tid < SB) {
+            const int s = sb * SB + tid;
+            s_hi[tid] = s < Q ? ah[s] : 0.f;
+            s_lo[tid] = s < Q ? al[s] : 0.f;
+            s_dt[tid] = s < Q ? dc[s] : 0.f;
+        }
+        __syncthreads();
+        // the tile of M: thread tid forms column j = tid % 64 of rows
+        // tid / 64 + 4 k, k = 0..15 (each row read as 64 consecutive floats)
+        {
+            const int j = tid & (SB - 1), s = sb * SB + j;
+            const float shi = s_hi[j], slo = s_lo[j], sdt = s_dt[j];
+#pragma unroll 4
+            for (int i = tid >> 6; i < SB; i += 4) {
+                const int l = lb * SB + i;
+                float v = 0.f;
+                if (l < Q && s <= l && s >= r_st[i])
+                    v = cb[(cbase + l) * Q + s] *
+                        fast_exp(prefix_diff(r_hi[i], r_lo[i], shi, slo)) * sdt;
+                MT[i * PITCH + j] = from_f32<T>(v);
+            }
+        }
         __syncthreads();
         if (!active) continue;
-        const int kend = min(min(sb * SB + SB, Q), l0 + 16);
-        for (int kk = sb * SB; kk < kend; kk += KS) {
-            const int sj0 = kk + VEC * q;
-            typename Mma<T>::frag m;
-#pragma unroll
-            for (int jj = 0; jj < VEC; ++jj) {
-                const int s = sj0 + jj;
-                float v = 0.f;
-                if (s <= row && s < Q)
-                    v = cbrow[s] * fast_exp(prefix_diff(row_hi, row_lo, ah[s], al[s])) * dc[s];
-                m[jj] = from_f32<T>(v);
-            }
+        // the diagonal tile stops at the wave's last row (M is 0 beyond it)
+        const int kend = sb < lb ? SB : min(SB, (wave * 16 + 16 + KS - 1) / KS * KS);
+        for (int kk = 0; kk < kend; kk += KS) {
+            const typename Mma<T>::frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
 #pragma unroll
             for (int pt = 0; pt < MAXPT; ++pt) {
                 if (pt >= npt) continue;
-                typename Mma<T>::frag bb = load_frag(XT + (pt * 16 + r) * PITCH + (sj0 - sb * SB));
+                typename Mma<T>::frag bb = load_frag(XT + (pt * 16 + r) * PITCH + kk + VEC * q);
                 acc[pt] = Mma<T>::mma(m, bb, acc[pt]);
             }
         }
@@ -412,9 +482,9 @@ const char *const kSplitKernelNames[kSplitKernels] = {
 
 void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float *acum_hi,
                       float *acum_lo, float *dtT, int batch, int L, int H, int nc, int Q,
-                      hipStream_t stream) {
+                      hipStream_t stream, const int *seq_idx, int *segst) {
     hipLaunchKernelGGL(k1_dA_cumsum, dim3(nc, (H + 15) / 16, batch), dim3(256), 0, stream, dt,
-                       dtp, A, acum_hi, acum_lo, dtT, L, H, nc, Q);
+                       dtp, A, acum_hi, acum_lo, dtT, L, H, nc, Q, seq_idx, segst);
 }
 
 template <typename T>
@@ -426,8 +496,9 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     };
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
+    const int *segst = a.seq_idx ? a.segst : nullptr;
     launch_dA_cumsum(a.dt, a.dtp, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q,
-                     stream);
+                     stream, a.seq_idx, a.segst);
     if ((err = mark()) != hipSuccess) return err;
     const int nlb = (Q + 63) / 64;
     hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
@@ -439,17 +510,17 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
     hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
                        stream, (const T *)a.x, (const T *)a.B, a.acum_hi, a.acum_lo, a.dtT,
-                       a.S, a.L, a.H, a.G, a.P, a.N, nc, Q);
+                       a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
     if ((err = mark()) != hipSuccess) return err;
     const int PN = a.P * a.N;
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
-                       0, stream, a.S, a.acum_hi, a.init, a.final_state, a.H, PN, nc, Q);
+                       0, stream, a.S, a.acum_hi, a.init, a.final_state, a.H, PN, nc, Q, segst);
     if ((err = mark()) != hipSuccess) return err;
-    const size_t k5_lds = (size_t)a.P * (64 + 16 / sizeof(T)) * sizeof(T);
+    const size_t k5_lds = (size_t)(a.P + 64) * (64 + 16 / sizeof(T)) * sizeof(T) + 6 * 64 * 4;
     hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
                        stream, (const T *)a.x, (const T *)a.C, (const float *)a.cb, a.S, a.acum_hi,
                        a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q,
-                       (const T *)a.z, a.D_hdim ? 1 : 0);
+                       (const T *)a.z, a.D_hdim ? 1 : 0, segst);
     if ((err = mark()) != hipSuccess) return err;
     return hipGetLastError();
 }

@@ -57,7 +57,7 @@ class Workload:
         return self.batch * self.seqlen
 
 
-# The five workloads.  Shapes of the "130M" and "2.7B" entries are the SSD
+# The workloads.  Shapes of the "130M" and "2.7B" entries are the SSD
 # layer shapes of those Mamba-2 sizes (d_inner = 2 * d_model, headdim 64,
 # d_state 128); no weights are involved.
 WORKLOADS = {
@@ -70,6 +70,9 @@ WORKLOADS = {
                            init_std=0.1, seed=1237),
     "decode_b256": Workload("decode_b256", 256, 64, 80, 64, 128, 1, 256, "bf16",
                             init_std=0.1, seed=1238, decode_steps=64),
+    # the 130M layer shape with fp32 x, B, C and y (the split path)
+    "mamba2_130m_f32": Workload("mamba2_130m_f32", 8, 2048, 24, 64, 128, 1, 256, "f32",
+                                seed=1239),
 }
 
 

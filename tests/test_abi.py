@@ -63,8 +63,9 @@ def test_workspace_size(lib, monkeypatch):
     monkeypatch.setenv("SSD_FORWARD_PATH", "split")
     st, n = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
     assert st == 0
-    expect = vec + 4 * nc * 1 * 256 * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4
-    assert n >= expect and n - expect < 6 * 256
+    # prefix sums (two), dt, C B^T, chunk states, packed-sequence starts
+    expect = vec + 4 * nc * 1 * 256 * 256 * 4 + 4 * nc * 80 * 64 * 128 * 4 + 4 * nc * 256 * 4
+    assert n >= expect and n - expect < 7 * 256
     monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
     st, n = ws_size(lib, 4, 8192, 80, 64, 128, 1, 256, 1)
     assert st == 0 and n == 0                               # the fused pass keeps all on chip

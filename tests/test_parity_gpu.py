@@ -213,12 +213,13 @@ def _sample_slices(b, H, n, seed):
     return sorted(sl)
 
 
-def check_every_slice(y, fin, yr, fr, io, what):
+def check_every_slice(y, fin, yr, fr, io, what, ya=None, fa=None):
     """y and the final state against the oracle over the whole workload: the
     whole arrays, every (batch, head) slice's final state, and every 32-token
-    block of every slice of y."""
-    check(y, yr, io, what + " y (every slice)", tok_axis=1)
-    check(fin, fr, io, what + " final (every slice)")
+    block of every slice of y (fp32: every element, against the magnitude
+    references ya and fa)."""
+    check(y, yr, io, what + " y (every slice)", ya, tok_axis=1)
+    check(fin, fr, io, what + " final (every slice)", fa)
     d = np.sqrt(((fin.astype(np.float64) - fr) ** 2).sum(axis=(-2, -1)))
     o = np.sqrt((fr ** 2).sum(axis=(-2, -1)))
     r = d / np.where(o > 0, o, 1.0)
@@ -226,7 +227,7 @@ def check_every_slice(y, fin, yr, fr, io, what):
     assert r.max() <= metrics.tolerance(io)
 
 
-@pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b", "grouped_g8"])
+@pytest.mark.parametrize("name", ["mamba2_130m", "mamba2_2p7b", "grouped_g8", "mamba2_130m_f32"])
 def test_full_size_workloads_every_slice(dev, oracle_mod, path, name):
     w = WORKLOADS[name]
     _say("workload %s path %s" % (name, path))
@@ -236,7 +237,11 @@ def test_full_size_workloads_every_slice(dev, oracle_mod, path, name):
     assert np.all(np.isfinite(y)) and np.all(np.isfinite(fin))
     # every (batch, head) slice: the serial oracle over the whole workload
     yr, fr = oracle_mod.forward(*(inp[k] for k in FWD_ARGS))
-    check_every_slice(y, fin, yr, fr, w.io_dtype, name)
+    ya = fa = None
+    if w.io_dtype == "f32":
+        ia = abs_inputs(inp)
+        ya, fa = oracle_mod.forward(*(ia[k] for k in FWD_ARGS))
+    check_every_slice(y, fin, yr, fr, w.io_dtype, name, ya, fa)
 
 
 def test_chunk_length_invariance_on_gpu(dev, oracle_mod):
@@ -634,72 +639,93 @@ def test_gated_rmsnorm_in_place(dev):
 # the head counts select the fused pass's three layouts (32, 64 and
 # 128-column workgroups)
 VARLEN = [
-    (2, 300, 4, 64, 1, 96, True, False),
-    (2, 333, 4, 64, 2, 8, True, False),        # several sequence starts per block
-    (2, 200, 132, 64, 2, 70, True, False),     # four-wave workgroups, two heads each
-    (2, 300, 66, 64, 1, 40, False, False),     # two-wave workgroups
-    (1, 257, 4, 64, 1, 96, True, True),        # with the time-step preprocessing
+    # b, L, H, P, G, max sequence length, initial state, dt preprocessing, io, Q, N
+    (2, 300, 4, 64, 1, 96, True, False, "bf16", 64, 128),
+    (2, 333, 4, 64, 2, 8, True, False, "bf16", 64, 128),     # several starts per block
+    (2, 200, 132, 64, 2, 70, True, False, "bf16", 64, 128),  # four-wave workgroups
+    (2, 300, 66, 64, 1, 40, False, False, "bf16", 64, 128),  # two-wave workgroups
+    (1, 257, 4, 64, 1, 96, True, True, "bf16", 64, 128),     # time-step preprocessing
+    (2, 300, 4, 64, 1, 96, True, False, "f32", 64, 128),     # fp32: the split path
+    (2, 333, 3, 32, 1, 8, True, True, "f32", 16, 64),        # starts in most 16-token chunks
+    (2, 520, 4, 48, 2, 300, True, False, "f32", 256, 32),    # few starts, long chunks
+    (1, 777, 2, 64, 1, 130, False, False, "bf16", 128, 96),  # dstate 96: the split path
 ]
 
 
-def _varlen_check(oracle_mod, dev, inp, seq, dtp=False):
+def _varlen_check(oracle_mod, dev, inp, seq, dtp=False, io="bf16", Q=64):
     import torch
     from oracle.dt import process_dt
     from oracle.varlen import forward_varlen
     from state_space_sequence_amd import libssd
     from state_space_sequence_amd.inputs import to_torch
-    t = to_torch(inp, "bf16", dev)
+    t = to_torch(inp, io, dev)
     ts = torch.from_numpy(seq).to(dev)
     if dtp:
         y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt_raw"], t["A"], t["B"], t["C"], t["D"],
-                                           t["initial_state"], chunk_len=64, seq_idx=ts,
+                                           t["initial_state"], chunk_len=Q, seq_idx=ts,
                                            dt_bias=t["dt_bias"], dt_softplus=True)
         dt_used = process_dt(inp["dt_raw"], inp["dt_bias"], True)
     else:
         y, fin = libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
-                                           t["initial_state"], chunk_len=64, seq_idx=ts)
+                                           t["initial_state"], chunk_len=Q, seq_idx=ts)
         dt_used = inp["dt"]
     torch.cuda.synchronize()
     yr, fr = forward_varlen(inp["x"], dt_used, inp["A"], inp["B"], inp["C"], inp["D"],
                             inp["initial_state"], seq)
-    check(y.float().cpu().numpy(), yr, "bf16", "varlen y", tok_axis=1)
-    check(fin.cpu().numpy(), fr, "bf16", "varlen final")
+    ya = fa = None
+    if io == "f32":
+        ia = abs_inputs(inp)
+        ya, fa = forward_varlen(ia["x"], dt_used, inp["A"], ia["B"], ia["C"], ia["D"],
+                                ia["initial_state"], seq)
+    check(y.float().cpu().numpy(), yr, io, "varlen y", ya, tok_axis=1)
+    check(fin.cpu().numpy(), fr, io, "varlen final", fa)
     # and every packed sequence on its own (a short one must not drown in the
     # norm of the others)
     from oracle.varlen import segments
     yg = y.float().cpu().numpy()
     for r in range(seq.shape[0]):
         for s0, s1 in segments(seq[r]):
-            assert metrics.normwise_err(yg[r, s0:s1], yr[r, s0:s1]) <= metrics.BF16_NORMWISE, (r, s0)
+            if io == "f32":
+                e = metrics.componentwise_err(yg[r, s0:s1], yr[r, s0:s1], ya[r, s0:s1])
+                assert e <= metrics.FP32_MAX_REL, (r, s0, e)
+            else:
+                e = metrics.normwise_err(yg[r, s0:s1], yr[r, s0:s1])
+                assert e <= metrics.BF16_NORMWISE, (r, s0, e)
 
 
 @pytest.mark.parametrize("case", VARLEN, ids=lambda c: "b%d_L%d_H%d_P%d_G%d_max%d" % c[:6]
-                         + ("_init" if c[6] else "") + ("_dtproc" if c[7] else ""))
-def test_varlen_packed_sequences(dev, oracle_mod, case):
+                         + ("_init" if c[6] else "") + ("_dtproc" if c[7] else "")
+                         + "_%s_Q%d_N%d" % c[8:])
+def test_varlen_packed_sequences(dev, oracle_mod, path, case):
     from state_space_sequence_amd.inputs import make_seq_idx
-    b, L, H, P, G, mx, init, dtp = case
-    _say("varlen case %s" % (case,))
-    inp = make_inputs(b, L, H, P, 128, G, io_dtype="bf16", init_std=0.1 if init else 0.0,
+    b, L, H, P, G, mx, init, dtp, io, Q, N = case
+    _say("varlen case %s path %s" % (case, path))
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1 if init else 0.0,
                       seed=700 + L + H)
-    skip_if_path_unsupported(inp, "bf16", 64)
+    skip_if_path_unsupported(inp, io, Q)
     seq = make_seq_idx(b, L, seed=800 + L, max_len=mx)
-    _varlen_check(oracle_mod, dev, inp, seq, dtp)
+    _varlen_check(oracle_mod, dev, inp, seq, dtp, io, Q)
 
 
-def test_varlen_placed_boundaries(dev, oracle_mod):
+@pytest.mark.parametrize("Q", [64, 32, 16])
+def test_varlen_placed_boundaries(dev, oracle_mod, path, Q):
     """Sequence starts at block starts (32, 64), a run of one-token sequences
-    (100, 101, 102), at the last token, and none in the first block's tail."""
+    (100, 101, 102), at the last token, and none in the first block's tail;
+    with 64-, 32- and 16-token chunks on the split path (starts at chunk
+    starts, a chunk of one-token sequences)."""
+    if path == "fused" and Q != 64:
+        pytest.skip("the fused pass does not depend on the chunk length")
     L = 230
     inp = make_inputs(2, L, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=61)
     seq = np.zeros((2, L), dtype=np.int32)
     for k, start in enumerate([32, 33, 64, 100, 101, 102, L - 1]):
         seq[:, start:] = k + 1
     seq[1, :] = np.minimum(seq[1], 3)      # row 1: starts at 32, 33 and 64 only
-    _varlen_check(oracle_mod, dev, inp, seq)
+    _varlen_check(oracle_mod, dev, inp, seq, Q=Q)
 
 
 @pytest.mark.parametrize("H", [4, 66, 132])
-def test_varlen_through_decay_regimes(dev, oracle_mod, H):
+def test_varlen_through_decay_regimes(dev, oracle_mod, path, H):
     """Packed sequences on the decay-regime inputs: sequence starts inside
     weak-decay, rescaling and exact blocks, at block starts and at the last
     token, in the fused pass's three workgroup layouts; every sequence on its
@@ -716,21 +742,6 @@ def test_varlen_through_decay_regimes(dev, oracle_mod, H):
     seq[1, 300:] = 2
     _say("varlen decay regimes H=%d" % H)
     _varlen_check(oracle_mod, dev, inp, seq)
-
-
-def test_varlen_unsupported_paths(dev, monkeypatch):
-    import torch
-    from state_space_sequence_amd import libssd
-    from state_space_sequence_amd.inputs import to_torch
-    seq = torch.zeros((1, 100), dtype=torch.int32, device=dev)
-    for io, path in (("f32", None), ("bf16", "split")):
-        if path:
-            monkeypatch.setenv("SSD_FORWARD_PATH", path)
-        inp = make_inputs(1, 100, 2, 64, 128, 1, io_dtype=io, seed=3)
-        t = to_torch(inp, io, dev)
-        with pytest.raises(libssd.SsdError) as ei:
-            libssd.ssd_chunk_scan_fwd(t["x"], t["dt"], t["A"], t["B"], t["C"], seq_idx=seq)
-        assert ei.value.status == libssd.SSD_ERR_UNSUPPORTED
 
 
 # ------------------------------------------ full-size checks of the layer steps
@@ -1018,8 +1029,6 @@ def test_gate_and_per_channel_D(dev, oracle_mod, path, case):
     else:
         inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=900 + L + H)
     skip_if_path_unsupported(inp, io, Q)
-    if extra == "varlen" and path == "split":
-        pytest.skip("packed sequences run on the fused pass only")
     g = make_gate_inputs(b, L, H, P, io_dtype=io, seed=901 + L)
     z = g["z"] if use_z else None
     D = g["D_hp"] if dhp else inp["D"]
