@@ -175,6 +175,8 @@ class FiniteCheck {
 
 struct Layout {
     size_t acum_hi, acum_lo, dtT, cb, S, segst, total;
+    int nseg = 1;            // fused path: sequence segments
+    size_t seg_buf = 0, seg_logdec = 0;
 };
 
 Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -196,9 +198,14 @@ Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate
         l.segst = l.S + round_up(b * nc * H * P * N * sizeof(float));
         l.total = l.segst + round_up(b * nc * Q * sizeof(int));
     } else {
-        // the fused kernel keeps every intermediate on chip
+        // the fused kernel keeps every intermediate on chip; a segmented
+        // sequence needs the states of its segments and their log decays
         l.acum_hi = l.acum_lo = l.dtT = l.cb = l.S = l.segst = 0;
-        l.total = 0;
+        l.nseg = ssd::fused_segments(batch, seqlen, nheads, ngroups, headdim);
+        const size_t ns = (size_t)ssd::fused_seg_ratio() * (l.nseg - 1);
+        l.seg_buf = 0;
+        l.seg_logdec = round_up(ns * b * H * P * N * sizeof(float));
+        l.total = l.nseg > 1 ? l.seg_logdec + round_up(ns * b * H * sizeof(float)) : 0;
     }
     return l;
 }
@@ -276,10 +283,14 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     a.cb = split ? ws + lay.cb : nullptr;
     a.S = split ? reinterpret_cast<float *>(ws + lay.S) : nullptr;
     a.segst = split ? reinterpret_cast<int *>(ws + lay.segst) : nullptr;
+    a.nseg = split ? 1 : lay.nseg;
+    a.seg_buf = a.nseg > 1 ? reinterpret_cast<float *>(ws + lay.seg_buf) : nullptr;
+    a.seg_logdec = a.nseg > 1 ? reinterpret_cast<float *>(ws + lay.seg_logdec) : nullptr;
 
-    const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::kFusedKernels;
-    const char *const *kn =
-        path == ssd::Path::Split ? ssd::kSplitKernelNames : ssd::kFusedKernelNames;
+    const int nk = path == ssd::Path::Split ? ssd::kSplitKernels : ssd::fused_kernel_count(a.nseg);
+    const char *const *kn = path == ssd::Path::Split ? ssd::kSplitKernelNames
+                            : a.nseg > 1             ? ssd::kFusedSegKernelNames
+                                                     : ssd::kFusedKernelNames;
     if (nkernels) *nkernels = nk;
     if (names)
         for (int i = 0; i < nk; ++i) names[i] = kn[i];

@@ -152,7 +152,7 @@ __device__ __forceinline__ float last_of_half(float v, int lane) {
 // contiguous over them): NW = PB / 32 waves of 32 columns each.  With
 // PB > P the workgroup spans NH = PB / P heads of one B/C group, which then
 // share the staged C and B rows.
-template <int PB>
+template <int PB, bool SO = false>
 struct Fused {
     static constexpr int NW = PB / 32;                 // compute waves: 32 headdim columns each
     // Helper waves.  The loader (wave NW) issues every global memory
@@ -167,8 +167,9 @@ struct Fused {
     // the barriers, so that no SIMD carries two helpers (the loader shares
     // SIMD 0) and the records wave has time to spare (the time-step
     // preprocessing of the raw dt runs there).  With fewer compute waves
-    // every helper has a SIMD of its own.
-    static constexpr int NHELP = NW == 4 ? 4 : 2;
+    // every helper has a SIMD of its own.  The state-only pass (SO) forms
+    // no C B^T blocks: one former wave (records only) and the loader.
+    static constexpr int NHELP = (NW == 4 && !SO) ? 4 : 2;
     static constexpr bool SPLIT_FORMER = NHELP == 4;
     static constexpr int NT = 64 * (NW + NHELP);       // threads
     static constexpr int N = 128;                      // dstate
@@ -185,13 +186,15 @@ struct Fused {
     // slots), formed by the former from the stage's C and B rows and dt;
     // then the block's y for the loader: 32 rows of XRB bytes, 16-byte
     // chunk c of row t in slot c ^ ys_swz(t)
+    // (the state-only pass has no C rows, C B^T block or y staging, so its
+    // stages are 18.5 KB and two of its workgroups fit on a compute unit)
     static constexpr int CS = 0;
-    static constexpr int BS = MAT;
-    static constexpr int CBF = 2 * MAT;                // 2 x 1 KB of C B^T fragments
-    static constexpr int XR = CBF + 2048;
+    static constexpr int BS = SO ? 0 : MAT;
+    static constexpr int CBF = BS + MAT;               // 2 x 1 KB of C B^T fragments
+    static constexpr int XR = CBF + (SO ? 0 : 2048);
     static constexpr int VR = XR + kBlk * XRB;
     static constexpr int YS = VR + 1024 * NRS;
-    static constexpr int DTR = YS + kBlk * XRB;
+    static constexpr int DTR = YS + (SO ? 0 : kBlk * XRB);
     static constexpr int SEQ = DTR + 256;              // seq_idx of the block (varlen), 2 x 32
     static constexpr int STG = SEQ + 256;
     // floats of the decay record
@@ -228,6 +231,11 @@ struct Fused {
                (block1 ? P_STORES : 0);
     }
     static_assert(wait_count(true, true, false) < 64, "vmcnt immediate");
+    // The state-only pass (kEpiState) loads no C rows and stores no y: at
+    // the end of block kb everything it issued in block kb is younger than
+    // the DMAs of block kb + 2.
+    static constexpr int P_LOADS_SO = MAT / 1024 + kBlk * XRB / 1024 + 1;
+    static constexpr int wait_count_so(bool varlen) { return P_LOADS_SO + (varlen ? 1 : 0); }
 };
 
 // Column-blocked LDS layout of the staged C, B and x tiles (32 rows): the
@@ -330,16 +338,23 @@ __device__ __forceinline__ int col_of(int q) {
 //             K-step kk).
 // Output variants (EPI): bit 0, D per (head, headdim column) instead of per
 // head; bit 1, the output gate y * silu(z).  EPI = 0 is the plain forward.
-constexpr int kEpiDhp = 1, kEpiGate = 2;
+// Bit 2 (kEpiState) is the state-only pass of a segmented forward: no C, no
+// C B^T, no y; each workgroup writes the state its segment leaves (from the
+// initial state in segment 0, from zero in the others) and, per head, the
+// segment's total log decay.
+constexpr int kEpiDhp = 1, kEpiGate = 2, kEpiState = 4;
 
 template <int PB, int EPI>
-__global__ void __launch_bounds__(Fused<PB>::NT)
+__global__ void __launch_bounds__((Fused<PB, (EPI & 4) != 0>::NT))
 k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const float *__restrict__ A,
             const bf16 *__restrict__ Bm, const bf16 *__restrict__ Cm,
-            const float *__restrict__ D, const float *init, float *final_state,
+            const float *__restrict__ D, const float *init_arg, float *final_arg,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp,
-            const int *__restrict__ seq_idx, const bf16 *__restrict__ z, int win_shift) {
-    typedef Fused<PB> S;
+            const int *__restrict__ seq_idx, const bf16 *__restrict__ z, int win_shift,
+            int seg_blocks, int seg_ratio, const float *seg_in, float *seg_out,
+            float *seg_logdec) {
+    constexpr bool SO = (EPI & kEpiState) != 0;
+    typedef Fused<PB, SO> S;
     constexpr int NW = S::NW, N = S::N;
     constexpr bool DHP = (EPI & kEpiDhp) != 0, GATE = (EPI & kEpiGate) != 0;
     // Every LDS region that a DMA fills is its own object: the compiler can
@@ -358,14 +373,32 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     // the consecutive range x * n / 8 .. of (batch, column block) pairs, so
     // a batch's workgroups share few L2s and fetch its C, B and dt rows a few
     // times instead of once per XCD.
-    int c0, b;
+    // The sequence may be cut into gridDim.z segments of seg_blocks blocks
+    // (the segment index varies slowest, so a segment's workgroups sit
+    // together on the XCDs as a batch's do).
+    int c0, b, seg;
     {
-        const int nc = H * P / PB, n = nc * gridDim.y;
-        const int i = blockIdx.y * nc + blockIdx.x;
+        const int nc = H * P / PB, nb = gridDim.y, n = nc * nb * gridDim.z;
+        const int i = (blockIdx.z * nb + blockIdx.y) * nc + blockIdx.x;
         const int v = (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
         c0 = (v % nc) * PB;
-        b = v / nc;
+        b = (v / nc) % nb;
+        seg = v / nc / nb;
     }
+    // the workgroup's blocks kb0 .. kb0 + nloc - 1 (the host makes every
+    // segment non-empty)
+    const int kb0 = seg * seg_blocks;
+    const int nloc = min(nblk, kb0 + seg_blocks) - kb0;
+    // The state entering the segment: the initial state in segment 0; zero
+    // in the other segments of the state-only pass; in the main pass,
+    // chained from the state-only pass's outputs (below).  The state leaving
+    // it: the final state after the last segment (main pass); every
+    // segment's own (state-only pass).
+    const size_t bHPN = (size_t)gridDim.y * H * P * N;
+    const float *init = seg == 0 ? init_arg : (SO ? nullptr : seg_in);
+    (void)seg_ratio;
+    float *final_state = SO ? seg_out + (size_t)seg * bHPN
+                            : (seg == (int)gridDim.z - 1 ? final_arg : nullptr);
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
@@ -454,13 +487,13 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // the DMAs of block kb into `buf`, and the dt of block kb + 1 into
         // `nbuf` (the stage of block kb + 1)
         auto pdma = [&](int kb, unsigned char *buf, unsigned char *nbuf) {
-            unsigned cbo, bo, xo;
-            const __amdgpu_buffer_rsrc_t &rc = wc.at(kb, cbo);
+            unsigned cbo = 0, bo, xo;
+            if constexpr (!SO) wc.at(kb, cbo);
             const __amdgpu_buffer_rsrc_t &rb = wb.at(kb, bo);
             const __amdgpu_buffer_rsrc_t &rx = wx.at(kb, xo);
 #pragma unroll
             for (int i = 0; i < NCB; ++i) {
-                bdma(rc, pcb[i], cbo, buf + S::CS + 1024 * i);
+                if constexpr (!SO) bdma(wc.r, pcb[i], cbo, buf + S::CS + 1024 * i);
                 bdma(rb, pcb[i], bo, buf + S::BS + 1024 * i);
             }
             if (x_nt) {
@@ -496,8 +529,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // Packed sequences: token t (> 0, < seqlen) whose seq_idx differs from
         // token t - 1's starts a new sequence, and the state entering it is 0.
         // pseq is the seq_idx of the last token of the previous block.
-        int pseq = 0;
-        bool pfirst = true;
+        bool pfirst = kb0 == 0;
+        int pseq = !pfirst && varlen ? seq_idx[(size_t)b * L + (size_t)kb0 * kBlk - 1] : 0;
+        // (state-only pass) the segment's total log decay of this lane's
+        // head, and whether a sequence starts in it (then its decay is 0)
+        float ltot = 0.f;
+        bool cut = false;
         // VL: the packed-sequence variant (a compile-time tag, so that the
         // plain one is the code without any of it)
         auto prec_v = [&](unsigned char *buf, int kblk, auto vl_tag) {
@@ -521,6 +558,14 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             }
             const float lam = scan32(d * pa, lane);
             const float le = last_of_half(lam, lane);
+            if constexpr (SO) {
+                // (records are also formed for up to two blocks past the
+                // segment; they are not its own)
+                if (kblk < kb0 + nloc) {
+                    ltot += le;
+                    cut = cut || s0e >= 0.f;
+                }
+            }
             // a block with a sequence start takes the exact path: the state
             // entering it does not reach past the start (delta = 0), the
             // state-in factor applies before it only, and the state leaving
@@ -638,11 +683,11 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         // records of blocks 0 and 1 formed), then one at the end of every
         // block.
         if (wave == NW) {
-            pdt_dma(0, stage(0));
+            pdt_dma(kb0, stage(0));
 #pragma unroll
-            for (int i = 0; i < S::NST - 1; ++i) pdma(i, stage(i), stage(i + 1));
+            for (int i = 0; i < S::NST - 1; ++i) pdma(kb0 + i, stage(i), stage(i + 1));
 #pragma unroll
-            for (int i = 0; i < S::NST - 1; ++i) zdma(i, stage(i));
+            for (int i = 0; i < S::NST - 1; ++i) zdma(kb0 + i, stage(i));
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
             lds_barrier();
             lds_barrier();
@@ -650,9 +695,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             // block kb + 4 in this block's stage: its records were formed two
             // blocks ago), store block kb - 1's y, then wait for the DMAs of
             // block kb + 2 and the end-of-block barrier
-            auto pblock = [&](int kb, const int si) {
+            auto pblock = [&](int j, const int si) {
+                const int kb = kb0 + j;
                 pdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST), stage(si));
-                if (kb > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+                if constexpr (!SO) {
+                    if (j > 0) pstore(kb - 1, stage((si + S::NST - 1) % S::NST));
+                }
                 // The z DMAs refill the staging rows that the y stores above
                 // read.  Each store waits for its LDS read, so DMAs issued after
                 // the stores cannot land first; nothing may be scheduled across
@@ -660,7 +708,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 // early one would zero the y not yet read).
                 if constexpr (GATE) __builtin_amdgcn_sched_barrier(0);
                 zdma(kb + S::NST - 1, stage((si + S::NST - 1) % S::NST));
-                if (kb == 1) {
+                if constexpr (SO) {
+                    if (varlen)
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count_so(true)));
+                    else
+                        __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count_so(false)));
+                } else if (j == 1) {
                     if (varlen)
                         __builtin_amdgcn_s_waitcnt(wait_vmcnt_imm(S::wait_count(GATE, true, true)));
                     else
@@ -673,28 +726,28 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 }
                 lds_barrier();
             };
-            for (int kb = 0; kb < nblk; kb += S::NST) {
-                pblock(kb, 0);
-                if (kb + 1 < nblk) {
-                    pblock(kb + 1, 1);
-                    if (kb + 2 < nblk) {
-                        pblock(kb + 2, 2);
-                        if (kb + 3 < nblk) pblock(kb + 3, 3);
+            for (int j = 0; j < nloc; j += S::NST) {
+                pblock(j, 0);
+                if (j + 1 < nloc) {
+                    pblock(j + 1, 1);
+                    if (j + 2 < nloc) {
+                        pblock(j + 2, 2);
+                        if (j + 3 < nloc) pblock(j + 3, 3);
                     }
                 }
             }
-            pstore(nblk - 1, stage((nblk - 1) % S::NST));
+            if constexpr (!SO) pstore(kb0 + nloc - 1, stage((nloc - 1) % S::NST));
             // no DMA may land in LDS after the workgroup ends
             __builtin_amdgcn_s_waitcnt(kWaitVmcnt0);
         } else {
             // the former's jobs: C B^T blocks (do_cbt) and records (do_rec)
-            const bool do_cbt = !S::SPLIT_FORMER || wave == NW + 2;
+            const bool do_cbt = !SO && (!S::SPLIT_FORMER || wave == NW + 2);
             const bool do_rec = !S::SPLIT_FORMER || wave == NW + 3;
             lds_barrier();
             if (do_cbt) pcbt(stage(0));
             if (do_rec) {
-                prec(stage(0), 0);
-                prec(stage(1), 1);
+                prec(stage(0), kb0);
+                prec(stage(1), kb0 + 1);
             }
             lds_barrier();
             // block kb: the C B^T block of block kb + 1 and the records of
@@ -707,15 +760,23 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
                 if (do_rec) prec(stage((si + 2) % S::NST), kb + 2);
                 lds_barrier();
             };
-            for (int kb = 0; kb < nblk; kb += S::NST) {
-                fblock(0, kb);
-                if (kb + 1 < nblk) {
-                    fblock(1, kb + 1);
-                    if (kb + 2 < nblk) {
-                        fblock(2, kb + 2);
-                        if (kb + 3 < nblk) fblock(3, kb + 3);
+            for (int j = 0; j < nloc; j += S::NST) {
+                fblock(0, kb0 + j);
+                if (j + 1 < nloc) {
+                    fblock(1, kb0 + j + 1);
+                    if (j + 2 < nloc) {
+                        fblock(2, kb0 + j + 2);
+                        if (j + 3 < nloc) fblock(3, kb0 + j + 3);
                     }
                 }
+            }
+            if constexpr (SO) {
+                // the segment's log decay per head (-inf: a sequence starts
+                // in it); workgroups sharing a head write the same value
+                const int q = lane >> 5;
+                if (do_rec && (lane & 31) == 0 && q < S::NRS && h0 + q < H)
+                    seg_logdec[((size_t)seg * gridDim.y + b) * H + h0 + q] =
+                        cut ? -__builtin_inff() : ltot;
             }
         }
         return;
@@ -782,6 +843,31 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             }
         }
     }
+    if (!SO && seg > 0) {
+        // Segment s of the main pass.  The state-only pass cut the sequence
+        // into seg_ratio times as many segments: seg_in[0] is the state
+        // entering its segment 1 (it ran segment 0 from the initial state)
+        // and seg_in[k], k >= 1, the state its segment k leaves from zero;
+        // with d_k = exp(logdec_k) the state entering k + 1 is
+        // d_k (state entering k) + seg_in[k] (the inter-chunk recurrence of
+        // the rustdoc's Step 3, over segments), chained here up to the
+        // start of this segment, its segment seg_ratio * s.
+        for (int k = 1; k < seg_ratio * seg; ++k) {
+            const float d = __expf(seg_logdec[((size_t)k * gridDim.y + b) * H + hw]);
+            const float *src = seg_in + (size_t)k * bHPN + (bh * P + pr) * N;
+#pragma unroll
+            for (int m = 0; m < 4; ++m)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int n = 32 * m + 16 * (i >> 1) + 8 * hi + 4 * (i & 1);
+                    const float4 q4 = *reinterpret_cast<const float4 *>(src + n);
+                    st[m][4 * i] = d * st[m][4 * i] + q4.x;
+                    st[m][4 * i + 1] = d * st[m][4 * i + 1] + q4.y;
+                    st[m][4 * i + 2] = d * st[m][4 * i + 2] + q4.z;
+                    st[m][4 * i + 3] = d * st[m][4 * i + 3] + q4.w;
+                }
+        }
+    }
 
     // staging slots of this lane's two 16-byte runs of y (row r, chunks
     // 4 wave + 2 i + hi of the workgroup's row)
@@ -834,10 +920,12 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         for (int kk = 0; kk < 2; ++kk)
             e.xs[kk] = join(lds_tr(buf, S::XR + xs_tr[0] + 1024 * kk),
                             lds_tr(buf, S::XR + xs_tr[1] + 1024 * kk));
+        if constexpr (!SO) {
 #pragma unroll
-        for (int m = 0; m < ECF; ++m)
+            for (int m = 0; m < ECF; ++m)
 #pragma unroll
-            for (int u = 0; u < 2; ++u) e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[u] + 2048 * m);
+                for (int u = 0; u < 2; ++u) e.cfr[m][u] = lds_b128(buf, S::CS + c_rd[u] + 2048 * m);
+        }
         e.rpv = v[S::F + r];
         e.fc = v[S::FLAG];
         e.rs = v[S::RESC];
@@ -862,6 +950,39 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     auto block = [&](int kb, const int si, Early &e, Early &nx) {
         unsigned char *cur = stage(si);
         const float *v = reinterpret_cast<const float *>(cur + rec_off);
+        if constexpr (SO) {
+            // the state update only: x' and B^T, the scale restart or the
+            // exact block's explicit decay, h~ += B^T x'
+            Ops o;
+            const bool fac = uniform(e.fc) != 0.f, rescale = uniform(e.rs) != 0.f;
+            bf16x8 xp[2];
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+#pragma unroll
+                for (int ee = 0; ee < 2; ++ee) {
+                    const int kk = q >> 2, j = 2 * (q & 3) + ee;
+                    xp[kk][j] = (bf16)((float)e.xs[kk][j] * e.cfv[2 * kk + (j >> 2)][j & 3]);
+                }
+                const int m = q >> 1, kk = q & 1;
+                o.bt[m][kk] = join(lds_tr(cur, S::BS + b_tr[0] + 2048 * m + 1024 * kk),
+                                   lds_tr(cur, S::BS + b_tr[1] + 2048 * m + 1024 * kk));
+            }
+            if (rescale || !fac) {
+                const float sig_in = uniform(v[S::SIGIN]);
+                const float sd = fac ? sig_in : sig_in * uniform(v[S::DELTA]);
+#pragma unroll
+                for (int m = 0; m < 4; ++m) st[m] *= sd;
+            }
+#pragma unroll
+            for (int q = 0; q < 8; ++q) {
+                const int kk = q >> 2, m = q & 3;
+                st[m] = mma32(o.bt[m][kk], xp[kk], st[m]);
+                if (q == 0) load_early(stage((si + 1) % S::NST), nx);
+            }
+            (void)kb;
+            lds_barrier();
+            return;
+        }
         // The block is written as a sequence of chunks fenced by scheduling
         // barriers: each chunk starts one MFMA and then issues vector work
         // that does not depend on it (the next state conversion and x'
@@ -1014,14 +1135,14 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     // (and the two sets of opening operands alternate)
     Early ea, eb;
     load_early(stage(0), ea);
-    for (int kb = 0; kb < nblk; kb += S::NST) {
-        block(kb, 0, ea, eb);
-        if (kb + 1 < nblk) {
-            block(kb + 1, 1, eb, ea);
-            if (kb + 2 < nblk) {
-                block(kb + 2, 2, ea, eb);
+    for (int j = 0; j < nloc; j += S::NST) {
+        block(kb0 + j, 0, ea, eb);
+        if (j + 1 < nloc) {
+            block(kb0 + j + 1, 1, eb, ea);
+            if (j + 2 < nloc) {
+                block(kb0 + j + 2, 2, ea, eb);
                 if constexpr (S::NST > 3) {
-                    if (kb + 3 < nblk) block(kb + 3, 3, eb, ea);
+                    if (j + 3 < nloc) block(kb0 + j + 3, 3, eb, ea);
                 }
             }
         }
@@ -1030,7 +1151,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     if (final_state) {
         // h = sigma h~ with the last block's sigma (its record is still staged)
         const float sig_out =
-            uniform(reinterpret_cast<const float *>(stage((nblk - 1) % S::NST) + rec_off)[S::SIGOUT]);
+            uniform(reinterpret_cast<const float *>(stage((nloc - 1) % S::NST) + rec_off)[S::SIGOUT]);
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
@@ -1079,18 +1200,49 @@ int fused_window_shift(const ForwardArgs &a) {
 }
 bool fused_row_fits(size_t row_bytes) { return window_shift_for(row_bytes) >= 3; }
 
+// The state-only pass of a segmented forward cuts each segment into this
+// many pieces (kSegRatio; SSD_FUSED_SEG_RATIO = 1 .. 4 overrides it, a
+// diagnostic for comparing the two).
+int fused_seg_ratio() {
+    if (const char *e = getenv("SSD_FUSED_SEG_RATIO")) {
+        const int r = atoi(e);
+        if (r >= 1 && r <= 4) return r;
+    }
+    return kSegRatio;
+}
+
+// Segments of a segmented forward: blocks per segment, a multiple of the
+// state-only pass's ratio.
+static int seg_blocks_of(int nblk, int nseg) {
+    const int R = fused_seg_ratio();
+    const int q = (nblk + nseg - 1) / nseg;
+    return (q + R - 1) / R * R;
+}
+
 template <int PB, int EPI>
 static void launch_fused_epi(const ForwardArgs &a, hipStream_t stream) {
-    typedef Fused<PB> S;
-    hipLaunchKernelGGL((k_fused_ssd<PB, EPI>), dim3(a.H * a.P / PB, a.batch), dim3(S::NT), 0,
+    constexpr bool SO = (EPI & kEpiState) != 0;
+    typedef Fused<PB, SO> S;
+    const int nblk = fused_nblk(a.L);
+    // the state-only pass runs the first nseg - 1 segments, each cut into
+    // kSegRatio pieces
+    const int sb = seg_blocks_of(nblk, a.nseg);
+    const int R = fused_seg_ratio();
+    const int nz = SO ? R * (a.nseg - 1) : a.nseg;
+    hipLaunchKernelGGL((k_fused_ssd<PB, EPI>), dim3(a.H * a.P / PB, a.batch, nz), dim3(S::NT), 0,
                        stream, (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C,
-                       a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P,
-                       fused_nblk(a.L), a.dtp, a.seq_idx, (const bf16 *)a.z,
-                       fused_window_shift(a));
+                       a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, nblk, a.dtp,
+                       a.seq_idx, (const bf16 *)a.z, fused_window_shift(a),
+                       SO ? sb / R : sb, R, a.seg_buf, a.seg_buf, a.seg_logdec);
 }
 
 template <int PB>
-static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
+static void launch_fused_main(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
+    if (PB == 128 && a.nseg > 1) {
+        // the state-only pass, then the main pass over all segments
+        if constexpr (PB == 128) launch_fused_epi<PB, kEpiState>(a, stream);
+        if (events) hipEventRecord(events[1], stream);
+    }
     const int epi = (a.D_hdim && a.D ? kEpiDhp : 0) | (a.z ? kEpiGate : 0);
     switch (epi) {
         case kEpiDhp: launch_fused_epi<PB, kEpiDhp>(a, stream); break;
@@ -1108,24 +1260,61 @@ static void launch_fused_main(const ForwardArgs &a, hipStream_t stream) {
 // waves) once 32-column ones would; else 32 (one wave).
 static int pick_pb(const ForwardArgs &a) {
     const long cols = (long)a.batch * a.H * a.P;
+    if (a.nseg > 1) return 128;
     if (a.P == 64 && a.H % 2 == 0 && (a.H / a.G) % 2 == 0 && cols / 64 > 256) return 128;
     if (a.P % 64 == 0 && cols / 32 > 256) return 64;
     return 32;
 }
 
-// The fused forward is one launch.
+// Sequence segments of the fused forward.  A layer with few 128-column
+// groups (batch x heads x headdim / 128 below 128) leaves most compute units
+// idle when every workgroup walks the whole sequence, each issue-bound on
+// one pass.  The sequence is then cut into nseg segments (nseg x groups <=
+// 256, at least 64 blocks per segment): a state-only pass forms the state
+// each segment leaves, and the main pass runs every segment from its
+// entering state, chaining those states as it starts.  Needs the 128-column layout (headdim 64, even heads per group).
+// SSD_FUSED_SEGMENTS=n forces n segments where the layout allows (a
+// diagnostic for comparing the two).
+int fused_segments(int batch, int L, int H, int G, int P) {
+    if (!(P == 64 && H % 2 == 0 && (H / G) % 2 == 0)) return 1;
+    const int nblk = fused_nblk(L);
+    const long chains = (long)batch * H * P / 128;
+    int n = 1;
+    if (chains < 128) {
+        n = (int)(256 / chains);
+        if (n > 8) n = 8;
+        while (n > 1 && nblk / n < 64) --n;
+    }
+    if (const char *e = getenv("SSD_FUSED_SEGMENTS")) {
+        int f = atoi(e);
+        if (f >= 1) {
+            if (f > 64) f = 64;
+            while (f > 1 && nblk / f < 4) --f;
+            n = f;
+        }
+    }
+    // every segment non-empty
+    while (n > 1 && seg_blocks_of(nblk, n) * (n - 1) >= nblk) --n;
+    return n;
+}
+int fused_kernel_count(int nseg) { return nseg > 1 ? 2 : 1; }
+const char *const kFusedSegKernelNames[2] = {"k_fused_ssd_state", "k_fused_ssd"};
+
+// The fused forward: one launch, or two with segments.
 template <typename T>
 hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
     if (sizeof(T) != 2) return hipErrorInvalidValue;  // bf16 only (fused_supported)
     hipError_t err;
     if (events && (err = hipEventRecord(events[0], stream)) != hipSuccess) return err;
     switch (pick_pb(a)) {
-        case 128: launch_fused_main<128>(a, stream); break;
-        case 64: launch_fused_main<64>(a, stream); break;
-        default: launch_fused_main<32>(a, stream); break;
+        case 128: launch_fused_main<128>(a, stream, events); break;
+        case 64: launch_fused_main<64>(a, stream, events); break;
+        default: launch_fused_main<32>(a, stream, events); break;
     }
     if ((err = hipGetLastError()) != hipSuccess) return err;
-    if (events && (err = hipEventRecord(events[1], stream)) != hipSuccess) return err;
+    if (events &&
+        (err = hipEventRecord(events[fused_kernel_count(a.nseg)], stream)) != hipSuccess)
+        return err;
     return hipSuccess;
 }
 

@@ -45,6 +45,12 @@ struct ForwardArgs {
     void *cb;        // split path: C B^T per chunk and group, fp32 [b][nc][G][Q][Q]
     float *S;        // split path: chunk states [b][nc][H][P][N]
     int *segst;      // split path, packed sequences: last start per token [b][nc][Q]
+    // fused path, segmented sequence (nseg > 1): the states of the
+    // state-only pass's segments [kSegRatio (nseg - 1)][b][H][P][N] and
+    // their log decays [kSegRatio (nseg - 1)][b][H]
+    int nseg = 1;
+    float *seg_buf = nullptr;
+    float *seg_logdec = nullptr;
                      // (acum_hi / acum_lo / dtT unused there)
 };
 
@@ -89,6 +95,15 @@ int fused_nblk(int L);
 // and whether a row of `row_bytes` (the widest stream) leaves a window of
 // at least 8 blocks.
 int fused_window_shift(const ForwardArgs &a);
+// Sequence segments of the fused forward for a shape (1: one pass), the
+// kernels it launches, and their names when segmented.
+int fused_segments(int batch, int L, int H, int G, int P);
+// The state-only pass of a segmented forward cuts each segment into
+// fused_seg_ratio() pieces (kSegRatio unless overridden).
+constexpr int kSegRatio = 1;
+int fused_seg_ratio();
+int fused_kernel_count(int nseg);
+extern const char *const kFusedSegKernelNames[2];
 bool fused_row_fits(size_t row_bytes);
 
 // k1 of the split path.

@@ -1220,3 +1220,95 @@ def test_fused_reads_and_writes_nothing_past_the_end(dev, oracle_mod, monkeypatc
     yr = (core + skip(inp["D"], inp["x"])) * silu(g["z"])
     check(y.float().cpu().numpy(), yr, "bf16", "guarded y", tok_axis=1)
     check(fin.cpu().numpy(), fr, "bf16", "guarded final state")
+
+
+# ------------------------------------------ the segmented fused forward
+
+SEGMENTED = [
+    # b, L, H, G, init, segments
+    (2, 1000, 4, 1, True, 4),      # 32 blocks: 8 per segment
+    (2, 1000, 4, 2, False, 7),     # uneven: 5 blocks per segment, the last 2
+    (1, 777, 6, 3, True, 3),       # ragged tail in the last segment
+    (2, 300, 132, 2, True, 2),     # four-wave workgroups, two heads of a group each
+]
+
+
+@pytest.mark.parametrize("ratio", [1, 2, 3])
+@pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: "b%d_L%d_H%d_G%d%s_seg%d" % (
+    c[0], c[1], c[2], c[3], "_init" if c[4] else "", c[5]))
+def test_fused_segments_every_element(dev, oracle_mod, monkeypatch, case, ratio):
+    """The fused forward with the sequence cut into segments (state-only
+    pass over `ratio` pieces per segment, then the main pass chaining the
+    pieces' states), forced onto small problems: every element of y and the
+    final state against the oracle."""
+    b, L, H, G, init, nseg = case
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
+    monkeypatch.setenv("SSD_FUSED_SEG_RATIO", str(ratio))
+    _say("segmented case %s" % (case,))
+    inp = make_inputs(b, L, H, 64, 128, G, io_dtype="bf16", init_std=0.1 if init else 0.0,
+                      seed=1400 + L + H)
+    y, fin = gpu_forward(inp, "bf16", 64, dev)
+    yr, fr, _, _ = reference(oracle_mod, inp, want_abs=False)
+    check(y, yr, "bf16", "segmented y", tok_axis=1)
+    check(fin, fr, "bf16", "segmented final")
+
+
+SEGMENTED_GATED = [c for i, c in enumerate(GATED) if i in (0, 4, 7, 8, 9, 10, 12, 13)]
+
+
+@pytest.mark.parametrize("nseg", [2, 3])
+@pytest.mark.parametrize("case", SEGMENTED_GATED, ids=lambda c: "b%d_L%d_H%d" % (c[0], c[1], c[2])
+                         + ("_z" if c[8] else "") + ("_Dhp" if c[9] else "")
+                         + ("_" + c[10] if c[10] else ""))
+def test_fused_segments_with_every_option(dev, oracle_mod, monkeypatch, case, nseg):
+    """Segments with the gate, per-column D, the time-step preprocessing,
+    packed sequences (a start in one segment cuts the decay of the state
+    handed on) and the decay regimes (rescaled and exact blocks on either
+    side of a segment boundary)."""
+    monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    test_gate_and_per_channel_D(dev, oracle_mod, "fused", case)
+
+
+@pytest.mark.parametrize("nseg", [2, 4])
+def test_fused_segments_sequence_starts_at_boundaries(dev, oracle_mod, monkeypatch, nseg):
+    """Packed sequences whose starts fall on a segment's first token, on its
+    last token, and a segment with no start between two with starts."""
+    monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    L = 1024                       # 32 blocks: segments of 16 (nseg 2) or 8 blocks
+    seg_tokens = L // nseg
+    inp = make_inputs(2, L, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=1501)
+    seq = np.zeros((2, L), dtype=np.int32)
+    starts = [seg_tokens, 2 * seg_tokens - 1, seg_tokens + 5] if nseg == 2 else \
+        [seg_tokens, 2 * seg_tokens - 1, 3 * seg_tokens + 17]
+    for k, st in enumerate(sorted(starts)):
+        seq[0, st:] = k + 1
+    seq[1, seg_tokens:] = 1          # row 1: one start, at the first segment boundary
+    _say("segments %d, starts %s" % (nseg, sorted(starts)))
+    _varlen_check(oracle_mod, dev, inp, seq)
+
+
+def test_fused_segments_timed_names_three_kernels(dev, monkeypatch):
+    """The timed forward of a segmented problem names its two kernels and
+    matches the untimed one bit for bit."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import to_torch
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    monkeypatch.setenv("SSD_FUSED_SEGMENTS", "3")
+    inp = make_inputs(2, 1000, 4, 64, 128, 1, io_dtype="bf16", init_std=0.1, seed=1502)
+    t = to_torch(inp, "bf16", dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    y0, f0 = libssd.ssd_chunk_scan_fwd(*args, chunk_len=64)
+    import bench
+    ev = bench.HipEvents()
+    evs = [ev.create() for _ in range(libssd.max_kernels() + 1)]
+    y1, f1, names = libssd.ssd_chunk_scan_fwd_timed(evs, *args, chunk_len=64)
+    torch.cuda.synchronize()
+    for e in evs:
+        ev.destroy(e)
+    _say("kernels %s" % names)
+    assert names == ["k_fused_ssd_state", "k_fused_ssd"]
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
