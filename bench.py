@@ -143,7 +143,8 @@ def kernel_alg_bytes(name, w, es):
     the C B^T diagonal blocks, so its algorithmic bytes are those of the
     forward itself (inputs read once, outputs written once).  The helper
     kernels and the five kernels of the split path count what each must
-    read and write given its own inputs and outputs."""
+    read and write given its own inputs and outputs.  (A segmented fused
+    forward's two passes are taken together, as the forward.)"""
     b, L, H, P, N, G, Q = w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len
     if name == "k_fused_ssd":
         return alg_bytes_forward(w, es)
@@ -208,8 +209,9 @@ def time_graph(fn, ev, reps, warmup=0, per_graph=1, dist=None):
     return ms
 
 
-def time_plain(fn, ev, reps, warmup=0, dist=None):
-    """GPU time of one call of ``fn``, in ms: ``warmup`` untimed calls, a
+def time_plain(fn, ev, reps, warmup=0, dist=None, warm_ms=40.0):
+    """GPU time of one call of ``fn``, in ms: ``warmup`` untimed calls (after
+    ``warm_ms`` of calls that bring the clocks up, when warmup > 0), a
     device synchronisation, then exactly ``reps`` calls with a HIP event on
     the launch stream before each and after the last, and a synchronisation.
     For calls whose GPU time exceeds their host time (tens of microseconds
@@ -217,6 +219,8 @@ def time_plain(fn, ev, reps, warmup=0, dist=None):
     back.  (A HIP graph holding a single forward costs about 10 us more per
     replay than a plain call on this runtime, so graphs are kept for calls
     shorter than their host time, several calls per graph.)"""
+    if warmup > 0 and warm_ms > 0:
+        warm(fn, warm_ms)
     import torch
     for _ in range(warmup):
         fn()
@@ -236,6 +240,20 @@ def time_plain(fn, ev, reps, warmup=0, dist=None):
     for e in evs:
         ev.destroy(e)
     return ms
+
+
+def warm(fn, ms=40.0):
+    """Calls ``fn`` back to back for at least ``ms`` of wall time: after the
+    seconds it takes to draw a workload's inputs the GPU clocks have dropped,
+    and a few warmup calls of a sub-millisecond forward do not bring them
+    back up."""
+    import torch
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    while (time.perf_counter() - t0) * 1e3 < ms:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
 
 
 def host_dispatch_ms(fn, n=50):
@@ -287,7 +305,7 @@ def per_kernel_split(call_timed, ev, steps):
     return dict(zip(names, per_kernel))
 
 
-def time_forward(w, dev, steps, warmup, ev, per_graph=1, prepared=None):
+def time_forward(w, dev, steps, warmup, ev, per_graph=1, prepared=None, warm_ms=40.0):
     """The forward of workload ``w``: ms per call (exactly ``steps`` timed
     calls after ``warmup``; plain calls, or with ``per_graph`` > 1 replays of
     a graph holding that many calls), the spread of single calls, the
@@ -308,7 +326,7 @@ def time_forward(w, dev, steps, warmup, ev, per_graph=1, prepared=None):
     if per_graph > 1:
         gpu_ms = time_graph(call, ev, steps, warmup, per_graph, dist)
     else:
-        gpu_ms = time_plain(call, ev, steps, warmup, dist)
+        gpu_ms = time_plain(call, ev, steps, warmup, dist, warm_ms)
     split = per_kernel_split(call_timed, ev, min(steps, 50))
     host_ms = host_dispatch_ms(call)
     del t, y, fin, ws
@@ -676,6 +694,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="mamba2_2p7b")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--extra-steps", type=int, default=100,
+                    help="timed calls per other workload (counter runs use a few)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads and the decode timing")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
@@ -719,7 +739,8 @@ def main():
         for name in ("tiny_f32", "mamba2_130m", "mamba2_130m_f32", "grouped_g8"):
             wx = WORKLOADS[name]
             # the tiny forward takes microseconds: 50 per captured graph
-            reps, per_graph = (20, 50) if name == "tiny_f32" else (100, 1)
+            reps, per_graph = ((max(1, args.extra_steps // 5), 50) if name == "tiny_f32"
+                               else (args.extra_steps, 1))
             rx = time_forward(wx, dev, reps, 5, ev, per_graph)
             fwd_ms[name] = rx["gpu_ms"]
             esx = 2 if wx.io_dtype == "bf16" else 4
@@ -730,20 +751,22 @@ def main():
                            "per_kernel_ms": {k: round(v, 4) for k, v in rx["per_kernel_ms"].items()},
                            "host_dispatch_ms": round(rx["host_dispatch_ms"], 4)}
             del rx
-        extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev)
+        extra["decode_b256"] = time_decode(WORKLOADS["decode_b256"], dev, ev,
+                                           reps=max(1, min(3, args.extra_steps // 30)))
         fwd_ms["decode_b256"] = extra["decode_b256"]["ms_per_step"]
-        msd = time_forward_dt_proc(w, dev, ev)
+        xs = args.extra_steps
+        msd = time_forward_dt_proc(w, dev, ev, steps=xs, warmup=min(20, xs))
         extra[w.name + "_dt_proc"] = {
             "what": "the same forward on the raw time step: softplus(dt + dt_bias) in the kernels",
             "ms_per_step": round(msd, 4),
             "tokens_per_s": round(w.batch * w.seqlen / (msd * 1e-3), 1)}
-        msv, nseq = time_forward_varlen(w, dev, ev)
+        msv, nseq = time_forward_varlen(w, dev, ev, steps=xs, warmup=min(20, xs))
         extra[w.name + "_varlen"] = {
             "what": "the same forward with %d packed sequences (lengths 1..2048) in its %d rows"
                     % (nseq, w.batch),
             "ms_per_step": round(msv, 4),
             "tokens_per_s": round(w.batch * w.seqlen / (msv * 1e-3), 1)}
-        msg = time_forward_gated(w, dev, ev)
+        msg = time_forward_gated(w, dev, ev, steps=xs, warmup=min(20, xs))
         extra[w.name + "_gated"] = {
             "what": "the same forward with the output gate and a per-(head, column) D: "
                     "y = (C h + D x) silu(z), z read like x",
@@ -752,11 +775,15 @@ def main():
             "alg_bytes": alg_bytes_forward(w, es) + w.batch * w.seqlen * w.nheads * w.headdim * es,
             "frac_hbm": round((alg_bytes_forward(w, es) + w.batch * w.seqlen * w.nheads * w.headdim
                                * es) / (msg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
-        extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(w, dev, ev)
-        extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev)
+        extra["conv1d_" + w.name], extra["conv1d_update_b256"] = time_conv(
+            w, dev, ev, steps=max(1, xs // 2), warmup=min(10, xs))
+        extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev, steps=max(1, xs // 2),
+                                                     warmup=min(10, xs))
 
     # the headline: exactly `steps` timed graph replays of one forward each
-    r = time_forward(w, dev, args.steps, args.warmup, ev, prepared=prepared)
+    # (exactly `warmup` untimed calls: the other workloads and the measured
+    # peaks have just brought the clocks up)
+    r = time_forward(w, dev, args.steps, args.warmup, ev, prepared=prepared, warm_ms=0.0)
     del prepared
     ms_step = r["gpu_ms"]
     fwd_ms[w.name] = ms_step
@@ -769,6 +796,12 @@ def main():
     # one kernel per forward: its average launch is the timed replays' time
     dom_ms = ms_step if len(per) == 1 else per[dom]
     dom_bytes = kernel_alg_bytes(dom, w, es)
+    if "k_fused_ssd_state" in per:
+        # a segmented fused forward: its two passes together do the
+        # forward's work, so the roofline is taken over both
+        dom = "k_fused_ssd_state + k_fused_ssd"
+        dom_ms = sum(per.values())
+        dom_bytes = alg_bytes_forward(w, es)
     dom_gbs = dom_bytes / (dom_ms * 1e-3) / 1e9
     traffic = None
     if os.path.exists(args.traffic_json):

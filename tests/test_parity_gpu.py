@@ -1290,7 +1290,7 @@ def test_fused_segments_sequence_starts_at_boundaries(dev, oracle_mod, monkeypat
     _varlen_check(oracle_mod, dev, inp, seq)
 
 
-def test_fused_segments_timed_names_three_kernels(dev, monkeypatch):
+def test_fused_segments_timed_names_two_kernels(dev, monkeypatch):
     """The timed forward of a segmented problem names its two kernels and
     matches the untimed one bit for bit."""
     import torch

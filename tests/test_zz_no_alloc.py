@@ -5,7 +5,8 @@ Two calls in a row, the second on a smaller problem, so the second runs on a
 scratch array that still holds the first call's intermediates: each must
 equal the workspace entry point bit for bit (the same kernels on the same
 inputs).  fp32 problems take the split path, which uses the scratch; a bf16
-problem takes the fused pass, which needs none."""
+problem takes the fused pass, which needs none unless its sequence is cut
+into segments."""
 import numpy as np
 import pytest
 
@@ -55,6 +56,20 @@ def test_noalloc_matches_workspace_entry_point_twice(dev):
         y_ws, f_ws, y_na, f_na, need = _both(dev, shape, io, Q, seed)
         assert (need > 0) == uses_scratch
         assert torch.isfinite(y_na).all() and torch.isfinite(f_na).all()
+        assert torch.equal(y_na, y_ws), shape
+        assert torch.equal(f_na, f_ws), shape
+
+
+def test_noalloc_segmented_fused_pass(dev, monkeypatch):
+    """The fused pass cut into segments keeps the segments' states in the
+    scratch: a larger then a smaller segmented problem, each equal to the
+    workspace entry point."""
+    import torch
+    monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+    for shape, nseg, seed in (((2, 1000, 4, 64, 128, 2), 4, 64), ((1, 600, 2, 64, 128, 1), 2, 65)):
+        monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
+        y_ws, f_ws, y_na, f_na, need = _both(dev, shape, "bf16", 64, seed)
+        assert need > 0
         assert torch.equal(y_na, y_ws), shape
         assert torch.equal(f_na, f_ws), shape
 
