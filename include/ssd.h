@@ -72,9 +72,15 @@ typedef enum ssd_status {
                                      or infinity in an input or an output  */
 } ssd_status;
 
+/* The element type of x, B, C, y (and z).  Any other value a caller passes
+ * is SSD_ERR_INVALID_ARGUMENT; the two sentinels give the type the range of
+ * int, so that every value a C caller can pass is one of its values (a C++
+ * implementation may then compare it without undefined behaviour). */
 typedef enum ssd_dtype {
+    SSD_DTYPE_RANGE_MIN_ = -0x7FFFFFFF - 1,
     SSD_F32 = 0,
-    SSD_BF16 = 1
+    SSD_BF16 = 1,
+    SSD_DTYPE_RANGE_MAX_ = 0x7FFFFFFF
 } ssd_dtype;
 
 /*
@@ -93,6 +99,13 @@ typedef enum ssd_dtype {
  * result word: they must not run concurrently.  With the variable unset or
  * "0" the call reads it and nothing else changes: no extra kernel runs and
  * nothing synchronises.  The variable is read on every call.
+ *
+ * A second debug mode, SSD_POISON_WORKSPACE (anything but "" or "0"), makes
+ * a forward that uses its workspace (the split path, and the fused path when
+ * it cuts the sequence into segments) first fill the whole workspace with
+ * quiet NaNs, on `stream`, so that any intermediate read before a kernel of
+ * the same call wrote it reaches the outputs (where SSD_CHECK_FINITE, or the
+ * caller, sees it).  It adds one fill kernel and nothing else.
  */
 
 /* Version of this ABI (SSD_ABI_VERSION of the built library). */

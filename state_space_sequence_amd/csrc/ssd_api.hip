@@ -138,6 +138,11 @@ ssd_status choose_path(int /*seqlen*/, int nheads, int ngroups, int headdim, int
 
 // The opt-in non-finite check: SSD_CHECK_FINITE set to anything but "" or
 // "0".  Read on every call, like SSD_FORWARD_PATH.
+bool poison_requested() {
+    const char *e = getenv("SSD_POISON_WORKSPACE");
+    return e && e[0] && strcmp(e, "0") != 0;
+}
+
 bool finite_check_requested() {
     const char *e = getenv("SSD_CHECK_FINITE");
     return e && e[0] && strcmp(e, "0") != 0;
@@ -311,6 +316,12 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     fc.input(z, z ? nx : 0, es);
 
     hipError_t err;
+    // Debug mode (SSD_POISON_WORKSPACE set to anything but "" or "0"): the
+    // workspace the call uses is filled with NaN first, so an intermediate
+    // read before any kernel of the call wrote it shows in the outputs.
+    if (lay.total > 0 && poison_requested()) {
+        if (ssd::launch_poison(workspace, lay.total, stream) != hipSuccess) return SSD_ERR_HIP;
+    }
     if (path == ssd::Path::Split)
         err = io_dtype == SSD_BF16 ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
                                    : ssd::launch_split_forward<float>(a, stream, events);

@@ -76,6 +76,26 @@ hipError_t launch_nonfinite_scan(const void *p, size_t nelems, int elem_bytes, u
     return hipGetLastError();
 }
 
+// The workspace poison of the debug mode: every 32-bit word of the
+// workspace becomes a quiet NaN (0x7FC00000) before a forward, so a kernel
+// that reads an element no earlier kernel of the call wrote passes the NaN
+// on to the outputs.  A plain fill kernel (no memset node).
+__global__ void __launch_bounds__(256) k_poison(unsigned *__restrict__ p, size_t nwords) {
+    const size_t stride = (size_t)gridDim.x * blockDim.x;
+    for (size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x; i < nwords; i += stride)
+        p[i] = 0x7FC00000u;
+}
+
+hipError_t launch_poison(void *p, size_t bytes, hipStream_t stream) {
+    const size_t nwords = bytes / 4;
+    if (!p || nwords == 0) return hipSuccess;
+    size_t blocks = (nwords + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(k_poison, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<unsigned *>(p), nwords);
+    return hipGetLastError();
+}
+
 hipError_t read_nonfinite(unsigned *out, hipStream_t stream) {
     hipError_t err = hipMemcpyFromSymbolAsync(out, HIP_SYMBOL(g_nonfinite), sizeof(unsigned), 0,
                                               hipMemcpyDeviceToHost, stream);

@@ -168,6 +168,9 @@ hipError_t launch_gated_rmsnorm(const NormArgs &a, hipStream_t stream);
 // values OR-ing `bit` into the flag when one is a NaN or an infinity, and
 // read the flag back (synchronises `stream`).
 constexpr unsigned kNonfiniteInput = 1u, kNonfiniteOutput = 2u;
+// Fills `bytes` of device memory with quiet-NaN words (the workspace
+// poison of the SSD_POISON_WORKSPACE debug mode).
+hipError_t launch_poison(void *p, size_t bytes, hipStream_t stream);
 hipError_t launch_nonfinite_reset(hipStream_t stream);
 hipError_t launch_nonfinite_scan(const void *p, size_t nelems, int elem_bytes, unsigned bit,
                                  hipStream_t stream);

@@ -1312,3 +1312,47 @@ def test_fused_segments_timed_names_two_kernels(dev, monkeypatch):
     _say("kernels %s" % names)
     assert names == ["k_fused_ssd_state", "k_fused_ssd"]
     assert torch.equal(y0, y1) and torch.equal(f0, f1)
+
+
+# ------------------------------------------ the NaN-poisoned workspace
+
+POISON = [
+    # path, io, b, L, H, P, N, G, Q, segments (fused), packed sequences
+    ("split", "f32", 2, 777, 4, 64, 128, 2, 128, 0, False),
+    ("split", "f32", 2, 333, 3, 32, 64, 1, 16, 0, True),
+    ("split", "bf16", 2, 520, 4, 48, 32, 2, 256, 0, False),
+    ("split", "bf16", 1, 300, 66, 64, 128, 1, 64, 0, True),
+    ("fused", "bf16", 2, 1000, 4, 64, 128, 2, 64, 4, False),
+    ("fused", "bf16", 2, 1000, 4, 64, 128, 1, 64, 3, True),
+]
+
+
+@pytest.mark.parametrize("case", POISON, ids=lambda c: "%s_%s_b%d_L%d_H%d_P%d_N%d_G%d_Q%d_seg%d" % (
+    c[:10]) + ("_varlen" if c[10] else ""))
+def test_workspace_poisoned_with_nan(dev, oracle_mod, monkeypatch, case):
+    """SSD_POISON_WORKSPACE fills the workspace with NaN before the call:
+    every intermediate a kernel reads must have been written by an earlier
+    kernel of the same call (with the non-finite check on, the call must
+    return SSD_OK), and the result is unchanged bit for bit."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_seq_idx, to_torch
+    path, io, b, L, H, P, N, G, Q, nseg, varlen = case
+    monkeypatch.setenv("SSD_FORWARD_PATH", path)
+    if nseg:
+        monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
+    inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=1600 + L)
+    t = to_torch(inp, io, dev)
+    kw = dict(chunk_len=Q)
+    if varlen:
+        kw["seq_idx"] = torch.from_numpy(make_seq_idx(b, L, seed=1601, max_len=50)).to(dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"])
+    y0, f0 = libssd.ssd_chunk_scan_fwd(*args, **kw)
+    monkeypatch.setenv("SSD_POISON_WORKSPACE", "1")
+    monkeypatch.setenv("SSD_CHECK_FINITE", "1")
+    need = libssd.ssd_chunk_scan_fwd_workspace_size(b, L, H, P, N, G, Q,
+                                                    libssd.SSD_BF16 if io == "bf16" else libssd.SSD_F32)
+    assert need > 0
+    y1, f1 = libssd.ssd_chunk_scan_fwd(*args, **kw)
+    torch.cuda.synchronize()
+    assert torch.equal(y0, y1) and torch.equal(f0, f1)
