@@ -193,11 +193,23 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
                int G, int P, int N, int nc, int Q, const int *__restrict__ segst) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int KB = 32;
-    constexpr int PITCH = KB + 16 / (int)sizeof(T);
+    // fp32: rows of 32 floats, two to a 64-float line, 4-float chunks XOR-swizzled per row; the staging stores
+    // (4 consecutive tokens of 16 rows 4 apart per instruction) and the 16-byte fragment reads (16 consecutive
+    // rows) then fall on distinct banks at headdim 64 (2-way at dstate 128).  bf16: padded rows.
+    constexpr bool SW = sizeof(T) == 4;
+    constexpr int PITCH = SW ? KB : KB + 16 / (int)sizeof(T);
     constexpr int TPW = kK3TilesPerWave;
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *XT = reinterpret_cast<T *>(smem_raw);
     T *BT = XT + (size_t)P * PITCH;
+    auto at = [](int row, int s) -> int {
+        if constexpr (SW) {
+            const int g = ((row >> 1) + (row >> 5)) & 15;
+            return (row >> 1) * 64 + 4 * ((((row & 1) * 8 + (s >> 2)) ^ g) & 15) + (s & 3);
+        } else {
+            return row * PITCH + s;
+        }
+    };
 
     const int c = blockIdx.x, h = blockIdx.y % H, tg = blockIdx.y / H, b = blockIdx.z;
     const int g = h / (H / G);
@@ -230,7 +242,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
             }
 #pragma unroll
             for (int jj = 0; jj < VEC; ++jj)
-                XT[(p0 + jj) * PITCH + sl] = from_f32<T>(to_f32(f[jj]) * w);
+                XT[at(p0 + jj, sl)] = from_f32<T>(to_f32(f[jj]) * w);
         }
         const int nv = N / VEC;
         for (int v = tid; v < KB * nv; v += 256) {
@@ -239,7 +251,7 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
             typename Mma<T>::frag f = zero_frag<T>();
             if (s < Q && t < L) f = load_frag(Bm + (((size_t)b * L + t) * G + g) * N + n0);
 #pragma unroll
-            for (int jj = 0; jj < VEC; ++jj) BT[(n0 + jj) * PITCH + sl] = f[jj];
+            for (int jj = 0; jj < VEC; ++jj) BT[at(n0 + jj, sl)] = f[jj];
         }
         __syncthreads();
 #pragma unroll
@@ -249,8 +261,8 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
                 const int t = tg * 4 * TPW + wave + 4 * i;
                 if (t >= ntiles) continue;
                 const int pt = t / ntn, nt = t % ntn;
-                typename Mma<T>::frag a = load_frag(XT + (pt * 16 + r) * PITCH + kk + VEC * q);
-                typename Mma<T>::frag bb = load_frag(BT + (nt * 16 + r) * PITCH + kk + VEC * q);
+                typename Mma<T>::frag a = load_frag(XT + at(pt * 16 + r, kk + VEC * q));
+                typename Mma<T>::frag bb = load_frag(BT + at(nt * 16 + r, kk + VEC * q));
                 acc[i] = Mma<T>::mma(a, bb, acc[i]);
             }
         }
@@ -340,11 +352,22 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
               const T *__restrict__ z, int D_hdim, const int *__restrict__ segst) {
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SB = 64;
-    constexpr int PITCH = SB + 16 / (int)sizeof(T);
+    constexpr int PITCH = SB + 16 / (int)sizeof(T);          // rows of the M tile (and of bf16 x^T)
+    // fp32 x^T: rows of 64 floats with their 4-float chunks XOR-swizzled by (row + row / 16) mod 16, so the
+    // staging stores (4 consecutive tokens of 16 rows 4 apart) and the 16-byte fragment reads (16 consecutive
+    // rows) fall on distinct banks at headdim 64; bf16 x^T: padded rows
+    constexpr bool SW = sizeof(T) == 4;
+    constexpr int XPITCH = SW ? SB : PITCH;
     constexpr int MAXPT = kMaxHeaddim / 16;
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    T *XT = reinterpret_cast<T *>(smem_raw);                 // [P][PITCH]: x^T of the s-block
-    T *MT = XT + (size_t)P * PITCH;                           // [64][PITCH]: M of (l-block, s-block)
+    T *XT = reinterpret_cast<T *>(smem_raw);                 // [P][XPITCH]: x^T of the s-block
+    T *MT = XT + (size_t)P * XPITCH;                          // [64][PITCH]: M of (l-block, s-block)
+    auto at = [](int row, int s) -> int {
+        if constexpr (SW)
+            return row * SB + 4 * (((s >> 2) ^ (row + (row >> 4))) & 15) + (s & 3);
+        else
+            return row * PITCH + s;
+    };
     float *s_hi = reinterpret_cast<float *>(MT + SB * PITCH);  // the s-block's prefix sums, dt
     float *s_lo = s_hi + SB;
     float *s_dt = s_lo + SB;
@@ -416,7 +439,7 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
             typename Mma<T>::frag f = zero_frag<T>();
             if (s < Q && t < L) f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
 #pragma unroll
-            for (int jj = 0; jj < VEC; ++jj) XT[(p0 + jj) * PITCH + sl] = f[jj];
+            for (int jj = 0; jj < VEC; ++jj) XT[at(p0 + jj, sl)] = f[jj];
         }
         if (tid < SB) {
             const int s = sb * SB + tid;
@@ -449,7 +472,7 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
 #pragma unroll
             for (int pt = 0; pt < MAXPT; ++pt) {
                 if (pt >= npt) continue;
-                typename Mma<T>::frag bb = load_frag(XT + (pt * 16 + r) * PITCH + kk + VEC * q);
+                typename Mma<T>::frag bb = load_frag(XT + at(pt * 16 + r, kk + VEC * q));
                 acc[pt] = Mma<T>::mma(m, bb, acc[pt]);
             }
         }
@@ -466,7 +489,7 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
         for (int pt = 0; pt < MAXPT; ++pt) {
             if (pt >= npt) continue;
             const int p = pt * 16 + r;
-            const float xv = to_f32(XT[p * PITCH + (l - lb * SB)]);
+            const float xv = to_f32(XT[at(p, l - lb * SB)]);
             const float dp = D_hdim && D ? D[(size_t)h * P + p] : Dh;
             float o = acc[pt][i] + dp * xv;
             if (z) o *= silu_f32(to_f32(z[ro + p]));
