@@ -33,10 +33,15 @@
  *    (no error is reported: A stays on the device, unread by the host).
  *  - x, B, C and y share one element type, `io_dtype` (fp32 or bf16).
  *    dt, A, D and every state are fp32.  Accumulation is fp32.
- *  - The caller owns every buffer.  The library allocates no device memory,
- *    keeps no state between calls and is reentrant.  Work is enqueued on
- *    `stream` (a hipStream_t; NULL = the legacy default stream) and nothing
- *    synchronises the host: results are ready when the stream is.
+ *  - The caller owns every buffer.  The library allocates no device memory
+ *    and is reentrant.  Work is enqueued on `stream` (a hipStream_t; NULL =
+ *    the legacy default stream) and nothing synchronises the host: results
+ *    are ready when the stream is.  The one state it keeps: a forward on
+ *    the fused path that cuts a long sequence of a narrow layer into
+ *    segments (see ssd_chunk_scan_fwd) forks part of its work onto an
+ *    auxiliary stream of its own and joins it back to `stream` with two
+ *    events; that stream and the events are created per device at the first
+ *    such call (default priority) and kept until the process ends.
  *  - Errors are reported as status codes, never by exceptions or aborts.
  *    Argument validation happens before anything is enqueued, so a call that
  *    returns SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED or
@@ -123,7 +128,10 @@ const char *ssd_status_string(ssd_status status);
  * ssd_chunk_scan_fwd_timed): the split path keeps the decay prefix sums,
  * the C B^T blocks and every chunk state (batch * nchunks * nheads *
  * headdim * dstate fp32); the fused path keeps every intermediate on chip
- * and needs none (0 bytes).
+ * and needs none (0 bytes), except when it cuts the sequence into segments
+ * (below): then it keeps the state each segment but the last leaves,
+ * (nsegments - 1) * batch * nheads * headdim * dstate fp32, and their log
+ * decays.
  */
 ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
                                              int headdim, int dstate,
@@ -151,6 +159,16 @@ ssd_status ssd_chunk_scan_fwd_workspace_size(int batch, int seqlen, int nheads,
  * of token seqlen-1.  y is rounded to io_dtype (round to nearest even for
  * bf16).  final_state may alias initial_state (a cache updated in place);
  * no other buffers may overlap.
+ *
+ * Sequence segments (fused path).  When the layer has fewer than 128
+ * groups of 128 columns (batch * nheads * headdim / 128) and a long enough
+ * sequence, the fused forward cuts the sequence into segments so that every
+ * compute unit has work: segment 0 runs while a state-only pass forms the
+ * state each later segment but the last leaves from zero (on the auxiliary
+ * stream, see above), then the other segments run, each from the state
+ * entering it, chained from those states (the inter-chunk recurrence of the
+ * burn-mamba rustdoc's Step 3, Eq. 22, over segments).  The results differ
+ * from a single pass by rounding only.
  */
 ssd_status ssd_chunk_scan_fwd(const void *x, const float *dt, const float *A,
                               const void *B, const void *C, const float *D,

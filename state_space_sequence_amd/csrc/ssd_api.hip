@@ -56,6 +56,45 @@ hipError_t scratch_address(hipStream_t stream, void **out) {
     return hipSuccess;
 }
 
+// The auxiliary stream and fork/join events on which a segmented fused
+// forward overlaps its first phase: one set per device, created with that
+// device current at the first segmented call and kept until the process
+// ends (default priority; non-blocking with respect to the null stream).
+// The mutex is held across each call's fork ... join sequence, so that
+// concurrent calls never re-record an event between another call's record
+// and its wait.
+struct Side {
+    hipStream_t stream = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr;
+};
+std::mutex g_side_mu;
+Side g_side[kMaxDevices];
+
+hipError_t side_for(hipStream_t stream, Side *out) {
+    int cur = 0, dev = 0;
+    hipError_t err = hipGetDevice(&cur);
+    if (err != hipSuccess) return err;
+    dev = cur;
+    if (stream && (err = hipStreamGetDevice(stream, &dev)) != hipSuccess) return err;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    Side &sd = g_side[dev];
+    if (!sd.stream) {
+        if (dev != cur && (err = hipSetDevice(dev)) != hipSuccess) return err;
+        Side n;
+        err = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
+        if (err == hipSuccess) err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
+        if (err == hipSuccess) err = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (dev != cur) {
+            const hipError_t back = hipSetDevice(cur);
+            if (err == hipSuccess) err = back;
+        }
+        if (err != hipSuccess) return err;
+        sd = n;
+    }
+    *out = sd;
+    return hipSuccess;
+}
+
 size_t round_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 
 bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
@@ -204,10 +243,11 @@ Layout forward_layout(int batch, int seqlen, int nheads, int headdim, int dstate
         l.total = l.segst + round_up(b * nc * Q * sizeof(int));
     } else {
         // the fused kernel keeps every intermediate on chip; a segmented
-        // sequence needs the states of its segments and their log decays
+        // sequence needs the states segments 0 .. nseg - 2 leave and their
+        // log decays
         l.acum_hi = l.acum_lo = l.dtT = l.cb = l.S = l.segst = 0;
         l.nseg = ssd::fused_segments(batch, seqlen, nheads, ngroups, headdim);
-        const size_t ns = (size_t)ssd::fused_seg_ratio() * (l.nseg - 1);
+        const size_t ns = (size_t)(l.nseg - 1);
         l.seg_buf = 0;
         l.seg_logdec = round_up(ns * b * H * P * N * sizeof(float));
         l.total = l.nseg > 1 ? l.seg_logdec + round_up(ns * b * H * sizeof(float)) : 0;
@@ -322,12 +362,24 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     if (lay.total > 0 && poison_requested()) {
         if (ssd::launch_poison(workspace, lay.total, stream) != hipSuccess) return SSD_ERR_HIP;
     }
-    if (path == ssd::Path::Split)
+    if (path == ssd::Path::Split) {
         err = io_dtype == SSD_BF16 ? ssd::launch_split_forward<ssd::bf16>(a, stream, events)
                                    : ssd::launch_split_forward<float>(a, stream, events);
-    else
+    } else if (a.nseg > 2 && !noalloc) {
+        // (the no-allocation entry point creates no stream: its phases run
+        // one after the other)
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        Side sd;
+        if (side_for(stream, &sd) != hipSuccess) return SSD_ERR_HIP;
+        a.side = sd.stream;
+        a.ev_fork = sd.fork;
+        a.ev_join = sd.join;
         err = io_dtype == SSD_BF16 ? ssd::launch_fused_forward<ssd::bf16>(a, stream, events)
                                    : ssd::launch_fused_forward<float>(a, stream, events);
+    } else {
+        err = io_dtype == SSD_BF16 ? ssd::launch_fused_forward<ssd::bf16>(a, stream, events)
+                                   : ssd::launch_fused_forward<float>(a, stream, events);
+    }
     if (err != hipSuccess) return SSD_ERR_HIP;
     if (events) {
         // unused trailing events are recorded too, so every handle is valid

@@ -351,8 +351,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             const float *__restrict__ D, const float *init_arg, float *final_arg,
             bf16 *__restrict__ y, int L, int H, int G, int P, int nblk, const DtProc dtp,
             const int *__restrict__ seq_idx, const bf16 *__restrict__ z, int win_shift,
-            int seg_blocks, int seg_ratio, const float *seg_in, float *seg_out,
-            float *seg_logdec) {
+            const SegPlan plan, const float *seg_in, float *seg_out, float *seg_logdec) {
     constexpr bool SO = (EPI & kEpiState) != 0;
     typedef Fused<PB, SO> S;
     constexpr int NW = S::NW, N = S::N;
@@ -373,9 +372,10 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     // the consecutive range x * n / 8 .. of (batch, column block) pairs, so
     // a batch's workgroups share few L2s and fetch its C, B and dt rows a few
     // times instead of once per XCD.
-    // The sequence may be cut into gridDim.z segments of seg_blocks blocks
-    // (the segment index varies slowest, so a segment's workgroups sit
-    // together on the XCDs as a batch's do).
+    // The sequence may be cut into segments (SegPlan); this launch runs
+    // segments plan.base .. plan.base + gridDim.z - 1 (the segment index
+    // varies slowest, so a segment's workgroups sit together on the XCDs as
+    // a batch's do).
     int c0, b, seg;
     {
         const int nc = H * P / PB, nb = gridDim.y, n = nc * nb * gridDim.z;
@@ -383,22 +383,21 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
         const int v = (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
         c0 = (v % nc) * PB;
         b = (v / nc) % nb;
-        seg = v / nc / nb;
+        seg = plan.base + v / nc / nb;
     }
     // the workgroup's blocks kb0 .. kb0 + nloc - 1 (the host makes every
     // segment non-empty)
-    const int kb0 = seg * seg_blocks;
-    const int nloc = min(nblk, kb0 + seg_blocks) - kb0;
+    const int kb0 = seg == 0 ? 0 : plan.first + (seg - 1) * plan.len;
+    const int nloc = (seg == 0 ? plan.first : min(nblk, kb0 + plan.len)) - kb0;
     // The state entering the segment: the initial state in segment 0; zero
-    // in the other segments of the state-only pass; in the main pass,
-    // chained from the state-only pass's outputs (below).  The state leaving
-    // it: the final state after the last segment (main pass); every
-    // segment's own (state-only pass).
+    // in the state-only pass; in the main pass, chained from the states of
+    // the earlier segments (below).  The state leaving it: the final state
+    // after the last segment; segment 0's into seg_out[0] when there are
+    // more; every segment's own into seg_out[seg] (state-only pass).
     const size_t bHPN = (size_t)gridDim.y * H * P * N;
     const float *init = seg == 0 ? init_arg : (SO ? nullptr : seg_in);
-    (void)seg_ratio;
     float *final_state = SO ? seg_out + (size_t)seg * bHPN
-                            : (seg == (int)gridDim.z - 1 ? final_arg : nullptr);
+                            : (seg == plan.nseg - 1 ? final_arg : (seg == 0 ? seg_out : nullptr));
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int g = (c0 / P) / (H / G);          // the workgroup's B / C group
@@ -843,16 +842,14 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
             }
         }
     }
-    if (!SO && seg > 0) {
-        // Segment s of the main pass.  The state-only pass cut the sequence
-        // into seg_ratio times as many segments: seg_in[0] is the state
-        // entering its segment 1 (it ran segment 0 from the initial state)
-        // and seg_in[k], k >= 1, the state its segment k leaves from zero;
-        // with d_k = exp(logdec_k) the state entering k + 1 is
+    if (!SO && seg > 1) {
+        // Segment s of the main pass: seg_in[0] is the state leaving segment
+        // 0 (its main pass wrote it) and seg_in[k], k >= 1, the state
+        // segment k leaves from zero (the state-only pass); with
+        // d_k = exp(logdec_k) the state entering k + 1 is
         // d_k (state entering k) + seg_in[k] (the inter-chunk recurrence of
-        // the rustdoc's Step 3, over segments), chained here up to the
-        // start of this segment, its segment seg_ratio * s.
-        for (int k = 1; k < seg_ratio * seg; ++k) {
+        // the rustdoc's Step 3, over segments), chained here up to s.
+        for (int k = 1; k < seg; ++k) {
             const float d = __expf(seg_logdec[((size_t)k * gridDim.y + b) * H + hw]);
             const float *src = seg_in + (size_t)k * bHPN + (bh * P + pr) * N;
 #pragma unroll
@@ -1200,56 +1197,97 @@ int fused_window_shift(const ForwardArgs &a) {
 }
 bool fused_row_fits(size_t row_bytes) { return window_shift_for(row_bytes) >= 3; }
 
-// The state-only pass of a segmented forward cuts each segment into this
-// many pieces (kSegRatio; SSD_FUSED_SEG_RATIO = 1 .. 4 overrides it, a
-// diagnostic for comparing the two).
-int fused_seg_ratio() {
-    if (const char *e = getenv("SSD_FUSED_SEG_RATIO")) {
-        const int r = atoi(e);
-        if (r >= 1 && r <= 4) return r;
+// The segments of a forward of nblk blocks cut into nseg: segment 0 has
+// `first` blocks and runs while the state-only pass covers segments 1 ..
+// nseg - 2, every later segment `len` blocks.  The two kernels of the
+// first phase share the chip and slow each other; measured on the 8-group
+// layer, segment 0 as long as the others balances the phases best (0.215 ms
+// against 0.2165 at 80% and 0.226 at 150%).  SSD_FUSED_SEG0_PCT sets the
+// percentage (a diagnostic).
+static SegPlan seg_plan(int nblk, int nseg) {
+    SegPlan p;
+    p.nseg = nseg;
+    p.base = 0;
+    if (nseg <= 1) {
+        p.first = nblk;
+        p.len = nblk;
+        return p;
     }
-    return kSegRatio;
-}
-
-// Segments of a segmented forward: blocks per segment, a multiple of the
-// state-only pass's ratio.
-static int seg_blocks_of(int nblk, int nseg) {
-    const int R = fused_seg_ratio();
-    const int q = (nblk + nseg - 1) / nseg;
-    return (q + R - 1) / R * R;
+    int pct = 100;
+    if (const char *e = getenv("SSD_FUSED_SEG0_PCT")) {
+        const int v = atoi(e);
+        if (v >= 10 && v <= 200) pct = v;
+    }
+    // len ~ nblk / (nseg - 1 + pct / 100), first = what is left
+    p.len = (int)(((long)nblk * 100 + (long)(nseg - 1) * 100 + pct - 1) / ((long)(nseg - 1) * 100 + pct));
+    if (p.len < 1) p.len = 1;
+    p.first = nblk - (nseg - 1) * p.len;
+    while (p.first < 1 && p.len > 1) {
+        --p.len;
+        p.first = nblk - (nseg - 1) * p.len;
+    }
+    return p;
 }
 
 template <int PB, int EPI>
-static void launch_fused_epi(const ForwardArgs &a, hipStream_t stream) {
+static void launch_fused_epi(const ForwardArgs &a, hipStream_t stream, SegPlan plan, int nz) {
     constexpr bool SO = (EPI & kEpiState) != 0;
     typedef Fused<PB, SO> S;
-    const int nblk = fused_nblk(a.L);
-    // the state-only pass runs the first nseg - 1 segments, each cut into
-    // kSegRatio pieces
-    const int sb = seg_blocks_of(nblk, a.nseg);
-    const int R = fused_seg_ratio();
-    const int nz = SO ? R * (a.nseg - 1) : a.nseg;
     hipLaunchKernelGGL((k_fused_ssd<PB, EPI>), dim3(a.H * a.P / PB, a.batch, nz), dim3(S::NT), 0,
                        stream, (const bf16 *)a.x, a.dt, a.A, (const bf16 *)a.B, (const bf16 *)a.C,
-                       a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P, nblk, a.dtp,
-                       a.seq_idx, (const bf16 *)a.z, fused_window_shift(a),
-                       SO ? sb / R : sb, R, a.seg_buf, a.seg_buf, a.seg_logdec);
+                       a.D, a.init, a.final_state, (bf16 *)a.y, a.L, a.H, a.G, a.P,
+                       fused_nblk(a.L), a.dtp, a.seq_idx, (const bf16 *)a.z, fused_window_shift(a),
+                       plan, a.seg_buf, a.seg_buf, a.seg_logdec);
 }
 
 template <int PB>
-static void launch_fused_main(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
-    if (PB == 128 && a.nseg > 1) {
-        // the state-only pass, then the main pass over all segments
-        if constexpr (PB == 128) launch_fused_epi<PB, kEpiState>(a, stream);
-        if (events) hipEventRecord(events[1], stream);
-    }
+static void launch_main_epi(const ForwardArgs &a, hipStream_t stream, SegPlan plan, int nz) {
     const int epi = (a.D_hdim && a.D ? kEpiDhp : 0) | (a.z ? kEpiGate : 0);
     switch (epi) {
-        case kEpiDhp: launch_fused_epi<PB, kEpiDhp>(a, stream); break;
-        case kEpiGate: launch_fused_epi<PB, kEpiGate>(a, stream); break;
-        case kEpiDhp | kEpiGate: launch_fused_epi<PB, kEpiDhp | kEpiGate>(a, stream); break;
-        default: launch_fused_epi<PB, 0>(a, stream); break;
+        case kEpiDhp: launch_fused_epi<PB, kEpiDhp>(a, stream, plan, nz); break;
+        case kEpiGate: launch_fused_epi<PB, kEpiGate>(a, stream, plan, nz); break;
+        case kEpiDhp | kEpiGate: launch_fused_epi<PB, kEpiDhp | kEpiGate>(a, stream, plan, nz); break;
+        default: launch_fused_epi<PB, 0>(a, stream, plan, nz); break;
     }
+}
+
+// One pass, or with segments two phases:
+//   1. the main pass over segment 0 (on `stream`; it leaves its state in
+//      seg_buf[0]) and, at the same time on the auxiliary stream a.side,
+//      the state-only pass over segments 1 .. nseg - 2 (forked from and
+//      joined back to `stream` with two events; without a.side the two
+//      run one after the other on `stream`);
+//   2. the main pass over segments 1 .. nseg - 1.
+template <int PB>
+static hipError_t launch_fused_main(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
+    const int nblk = fused_nblk(a.L);
+    SegPlan plan = seg_plan(nblk, PB == 128 ? a.nseg : 1);
+    if (plan.nseg <= 1) {
+        launch_main_epi<PB>(a, stream, plan, 1);
+        return hipSuccess;
+    }
+    hipError_t err;
+    const bool fork = a.side != nullptr && plan.nseg > 2;
+    hipStream_t so_stream = fork ? a.side : stream;
+    if (fork) {
+        if ((err = hipEventRecord(a.ev_fork, stream)) != hipSuccess) return err;
+        if ((err = hipStreamWaitEvent(a.side, a.ev_fork, 0)) != hipSuccess) return err;
+    }
+    SegPlan so = plan;
+    so.base = 1;
+    if constexpr (PB == 128) {
+        if (plan.nseg > 2) launch_fused_epi<PB, kEpiState>(a, so_stream, so, plan.nseg - 2);
+    }
+    launch_main_epi<PB>(a, stream, plan, 1);
+    if (fork) {
+        if ((err = hipEventRecord(a.ev_join, a.side)) != hipSuccess) return err;
+        if ((err = hipStreamWaitEvent(stream, a.ev_join, 0)) != hipSuccess) return err;
+    }
+    if (events && (err = hipEventRecord(events[1], stream)) != hipSuccess) return err;
+    SegPlan rest = plan;
+    rest.base = 1;
+    launch_main_epi<PB>(a, stream, rest, plan.nseg - 1);
+    return hipSuccess;
 }
 
 // Columns per workgroup.  One workgroup per compute unit is the target
@@ -1269,21 +1307,24 @@ static int pick_pb(const ForwardArgs &a) {
 // Sequence segments of the fused forward.  A layer with few 128-column
 // groups (batch x heads x headdim / 128 below 128) leaves most compute units
 // idle when every workgroup walks the whole sequence, each issue-bound on
-// one pass.  The sequence is then cut into nseg segments (nseg x groups <=
-// 256, at least 64 blocks per segment): a state-only pass forms the state
-// each segment leaves, and the main pass runs every segment from its
-// entering state, chaining those states as it starts.  Needs the 128-column layout (headdim 64, even heads per group).
-// SSD_FUSED_SEGMENTS=n forces n segments where the layout allows (a
-// diagnostic for comparing the two).
+// one pass.  The sequence is then cut into nseg segments, with
+// (nseg - 1) x groups <= 256 and at least 64 blocks per later segment: while
+// the main pass runs segment 0, a state-only pass forms the state segments
+// 1 .. nseg - 2 leave from zero; then the main pass runs the other
+// segments, each from its entering state, which it chains from those states
+// as it starts.  Needs the 128-column layout (headdim 64, even heads per
+// group).  SSD_FUSED_SEGMENTS=n forces n segments where the layout allows
+// (a diagnostic for comparing the two).
 int fused_segments(int batch, int L, int H, int G, int P) {
     if (!(P == 64 && H % 2 == 0 && (H / G) % 2 == 0)) return 1;
     const int nblk = fused_nblk(L);
     const long chains = (long)batch * H * P / 128;
     int n = 1;
     if (chains < 128) {
-        n = (int)(256 / chains);
-        if (n > 8) n = 8;
+        n = 1 + (int)(256 / chains);
+        if (n > 9) n = 9;
         while (n > 1 && nblk / n < 64) --n;
+        if (n == 2) n = 1;     // (no segment would overlap the first)
     }
     if (const char *e = getenv("SSD_FUSED_SEGMENTS")) {
         int f = atoi(e);
@@ -1293,12 +1334,12 @@ int fused_segments(int batch, int L, int H, int G, int P) {
             n = f;
         }
     }
-    // every segment non-empty
-    while (n > 1 && seg_blocks_of(nblk, n) * (n - 1) >= nblk) --n;
+    if (n > nblk) n = nblk;
     return n;
 }
 int fused_kernel_count(int nseg) { return nseg > 1 ? 2 : 1; }
-const char *const kFusedSegKernelNames[2] = {"k_fused_ssd_state", "k_fused_ssd"};
+// (the first phase's two kernels run on two streams and are timed together)
+const char *const kFusedSegKernelNames[2] = {"k_fused_ssd_state+seg0", "k_fused_ssd"};
 
 // The fused forward: one launch, or two with segments.
 template <typename T>
@@ -1307,10 +1348,11 @@ hipError_t launch_fused_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     hipError_t err;
     if (events && (err = hipEventRecord(events[0], stream)) != hipSuccess) return err;
     switch (pick_pb(a)) {
-        case 128: launch_fused_main<128>(a, stream, events); break;
-        case 64: launch_fused_main<64>(a, stream, events); break;
-        default: launch_fused_main<32>(a, stream, events); break;
+        case 128: err = launch_fused_main<128>(a, stream, events); break;
+        case 64: err = launch_fused_main<64>(a, stream, events); break;
+        default: err = launch_fused_main<32>(a, stream, events); break;
     }
+    if (err != hipSuccess) return err;
     if ((err = hipGetLastError()) != hipSuccess) return err;
     if (events &&
         (err = hipEventRecord(events[fused_kernel_count(a.nseg)], stream)) != hipSuccess)

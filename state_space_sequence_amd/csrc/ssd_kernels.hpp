@@ -45,12 +45,17 @@ struct ForwardArgs {
     void *cb;        // split path: C B^T per chunk and group, fp32 [b][nc][G][Q][Q]
     float *S;        // split path: chunk states [b][nc][H][P][N]
     int *segst;      // split path, packed sequences: last start per token [b][nc][Q]
-    // fused path, segmented sequence (nseg > 1): the states of the
-    // state-only pass's segments [kSegRatio (nseg - 1)][b][H][P][N] and
-    // their log decays [kSegRatio (nseg - 1)][b][H]
+    // fused path, segmented sequence (nseg > 1): the states segments
+    // 0 .. nseg - 2 leave [nseg - 1][b][H][P][N] (segment 0's from the
+    // initial state, the others' from zero) and their log decays
+    // [nseg - 1][b][H]
     int nseg = 1;
     float *seg_buf = nullptr;
     float *seg_logdec = nullptr;
+    // an auxiliary stream and two events on which the segmented forward
+    // overlaps its first phase (null: the phases run on the caller's stream)
+    hipStream_t side = nullptr;
+    hipEvent_t ev_fork = nullptr, ev_join = nullptr;
                      // (acum_hi / acum_lo / dtT unused there)
 };
 
@@ -98,10 +103,12 @@ int fused_window_shift(const ForwardArgs &a);
 // Sequence segments of the fused forward for a shape (1: one pass), the
 // kernels it launches, and their names when segmented.
 int fused_segments(int batch, int L, int H, int G, int P);
-// The state-only pass of a segmented forward cuts each segment into
-// fused_seg_ratio() pieces (kSegRatio unless overridden).
-constexpr int kSegRatio = 1;
-int fused_seg_ratio();
+// The segments of a segmented forward, as a kernel argument: segment 0 has
+// `first` blocks, every later one `len` (the last the rest); a launch runs
+// segments base .. base + gridDim.z - 1 of nseg.
+struct SegPlan {
+    int first, len, base, nseg;
+};
 int fused_kernel_count(int nseg);
 extern const char *const kFusedSegKernelNames[2];
 bool fused_row_fits(size_t row_bytes);

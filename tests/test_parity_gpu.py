@@ -838,16 +838,22 @@ def test_dt_preprocessing_full_size_every_slice(dev, oracle_mod):
                       "dt_proc full size")
 
 
-@pytest.mark.parametrize("io", ["bf16", "f32"])
-def test_forward_and_decode_replay_in_a_graph(dev, io):
+@pytest.mark.parametrize("io", ["bf16", "f32", "bf16_segmented"])
+def test_forward_and_decode_replay_in_a_graph(dev, monkeypatch, io):
     """The library allocates nothing and sets no memory from the host, so a
     forward and a decode step can be captured in one HIP graph.  Each replay
     (after eager resets and synchronisations) equals the eager calls bit for
-    bit.  bf16 runs the fused kernel, fp32 the split kernels."""
+    bit.  bf16 runs the fused kernel, fp32 the split kernels, and the
+    segmented fused forward forks its state-only pass onto the library's
+    auxiliary stream and joins it back inside the capture."""
     import torch
     from state_space_sequence_amd import libssd
     from state_space_sequence_amd.inputs import to_torch
     b, L, H, P, N, G, Q = 2, 1000, 8, 64, 128, 2, 256
+    if io == "bf16_segmented":
+        io = "bf16"
+        monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
+        monkeypatch.setenv("SSD_FUSED_SEGMENTS", "4")
     inp = make_inputs(b, L, H, P, N, G, io_dtype=io, init_std=0.1, seed=31)
     t = to_torch(inp, io, dev)
     code = libssd.SSD_BF16 if io == "bf16" else libssd.SSD_F32
@@ -1233,18 +1239,19 @@ SEGMENTED = [
 ]
 
 
-@pytest.mark.parametrize("ratio", [1, 2, 3])
+@pytest.mark.parametrize("seg0_pct", [30, 80, 150])
 @pytest.mark.parametrize("case", SEGMENTED, ids=lambda c: "b%d_L%d_H%d_G%d%s_seg%d" % (
     c[0], c[1], c[2], c[3], "_init" if c[4] else "", c[5]))
-def test_fused_segments_every_element(dev, oracle_mod, monkeypatch, case, ratio):
-    """The fused forward with the sequence cut into segments (state-only
-    pass over `ratio` pieces per segment, then the main pass chaining the
-    pieces' states), forced onto small problems: every element of y and the
-    final state against the oracle."""
+def test_fused_segments_every_element(dev, oracle_mod, monkeypatch, case, seg0_pct):
+    """The fused forward with the sequence cut into segments (the main pass
+    over segment 0 beside the state-only pass over segments 1 .. n - 2, then
+    the main pass over the rest, chaining the segments' states), forced onto
+    small problems with segment 0 at 30%, 80% and 150% of the others' length:
+    every element of y and the final state against the oracle."""
     b, L, H, G, init, nseg = case
     monkeypatch.setenv("SSD_FORWARD_PATH", "fused")
     monkeypatch.setenv("SSD_FUSED_SEGMENTS", str(nseg))
-    monkeypatch.setenv("SSD_FUSED_SEG_RATIO", str(ratio))
+    monkeypatch.setenv("SSD_FUSED_SEG0_PCT", str(seg0_pct))
     _say("segmented case %s" % (case,))
     inp = make_inputs(b, L, H, 64, 128, G, io_dtype="bf16", init_std=0.1 if init else 0.0,
                       seed=1400 + L + H)
@@ -1291,8 +1298,9 @@ def test_fused_segments_sequence_starts_at_boundaries(dev, oracle_mod, monkeypat
 
 
 def test_fused_segments_timed_names_two_kernels(dev, monkeypatch):
-    """The timed forward of a segmented problem names its two kernels and
-    matches the untimed one bit for bit."""
+    """The timed forward of a segmented problem names its two phases (the
+    first runs two kernels on two streams) and matches the untimed one bit
+    for bit."""
     import torch
     from state_space_sequence_amd import libssd
     from state_space_sequence_amd.inputs import to_torch
@@ -1310,7 +1318,7 @@ def test_fused_segments_timed_names_two_kernels(dev, monkeypatch):
     for e in evs:
         ev.destroy(e)
     _say("kernels %s" % names)
-    assert names == ["k_fused_ssd_state", "k_fused_ssd"]
+    assert names == ["k_fused_ssd_state+seg0", "k_fused_ssd"]
     assert torch.equal(y0, y1) and torch.equal(f0, f1)
 
 
