@@ -560,6 +560,18 @@ def measure_peaks(dev, ev):
             "gemm_what": "8192 x 8192 x 8192 bf16 torch.matmul (hipBLASLt)"}
 
 
+def _cpu_model():
+    """The host CPU's model name (Linux /proc/cpuinfo), or None."""
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
 def cpu_baseline(w, inp, target_s=12.0):
     """The fp64 serial oracle on the host cores, on a bounded sample of the
     workload's (batch, head) slices over the full sequence; tokens/s scaled to
@@ -612,7 +624,7 @@ def cpu_baseline(w, inp, target_s=12.0):
         t_run = (time.perf_counter() - t0) / reps
     tokens_equiv = w.batch * w.seqlen * (k / nsl)
     return {"value": round(tokens_equiv / t_run, 1), "unit": "tokens/s", "cores": threads,
-            "kind": "oracle",
+            "kind": "oracle", "cpu_model": _cpu_model(),
             "sample": "%d of %d (batch, head) slices, all %d tokens each, fp64 serial "
                       "recurrence (C, OpenMP over slices), %.3g s per pass%s; tokens/s scaled by "
                       "the slice fraction" % (k, nsl, w.seqlen, t_run,
