@@ -368,13 +368,14 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
 
     const int HP = H * P, GN = G * N;
     // Workgroups are dealt to the 8 XCDs in turn (workgroup i to XCD i % 8),
-    // each XCD with its own L2.  With grouped B and C (G > 1) and a multiple
-    // of 8 workgroups, XCD x gets the consecutive range x * n / 8 .. of
-    // (segment, batch, column block) triples, so the workgroups that share a
-    // group's C, B and dt rows share few L2s (spreading them made the 8-group
-    // layer 28% slower).  With one group the rows are a small share of the
-    // traffic and the plain order, which spreads a batch over all eight L2s,
-    // measured about 1% faster (2.7B and 130M layers).
+    // each XCD with its own L2.  With a multiple of 8 workgroups, XCD x gets
+    // the consecutive range x * n / 8 .. of (segment, batch, column block)
+    // triples, so the workgroups that share a batch's (or group's) C, B and
+    // dt rows share few L2s and fetch those rows a few times instead of once
+    // per XCD.  (The plain order, which spreads a batch over all eight L2s,
+    // made the 8-group layer 28% slower; on the 2.7B layer it was 0.8%
+    // faster but fetched 168 MB more per launch, 1.27x the algorithmic
+    // bytes, so it is not used.)
     // The sequence may be cut into segments (SegPlan); this launch runs
     // segments plan.base .. plan.base + gridDim.z - 1 (the segment index
     // varies slowest, so a segment's workgroups sit together on the XCDs as
@@ -383,7 +384,7 @@ k_fused_ssd(const bf16 *__restrict__ x, const float *__restrict__ dt, const floa
     {
         const int nc = H * P / PB, nb = gridDim.y, n = nc * nb * gridDim.z;
         const int i = (blockIdx.z * nb + blockIdx.y) * nc + blockIdx.x;
-        const int v = (G > 1 && n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
+        const int v = (n % 8 == 0) ? (i % 8) * (n / 8) + i / 8 : i;
         c0 = (v % nc) * PB;
         b = (v / nc) % nb;
         seg = plan.base + v / nc / nb;
