@@ -326,175 +326,421 @@ k4_state_passing(float *__restrict__ S, const float *__restrict__ acum_hi,
 }
 
 // --------------------------------------------------------------------- k5
-// grid (nc * nlb, H, b), 256 threads, dynamic LDS; nlb = ceil(Q/64).
-// Block (c, lb) produces rows l in [64 lb, 64 lb + 64) of chunk c; wave w
-// owns the 16 rows l0 = 64 lb + 16 w and every 16-column p-tile.
+// word 3 of a raw buffer resource on gfx9-family targets (32-bit data format)
+constexpr int kRawBufferWord3 = 0x00020000;
+
+// LDS of k5, shared by the kernel and its launch, for headdims padded to 64
+// or 128 (the padded columns feed only accumulators that are never stored).
+// fp32: the source block's x as token rows of a pitch = 16 (mod 64) floats,
+// so a fragment read (4 consecutive tokens x 16 consecutive columns) falls
+// on 64 distinct banks and staging is a plain 16-byte copy; bf16: x^T, rows
+// of 64 + 8.  Then the tile of M (64 rows), two K-slabs of the entering
+// state, and float vectors: the chunk's prefix sums, decays and starts by
+// row (4 x 256) and the source block's prefix sums, dt and decays (4 x 64).
+struct K5Lds {
+    static constexpr int kSB = 64;   // the largest row / source block
+    static __host__ __device__ constexpr int ppad(int P) { return P <= 64 ? 64 : 128; }
+    static __host__ __device__ constexpr int xpitch(int PP, int sz) {
+        return sz == 4 ? PP + (80 - PP % 64) % 64 : kSB + 16 / sz;
+    }
+    static __host__ __device__ constexpr int mpitch(int sz) { return kSB + 16 / sz; }
+    static __host__ __device__ constexpr int hpitch(int sz) { return (sz == 4 ? 16 : 32) + 16 / sz; }
+    static __host__ __device__ constexpr size_t x_elems(int PP, int sz) {
+        return (size_t)(sz == 4 ? kSB : PP) * xpitch(PP, sz);
+    }
+    static __host__ __device__ constexpr size_t h_elems(int PP, int sz) {
+        return (size_t)2 * PP * hpitch(sz);
+    }
+    static size_t bytes(int P, int sz) {
+        const int PP = ppad(P);
+        return (x_elems(PP, sz) + (size_t)kSB * mpitch(sz) + h_elems(PP, sz)) * sz +
+               (4 * 256 + 4 * kSB) * 4;
+    }
+};
+
+// acc[i][k] += a[i] b[k] over the fragments' K; the MFMAs run in an order in
+// which consecutive ones write different accumulators
+template <typename T, int NA, int NB>
+__device__ __forceinline__ void mma_grid(const typename Mma<T>::frag (&a)[NA],
+                                         const typename Mma<T>::frag (&b)[NB],
+                                         f32x4 (&acc)[NA][NB]) {
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int i = 0; i < NA; ++i)
+#pragma unroll
+                for (int k = 0; k < NB; ++k)
+                    acc[i][k] = __builtin_amdgcn_mfma_f32_16x16x4f32(a[i][j], b[k][j], acc[i][k], 0, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < NA; ++i)
+#pragma unroll
+            for (int k = 0; k < NB; ++k) acc[i][k] = Mma<T>::mma(a[i], b[k], acc[i][k]);
+    }
+}
+
+// grid (nc * NRB / NOWN, H, b), 256 threads (4 waves), dynamic LDS
+// K5Lds::bytes.  Chunk c of head h has NRB row blocks of SB = min(Q, 64)
+// rows; workgroup `half` of the chunk owns NOWN of them: {half} alone, or
+// {half, NRB - 1 - half} (one long and one short row block, so that the two
+// workgroups of a chunk have equal numbers of tiles).  Wave w computes the
+// 16-row tile w of each owned row block; NPT 16-column tiles span the
+// (padded) headdim.
 //   acc  = C[l] . h_in^T                 (state-to-output, Eq. 23)
 //   acc *= exp(acum_l)                   (0 past a sequence start in the chunk)
 //   acc += sum_{s<=l} M[l][s] x[s],  M[l][s] = CB[l,s] exp(acum_l - acum_s) dt_s
 //                                        (Step 1; s >= segst[l] with packed sequences)
 //   y    = acc + D x[l]               (D per head, or per head and column)
 //   y   *= silu(z[l])                 (when gated)
-// For each 64-token s-block at or before the l-block the workgroup stages x^T
-// of the s-block and builds the 64 x 64 tile of M in LDS, in the MFMA operand
-// type: each thread forms 16 entries from coalesced reads of the C B^T rows
-// and the staged prefix sums and dt, so the product loop is LDS reads and
-// MFMAs only.  The mask is a select, so entries above the diagonal are
-// exactly 0 (the upper-triangle protection of the Kernel 5 page: no exponent
-// of s > l reaches the tile).
-template <typename T>
-__global__ void __launch_bounds__(256)
+// The state entering the chunk passes through LDS once, in K-slabs, and x
+// once per SB-token source block.  For each (row block, source block) pair at
+// or below the diagonal the workgroup builds the tile of M in LDS, in the
+// MFMA operand type, each thread forming up to 16 entries of one column from
+// coalesced reads of C B^T rows.  On the diagonal tile every entry takes its
+// own exponential of a prefix-sum difference, and the mask is a select, so
+// entries above the diagonal are exactly 0 (the upper-triangle protection of
+// the Kernel 5 page: no exponent of s > l reaches the tile).  Below it the
+// decay factors through the block's last source s0: exp(acum_l - acum_s) =
+// exp(acum_l - acum_s0) exp(acum_s0 - acum_s), both exponents <= 0 (A <= 0),
+// one exponential per row and per source instead of one per entry.  Loads
+// run one step ahead of the MFMAs: the next state slab during a slab's
+// products, the next tile's C B^T entries (and the next block's x) during a
+// tile's.  A row block's outputs are finished right after its diagonal tile,
+// while that block's x is staged.
+// (three workgroups of 64-column tiles fit a compute unit's LDS; the register
+// cap that lets them all run costs a couple of spilled registers)
+template <typename T, int NPT, int NRB, int NOWN>
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(NPT == 4 ? 3 : 1)))
 k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
               const float *__restrict__ cb, const float *__restrict__ S,
               const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
               const float *__restrict__ dtT, const float *__restrict__ D,
               T *__restrict__ y, int L, int H, int G, int P, int N, int nc, int Q,
               const T *__restrict__ z, int D_hdim, const int *__restrict__ segst) {
+    typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
-    constexpr int SB = 64;
-    constexpr int PITCH = SB + 16 / (int)sizeof(T);          // rows of the M tile (and of bf16 x^T)
-    // fp32 x^T: rows of 64 floats with their 4-float chunks XOR-swizzled by (row + row / 16) mod 16, so the
-    // staging stores (4 consecutive tokens of 16 rows 4 apart) and the 16-byte fragment reads (16 consecutive
-    // rows) fall on distinct banks at headdim 64; bf16 x^T: padded rows
-    constexpr bool SW = sizeof(T) == 4;
-    constexpr int XPITCH = SW ? SB : PITCH;
-    constexpr int MAXPT = kMaxHeaddim / 16;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int SBX = K5Lds::kSB;
+    constexpr bool F32 = SZ == 4;
+    constexpr int PP = 16 * NPT;                              // the padded headdim
+    constexpr int XP = K5Lds::xpitch(PP, SZ);
+    constexpr int PITCH = K5Lds::mpitch(SZ);
+    constexpr int HPITCH = K5Lds::hpitch(SZ);
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    T *XT = reinterpret_cast<T *>(smem_raw);                 // [P][XPITCH]: x^T of the s-block
-    T *MT = XT + (size_t)P * XPITCH;                          // [64][PITCH]: M of (l-block, s-block)
-    auto at = [](int row, int s) -> int {
-        if constexpr (SW)
-            return row * SB + 4 * (((s >> 2) ^ (row + (row >> 4))) & 15) + (s & 3);
+    T *XS = reinterpret_cast<T *>(smem_raw);                 // x of the source block (see K5Lds)
+    T *MT = XS + K5Lds::x_elems(PP, SZ);                     // [SBX][PITCH]: M of (row block, source block)
+    T *HS = MT + (size_t)SBX * PITCH;                         // [2][PP][HPITCH]: K-slabs of the entering state
+    float *r_hi = reinterpret_cast<float *>(HS + K5Lds::h_elems(PP, SZ));  // by row of the chunk:
+    float *r_lo = r_hi + 256;                                 //   prefix sums (hi + lo),
+    float *r_u = r_lo + 256;                                  //   exp(acum_l - acum_s0),
+    int *r_st = reinterpret_cast<int *>(r_u + 256);           //   sequence starts
+    float *s_hi = reinterpret_cast<float *>(r_st + 256);      // by source of the block: prefix sums,
+    float *s_lo = s_hi + SBX;
+    float *s_dt = s_lo + SBX;                                 //   dt,
+    float *s_v = s_dt + SBX;                                  //   exp(acum_s0 - acum_s) dt_s
+    // position of tile column s in an M row: fp32 fragments take the K index
+    // s = kk + q + 4 j (lane group q, MFMA j of four), stored at kk + 4 q + j
+    // so that a lane's four A values are one 16-byte read; bf16 keeps order
+    auto mcol = [](int s) -> int {
+        if constexpr (F32)
+            return (s & ~15) | ((s & 3) << 2) | ((s >> 2) & 3);
         else
-            return row * PITCH + s;
+            return s;
     };
-    float *s_hi = reinterpret_cast<float *>(MT + SB * PITCH);  // the s-block's prefix sums, dt
-    float *s_lo = s_hi + SB;
-    float *s_dt = s_lo + SB;
-    float *r_hi = s_dt + SB;                                  // the l-block's prefix sums
-    float *r_lo = r_hi + SB;
-    int *r_st = reinterpret_cast<int *>(r_lo + SB);           // and sequence starts
+    // x of source token s (in the block), column p
+    auto xat = [](int s, int p) -> int {
+        if constexpr (F32)
+            return s * XP + p;
+        else
+            return p * PITCH + s;
+    };
 
-    const int nlb = (Q + 63) / 64;
-    const int c = blockIdx.x / nlb, lb = blockIdx.x % nlb;
+    constexpr int NSPLIT = NRB / NOWN;                        // workgroups per chunk
+    const int c = blockIdx.x / NSPLIT, half = blockIdx.x % NSPLIT;
     const int h = blockIdx.y, b = blockIdx.z, g = h / (H / G);
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    // (the wave index as a wave-uniform value: row tests become scalar)
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    // the owned row blocks, in increasing order
+    auto own = [&](int j) -> int { return j == 0 ? half : NRB - 1 - half; };
+    const int own_last = own(NOWN - 1);
     const int r = lane & 15, q = lane >> 4;
-    const int l0 = lb * 64 + wave * 16;
-    const bool active = l0 < Q;
-    const int npt = P / 16;
+    const int SB = NRB > 1 || Q >= SBX ? SBX : Q;   // Q / NRB
+    const int SBK = SB < KS ? KS : SB;        // columns of a tile the product reads (zeros past SB)
+    const bool active = wave * 16 < SB;       // this wave owns tile `wave` of every row block
     const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
     const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
     const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
     const int *sg = segst ? segst + ((size_t)b * nc + c) * Q : nullptr;
 
-    if (tid < SB) {
-        const int l = lb * SB + tid;
-        r_hi[tid] = l < Q ? ah[l] : 0.f;
-        r_lo[tid] = l < Q ? al[l] : 0.f;
-        r_st[tid] = sg && l < Q ? sg[l] : -1;
+    for (int l = tid; l < Q; l += 256) {
+        r_hi[l] = ah[l];
+        r_lo[l] = al[l];
+        r_st[l] = sg ? sg[l] : -1;
     }
-    __syncthreads();
 
-    f32x4 acc[MAXPT];
+    f32x4 acc[NOWN][NPT];
 #pragma unroll
-    for (int i = 0; i < MAXPT; ++i) acc[i] = zero4();
+    for (int j = 0; j < NOWN; ++j)
+#pragma unroll
+        for (int i = 0; i < NPT; ++i) acc[j][i] = zero4();
 
-    if (active) {
-        const float *hin = S + ((size_t)(b * nc + c) * H + h) * P * N;
-        const int t = c * Q + l0 + r;
-        const T *crow = Cm + (((size_t)b * L + t) * G + g) * N;
-        for (int k0 = 0; k0 < N; k0 += KS) {
+    // ---- state to output: C of every row of the wave, times the state
+    // entering the chunk, staged a K-slab (KS dstate columns) at a time into
+    // two alternating LDS buffers; the next slab's state and C fragments are
+    // loaded while this slab's MFMAs run
+    const float *hin = S + ((size_t)(b * nc + c) * H + h) * P * N;
+    const T *crow = Cm + (((size_t)b * L + (size_t)c * Q) * G + g) * N;
+    constexpr int KQ = KS / VEC;                   // fragments per slab row
+    constexpr int HF = (PP * KQ + 255) / 256;      // slab fragments per thread
+    const int hv = P * KQ;                         // fragments of a slab (rows past P stay unset)
+    frag hf[HF], cf[NOWN], cn[NOWN];
+    auto load_slab = [&](int k0) {
+#pragma unroll
+        for (int u = 0; u < HF; ++u) {
+            const int v = tid + 256 * u;
+            if (v >= hv) continue;
+            const int p = v / KQ, kq = (v % KQ) * VEC;
+#pragma unroll
+            for (int jj = 0; jj < VEC; ++jj)
+                hf[u][jj] = k0 + kq + jj < N ? from_f32<T>(hin[(size_t)p * N + k0 + kq + jj]) : from_f32<T>(0.f);
+        }
+#pragma unroll
+        for (int j = 0; j < NOWN; ++j) {
+            cn[j] = zero_frag<T>();
+            const int l = own(j) * SB + wave * 16 + r;
             const int k = k0 + VEC * q;
-            const bool kin = k < N;
-            typename Mma<T>::frag a = (t < L && kin) ? load_frag(crow + k) : zero_frag<T>();
+            if (active && (size_t)c * Q + l < (size_t)L && k < N)
+                cn[j] = load_frag(crow + (size_t)l * G * N + k);
+        }
+    };
+    load_slab(0);
+    for (int k0 = 0, buf = 0; k0 < N; k0 += KS, buf ^= 1) {
+        T *hs = HS + (size_t)buf * PP * HPITCH;
 #pragma unroll
-            for (int pt = 0; pt < MAXPT; ++pt) {
-                if (pt >= npt) continue;
-                typename Mma<T>::frag bb = zero_frag<T>();
-                if (kin) {
-                    const float *hp = hin + (size_t)(pt * 16 + r) * N + k;
+        for (int u = 0; u < HF; ++u) {
+            const int v = tid + 256 * u;
+            if (v < hv) *reinterpret_cast<frag *>(hs + (v / KQ) * HPITCH + (v % KQ) * VEC) = hf[u];
+        }
 #pragma unroll
-                    for (int jj = 0; jj < VEC; ++jj) bb[jj] = from_f32<T>(hp[jj]);
-                }
-                acc[pt] = Mma<T>::mma(a, bb, acc[pt]);
+        for (int j = 0; j < NOWN; ++j) cf[j] = cn[j];
+        __syncthreads();
+        if (k0 + KS < N) load_slab(k0 + KS);
+        if (active) {
+            frag bb[NPT];
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) bb[pt] = load_frag(hs + (pt * 16 + r) * HPITCH + VEC * q);
+            mma_grid<T>(cf, bb, acc);
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int j = 0; j < NOWN; ++j) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int l = own(j) * SB + wave * 16 + 4 * q + i;
+                const float e = r_st[l] < 0 ? fast_exp(r_hi[l]) : 0.f;
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) acc[j][pt][i] *= e;
             }
         }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int li = wave * 16 + 4 * q + i;
-            const float e = r_st[li] < 0 ? fast_exp(r_hi[li]) : 0.f;
-#pragma unroll
-            for (int pt = 0; pt < MAXPT; ++pt) acc[pt][i] *= e;
-        }
     }
 
+    // ---- the intra-chunk product over the pairs (row block lb, source block
+    // sb): for sb = 0, 1, ..., the owned lb >= sb in increasing order, so
+    // that the diagonal pair (lb = sb) opens its source block.  Per pair: the
+    // MFMAs of this pair's tile, meanwhile the loads of the next pair's C B^T
+    // entries (and, when the next pair starts a source block, its x); then,
+    // after a barrier, the next tile of M built from those registers.
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
     const int pv = P / VEC;
-    for (int sb = 0; sb <= lb; ++sb) {
-        __syncthreads();
-        for (int v = tid; v < SB * pv; v += 256) {
-            const int sl = v / pv, p0 = (v % pv) * VEC;
-            const int s = sb * SB + sl, t = c * Q + s;
-            typename Mma<T>::frag f = zero_frag<T>();
-            if (s < Q && t < L) f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
+    const float Dh = D ? D[h] : 0.f;
+    const int jc = tid & (SBX - 1);          // the tile column this thread builds
+    constexpr int XF = (SBX * PP / VEC + 255) / 256;
+    frag xr[XF];                             // x of a source block, in flight
+    float cbr[SBX / 4];                      // C B^T entries of the next tile, in flight
+    auto load_x = [&](int sb) {
 #pragma unroll
-            for (int jj = 0; jj < VEC; ++jj) XT[at(p0 + jj, sl)] = f[jj];
+        for (int u = 0; u < XF; ++u) {
+            const int v = tid + 256 * u;
+            xr[u] = zero_frag<T>();
+            if (v >= SBK * pv) continue;
+            const int sl = v / pv, p0 = (v % pv) * VEC, t = c * Q + sb * SB + sl;
+            if (sl < SB && t < L) xr[u] = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
         }
+    };
+    // stage block sb: its x, the prefix sums, dt and decays of its sources,
+    // and the decays of the later rows to its last source s0
+    auto stage = [&](int sb) {
+#pragma unroll
+        for (int u = 0; u < XF; ++u) {
+            const int v = tid + 256 * u;
+            if (v >= SBK * pv) continue;
+            const int sl = v / pv, p0 = (v % pv) * VEC;
+            if constexpr (F32) {
+                *reinterpret_cast<frag *>(XS + xat(sl, p0)) = xr[u];
+            } else {
+#pragma unroll
+                for (int jj = 0; jj < VEC; ++jj) XS[xat(sl, p0 + jj)] = xr[u][jj];
+            }
+        }
+        const int s0 = sb * SB + SB - 1;
         if (tid < SB) {
             const int s = sb * SB + tid;
-            s_hi[tid] = s < Q ? ah[s] : 0.f;
-            s_lo[tid] = s < Q ? al[s] : 0.f;
-            s_dt[tid] = s < Q ? dc[s] : 0.f;
+            const float hi = r_hi[s], lo = r_lo[s], d = dc[s];
+            s_hi[tid] = hi;
+            s_lo[tid] = lo;
+            s_dt[tid] = d;
+            s_v[tid] = fast_exp(prefix_diff(r_hi[s0], r_lo[s0], hi, lo)) * d;
         }
-        __syncthreads();
-        // the tile of M: thread tid forms column j = tid % 64 of rows
-        // tid / 64 + 4 k, k = 0..15 (each row read as 64 consecutive floats)
-        {
-            const int j = tid & (SB - 1), s = sb * SB + j;
-            const float shi = s_hi[j], slo = s_lo[j], sdt = s_dt[j];
-#pragma unroll 4
-            for (int i = tid >> 6; i < SB; i += 4) {
-                const int l = lb * SB + i;
+        for (int l = s0 + 1 + tid; l < Q; l += 256)
+            r_u[l] = fast_exp(prefix_diff(r_hi[l], r_lo[l], r_hi[s0], r_lo[s0]));
+    };
+    // the entries of tile (lb, sb) in this thread's column: rows tid / 64 + 4 k
+    // (buffer loads: one address per thread, the row step in the scalar offset)
+    const __amdgpu_buffer_rsrc_t rcb =
+        __builtin_amdgcn_make_buffer_rsrc((void *)(cb + cbase * Q), 0, (unsigned)Q * Q * 4, kRawBufferWord3);
+    auto load_cb = [&](int lb, int sb) {
+        const int voff = ((lb * SB + wave) * Q + sb * SB + jc) * 4;
+#pragma unroll
+        for (int k = 0; k < SBX / 4; ++k) {
+            const int i = wave + 4 * k;
+            cbr[k] = 0.f;
+            if (i < SB && jc < SB)
+                cbr[k] = __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(rcb, voff, 16 * k * Q, 0));
+        }
+    };
+    // the tile of M from cbr.  On the diagonal each entry takes its own
+    // exponential and the causal mask; below it, the factored decays
+    auto build = [&](int lb, int sb) {
+        if (jc >= SBK) return;
+        T *mc = MT + mcol(jc);
+        const int s = sb * SB + jc;
+        if (lb > sb) {
+            const float sv = s_v[jc];
+#pragma unroll
+            for (int k = 0; k < SBX / 4; ++k) {
+                const int i = wave + 4 * k, l = lb * SB + i;
+                if (i >= SB) continue;
+                const float v = jc < SB && s >= r_st[l] ? cbr[k] * r_u[l] * sv : 0.f;
+                mc[i * PITCH] = from_f32<T>(v);
+            }
+        } else {
+            const float shi = s_hi[jc], slo = s_lo[jc], sdt = s_dt[jc];
+#pragma unroll
+            for (int k = 0; k < SBX / 4; ++k) {
+                const int i = wave + 4 * k, l = lb * SB + i;
+                if (i >= SB) continue;
                 float v = 0.f;
-                if (l < Q && s <= l && s >= r_st[i])
-                    v = cb[(cbase + l) * Q + s] *
-                        fast_exp(prefix_diff(r_hi[i], r_lo[i], shi, slo)) * sdt;
-                MT[i * PITCH + j] = from_f32<T>(v);
+                if (jc < SB && s <= l && s >= r_st[l])
+                    v = cbr[k] * fast_exp(prefix_diff(r_hi[l], r_lo[l], shi, slo)) * sdt;
+                mc[i * PITCH] = from_f32<T>(v);
             }
         }
-        __syncthreads();
-        if (!active) continue;
-        // the diagonal tile stops at the wave's last row (M is 0 beyond it)
-        const int kend = sb < lb ? SB : min(SB, (wave * 16 + 16 + KS - 1) / KS * KS);
-        for (int kk = 0; kk < kend; kk += KS) {
-            const typename Mma<T>::frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
+    };
+    // row block sb is complete (its last source block is its diagonal, whose
+    // x is staged): the skip term, the gate, y
+    auto finish = [&](const f32x4(&ac)[NPT], int sb) {
 #pragma unroll
-            for (int pt = 0; pt < MAXPT; ++pt) {
-                if (pt >= npt) continue;
-                typename Mma<T>::frag bb = load_frag(XT + at(pt * 16 + r, kk + VEC * q));
-                acc[pt] = Mma<T>::mma(m, bb, acc[pt]);
+        for (int i = 0; i < 4; ++i) {
+            const int l = sb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+            if (t >= L) continue;
+            const size_t ro = (((size_t)b * L + t) * H + h) * P;
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) {
+                const int p = pt * 16 + r;
+                if (p >= P) continue;
+                const float xv = to_f32(XS[xat(l - sb * SB, p)]);
+                const float dp = D_hdim && D ? D[(size_t)h * P + p] : Dh;
+                float o = ac[pt][i] + dp * xv;
+                if (z) o *= silu_f32(to_f32(z[ro + p]));
+                y[ro + p] = from_f32<T>(o);
             }
         }
-    }
+    };
 
-    if (!active) return;
-    const float Dh = D ? D[h] : 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int l = l0 + 4 * q + i, t = c * Q + l;
-        if (l >= Q || t >= L) continue;
-        const size_t ro = (((size_t)b * L + t) * H + h) * P;
-#pragma unroll
-        for (int pt = 0; pt < MAXPT; ++pt) {
-            if (pt >= npt) continue;
-            const int p = pt * 16 + r;
-            const float xv = to_f32(XT[at(p, l - lb * SB)]);
-            const float dp = D_hdim && D ? D[(size_t)h * P + p] : Dh;
-            float o = acc[pt][i] + dp * xv;
-            if (z) o *= silu_f32(to_f32(z[ro + p]));
-            y[ro + p] = from_f32<T>(o);
+    // the pair after (sb, j), if any
+    auto next_pair = [&](int sb, int j, int &nsb, int &nj) -> bool {
+        nsb = sb;
+        nj = j + 1;
+        for (;;) {
+            if (nj >= NOWN) {
+                ++nsb;
+                nj = 0;
+            }
+            if (nsb > own_last) return false;
+            if (own(nj) >= nsb) return true;
+            ++nj;
         }
+    };
+
+    load_x(0);
+    load_cb(own(0), 0);
+    stage(0);
+    __syncthreads();
+    build(own(0), 0);
+    __syncthreads();
+    f32x4 tmp[1][NPT];
+    int sb = 0, j = 0;
+#pragma nounroll
+    for (;;) {
+        const int lb = own(j);
+        int nsb, nj;
+        const bool more = next_pair(sb, j, nsb, nj), next_block = more && nsb != sb;
+        if (more) {
+            load_cb(own(nj), nsb);
+            if (next_block) load_x(nsb);
+        }
+#pragma unroll
+        for (int pt = 0; pt < NPT; ++pt) tmp[0][pt] = zero4();
+        if (active) {
+            // this wave's rows of the tile times x; the diagonal tile stops
+            // at the wave's last row (M is 0 beyond it)
+            const int kend = sb < lb ? SB : min(SB, (wave * 16 + 16 + KS - 1) / KS * KS);
+#pragma unroll
+            for (int kk = 0; kk < SBX; kk += KS) {
+                if (kk >= kend) break;
+                const frag m[1] = {load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q)};
+                frag bb[NPT];
+#pragma unroll
+                for (int pt = 0; pt < NPT; ++pt) {
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) bb[pt][jj] = XS[xat(kk + q + 4 * jj, pt * 16 + r)];
+                    } else {
+                        bb[pt] = load_frag(XS + xat(kk + VEC * q, pt * 16 + r));
+                    }
+                }
+                mma_grid<T>(m, bb, tmp);
+            }
+        }
+        // (one copy of the product above; the sum goes to the row block's
+        // accumulators through constant indexes, which keeps them in registers)
+        auto add = [&](f32x4(&ac)[NPT]) {
+#pragma unroll
+            for (int pt = 0; pt < NPT; ++pt) ac[pt] += tmp[0][pt];
+        };
+        if (!more) {
+            // the last pair is the diagonal of the last owned row block
+            add(acc[NOWN - 1]);
+            if (active) finish(acc[NOWN - 1], sb);
+            break;
+        }
+        __syncthreads();   // (the tile of M, and x when replaced, no longer read)
+        if (next_block) {
+            // a diagonal pair is followed by a pair of its own source block
+            // (its row block's rows are finished below, from the staged x)
+            // unless it is the last pair, so the pair just done is below
+            // the diagonal
+            stage(nsb);
+            __syncthreads();
+        }
+        build(own(nj), nsb);
+        if (j == 0) add(acc[0]); else add(acc[NOWN - 1]);
+        if (lb == sb && active) finish(j == 0 ? acc[0] : acc[NOWN - 1], sb);
+        __syncthreads();   // (the next tile of M is built)
+        sb = nsb;
+        j = nj;
     }
 }
 
@@ -539,8 +785,17 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
                        0, stream, a.S, a.acum_hi, a.init, a.final_state, a.H, PN, nc, Q, segst);
     if ((err = mark()) != hipSuccess) return err;
-    const size_t k5_lds = (size_t)(a.P + 64) * (64 + 16 / sizeof(T)) * sizeof(T) + 6 * 64 * 4;
-    hipLaunchKernelGGL(k5_chunk_scan<T>, dim3(nc * nlb, a.H, a.batch), dim3(256), k5_lds,
+    const size_t k5_lds = K5Lds::bytes(a.P, (int)sizeof(T));
+    // (the accumulators are sized by the padded headdim and the row blocks of a chunk)
+    static_assert(kMaxHeaddim == 128, "k5 pads the headdim to 64 or 128");
+    const bool p64 = a.P <= 64;
+    const int nrb = Q >= 256 ? 4 : Q >= 128 ? 2 : 1;
+    // (a chunk of 4 row blocks takes two workgroups of two blocks each, 2 row blocks two of one)
+    auto k5 = nrb == 4 ? (p64 ? k5_chunk_scan<T, 4, 4, 2> : k5_chunk_scan<T, 8, 4, 2>)
+            : nrb == 2 ? (p64 ? k5_chunk_scan<T, 4, 2, 1> : k5_chunk_scan<T, 8, 2, 1>)
+                       : (p64 ? k5_chunk_scan<T, 4, 1, 1> : k5_chunk_scan<T, 8, 1, 1>);
+    const int nsplit = nrb == 1 ? 1 : 2;
+    hipLaunchKernelGGL(k5, dim3(nc * nsplit, a.H, a.batch), dim3(256), k5_lds,
                        stream, (const T *)a.x, (const T *)a.C, (const float *)a.cb, a.S, a.acum_hi,
                        a.acum_lo, a.dtT, a.D, (T *)a.y, a.L, a.H, a.G, a.P, a.N, nc, Q,
                        (const T *)a.z, a.D_hdim ? 1 : 0, segst);
