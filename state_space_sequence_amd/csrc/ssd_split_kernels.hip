@@ -744,6 +744,128 @@ k5_chunk_scan(const T *__restrict__ x, const T *__restrict__ Cm,
     }
 }
 
+// --------------------------------------------------------------------- k3, fp32
+// fp32 k3: grid (nc, H * npg * nng, b), 256 threads, dynamic LDS
+// K3F32Lds::bytes.  Workgroup (pg, ng) computes the 64 x 128 block
+// S[64 pg .., 128 ng ..] of the chunk state (headdim and dstate padded to
+// those multiples; padded rows and columns feed only tiles never stored);
+// waves form a 2 x 2 grid of 32 x 64 sub-blocks, 2 x 4 tiles of 16 x 16 each.
+// The per-token weight w_s (0 before the chunk's last sequence start and
+// past the end) is computed once per token; a chunk shorter than a slab
+// (16 tokens) leaves the rest of the slab zero.  32-token slabs of x and B go
+// to LDS untransposed, w folded into x, as rows of a pitch = 16 (mod 64)
+// floats: the fragments take K index s = kk + q + 4 j (lane group q, MFMA j
+// of four), so a lane's operands are single floats of 4 consecutive rows x
+// 16 consecutive columns, 64 distinct banks.  The next slab is loaded into
+// registers while this slab's MFMAs run.
+struct K3F32Lds {
+    static constexpr int kKB = 32;   // tokens per slab
+    static __host__ __device__ constexpr int pitch(int cols) { return cols + (80 - cols % 64) % 64; }
+    static size_t bytes() { return ((size_t)kKB * pitch(64) + (size_t)kKB * pitch(128) + 256) * 4; }
+};
+
+__global__ void __launch_bounds__(256)
+k3_chunk_state_f32(const float *__restrict__ x, const float *__restrict__ Bm,
+                   const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+                   const float *__restrict__ dtT, float *__restrict__ S, int L, int H,
+                   int G, int P, int N, int nc, int Q, const int *__restrict__ segst) {
+    constexpr int KB = K3F32Lds::kKB;
+    constexpr int XP = K3F32Lds::pitch(64), BP = K3F32Lds::pitch(128);
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    float *XS = reinterpret_cast<float *>(smem_raw);   // [KB][XP]: w_s x[s][64 pg + p]
+    float *BS = XS + KB * XP;                           // [KB][BP]: B[s][128 ng + n]
+    float *s_w = BS + KB * BP;                          // [256]: w_s (0 past the chunk)
+
+    const int npg = (P + 63) / 64, nng = (N + 127) / 128;
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int h = blockIdx.y / (npg * nng), pg = blockIdx.y / nng % npg, ng = blockIdx.y % nng;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int wp = (wave >> 1) * 32, wn = (wave & 1) * 64;   // this wave's sub-block
+    const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
+    {
+        const float end_hi = ah[Q - 1], end_lo = al[Q - 1];
+        // packed sequences: only the chunk's last sequence reaches its end state
+        const int s_first = segst ? segst[((size_t)b * nc + c) * Q + Q - 1] : -1;
+        for (int s = tid; s < 256; s += 256) {
+            const bool in = s < Q && c * Q + s < L && s >= s_first;
+            s_w[s] = in ? fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s] : 0.f;
+        }
+    }
+
+    // slab loads: x rows of 64 columns (16 float4 per token), B rows of 128
+    // (32 float4 per token); 2 + 4 per thread
+    constexpr int XV = KB * 16 / 256, BV = KB * 32 / 256;
+    f32x4 xr[XV], br[BV];
+    const int p_lo = 64 * pg, n_lo = 128 * ng;
+    auto load = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 4, p = p_lo + 4 * (v & 15), t = c * Q + s0 + sl;
+            xr[u] = zero4();
+            if (s0 + sl < Q && t < L && p < P) xr[u] = *reinterpret_cast<const f32x4 *>(x + (((size_t)b * L + t) * H + h) * P + p);
+        }
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 5, n = n_lo + 4 * (v & 31), t = c * Q + s0 + sl;
+            br[u] = zero4();
+            if (s0 + sl < Q && t < L && n < N) br[u] = *reinterpret_cast<const f32x4 *>(Bm + (((size_t)b * L + t) * G + g) * N + n);
+        }
+    };
+
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] = zero4();
+
+    load(0);
+    for (int s0 = 0; s0 < Q; s0 += KB) {
+        __syncthreads();   // (the previous slab is no longer read; s_w visible)
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 4;
+            const float w = s_w[s0 + sl];
+            *reinterpret_cast<f32x4 *>(XS + sl * XP + 4 * (v & 15)) = xr[u] * w;
+        }
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+            const int v = tid + 256 * u;
+            *reinterpret_cast<f32x4 *>(BS + (v >> 5) * BP + 4 * (v & 31)) = br[u];
+        }
+        __syncthreads();
+        if (s0 + KB < Q) load(s0 + KB);
+#pragma unroll
+        for (int kk = 0; kk < KB; kk += 16) {
+            f32x4 a[2], bb[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int row = kk + q + 4 * j;
+#pragma unroll
+                for (int i = 0; i < 2; ++i) a[i][j] = XS[row * XP + wp + 16 * i + r];
+#pragma unroll
+                for (int k = 0; k < 4; ++k) bb[k][j] = BS[row * BP + wn + 16 * k + r];
+            }
+            mma_grid<float>(a, bb, acc);
+        }
+    }
+    float *Sc = S + ((size_t)(b * nc + c) * H + h) * P * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = n_lo + wn + 16 * k + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = p_lo + wp + 16 * i + 4 * q + e;
+                if (p < P && n < N) Sc[(size_t)p * N + n] = acc[i][k][e];
+            }
+        }
+}
+
 // --------------------------------------------------------------------- launch
 
 const char *const kSplitKernelNames[kSplitKernels] = {
@@ -774,12 +896,19 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
                        dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, (float *)a.cb, a.L,
                        a.G, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
-    const int ntiles = (a.P / 16) * (a.N / 16);
-    const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
-    const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
-    hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
-                       stream, (const T *)a.x, (const T *)a.B, a.acum_hi, a.acum_lo, a.dtT,
-                       a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+    if constexpr (sizeof(T) == 4) {
+        const int nblk = ((a.P + 63) / 64) * ((a.N + 127) / 128);
+        hipLaunchKernelGGL(k3_chunk_state_f32, dim3(nc, a.H * nblk, a.batch), dim3(256),
+                           K3F32Lds::bytes(), stream, (const float *)a.x, (const float *)a.B,
+                           a.acum_hi, a.acum_lo, a.dtT, a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+    } else {
+        const int ntiles = (a.P / 16) * (a.N / 16);
+        const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
+        const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
+        hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
+                           stream, (const T *)a.x, (const T *)a.B, a.acum_hi, a.acum_lo, a.dtT,
+                           a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+    }
     if ((err = mark()) != hipSuccess) return err;
     const int PN = a.P * a.N;
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
