@@ -10,7 +10,8 @@ Contents
 --------
 ``serial``   the plain serial recurrence in C (``ssd_oracle.c``), built with
              gcc + OpenMP and called through ctypes; the definition every GPU
-             result is compared against.
+             result is compared against.  Also its gradients (``backward``),
+             by reverse-mode differentiation of the same loop.
 ``forms``    independent NumPy formulations used to pin the serial oracle:
              a NumPy serial loop, the quadratic (masked semiseparable-matrix)
              form and the four-step chunked form.
@@ -25,5 +26,5 @@ Contents
 ``gate``     the output gate y * silu(z) and a per-(head, column) D on top of
              the serial oracle, in fp64.
 """
-from .serial import build, forward, forward_slices, state_update, max_threads  # noqa: F401
+from .serial import backward, build, forward, forward_slices, state_update, max_threads  # noqa: F401
 from . import conv, dt, forms, gate, metrics, norm, varlen  # noqa: F401

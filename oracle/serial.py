@@ -56,6 +56,8 @@ def _load():
             lib = ctypes.CDLL(path)
             lib.ssd_oracle_forward.restype = ctypes.c_int
             lib.ssd_oracle_forward.argtypes = [ctypes.c_int] * 6 + [_dp] * 9 + [ctypes.c_int]
+            lib.ssd_oracle_backward.restype = ctypes.c_int
+            lib.ssd_oracle_backward.argtypes = [ctypes.c_int] * 6 + [_dp] * 16 + [ctypes.c_int]
             lib.ssd_oracle_max_threads.restype = ctypes.c_int
             lib.ssd_oracle_max_threads.argtypes = []
             _lib = lib
@@ -105,6 +107,43 @@ def forward(x, dt, A, B, C, D=None, initial_state=None, ngroups=None,
     if rc != 0:
         raise ValueError("oracle rejected the problem (code %d)" % rc)
     return y, final
+
+
+def backward(x, dt, A, B, C, D, initial_state, dy, dfinal=None, nthreads: int = 0):
+    """Gradients of the serial fp64 forward, by reverse-mode differentiation
+    of its loop (``ssd_oracle_backward`` in ``ssd_oracle.c``).
+
+    dy [b,L,H,P] is the gradient of the loss with respect to y, dfinal
+    [b,H,P,N] (or None = 0) with respect to the final state.  Returns a dict
+    of float64 arrays: dx [b,L,H,P], ddt [b,L,H], dA [H], dB and dC
+    [b,L,G,N], dD [H] and dinit [b,H,P,N] (the gradients with respect to D
+    and the initial state also when those are None, i.e. at D = 0 and a
+    zero initial state).
+    """
+    x, dt, A, B, C, dy = (_f64(v) for v in (x, dt, A, B, C, dy))
+    D = None if D is None else _f64(D)
+    init = None if initial_state is None else _f64(initial_state)
+    dfin = None if dfinal is None else _f64(dfinal)
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if dt.shape != (b, L, H) or A.shape != (H,) or B.shape != (b, L, G, N) \
+            or C.shape != B.shape or dy.shape != x.shape:
+        raise ValueError("inconsistent input shapes")
+    if D is not None and D.shape != (H,):
+        raise ValueError("D must have shape [nheads]")
+    for v in (init, dfin):
+        if v is not None and v.shape != (b, H, P, N):
+            raise ValueError("states must have shape [b,H,P,N]")
+    out = {"dx": np.empty_like(x), "ddt": np.empty_like(dt), "dA": np.empty(H),
+           "dB": np.empty_like(B), "dC": np.empty_like(C), "dD": np.empty(H),
+           "dinit": np.empty((b, H, P, N))}
+    rc = _load().ssd_oracle_backward(
+        b, L, H, P, N, G, _ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(init),
+        _ptr(dy), _ptr(dfin), _ptr(out["dx"]), _ptr(out["ddt"]), _ptr(out["dA"]),
+        _ptr(out["dB"]), _ptr(out["dC"]), _ptr(out["dD"]), _ptr(out["dinit"]), int(nthreads))
+    if rc != 0:
+        raise ValueError("oracle rejected the problem (code %d)" % rc)
+    return out
 
 
 def forward_slices(x, dt, A, B, C, D, initial_state, ngroups, slices,
