@@ -246,6 +246,78 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
                                     const char **kernel_names);
 
 /*
+ * Gradients of the chunked forward (the recompute-backward path: the pages
+ * name it, burn-mamba `Mamba2SsdInput::ssd_serial_recalculated`, and say
+ * nothing of its steps; these are the derivative of the four steps of the
+ * rustdoc's `ssd_minimal`, Eqs. 20-23, and their sum over a chunk is the
+ * reverse-mode loop of the serial recurrence).  For a loss with gradients
+ * dy = dLoss/dy and dfinal_state = dLoss/d final_state, it returns the
+ * gradients of that loss with respect to every input of ssd_chunk_scan_fwd:
+ *
+ *   x, dt, A, B, C, D, initial_state, chunk_len ... io_dtype   as for
+ *                   ssd_chunk_scan_fwd (no time-step preprocessing, gate or
+ *                   packed sequences: dt is the processed time step)
+ *   dy            [batch, seqlen, nheads, headdim]    io_dtype   in
+ *   dfinal_state  [batch, nheads, headdim, dstate]    fp32       in, NULL = 0
+ *   dx            [batch, seqlen, nheads, headdim]    io_dtype   out
+ *   ddt           [batch, seqlen, nheads]             fp32       out
+ *   dA            [nheads]                            fp32       out
+ *   dB, dC        [batch, seqlen, ngroups, dstate]    io_dtype   out (summed
+ *                                                                over the group's heads)
+ *   dD            [nheads]                            fp32       out, NULL = skip
+ *                 (written also when D is NULL: the gradient at D = 0)
+ *   dinitial_state [batch, nheads, headdim, dstate]   fp32       out, NULL = skip
+ *                 (written also when initial_state is NULL)
+ *   workspace     >= ssd_chunk_scan_bwd_workspace_size bytes, 256-byte aligned
+ *
+ * The call recomputes the forward's prefix sums, C B^T blocks and chunk
+ * states (the split path's first four kernels, with this chunk_len), then
+ * runs the gradient kernels; nothing from a forward call is needed.  The
+ * outputs must not overlap the inputs or each other.  dA and dD are summed
+ * in a fixed order: the results are deterministic.  Accumulation is fp32;
+ * bf16 runs round the products' operands to bf16 like the forward.  Errors
+ * as for ssd_chunk_scan_fwd (dy and the seven outputs but dD and
+ * dinitial_state are required); SSD_CHECK_FINITE and SSD_POISON_WORKSPACE
+ * apply.
+ */
+ssd_status ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads,
+                                             int headdim, int dstate, int ngroups,
+                                             int chunk_len, ssd_dtype io_dtype,
+                                             size_t *bytes);
+
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A,
+                              const void *B, const void *C, const float *D,
+                              const float *initial_state, const void *dy,
+                              const float *dfinal_state, int chunk_len, int ngroups,
+                              int batch, int seqlen, int nheads, int headdim,
+                              int dstate, ssd_dtype io_dtype, void *dx, float *ddt,
+                              float *dA, void *dB, void *dC, float *dD,
+                              float *dinitial_state, void *workspace,
+                              size_t workspace_bytes, hipStream_t stream);
+
+/* Number of timed kernel groups of one ssd_chunk_scan_bwd call. */
+int ssd_chunk_scan_bwd_max_kernels(void);
+
+/*
+ * Diagnostic twin of ssd_chunk_scan_bwd with per-kernel events, as
+ * ssd_chunk_scan_fwd_timed: events[i] is recorded before kernel group i and
+ * events[k] after the last (k = ssd_chunk_scan_bwd_max_kernels(); the first
+ * group is the four recompute kernels).  nevents >= k + 1, every handle
+ * non-NULL.
+ */
+ssd_status ssd_chunk_scan_bwd_timed(const void *x, const float *dt, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const float *initial_state, const void *dy,
+                                    const float *dfinal_state, int chunk_len, int ngroups,
+                                    int batch, int seqlen, int nheads, int headdim,
+                                    int dstate, ssd_dtype io_dtype, void *dx, float *ddt,
+                                    float *dA, void *dB, void *dC, float *dD,
+                                    float *dinitial_state, void *workspace,
+                                    size_t workspace_bytes, hipStream_t stream,
+                                    hipEvent_t *events, int nevents, int *nkernels,
+                                    const char **kernel_names);
+
+/*
  * One decode step, in place.
  *
  *   state  [batch, nheads, headdim, dstate]  fp32      in/out

@@ -12,6 +12,7 @@
 
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
+#include "ssd_backward.hpp"
 
 // Scratch of the no-allocation forward (ssd_chunk_scan_fwd_noalloc): every
 // GPU that the library runs on holds one copy of this array until the
@@ -391,6 +392,150 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
     return fc.finish(SSD_OK);
 }
 
+// ---------------------------------------------------------------- gradients
+
+struct BwdLayout {
+    Layout f;   // the split forward's regions, recomputed
+    size_t adj, qpart, roff, dint, dd, rect, colsum, dDpart, dApart, total;
+};
+
+BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
+                          int ngroups, int chunk_len, ssd_dtype io) {
+    BwdLayout l;
+    l.f = forward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len, io,
+                         ssd::Path::Split);
+    const size_t b = batch, H = nheads, P = headdim, N = dstate, Q = chunk_len;
+    const size_t nc = ((size_t)seqlen + Q - 1) / Q;
+    const size_t nsl = ssd::bwd_state_slices(headdim, dstate);
+    const size_t nrb = ssd::bwd_row_blocks(chunk_len);
+    const size_t tok = round_up(b * H * nc * Q * sizeof(float));
+    size_t off = l.f.total;
+    l.adj = off;
+    off += round_up(b * nc * H * P * N * sizeof(float));
+    l.qpart = off;
+    off += round_up(b * nc * H * nsl * sizeof(double));
+    l.roff = off;
+    off += tok;
+    l.dint = off;
+    off += tok;
+    l.dd = off;
+    off += tok;
+    l.rect = off;
+    off += tok;
+    l.colsum = off;
+    off += round_up(b * H * nc * nrb * Q * sizeof(float));
+    l.dDpart = off;
+    off += round_up(b * nc * H * nrb * sizeof(float));
+    l.dApart = off;
+    off += round_up(b * nc * H * sizeof(double));
+    l.total = off;
+    return l;
+}
+
+ssd_status backward_impl(const void *x, const float *dt, const float *A, const void *B,
+                         const void *C, const float *D, const float *initial_state,
+                         const void *dy, const float *dfinal, int chunk_len, int ngroups,
+                         int batch, int seqlen, int nheads, int headdim, int dstate,
+                         ssd_dtype io_dtype, void *dx, float *ddt, float *dA, void *dB,
+                         void *dC, float *dD, float *dinit, void *workspace,
+                         size_t workspace_bytes, hipStream_t stream, hipEvent_t *events,
+                         int *nkernels, const char **names) {
+    ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                        chunk_len, io_dtype);
+    if (st != SSD_OK) return st;
+    if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
+        return SSD_ERR_INVALID_ARGUMENT;
+    if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) ||
+        !aligned(dx, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(dt, 4) ||
+        !aligned(A, 4) || !aligned(ddt, 4) || !aligned(dA, 4) || (D && !aligned(D, 4)) ||
+        (dD && !aligned(dD, 4)) || (initial_state && !aligned(initial_state, 16)) ||
+        (dfinal && !aligned(dfinal, 16)) || (dinit && !aligned(dinit, 16)))
+        return SSD_ERR_INVALID_ARGUMENT;
+    const BwdLayout lay = backward_layout(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                          chunk_len, io_dtype);
+    if (!workspace || workspace_bytes < lay.total || !aligned(workspace, kAlign))
+        return SSD_ERR_WORKSPACE;
+
+    char *ws = static_cast<char *>(workspace);
+    ssd::BackwardArgs a;
+    ssd::ForwardArgs &f = a.f;
+    f.x = x;
+    f.dt = dt;
+    f.A = A;
+    f.B = B;
+    f.C = C;
+    f.D = D;
+    f.init = initial_state;
+    f.y = nullptr;
+    f.batch = batch;
+    f.L = seqlen;
+    f.H = nheads;
+    f.G = ngroups;
+    f.P = headdim;
+    f.N = dstate;
+    f.Q = chunk_len;
+    f.nchunks = (seqlen + chunk_len - 1) / chunk_len;
+    f.acum_hi = reinterpret_cast<float *>(ws + lay.f.acum_hi);
+    f.acum_lo = reinterpret_cast<float *>(ws + lay.f.acum_lo);
+    f.dtT = reinterpret_cast<float *>(ws + lay.f.dtT);
+    f.cb = ws + lay.f.cb;
+    f.S = reinterpret_cast<float *>(ws + lay.f.S);
+    f.segst = nullptr;
+    f.final_state = nullptr;
+    a.dy = dy;
+    a.dfinal = dfinal;
+    a.dx = dx;
+    a.ddt = ddt;
+    a.dA = dA;
+    a.dB = dB;
+    a.dC = dC;
+    a.dD = dD;
+    a.dinit = dinit;
+    a.adj = reinterpret_cast<float *>(ws + lay.adj);
+    a.qpart = reinterpret_cast<double *>(ws + lay.qpart);
+    a.roff = reinterpret_cast<float *>(ws + lay.roff);
+    a.dint = reinterpret_cast<float *>(ws + lay.dint);
+    a.dd = reinterpret_cast<float *>(ws + lay.dd);
+    a.rect = reinterpret_cast<float *>(ws + lay.rect);
+    a.colsum = reinterpret_cast<float *>(ws + lay.colsum);
+    a.dDpart = reinterpret_cast<float *>(ws + lay.dDpart);
+    a.dApart = reinterpret_cast<double *>(ws + lay.dApart);
+
+    if (nkernels) *nkernels = ssd::kBackwardKernels;
+    if (names)
+        for (int i = 0; i < ssd::kBackwardKernels; ++i) names[i] = ssd::kBackwardKernelNames[i];
+
+    const int es = io_dtype == SSD_BF16 ? 2 : 4;
+    const size_t nx = (size_t)batch * seqlen * nheads * headdim;
+    const size_t nbc = (size_t)batch * seqlen * ngroups * dstate;
+    const size_t nst = (size_t)batch * nheads * headdim * dstate;
+    const size_t ntok = (size_t)batch * seqlen * nheads;
+    FiniteCheck fc(stream);
+    fc.input(x, nx, es);
+    fc.input(dt, ntok, 4);
+    fc.input(A, nheads, 4);
+    fc.input(B, nbc, es);
+    fc.input(C, nbc, es);
+    fc.input(D, D ? (size_t)nheads : 0, 4);
+    fc.input(initial_state, initial_state ? nst : 0, 4);
+    fc.input(dy, nx, es);
+    fc.input(dfinal, dfinal ? nst : 0, 4);
+    if (poison_requested()) {
+        if (ssd::launch_poison(workspace, lay.total, stream) != hipSuccess) return SSD_ERR_HIP;
+    }
+    const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_backward<ssd::bf16>(a, stream, events)
+                                                : ssd::launch_backward<float>(a, stream, events);
+    if (err != hipSuccess) return SSD_ERR_HIP;
+    fc.output(dx, nx, es);
+    fc.output(ddt, ntok, 4);
+    fc.output(dA, nheads, 4);
+    fc.output(dB, nbc, es);
+    fc.output(dC, nbc, es);
+    fc.output(dD, dD ? (size_t)nheads : 0, 4);
+    fc.output(dinit, dinit ? nst : 0, 4);
+    return fc.finish(SSD_OK);
+}
+
 }  // namespace
 
 extern "C" {
@@ -690,6 +835,53 @@ ssd_status ssd_gated_rmsnorm_fwd(const void *y, const void *z, const float *weig
     if (err != hipSuccess) return SSD_ERR_HIP;
     fc.output(out, n, es);
     return fc.finish(SSD_OK);
+}
+
+ssd_status ssd_chunk_scan_bwd_workspace_size(int batch, int seqlen, int nheads, int headdim,
+                                             int dstate, int ngroups, int chunk_len,
+                                             ssd_dtype io_dtype, size_t *bytes) {
+    if (!bytes) return SSD_ERR_INVALID_ARGUMENT;
+    const ssd_status st = check_forward_shape(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                              chunk_len, io_dtype);
+    if (st != SSD_OK) return st;
+    *bytes = backward_layout(batch, seqlen, nheads, headdim, dstate, ngroups, chunk_len,
+                             io_dtype)
+                 .total;
+    return SSD_OK;
+}
+
+ssd_status ssd_chunk_scan_bwd(const void *x, const float *dt, const float *A, const void *B,
+                              const void *C, const float *D, const float *initial_state,
+                              const void *dy, const float *dfinal_state, int chunk_len,
+                              int ngroups, int batch, int seqlen, int nheads, int headdim,
+                              int dstate, ssd_dtype io_dtype, void *dx, float *ddt, float *dA,
+                              void *dB, void *dC, float *dD, float *dinitial_state,
+                              void *workspace, size_t workspace_bytes, hipStream_t stream) {
+    return backward_impl(x, dt, A, B, C, D, initial_state, dy, dfinal_state, chunk_len, ngroups,
+                         batch, seqlen, nheads, headdim, dstate, io_dtype, dx, ddt, dA, dB, dC,
+                         dD, dinitial_state, workspace, workspace_bytes, stream, nullptr,
+                         nullptr, nullptr);
+}
+
+int ssd_chunk_scan_bwd_max_kernels(void) { return ssd::kBackwardKernels; }
+
+ssd_status ssd_chunk_scan_bwd_timed(const void *x, const float *dt, const float *A,
+                                    const void *B, const void *C, const float *D,
+                                    const float *initial_state, const void *dy,
+                                    const float *dfinal_state, int chunk_len, int ngroups,
+                                    int batch, int seqlen, int nheads, int headdim, int dstate,
+                                    ssd_dtype io_dtype, void *dx, float *ddt, float *dA,
+                                    void *dB, void *dC, float *dD, float *dinitial_state,
+                                    void *workspace, size_t workspace_bytes,
+                                    hipStream_t stream, hipEvent_t *events, int nevents,
+                                    int *nkernels, const char **kernel_names) {
+    if (!events || nevents < ssd::kBackwardKernels + 1) return SSD_ERR_INVALID_ARGUMENT;
+    for (int i = 0; i <= ssd::kBackwardKernels; ++i)
+        if (!events[i]) return SSD_ERR_INVALID_ARGUMENT;
+    return backward_impl(x, dt, A, B, C, D, initial_state, dy, dfinal_state, chunk_len, ngroups,
+                         batch, seqlen, nheads, headdim, dstate, io_dtype, dx, ddt, dA, dB, dC,
+                         dD, dinitial_state, workspace, workspace_bytes, stream, events,
+                         nkernels, kernel_names);
 }
 
 }  // extern "C"

@@ -1,0 +1,59 @@
+// ssd_backward.hpp -- internal interface of the gradient pass of the chunked
+// forward (ssd_chunk_scan_bwd): its arguments and workspace, and the launch
+// functions it shares with the split forward.  Not installed; the public ABI
+// is include/ssd.h.
+#pragma once
+
+#include "ssd_kernels.hpp"
+
+namespace ssd {
+
+// One gradient call.  `f` holds the forward's inputs, shapes and the
+// workspace regions of the split forward (prefix sums, C B^T, chunk states),
+// which the pass recomputes (f.final_state is not needed: null).
+struct BackwardArgs {
+    ForwardArgs f;
+    const void *dy;        // [b][L][H][P] io type
+    const float *dfinal;   // [b][H][P][N], or null (0)
+    void *dx;              // [b][L][H][P] io type
+    float *ddt;            // [b][L][H]
+    float *dA;             // [H]
+    void *dB, *dC;         // [b][L][G][N] io type
+    float *dD;             // [H], or null
+    float *dinit;          // [b][H][P][N], or null
+    // workspace
+    float *adj;     // [b][nc][H][P][N]: G_c, then the gradient with respect
+                    // to the state at the end of chunk c
+    double *qpart;  // [b][nc][H][nsl]: partial sums of <that gradient, h_in[c]>
+    float *roff;    // [b][H][nc][Q]: <dy_t, e^(acum_t) h_in C_t> per head
+    float *dint;    // [b][H][nc][Q]: x_t . (e^(acum_end - acum_t) Lam B_t)
+    float *dd;      // [b][H][nc][Q]: x_t . u_t (the direct part of ddt)
+    float *rect;    // [b][H][nc][Q]: the in-block part of the rectangle sums of W
+    float *colsum;  // [b][H][nc][nrb][Q]: column sums of W over each row block
+    float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
+    double *dApart; // [b][nc][H]: partial sums of dt * dLoss/d(dt A)
+};
+
+// Slices of a state (4 elements per thread, 256 threads) in the reverse
+// state pass.
+inline int bwd_state_slices(int P, int N) { return (P * N + 1023) / 1024; }
+// Row blocks of a chunk in the gradient kernels (64 rows, or the chunk).
+inline int bwd_row_blocks(int Q) { return Q > 64 ? Q / 64 : 1; }
+
+constexpr int kBackwardKernels = 8;
+extern const char *const kBackwardKernelNames[kBackwardKernels];
+
+// The first four kernels of the split forward (k1 .. k4), and k3 in its
+// gradient form (G_c = sum_s dy_s exp(acum_s) C_s^T into `out`).
+template <typename T> hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream);
+template <typename T>
+hipError_t launch_adj_chunk_states(const ForwardArgs &a, const void *dy, float *out,
+                                   hipStream_t stream);
+
+// The whole gradient pass.  When `events` is non-null, events[i] is recorded
+// right before kernel i and events[kBackwardKernels] after the last.
+template <typename T>
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream,
+                           hipEvent_t *events = nullptr);
+
+}  // namespace ssd

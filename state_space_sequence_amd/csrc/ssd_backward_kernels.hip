@@ -1,0 +1,646 @@
+// ssd_backward_kernels.hip -- the gradient pass of the chunked SSD forward
+// (ssd_chunk_scan_bwd): the gradients of (y, final_state) with respect to x,
+// dt, A, B, C, D and the initial state, recomputing the forward's
+// intermediates instead of storing them (the recompute-backward path of the
+// burn-mamba rustdoc, `ssd_serial_recalculated`; the pages give only its
+// existence, the steps below are the derivative of the four steps of
+// `ssd_minimal`, Eqs. 20-23).
+//
+// Notation, per batch b, head h (group g), chunk c of Q tokens; acum_t the
+// chunk's inclusive prefix sum of dt A; h_in[c] the state entering chunk c
+// (h_in[nc] the final state); Lam[c] = dLoss/dh_in[c + 1], the gradient with
+// respect to the state at the end of chunk c.
+//
+//   Lam[nc-1] = dfinal;  Lam[c-1] = exp(acum_end[c]) Lam[c] + G_c,
+//     G_c = sum_{s in c} exp(acum_s) dy_s (outer) C_s,  dinit = Lam[-1]
+//   u_t   = sum_{s >= t} exp(acum_s - acum_t) (C_s . B_t) dy_s
+//           + exp(acum_end - acum_t) Lam[c] B_t                          [P]
+//   dx_t  = D dy_t + dt_t u_t
+//   dB_t  = sum_h dt_t [ sum_{s >= t} exp(acum_s - acum_t) (x_t . dy_s) C_s
+//           + exp(acum_end - acum_t) x_t Lam[c] ]                        [N]
+//   dC_t  = sum_h [ sum_{s <= t} exp(acum_t - acum_s) dt_s (dy_t . x_s) B_s
+//           + exp(acum_t) dy_t h_in[c] ]                                 [N]
+//   dLoss/d(dt_t A) = g_t
+//     = sum_{s >= t} roff_s + e^(acum_end) <Lam[c], h_in[c]>
+//       + sum_{s >= t} sum_{s' < t} W[s][s'] + sum_{s' < t} dt_s' dint_s',
+//     roff_s = <dy_s, e^(acum_s) h_in[c] C_s>  (the state part of <dy, y - D x>)
+//     dint_s = x_s . (e^(acum_end - acum_s) Lam[c] B_s)  (the state part of x . u)
+//     W[s][s'] = e^(acum_s - acum_s') dt_s' (dy_s . x_s') (C_s . B_s'), s' <= s
+//   ddt_t = x_t . u_t + A g_t,  dA = sum_t dt_t g_t,  dD = sum_t dy_t . x_t
+// g_t is <grad h_t, e^(dt_t A) h_{t-1}> of the serial loop (the fp64
+// oracle's backward), regrouped by the chunked factors of Eqs. 20-23.  The
+// plainer form, a reverse prefix sum over the chunk of <dy_k, y_k - D x_k> -
+// dt_k x_k . u_k, subtracts terms that mostly cancel (the W block below the
+// diagonal from both t onwards appears in both); the rectangle sum of W
+// (rows >= t, columns < t) keeps only what remains, so g_t and dA keep the
+// accuracy of their terms.
+#include "ssd_device.hpp"
+#include "ssd_backward.hpp"
+
+namespace ssd {
+
+namespace {
+
+// Sum over the 64 lanes of the wave.
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+__device__ __forceinline__ double wave_sum_f64(double v) {
+#pragma unroll
+    for (int d = 32; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+// Sum over the 16 lanes of each 16-lane group (the lanes of one MFMA row).
+__device__ __forceinline__ float row16_sum(float v) {
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------ reverse state pass
+// grid (nsl, H, b), 256 threads, 4 consecutive state elements per thread.
+// Serial over chunks from the last: adj[c] holds G_c on entry and Lam[c] on
+// exit; qpart gets each slice's share of <Lam[c], h_in[c]> (fp64).
+__global__ void __launch_bounds__(256)
+kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
+                 const float *__restrict__ acum_hi,
+                 const float *__restrict__ dfinal, float *__restrict__ dinit,
+                 double *__restrict__ qpart, int H, int PN, int nc, int Q, int nsl) {
+    __shared__ double red[4];
+    const int h = blockIdx.y, b = blockIdx.z, tid = threadIdx.x;
+    const int e0 = (blockIdx.x * 256 + tid) * 4;
+    const bool in = e0 < PN;   // (PN is a multiple of 4: all four or none)
+    const size_t soff = (size_t)(b * H + h) * PN + e0;
+    f32x4 lam = zero4();
+    if (in && dfinal) lam = *reinterpret_cast<const f32x4 *>(dfinal + soff);
+    const float *ac = acum_hi + (size_t)(b * H + h) * nc * Q;
+    for (int c = nc - 1; c >= 0; --c) {
+        const size_t off = ((size_t)(b * nc + c) * H + h) * PN + e0;
+        double part = 0.0;
+        f32x4 G = zero4();
+        if (in) {
+            G = *reinterpret_cast<const f32x4 *>(adj + off);
+            const f32x4 hn = *reinterpret_cast<const f32x4 *>(S + off);
+            part = (double)lam[0] * hn[0] + (double)lam[1] * hn[1] + (double)lam[2] * hn[2] +
+                   (double)lam[3] * hn[3];
+            *reinterpret_cast<f32x4 *>(adj + off) = lam;
+        }
+        part = wave_sum_f64(part);
+        if ((tid & 63) == 0) red[tid >> 6] = part;
+        __syncthreads();
+        if (tid == 0)
+            qpart[((size_t)(b * nc + c) * H + h) * nsl + blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+        __syncthreads();
+        const float dec = fast_exp(ac[(size_t)c * Q + Q - 1]);
+        lam = dec * lam + G;
+    }
+    if (in && dinit) *reinterpret_cast<f32x4 *>(dinit + soff) = lam;
+}
+
+// ------------------------------------------------------------ intra-chunk gradients
+// One kernel, three products (MODE):
+//   kDx: rows t of head h, columns p:  u_t  (then dx_t, d_t, dD partials)
+//   kDb: rows t of group g, columns n: dB_t, summed over the group's heads
+//   kDc: rows t of group g, columns n: dC_t, summed over the group's heads
+//        (and r_t per head)
+// Each is   out_t = rowscale_t [ stscale_t U_t St  +  sum_s Wt[t][s] V_s ]:
+//            U (K)        St [K x W]        Wt[t][s]                        V
+//   kDx:   B_t (N)      Lam^T            (C_s . B_t) e^(acum_s - acum_t), s >= t   dy_s
+//   kDb:   x_t (P)      Lam              (x_t . dy_s) e^(acum_s - acum_t), s >= t  C_s
+//   kDc:   dy_t (P)     h_in             (dy_t . x_s) e^(acum_t - acum_s) dt_s,
+//                                                                      s <= t      B_s
+// with stscale e^(acum_end - acum_t) (kDx, kDb) or e^(acum_t) (kDc), and
+// rowscale dt_t for kDb (kDx applies dt_t in its epilogue).  C_s . B_t comes
+// from the forward's C B^T blocks (its lower triangle, row s >= column t);
+// the (x . dy) scores are MFMA products over the headdim.
+//
+// grid (nc * nrb, H (kDx) or G, b), 256 threads (4 waves), dynamic LDS
+// KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64) rows of row
+// block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column tiles span
+// the output width W (P or N, padded; padded columns are never stored).
+// Per source block: V staged in LDS (fp32: token rows of a pitch = 16 mod 64
+// floats, read with the K index kk + q + 4 j; bf16: transposed rows), the
+// wave's rows of Wt built in LDS in the operand type, then the MFMAs.
+enum { kDx = 0, kDb = 1, kDc = 2 };
+
+struct KbLds {
+    static constexpr int kSB = 64;
+    static __host__ __device__ constexpr int vpitch(int WP, int sz) {
+        return sz == 4 ? WP + (80 - WP % 64) % 64 : kSB + 16 / sz;
+    }
+    static __host__ __device__ constexpr size_t v_elems(int WP, int sz) {
+        return (size_t)(sz == 4 ? kSB : WP) * vpitch(WP, sz);
+    }
+    static __host__ __device__ constexpr int mpitch(int sz) { return kSB + 16 / sz; }
+    // + prefix sums and dt by token, a reduction slot per wave, and for the
+    // dC pass the diagonal block of W, its rows' sums over the earlier
+    // blocks and the column sums of each earlier block (fp32)
+    static size_t bytes(int WP, int sz) {
+        return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz)) * sz + 3 * 256 * 4 + 64 +
+               ((size_t)kSB * (kSB + 1) + kSB + 4 * kSB) * 4;
+    }
+};
+
+template <typename T, int MODE, int NW>
+__global__ void __launch_bounds__(256)
+kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
+       const T *__restrict__ dy, const float *__restrict__ cb, const float *__restrict__ S,
+       const float *__restrict__ adj, const float *__restrict__ acum_hi,
+       const float *__restrict__ acum_lo, const float *__restrict__ dtT,
+       const float *__restrict__ D, T *__restrict__ out, float *__restrict__ roff,
+       float *__restrict__ dint, float *__restrict__ dd, float *__restrict__ rect,
+       float *__restrict__ colsum, float *__restrict__ dDpart, int L, int H, int G, int P,
+       int N, int nc, int Q) {
+    typedef typename Mma<T>::frag frag;
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr bool F32 = SZ == 4;
+    constexpr int SBX = KbLds::kSB;
+    constexpr int WP = 16 * NW;
+    constexpr int VP = KbLds::vpitch(WP, SZ);
+    constexpr int PITCH = KbLds::mpitch(SZ);
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *VS = reinterpret_cast<T *>(smem_raw);                 // V of the source block
+    T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: Wt, this row block
+    float *r_hi = reinterpret_cast<float *>(MT + (size_t)SBX * PITCH);
+    float *r_lo = r_hi + 256;
+    float *r_dt = r_lo + 256;
+    float *red = r_dt + 256;                                  // [16]
+    float *Wd = red + 16;                                     // [SBX][SBX + 1]
+    float *s_rrow = Wd + SBX * (SBX + 1);                     // [SBX]
+    float *s_col = s_rrow + SBX;                              // [4][SBX]
+    // the position of tile column s in an Wt row (fp32: the fragments take
+    // the K index kk + q + 4 j, stored at kk + 4 q + j)
+    auto mcol = [](int s) -> int {
+        if constexpr (F32)
+            return (s & ~15) | ((s & 3) << 2) | ((s >> 2) & 3);
+        else
+            return s;
+    };
+    auto vat = [](int s, int w) -> int {
+        if constexpr (F32)
+            return s * VP + w;
+        else
+            return w * PITCH + s;
+    };
+
+    const int nrb = Q > SBX ? Q / SBX : 1;
+    const int c = blockIdx.x / nrb, lb = blockIdx.x % nrb;
+    const int b = blockIdx.z;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int SB = Q < SBX ? Q : SBX;
+    const int SBK = SB < KS ? KS : SB;       // tile columns the MFMAs read (zeros past SB)
+    const bool active = wave * 16 < SB;
+    const int W = MODE == kDx ? P : N;       // output width
+    const int KD = MODE == kDx ? N : P;      // K of the state product
+    const int hpg = H / G;
+    const int g = MODE == kDx ? blockIdx.y / hpg : blockIdx.y;
+    const int h_first = MODE == kDx ? blockIdx.y : g * hpg;
+    const int h_count = MODE == kDx ? 1 : hpg;
+    const int t0 = c * Q + lb * SB;          // the row block's first token
+    const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
+
+    f32x4 tot[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) tot[i] = zero4();
+
+    for (int hh = 0; hh < h_count; ++hh) {
+        const int h = h_first + hh;
+        const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;   // prefix sums, dt
+        __syncthreads();   // (the previous head's vectors and tiles are no longer read)
+        for (int l = tid; l < Q; l += 256) {
+            r_hi[l] = acum_hi[vbase + l];
+            r_lo[l] = acum_lo[vbase + l];
+            r_dt[l] = dtT[vbase + l];
+        }
+        __syncthreads();
+        const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
+
+        // ---- the state product U_t St, scaled per row
+        f32x4 acc[NW];
+#pragma unroll
+        for (int i = 0; i < NW; ++i) acc[i] = zero4();
+        const float *st = MODE == kDc ? S + ((size_t)(b * nc + c) * H + h) * P * N
+                                      : adj + ((size_t)(b * nc + c) * H + h) * P * N;
+        if (active) {
+            const int tr = t0 + wave * 16 + r;   // this lane's U row
+            const T *urow = MODE == kDx ? Bm + (((size_t)b * L + tr) * G + g) * N
+                          : MODE == kDb ? x + (((size_t)b * L + tr) * H + h) * P
+                                        : dy + (((size_t)b * L + tr) * H + h) * P;
+            for (int k0 = 0; k0 < KD; k0 += KS) {
+                const int k = k0 + VEC * q;
+                const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
+#pragma unroll
+                for (int wt = 0; wt < NW; ++wt) {
+                    const int w = wt * 16 + r;
+                    frag sb;
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) {
+                        float v = 0.f;
+                        if (w < W && k + j < KD)
+                            v = MODE == kDx ? st[(size_t)w * N + k + j] : st[(size_t)(k + j) * N + w];
+                        sb[j] = from_f32<T>(v);
+                    }
+                    acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int l = lb * SB + wave * 16 + 4 * q + i;
+                const float e = MODE == kDc ? fast_exp(r_hi[l])
+                                            : fast_exp(prefix_diff(end_hi, end_lo, r_hi[l], r_lo[l]));
+#pragma unroll
+                for (int wt = 0; wt < NW; ++wt) acc[wt][i] *= e;
+            }
+            // the state part of x . u (kDx) or of <dy, y - D x> (kDc), per row
+            if constexpr (MODE != kDb) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+                    const bool tin = t < L && l < Q;
+                    float v = 0.f;
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) {
+                        const int w = wt * 16 + r;
+                        if (!tin || w >= W) continue;
+                        const T *o = MODE == kDx ? x + (((size_t)b * L + t) * H + h) * P
+                                                 : Cm + (((size_t)b * L + t) * G + g) * N;
+                        v += to_f32(o[w]) * acc[wt][i];
+                    }
+                    v = row16_sum(v);
+                    if (r == 0 && l < Q) (MODE == kDx ? dint : roff)[vbase + l] = tin ? v : 0.f;
+                }
+            }
+        }
+        float rowp[4] = {0.f, 0.f, 0.f, 0.f};   // kDc: this lane's share of W's row sums
+
+        // ---- the intra-chunk product, source block by source block
+        const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
+        for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+            __syncthreads();   // (the previous block's V and Wt are no longer read)
+            // V of the block
+            const int wv = WP / VEC;
+            for (int v = tid; v < SBK * wv; v += 256) {
+                const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+                frag f = zero_frag<T>();
+                if (sl < SB && ts < L && w0 < W)
+                    f = load_frag(MODE == kDx ? dy + (((size_t)b * L + ts) * H + h) * P + w0
+                                  : MODE == kDb ? Cm + (((size_t)b * L + ts) * G + g) * N + w0
+                                                : Bm + (((size_t)b * L + ts) * G + g) * N + w0);
+                if constexpr (F32) {
+                    *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
+                } else {
+#pragma unroll
+                    for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
+                }
+            }
+            // this wave's rows of Wt
+            if (active) {
+                if constexpr (MODE == kDx) {
+                    // lane: row tl = lane % 16, columns 16 (lane / 16) + j
+#pragma unroll 4
+                    for (int j = 0; j < 16; ++j) {
+                        const int tl = wave * 16 + r, sl = q * 16 + j;
+                        const int lt = lb * SB + tl, ls = sb * SB + sl;
+                        float v = 0.f;
+                        if (sl < SB && ls >= lt)
+                            v = cb[(cbase + ls) * Q + lt] *
+                                fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
+                        MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
+                    }
+                    if (SBK > SB) {   // (bf16 chunks of 16: zero columns SB .. SBK - 1)
+                        for (int j = 0; j < 16; ++j) {
+                            const int sl = SB + q * 16 + j;
+                            if (sl < SBK) MT[(wave * 16 + r) * PITCH + mcol(sl)] = from_f32<T>(0.f);
+                        }
+                    }
+                } else {
+                    // scores (x_t . dy_s) or (dy_t . x_s): 16 rows x 64 columns over the headdim
+                    f32x4 z[4] = {zero4(), zero4(), zero4(), zero4()};
+                    const int tr = t0 + wave * 16 + r;
+                    const T *arow = (MODE == kDb ? x : dy) + (((size_t)b * L + tr) * H + h) * P;
+                    const T *bsrc = MODE == kDb ? dy : x;
+                    for (int k0 = 0; k0 < P; k0 += KS) {
+                        const int k = k0 + VEC * q;
+                        const frag za = tr < L && k < P ? load_frag(arow + k) : zero_frag<T>();
+#pragma unroll
+                        for (int stl = 0; stl < 4; ++stl) {
+                            const int sl = stl * 16 + r, ts = c * Q + sb * SB + sl;
+                            const frag zb = sl < SB && ts < L && k < P
+                                                ? load_frag(bsrc + (((size_t)b * L + ts) * H + h) * P + k)
+                                                : zero_frag<T>();
+                            z[stl] = Mma<T>::mma(za, zb, z[stl]);
+                        }
+                    }
+#pragma unroll
+                    for (int stl = 0; stl < 4; ++stl) {
+                        float colp = 0.f;
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) {
+                            const int tl = wave * 16 + 4 * q + i, sl = stl * 16 + r;
+                            const int lt = lb * SB + tl, ls = sb * SB + sl;
+                            float v = 0.f;
+                            if (sl < SB) {
+                                if (MODE == kDb && ls >= lt)
+                                    v = z[stl][i] * fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
+                                if (MODE == kDc && ls <= lt)
+                                    v = z[stl][i] * fast_exp(prefix_diff(r_hi[lt], r_lo[lt], r_hi[ls], r_lo[ls])) *
+                                        r_dt[ls];
+                            }
+                            if (sl < SBK) MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
+                            if constexpr (MODE == kDc) {
+                                // W = v (C_t . B_s), in fp32, for the dt A gradient
+                                const float w = v != 0.f ? v * cb[(cbase + lt) * Q + ls] : 0.f;
+                                if (sb < lb) {
+                                    rowp[i] += w;
+                                    colp += w;
+                                } else if (sl < SB) {
+                                    Wd[tl * (SBX + 1) + sl] = w;
+                                }
+                            }
+                        }
+                        if constexpr (MODE == kDc) {
+                            if (sb < lb) {
+                                colp += __shfl_xor(colp, 16, kWave);
+                                colp += __shfl_xor(colp, 32, kWave);
+                                if (q == 0) s_col[wave * SBX + stl * 16 + r] = colp;
+                            }
+                        }
+                    }
+                }
+            }
+            __syncthreads();
+            if constexpr (MODE == kDc) {
+                // the column sums of W over this row block, for the rows of
+                // earlier blocks' dt A gradients (every wave is active here:
+                // a chunk with an earlier block has 64-row blocks)
+                if (sb < lb && tid < SBX)
+                    colsum[(((size_t)(b * H + h) * nc + c) * nrb + lb) * Q + sb * SB + tid] =
+                        s_col[tid] + s_col[SBX + tid] + s_col[2 * SBX + tid] + s_col[3 * SBX + tid];
+            }
+            if (!active) continue;
+            for (int kk = 0; kk < SBK; kk += KS) {
+                const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
+#pragma unroll
+                for (int wt = 0; wt < NW; ++wt) {
+                    frag vb;
+                    if constexpr (F32) {
+#pragma unroll
+                        for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
+                    } else {
+                        vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
+                    }
+                    acc[wt] = Mma<T>::mma(m, vb, acc[wt]);
+                }
+            }
+        }
+
+        // ---- per head
+        if (active) {
+            if constexpr (MODE == kDx) {
+                const float Dh = D ? D[h] : 0.f;
+                float dsum = 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+                    const bool tin = t < L && l < Q;
+                    const float dtl = r_dt[l];
+                    const size_t ro = (((size_t)b * L + t) * H + h) * P;
+                    float ds = 0.f;
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) {
+                        const int p = wt * 16 + r;
+                        if (!tin || p >= P) continue;
+                        const float xv = to_f32(x[ro + p]), gv = to_f32(dy[ro + p]);
+                        const float u = acc[wt][i];
+                        ds += xv * u;
+                        dsum += gv * xv;
+                        out[ro + p] = from_f32<T>(Dh * gv + dtl * u);
+                    }
+                    ds = row16_sum(ds);
+                    if (r == 0 && l < Q) dd[vbase + l] = tin ? ds : 0.f;
+                }
+                dsum = wave_sum(dsum);
+                if (lane == 0) red[wave] = dsum;
+            } else if constexpr (MODE == kDc) {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += acc[wt][i];
+                    const float rs = row16_sum(rowp[i]);
+                    if (r == 0) s_rrow[wave * 16 + 4 * q + i] = rs;
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    const int l = lb * SB + wave * 16 + 4 * q + i;
+                    const float dtl = r_dt[l];
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += dtl * acc[wt][i];
+                }
+            }
+        }
+        if constexpr (MODE == kDc) {
+            // the block's rows of the rectangle sums: for t in this block,
+            // sum_{s >= t in the block} (sum_{s' in earlier blocks} W[s][s']
+            // + sum_{t > s' in this block} W[s][s']); four threads per t
+            __syncthreads();
+            const int tau = tid >> 2, sub = tid & 3;
+            float v = 0.f;
+            if (tau < SB) {
+                for (int rho = tau + sub; rho < SB; rho += 4) {
+                    float a = s_rrow[rho];
+                    for (int col = 0; col < tau; ++col) a += Wd[rho * (SBX + 1) + col];
+                    v += a;
+                }
+            }
+            v += __shfl_xor(v, 1, kWave);
+            v += __shfl_xor(v, 2, kWave);
+            if (sub == 0 && tau < SB) rect[vbase + lb * SB + tau] = v;
+        }
+        if constexpr (MODE == kDx) {
+            __syncthreads();
+            if (tid == 0) {
+                float s = 0.f;
+                for (int w = 0; w < 4; ++w)
+                    if (w * 16 < SB) s += red[w];
+                dDpart[((size_t)(b * nc + c) * H + h) * nrb + lb] = s;
+            }
+        }
+    }
+
+    // ---- dB / dC rows of the row block
+    if constexpr (MODE != kDx) {
+        if (active) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+                if (t >= L || l >= Q) continue;
+#pragma unroll
+                for (int wt = 0; wt < NW; ++wt) {
+                    const int n = wt * 16 + r;
+                    if (n < N) out[(((size_t)b * L + t) * G + g) * N + n] = from_f32<T>(tot[wt][i]);
+                }
+            }
+        }
+    }
+}
+
+// ------------------------------------------------------------ ddt and dA
+// Inclusive prefix sum over the workgroup's 256 threads (fp64); `tot` is a
+// 4-slot LDS scratch, free again when the call returns.
+__device__ __forceinline__ double block_scan_f64(double v, double *tot) {
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    double inc = wave_inclusive_scan_f64(v, lane);
+    if (lane == 63) tot[wave] = inc;
+    __syncthreads();
+    for (int w = 0; w < wave; ++w) inc += tot[w];
+    __syncthreads();
+    return inc;
+}
+
+// grid (nc, H, b), 256 threads, token t = tid of the chunk: g_t (the
+// gradient with respect to dt_t A) from its four parts, ddt_t, and the
+// chunk's share of dA, in fp64.
+__global__ void __launch_bounds__(256)
+kb_ddt(const float *__restrict__ roff, const float *__restrict__ dint,
+       const float *__restrict__ dd, const float *__restrict__ rect,
+       const float *__restrict__ colsum, const float *__restrict__ dtT,
+       const float *__restrict__ acum_hi, const double *__restrict__ qpart,
+       const float *__restrict__ A, float *__restrict__ ddt, double *__restrict__ dApart,
+       int L, int H, int nc, int Q, int nsl, int nrb) {
+    __shared__ double s_tot[4];
+    __shared__ double s_red[4];
+    const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
+    const int SB = Q < 64 ? Q : 64;
+    const bool in = tid < Q;
+    double qc = 0.0;
+    for (int i = 0; i < nsl; ++i) qc += qpart[((size_t)(b * nc + c) * H + h) * nsl + i];
+    qc *= (double)fast_exp(acum_hi[vbase + Q - 1]);
+    const float dtl = in ? dtT[vbase + tid] : 0.f;
+    // sum_{s >= t} roff_s: a prefix sum over the reversed order
+    const double ro = tid < Q ? (double)roff[vbase + (Q - 1 - tid)] : 0.0;
+    const double suf_rev = block_scan_f64(ro, s_tot);   // at thread j: sum over s >= Q-1-j
+    __shared__ double s_suf[256];
+    if (in) s_suf[Q - 1 - tid] = suf_rev;
+    // sum_{s' < t} dt_s' dint_s'
+    const double di = in ? (double)dtl * dint[vbase + tid] : 0.0;
+    const double pre = block_scan_f64(di, s_tot) - di;
+    // the rectangle's rows in later blocks: sum over blocks lb > t's block of
+    // sum_{s' < t} colsum_lb[s'] (colsum_lb is defined below block lb)
+    double cross = 0.0;
+    const int tb = tid / SB;
+    for (int lb = 1; lb < nrb; ++lb) {
+        const double cv = tid < lb * SB ? (double)colsum[(vbase / Q * nrb + lb) * Q + tid] : 0.0;
+        const double p = block_scan_f64(cv, s_tot) - cv;
+        if (lb > tb) cross += p;
+    }
+    __syncthreads();
+    double gt = 0.0, contrib = 0.0;
+    if (in) {
+        gt = s_suf[tid] + qc + (double)rect[vbase + tid] + cross + pre;
+        const int t = c * Q + tid;
+        if (t < L) ddt[((size_t)b * L + t) * H + h] = (float)((double)dd[vbase + tid] + (double)A[h] * gt);
+        contrib = (double)dtl * gt;
+    }
+    contrib = wave_sum_f64(contrib);
+    if (lane == 0) s_red[wave] = contrib;
+    __syncthreads();
+    if (tid == 0) dApart[(size_t)(b * nc + c) * H + h] = s_red[0] + s_red[1] + s_red[2] + s_red[3];
+}
+
+// ------------------------------------------------------------ dA and dD
+// grid (ceil(H / 256)), one head per thread: the partial sums in a fixed
+// order (deterministic).
+__global__ void __launch_bounds__(256)
+kb_reduce(const double *__restrict__ dApart, const float *__restrict__ dDpart, float *__restrict__ dA,
+          float *__restrict__ dD, int batch, int H, int nc, int nrb) {
+    const int h = blockIdx.x * 256 + threadIdx.x;
+    if (h >= H) return;
+    double sa = 0.0, sd = 0.0;
+    for (int bc = 0; bc < batch * nc; ++bc) {
+        sa += dApart[(size_t)bc * H + h];
+        for (int k = 0; k < nrb; ++k) sd += dDpart[((size_t)bc * H + h) * nrb + k];
+    }
+    dA[h] = (float)sa;
+    if (dD) dD[h] = (float)sd;
+}
+
+// ------------------------------------------------------------ launch
+
+const char *const kBackwardKernelNames[kBackwardKernels] = {
+    "k1..k4 (recompute)", "kb_adj_chunk_state", "kb_state_passing", "kb_dx", "kb_dB",
+    "kb_dC", "kb_ddt", "kb_reduce"};
+
+template <typename T, int MODE, int NW>
+static void launch_mix(const BackwardArgs &a, void *out, hipStream_t stream) {
+    const ForwardArgs &f = a.f;
+    const int nrb = bwd_row_blocks(f.Q);
+    const size_t lds = KbLds::bytes(16 * NW, (int)sizeof(T));
+    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, MODE == kDx ? f.H : f.G, f.batch),
+                       dim3(256), lds, stream, (const T *)f.x, (const T *)f.B, (const T *)f.C,
+                       (const T *)a.dy, (const float *)f.cb, (const float *)f.S, (const float *)a.adj,
+                       (const float *)f.acum_hi, (const float *)f.acum_lo, (const float *)f.dtT,
+                       f.D, (T *)out, a.roff, a.dint, a.dd, a.rect, a.colsum, a.dDpart, f.L, f.H, f.G,
+                       f.P, f.N, f.nchunks, f.Q);
+}
+
+template <typename T>
+hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t *events) {
+    const ForwardArgs &f = a.f;
+    int ev = 0;
+    auto mark = [&]() -> hipError_t {
+        return events ? hipEventRecord(events[ev++], stream) : hipSuccess;
+    };
+    hipError_t err;
+    if ((err = mark()) != hipSuccess) return err;
+    if ((err = launch_split_states<T>(f, stream)) != hipSuccess) return err;
+    if ((err = mark()) != hipSuccess) return err;
+    if ((err = launch_adj_chunk_states<T>(f, a.dy, a.adj, stream)) != hipSuccess) return err;
+    if ((err = mark()) != hipSuccess) return err;
+    const int PN = f.P * f.N, nsl = bwd_state_slices(f.P, f.N);
+    hipLaunchKernelGGL(kb_state_passing, dim3(nsl, f.H, f.batch), dim3(256), 0, stream, a.adj,
+                       (const float *)f.S, (const float *)f.acum_hi,
+                       a.dfinal, a.dinit, a.qpart, f.H, PN, f.nchunks, f.Q, nsl);
+    if ((err = mark()) != hipSuccess) return err;
+    if (f.P <= 64)
+        launch_mix<T, kDx, 4>(a, a.dx, stream);
+    else
+        launch_mix<T, kDx, 8>(a, a.dx, stream);
+    if ((err = mark()) != hipSuccess) return err;
+    if (f.N <= 128)
+        launch_mix<T, kDb, 8>(a, a.dB, stream);
+    else
+        launch_mix<T, kDb, 16>(a, a.dB, stream);
+    if ((err = mark()) != hipSuccess) return err;
+    if (f.N <= 128)
+        launch_mix<T, kDc, 8>(a, a.dC, stream);
+    else
+        launch_mix<T, kDc, 16>(a, a.dC, stream);
+    if ((err = mark()) != hipSuccess) return err;
+    hipLaunchKernelGGL(kb_ddt, dim3(f.nchunks, f.H, f.batch), dim3(256), 0, stream,
+                       (const float *)a.roff, (const float *)a.dint, (const float *)a.dd,
+                       (const float *)a.rect, (const float *)a.colsum, (const float *)f.dtT,
+                       (const float *)f.acum_hi, (const double *)a.qpart, f.A, a.ddt, a.dApart,
+                       f.L, f.H, f.nchunks, f.Q, nsl, bwd_row_blocks(f.Q));
+    if ((err = mark()) != hipSuccess) return err;
+    hipLaunchKernelGGL(kb_reduce, dim3((f.H + 255) / 256), dim3(256), 0, stream,
+                       (const double *)a.dApart, (const float *)a.dDpart, a.dA, a.dD, f.batch, f.H,
+                       f.nchunks, bwd_row_blocks(f.Q));
+    if ((err = mark()) != hipSuccess) return err;
+    return hipGetLastError();
+}
+
+template hipError_t launch_backward<float>(const BackwardArgs &, hipStream_t, hipEvent_t *);
+template hipError_t launch_backward<bf16>(const BackwardArgs &, hipStream_t, hipEvent_t *);
+
+}  // namespace ssd

@@ -34,6 +34,7 @@
 // start passes nothing of the state entering it on (decay 0 in k4).
 #include "ssd_device.hpp"
 #include "ssd_kernels.hpp"
+#include "ssd_backward.hpp"
 
 namespace ssd {
 
@@ -185,7 +186,11 @@ k2_chunk_cb(const T *__restrict__ Bm, const T *__restrict__ Cm,
 // B in memory, so 32-token slabs of both are staged transposed in LDS
 // (XT[p][s], BT[n][s]) with w_s folded into x on the way in; fragments are
 // then 16-byte LDS reads.  Each wave owns up to kK3TilesPerWave 16x16 tiles.
-template <typename T>
+// ADJ: the same product for the gradient pass, G[p][n] = sum_s dy[s][p] *
+// exp(acum_s) * C[s][n] (x -> dy, B -> C, w_s = exp(acum_s)), the part of
+// the gradient with respect to the state entering the chunk that the
+// chunk's own outputs contribute.
+template <typename T, bool ADJ = false>
 __global__ void __launch_bounds__(256)
 k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
                const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
@@ -233,11 +238,11 @@ k3_chunk_state(const T *__restrict__ x, const T *__restrict__ Bm,
         for (int v = tid; v < KB * pv; v += 256) {
             const int sl = v / pv, p0 = (v % pv) * VEC;
             const int s = s0 + sl, t = c * Q + s;
-            const bool in = s < Q && t < L && s >= s_first;
+            const bool in = s < Q && t < L && (ADJ || s >= s_first);
             float w = 0.f;
             typename Mma<T>::frag f = zero_frag<T>();
             if (in) {
-                w = fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s];
+                w = ADJ ? fast_exp(ah[s]) : fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s];
                 f = load_frag(x + (((size_t)b * L + t) * H + h) * P + p0);
             }
 #pragma unroll
@@ -764,6 +769,8 @@ struct K3F32Lds {
     static size_t bytes() { return ((size_t)kKB * pitch(64) + (size_t)kKB * pitch(128) + 256) * 4; }
 };
 
+// (ADJ: the gradient pass's product, as for the bf16 kernel above.)
+template <bool ADJ = false>
 __global__ void __launch_bounds__(256)
 k3_chunk_state_f32(const float *__restrict__ x, const float *__restrict__ Bm,
                    const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
@@ -791,8 +798,10 @@ k3_chunk_state_f32(const float *__restrict__ x, const float *__restrict__ Bm,
         // packed sequences: only the chunk's last sequence reaches its end state
         const int s_first = segst ? segst[((size_t)b * nc + c) * Q + Q - 1] : -1;
         for (int s = tid; s < 256; s += 256) {
-            const bool in = s < Q && c * Q + s < L && s >= s_first;
-            s_w[s] = in ? fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s] : 0.f;
+            const bool in = s < Q && c * Q + s < L && (ADJ || s >= s_first);
+            s_w[s] = !in ? 0.f
+                   : ADJ ? fast_exp(ah[s])
+                         : fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s];
         }
     }
 
@@ -878,6 +887,58 @@ void launch_dA_cumsum(const float *dt, const DtProc &dtp, const float *A, float 
                        dtp, A, acum_hi, acum_lo, dtT, L, H, nc, Q, seq_idx, segst);
 }
 
+// k3 (ADJ: its gradient-pass form) on operands xx, bb into out.
+template <typename T, bool ADJ>
+void launch_k3(const ForwardArgs &a, const void *xx, const void *bb, float *out,
+               const int *segst, hipStream_t stream) {
+    const int nc = a.nchunks, Q = a.Q;
+    if constexpr (sizeof(T) == 4) {
+        const int nblk = ((a.P + 63) / 64) * ((a.N + 127) / 128);
+        hipLaunchKernelGGL(k3_chunk_state_f32<ADJ>, dim3(nc, a.H * nblk, a.batch), dim3(256),
+                           K3F32Lds::bytes(), stream, (const float *)xx, (const float *)bb,
+                           a.acum_hi, a.acum_lo, a.dtT, out, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+    } else {
+        const int ntiles = (a.P / 16) * (a.N / 16);
+        const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
+        const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
+        hipLaunchKernelGGL((k3_chunk_state<T, ADJ>), dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
+                           stream, (const T *)xx, (const T *)bb, a.acum_hi, a.acum_lo, a.dtT,
+                           out, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+    }
+}
+
+// The first four kernels of the forward alone (prefix sums, C B^T, chunk
+// states, state passing; a.final_state receives the final state): what the
+// gradient pass recomputes.
+template <typename T>
+hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream) {
+    const int nc = a.nchunks, Q = a.Q;
+    launch_dA_cumsum(a.dt, a.dtp, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q,
+                     stream);
+    const int nlb = (Q + 63) / 64;
+    hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
+                       dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, (float *)a.cb, a.L,
+                       a.G, a.N, nc, Q);
+    launch_k3<T, false>(a, a.x, a.B, a.S, nullptr, stream);
+    const int PN = a.P * a.N;
+    hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
+                       0, stream, a.S, a.acum_hi, a.init, a.final_state, a.H, PN, nc, Q, nullptr);
+    return hipGetLastError();
+}
+
+// The gradient pass's chunk products G_c = sum_s dy_s exp(acum_s) C_s^T.
+template <typename T>
+hipError_t launch_adj_chunk_states(const ForwardArgs &a, const void *dy, float *out,
+                                   hipStream_t stream) {
+    launch_k3<T, true>(a, dy, a.C, out, nullptr, stream);
+    return hipGetLastError();
+}
+
+template hipError_t launch_split_states<float>(const ForwardArgs &, hipStream_t);
+template hipError_t launch_split_states<bf16>(const ForwardArgs &, hipStream_t);
+template hipError_t launch_adj_chunk_states<float>(const ForwardArgs &, const void *, float *, hipStream_t);
+template hipError_t launch_adj_chunk_states<bf16>(const ForwardArgs &, const void *, float *, hipStream_t);
+
 template <typename T>
 hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEvent_t *events) {
     const int nc = a.nchunks, Q = a.Q;
@@ -896,19 +957,7 @@ hipError_t launch_split_forward(const ForwardArgs &a, hipStream_t stream, hipEve
                        dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, (float *)a.cb, a.L,
                        a.G, a.N, nc, Q);
     if ((err = mark()) != hipSuccess) return err;
-    if constexpr (sizeof(T) == 4) {
-        const int nblk = ((a.P + 63) / 64) * ((a.N + 127) / 128);
-        hipLaunchKernelGGL(k3_chunk_state_f32, dim3(nc, a.H * nblk, a.batch), dim3(256),
-                           K3F32Lds::bytes(), stream, (const float *)a.x, (const float *)a.B,
-                           a.acum_hi, a.acum_lo, a.dtT, a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
-    } else {
-        const int ntiles = (a.P / 16) * (a.N / 16);
-        const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
-        const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
-        hipLaunchKernelGGL(k3_chunk_state<T>, dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
-                           stream, (const T *)a.x, (const T *)a.B, a.acum_hi, a.acum_lo, a.dtT,
-                           a.S, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
-    }
+    launch_k3<T, false>(a, a.x, a.B, a.S, segst, stream);
     if ((err = mark()) != hipSuccess) return err;
     const int PN = a.P * a.N;
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),

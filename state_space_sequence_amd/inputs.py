@@ -192,6 +192,20 @@ def make_norm_inputs(rows, dim, io_dtype="bf16", seed=1234):
     return {"y": np.ascontiguousarray(y), "z": np.ascontiguousarray(z), "weight": w}
 
 
+def make_grad_inputs(batch, seqlen, nheads, headdim, dstate, io_dtype="bf16", seed=0):
+    """The gradients a backward call receives: dy ~ N(0, 1) [b, L, H, P]
+    (rounded to bf16 for a bf16 problem) and dfinal ~ N(0, 1) [b, H, P, N]
+    fp32, drawn in that order from PCG64(seed)."""
+    rng = np.random.Generator(np.random.PCG64(seed))
+    dy = rng.standard_normal(size=(batch, seqlen, nheads, headdim), dtype=np.float32)
+    dfin = rng.standard_normal(size=(batch, nheads, headdim, dstate), dtype=np.float32)
+    if io_dtype == "bf16":
+        dy = round_to_bf16(dy)
+    elif io_dtype != "f32":
+        raise ValueError("io_dtype must be 'f32' or 'bf16'")
+    return {"dy": np.ascontiguousarray(dy), "dfinal": dfin}
+
+
 def make_seq_idx(batch, seqlen, seed=1234, max_len=96):
     """Packed-sequence labels [batch, seqlen] int32: each row is cut into
     sequences of lengths drawn uniformly from 1 .. max_len, labelled 0, 1, 2,

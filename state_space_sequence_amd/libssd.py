@@ -9,6 +9,7 @@ Python names mirror the C entry points:
     ssd_chunk_scan_fwd(x, dt, A, B, C, ...)      -> (y, final_state)
     ssd_chunk_scan_fwd_timed(events, x, ...)     -> (y, final_state, kernel names)
     ssd_state_update(state, x, dt, A, B, C, ...) -> y   (state updated in place)
+    ssd_chunk_scan_bwd(x, ..., dy, dfinal_state)  -> dict of gradients
 """
 from __future__ import annotations
 
@@ -45,6 +46,8 @@ _p = ctypes.c_void_p
 _sz = ctypes.c_size_t
 
 _FWD_ARGS = [_p, _p, _p, _p, _p, _p, _p, _i, _i, _i, _i, _i, _i, _i, _i, _p, _p, _p, _sz, _p]
+# x dt A B C D init dy dfinal, chunk_len ngroups b L H P N io, dx ddt dA dB dC dD dinit, ws bytes stream
+_BWD_ARGS = [_p] * 9 + [_i] * 8 + [_p] * 7 + [_p, _sz, _p]
 
 
 class DtProc(ctypes.Structure):
@@ -86,6 +89,14 @@ def load():
             ctypes.POINTER(_p), _i, ctypes.POINTER(_i), ctypes.POINTER(ctypes.c_char_p)]
         lib.ssd_state_update.restype = _i
         lib.ssd_state_update.argtypes = [_p] * 7 + [_i] * 6 + [_p, _p]
+        lib.ssd_chunk_scan_bwd_workspace_size.restype = _i
+        lib.ssd_chunk_scan_bwd_workspace_size.argtypes = [_i] * 8 + [ctypes.POINTER(_sz)]
+        lib.ssd_chunk_scan_bwd.restype = _i
+        lib.ssd_chunk_scan_bwd.argtypes = _BWD_ARGS
+        lib.ssd_chunk_scan_bwd_max_kernels.restype = _i
+        lib.ssd_chunk_scan_bwd_max_kernels.argtypes = []
+        lib.ssd_chunk_scan_bwd_timed.restype = _i
+        lib.ssd_chunk_scan_bwd_timed.argtypes = _BWD_ARGS + [_p, _i, ctypes.POINTER(_i), _p]
         lib.ssd_chunk_scan_fwd_noalloc.restype = _i
         lib.ssd_chunk_scan_fwd_noalloc.argtypes = _FWD_ARGS[:17] + [_p]
         lib.ssd_chunk_scan_fwd_ex.restype = _i
@@ -311,6 +322,100 @@ def ssd_chunk_scan_fwd_timed(events, x, dt, A, B, C, D=None, initial_state=None,
     (y, final_state, kernel_names)."""
     return _forward(list(events), x, dt, A, B, C, D, initial_state, chunk_len, ngroups,
                     y, final_state, workspace, return_final_state, stream)
+
+
+def ssd_chunk_scan_bwd_workspace_size(batch, seqlen, nheads, headdim, dstate, ngroups,
+                                      chunk_len, io_dtype) -> int:
+    out = _sz(0)
+    st = load().ssd_chunk_scan_bwd_workspace_size(batch, seqlen, nheads, headdim, dstate,
+                                                  ngroups, chunk_len, io_dtype,
+                                                  ctypes.byref(out))
+    if st != SSD_OK:
+        raise SsdError(st, "ssd_chunk_scan_bwd_workspace_size")
+    return out.value
+
+
+def bwd_max_kernels() -> int:
+    return load().ssd_chunk_scan_bwd_max_kernels()
+
+
+def ssd_chunk_scan_bwd(x, dt, A, B, C, D, initial_state, dy, dfinal_state=None,
+                       chunk_len=256, ngroups=None, want_dD=True, want_dinit=True,
+                       out=None, workspace=None, stream=None, events=None):
+    """Gradients of the chunked forward (ssd_chunk_scan_bwd).
+
+    The forward's inputs as for ssd_chunk_scan_fwd (processed dt, no gate or
+    packed sequences), dy (x's shape and dtype) and dfinal_state ([b,H,P,N]
+    fp32 or None = 0).  Returns a dict dx, ddt, dA, dB, dC, dD, dinit (the
+    last two None unless wanted), allocated with torch unless ``out`` (a
+    dict of the same keys) supplies them.  With ``events`` (at least
+    bwd_max_kernels()+1 hipEvent_t handles) the timed twin runs and the dict
+    also holds ``kernel_names``."""
+    import torch
+    lib = load()
+    dev = x.device
+    if dev.type != "cuda":
+        raise ValueError("x must be a GPU tensor")
+    io = _dtype_code(x)
+    _check_dev("x", x, None, dev)
+    for n, t in (("B", B), ("C", C), ("dy", dy)):
+        _check_dev(n, t, x.dtype, dev)
+    for n, t in (("dt", dt), ("A", A), ("D", D), ("initial_state", initial_state),
+                 ("dfinal_state", dfinal_state)):
+        _check_dev(n, t, torch.float32, dev)
+    if x.dim() != 4 or B.dim() != 4:
+        raise ValueError("x must be [b,L,H,P] and B/C [b,L,G,N]")
+    b, L, H, P = x.shape
+    G, N = B.shape[2], B.shape[3]
+    if ngroups is not None and ngroups != G:
+        raise ValueError("ngroups=%d but B has %d groups" % (ngroups, G))
+    if tuple(dt.shape) != (b, L, H) or tuple(A.shape) != (H,) or \
+            tuple(B.shape) != (b, L, G, N) or tuple(C.shape) != (b, L, G, N) or \
+            tuple(dy.shape) != tuple(x.shape):
+        raise ValueError("inconsistent shapes")
+    if D is not None and tuple(D.shape) != (H,):
+        raise ValueError("D must be [H]")
+    for n, t in (("initial_state", initial_state), ("dfinal_state", dfinal_state)):
+        if t is not None and tuple(t.shape) != (b, H, P, N):
+            raise ValueError("%s must be [b,H,P,N]" % n)
+    o = dict(out or {})
+    f32 = torch.float32
+    shapes = {"dx": (tuple(x.shape), x.dtype), "ddt": ((b, L, H), f32), "dA": ((H,), f32),
+              "dB": ((b, L, G, N), x.dtype), "dC": ((b, L, G, N), x.dtype),
+              "dD": ((H,), f32), "dinit": ((b, H, P, N), f32)}
+    for k, (shape, dtype) in shapes.items():
+        if k == "dD" and not want_dD or k == "dinit" and not want_dinit:
+            o.setdefault(k, None)
+            continue
+        if o.get(k) is None:
+            o[k] = torch.empty(shape, dtype=dtype, device=dev)
+        _check_dev(k, o[k], dtype, dev)
+        if tuple(o[k].shape) != shape:
+            raise ValueError("%s must be %s" % (k, shape))
+    need = ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, chunk_len, io)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    _check_dev("workspace", workspace, torch.uint8, dev)
+    args = (_ptr(x), _ptr(dt), _ptr(A), _ptr(B), _ptr(C), _ptr(D), _ptr(initial_state),
+            _ptr(dy), _ptr(dfinal_state), int(chunk_len), G, b, L, H, P, N, io,
+            _ptr(o["dx"]), _ptr(o["ddt"]), _ptr(o["dA"]), _ptr(o["dB"]), _ptr(o["dC"]),
+            _ptr(o["dD"]), _ptr(o["dinit"]), _ptr(workspace), _sz(workspace.numel()),
+            _stream_handle(stream))
+    if events is None:
+        st = lib.ssd_chunk_scan_bwd(*args)
+        where = "ssd_chunk_scan_bwd"
+    else:
+        ev = list(events)
+        arr = (ctypes.c_void_p * len(ev))(*[ctypes.c_void_p(e) for e in ev])
+        nk = _i(0)
+        names = (ctypes.c_char_p * bwd_max_kernels())()
+        st = lib.ssd_chunk_scan_bwd_timed(*args, arr, len(ev), ctypes.byref(nk), names)
+        where = "ssd_chunk_scan_bwd_timed"
+        if st == SSD_OK:
+            o["kernel_names"] = [names[i].decode() for i in range(nk.value)]
+    if st != SSD_OK:
+        raise SsdError(st, where)
+    return o
 
 
 NOALLOC_SCRATCH_BYTES = 64 << 20   # SSD_NOALLOC_SCRATCH_BYTES of include/ssd.h
