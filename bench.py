@@ -384,6 +384,64 @@ def time_forward_gated(w, dev, ev, steps=100, warmup=20):
     return ms
 
 
+def alg_flops_backward(w):
+    """Dense-product FLOPs of one gradient pass as the kernels form it, per
+    (batch, chunk, head): the adjoint chunk product G_c and the recomputed
+    chunk state (2 QPN each), u's state and causal parts (2 QNP + Q(Q+1)P),
+    and dB's and dC's state parts, causal scores and causal products (2 QPN +
+    Q(Q+1)P + Q(Q+1)N each); plus the recomputed C B^T, Q(Q+1)N per (batch,
+    chunk, group).  Causal blocks count their lower triangle."""
+    Q, P, N = w.chunk_len, w.headdim, w.dstate
+    nc = -(-w.seqlen // Q)
+    per_head = 10 * Q * P * N + 3 * Q * (Q + 1) * P + 2 * Q * (Q + 1) * N
+    return w.batch * nc * (w.nheads * per_head + w.ngroups * Q * (Q + 1) * N)
+
+
+def time_backward(w, dev, ev, steps=10, warmup=2):
+    """ms per gradient pass (ssd_chunk_scan_bwd) on this workload with seeded
+    dy and dfinal, its kernels' times (per-kernel events, separate calls),
+    and its dense-product rate against the MFMA peak of its operand type."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import make_grad_inputs
+    inp, t, y, fin, ws = setup(w, dev)
+    del y, fin, ws
+    g = make_grad_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.io_dtype,
+                         seed=w.seed + 1)
+    tdt = torch.bfloat16 if w.io_dtype == "bf16" else torch.float32
+    dy = torch.from_numpy(g["dy"]).to(tdt).to(dev)
+    dfin = torch.from_numpy(g["dfinal"]).to(dev)
+    args = (t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"], t["initial_state"], dy, dfin)
+    io = libssd.SSD_BF16 if w.io_dtype == "bf16" else libssd.SSD_F32
+    wsb = torch.empty(libssd.ssd_chunk_scan_bwd_workspace_size(
+        w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.ngroups, w.chunk_len, io),
+        dtype=torch.uint8, device=dev)
+    out = libssd.ssd_chunk_scan_bwd(*args, chunk_len=w.chunk_len, workspace=wsb)
+    ms = time_plain(lambda: libssd.ssd_chunk_scan_bwd(*args, chunk_len=w.chunk_len, out=out,
+                                                      workspace=wsb), ev, steps, warmup)
+    evs = [ev.create() for _ in range(libssd.bwd_max_kernels() + 1)]
+    per = {}
+    for _ in range(max(1, steps // 2)):
+        o = libssd.ssd_chunk_scan_bwd(*args, chunk_len=w.chunk_len, out=out, workspace=wsb,
+                                      events=evs)
+        torch.cuda.synchronize()
+        for i, n in enumerate(o["kernel_names"]):
+            per.setdefault(n, []).append(ev.ms(evs[i], evs[i + 1]))
+    for e in evs:
+        ev.destroy(e)
+    flops = alg_flops_backward(w)
+    peak = BF16_PEAK_TFLOPS if w.io_dtype == "bf16" else FP32_PEAK_TFLOPS
+    tf = flops / (ms * 1e-3) / 1e12
+    del t, dy, dfin, wsb, out
+    return {"what": "gradients of (y, final_state) with respect to every input "
+                    "(ssd_chunk_scan_bwd, recomputing the forward's chunk states)",
+            "ms_per_step": round(ms, 4),
+            "tokens_per_s": round(w.batch * w.seqlen / (ms * 1e-3), 1),
+            "alg_flops": flops, "tflops": round(tf, 2),
+            "frac_mfma": round(tf / peak, 4),
+            "per_kernel_ms": {k: round(sum(v) / len(v), 4) for k, v in per.items()}}
+
+
 def time_conv(w, dev, ev, steps=50, warmup=10, decode_batch=256):
     """The causal depthwise conv that precedes the scan, on this layer's
     x | B | C channels (dim = H P + 2 G N, width 4, SiLU, bias): the
@@ -791,6 +849,10 @@ def main():
             w, dev, ev, steps=max(1, xs // 2), warmup=min(10, xs))
         extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev, steps=max(1, xs // 2),
                                                      warmup=min(10, xs))
+        for name in ("mamba2_130m", "mamba2_130m_f32", w.name):
+            extra["backward_" + name] = time_backward(WORKLOADS[name], dev, ev,
+                                                      steps=max(2, min(10, xs // 10)),
+                                                      warmup=min(2, xs))
 
     # the headline: exactly `steps` timed graph replays of one forward each
     # (exactly `warmup` untimed calls: the other workloads and the measured

@@ -396,7 +396,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
 
 struct BwdLayout {
     Layout f;   // the split forward's regions, recomputed
-    size_t adj, qpart, roff, dint, dd, rect, colsum, dDpart, dApart, total;
+    size_t adj, qpart, roff, dint, dd, rect, colsum, dDpart, dApart, partB, partC, total;
 };
 
 BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -428,6 +428,13 @@ BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int ds
     off += round_up(b * nc * H * nrb * sizeof(float));
     l.dApart = off;
     off += round_up(b * nc * H * sizeof(double));
+    // per head group partial dB and dC, when the groups' heads are split
+    const int nhg = ssd::bwd_head_groups(batch, (int)nc, (int)nrb, ngroups, nheads / ngroups);
+    const size_t part = nhg > 1 ? round_up((size_t)nhg * b * seqlen * ngroups * N * sizeof(float)) : 0;
+    l.partB = off;
+    off += part;
+    l.partC = off;
+    off += part;
     l.total = off;
     return l;
 }
@@ -498,6 +505,8 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     a.dd = reinterpret_cast<float *>(ws + lay.dd);
     a.rect = reinterpret_cast<float *>(ws + lay.rect);
     a.colsum = reinterpret_cast<float *>(ws + lay.colsum);
+    a.partB = reinterpret_cast<float *>(ws + lay.partB);
+    a.partC = reinterpret_cast<float *>(ws + lay.partC);
     a.dDpart = reinterpret_cast<float *>(ws + lay.dDpart);
     a.dApart = reinterpret_cast<double *>(ws + lay.dApart);
 

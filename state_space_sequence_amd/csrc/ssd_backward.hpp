@@ -32,6 +32,7 @@ struct BackwardArgs {
     float *colsum;  // [b][H][nc][nrb][Q]: column sums of W over each row block
     float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
     double *dApart; // [b][nc][H]: partial sums of dt * dLoss/d(dt A)
+    float *partB, *partC; // [nhg][b][L][G][N]: per head group dB / dC (nhg > 1)
 };
 
 // Slices of a state (4 elements per thread, 256 threads) in the reverse
@@ -39,6 +40,21 @@ struct BackwardArgs {
 inline int bwd_state_slices(int P, int N) { return (P * N + 1023) / 1024; }
 // Row blocks of a chunk in the gradient kernels (64 rows, or the chunk).
 inline int bwd_row_blocks(int Q) { return Q > 64 ? Q / 64 : 1; }
+
+// Heads per workgroup of the dB and dC kernels, which sum over a group's
+// heads: enough head groups for about 8192 workgroups (then each group's
+// fp32 partial sum is added up by a separate pass).
+inline int bwd_heads_per_group(int batch, int nc, int nrb, int G, int hpg) {
+    const long wg = (long)batch * nc * nrb * G;
+    long ng = (8192 + wg - 1) / wg;
+    if (ng > hpg) ng = hpg;
+    if (ng < 1) ng = 1;
+    return (int)((hpg + ng - 1) / ng);
+}
+inline int bwd_head_groups(int batch, int nc, int nrb, int G, int hpg) {
+    const int hpw = bwd_heads_per_group(batch, nc, nrb, G, hpg);
+    return (hpg + hpw - 1) / hpw;
+}
 
 constexpr int kBackwardKernels = 8;
 extern const char *const kBackwardKernelNames[kBackwardKernels];

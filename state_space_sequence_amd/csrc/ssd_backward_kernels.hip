@@ -141,9 +141,11 @@ struct KbLds {
     // + prefix sums and dt by token, a reduction slot per wave, and for the
     // dC pass the diagonal block of W, its rows' sums over the earlier
     // blocks and the column sums of each earlier block (fp32)
+    // + a K-slab of the state, transposed: [WP][KS + 16 / sz]
+    static __host__ __device__ constexpr int spitch(int sz) { return (sz == 4 ? 16 : 32) + 16 / sz; }
     static size_t bytes(int WP, int sz) {
-        return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz)) * sz + 3 * 256 * 4 + 64 +
-               ((size_t)kSB * (kSB + 1) + kSB + 4 * kSB) * 4;
+        return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz) + (size_t)WP * spitch(sz)) * sz +
+               3 * 256 * 4 + 64 + ((size_t)kSB * (kSB + 1) + kSB + 4 * kSB) * 4;
     }
 };
 
@@ -155,8 +157,8 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
        const float *__restrict__ acum_lo, const float *__restrict__ dtT,
        const float *__restrict__ D, T *__restrict__ out, float *__restrict__ roff,
        float *__restrict__ dint, float *__restrict__ dd, float *__restrict__ rect,
-       float *__restrict__ colsum, float *__restrict__ dDpart, int L, int H, int G, int P,
-       int N, int nc, int Q) {
+       float *__restrict__ colsum, float *__restrict__ dDpart, float *__restrict__ part,
+       int L, int H, int G, int P, int N, int nc, int Q, int hpw) {
     typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SZ = (int)sizeof(T);
@@ -168,7 +170,9 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *VS = reinterpret_cast<T *>(smem_raw);                 // V of the source block
     T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: Wt, this row block
-    float *r_hi = reinterpret_cast<float *>(MT + (size_t)SBX * PITCH);
+    constexpr int SP = KbLds::spitch(SZ);
+    T *SS = MT + (size_t)SBX * PITCH;                         // [WP][SP]: a K-slab of the state
+    float *r_hi = reinterpret_cast<float *>(SS + (size_t)WP * SP);
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
     float *red = r_dt + 256;                                  // [16]
@@ -201,9 +205,11 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     const int W = MODE == kDx ? P : N;       // output width
     const int KD = MODE == kDx ? N : P;      // K of the state product
     const int hpg = H / G;
-    const int g = MODE == kDx ? blockIdx.y / hpg : blockIdx.y;
-    const int h_first = MODE == kDx ? blockIdx.y : g * hpg;
-    const int h_count = MODE == kDx ? 1 : hpg;
+    // kDb / kDc: workgroup y = g * nhg + k takes heads k hpw .. of group g
+    const int nhg = MODE == kDx ? 1 : (int)gridDim.y / G, hgi = MODE == kDx ? 0 : blockIdx.y % nhg;
+    const int g = MODE == kDx ? blockIdx.y / hpg : blockIdx.y / nhg;
+    const int h_first = MODE == kDx ? blockIdx.y : g * hpg + hgi * hpw;
+    const int h_count = MODE == kDx ? 1 : min(hpw, hpg - hgi * hpw);
     const int t0 = c * Q + lb * SB;          // the row block's first token
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
 
@@ -223,34 +229,61 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         __syncthreads();
         const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
 
-        // ---- the state product U_t St, scaled per row
+        // ---- the state product U_t St, scaled per row.  kDx's fragments are
+        // VEC consecutive dstate entries of a Lam row, read straight from
+        // memory; kDb and kDc take K along the headdim, across the state's
+        // rows, so the state passes through LDS in K-slabs, transposed.
         f32x4 acc[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[i] = zero4();
         const float *st = MODE == kDc ? S + ((size_t)(b * nc + c) * H + h) * P * N
                                       : adj + ((size_t)(b * nc + c) * H + h) * P * N;
-        if (active) {
-            const int tr = t0 + wave * 16 + r;   // this lane's U row
-            const T *urow = MODE == kDx ? Bm + (((size_t)b * L + tr) * G + g) * N
-                          : MODE == kDb ? x + (((size_t)b * L + tr) * H + h) * P
-                                        : dy + (((size_t)b * L + tr) * H + h) * P;
-            for (int k0 = 0; k0 < KD; k0 += KS) {
-                const int k = k0 + VEC * q;
-                const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
+        const int tr = t0 + wave * 16 + r;   // this lane's U row
+        const T *urow = MODE == kDx ? Bm + (((size_t)b * L + tr) * G + g) * N
+                      : MODE == kDb ? x + (((size_t)b * L + tr) * H + h) * P
+                                    : dy + (((size_t)b * L + tr) * H + h) * P;
+        for (int k0 = 0; k0 < KD; k0 += KS) {
+            const int k = k0 + VEC * q;
+            if constexpr (MODE != kDx) {
+                __syncthreads();   // (the previous slab is no longer read)
+                const int wq = W / 4;
+                for (int v = tid; v < KS * wq; v += 256) {
+                    const int kr = v / wq, w0 = (v % wq) * 4;
+                    f32x4 f = zero4();
+                    if (k0 + kr < KD) f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
 #pragma unroll
-                for (int wt = 0; wt < NW; ++wt) {
-                    const int w = wt * 16 + r;
-                    frag sb;
-#pragma unroll
-                    for (int j = 0; j < VEC; ++j) {
-                        float v = 0.f;
-                        if (w < W && k + j < KD)
-                            v = MODE == kDx ? st[(size_t)w * N + k + j] : st[(size_t)(k + j) * N + w];
-                        sb[j] = from_f32<T>(v);
-                    }
-                    acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
+                    for (int jj = 0; jj < 4; ++jj) SS[(w0 + jj) * SP + kr] = from_f32<T>(f[jj]);
                 }
+                __syncthreads();
             }
+            if (!active) continue;
+            const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) {
+                const int w = wt * 16 + r;
+                frag sb = zero_frag<T>();
+                if (w < W && k < KD) {
+                    if constexpr (MODE == kDx) {
+                        const float *sp = st + (size_t)w * N + k;
+                        if constexpr (F32) {
+                            sb = *reinterpret_cast<const f32x4 *>(sp);
+                        } else {
+                            const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
+                            const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj) {
+                                sb[jj] = from_f32<T>(lo[jj]);
+                                sb[4 + jj] = from_f32<T>(hi[jj]);
+                            }
+                        }
+                    } else {
+                        sb = load_frag(SS + w * SP + VEC * q);
+                    }
+                }
+                acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
+            }
+        }
+        if (active) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
                 const int l = lb * SB + wave * 16 + 4 * q + i;
@@ -451,19 +484,25 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             // the block's rows of the rectangle sums: for t in this block,
             // sum_{s >= t in the block} (sum_{s' in earlier blocks} W[s][s']
             // + sum_{t > s' in this block} W[s][s']); four threads per t
+            // (each row of Wd becomes its exclusive prefix sums plus the
+            // row's earlier-block sum, then each column is summed from the
+            // diagonal down: two passes of 64 threads)
             __syncthreads();
-            const int tau = tid >> 2, sub = tid & 3;
-            float v = 0.f;
-            if (tau < SB) {
-                for (int rho = tau + sub; rho < SB; rho += 4) {
-                    float a = s_rrow[rho];
-                    for (int col = 0; col < tau; ++col) a += Wd[rho * (SBX + 1) + col];
-                    v += a;
+            if (tid < SB) {
+                float run = s_rrow[tid];
+                float *row = Wd + tid * (SBX + 1);
+                for (int col = 0; col < SB; ++col) {
+                    const float w = row[col];
+                    row[col] = run;
+                    run += w;
                 }
             }
-            v += __shfl_xor(v, 1, kWave);
-            v += __shfl_xor(v, 2, kWave);
-            if (sub == 0 && tau < SB) rect[vbase + lb * SB + tau] = v;
+            __syncthreads();
+            if (tid < SB) {
+                float v = 0.f;
+                for (int rho = tid; rho < SB; ++rho) v += Wd[rho * (SBX + 1) + tid];
+                rect[vbase + lb * SB + tid] = v;
+            }
         }
         if constexpr (MODE == kDx) {
             __syncthreads();
@@ -486,11 +525,30 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
 #pragma unroll
                 for (int wt = 0; wt < NW; ++wt) {
                     const int n = wt * 16 + r;
-                    if (n < N) out[(((size_t)b * L + t) * G + g) * N + n] = from_f32<T>(tot[wt][i]);
+                    if (n >= N) continue;
+                    const size_t o = (((size_t)b * L + t) * G + g) * N + n;
+                    // (several head groups: an fp32 partial sum each, added up afterwards)
+                    if (part)
+                        part[(size_t)hgi * gridDim.z * L * G * N + o] = tot[wt][i];
+                    else
+                        out[o] = from_f32<T>(tot[wt][i]);
                 }
             }
         }
     }
+}
+
+// ------------------------------------------------------------ head-group sums
+// out[e] = the sum over k < nhg of part[k n + e], in that order.
+template <typename T>
+__global__ void __launch_bounds__(256)
+kb_sum_heads(const float *__restrict__ part, T *__restrict__ out, size_t n, int nhg) {
+    const size_t e = ((size_t)blockIdx.x * 256 + threadIdx.x) * 4;
+    if (e >= n) return;   // (n is a multiple of 16)
+    f32x4 acc = *reinterpret_cast<const f32x4 *>(part + e);
+    for (int k = 1; k < nhg; ++k) acc += *reinterpret_cast<const f32x4 *>(part + (size_t)k * n + e);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) out[e + j] = from_f32<T>(acc[j]);
 }
 
 // ------------------------------------------------------------ ddt and dA
@@ -582,16 +640,25 @@ const char *const kBackwardKernelNames[kBackwardKernels] = {
     "kb_dC", "kb_ddt", "kb_reduce"};
 
 template <typename T, int MODE, int NW>
-static void launch_mix(const BackwardArgs &a, void *out, hipStream_t stream) {
+static void launch_mix(const BackwardArgs &a, void *out, float *part, hipStream_t stream) {
     const ForwardArgs &f = a.f;
     const int nrb = bwd_row_blocks(f.Q);
+    const int hpg = f.H / f.G;
+    const int hpw = MODE == kDx ? 1 : bwd_heads_per_group(f.batch, f.nchunks, nrb, f.G, hpg);
+    const int ny = MODE == kDx ? f.H : f.G * ((hpg + hpw - 1) / hpw);
     const size_t lds = KbLds::bytes(16 * NW, (int)sizeof(T));
-    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, MODE == kDx ? f.H : f.G, f.batch),
+    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, ny, f.batch),
                        dim3(256), lds, stream, (const T *)f.x, (const T *)f.B, (const T *)f.C,
                        (const T *)a.dy, (const float *)f.cb, (const float *)f.S, (const float *)a.adj,
                        (const float *)f.acum_hi, (const float *)f.acum_lo, (const float *)f.dtT,
-                       f.D, (T *)out, a.roff, a.dint, a.dd, a.rect, a.colsum, a.dDpart, f.L, f.H, f.G,
-                       f.P, f.N, f.nchunks, f.Q);
+                       f.D, (T *)out, a.roff, a.dint, a.dd, a.rect, a.colsum, a.dDpart,
+                       (MODE != kDx && ny > f.G) ? part : nullptr, f.L, f.H, f.G, f.P, f.N,
+                       f.nchunks, f.Q, hpw);
+    if (MODE != kDx && ny > f.G) {
+        const size_t n = (size_t)f.batch * f.L * f.G * f.N;
+        hipLaunchKernelGGL(kb_sum_heads<T>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                           stream, (const float *)part, (T *)out, n, ny / f.G);
+    }
 }
 
 template <typename T>
@@ -613,19 +680,19 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
                        a.dfinal, a.dinit, a.qpart, f.H, PN, f.nchunks, f.Q, nsl);
     if ((err = mark()) != hipSuccess) return err;
     if (f.P <= 64)
-        launch_mix<T, kDx, 4>(a, a.dx, stream);
+        launch_mix<T, kDx, 4>(a, a.dx, nullptr, stream);
     else
-        launch_mix<T, kDx, 8>(a, a.dx, stream);
+        launch_mix<T, kDx, 8>(a, a.dx, nullptr, stream);
     if ((err = mark()) != hipSuccess) return err;
     if (f.N <= 128)
-        launch_mix<T, kDb, 8>(a, a.dB, stream);
+        launch_mix<T, kDb, 8>(a, a.dB, a.partB, stream);
     else
-        launch_mix<T, kDb, 16>(a, a.dB, stream);
+        launch_mix<T, kDb, 16>(a, a.dB, a.partB, stream);
     if ((err = mark()) != hipSuccess) return err;
     if (f.N <= 128)
-        launch_mix<T, kDc, 8>(a, a.dC, stream);
+        launch_mix<T, kDc, 8>(a, a.dC, a.partC, stream);
     else
-        launch_mix<T, kDc, 16>(a, a.dC, stream);
+        launch_mix<T, kDc, 16>(a, a.dC, a.partC, stream);
     if ((err = mark()) != hipSuccess) return err;
     hipLaunchKernelGGL(kb_ddt, dim3(f.nchunks, f.H, f.batch), dim3(256), 0, stream,
                        (const float *)a.roff, (const float *)a.dint, (const float *)a.dd,

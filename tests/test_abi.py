@@ -317,3 +317,64 @@ def test_fused_segments_only_for_few_column_groups(lib, monkeypatch):
     monkeypatch.setenv("SSD_FUSED_SEGMENTS", "3")
     st, n = ws_size(lib, 2, 1000, 64, 64, 128, 8, 256, 1)
     assert st == 0 and n // state == 2
+
+
+# ---------------------------------------------------------------- gradients
+
+def bwd(lib, **kw):
+    a = dict(x=FAKE, dt=FAKE, A=FAKE, B=FAKE, C=FAKE, D=None, init=None, dy=FAKE, dfin=None,
+             Q=64, G=1, b=1, L=100, H=2, P=16, N=16, io=0, dx=FAKE, ddt=FAKE, dA=FAKE,
+             dB=FAKE, dC=FAKE, dD=None, dinit=None, ws=FAKE, wsb=1 << 40, stream=None)
+    a.update(kw)
+    return lib.ssd_chunk_scan_bwd(a["x"], a["dt"], a["A"], a["B"], a["C"], a["D"], a["init"],
+                                  a["dy"], a["dfin"], a["Q"], a["G"], a["b"], a["L"], a["H"],
+                                  a["P"], a["N"], a["io"], a["dx"], a["ddt"], a["dA"], a["dB"],
+                                  a["dC"], a["dD"], a["dinit"], a["ws"], a["wsb"], a["stream"])
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(G=3, H=4), 1),
+    (dict(L=0), 1),
+    (dict(io=7), 1),
+    (dict(dy=None), 1),
+    (dict(dx=None), 1),
+    (dict(ddt=None), 1),
+    (dict(dA=None), 1),
+    (dict(dB=None), 1),
+    (dict(dC=None), 1),
+    (dict(dy=FAKE + 2), 1),
+    (dict(dfin=FAKE + 4), 1),
+    (dict(dinit=FAKE + 8), 1),
+    (dict(dD=FAKE + 2), 1),
+    (dict(Q=48), 2),
+    (dict(P=24), 2),
+    (dict(N=512), 2),
+    (dict(wsb=16), 3),
+    (dict(ws=None), 3),
+    (dict(ws=FAKE + 16), 3),
+])
+def test_backward_validation(lib, kw, code):
+    assert bwd(lib, **kw) == code
+
+
+def test_backward_workspace_size(lib):
+    """The recomputed forward's regions plus the gradient pass's: the
+    adjoint chunk products (a state per chunk), fp64 chunk-end products per
+    state slice, four per-token vectors per head and the row-block column
+    sums (one per 64-row block), the dD / dA partial sums, and the head
+    groups' partial dB and dC."""
+    b, L, H, P, N, G, Q = 4, 8192, 80, 64, 128, 1, 256
+    nc, nsl, nrb = L // Q, (P * N + 1023) // 1024, Q // 64
+    out = ctypes.c_size_t(0)
+    assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, Q, 1, ctypes.byref(out)) == 0
+    fwd_split = 3 * b * H * nc * Q * 4 + b * nc * G * Q * Q * 4 + b * nc * H * P * N * 4 + b * nc * Q * 4
+    # the dB / dC kernels split a group's 80 heads so that there are about
+    # 8192 workgroups: 512 (batch x chunks x row blocks) -> 16 groups of 5,
+    # each with an fp32 partial dB and dC
+    nhg = 16
+    extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 4 * b * H * nc * Q * 4 +
+             b * H * nc * nrb * Q * 4 + b * nc * H * nrb * 4 + b * nc * H * 8 +
+             2 * nhg * b * L * G * N * 4)
+    assert out.value >= fwd_split + extra and out.value - (fwd_split + extra) < 16 * 256
+    assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, 3, Q, 1, ctypes.byref(out)) == 1
+    assert lib.ssd_chunk_scan_bwd_max_kernels() == 8
