@@ -396,7 +396,7 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
 
 struct BwdLayout {
     Layout f;   // the split forward's regions, recomputed
-    size_t adj, qpart, roff, dint, dd, rect, colsum, dDpart, dApart, partB, partC, total;
+    size_t adj, qpart, roff, dint, dd, wsm, rowp, colp, dDpart, dApart, partB, partC, total;
 };
 
 BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -420,10 +420,12 @@ BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int ds
     off += tok;
     l.dd = off;
     off += tok;
-    l.rect = off;
-    off += tok;
-    l.colsum = off;
-    off += round_up(b * H * nc * nrb * Q * sizeof(float));
+    l.wsm = off;
+    off += round_up(b * nc * ngroups * Q * Q * (io == SSD_BF16 ? 2 : 4));
+    l.rowp = off;
+    off += round_up(b * H * nc * nrb * Q * sizeof(double));
+    l.colp = off;
+    off += round_up(b * H * nc * nrb * 4 * Q * sizeof(double));
     l.dDpart = off;
     off += round_up(b * nc * H * nrb * sizeof(float));
     l.dApart = off;
@@ -503,8 +505,9 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     a.roff = reinterpret_cast<float *>(ws + lay.roff);
     a.dint = reinterpret_cast<float *>(ws + lay.dint);
     a.dd = reinterpret_cast<float *>(ws + lay.dd);
-    a.rect = reinterpret_cast<float *>(ws + lay.rect);
-    a.colsum = reinterpret_cast<float *>(ws + lay.colsum);
+    a.wsm = ws + lay.wsm;
+    a.rowp = reinterpret_cast<double *>(ws + lay.rowp);
+    a.colp = reinterpret_cast<double *>(ws + lay.colp);
     a.partB = reinterpret_cast<float *>(ws + lay.partB);
     a.partC = reinterpret_cast<float *>(ws + lay.partC);
     a.dDpart = reinterpret_cast<float *>(ws + lay.dDpart);

@@ -28,8 +28,9 @@ struct BackwardArgs {
     float *roff;    // [b][H][nc][Q]: <dy_t, e^(acum_t) h_in C_t> per head
     float *dint;    // [b][H][nc][Q]: x_t . (e^(acum_end - acum_t) Lam B_t)
     float *dd;      // [b][H][nc][Q]: x_t . u_t (the direct part of ddt)
-    float *rect;    // [b][H][nc][Q]: the in-block part of the rectangle sums of W
-    float *colsum;  // [b][H][nc][nrb][Q]: column sums of W over each row block
+    void *wsm;      // [b][nc][G][Q][Q] io type: the group's summed score tiles Ws
+    double *rowp;   // [b][H][nc][nrb][Q]: strict row sums of W per (row block's) tile
+    double *colp;   // [b][H][nc][nrb][4][Q]: strict column sums of W per tile and wave
     float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
     double *dApart; // [b][nc][H]: partial sums of dt * dLoss/d(dt A)
     float *partB, *partC; // [nhg][b][L][G][N]: per head group dB / dC (nhg > 1)
@@ -56,7 +57,7 @@ inline int bwd_head_groups(int batch, int nc, int nrb, int G, int hpg) {
     return (hpg + hpw - 1) / hpw;
 }
 
-constexpr int kBackwardKernels = 8;
+constexpr int kBackwardKernels = 9;
 extern const char *const kBackwardKernelNames[kBackwardKernels];
 
 // The first four kernels of the split forward (k1 .. k4), and k3 in its

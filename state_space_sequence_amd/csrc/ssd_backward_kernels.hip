@@ -54,6 +54,12 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
+__device__ __forceinline__ double row16_sum_f64(double v) {
+#pragma unroll
+    for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
+    return v;
+}
+
 // Sum over the 16 lanes of each 16-lane group (the lanes of one MFMA row).
 __device__ __forceinline__ float row16_sum(float v) {
 #pragma unroll
@@ -103,30 +109,155 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
     if (in && dinit) *reinterpret_cast<f32x4 *>(dinit + soff) = lam;
 }
 
+// ------------------------------------------------------------ summed score tiles
+// The dB and dC products share one matrix per (batch, chunk, group):
+//   Ws[l][s] = sum_h e^(acum_l - acum_s) dt_s (dy_l . x_s)     (s <= l)
+// dC_l gets sum_s Ws[l][s] B_s and dB_s gets sum_l Ws[l][s] C_l, so the
+// products with B and C run once per group instead of once per head.  The
+// dt A gradient needs, per head, the rectangle sums of W = Ws's head term
+// times (C_l . B_s); they are the prefix over k < t of (column sum -
+// row sum) of W's strict lower triangle (the entries with s < t, less
+// those with l < t), so this kernel also writes each head's strict row sums
+// (per tile) and column sums (per tile and wave), summed in fp64 from the
+// fp32 entries (the prefix subtracts sums much larger than the result).
+//
+// grid (tiles = nrb (nrb + 1) / 2, nc * G, b), 256 threads, no LDS.
+// Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile of rows l in block lb,
+// columns s in block sb; wave w its rows 16 w ..; it loops over the group's
+// heads with the tile's sum in registers and writes Ws in the operand type.
+template <typename T>
+__global__ void __launch_bounds__(256)
+kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restrict__ cb,
+        const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+        const float *__restrict__ dtT, T *__restrict__ ws, double *__restrict__ rowp,
+        double *__restrict__ colp, int L, int H, int G, int P, int nc, int Q) {
+    typedef typename Mma<T>::frag frag;
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    int pair = blockIdx.x, lb = 0;
+    while ((lb + 1) * (lb + 2) / 2 <= pair) ++lb;
+    const int sb = pair - lb * (lb + 1) / 2;
+    const int c = blockIdx.y / G, g = blockIdx.y % G, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int nrb = Q > 64 ? Q / 64 : 1;
+    const int SB = Q < 64 ? Q : 64;
+    const bool active = wave * 16 < SB;
+    const int hpg = H / G;
+    const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
+    // this lane's entries: rows l = lb SB + 16 w + 4 q + i, columns s = sb SB + 16 st + r
+    int lrow[4], scol[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lrow[i] = lb * SB + wave * 16 + 4 * q + i;
+#pragma unroll
+    for (int st = 0; st < 4; ++st) scol[st] = sb * SB + st * 16 + r;
+    // C . B of the entries (the forward's lower triangle), 0 where unused
+    float cbv[4][4];
+#pragma unroll
+    for (int st = 0; st < 4; ++st)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const bool ok = active && st * 16 + r < SB && scol[st] <= lrow[i];
+            cbv[st][i] = ok ? cb[(cbase + lrow[i]) * Q + scol[st]] : 0.f;
+        }
+    f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
+    for (int hh = 0; hh < hpg; ++hh) {
+        const int h = g * hpg + hh;
+        const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
+        double rsum[4] = {0.0, 0.0, 0.0, 0.0}, csum[4] = {0.0, 0.0, 0.0, 0.0};
+        if (active) {
+            // scores dy_l . x_s over the headdim
+            f32x4 z[4] = {zero4(), zero4(), zero4(), zero4()};
+            const int tr = c * Q + lb * SB + wave * 16 + r;
+            const T *arow = dy + (((size_t)b * L + tr) * H + h) * P;
+            for (int k0 = 0; k0 < P; k0 += KS) {
+                const int k = k0 + VEC * q;
+                const frag za = tr < L && k < P ? load_frag(arow + k) : zero_frag<T>();
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const int ts = c * Q + sb * SB + st * 16 + r;
+                    const frag zb = st * 16 + r < SB && ts < L && k < P
+                                        ? load_frag(x + (((size_t)b * L + ts) * H + h) * P + k)
+                                        : zero_frag<T>();
+                    z[st] = Mma<T>::mma(za, zb, z[st]);
+                }
+            }
+            float lhi[4], llo[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                lhi[i] = acum_hi[vbase + lrow[i]];
+                llo[i] = acum_lo[vbase + lrow[i]];
+            }
+#pragma unroll
+            for (int st = 0; st < 4; ++st) {
+                const bool cin = st * 16 + r < SB;
+                const float shi = cin ? acum_hi[vbase + scol[st]] : 0.f;
+                const float slo = cin ? acum_lo[vbase + scol[st]] : 0.f;
+                const float sdt = cin ? dtT[vbase + scol[st]] : 0.f;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) {
+                    float v = 0.f;
+                    if (cin && scol[st] <= lrow[i])
+                        v = z[st][i] * fast_exp(prefix_diff(lhi[i], llo[i], shi, slo)) * sdt;
+                    acc[st][i] += v;
+                    const double w = scol[st] < lrow[i] ? (double)v * cbv[st][i] : 0.0;   // strict
+                    rsum[i] += w;
+                    csum[st] += w;
+                }
+            }
+        }
+        // strict row sums (complete over the tile's columns) and the wave's
+        // column sums over its 16 rows
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const double v = row16_sum_f64(rsum[i]);
+            if (active && r == 0 && lrow[i] - lb * SB < SB)
+                rowp[(((size_t)(b * H + h) * nc + c) * nrb + sb) * Q + lrow[i]] = v;
+        }
+#pragma unroll
+        for (int st = 0; st < 4; ++st) {
+            double v = csum[st];
+            v += __shfl_xor(v, 16, kWave);
+            v += __shfl_xor(v, 32, kWave);
+            if (q == 0 && st * 16 + r < SB)
+                colp[((((size_t)(b * H + h) * nc + c) * nrb + lb) * 4 + wave) * Q + scol[st]] = v;
+        }
+    }
+    if (active) {
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                if (st * 16 + r < SB && lrow[i] - lb * SB < SB)
+                    ws[(cbase + lrow[i]) * Q + scol[st]] = from_f32<T>(acc[st][i]);
+    }
+}
+
 // ------------------------------------------------------------ intra-chunk gradients
 // One kernel, three products (MODE):
-//   kDx: rows t of head h, columns p:  u_t  (then dx_t, d_t, dD partials)
+//   kDx: rows t of head h, columns p:  u_t  (then dx_t, x_t . u_t, dD partials)
 //   kDb: rows t of group g, columns n: dB_t, summed over the group's heads
 //   kDc: rows t of group g, columns n: dC_t, summed over the group's heads
-//        (and r_t per head)
-// Each is   out_t = rowscale_t [ stscale_t U_t St  +  sum_s Wt[t][s] V_s ]:
-//            U (K)        St [K x W]        Wt[t][s]                        V
-//   kDx:   B_t (N)      Lam^T            (C_s . B_t) e^(acum_s - acum_t), s >= t   dy_s
-//   kDb:   x_t (P)      Lam              (x_t . dy_s) e^(acum_s - acum_t), s >= t  C_s
-//   kDc:   dy_t (P)     h_in             (dy_t . x_s) e^(acum_t - acum_s) dt_s,
-//                                                                      s <= t      B_s
+// Each is   out_t = sum_heads rowscale_t stscale_t U_t St  +  sum_s Wt[t][s] V_s:
+//            U (K)        St [K x W]        Wt[t][s]                            V
+//   kDx:   B_t (N)      Lam^T            (C_s . B_t) e^(acum_s - acum_t), s >= t     dy_s
+//   kDb:   x_t (P)      Lam              Ws[s][t], s >= t                            C_s
+//   kDc:   dy_t (P)     h_in             Ws[t][s], s <= t                            B_s
 // with stscale e^(acum_end - acum_t) (kDx, kDb) or e^(acum_t) (kDc), and
 // rowscale dt_t for kDb (kDx applies dt_t in its epilogue).  C_s . B_t comes
-// from the forward's C B^T blocks (its lower triangle, row s >= column t);
-// the (x . dy) scores are MFMA products over the headdim.
+// from the forward's C B^T blocks (its lower triangle, row s >= column t),
+// Ws from kb_wsum.  kDx also writes x_t . (its state part), kDc <dy_t, its
+// state part> per head.
 //
-// grid (nc * nrb, H (kDx) or G, b), 256 threads (4 waves), dynamic LDS
-// KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64) rows of row
-// block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column tiles span
-// the output width W (P or N, padded; padded columns are never stored).
-// Per source block: V staged in LDS (fp32: token rows of a pitch = 16 mod 64
-// floats, read with the K index kk + q + 4 j; bf16: transposed rows), the
-// wave's rows of Wt built in LDS in the operand type, then the MFMAs.
+// grid (nc * nrb, H (kDx) or G * nhg (kDb, kDc), b), 256 threads (4 waves),
+// dynamic LDS KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64)
+// rows of row block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column
+// tiles span the output width W (P or N, padded; padded columns are never
+// stored).  kDb / kDc split a group's heads over nhg workgroups for the
+// state products (fp32 partial sums, added up afterwards); the first of
+// them also takes the intra-chunk product.  Per source block: V staged in
+// LDS (fp32: token rows of a pitch = 16 mod 64 floats, read with the K index
+// kk + q + 4 j; bf16: transposed rows), the rows of Wt in LDS in the operand
+// type, then the MFMAs.
 enum { kDx = 0, kDb = 1, kDc = 2 };
 
 struct KbLds {
@@ -138,27 +269,25 @@ struct KbLds {
         return (size_t)(sz == 4 ? kSB : WP) * vpitch(WP, sz);
     }
     static __host__ __device__ constexpr int mpitch(int sz) { return kSB + 16 / sz; }
-    // + prefix sums and dt by token, a reduction slot per wave, and for the
-    // dC pass the diagonal block of W, its rows' sums over the earlier
-    // blocks and the column sums of each earlier block (fp32)
     // + a K-slab of the state, transposed: [WP][KS + 16 / sz]
     static __host__ __device__ constexpr int spitch(int sz) { return (sz == 4 ? 16 : 32) + 16 / sz; }
+    // + prefix sums and dt by token and a reduction slot per wave (fp32)
     static size_t bytes(int WP, int sz) {
         return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz) + (size_t)WP * spitch(sz)) * sz +
-               3 * 256 * 4 + 64 + ((size_t)kSB * (kSB + 1) + kSB + 4 * kSB) * 4;
+               3 * 256 * 4 + 64;
     }
 };
 
 template <typename T, int MODE, int NW>
 __global__ void __launch_bounds__(256)
 kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
-       const T *__restrict__ dy, const float *__restrict__ cb, const float *__restrict__ S,
-       const float *__restrict__ adj, const float *__restrict__ acum_hi,
-       const float *__restrict__ acum_lo, const float *__restrict__ dtT,
-       const float *__restrict__ D, T *__restrict__ out, float *__restrict__ roff,
-       float *__restrict__ dint, float *__restrict__ dd, float *__restrict__ rect,
-       float *__restrict__ colsum, float *__restrict__ dDpart, float *__restrict__ part,
-       int L, int H, int G, int P, int N, int nc, int Q, int hpw) {
+       const T *__restrict__ dy, const float *__restrict__ cb, const T *__restrict__ wsm,
+       const float *__restrict__ S, const float *__restrict__ adj,
+       const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+       const float *__restrict__ dtT, const float *__restrict__ D, T *__restrict__ out,
+       float *__restrict__ roff, float *__restrict__ dint, float *__restrict__ dd,
+       float *__restrict__ dDpart, float *__restrict__ part, int L, int H, int G, int P,
+       int N, int nc, int Q, int hpw) {
     typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SZ = (int)sizeof(T);
@@ -176,9 +305,6 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
     float *red = r_dt + 256;                                  // [16]
-    float *Wd = red + 16;                                     // [SBX][SBX + 1]
-    float *s_rrow = Wd + SBX * (SBX + 1);                     // [SBX]
-    float *s_col = s_rrow + SBX;                              // [4][SBX]
     // the position of tile column s in an Wt row (fp32: the fragments take
     // the K index kk + q + 4 j, stored at kk + 4 q + j)
     auto mcol = [](int s) -> int {
@@ -220,7 +346,7 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     for (int hh = 0; hh < h_count; ++hh) {
         const int h = h_first + hh;
         const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;   // prefix sums, dt
-        __syncthreads();   // (the previous head's vectors and tiles are no longer read)
+        __syncthreads();   // (the previous head's vectors are no longer read)
         for (int l = tid; l < Q; l += 256) {
             r_hi[l] = acum_hi[vbase + l];
             r_lo[l] = acum_lo[vbase + l];
@@ -311,32 +437,34 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                     if (r == 0 && l < Q) (MODE == kDx ? dint : roff)[vbase + l] = tin ? v : 0.f;
                 }
             }
-        }
-        float rowp[4] = {0.f, 0.f, 0.f, 0.f};   // kDc: this lane's share of W's row sums
-
-        // ---- the intra-chunk product, source block by source block
-        const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
-        for (int sb = sb_lo; sb <= sb_hi; ++sb) {
-            __syncthreads();   // (the previous block's V and Wt are no longer read)
-            // V of the block
-            const int wv = WP / VEC;
-            for (int v = tid; v < SBK * wv; v += 256) {
-                const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
-                frag f = zero_frag<T>();
-                if (sl < SB && ts < L && w0 < W)
-                    f = load_frag(MODE == kDx ? dy + (((size_t)b * L + ts) * H + h) * P + w0
-                                  : MODE == kDb ? Cm + (((size_t)b * L + ts) * G + g) * N + w0
-                                                : Bm + (((size_t)b * L + ts) * G + g) * N + w0);
-                if constexpr (F32) {
-                    *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
-                } else {
+            if constexpr (MODE != kDx) {
+                // the head's state product into the group's sum (dB: times dt_t)
 #pragma unroll
-                    for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
+                for (int i = 0; i < 4; ++i) {
+                    const int l = lb * SB + wave * 16 + 4 * q + i;
+                    const float sc = MODE == kDb ? r_dt[l] : 1.f;
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += sc * acc[wt][i];
                 }
             }
-            // this wave's rows of Wt
-            if (active) {
-                if constexpr (MODE == kDx) {
+        }
+        if constexpr (MODE == kDx) {
+            // ---- the intra-chunk product, source block by source block
+            for (int sb = lb; sb < nrb; ++sb) {
+                __syncthreads();   // (the previous block's V and Wt are no longer read)
+                const int wv = WP / VEC;
+                for (int v = tid; v < SBK * wv; v += 256) {
+                    const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+                    frag f = zero_frag<T>();
+                    if (sl < SB && ts < L && w0 < W) f = load_frag(dy + (((size_t)b * L + ts) * H + h) * P + w0);
+                    if constexpr (F32) {
+                        *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
+                    }
+                }
+                if (active) {
                     // lane: row tl = lane % 16, columns 16 (lane / 16) + j
 #pragma unroll 4
                     for (int j = 0; j < 16; ++j) {
@@ -354,90 +482,26 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                             if (sl < SBK) MT[(wave * 16 + r) * PITCH + mcol(sl)] = from_f32<T>(0.f);
                         }
                     }
-                } else {
-                    // scores (x_t . dy_s) or (dy_t . x_s): 16 rows x 64 columns over the headdim
-                    f32x4 z[4] = {zero4(), zero4(), zero4(), zero4()};
-                    const int tr = t0 + wave * 16 + r;
-                    const T *arow = (MODE == kDb ? x : dy) + (((size_t)b * L + tr) * H + h) * P;
-                    const T *bsrc = MODE == kDb ? dy : x;
-                    for (int k0 = 0; k0 < P; k0 += KS) {
-                        const int k = k0 + VEC * q;
-                        const frag za = tr < L && k < P ? load_frag(arow + k) : zero_frag<T>();
+                }
+                __syncthreads();
+                if (!active) continue;
+                for (int kk = 0; kk < SBK; kk += KS) {
+                    const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
 #pragma unroll
-                        for (int stl = 0; stl < 4; ++stl) {
-                            const int sl = stl * 16 + r, ts = c * Q + sb * SB + sl;
-                            const frag zb = sl < SB && ts < L && k < P
-                                                ? load_frag(bsrc + (((size_t)b * L + ts) * H + h) * P + k)
-                                                : zero_frag<T>();
-                            z[stl] = Mma<T>::mma(za, zb, z[stl]);
-                        }
-                    }
+                    for (int wt = 0; wt < NW; ++wt) {
+                        frag vb;
+                        if constexpr (F32) {
 #pragma unroll
-                    for (int stl = 0; stl < 4; ++stl) {
-                        float colp = 0.f;
-#pragma unroll
-                        for (int i = 0; i < 4; ++i) {
-                            const int tl = wave * 16 + 4 * q + i, sl = stl * 16 + r;
-                            const int lt = lb * SB + tl, ls = sb * SB + sl;
-                            float v = 0.f;
-                            if (sl < SB) {
-                                if (MODE == kDb && ls >= lt)
-                                    v = z[stl][i] * fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
-                                if (MODE == kDc && ls <= lt)
-                                    v = z[stl][i] * fast_exp(prefix_diff(r_hi[lt], r_lo[lt], r_hi[ls], r_lo[ls])) *
-                                        r_dt[ls];
-                            }
-                            if (sl < SBK) MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
-                            if constexpr (MODE == kDc) {
-                                // W = v (C_t . B_s), in fp32, for the dt A gradient
-                                const float w = v != 0.f ? v * cb[(cbase + lt) * Q + ls] : 0.f;
-                                if (sb < lb) {
-                                    rowp[i] += w;
-                                    colp += w;
-                                } else if (sl < SB) {
-                                    Wd[tl * (SBX + 1) + sl] = w;
-                                }
-                            }
+                            for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
+                        } else {
+                            vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
                         }
-                        if constexpr (MODE == kDc) {
-                            if (sb < lb) {
-                                colp += __shfl_xor(colp, 16, kWave);
-                                colp += __shfl_xor(colp, 32, kWave);
-                                if (q == 0) s_col[wave * SBX + stl * 16 + r] = colp;
-                            }
-                        }
+                        acc[wt] = Mma<T>::mma(m, vb, acc[wt]);
                     }
                 }
             }
-            __syncthreads();
-            if constexpr (MODE == kDc) {
-                // the column sums of W over this row block, for the rows of
-                // earlier blocks' dt A gradients (every wave is active here:
-                // a chunk with an earlier block has 64-row blocks)
-                if (sb < lb && tid < SBX)
-                    colsum[(((size_t)(b * H + h) * nc + c) * nrb + lb) * Q + sb * SB + tid] =
-                        s_col[tid] + s_col[SBX + tid] + s_col[2 * SBX + tid] + s_col[3 * SBX + tid];
-            }
-            if (!active) continue;
-            for (int kk = 0; kk < SBK; kk += KS) {
-                const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
-#pragma unroll
-                for (int wt = 0; wt < NW; ++wt) {
-                    frag vb;
-                    if constexpr (F32) {
-#pragma unroll
-                        for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
-                    } else {
-                        vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
-                    }
-                    acc[wt] = Mma<T>::mma(m, vb, acc[wt]);
-                }
-            }
-        }
-
-        // ---- per head
-        if (active) {
-            if constexpr (MODE == kDx) {
+            // ---- the head's epilogue: dx, x . u, dD
+            if (active) {
                 const float Dh = D ? D[h] : 0.f;
                 float dsum = 0.f;
 #pragma unroll
@@ -462,61 +526,77 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                 }
                 dsum = wave_sum(dsum);
                 if (lane == 0) red[wave] = dsum;
-            } else if constexpr (MODE == kDc) {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += acc[wt][i];
-                    const float rs = row16_sum(rowp[i]);
-                    if (r == 0) s_rrow[wave * 16 + 4 * q + i] = rs;
-                }
-            } else {
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int l = lb * SB + wave * 16 + 4 * q + i;
-                    const float dtl = r_dt[l];
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += dtl * acc[wt][i];
-                }
             }
-        }
-        if constexpr (MODE == kDc) {
-            // the block's rows of the rectangle sums: for t in this block,
-            // sum_{s >= t in the block} (sum_{s' in earlier blocks} W[s][s']
-            // + sum_{t > s' in this block} W[s][s']); four threads per t
-            // (each row of Wd becomes its exclusive prefix sums plus the
-            // row's earlier-block sum, then each column is summed from the
-            // diagonal down: two passes of 64 threads)
-            __syncthreads();
-            if (tid < SB) {
-                float run = s_rrow[tid];
-                float *row = Wd + tid * (SBX + 1);
-                for (int col = 0; col < SB; ++col) {
-                    const float w = row[col];
-                    row[col] = run;
-                    run += w;
-                }
-            }
-            __syncthreads();
-            if (tid < SB) {
-                float v = 0.f;
-                for (int rho = tid; rho < SB; ++rho) v += Wd[rho * (SBX + 1) + tid];
-                rect[vbase + lb * SB + tid] = v;
-            }
-        }
-        if constexpr (MODE == kDx) {
             __syncthreads();
             if (tid == 0) {
-                float s = 0.f;
+                float sdd = 0.f;
                 for (int w = 0; w < 4; ++w)
-                    if (w * 16 < SB) s += red[w];
-                dDpart[((size_t)(b * nc + c) * H + h) * nrb + lb] = s;
+                    if (w * 16 < SB) sdd += red[w];
+                dDpart[((size_t)(b * nc + c) * H + h) * nrb + lb] = sdd;
             }
         }
     }
 
-    // ---- dB / dC rows of the row block
     if constexpr (MODE != kDx) {
+        // ---- the intra-chunk product with the group's summed score tiles
+        // (by the first head group only): dC rows lb x Ws[lb][sb] B[sb],
+        // sb <= lb; dB rows lb x Ws[sb][lb]^T C[sb], sb >= lb
+        if (hgi == 0) {
+            const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
+            for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+                __syncthreads();   // (the previous block's V and Wt are no longer read)
+                const int wv = WP / VEC;
+                for (int v = tid; v < SBK * wv; v += 256) {
+                    const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+                    frag f = zero_frag<T>();
+                    if (sl < SB && ts < L && w0 < W)
+                        f = load_frag((MODE == kDb ? Cm : Bm) + (((size_t)b * L + ts) * G + g) * N + w0);
+                    if constexpr (F32) {
+                        *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
+                    } else {
+#pragma unroll
+                        for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
+                    }
+                }
+                if (active) {
+                    // lane: row tl = lane % 16, columns 16 (lane / 16) + j
+#pragma unroll 4
+                    for (int j = 0; j < 16; ++j) {
+                        const int tl = wave * 16 + r, sl = q * 16 + j;
+                        const int lt = lb * SB + tl, ls = sb * SB + sl;
+                        T v = from_f32<T>(0.f);
+                        if (sl < SB) {
+                            if (MODE == kDc && ls <= lt) v = wsm[(cbase + lt) * Q + ls];
+                            if (MODE == kDb && ls >= lt) v = wsm[(cbase + ls) * Q + lt];
+                        }
+                        MT[tl * PITCH + mcol(sl)] = v;
+                    }
+                    if (SBK > SB) {
+                        for (int j = 0; j < 16; ++j) {
+                            const int sl = SB + q * 16 + j;
+                            if (sl < SBK) MT[(wave * 16 + r) * PITCH + mcol(sl)] = from_f32<T>(0.f);
+                        }
+                    }
+                }
+                __syncthreads();
+                if (!active) continue;
+                for (int kk = 0; kk < SBK; kk += KS) {
+                    const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) {
+                        frag vb;
+                        if constexpr (F32) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
+                        } else {
+                            vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
+                        }
+                        tot[wt] = Mma<T>::mma(m, vb, tot[wt]);
+                    }
+                }
+            }
+        }
+        // ---- dB / dC rows of the row block
         if (active) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
@@ -566,19 +646,23 @@ __device__ __forceinline__ double block_scan_f64(double v, double *tot) {
 
 // grid (nc, H, b), 256 threads, token t = tid of the chunk: g_t (the
 // gradient with respect to dt_t A) from its four parts, ddt_t, and the
-// chunk's share of dA, in fp64.
+// chunk's share of dA, in fp64.  The rectangle sum is the exclusive prefix
+// of (strict column sum - strict row sum) of W, each gathered from the
+// per-tile partial sums of kb_wsum.
 __global__ void __launch_bounds__(256)
 kb_ddt(const float *__restrict__ roff, const float *__restrict__ dint,
-       const float *__restrict__ dd, const float *__restrict__ rect,
-       const float *__restrict__ colsum, const float *__restrict__ dtT,
+       const float *__restrict__ dd, const double *__restrict__ rowp,
+       const double *__restrict__ colp, const float *__restrict__ dtT,
        const float *__restrict__ acum_hi, const double *__restrict__ qpart,
        const float *__restrict__ A, float *__restrict__ ddt, double *__restrict__ dApart,
        int L, int H, int nc, int Q, int nsl, int nrb) {
     __shared__ double s_tot[4];
     __shared__ double s_red[4];
+    __shared__ double s_suf[256];
     const int c = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
     const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
+    const size_t tbase = ((size_t)(b * H + h) * nc + c) * nrb;   // per-tile partials
     const int SB = Q < 64 ? Q : 64;
     const bool in = tid < Q;
     double qc = 0.0;
@@ -586,26 +670,25 @@ kb_ddt(const float *__restrict__ roff, const float *__restrict__ dint,
     qc *= (double)fast_exp(acum_hi[vbase + Q - 1]);
     const float dtl = in ? dtT[vbase + tid] : 0.f;
     // sum_{s >= t} roff_s: a prefix sum over the reversed order
-    const double ro = tid < Q ? (double)roff[vbase + (Q - 1 - tid)] : 0.0;
+    const double ro = in ? (double)roff[vbase + (Q - 1 - tid)] : 0.0;
     const double suf_rev = block_scan_f64(ro, s_tot);   // at thread j: sum over s >= Q-1-j
-    __shared__ double s_suf[256];
     if (in) s_suf[Q - 1 - tid] = suf_rev;
     // sum_{s' < t} dt_s' dint_s'
     const double di = in ? (double)dtl * dint[vbase + tid] : 0.0;
     const double pre = block_scan_f64(di, s_tot) - di;
-    // the rectangle's rows in later blocks: sum over blocks lb > t's block of
-    // sum_{s' < t} colsum_lb[s'] (colsum_lb is defined below block lb)
-    double cross = 0.0;
-    const int tb = tid / SB;
-    for (int lb = 1; lb < nrb; ++lb) {
-        const double cv = tid < lb * SB ? (double)colsum[(vbase / Q * nrb + lb) * Q + tid] : 0.0;
-        const double p = block_scan_f64(cv, s_tot) - cv;
-        if (lb > tb) cross += p;
+    // the rectangle sum
+    double cr = 0.0;
+    if (in) {
+        const int kb = tid / SB;
+        for (int lb = kb; lb < nrb; ++lb)
+            for (int w = 0; w < 4; ++w) cr += colp[((tbase + lb) * 4 + w) * Q + tid];
+        for (int sb = 0; sb <= kb; ++sb) cr -= rowp[(tbase + sb) * Q + tid];
     }
+    const double rect = block_scan_f64(cr, s_tot) - cr;
     __syncthreads();
     double gt = 0.0, contrib = 0.0;
     if (in) {
-        gt = s_suf[tid] + qc + (double)rect[vbase + tid] + cross + pre;
+        gt = s_suf[tid] + qc + rect + pre;
         const int t = c * Q + tid;
         if (t < L) ddt[((size_t)b * L + t) * H + h] = (float)((double)dd[vbase + tid] + (double)A[h] * gt);
         contrib = (double)dtl * gt;
@@ -636,8 +719,8 @@ kb_reduce(const double *__restrict__ dApart, const float *__restrict__ dDpart, f
 // ------------------------------------------------------------ launch
 
 const char *const kBackwardKernelNames[kBackwardKernels] = {
-    "k1..k4 (recompute)", "kb_adj_chunk_state", "kb_state_passing", "kb_dx", "kb_dB",
-    "kb_dC", "kb_ddt", "kb_reduce"};
+    "k1..k4 (recompute)", "kb_adj_chunk_state", "kb_state_passing", "kb_dx", "kb_wsum",
+    "kb_dB", "kb_dC", "kb_ddt", "kb_reduce"};
 
 template <typename T, int MODE, int NW>
 static void launch_mix(const BackwardArgs &a, void *out, float *part, hipStream_t stream) {
@@ -649,9 +732,9 @@ static void launch_mix(const BackwardArgs &a, void *out, float *part, hipStream_
     const size_t lds = KbLds::bytes(16 * NW, (int)sizeof(T));
     hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, ny, f.batch),
                        dim3(256), lds, stream, (const T *)f.x, (const T *)f.B, (const T *)f.C,
-                       (const T *)a.dy, (const float *)f.cb, (const float *)f.S, (const float *)a.adj,
-                       (const float *)f.acum_hi, (const float *)f.acum_lo, (const float *)f.dtT,
-                       f.D, (T *)out, a.roff, a.dint, a.dd, a.rect, a.colsum, a.dDpart,
+                       (const T *)a.dy, (const float *)f.cb, (const T *)a.wsm, (const float *)f.S,
+                       (const float *)a.adj, (const float *)f.acum_hi, (const float *)f.acum_lo,
+                       (const float *)f.dtT, f.D, (T *)out, a.roff, a.dint, a.dd, a.dDpart,
                        (MODE != kDx && ny > f.G) ? part : nullptr, f.L, f.H, f.G, f.P, f.N,
                        f.nchunks, f.Q, hpw);
     if (MODE != kDx && ny > f.G) {
@@ -684,6 +767,15 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     else
         launch_mix<T, kDx, 8>(a, a.dx, nullptr, stream);
     if ((err = mark()) != hipSuccess) return err;
+    {
+        const int nrb = bwd_row_blocks(f.Q);
+        hipLaunchKernelGGL(kb_wsum<T>, dim3(nrb * (nrb + 1) / 2, f.nchunks * f.G, f.batch),
+                           dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
+                           (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
+                           (const float *)f.dtT, (T *)a.wsm, a.rowp, a.colp, f.L, f.H, f.G, f.P,
+                           f.nchunks, f.Q);
+    }
+    if ((err = mark()) != hipSuccess) return err;
     if (f.N <= 128)
         launch_mix<T, kDb, 8>(a, a.dB, a.partB, stream);
     else
@@ -696,7 +788,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     if ((err = mark()) != hipSuccess) return err;
     hipLaunchKernelGGL(kb_ddt, dim3(f.nchunks, f.H, f.batch), dim3(256), 0, stream,
                        (const float *)a.roff, (const float *)a.dint, (const float *)a.dd,
-                       (const float *)a.rect, (const float *)a.colsum, (const float *)f.dtT,
+                       (const double *)a.rowp, (const double *)a.colp, (const float *)f.dtT,
                        (const float *)f.acum_hi, (const double *)a.qpart, f.A, a.ddt, a.dApart,
                        f.L, f.H, f.nchunks, f.Q, nsl, bwd_row_blocks(f.Q));
     if ((err = mark()) != hipSuccess) return err;

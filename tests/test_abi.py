@@ -360,8 +360,9 @@ def test_backward_validation(lib, kw, code):
 def test_backward_workspace_size(lib):
     """The recomputed forward's regions plus the gradient pass's: the
     adjoint chunk products (a state per chunk), fp64 chunk-end products per
-    state slice, four per-token vectors per head and the row-block column
-    sums (one per 64-row block), the dD / dA partial sums, and the head
+    state slice, three per-token vectors per head, the summed score tiles
+    (a C B^T-sized block in the io type), the per-tile strict row sums and
+    per-tile-and-wave column sums, the dD / dA partial sums, and the head
     groups' partial dB and dC."""
     b, L, H, P, N, G, Q = 4, 8192, 80, 64, 128, 1, 256
     nc, nsl, nrb = L // Q, (P * N + 1023) // 1024, Q // 64
@@ -372,9 +373,9 @@ def test_backward_workspace_size(lib):
     # 8192 workgroups: 512 (batch x chunks x row blocks) -> 16 groups of 5,
     # each with an fp32 partial dB and dC
     nhg = 16
-    extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 4 * b * H * nc * Q * 4 +
-             b * H * nc * nrb * Q * 4 + b * nc * H * nrb * 4 + b * nc * H * 8 +
-             2 * nhg * b * L * G * N * 4)
+    extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 3 * b * H * nc * Q * 4 +
+             b * nc * G * Q * Q * 2 + b * H * nc * nrb * Q * 8 + b * H * nc * nrb * 4 * Q * 8 +
+             b * nc * H * nrb * 4 + b * nc * H * 8 + 2 * nhg * b * L * G * N * 4)
     assert out.value >= fwd_split + extra and out.value - (fwd_split + extra) < 16 * 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, 3, Q, 1, ctypes.byref(out)) == 1
-    assert lib.ssd_chunk_scan_bwd_max_kernels() == 8
+    assert lib.ssd_chunk_scan_bwd_max_kernels() == 9

@@ -5,10 +5,12 @@ Bar (normwise relative error of each gradient tensor, ||got - ref|| /
 ||ref||): fp32 runs 1e-4 (the forward's fp32 bar; fp32 accumulation and
 fp32 operands leave about 1e-6), bf16 runs 2e-2 (the forward's bf16 bar:
 the bf16 rounding of dx, dB and dC and of the products' operands is 2^-9
-relative per term).  The same bars hold for dA, whose gradient the
-kernels form from terms that do not cancel (a prefix sum over the chunk of
-<dy, y - D x> - dt x . u would lose about 1e-4 in fp32 and 3e-2 in bf16 on
-these cases).  Every gradient is also checked for non-finite values.
+relative per term).  The same bars hold for dA: the kernels form its terms
+without the large cancellation of the plain chunked form (a prefix sum over
+the chunk of <dy, y - D x> - dt x . u loses about 1e-4 in fp32 and 3e-2 in
+bf16 on these cases; the one difference they keep, of the strict row and
+column sums of W, is summed in fp64).  Every gradient is also checked for
+non-finite values.
 """
 import numpy as np
 import pytest
