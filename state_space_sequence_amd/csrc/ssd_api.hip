@@ -396,7 +396,8 @@ ssd_status forward_impl(const void *x, const float *dt, const float *A, const vo
 
 struct BwdLayout {
     Layout f;   // the split forward's regions, recomputed
-    size_t adj, qpart, roff, dint, dd, wsm, rowp, colp, dDpart, dApart, partB, partC, total;
+    size_t adj, qpart, roff, dint, dd, wsm, wpart, rowp, colp, dDpart, dApart, partB, partC,
+        total;
 };
 
 BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int dstate,
@@ -422,6 +423,13 @@ BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int ds
     off += tok;
     l.wsm = off;
     off += round_up(b * nc * ngroups * Q * Q * (io == SSD_BF16 ? 2 : 4));
+    {
+        const int nt = (int)(nrb * (nrb + 1) / 2), hpg = nheads / ngroups;
+        const int hpw = ssd::bwd_wsum_heads(nt, (int)nc, ngroups, batch, hpg);
+        const size_t ng = (size_t)((hpg + hpw - 1) / hpw);
+        l.wpart = off;
+        off += ng > 1 ? round_up(ng * b * nc * ngroups * Q * Q * sizeof(float)) : 0;
+    }
     l.rowp = off;
     off += round_up(b * H * nc * nrb * Q * sizeof(double));
     l.colp = off;
@@ -506,6 +514,7 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     a.dint = reinterpret_cast<float *>(ws + lay.dint);
     a.dd = reinterpret_cast<float *>(ws + lay.dd);
     a.wsm = ws + lay.wsm;
+    a.wpart = reinterpret_cast<float *>(ws + lay.wpart);
     a.rowp = reinterpret_cast<double *>(ws + lay.rowp);
     a.colp = reinterpret_cast<double *>(ws + lay.colp);
     a.partB = reinterpret_cast<float *>(ws + lay.partB);

@@ -29,6 +29,7 @@ struct BackwardArgs {
     float *dint;    // [b][H][nc][Q]: x_t . (e^(acum_end - acum_t) Lam B_t)
     float *dd;      // [b][H][nc][Q]: x_t . u_t (the direct part of ddt)
     void *wsm;      // [b][nc][G][Q][Q] io type: the group's summed score tiles Ws
+    float *wpart;   // [nhg][b][nc][G][Q][Q]: per head group partial Ws (nhg > 1)
     double *rowp;   // [b][H][nc][nrb][Q]: strict row sums of W per (row block's) tile
     double *colp;   // [b][H][nc][nrb][4][Q]: strict column sums of W per tile and wave
     float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
@@ -48,6 +49,16 @@ inline int bwd_row_blocks(int Q) { return Q > 64 ? Q / 64 : 1; }
 inline int bwd_heads_per_group(int batch, int nc, int nrb, int G, int hpg) {
     const long wg = (long)batch * nc * nrb * G;
     long ng = (8192 + wg - 1) / wg;
+    if (ng > hpg) ng = hpg;
+    if (ng < 1) ng = 1;
+    return (int)((hpg + ng - 1) / ng);
+}
+// Heads per workgroup of the summed-score kernel: enough head groups for
+// about 4096 workgroups (each group's fp32 partial tiles are added up by a
+// separate pass).
+inline int bwd_wsum_heads(int ntile, int nc, int G, int batch, int hpg) {
+    const long wg = (long)ntile * nc * G * batch;
+    long ng = (4096 + wg - 1) / wg;
     if (ng > hpg) ng = hpg;
     if (ng < 1) ng = 1;
     return (int)((hpg + ng - 1) / ng);

@@ -121,28 +121,32 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // (per tile) and column sums (per tile and wave), summed in fp64 from the
 // fp32 entries (the prefix subtracts sums much larger than the result).
 //
-// grid (tiles = nrb (nrb + 1) / 2, nc * G, b), 256 threads, no LDS.
+// grid (tiles = nrb (nrb + 1) / 2, nc * G * nhg, b), 256 threads, no LDS.
 // Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile of rows l in block lb,
-// columns s in block sb; wave w its rows 16 w ..; it loops over the group's
-// heads with the tile's sum in registers and writes Ws in the operand type.
+// columns s in block sb; wave w its rows 16 w ..; it loops over hpw of the
+// group's heads (head group k of nhg) with the tile's sum in registers and
+// writes it as Ws in the operand type, or, with several head groups, as an
+// fp32 partial sum that a separate pass adds up.
 template <typename T>
 __global__ void __launch_bounds__(256)
 kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restrict__ cb,
         const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
-        const float *__restrict__ dtT, T *__restrict__ ws, double *__restrict__ rowp,
-        double *__restrict__ colp, int L, int H, int G, int P, int nc, int Q) {
+        const float *__restrict__ dtT, T *__restrict__ ws, float *__restrict__ wpart,
+        double *__restrict__ rowp, double *__restrict__ colp, int L, int H, int G, int P,
+        int nc, int Q, int hpw) {
     typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     int pair = blockIdx.x, lb = 0;
     while ((lb + 1) * (lb + 2) / 2 <= pair) ++lb;
     const int sb = pair - lb * (lb + 1) / 2;
-    const int c = blockIdx.y / G, g = blockIdx.y % G, b = blockIdx.z;
+    const int hpg = H / G, nhg = (hpg + hpw - 1) / hpw;
+    const int hgi = blockIdx.y % nhg, cg = blockIdx.y / nhg;
+    const int c = cg / G, g = cg % G, b = blockIdx.z;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
     const int nrb = Q > 64 ? Q / 64 : 1;
     const int SB = Q < 64 ? Q : 64;
     const bool active = wave * 16 < SB;
-    const int hpg = H / G;
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
     // this lane's entries: rows l = lb SB + 16 w + 4 q + i, columns s = sb SB + 16 st + r
     int lrow[4], scol[4];
@@ -160,7 +164,8 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
             cbv[st][i] = ok ? cb[(cbase + lrow[i]) * Q + scol[st]] : 0.f;
         }
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    for (int hh = 0; hh < hpg; ++hh) {
+    const int h0 = hgi * hpw, h1 = min(hpg, h0 + hpw);
+    for (int hh = h0; hh < h1; ++hh) {
         const int h = g * hpg + hh;
         const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
         double rsum[4] = {0.0, 0.0, 0.0, 0.0}, csum[4] = {0.0, 0.0, 0.0, 0.0};
@@ -227,8 +232,13 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
         for (int st = 0; st < 4; ++st)
 #pragma unroll
             for (int i = 0; i < 4; ++i)
-                if (st * 16 + r < SB && lrow[i] - lb * SB < SB)
-                    ws[(cbase + lrow[i]) * Q + scol[st]] = from_f32<T>(acc[st][i]);
+                if (st * 16 + r < SB && lrow[i] - lb * SB < SB) {
+                    const size_t o = (cbase + lrow[i]) * Q + scol[st];
+                    if (wpart)
+                        wpart[(size_t)hgi * gridDim.z * nc * G * Q * Q + o] = acc[st][i];
+                    else
+                        ws[o] = from_f32<T>(acc[st][i]);
+                }
     }
 }
 
@@ -700,20 +710,29 @@ kb_ddt(const float *__restrict__ roff, const float *__restrict__ dint,
 }
 
 // ------------------------------------------------------------ dA and dD
-// grid (ceil(H / 256)), one head per thread: the partial sums in a fixed
-// order (deterministic).
+// grid (H), 256 threads: head h's partial sums, each thread a fixed strided
+// share, then a fixed-order tree (deterministic).
 __global__ void __launch_bounds__(256)
 kb_reduce(const double *__restrict__ dApart, const float *__restrict__ dDpart, float *__restrict__ dA,
           float *__restrict__ dD, int batch, int H, int nc, int nrb) {
-    const int h = blockIdx.x * 256 + threadIdx.x;
-    if (h >= H) return;
+    __shared__ double s_a[4], s_d[4];
+    const int h = blockIdx.x, tid = threadIdx.x;
     double sa = 0.0, sd = 0.0;
-    for (int bc = 0; bc < batch * nc; ++bc) {
+    for (int bc = tid; bc < batch * nc; bc += 256) {
         sa += dApart[(size_t)bc * H + h];
         for (int k = 0; k < nrb; ++k) sd += dDpart[((size_t)bc * H + h) * nrb + k];
     }
-    dA[h] = (float)sa;
-    if (dD) dD[h] = (float)sd;
+    sa = wave_sum_f64(sa);
+    sd = wave_sum_f64(sd);
+    if ((tid & 63) == 0) {
+        s_a[tid >> 6] = sa;
+        s_d[tid >> 6] = sd;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        dA[h] = (float)(s_a[0] + s_a[1] + s_a[2] + s_a[3]);
+        if (dD) dD[h] = (float)(s_d[0] + s_d[1] + s_d[2] + s_d[3]);
+    }
 }
 
 // ------------------------------------------------------------ launch
@@ -769,11 +788,21 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     if ((err = mark()) != hipSuccess) return err;
     {
         const int nrb = bwd_row_blocks(f.Q);
-        hipLaunchKernelGGL(kb_wsum<T>, dim3(nrb * (nrb + 1) / 2, f.nchunks * f.G, f.batch),
+        const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
+        const int hpw = bwd_wsum_heads(ntile, f.nchunks, f.G, f.batch, hpg);
+        const int nhg = (hpg + hpw - 1) / hpw;
+        hipLaunchKernelGGL(kb_wsum<T>, dim3(ntile, f.nchunks * f.G * nhg, f.batch),
                            dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
                            (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
-                           (const float *)f.dtT, (T *)a.wsm, a.rowp, a.colp, f.L, f.H, f.G, f.P,
-                           f.nchunks, f.Q);
+                           (const float *)f.dtT, (T *)a.wsm, nhg > 1 ? a.wpart : nullptr, a.rowp,
+                           a.colp, f.L, f.H, f.G, f.P, f.nchunks, f.Q, hpw);
+        if (nhg > 1) {
+            // (entries of a chunk's Q x Q block above its diagonal blocks stay
+            // unwritten and are never read)
+            const size_t n = (size_t)f.batch * f.nchunks * f.G * f.Q * f.Q;
+            hipLaunchKernelGGL(kb_sum_heads<T>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                               stream, (const float *)a.wpart, (T *)a.wsm, n, nhg);
+        }
     }
     if ((err = mark()) != hipSuccess) return err;
     if (f.N <= 128)
@@ -792,7 +821,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
                        (const float *)f.acum_hi, (const double *)a.qpart, f.A, a.ddt, a.dApart,
                        f.L, f.H, f.nchunks, f.Q, nsl, bwd_row_blocks(f.Q));
     if ((err = mark()) != hipSuccess) return err;
-    hipLaunchKernelGGL(kb_reduce, dim3((f.H + 255) / 256), dim3(256), 0, stream,
+    hipLaunchKernelGGL(kb_reduce, dim3(f.H), dim3(256), 0, stream,
                        (const double *)a.dApart, (const float *)a.dDpart, a.dA, a.dD, f.batch, f.H,
                        f.nchunks, bwd_row_blocks(f.Q));
     if ((err = mark()) != hipSuccess) return err;

@@ -373,9 +373,13 @@ def test_backward_workspace_size(lib):
     # 8192 workgroups: 512 (batch x chunks x row blocks) -> 16 groups of 5,
     # each with an fp32 partial dB and dC
     nhg = 16
+    # the summed-score kernel: 10 tiles x 32 chunks x 4 rows = 1280 workgroups
+    # -> 4 head groups of 20 for about 4096, each with fp32 partial tiles
+    nhw = 4
     extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 3 * b * H * nc * Q * 4 +
              b * nc * G * Q * Q * 2 + b * H * nc * nrb * Q * 8 + b * H * nc * nrb * 4 * Q * 8 +
-             b * nc * H * nrb * 4 + b * nc * H * 8 + 2 * nhg * b * L * G * N * 4)
+             b * nc * H * nrb * 4 + b * nc * H * 8 + 2 * nhg * b * L * G * N * 4 +
+             nhw * b * nc * G * Q * Q * 4)
     assert out.value >= fwd_split + extra and out.value - (fwd_split + extra) < 16 * 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, 3, Q, 1, ctypes.byref(out)) == 1
     assert lib.ssd_chunk_scan_bwd_max_kernels() == 9
