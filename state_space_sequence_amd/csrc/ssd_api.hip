@@ -462,6 +462,9 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     if (st != SSD_OK) return st;
     if (!x || !dt || !A || !B || !C || !dy || !dx || !ddt || !dA || !dB || !dC)
         return SSD_ERR_INVALID_ARGUMENT;
+    // (the gradient kernels put chunks x row blocks on the y grid dimension)
+    if ((long)((seqlen + chunk_len - 1) / chunk_len) * ssd::bwd_row_blocks(chunk_len) > 65535)
+        return SSD_ERR_UNSUPPORTED;
     if (!aligned(x, 16) || !aligned(B, 16) || !aligned(C, 16) || !aligned(dy, 16) ||
         !aligned(dx, 16) || !aligned(dB, 16) || !aligned(dC, 16) || !aligned(dt, 4) ||
         !aligned(A, 4) || !aligned(ddt, 4) || !aligned(dA, 4) || (D && !aligned(D, 4)) ||

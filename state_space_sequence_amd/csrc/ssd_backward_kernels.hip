@@ -258,8 +258,9 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
 // Ws from kb_wsum.  kDx also writes x_t . (its state part), kDc <dy_t, its
 // state part> per head.
 //
-// grid (nc * nrb, H (kDx) or G * nhg (kDb, kDc), b), 256 threads (4 waves),
-// dynamic LDS KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64)
+// grid (H, nc * nrb, b) for kDx (heads fastest, so that the workgroups
+// running together share a chunk's C B^T in L2) and (nc * nrb, G * nhg, b)
+// for kDb and kDc, 256 threads (4 waves), dynamic LDS KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64)
 // rows of row block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column
 // tiles span the output width W (P or N, padded; padded columns are never
 // stored).  kDb / kDc split a group's heads over nhg workgroups for the
@@ -281,10 +282,11 @@ struct KbLds {
     static __host__ __device__ constexpr int mpitch(int sz) { return kSB + 16 / sz; }
     // + a K-slab of the state, transposed: [WP][KS + 16 / sz]
     static __host__ __device__ constexpr int spitch(int sz) { return (sz == 4 ? 16 : 32) + 16 / sz; }
-    // + prefix sums and dt by token and a reduction slot per wave (fp32)
+    // + prefix sums and dt by token, a reduction slot per wave and a decay
+    // factor per source column (fp32)
     static size_t bytes(int WP, int sz) {
         return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz) + (size_t)WP * spitch(sz)) * sz +
-               3 * 256 * 4 + 64;
+               3 * 256 * 4 + 64 + kSB * 4;
     }
 };
 
@@ -315,6 +317,7 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
     float *red = r_dt + 256;                                  // [16]
+    float *colf = red + 16;                                   // [SBX]: kDx's column decay factors
     // the position of tile column s in an Wt row (fp32: the fragments take
     // the K index kk + q + 4 j, stored at kk + 4 q + j)
     auto mcol = [](int s) -> int {
@@ -331,7 +334,10 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     };
 
     const int nrb = Q > SBX ? Q / SBX : 1;
-    const int c = blockIdx.x / nrb, lb = blockIdx.x % nrb;
+    // (kDx: heads on x, chunk row blocks on y; kDb / kDc the other way round)
+    const int bx = MODE == kDx ? blockIdx.x : blockIdx.y, by = MODE == kDx ? blockIdx.y : blockIdx.x;
+    const int nx = MODE == kDx ? gridDim.x : gridDim.y;
+    const int c = by / nrb, lb = by % nrb;
     const int b = blockIdx.z;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
@@ -342,9 +348,9 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     const int KD = MODE == kDx ? N : P;      // K of the state product
     const int hpg = H / G;
     // kDb / kDc: workgroup y = g * nhg + k takes heads k hpw .. of group g
-    const int nhg = MODE == kDx ? 1 : (int)gridDim.y / G, hgi = MODE == kDx ? 0 : blockIdx.y % nhg;
-    const int g = MODE == kDx ? blockIdx.y / hpg : blockIdx.y / nhg;
-    const int h_first = MODE == kDx ? blockIdx.y : g * hpg + hgi * hpw;
+    const int nhg = MODE == kDx ? 1 : nx / G, hgi = MODE == kDx ? 0 : bx % nhg;
+    const int g = MODE == kDx ? bx / hpg : bx / nhg;
+    const int h_first = MODE == kDx ? bx : g * hpg + hgi * hpw;
     const int h_count = MODE == kDx ? 1 : min(hpw, hpg - hgi * hpw);
     const int t0 = c * Q + lb * SB;          // the row block's first token
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
@@ -365,10 +371,10 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         __syncthreads();
         const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
 
-        // ---- the state product U_t St, scaled per row.  kDx's fragments are
-        // VEC consecutive dstate entries of a Lam row, read straight from
-        // memory; kDb and kDc take K along the headdim, across the state's
-        // rows, so the state passes through LDS in K-slabs, transposed.
+        // ---- the state product U_t St, scaled per row.  The state passes
+        // through LDS in K-slabs, as SS[w][k]: for kDx the slab is columns
+        // k0 .. of Lam's rows (a copy), for kDb and kDc rows k0 .. of the
+        // state (a transpose).
         f32x4 acc[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[i] = zero4();
@@ -380,8 +386,17 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                                     : dy + (((size_t)b * L + tr) * H + h) * P;
         for (int k0 = 0; k0 < KD; k0 += KS) {
             const int k = k0 + VEC * q;
-            if constexpr (MODE != kDx) {
-                __syncthreads();   // (the previous slab is no longer read)
+            __syncthreads();   // (the previous slab is no longer read)
+            if constexpr (MODE == kDx) {
+                constexpr int kq = KS / 4;
+                for (int v = tid; v < W * kq; v += 256) {
+                    const int w = v / kq, kr = (v % kq) * 4;
+                    f32x4 f = zero4();
+                    if (k0 + kr < KD) f = *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
+#pragma unroll
+                    for (int jj = 0; jj < 4; ++jj) SS[w * SP + kr + jj] = from_f32<T>(f[jj]);
+                }
+            } else {
                 const int wq = W / 4;
                 for (int v = tid; v < KS * wq; v += 256) {
                     const int kr = v / wq, w0 = (v % wq) * 4;
@@ -390,32 +405,15 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
 #pragma unroll
                     for (int jj = 0; jj < 4; ++jj) SS[(w0 + jj) * SP + kr] = from_f32<T>(f[jj]);
                 }
-                __syncthreads();
             }
+            __syncthreads();
             if (!active) continue;
             const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
 #pragma unroll
             for (int wt = 0; wt < NW; ++wt) {
                 const int w = wt * 16 + r;
                 frag sb = zero_frag<T>();
-                if (w < W && k < KD) {
-                    if constexpr (MODE == kDx) {
-                        const float *sp = st + (size_t)w * N + k;
-                        if constexpr (F32) {
-                            sb = *reinterpret_cast<const f32x4 *>(sp);
-                        } else {
-                            const f32x4 lo = *reinterpret_cast<const f32x4 *>(sp);
-                            const f32x4 hi = *reinterpret_cast<const f32x4 *>(sp + 4);
-#pragma unroll
-                            for (int jj = 0; jj < 4; ++jj) {
-                                sb[jj] = from_f32<T>(lo[jj]);
-                                sb[4 + jj] = from_f32<T>(hi[jj]);
-                            }
-                        }
-                    } else {
-                        sb = load_frag(SS + w * SP + VEC * q);
-                    }
-                }
+                if (w < W && k < KD) sb = load_frag(SS + w * SP + VEC * q);
                 acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
             }
         }
@@ -474,17 +472,42 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                         for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
                     }
                 }
+                if (sb > lb && tid < SB) {
+                    // below the diagonal the decay factors through the row
+                    // block's last row te: e^(acum_s - acum_t) =
+                    // e^(acum_s - acum_te) e^(acum_te - acum_t), both <= 1
+                    const int te = lb * SB + SB - 1, ls = sb * SB + tid;
+                    colf[tid] = fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[te], r_lo[te]));
+                }
+                __syncthreads();
                 if (active) {
                     // lane: row tl = lane % 16, columns 16 (lane / 16) + j
+                    const int tl = wave * 16 + r, lt = lb * SB + tl;
+                    if (sb > lb) {
+                        const int te = lb * SB + SB - 1;
+                        const float rowf = fast_exp(prefix_diff(r_hi[te], r_lo[te], r_hi[lt], r_lo[lt]));
+                        float cv[16];
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int sl = q * 16 + j;
+                            cv[j] = sl < SB ? cb[(cbase + sb * SB + sl) * Q + lt] : 0.f;
+                        }
+#pragma unroll
+                        for (int j = 0; j < 16; ++j) {
+                            const int sl = q * 16 + j;
+                            MT[tl * PITCH + mcol(sl)] = from_f32<T>(sl < SB ? cv[j] * rowf * colf[sl] : 0.f);
+                        }
+                    } else {
 #pragma unroll 4
-                    for (int j = 0; j < 16; ++j) {
-                        const int tl = wave * 16 + r, sl = q * 16 + j;
-                        const int lt = lb * SB + tl, ls = sb * SB + sl;
-                        float v = 0.f;
-                        if (sl < SB && ls >= lt)
-                            v = cb[(cbase + ls) * Q + lt] *
-                                fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
-                        MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
+                        for (int j = 0; j < 16; ++j) {
+                            const int sl = q * 16 + j;
+                            const int ls = sb * SB + sl;
+                            float v = 0.f;
+                            if (sl < SB && ls >= lt)
+                                v = cb[(cbase + ls) * Q + lt] *
+                                    fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
+                            MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
+                        }
                     }
                     if (SBK > SB) {   // (bf16 chunks of 16: zero columns SB .. SBK - 1)
                         for (int j = 0; j < 16; ++j) {
@@ -749,7 +772,9 @@ static void launch_mix(const BackwardArgs &a, void *out, float *part, hipStream_
     const int hpw = MODE == kDx ? 1 : bwd_heads_per_group(f.batch, f.nchunks, nrb, f.G, hpg);
     const int ny = MODE == kDx ? f.H : f.G * ((hpg + hpw - 1) / hpw);
     const size_t lds = KbLds::bytes(16 * NW, (int)sizeof(T));
-    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, ny, f.batch),
+    const dim3 grid = MODE == kDx ? dim3(ny, f.nchunks * nrb, f.batch)
+                                  : dim3(f.nchunks * nrb, ny, f.batch);
+    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), grid,
                        dim3(256), lds, stream, (const T *)f.x, (const T *)f.B, (const T *)f.C,
                        (const T *)a.dy, (const float *)f.cb, (const T *)a.wsm, (const float *)f.S,
                        (const float *)a.adj, (const float *)f.acum_hi, (const float *)f.acum_lo,
