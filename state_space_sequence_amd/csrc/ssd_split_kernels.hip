@@ -875,6 +875,142 @@ k3_chunk_state_f32(const float *__restrict__ x, const float *__restrict__ Bm,
         }
 }
 
+// --------------------------------------------------------------------- k3, bf16
+// The bf16 chunk state, built as the fp32 one (K3F32Lds): a workgroup
+// computes a 64 x 128 block of the state, its waves 2 x 2 sub-blocks of 2 x 4
+// tiles; the per-token weight once per token; 32-token slabs of (weighted)
+// x and of B staged untransposed in LDS, rows padded by 8 elements; the next
+// slab loaded into registers while this slab's MFMAs run.  The MFMA takes K
+// (tokens) 8 to a lane, so the fragments come from the transposing LDS read
+// (ds_read_b64_tr_b16): within each 16-lane group lane a + 4 e reads 4
+// columns 4a .. 4a + 3 of token row kbase + e, and lane 4 a + c receives
+// column 4 a + c of the four rows; two reads (rows kbase .. kbase + 7) make a
+// fragment.  With the padding, the 16 rows one read touches spread over the
+// banks (at most two lanes per bank).
+struct K3Bf16Lds {
+    static constexpr int kKB = 32;
+    static constexpr int kXP = 64 + 8, kBP = 128 + 8;   // row pitches (elements)
+    static size_t bytes() { return ((size_t)kKB * (kXP + kBP)) * 2 + 256 * 4; }
+};
+
+typedef __bf16 k3_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) k3_bf16x4 k3_lds_bf16x4;
+typedef __attribute__((address_space(3))) unsigned char k3_lds_u8;
+
+__device__ __forceinline__ bf16x8 k3_tr_frag(const bf16 *base, int off0, int off1) {
+    const k3_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (k3_lds_bf16x4 *)((k3_lds_u8 *)base + off0));
+    const k3_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (k3_lds_bf16x4 *)((k3_lds_u8 *)base + off1));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+template <bool ADJ = false>
+__global__ void __launch_bounds__(256)
+k3_chunk_state_bf16(const bf16 *__restrict__ x, const bf16 *__restrict__ Bm,
+                    const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+                    const float *__restrict__ dtT, float *__restrict__ S, int L, int H,
+                    int G, int P, int N, int nc, int Q, const int *__restrict__ segst) {
+    constexpr int KB = K3Bf16Lds::kKB, XP = K3Bf16Lds::kXP, BP = K3Bf16Lds::kBP;
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    bf16 *XS = reinterpret_cast<bf16 *>(smem_raw);     // [KB][XP]: w_s x[s][64 pg + p]
+    bf16 *BS = XS + KB * XP;                            // [KB][BP]: B[s][128 ng + n]
+    float *s_w = reinterpret_cast<float *>(BS + KB * BP);   // [256]
+
+    const int npg = (P + 63) / 64, nng = (N + 127) / 128;
+    const int c = blockIdx.x, b = blockIdx.z;
+    const int h = blockIdx.y / (npg * nng), pg = blockIdx.y / nng % npg, ng = blockIdx.y % nng;
+    const int g = h / (H / G);
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int wp = (wave >> 1) * 32, wn = (wave & 1) * 64;
+    const float *ah = acum_hi + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *al = acum_lo + ((size_t)(b * H + h) * nc + c) * Q;
+    const float *dc = dtT + ((size_t)(b * H + h) * nc + c) * Q;
+    {
+        const float end_hi = ah[Q - 1], end_lo = al[Q - 1];
+        const int s_first = segst ? segst[((size_t)b * nc + c) * Q + Q - 1] : -1;
+        const int s = tid;
+        const bool in = s < Q && c * Q + s < L && (ADJ || s >= s_first);
+        s_w[s] = !in ? 0.f
+               : ADJ ? fast_exp(ah[s])
+                     : fast_exp(prefix_diff(end_hi, end_lo, ah[s], al[s])) * dc[s];
+    }
+    // slab loads, 8 bf16 per piece: x rows of 64 (8 pieces per token), B rows
+    // of 128 (16 per token); 1 + 2 per thread
+    constexpr int XV = KB * 8 / 256, BV = KB * 16 / 256;
+    bf16x8 xr[XV], br[BV];
+    const int p_lo = 64 * pg, n_lo = 128 * ng;
+    auto load = [&](int s0) {
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 3, p = p_lo + 8 * (v & 7), t = c * Q + s0 + sl;
+            xr[u] = zero_frag<bf16>();
+            if (s0 + sl < Q && t < L && p < P) xr[u] = load_frag(x + (((size_t)b * L + t) * H + h) * P + p);
+        }
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 4, n = n_lo + 8 * (v & 15), t = c * Q + s0 + sl;
+            br[u] = zero_frag<bf16>();
+            if (s0 + sl < Q && t < L && n < N) br[u] = load_frag(Bm + (((size_t)b * L + t) * G + g) * N + n);
+        }
+    };
+    // this lane's read addresses (bytes) within a slab: rows e = r / 4 (+ 4),
+    // columns 4 (r % 4) of each 16-column tile, K rows 8 q ..
+    const int er = r >> 2, ca = 4 * (r & 3);
+    f32x4 acc[2][4];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) acc[i][k] = zero4();
+
+    load(0);
+    for (int s0 = 0; s0 < Q; s0 += KB) {
+        __syncthreads();   // (the previous slab is no longer read; s_w visible)
+#pragma unroll
+        for (int u = 0; u < XV; ++u) {
+            const int v = tid + 256 * u, sl = v >> 3;
+            const float w = s_w[(s0 + sl) & 255];
+            bf16x8 f;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) f[j] = (bf16)((float)xr[u][j] * w);
+            *reinterpret_cast<bf16x8 *>(XS + sl * XP + 8 * (v & 7)) = f;
+        }
+#pragma unroll
+        for (int u = 0; u < BV; ++u) {
+            const int v = tid + 256 * u;
+            *reinterpret_cast<bf16x8 *>(BS + (v >> 4) * BP + 8 * (v & 15)) = br[u];
+        }
+        __syncthreads();
+        if (s0 + KB < Q) load(s0 + KB);
+        bf16x8 a[2], bb[4];
+        const int k0 = 8 * q + er;   // this lane's first K row (token) in the slab
+#pragma unroll
+        for (int i = 0; i < 2; ++i) {
+            const int col = wp + 16 * i + ca;
+            a[i] = k3_tr_frag(XS, (k0 * XP + col) * 2, ((k0 + 4) * XP + col) * 2);
+        }
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int col = wn + 16 * k + ca;
+            bb[k] = k3_tr_frag(BS, (k0 * BP + col) * 2, ((k0 + 4) * BP + col) * 2);
+        }
+        mma_grid<bf16>(a, bb, acc);
+    }
+    float *Sc = S + ((size_t)(b * nc + c) * H + h) * P * N;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int n = n_lo + wn + 16 * k + r;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const int p = p_lo + wp + 16 * i + 4 * q + e;
+                if (p < P && n < N) Sc[(size_t)p * N + n] = acc[i][k][e];
+            }
+        }
+}
+
 // --------------------------------------------------------------------- launch
 
 const char *const kSplitKernelNames[kSplitKernels] = {
@@ -898,12 +1034,10 @@ void launch_k3(const ForwardArgs &a, const void *xx, const void *bb, float *out,
                            K3F32Lds::bytes(), stream, (const float *)xx, (const float *)bb,
                            a.acum_hi, a.acum_lo, a.dtT, out, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
     } else {
-        const int ntiles = (a.P / 16) * (a.N / 16);
-        const int ntg = (ntiles + 4 * kK3TilesPerWave - 1) / (4 * kK3TilesPerWave);
-        const size_t k3_lds = (size_t)(a.P + a.N) * (32 + 16 / sizeof(T)) * sizeof(T);
-        hipLaunchKernelGGL((k3_chunk_state<T, ADJ>), dim3(nc, a.H * ntg, a.batch), dim3(256), k3_lds,
-                           stream, (const T *)xx, (const T *)bb, a.acum_hi, a.acum_lo, a.dtT,
-                           out, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
+        const int nblk = ((a.P + 63) / 64) * ((a.N + 127) / 128);
+        hipLaunchKernelGGL(k3_chunk_state_bf16<ADJ>, dim3(nc, a.H * nblk, a.batch), dim3(256),
+                           K3Bf16Lds::bytes(), stream, (const bf16 *)xx, (const bf16 *)bb,
+                           a.acum_hi, a.acum_lo, a.dtT, out, a.L, a.H, a.G, a.P, a.N, nc, Q, segst);
     }
 }
 
