@@ -136,11 +136,20 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
         int nc, int Q, int hpw) {
     typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
-    int pair = blockIdx.x, lb = 0;
+    // Workgroups are dealt to the 8 XCDs in turn: when gridDim.y is a
+    // multiple of 8 the tiles of one y (which read the same rows of x and
+    // dy) are placed 8 apart, so that they share an L2.
+    int pair = blockIdx.x, yy = blockIdx.y;
+    if ((gridDim.y & 7) == 0) {
+        const int id = blockIdx.x + gridDim.x * blockIdx.y, k = id >> 3;
+        pair = k % gridDim.x;
+        yy = (k / gridDim.x) * 8 + (id & 7);
+    }
+    int lb = 0;
     while ((lb + 1) * (lb + 2) / 2 <= pair) ++lb;
     const int sb = pair - lb * (lb + 1) / 2;
     const int hpg = H / G, nhg = (hpg + hpw - 1) / hpw;
-    const int hgi = blockIdx.y % nhg, cg = blockIdx.y / nhg;
+    const int hgi = yy % nhg, cg = yy / nhg;
     const int c = cg / G, g = cg % G, b = blockIdx.z;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
@@ -260,35 +269,86 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
 //
 // grid (H, nc * nrb, b) for kDx (heads fastest, so that the workgroups
 // running together share a chunk's C B^T in L2) and (nc * nrb, G * nhg, b)
-// for kDb and kDc, 256 threads (4 waves), dynamic LDS KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64)
-// rows of row block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column
-// tiles span the output width W (P or N, padded; padded columns are never
-// stored).  kDb / kDc split a group's heads over nhg workgroups for the
-// state products (fp32 partial sums, added up afterwards); the first of
-// them also takes the intra-chunk product.  Per source block: V staged in
-// LDS (fp32: token rows of a pitch = 16 mod 64 floats, read with the K index
-// kk + q + 4 j; bf16: transposed rows), the rows of Wt in LDS in the operand
-// type, then the MFMAs.
+// for kDb and kDc, 256 threads (4 waves), dynamic LDS KbLds::bytes.
+// Workgroup (c, lb) owns the SB = min(Q, 64) rows of row block lb; wave w
+// the 16 rows 16 w .. 16 w + 15; NW 16-column tiles span the output width W
+// (P or N, padded; padded columns are never stored).  kDb / kDc split a
+// group's heads over nhg workgroups for the state products (fp32 partial
+// sums, added up afterwards); the first of them also takes the intra-chunk
+// product.  Workgroups are dealt to the 8 XCDs in turn; kDb / kDc place the
+// row blocks of a chunk, which read the same states, 8 apart, so that they
+// share an L2 (when nc is a multiple of 8).  (For kDx, with H a multiple of
+// 8, the heads-fastest order already does that.)
+//
+// LDS operands keep the layout they arrive in (rows of tokens, of the state
+// or of the score tile) and are read across rows where the MFMA wants
+// columns: bf16 with the transposing LDS read, fp32 as four scalars with
+// the K index kk + q + 4 j, from rows whose pitch puts the 64 lanes in 64
+// banks.
 enum { kDx = 0, kDb = 1, kDc = 2 };
 
 struct KbLds {
     static constexpr int kSB = 64;
+    // V by token: [kSB][vpitch] (fp32: = 16 mod 64 floats; bf16: 8 elements of padding)
     static __host__ __device__ constexpr int vpitch(int WP, int sz) {
-        return sz == 4 ? WP + (80 - WP % 64) % 64 : kSB + 16 / sz;
+        return sz == 4 ? WP + (80 - WP % 64) % 64 : WP + 8;
     }
     static __host__ __device__ constexpr size_t v_elems(int WP, int sz) {
-        return (size_t)(sz == 4 ? kSB : WP) * vpitch(WP, sz);
+        return (size_t)kSB * vpitch(WP, sz);
     }
-    static __host__ __device__ constexpr int mpitch(int sz) { return kSB + 16 / sz; }
-    // + a K-slab of the state, transposed: [WP][KS + 16 / sz]
-    static __host__ __device__ constexpr int spitch(int sz) { return (sz == 4 ? 16 : 32) + 16 / sz; }
+    // + the score tile: [kSB][mpitch] (fp32 kDx and kDc rows = 4 mod 64
+    // floats, kDb rows = 16 mod 64; bf16 8 elements of padding)
+    static __host__ __device__ constexpr int mpitch(int sz, int mode) {
+        return sz == 4 ? (mode == kDb ? kSB + 16 : kSB + 4) : kSB + 8;
+    }
+    static __host__ __device__ constexpr size_t m_elems(int sz) {
+        return (size_t)kSB * (sz == 4 ? kSB + 16 : kSB + 8);
+    }
+    // + a K-slab of the state: kDx [WP][ks + 16 / sz] (Lam's rows cut to the
+    // slab's columns), kDb / kDc [ks][WP + 16 / sz] (the slab's rows)
+    static __host__ __device__ constexpr int ks(int sz) { return sz == 4 ? 16 : 32; }
+    static __host__ __device__ constexpr int spitch(int WP, int sz, int mode) {
+        return mode == kDx ? ks(sz) + 16 / sz : WP + 16 / sz;
+    }
+    static __host__ __device__ constexpr size_t s_elems(int WP, int sz) {
+        return (size_t)WP * spitch(WP, sz, kDx) > (size_t)ks(sz) * spitch(WP, sz, kDb)
+                   ? (size_t)WP * spitch(WP, sz, kDx)
+                   : (size_t)ks(sz) * spitch(WP, sz, kDb);
+    }
     // + prefix sums and dt by token, a reduction slot per wave and a decay
     // factor per source column (fp32)
     static size_t bytes(int WP, int sz) {
-        return (v_elems(WP, sz) + (size_t)kSB * mpitch(sz) + (size_t)WP * spitch(sz)) * sz +
-               3 * 256 * 4 + 64 + kSB * 4;
+        return (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64 + kSB * 4;
     }
 };
+
+typedef __bf16 kb_bf16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) kb_bf16x4 kb_lds_bf16x4;
+typedef __attribute__((address_space(3))) unsigned char kb_lds_u8;
+
+// The bf16 MFMA operand of K rows k0 .. k0 + 7 and 16 columns c0 .. of a
+// row-major LDS tile, read across its rows: lane r + 16 q passes row
+// k0 + (r >> 2) (row k0 + 4 + (r >> 2) for the second read) and columns
+// c0 + 4 (r & 3) .. + 3, and receives column c0 + r of the four rows each
+// read covers.  Called with row = k0 + (r >> 2), col = c0 + 4 (r & 3).
+__device__ __forceinline__ bf16x8 kb_tr_frag(const bf16 *tile, int pitch, int row, int col) {
+    const kb_bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (kb_lds_bf16x4 *)((kb_lds_u8 *)tile + (row * pitch + col) * 2));
+    const kb_bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (kb_lds_bf16x4 *)((kb_lds_u8 *)tile + ((row + 4) * pitch + col) * 2));
+    return bf16x8{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+}
+
+// Four fp32 values to LDS in the operand type (one 16- or 8-byte store).
+template <typename T>
+__device__ __forceinline__ void kb_store4(T *dst, f32x4 f) {
+    if constexpr (sizeof(T) == 4) {
+        *reinterpret_cast<f32x4 *>(dst) = f;
+    } else {
+        *reinterpret_cast<kb_bf16x4 *>(dst) =
+            kb_bf16x4{(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3]};
+    }
+}
 
 template <typename T, int MODE, int NW>
 __global__ void __launch_bounds__(256)
@@ -307,53 +367,81 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     constexpr int SBX = KbLds::kSB;
     constexpr int WP = 16 * NW;
     constexpr int VP = KbLds::vpitch(WP, SZ);
-    constexpr int PITCH = KbLds::mpitch(SZ);
+    constexpr int PITCH = KbLds::mpitch(SZ, MODE);
+    constexpr int SP = KbLds::spitch(WP, SZ, MODE);
+    static_assert(KS == KbLds::ks(SZ), "state slab height");
     extern __shared__ __align__(16) unsigned char smem_raw[];
-    T *VS = reinterpret_cast<T *>(smem_raw);                 // V of the source block
-    T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: Wt, this row block
-    constexpr int SP = KbLds::spitch(SZ);
-    T *SS = MT + (size_t)SBX * PITCH;                         // [WP][SP]: a K-slab of the state
-    float *r_hi = reinterpret_cast<float *>(SS + (size_t)WP * SP);
+    T *VS = reinterpret_cast<T *>(smem_raw);                 // [SBX][VP]: V of the source block
+    T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: the score tile
+    T *SS = MT + KbLds::m_elems(SZ);                          // a K-slab of the state
+    float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
     float *red = r_dt + 256;                                  // [16]
     float *colf = red + 16;                                   // [SBX]: kDx's column decay factors
-    // the position of tile column s in an Wt row (fp32: the fragments take
-    // the K index kk + q + 4 j, stored at kk + 4 q + j)
-    auto mcol = [](int s) -> int {
-        if constexpr (F32)
-            return (s & ~15) | ((s & 3) << 2) | ((s >> 2) & 3);
-        else
-            return s;
-    };
-    auto vat = [](int s, int w) -> int {
-        if constexpr (F32)
-            return s * VP + w;
-        else
-            return w * PITCH + s;
-    };
 
     const int nrb = Q > SBX ? Q / SBX : 1;
-    // (kDx: heads on x, chunk row blocks on y; kDb / kDc the other way round)
-    const int bx = MODE == kDx ? blockIdx.x : blockIdx.y, by = MODE == kDx ? blockIdx.y : blockIdx.x;
-    const int nx = MODE == kDx ? gridDim.x : gridDim.y;
-    const int c = by / nrb, lb = by % nrb;
-    const int b = blockIdx.z;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
+    const int er = r >> 2, ca = 4 * (r & 3);   // (this lane's row and columns in a transposing read)
+    // kDx: x = head, y = (chunk, row block); kDb / kDc: x = (chunk, row
+    // block), y = (group, head group)
+    int bx, c, lb;
+    if constexpr (MODE == kDx) {
+        bx = blockIdx.x;
+        c = blockIdx.y / nrb;
+        lb = blockIdx.y % nrb;
+    } else {
+        bx = blockIdx.y;
+        const int xi = blockIdx.x;
+        if ((nc & 7) == 0) {
+            const int m = xi >> 3;
+            lb = m % nrb;
+            c = (m / nrb) * 8 + (xi & 7);
+        } else {
+            c = xi / nrb;
+            lb = xi % nrb;
+        }
+    }
+    const int nx = MODE == kDx ? gridDim.x : gridDim.y;
+    const int b = blockIdx.z;
     const int SB = Q < SBX ? Q : SBX;
     const int SBK = SB < KS ? KS : SB;       // tile columns the MFMAs read (zeros past SB)
     const bool active = wave * 16 < SB;
     const int W = MODE == kDx ? P : N;       // output width
     const int KD = MODE == kDx ? N : P;      // K of the state product
     const int hpg = H / G;
-    // kDb / kDc: workgroup y = g * nhg + k takes heads k hpw .. of group g
+    // kDb / kDc: y = g * nhg + k takes heads k hpw .. of group g
     const int nhg = MODE == kDx ? 1 : nx / G, hgi = MODE == kDx ? 0 : bx % nhg;
     const int g = MODE == kDx ? bx / hpg : bx / nhg;
     const int h_first = MODE == kDx ? bx : g * hpg + hgi * hpw;
     const int h_count = MODE == kDx ? 1 : min(hpw, hpg - hgi * hpw);
     const int t0 = c * Q + lb * SB;          // the row block's first token
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
+
+    // V's operand for K rows (tokens of the staged block) kk .. and output
+    // columns w0 .. w0 + 15
+    auto vfrag = [&](int kk, int w0) -> frag {
+        if constexpr (F32) {
+            frag v;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) v[j] = VS[(kk + q + 4 * j) * VP + w0 + r];
+            return v;
+        } else {
+            return kb_tr_frag(reinterpret_cast<const bf16 *>(VS), VP, kk + 8 * q + er, w0 + ca);
+        }
+    };
+    // V's rows for source block sb: row sl = token c Q + sb SB + sl of vsrc
+    // (rows rs elements apart), zero past the block, L or W
+    auto stage_v = [&](const T *vsrc, size_t rs, int sb) {
+        const int wv = WP / VEC;
+        for (int v = tid; v < SBK * wv; v += 256) {
+            const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+            frag f = zero_frag<T>();
+            if (sl < SB && ts < L && w0 < W) f = load_frag(vsrc + (size_t)ts * rs + w0);
+            *reinterpret_cast<frag *>(VS + sl * VP + w0) = f;
+        }
+    };
 
     f32x4 tot[NW];
 #pragma unroll
@@ -372,9 +460,8 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
 
         // ---- the state product U_t St, scaled per row.  The state passes
-        // through LDS in K-slabs, as SS[w][k]: for kDx the slab is columns
-        // k0 .. of Lam's rows (a copy), for kDb and kDc rows k0 .. of the
-        // state (a transpose).
+        // through LDS in K-slabs: for kDx the slab's columns of Lam's rows
+        // (SS[w][k]), for kDb and kDc the slab's rows of the state (SS[k][w]).
         f32x4 acc[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[i] = zero4();
@@ -389,21 +476,21 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             __syncthreads();   // (the previous slab is no longer read)
             if constexpr (MODE == kDx) {
                 constexpr int kq = KS / 4;
-                for (int v = tid; v < W * kq; v += 256) {
+                for (int v = tid; v < WP * kq; v += 256) {
                     const int w = v / kq, kr = (v % kq) * 4;
                     f32x4 f = zero4();
-                    if (k0 + kr < KD) f = *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) SS[w * SP + kr + jj] = from_f32<T>(f[jj]);
+                    if (w < W && k0 + kr < KD)
+                        f = *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
+                    kb_store4(SS + w * SP + kr, f);
                 }
             } else {
-                const int wq = W / 4;
+                constexpr int wq = WP / 4;
                 for (int v = tid; v < KS * wq; v += 256) {
                     const int kr = v / wq, w0 = (v % wq) * 4;
                     f32x4 f = zero4();
-                    if (k0 + kr < KD) f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
-#pragma unroll
-                    for (int jj = 0; jj < 4; ++jj) SS[(w0 + jj) * SP + kr] = from_f32<T>(f[jj]);
+                    if (w0 < W && k0 + kr < KD)
+                        f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
+                    kb_store4(SS + kr * SP + w0, f);
                 }
             }
             __syncthreads();
@@ -411,9 +498,15 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
 #pragma unroll
             for (int wt = 0; wt < NW; ++wt) {
-                const int w = wt * 16 + r;
-                frag sb = zero_frag<T>();
-                if (w < W && k < KD) sb = load_frag(SS + w * SP + VEC * q);
+                frag sb;
+                if constexpr (MODE == kDx) {
+                    sb = load_frag(SS + (wt * 16 + r) * SP + VEC * q);
+                } else if constexpr (F32) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) sb[j] = SS[(VEC * q + j) * SP + wt * 16 + r];
+                } else {
+                    sb = kb_tr_frag(reinterpret_cast<const bf16 *>(SS), SP, 8 * q + er, wt * 16 + ca);
+                }
                 acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
             }
         }
@@ -458,20 +551,10 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         }
         if constexpr (MODE == kDx) {
             // ---- the intra-chunk product, source block by source block
+            const T *vsrc = dy + ((size_t)b * L * H + h) * P;
             for (int sb = lb; sb < nrb; ++sb) {
                 __syncthreads();   // (the previous block's V and Wt are no longer read)
-                const int wv = WP / VEC;
-                for (int v = tid; v < SBK * wv; v += 256) {
-                    const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
-                    frag f = zero_frag<T>();
-                    if (sl < SB && ts < L && w0 < W) f = load_frag(dy + (((size_t)b * L + ts) * H + h) * P + w0);
-                    if constexpr (F32) {
-                        *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
-                    }
-                }
+                stage_v(vsrc, (size_t)H * P, sb);
                 if (sb > lb && tid < SB) {
                     // below the diagonal the decay factors through the row
                     // block's last row te: e^(acum_s - acum_t) =
@@ -483,22 +566,22 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                 if (active) {
                     // lane: row tl = lane % 16, columns 16 (lane / 16) + j
                     const int tl = wave * 16 + r, lt = lb * SB + tl;
+                    float m[16];
                     if (sb > lb) {
                         const int te = lb * SB + SB - 1;
                         const float rowf = fast_exp(prefix_diff(r_hi[te], r_lo[te], r_hi[lt], r_lo[lt]));
-                        float cv[16];
 #pragma unroll
                         for (int j = 0; j < 16; ++j) {
                             const int sl = q * 16 + j;
-                            cv[j] = sl < SB ? cb[(cbase + sb * SB + sl) * Q + lt] : 0.f;
+                            m[j] = sl < SB ? cb[(cbase + sb * SB + sl) * Q + lt] : 0.f;
                         }
 #pragma unroll
                         for (int j = 0; j < 16; ++j) {
                             const int sl = q * 16 + j;
-                            MT[tl * PITCH + mcol(sl)] = from_f32<T>(sl < SB ? cv[j] * rowf * colf[sl] : 0.f);
+                            m[j] = sl < SB ? m[j] * rowf * colf[sl] : 0.f;
                         }
                     } else {
-#pragma unroll 4
+#pragma unroll
                         for (int j = 0; j < 16; ++j) {
                             const int sl = q * 16 + j;
                             const int ls = sb * SB + sl;
@@ -506,31 +589,27 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                             if (sl < SB && ls >= lt)
                                 v = cb[(cbase + ls) * Q + lt] *
                                     fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
-                            MT[tl * PITCH + mcol(sl)] = from_f32<T>(v);
+                            m[j] = v;
                         }
                     }
-                    if (SBK > SB) {   // (bf16 chunks of 16: zero columns SB .. SBK - 1)
-                        for (int j = 0; j < 16; ++j) {
-                            const int sl = SB + q * 16 + j;
-                            if (sl < SBK) MT[(wave * 16 + r) * PITCH + mcol(sl)] = from_f32<T>(0.f);
-                        }
+                    // the lane's 16 columns (zero past SB: they cover the
+                    // padded K of a bf16 block of 16) in two or four stores;
+                    // fp32 places column 16 q + 4 i + j at 16 q + 4 j + i
+                    T *mrow = MT + tl * PITCH + 16 * q;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if constexpr (F32)
+                            kb_store4(mrow + 4 * j, f32x4{m[j], m[4 + j], m[8 + j], m[12 + j]});
+                        else
+                            kb_store4(mrow + 4 * j, f32x4{m[4 * j], m[4 * j + 1], m[4 * j + 2], m[4 * j + 3]});
                     }
                 }
                 __syncthreads();
                 if (!active) continue;
                 for (int kk = 0; kk < SBK; kk += KS) {
-                    const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
+                    const frag mf = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
 #pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) {
-                        frag vb;
-                        if constexpr (F32) {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
-                        } else {
-                            vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
-                        }
-                        acc[wt] = Mma<T>::mma(m, vb, acc[wt]);
-                    }
+                    for (int wt = 0; wt < NW; ++wt) acc[wt] = Mma<T>::mma(mf, vfrag(kk, wt * 16), acc[wt]);
                 }
             }
             // ---- the head's epilogue: dx, x . u, dD
@@ -576,56 +655,46 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         // sb <= lb; dB rows lb x Ws[sb][lb]^T C[sb], sb >= lb
         if (hgi == 0) {
             const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
+            const T *vsrc = (MODE == kDb ? Cm : Bm) + ((size_t)b * L * G + g) * N;
             for (int sb = sb_lo; sb <= sb_hi; ++sb) {
-                __syncthreads();   // (the previous block's V and Wt are no longer read)
-                const int wv = WP / VEC;
-                for (int v = tid; v < SBK * wv; v += 256) {
-                    const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
-                    frag f = zero_frag<T>();
-                    if (sl < SB && ts < L && w0 < W)
-                        f = load_frag((MODE == kDb ? Cm : Bm) + (((size_t)b * L + ts) * G + g) * N + w0);
-                    if constexpr (F32) {
-                        *reinterpret_cast<frag *>(VS + vat(sl, w0)) = f;
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < VEC; ++j) VS[vat(sl, w0 + j)] = f[j];
-                    }
-                }
-                if (active) {
-                    // lane: row tl = lane % 16, columns 16 (lane / 16) + j
-#pragma unroll 4
-                    for (int j = 0; j < 16; ++j) {
-                        const int tl = wave * 16 + r, sl = q * 16 + j;
-                        const int lt = lb * SB + tl, ls = sb * SB + sl;
-                        T v = from_f32<T>(0.f);
-                        if (sl < SB) {
-                            if (MODE == kDc && ls <= lt) v = wsm[(cbase + lt) * Q + ls];
-                            if (MODE == kDb && ls >= lt) v = wsm[(cbase + ls) * Q + lt];
-                        }
-                        MT[tl * PITCH + mcol(sl)] = v;
-                    }
-                    if (SBK > SB) {
-                        for (int j = 0; j < 16; ++j) {
-                            const int sl = SB + q * 16 + j;
-                            if (sl < SBK) MT[(wave * 16 + r) * PITCH + mcol(sl)] = from_f32<T>(0.f);
-                        }
+                __syncthreads();   // (the previous block's V and tile are no longer read)
+                stage_v(vsrc, (size_t)G * N, sb);
+                {
+                    // the tile as stored (its upper triangle on the diagonal
+                    // is zero): kDc rows t of this block and columns s of
+                    // block sb, kDb rows s of block sb and columns t
+                    const int r0 = MODE == kDc ? lb * SB : sb * SB, c0 = MODE == kDc ? sb * SB : lb * SB;
+                    const int mv = SBK / VEC;
+                    for (int v = tid; v < SBK * mv; v += 256) {
+                        const int i = v / mv, j = (v % mv) * VEC;
+                        frag f = zero_frag<T>();
+                        if (i < SB && j < SB) f = load_frag(wsm + (cbase + r0 + i) * Q + c0 + j);
+                        *reinterpret_cast<frag *>(MT + i * PITCH + j) = f;
                     }
                 }
                 __syncthreads();
                 if (!active) continue;
                 for (int kk = 0; kk < SBK; kk += KS) {
-                    const frag m = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) {
-                        frag vb;
+                    // A: rows t (this wave's 16), K = s
+                    frag mf;
+                    if constexpr (MODE == kDc) {
                         if constexpr (F32) {
 #pragma unroll
-                            for (int j = 0; j < 4; ++j) vb[j] = VS[vat(kk + q + 4 * j, wt * 16 + r)];
+                            for (int j = 0; j < 4; ++j) mf[j] = MT[(wave * 16 + r) * PITCH + kk + q + 4 * j];
                         } else {
-                            vb = load_frag(VS + vat(kk + VEC * q, wt * 16 + r));
+                            mf = load_frag(MT + (wave * 16 + r) * PITCH + kk + 8 * q);
                         }
-                        tot[wt] = Mma<T>::mma(m, vb, tot[wt]);
+                    } else {
+                        if constexpr (F32) {
+#pragma unroll
+                            for (int j = 0; j < 4; ++j) mf[j] = MT[(kk + q + 4 * j) * PITCH + wave * 16 + r];
+                        } else {
+                            mf = kb_tr_frag(reinterpret_cast<const bf16 *>(MT), PITCH, kk + 8 * q + er,
+                                            wave * 16 + ca);
+                        }
                     }
+#pragma unroll
+                    for (int wt = 0; wt < NW; ++wt) tot[wt] = Mma<T>::mma(mf, vfrag(kk, wt * 16), tot[wt]);
                 }
             }
         }
