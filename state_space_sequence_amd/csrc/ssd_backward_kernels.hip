@@ -252,33 +252,27 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
 }
 
 // ------------------------------------------------------------ intra-chunk gradients
-// One kernel, three products (MODE):
-//   kDx: rows t of head h, columns p:  u_t  (then dx_t, x_t . u_t, dD partials)
+// The gradient products with the state and within the chunk.  dx has its
+// own kernel (kb_dx); dB and dC share one (kb_mix, MODE):
 //   kDb: rows t of group g, columns n: dB_t, summed over the group's heads
 //   kDc: rows t of group g, columns n: dC_t, summed over the group's heads
 // Each is   out_t = sum_heads rowscale_t stscale_t U_t St  +  sum_s Wt[t][s] V_s:
-//            U (K)        St [K x W]        Wt[t][s]                            V
-//   kDx:   B_t (N)      Lam^T            (C_s . B_t) e^(acum_s - acum_t), s >= t     dy_s
-//   kDb:   x_t (P)      Lam              Ws[s][t], s >= t                            C_s
-//   kDc:   dy_t (P)     h_in             Ws[t][s], s <= t                            B_s
-// with stscale e^(acum_end - acum_t) (kDx, kDb) or e^(acum_t) (kDc), and
-// rowscale dt_t for kDb (kDx applies dt_t in its epilogue).  C_s . B_t comes
-// from the forward's C B^T blocks (its lower triangle, row s >= column t),
-// Ws from kb_wsum.  kDx also writes x_t . (its state part), kDc <dy_t, its
-// state part> per head.
+//            U (K)        St [K x W]        Wt[t][s]                 V
+//   kDb:   x_t (P)      Lam              Ws[s][t], s >= t           C_s
+//   kDc:   dy_t (P)     h_in             Ws[t][s], s <= t           B_s
+// with stscale e^(acum_end - acum_t) (kDb) or e^(acum_t) (kDc), rowscale
+// dt_t for kDb, and Ws from kb_wsum.  kDc also writes <dy_t, its state
+// part> per head.
 //
-// grid (H, nc * nrb, b) for kDx (heads fastest, so that the workgroups
-// running together share a chunk's C B^T in L2) and (nc * nrb, G * nhg, b)
-// for kDb and kDc, 256 threads (4 waves), dynamic LDS KbLds::bytes.
-// Workgroup (c, lb) owns the SB = min(Q, 64) rows of row block lb; wave w
-// the 16 rows 16 w .. 16 w + 15; NW 16-column tiles span the output width W
-// (P or N, padded; padded columns are never stored).  kDb / kDc split a
-// group's heads over nhg workgroups for the state products (fp32 partial
+// grid (nc * nrb, G * nhg, b), 256 threads (4 waves), dynamic LDS
+// KbLds::bytes.  Workgroup (c, lb) owns the SB = min(Q, 64) rows of row
+// block lb; wave w the 16 rows 16 w .. 16 w + 15; NW 16-column tiles span
+// the output width N (padded; padded columns are never stored).  A group's
+// heads are split over nhg workgroups for the state products (fp32 partial
 // sums, added up afterwards); the first of them also takes the intra-chunk
-// product.  Workgroups are dealt to the 8 XCDs in turn; kDb / kDc place the
-// row blocks of a chunk, which read the same states, 8 apart, so that they
-// share an L2 (when nc is a multiple of 8).  (For kDx, with H a multiple of
-// 8, the heads-fastest order already does that.)
+// product.  Workgroups are dealt to the 8 XCDs in turn; the row blocks of a
+// chunk, which read the same states, are placed 8 apart so that they share
+// an L2 (when nc is a multiple of 8).
 //
 // LDS operands keep the layout they arrive in (rows of tokens, of the state
 // or of the score tile) and are read across rows where the MFMA wants
@@ -296,16 +290,17 @@ struct KbLds {
     static __host__ __device__ constexpr size_t v_elems(int WP, int sz) {
         return (size_t)kSB * vpitch(WP, sz);
     }
-    // + the score tile: [kSB][mpitch] (fp32 kDx and kDc rows = 4 mod 64
-    // floats, kDb rows = 16 mod 64; bf16 8 elements of padding)
+    // + the score tile: [kSB][mpitch] (fp32: kDc's rows, read along them,
+    // = 4 mod 64 floats; kDb's and kb_dx's, read across them, = 16 mod 64;
+    // bf16: 8 elements of padding)
     static __host__ __device__ constexpr int mpitch(int sz, int mode) {
-        return sz == 4 ? (mode == kDb ? kSB + 16 : kSB + 4) : kSB + 8;
+        return sz == 4 ? (mode == kDc ? kSB + 4 : kSB + 16) : kSB + 8;
     }
     static __host__ __device__ constexpr size_t m_elems(int sz) {
         return (size_t)kSB * (sz == 4 ? kSB + 16 : kSB + 8);
     }
-    // + a K-slab of the state: kDx [WP][ks + 16 / sz] (Lam's rows cut to the
-    // slab's columns), kDb / kDc [ks][WP + 16 / sz] (the slab's rows)
+    // + a K-slab of the state: kb_dx [WP][ks + 16 / sz] (Lam's rows cut to
+    // the slab's columns), kDb / kDc [ks][WP + 16 / sz] (the slab's rows)
     static __host__ __device__ constexpr int ks(int sz) { return sz == 4 ? 16 : 32; }
     static __host__ __device__ constexpr int spitch(int WP, int sz, int mode) {
         return mode == kDx ? ks(sz) + 16 / sz : WP + 16 / sz;
@@ -315,10 +310,9 @@ struct KbLds {
                    ? (size_t)WP * spitch(WP, sz, kDx)
                    : (size_t)ks(sz) * spitch(WP, sz, kDb);
     }
-    // + prefix sums and dt by token, a reduction slot per wave and a decay
-    // factor per source column (fp32)
+    // + prefix sums and dt by token and a reduction slot per wave (fp32)
     static size_t bytes(int WP, int sz) {
-        return (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64 + kSB * 4;
+        return (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64;
     }
 };
 
@@ -350,16 +344,250 @@ __device__ __forceinline__ void kb_store4(T *dst, f32x4 f) {
     }
 }
 
+// The MFMA operand of a row-major LDS tile read across its rows: K rows
+// kk .. (fp32: kk + q + 4 j; bf16: kk + 8 q ..) and columns c0 + r.
+template <typename T, int PITCH>
+__device__ __forceinline__ typename Mma<T>::frag kb_across(const T *tile, int kk, int c0, int r,
+                                                           int q) {
+    if constexpr (sizeof(T) == 4) {
+        typename Mma<T>::frag v;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) v[j] = tile[(kk + q + 4 * j) * PITCH + c0 + r];
+        return v;
+    } else {
+        return kb_tr_frag(reinterpret_cast<const bf16 *>(tile), PITCH, kk + 8 * q + (r >> 2),
+                          c0 + 4 * (r & 3));
+    }
+}
+
+// dy (or C, B) rows of source block sb into VS: row sl = token
+// c Q + sb SB + sl of vsrc (rows rs elements apart), zero past the block, L
+// or the width W; SBK rows of WP columns, 256 threads.
+template <typename T, int WP, int VP>
+__device__ __forceinline__ void kb_stage_rows(T *VS, const T *vsrc, size_t rs, int c, int Q,
+                                              int sb, int SB, int SBK, int L, int W) {
+    constexpr int VEC = Mma<T>::VEC, wv = WP / VEC;
+    for (int v = threadIdx.x; v < SBK * wv; v += 256) {
+        const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+        typename Mma<T>::frag f = zero_frag<T>();
+        if (sl < SB && ts < L && w0 < W) f = load_frag(vsrc + (size_t)ts * rs + w0);
+        *reinterpret_cast<typename Mma<T>::frag *>(VS + sl * VP + w0) = f;
+    }
+}
+
+// ------------------------------------------------------------ dx
+// u_t for the SB rows of row block lb of chunk c, head h, and from it dx_t,
+// x_t . u_t, the state part x_t . (e^(acum_end - acum_t) Lam B_t) and the
+// partial sum of dy . x.  With te the row block's last row, every decay
+// that the rows take from beyond te factors through it (A <= 0: each
+// factor is at most 1):
+//   u_t = f_t [ B_t (e^(acum_end - acum_te) Lam)^T
+//               + sum_{s beyond the block} (C_s . B_t) e^(acum_s - acum_te) dy_s ]
+//         + sum_{s in the block, s >= t} (C_s . B_t) e^(acum_s - acum_t) dy_s,
+//   f_t = e^(acum_te - acum_t),
+// so only the diagonal block takes an exponential per entry.
+//
+// grid (H, nc * nrb, b) (heads fastest: the workgroups running together
+// share a chunk's C B^T in L2, and with H a multiple of 8 a head's row
+// blocks share an XCD), 256 threads, dynamic LDS KbLds::bytes(16 NW).  Wave
+// w owns rows 16 w ..; NW 16-column tiles span P.  The source blocks run
+// from the chunk's last down to the diagonal one, which leaves dy of the
+// row block itself staged for the epilogue.  The weighted C B^T block is
+// staged by source rows s (as it is stored) and read across them.
+template <typename T, int NW>
+__global__ void __launch_bounds__(256)
+kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ dy,
+      const float *__restrict__ cb, const float *__restrict__ adj,
+      const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
+      const float *__restrict__ dtT, const float *__restrict__ D, T *__restrict__ out,
+      float *__restrict__ dint, float *__restrict__ dd, float *__restrict__ dDpart, int L,
+      int H, int G, int P, int N, int nc, int Q) {
+    typedef typename Mma<T>::frag frag;
+    constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
+    constexpr int SZ = (int)sizeof(T);
+    constexpr int SBX = KbLds::kSB;
+    constexpr int WP = 16 * NW;
+    constexpr int VP = KbLds::vpitch(WP, SZ);
+    constexpr int PITCH = KbLds::mpitch(SZ, kDx);
+    constexpr int SP = KbLds::spitch(WP, SZ, kDx);
+    static_assert(KS == KbLds::ks(SZ), "state slab width");
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *VS = reinterpret_cast<T *>(smem_raw);            // [SBX][VP]: dy of the source block
+    T *MT = VS + KbLds::v_elems(WP, SZ);                 // [SBX][PITCH]: weighted C B^T, rows s
+    T *SS = MT + KbLds::m_elems(SZ);                     // [WP][SP]: a K-slab of Lam's rows
+    float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
+    float *r_lo = r_hi + 256;
+    float *r_dt = r_lo + 256;
+    float *red = r_dt + 256;                             // [4]
+
+    const int nrb = Q > SBX ? Q / SBX : 1;
+    const int h = blockIdx.x, c = blockIdx.y / nrb, lb = blockIdx.y % nrb, b = blockIdx.z;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
+    const int r = lane & 15, q = lane >> 4;
+    const int SB = Q < SBX ? Q : SBX;
+    const int SBK = SB < KS ? KS : SB;       // rows the MFMAs read (zeros past SB)
+    const bool active = wave * 16 < SB;
+    const int g = h / (H / G);
+    const int te = lb * SB + SB - 1;         // the row block's last row in the chunk
+    const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;   // prefix sums, dt
+    const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
+
+    for (int l = tid; l < Q; l += 256) {
+        r_hi[l] = acum_hi[vbase + l];
+        r_lo[l] = acum_lo[vbase + l];
+        r_dt[l] = dtT[vbase + l];
+    }
+    // x at this lane's output positions (rows 4 q + i of the wave's 16,
+    // columns 16 wt + r)
+    float xv[4][NW];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+        const bool tin = active && t < L && l < Q;
+#pragma unroll
+        for (int wt = 0; wt < NW; ++wt) {
+            const int p = wt * 16 + r;
+            xv[i][wt] = tin && p < P ? to_f32(x[(((size_t)b * L + t) * H + h) * P + p]) : 0.f;
+        }
+    }
+    __syncthreads();
+    const float e_te = fast_exp(prefix_diff(r_hi[Q - 1], r_lo[Q - 1], r_hi[te], r_lo[te]));
+    float rowf[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int l = min(lb * SB + wave * 16 + 4 * q + i, te);
+        rowf[i] = fast_exp(prefix_diff(r_hi[te], r_lo[te], r_hi[l], r_lo[l]));
+    }
+
+    // ---- the state product B_t (e^(acum_end - acum_te) Lam)^T; Lam passes
+    // through LDS in K-slabs of its rows' columns (SS[p][k])
+    f32x4 acc[NW];
+#pragma unroll
+    for (int i = 0; i < NW; ++i) acc[i] = zero4();
+    const float *st = adj + ((size_t)(b * nc + c) * H + h) * P * N;
+    const int tr = c * Q + lb * SB + wave * 16 + r;   // this lane's B row
+    const T *urow = Bm + (((size_t)b * L + tr) * G + g) * N;
+    for (int k0 = 0; k0 < N; k0 += KS) {
+        const int k = k0 + VEC * q;
+        __syncthreads();   // (the previous slab is no longer read)
+        constexpr int kq = KS / 4;
+        for (int v = tid; v < WP * kq; v += 256) {
+            const int w = v / kq, kr = (v % kq) * 4;
+            f32x4 f = zero4();
+            if (w < P && k0 + kr < N)
+                f = e_te * *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
+            kb_store4(SS + w * SP + kr, f);
+        }
+        __syncthreads();
+        if (!active) continue;
+        const frag ua = tr < L && k < N ? load_frag(urow + k) : zero_frag<T>();
+#pragma unroll
+        for (int wt = 0; wt < NW; ++wt)
+            acc[wt] = Mma<T>::mma(ua, load_frag(SS + (wt * 16 + r) * SP + VEC * q), acc[wt]);
+    }
+    if (active) {
+        // the state part of x . u, per row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+            float v = 0.f;
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) v += xv[i][wt] * acc[wt][i];
+            v = row16_sum(v) * rowf[i];
+            if (r == 0 && l < Q) dint[vbase + l] = t < L ? v : 0.f;
+        }
+    }
+
+    // ---- the intra-chunk product, from the chunk's last source block down
+    // to the diagonal one
+    const T *vsrc = dy + ((size_t)b * L * H + h) * P;
+    for (int sb = nrb - 1; sb >= lb; --sb) {
+        __syncthreads();   // (the previous block's operands are no longer read)
+        kb_stage_rows<T, WP, VP>(VS, vsrc, (size_t)H * P, c, Q, sb, SB, SBK, L, P);
+        // MT[s][t] = (C_s . B_t) e^(acum_s - acum_te) beyond the block,
+        // (C_s . B_t) e^(acum_s - acum_t) for s >= t in it (the upper
+        // triangle, which the forward leaves unwritten, is selected away)
+        const int mq = SBK / 4;
+        for (int v = tid; v < SBK * mq; v += 256) {
+            const int sl = v / mq, tl = (v % mq) * 4;
+            f32x4 f = zero4();
+            if (sl < SB && tl < SB) {
+                const int ls = sb * SB + sl, lt0 = lb * SB + tl;
+                const f32x4 cv = *reinterpret_cast<const f32x4 *>(cb + (cbase + ls) * Q + lt0);
+                const float shi = r_hi[ls], slo = r_lo[ls];
+                if (sb > lb) {
+                    f = cv * fast_exp(prefix_diff(shi, slo, r_hi[te], r_lo[te]));
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int lt = lt0 + j;
+                        const float e = fast_exp(fminf(prefix_diff(shi, slo, r_hi[lt], r_lo[lt]), 0.f));
+                        f[j] = ls >= lt ? cv[j] * e : 0.f;
+                    }
+                }
+            }
+            kb_store4(MT + sl * PITCH + tl, f);
+        }
+        __syncthreads();
+        if (!active) continue;
+        if (sb == lb) {
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt)
+#pragma unroll
+                for (int i = 0; i < 4; ++i) acc[wt][i] *= rowf[i];
+        }
+        for (int kk = 0; kk < SBK; kk += KS) {
+            const frag mf = kb_across<T, PITCH>(MT, kk, wave * 16, r, q);
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt)
+                acc[wt] = Mma<T>::mma(mf, kb_across<T, VP>(VS, kk, wt * 16, r, q), acc[wt]);
+        }
+    }
+
+    // ---- the epilogue: dx, x . u, dD (dy from the staged diagonal block)
+    if (active) {
+        const float Dh = D ? D[h] : 0.f;
+        float dsum = 0.f;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl, t = c * Q + l;
+            const bool tin = t < L && l < Q;
+            const float dtl = r_dt[l];
+            const size_t ro = (((size_t)b * L + t) * H + h) * P;
+            float ds = 0.f;
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) {
+                const int p = wt * 16 + r;
+                const float gv = to_f32(VS[sl * VP + p]), u = acc[wt][i];
+                ds += xv[i][wt] * u;
+                dsum += gv * xv[i][wt];
+                if (tin && p < P) out[ro + p] = from_f32<T>(Dh * gv + dtl * u);
+            }
+            ds = row16_sum(ds);
+            if (r == 0 && l < Q) dd[vbase + l] = tin ? ds : 0.f;
+        }
+        dsum = wave_sum(dsum);
+        if (lane == 0) red[wave] = dsum;
+    }
+    __syncthreads();
+    if (tid == 0) {
+        float sdd = 0.f;
+        for (int w = 0; w < 4; ++w)
+            if (w * 16 < SB) sdd += red[w];
+        dDpart[((size_t)(b * nc + c) * H + h) * nrb + lb] = sdd;
+    }
+}
+
+// ------------------------------------------------------------ dB and dC
 template <typename T, int MODE, int NW>
 __global__ void __launch_bounds__(256)
 kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ Cm,
-       const T *__restrict__ dy, const float *__restrict__ cb, const T *__restrict__ wsm,
-       const float *__restrict__ S, const float *__restrict__ adj,
-       const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
-       const float *__restrict__ dtT, const float *__restrict__ D, T *__restrict__ out,
-       float *__restrict__ roff, float *__restrict__ dint, float *__restrict__ dd,
-       float *__restrict__ dDpart, float *__restrict__ part, int L, int H, int G, int P,
-       int N, int nc, int Q, int hpw) {
+       const T *__restrict__ dy, const T *__restrict__ wsm, const float *__restrict__ S,
+       const float *__restrict__ adj, const float *__restrict__ acum_hi,
+       const float *__restrict__ acum_lo, const float *__restrict__ dtT, T *__restrict__ out,
+       float *__restrict__ roff, float *__restrict__ part, int L, int H, int G, int P, int N,
+       int nc, int Q, int hpw) {
+    static_assert(MODE == kDb || MODE == kDc, "dB or dC");
     typedef typename Mma<T>::frag frag;
     constexpr int VEC = Mma<T>::VEC, KS = Mma<T>::KS;
     constexpr int SZ = (int)sizeof(T);
@@ -373,26 +601,17 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *VS = reinterpret_cast<T *>(smem_raw);                 // [SBX][VP]: V of the source block
     T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: the score tile
-    T *SS = MT + KbLds::m_elems(SZ);                          // a K-slab of the state
+    T *SS = MT + KbLds::m_elems(SZ);                          // [KS][SP]: a K-slab of the state
     float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
-    float *red = r_dt + 256;                                  // [16]
-    float *colf = red + 16;                                   // [SBX]: kDx's column decay factors
 
     const int nrb = Q > SBX ? Q / SBX : 1;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int r = lane & 15, q = lane >> 4;
-    const int er = r >> 2, ca = 4 * (r & 3);   // (this lane's row and columns in a transposing read)
-    // kDx: x = head, y = (chunk, row block); kDb / kDc: x = (chunk, row
-    // block), y = (group, head group)
-    int bx, c, lb;
-    if constexpr (MODE == kDx) {
-        bx = blockIdx.x;
-        c = blockIdx.y / nrb;
-        lb = blockIdx.y % nrb;
-    } else {
-        bx = blockIdx.y;
+    // x = (chunk, row block), y = (group, head group)
+    int c, lb;
+    {
         const int xi = blockIdx.x;
         if ((nc & 7) == 0) {
             const int m = xi >> 3;
@@ -403,49 +622,38 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             lb = xi % nrb;
         }
     }
-    const int nx = MODE == kDx ? gridDim.x : gridDim.y;
     const int b = blockIdx.z;
     const int SB = Q < SBX ? Q : SBX;
     const int SBK = SB < KS ? KS : SB;       // tile columns the MFMAs read (zeros past SB)
     const bool active = wave * 16 < SB;
-    const int W = MODE == kDx ? P : N;       // output width
-    const int KD = MODE == kDx ? N : P;      // K of the state product
     const int hpg = H / G;
-    // kDb / kDc: y = g * nhg + k takes heads k hpw .. of group g
-    const int nhg = MODE == kDx ? 1 : nx / G, hgi = MODE == kDx ? 0 : bx % nhg;
-    const int g = MODE == kDx ? bx / hpg : bx / nhg;
-    const int h_first = MODE == kDx ? bx : g * hpg + hgi * hpw;
-    const int h_count = MODE == kDx ? 1 : min(hpw, hpg - hgi * hpw);
+    // y = g * nhg + k takes heads k hpw .. of group g
+    const int nhg = gridDim.y / G, hgi = blockIdx.y % nhg, g = blockIdx.y / nhg;
+    const int h_first = g * hpg + hgi * hpw;
+    const int h_count = min(hpw, hpg - hgi * hpw);
     const int t0 = c * Q + lb * SB;          // the row block's first token
     const size_t cbase = ((size_t)(b * nc + c) * G + g) * Q;
-
-    // V's operand for K rows (tokens of the staged block) kk .. and output
-    // columns w0 .. w0 + 15
-    auto vfrag = [&](int kk, int w0) -> frag {
-        if constexpr (F32) {
-            frag v;
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[j] = VS[(kk + q + 4 * j) * VP + w0 + r];
-            return v;
-        } else {
-            return kb_tr_frag(reinterpret_cast<const bf16 *>(VS), VP, kk + 8 * q + er, w0 + ca);
-        }
-    };
-    // V's rows for source block sb: row sl = token c Q + sb SB + sl of vsrc
-    // (rows rs elements apart), zero past the block, L or W
-    auto stage_v = [&](const T *vsrc, size_t rs, int sb) {
-        const int wv = WP / VEC;
-        for (int v = tid; v < SBK * wv; v += 256) {
-            const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
-            frag f = zero_frag<T>();
-            if (sl < SB && ts < L && w0 < W) f = load_frag(vsrc + (size_t)ts * rs + w0);
-            *reinterpret_cast<frag *>(VS + sl * VP + w0) = f;
-        }
-    };
 
     f32x4 tot[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot[i] = zero4();
+    // kDc: C at this lane's output positions (rows 4 q + i of the wave's 16,
+    // columns 16 wt + r), the same for every head of the group, held in
+    // registers up to 128 columns
+    constexpr bool CREG = MODE == kDc && NW <= 8;
+    T cpos[CREG ? NW : 1][4];
+    if constexpr (CREG) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+            const bool tin = active && t < L && l < Q;
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) {
+                const int w = wt * 16 + r;
+                cpos[wt][i] = tin && w < N ? Cm[(((size_t)b * L + t) * G + g) * N + w] : from_f32<T>(0.f);
+            }
+        }
+    }
 
     for (int hh = 0; hh < h_count; ++hh) {
         const int h = h_first + hh;
@@ -460,52 +668,35 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
 
         // ---- the state product U_t St, scaled per row.  The state passes
-        // through LDS in K-slabs: for kDx the slab's columns of Lam's rows
-        // (SS[w][k]), for kDb and kDc the slab's rows of the state (SS[k][w]).
+        // through LDS in K-slabs of its rows (SS[k][n]).
         f32x4 acc[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[i] = zero4();
-        const float *st = MODE == kDc ? S + ((size_t)(b * nc + c) * H + h) * P * N
-                                      : adj + ((size_t)(b * nc + c) * H + h) * P * N;
+        const float *st = (MODE == kDc ? S : adj) + ((size_t)(b * nc + c) * H + h) * P * N;
         const int tr = t0 + wave * 16 + r;   // this lane's U row
-        const T *urow = MODE == kDx ? Bm + (((size_t)b * L + tr) * G + g) * N
-                      : MODE == kDb ? x + (((size_t)b * L + tr) * H + h) * P
-                                    : dy + (((size_t)b * L + tr) * H + h) * P;
-        for (int k0 = 0; k0 < KD; k0 += KS) {
+        const T *urow = (MODE == kDb ? x : dy) + (((size_t)b * L + tr) * H + h) * P;
+        for (int k0 = 0; k0 < P; k0 += KS) {
             const int k = k0 + VEC * q;
             __syncthreads();   // (the previous slab is no longer read)
-            if constexpr (MODE == kDx) {
-                constexpr int kq = KS / 4;
-                for (int v = tid; v < WP * kq; v += 256) {
-                    const int w = v / kq, kr = (v % kq) * 4;
-                    f32x4 f = zero4();
-                    if (w < W && k0 + kr < KD)
-                        f = *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
-                    kb_store4(SS + w * SP + kr, f);
-                }
-            } else {
-                constexpr int wq = WP / 4;
-                for (int v = tid; v < KS * wq; v += 256) {
-                    const int kr = v / wq, w0 = (v % wq) * 4;
-                    f32x4 f = zero4();
-                    if (w0 < W && k0 + kr < KD)
-                        f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
-                    kb_store4(SS + kr * SP + w0, f);
-                }
+            constexpr int wq = WP / 4;
+            for (int v = tid; v < KS * wq; v += 256) {
+                const int kr = v / wq, w0 = (v % wq) * 4;
+                f32x4 f = zero4();
+                if (w0 < N && k0 + kr < P)
+                    f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
+                kb_store4(SS + kr * SP + w0, f);
             }
             __syncthreads();
             if (!active) continue;
-            const frag ua = tr < L && k < KD ? load_frag(urow + k) : zero_frag<T>();
+            const frag ua = tr < L && k < P ? load_frag(urow + k) : zero_frag<T>();
 #pragma unroll
             for (int wt = 0; wt < NW; ++wt) {
                 frag sb;
-                if constexpr (MODE == kDx) {
-                    sb = load_frag(SS + (wt * 16 + r) * SP + VEC * q);
-                } else if constexpr (F32) {
+                if constexpr (F32) {
 #pragma unroll
                     for (int j = 0; j < 4; ++j) sb[j] = SS[(VEC * q + j) * SP + wt * 16 + r];
                 } else {
-                    sb = kb_tr_frag(reinterpret_cast<const bf16 *>(SS), SP, 8 * q + er, wt * 16 + ca);
+                    sb = kb_across<T, SP>(SS, 0, wt * 16, r, q);
                 }
                 acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
             }
@@ -519,8 +710,8 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
 #pragma unroll
                 for (int wt = 0; wt < NW; ++wt) acc[wt][i] *= e;
             }
-            // the state part of x . u (kDx) or of <dy, y - D x> (kDc), per row
-            if constexpr (MODE != kDb) {
+            if constexpr (MODE == kDc) {
+                // the state part of <dy, y - D x>, per row
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
@@ -529,192 +720,87 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
 #pragma unroll
                     for (int wt = 0; wt < NW; ++wt) {
                         const int w = wt * 16 + r;
-                        if (!tin || w >= W) continue;
-                        const T *o = MODE == kDx ? x + (((size_t)b * L + t) * H + h) * P
-                                                 : Cm + (((size_t)b * L + t) * G + g) * N;
-                        v += to_f32(o[w]) * acc[wt][i];
+                        if constexpr (CREG) {
+                            v += to_f32(cpos[wt][i]) * acc[wt][i];
+                        } else {
+                            if (!tin || w >= N) continue;
+                            v += to_f32(Cm[(((size_t)b * L + t) * G + g) * N + w]) * acc[wt][i];
+                        }
                     }
                     v = row16_sum(v);
-                    if (r == 0 && l < Q) (MODE == kDx ? dint : roff)[vbase + l] = tin ? v : 0.f;
+                    if (r == 0 && l < Q) roff[vbase + l] = tin ? v : 0.f;
                 }
             }
-            if constexpr (MODE != kDx) {
-                // the head's state product into the group's sum (dB: times dt_t)
+            // the head's state product into the group's sum (dB: times dt_t)
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int l = lb * SB + wave * 16 + 4 * q + i;
-                    const float sc = MODE == kDb ? r_dt[l] : 1.f;
+            for (int i = 0; i < 4; ++i) {
+                const int l = lb * SB + wave * 16 + 4 * q + i;
+                const float sc = MODE == kDb ? r_dt[l] : 1.f;
 #pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) tot[wt][i] += sc * acc[wt][i];
-                }
-            }
-        }
-        if constexpr (MODE == kDx) {
-            // ---- the intra-chunk product, source block by source block
-            const T *vsrc = dy + ((size_t)b * L * H + h) * P;
-            for (int sb = lb; sb < nrb; ++sb) {
-                __syncthreads();   // (the previous block's V and Wt are no longer read)
-                stage_v(vsrc, (size_t)H * P, sb);
-                if (sb > lb && tid < SB) {
-                    // below the diagonal the decay factors through the row
-                    // block's last row te: e^(acum_s - acum_t) =
-                    // e^(acum_s - acum_te) e^(acum_te - acum_t), both <= 1
-                    const int te = lb * SB + SB - 1, ls = sb * SB + tid;
-                    colf[tid] = fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[te], r_lo[te]));
-                }
-                __syncthreads();
-                if (active) {
-                    // lane: row tl = lane % 16, columns 16 (lane / 16) + j
-                    const int tl = wave * 16 + r, lt = lb * SB + tl;
-                    float m[16];
-                    if (sb > lb) {
-                        const int te = lb * SB + SB - 1;
-                        const float rowf = fast_exp(prefix_diff(r_hi[te], r_lo[te], r_hi[lt], r_lo[lt]));
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int sl = q * 16 + j;
-                            m[j] = sl < SB ? cb[(cbase + sb * SB + sl) * Q + lt] : 0.f;
-                        }
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int sl = q * 16 + j;
-                            m[j] = sl < SB ? m[j] * rowf * colf[sl] : 0.f;
-                        }
-                    } else {
-#pragma unroll
-                        for (int j = 0; j < 16; ++j) {
-                            const int sl = q * 16 + j;
-                            const int ls = sb * SB + sl;
-                            float v = 0.f;
-                            if (sl < SB && ls >= lt)
-                                v = cb[(cbase + ls) * Q + lt] *
-                                    fast_exp(prefix_diff(r_hi[ls], r_lo[ls], r_hi[lt], r_lo[lt]));
-                            m[j] = v;
-                        }
-                    }
-                    // the lane's 16 columns (zero past SB: they cover the
-                    // padded K of a bf16 block of 16) in two or four stores;
-                    // fp32 places column 16 q + 4 i + j at 16 q + 4 j + i
-                    T *mrow = MT + tl * PITCH + 16 * q;
-#pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if constexpr (F32)
-                            kb_store4(mrow + 4 * j, f32x4{m[j], m[4 + j], m[8 + j], m[12 + j]});
-                        else
-                            kb_store4(mrow + 4 * j, f32x4{m[4 * j], m[4 * j + 1], m[4 * j + 2], m[4 * j + 3]});
-                    }
-                }
-                __syncthreads();
-                if (!active) continue;
-                for (int kk = 0; kk < SBK; kk += KS) {
-                    const frag mf = load_frag(MT + (wave * 16 + r) * PITCH + kk + VEC * q);
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) acc[wt] = Mma<T>::mma(mf, vfrag(kk, wt * 16), acc[wt]);
-                }
-            }
-            // ---- the head's epilogue: dx, x . u, dD
-            if (active) {
-                const float Dh = D ? D[h] : 0.f;
-                float dsum = 0.f;
-#pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-                    const bool tin = t < L && l < Q;
-                    const float dtl = r_dt[l];
-                    const size_t ro = (((size_t)b * L + t) * H + h) * P;
-                    float ds = 0.f;
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) {
-                        const int p = wt * 16 + r;
-                        if (!tin || p >= P) continue;
-                        const float xv = to_f32(x[ro + p]), gv = to_f32(dy[ro + p]);
-                        const float u = acc[wt][i];
-                        ds += xv * u;
-                        dsum += gv * xv;
-                        out[ro + p] = from_f32<T>(Dh * gv + dtl * u);
-                    }
-                    ds = row16_sum(ds);
-                    if (r == 0 && l < Q) dd[vbase + l] = tin ? ds : 0.f;
-                }
-                dsum = wave_sum(dsum);
-                if (lane == 0) red[wave] = dsum;
-            }
-            __syncthreads();
-            if (tid == 0) {
-                float sdd = 0.f;
-                for (int w = 0; w < 4; ++w)
-                    if (w * 16 < SB) sdd += red[w];
-                dDpart[((size_t)(b * nc + c) * H + h) * nrb + lb] = sdd;
+                for (int wt = 0; wt < NW; ++wt) tot[wt][i] += sc * acc[wt][i];
             }
         }
     }
 
-    if constexpr (MODE != kDx) {
-        // ---- the intra-chunk product with the group's summed score tiles
-        // (by the first head group only): dC rows lb x Ws[lb][sb] B[sb],
-        // sb <= lb; dB rows lb x Ws[sb][lb]^T C[sb], sb >= lb
-        if (hgi == 0) {
-            const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
-            const T *vsrc = (MODE == kDb ? Cm : Bm) + ((size_t)b * L * G + g) * N;
-            for (int sb = sb_lo; sb <= sb_hi; ++sb) {
-                __syncthreads();   // (the previous block's V and tile are no longer read)
-                stage_v(vsrc, (size_t)G * N, sb);
-                {
-                    // the tile as stored (its upper triangle on the diagonal
-                    // is zero): kDc rows t of this block and columns s of
-                    // block sb, kDb rows s of block sb and columns t
-                    const int r0 = MODE == kDc ? lb * SB : sb * SB, c0 = MODE == kDc ? sb * SB : lb * SB;
-                    const int mv = SBK / VEC;
-                    for (int v = tid; v < SBK * mv; v += 256) {
-                        const int i = v / mv, j = (v % mv) * VEC;
-                        frag f = zero_frag<T>();
-                        if (i < SB && j < SB) f = load_frag(wsm + (cbase + r0 + i) * Q + c0 + j);
-                        *reinterpret_cast<frag *>(MT + i * PITCH + j) = f;
-                    }
-                }
-                __syncthreads();
-                if (!active) continue;
-                for (int kk = 0; kk < SBK; kk += KS) {
-                    // A: rows t (this wave's 16), K = s
-                    frag mf;
-                    if constexpr (MODE == kDc) {
-                        if constexpr (F32) {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) mf[j] = MT[(wave * 16 + r) * PITCH + kk + q + 4 * j];
-                        } else {
-                            mf = load_frag(MT + (wave * 16 + r) * PITCH + kk + 8 * q);
-                        }
-                    } else {
-                        if constexpr (F32) {
-#pragma unroll
-                            for (int j = 0; j < 4; ++j) mf[j] = MT[(kk + q + 4 * j) * PITCH + wave * 16 + r];
-                        } else {
-                            mf = kb_tr_frag(reinterpret_cast<const bf16 *>(MT), PITCH, kk + 8 * q + er,
-                                            wave * 16 + ca);
-                        }
-                    }
-#pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) tot[wt] = Mma<T>::mma(mf, vfrag(kk, wt * 16), tot[wt]);
+    // ---- the intra-chunk product with the group's summed score tiles (by
+    // the first head group only): dC rows lb x Ws[lb][sb] B[sb], sb <= lb;
+    // dB rows lb x Ws[sb][lb]^T C[sb], sb >= lb
+    if (hgi == 0) {
+        const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
+        const T *vsrc = (MODE == kDb ? Cm : Bm) + ((size_t)b * L * G + g) * N;
+        for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+            __syncthreads();   // (the previous block's V and tile are no longer read)
+            kb_stage_rows<T, WP, VP>(VS, vsrc, (size_t)G * N, c, Q, sb, SB, SBK, L, N);
+            {
+                // the tile as stored (its upper triangle on the diagonal is
+                // zero): kDc rows t of this block and columns s of block sb,
+                // kDb rows s of block sb and columns t
+                const int r0 = MODE == kDc ? lb * SB : sb * SB, c0 = MODE == kDc ? sb * SB : lb * SB;
+                const int mv = SBK / VEC;
+                for (int v = tid; v < SBK * mv; v += 256) {
+                    const int i = v / mv, j = (v % mv) * VEC;
+                    frag f = zero_frag<T>();
+                    if (i < SB && j < SB) f = load_frag(wsm + (cbase + r0 + i) * Q + c0 + j);
+                    *reinterpret_cast<frag *>(MT + i * PITCH + j) = f;
                 }
             }
-        }
-        // ---- dB / dC rows of the row block
-        if (active) {
+            __syncthreads();
+            if (!active) continue;
+            for (int kk = 0; kk < SBK; kk += KS) {
+                // A: rows t (this wave's 16), K = s
+                frag mf;
+                if constexpr (MODE == kDc) {
+                    if constexpr (F32) {
 #pragma unroll
-            for (int i = 0; i < 4; ++i) {
-                const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-                if (t >= L || l >= Q) continue;
-#pragma unroll
-                for (int wt = 0; wt < NW; ++wt) {
-                    const int n = wt * 16 + r;
-                    if (n >= N) continue;
-                    const size_t o = (((size_t)b * L + t) * G + g) * N + n;
-                    // (several head groups: an fp32 partial sum each, added up afterwards)
-                    if (part)
-                        part[(size_t)hgi * gridDim.z * L * G * N + o] = tot[wt][i];
-                    else
-                        out[o] = from_f32<T>(tot[wt][i]);
+                        for (int j = 0; j < 4; ++j) mf[j] = MT[(wave * 16 + r) * PITCH + kk + q + 4 * j];
+                    } else {
+                        mf = load_frag(MT + (wave * 16 + r) * PITCH + kk + 8 * q);
+                    }
+                } else {
+                    mf = kb_across<T, PITCH>(MT, kk, wave * 16, r, q);
                 }
+#pragma unroll
+                for (int wt = 0; wt < NW; ++wt)
+                    tot[wt] = Mma<T>::mma(mf, kb_across<T, VP>(VS, kk, wt * 16, r, q), tot[wt]);
+            }
+        }
+    }
+    // ---- dB / dC rows of the row block
+    if (active) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+            if (t >= L || l >= Q) continue;
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) {
+                const int n = wt * 16 + r;
+                if (n >= N) continue;
+                const size_t o = (((size_t)b * L + t) * G + g) * N + n;
+                // (several head groups: an fp32 partial sum each, added up afterwards)
+                if (part)
+                    part[(size_t)hgi * gridDim.z * L * G * N + o] = tot[wt][i];
+                else
+                    out[o] = from_f32<T>(tot[wt][i]);
             }
         }
     }
@@ -833,24 +919,32 @@ const char *const kBackwardKernelNames[kBackwardKernels] = {
     "k1..k4 (recompute)", "kb_adj_chunk_state", "kb_state_passing", "kb_dx", "kb_wsum",
     "kb_dB", "kb_dC", "kb_ddt", "kb_reduce"};
 
+template <typename T, int NW>
+static void launch_dx(const BackwardArgs &a, hipStream_t stream) {
+    const ForwardArgs &f = a.f;
+    const int nrb = bwd_row_blocks(f.Q);
+    hipLaunchKernelGGL((kb_dx<T, NW>), dim3(f.H, f.nchunks * nrb, f.batch), dim3(256),
+                       KbLds::bytes(16 * NW, (int)sizeof(T)), stream, (const T *)f.x,
+                       (const T *)f.B, (const T *)a.dy, (const float *)f.cb, (const float *)a.adj,
+                       (const float *)f.acum_hi, (const float *)f.acum_lo, (const float *)f.dtT,
+                       f.D, (T *)a.dx, a.dint, a.dd, a.dDpart, f.L, f.H, f.G, f.P, f.N,
+                       f.nchunks, f.Q);
+}
+
 template <typename T, int MODE, int NW>
 static void launch_mix(const BackwardArgs &a, void *out, float *part, hipStream_t stream) {
     const ForwardArgs &f = a.f;
     const int nrb = bwd_row_blocks(f.Q);
     const int hpg = f.H / f.G;
-    const int hpw = MODE == kDx ? 1 : bwd_heads_per_group(f.batch, f.nchunks, nrb, f.G, hpg);
-    const int ny = MODE == kDx ? f.H : f.G * ((hpg + hpw - 1) / hpw);
-    const size_t lds = KbLds::bytes(16 * NW, (int)sizeof(T));
-    const dim3 grid = MODE == kDx ? dim3(ny, f.nchunks * nrb, f.batch)
-                                  : dim3(f.nchunks * nrb, ny, f.batch);
-    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), grid,
-                       dim3(256), lds, stream, (const T *)f.x, (const T *)f.B, (const T *)f.C,
-                       (const T *)a.dy, (const float *)f.cb, (const T *)a.wsm, (const float *)f.S,
-                       (const float *)a.adj, (const float *)f.acum_hi, (const float *)f.acum_lo,
-                       (const float *)f.dtT, f.D, (T *)out, a.roff, a.dint, a.dd, a.dDpart,
-                       (MODE != kDx && ny > f.G) ? part : nullptr, f.L, f.H, f.G, f.P, f.N,
-                       f.nchunks, f.Q, hpw);
-    if (MODE != kDx && ny > f.G) {
+    const int hpw = bwd_heads_per_group(f.batch, f.nchunks, nrb, f.G, hpg);
+    const int ny = f.G * ((hpg + hpw - 1) / hpw);
+    hipLaunchKernelGGL((kb_mix<T, MODE, NW>), dim3(f.nchunks * nrb, ny, f.batch), dim3(256),
+                       KbLds::bytes(16 * NW, (int)sizeof(T)), stream, (const T *)f.x,
+                       (const T *)f.B, (const T *)f.C, (const T *)a.dy, (const T *)a.wsm,
+                       (const float *)f.S, (const float *)a.adj, (const float *)f.acum_hi,
+                       (const float *)f.acum_lo, (const float *)f.dtT, (T *)out, a.roff,
+                       ny > f.G ? part : nullptr, f.L, f.H, f.G, f.P, f.N, f.nchunks, f.Q, hpw);
+    if (ny > f.G) {
         const size_t n = (size_t)f.batch * f.L * f.G * f.N;
         hipLaunchKernelGGL(kb_sum_heads<T>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
                            stream, (const float *)part, (T *)out, n, ny / f.G);
@@ -876,9 +970,9 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
                        a.dfinal, a.dinit, a.qpart, f.H, PN, f.nchunks, f.Q, nsl);
     if ((err = mark()) != hipSuccess) return err;
     if (f.P <= 64)
-        launch_mix<T, kDx, 4>(a, a.dx, nullptr, stream);
+        launch_dx<T, 4>(a, stream);
     else
-        launch_mix<T, kDx, 8>(a, a.dx, nullptr, stream);
+        launch_dx<T, 8>(a, stream);
     if ((err = mark()) != hipSuccess) return err;
     {
         const int nrb = bwd_row_blocks(f.Q);
