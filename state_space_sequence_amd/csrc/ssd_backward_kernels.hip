@@ -121,13 +121,16 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // (per tile) and column sums (per tile and wave), summed in fp64 from the
 // fp32 entries (the prefix subtracts sums much larger than the result).
 //
-// grid (tiles = nrb (nrb + 1) / 2, nc * G * nhg, b), 256 threads, no LDS.
-// Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile of rows l in block lb,
-// columns s in block sb; wave w its rows 16 w ..; it loops over hpw of the
-// group's heads (head group k of nhg) with the tile's sum in registers and
-// writes it as Ws in the operand type, or, with several head groups, as an
-// fp32 partial sum that a separate pass adds up.
-template <typename T>
+// Two launches: DIAG, grid (nrb, nc * G * nhg, b), the diagonal tiles; and
+// grid (nrb (nrb - 1) / 2, nc * G * nhg, b), the tiles below them, where
+// every entry is strict and the decay factors through the last row of the
+// column block (one exponential per row and per column, not per entry).
+// 256 threads, no LDS.  Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile
+// of rows l in block lb, columns s in block sb; wave w its rows 16 w ..; it
+// loops over hpw of the group's heads (head group k of nhg) with the tile's
+// sum in registers and writes it as Ws in the operand type, or, with
+// several head groups, as an fp32 partial sum that a separate pass adds up.
+template <typename T, bool DIAG>
 __global__ void __launch_bounds__(256)
 kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restrict__ cb,
         const float *__restrict__ acum_hi, const float *__restrict__ acum_lo,
@@ -145,9 +148,12 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
         pair = k % gridDim.x;
         yy = (k / gridDim.x) * 8 + (id & 7);
     }
-    int lb = 0;
-    while ((lb + 1) * (lb + 2) / 2 <= pair) ++lb;
-    const int sb = pair - lb * (lb + 1) / 2;
+    int lb = pair, sb = pair;
+    if constexpr (!DIAG) {
+        lb = 1;
+        while ((lb + 1) * lb / 2 <= pair) ++lb;
+        sb = pair - lb * (lb - 1) / 2;
+    }
     const int hpg = H / G, nhg = (hpg + hpw - 1) / hpw;
     const int hgi = yy % nhg, cg = yy / nhg;
     const int c = cg / G, g = cg % G, b = blockIdx.z;
@@ -169,7 +175,7 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     for (int st = 0; st < 4; ++st)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const bool ok = active && st * 16 + r < SB && scol[st] <= lrow[i];
+            const bool ok = active && (!DIAG || (st * 16 + r < SB && scol[st] <= lrow[i]));
             cbv[st][i] = ok ? cb[(cbase + lrow[i]) * Q + scol[st]] : 0.f;
         }
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -201,21 +207,47 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
                 lhi[i] = acum_hi[vbase + lrow[i]];
                 llo[i] = acum_lo[vbase + lrow[i]];
             }
+            if constexpr (!DIAG) {
+                // below the diagonal (blocks of 64, all within the chunk)
+                // every entry is strict (s < l) and the decay factors
+                // through te, the last row of block sb: e^(acum_l - acum_s)
+                // = e^(acum_l - acum_te) e^(acum_te - acum_s), both at most 1
+                const int te = sb * SB + SB - 1;
+                const float thi = acum_hi[vbase + te], tlo = acum_lo[vbase + te];
+                float rf[4];
 #pragma unroll
-            for (int st = 0; st < 4; ++st) {
-                const bool cin = st * 16 + r < SB;
-                const float shi = cin ? acum_hi[vbase + scol[st]] : 0.f;
-                const float slo = cin ? acum_lo[vbase + scol[st]] : 0.f;
-                const float sdt = cin ? dtT[vbase + scol[st]] : 0.f;
+                for (int i = 0; i < 4; ++i) rf[i] = fast_exp(prefix_diff(lhi[i], llo[i], thi, tlo));
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    float v = 0.f;
-                    if (cin && scol[st] <= lrow[i])
-                        v = z[st][i] * fast_exp(prefix_diff(lhi[i], llo[i], shi, slo)) * sdt;
-                    acc[st][i] += v;
-                    const double w = scol[st] < lrow[i] ? (double)v * cbv[st][i] : 0.0;   // strict
-                    rsum[i] += w;
-                    csum[st] += w;
+                for (int st = 0; st < 4; ++st) {
+                    const float shi = acum_hi[vbase + scol[st]], slo = acum_lo[vbase + scol[st]];
+                    const float cf = fast_exp(prefix_diff(thi, tlo, shi, slo)) * dtT[vbase + scol[st]];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        const float v = z[st][i] * rf[i] * cf;
+                        acc[st][i] += v;
+                        const double w = (double)(v * cbv[st][i]);
+                        rsum[i] += w;
+                        csum[st] += w;
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int st = 0; st < 4; ++st) {
+                    const bool cin = st * 16 + r < SB;
+                    const float shi = cin ? acum_hi[vbase + scol[st]] : 0.f;
+                    const float slo = cin ? acum_lo[vbase + scol[st]] : 0.f;
+                    const float sdt = cin ? dtT[vbase + scol[st]] : 0.f;
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) {
+                        // (exponent clamped at 0: the entries above the
+                        // diagonal are selected away)
+                        const float e = fast_exp(fminf(prefix_diff(lhi[i], llo[i], shi, slo), 0.f));
+                        const float v = cin && scol[st] <= lrow[i] ? z[st][i] * e * sdt : 0.f;
+                        acc[st][i] += v;
+                        const double w = scol[st] < lrow[i] ? (double)(v * cbv[st][i]) : 0.0;   // strict
+                        rsum[i] += w;
+                        csum[st] += w;
+                    }
                 }
             }
         }
@@ -979,11 +1011,18 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
         const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
         const int hpw = bwd_wsum_heads(ntile, f.nchunks, f.G, f.batch, hpg);
         const int nhg = (hpg + hpw - 1) / hpw;
-        hipLaunchKernelGGL(kb_wsum<T>, dim3(ntile, f.nchunks * f.G * nhg, f.batch),
+        hipLaunchKernelGGL((kb_wsum<T, true>), dim3(nrb, f.nchunks * f.G * nhg, f.batch),
                            dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
                            (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
                            (const float *)f.dtT, (T *)a.wsm, nhg > 1 ? a.wpart : nullptr, a.rowp,
                            a.colp, f.L, f.H, f.G, f.P, f.nchunks, f.Q, hpw);
+        if (nrb > 1)
+            hipLaunchKernelGGL((kb_wsum<T, false>), dim3(ntile - nrb, f.nchunks * f.G * nhg, f.batch),
+                               dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
+                               (const float *)f.cb, (const float *)f.acum_hi,
+                               (const float *)f.acum_lo, (const float *)f.dtT, (T *)a.wsm,
+                               nhg > 1 ? a.wpart : nullptr, a.rowp, a.colp, f.L, f.H, f.G, f.P,
+                               f.nchunks, f.Q, hpw);
         if (nhg > 1) {
             // (entries of a chunk's Q x Q block above its diagonal blocks stay
             // unwritten and are never read)
