@@ -331,16 +331,20 @@ struct KbLds {
     static __host__ __device__ constexpr size_t m_elems(int sz) {
         return (size_t)kSB * (sz == 4 ? kSB + 16 : kSB + 8);
     }
-    // + a K-slab of the state: kb_dx [WP][ks + 16 / sz] (Lam's rows cut to
-    // the slab's columns), kDb / kDc [ks][WP + 16 / sz] (the slab's rows)
+    // + a slab of the state: kb_dx [WP][ks + 16 / sz] (Lam's rows cut to
+    // the K-slab's columns), kDb / kDc [srows][WP + 16 / sz] (srows of the
+    // state's rows: the whole of a bf16 headdim of 64, at most 8192 values)
     static __host__ __device__ constexpr int ks(int sz) { return sz == 4 ? 16 : 32; }
+    static __host__ __device__ constexpr int srows(int WP, int sz) {
+        return (sz == 4 ? 16 : 32) < 8192 / WP ? (sz == 4 ? 16 : 32) : 8192 / WP;
+    }
     static __host__ __device__ constexpr int spitch(int WP, int sz, int mode) {
         return mode == kDx ? ks(sz) + 16 / sz : WP + 16 / sz;
     }
     static __host__ __device__ constexpr size_t s_elems(int WP, int sz) {
-        return (size_t)WP * spitch(WP, sz, kDx) > (size_t)ks(sz) * spitch(WP, sz, kDb)
+        return (size_t)WP * spitch(WP, sz, kDx) > (size_t)srows(WP, sz) * spitch(WP, sz, kDb)
                    ? (size_t)WP * spitch(WP, sz, kDx)
-                   : (size_t)ks(sz) * spitch(WP, sz, kDb);
+                   : (size_t)srows(WP, sz) * spitch(WP, sz, kDb);
     }
     // + prefix sums and dt by token and a reduction slot per wave (fp32)
     static size_t bytes(int WP, int sz) {
@@ -629,14 +633,11 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     constexpr int VP = KbLds::vpitch(WP, SZ);
     constexpr int PITCH = KbLds::mpitch(SZ, MODE);
     constexpr int SP = KbLds::spitch(WP, SZ, MODE);
-    static_assert(KS == KbLds::ks(SZ), "state slab height");
+    static_assert(KbLds::srows(WP, SZ) % KS == 0, "state slab height");
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *VS = reinterpret_cast<T *>(smem_raw);                 // [SBX][VP]: V of the source block
     T *MT = VS + KbLds::v_elems(WP, SZ);                      // [SBX][PITCH]: the score tile
-    T *SS = MT + KbLds::m_elems(SZ);                          // [KS][SP]: a K-slab of the state
-    float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
-    float *r_lo = r_hi + 256;
-    float *r_dt = r_lo + 256;
+    T *SS = MT + KbLds::m_elems(SZ);                          // [SR][SP]: a slab of the state
 
     const int nrb = Q > SBX ? Q / SBX : 1;
     const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -687,58 +688,82 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
         }
     }
 
+    // ---- the state products U_t St, scaled per row, head by head.  The
+    // state passes through LDS in slabs of SR of its rows (SS[k][n]); a
+    // slab's loads are issued before the barrier that waits for the
+    // previous one to be used.
+    constexpr int SR = KbLds::srows(WP, SZ);
+    constexpr int NPRE = SR * WP / 1024;   // float4 per thread and slab
+    constexpr int wq = WP / 4;
+    const int nks = (P + SR - 1) / SR;     // slabs per head
+    f32x4 pre[NPRE];
+    auto load_slab = [&](int hh, int k0) {
+        const float *st = (MODE == kDc ? S : adj) + ((size_t)(b * nc + c) * H + h_first + hh) * P * N;
+#pragma unroll
+        for (int u = 0; u < NPRE; ++u) {
+            const int v = tid + 256 * u, kr = v / wq, w0 = (v % wq) * 4;
+            pre[u] = w0 < N && k0 + kr < P ? *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0)
+                                           : zero4();
+        }
+    };
     for (int hh = 0; hh < h_count; ++hh) {
         const int h = h_first + hh;
         const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;   // prefix sums, dt
-        __syncthreads();   // (the previous head's vectors are no longer read)
-        for (int l = tid; l < Q; l += 256) {
-            r_hi[l] = acum_hi[vbase + l];
-            r_lo[l] = acum_lo[vbase + l];
-            r_dt[l] = dtT[vbase + l];
+        // this lane's rows' prefix sums and dt
+        float rh[4], rl[4], rdt[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int l = min(lb * SB + wave * 16 + 4 * q + i, Q - 1);
+            rh[i] = acum_hi[vbase + l];
+            rl[i] = acum_lo[vbase + l];
+            rdt[i] = MODE == kDb ? dtT[vbase + l] : 0.f;
         }
-        __syncthreads();
-        const float end_hi = r_hi[Q - 1], end_lo = r_lo[Q - 1];
-
-        // ---- the state product U_t St, scaled per row.  The state passes
-        // through LDS in K-slabs of its rows (SS[k][n]).
+        const float end_hi = acum_hi[vbase + Q - 1], end_lo = acum_lo[vbase + Q - 1];
         f32x4 acc[NW];
 #pragma unroll
         for (int i = 0; i < NW; ++i) acc[i] = zero4();
-        const float *st = (MODE == kDc ? S : adj) + ((size_t)(b * nc + c) * H + h) * P * N;
         const int tr = t0 + wave * 16 + r;   // this lane's U row
         const T *urow = (MODE == kDb ? x : dy) + (((size_t)b * L + tr) * H + h) * P;
-        for (int k0 = 0; k0 < P; k0 += KS) {
-            const int k = k0 + VEC * q;
+        for (int ks = 0; ks < nks; ++ks) {
+            const int k0 = ks * SR;
+            frag ua[SR / KS];
+#pragma unroll
+            for (int j = 0; j < SR / KS; ++j) {
+                const int k = k0 + j * KS + VEC * q;
+                ua[j] = active && tr < L && k < P ? load_frag(urow + k) : zero_frag<T>();
+            }
+            load_slab(hh, k0);
             __syncthreads();   // (the previous slab is no longer read)
-            constexpr int wq = WP / 4;
-            for (int v = tid; v < KS * wq; v += 256) {
-                const int kr = v / wq, w0 = (v % wq) * 4;
-                f32x4 f = zero4();
-                if (w0 < N && k0 + kr < P)
-                    f = *reinterpret_cast<const f32x4 *>(st + (size_t)(k0 + kr) * N + w0);
-                kb_store4(SS + kr * SP + w0, f);
+#pragma unroll
+            for (int u = 0; u < NPRE; ++u) {
+                const int v = tid + 256 * u, kr = v / wq, w0 = (v % wq) * 4;
+                kb_store4(SS + kr * SP + w0, pre[u]);
             }
             __syncthreads();
-            if (!active) continue;
-            const frag ua = tr < L && k < P ? load_frag(urow + k) : zero_frag<T>();
+            if (active) {
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) {
-                frag sb;
-                if constexpr (F32) {
+                for (int j = 0; j < SR / KS; ++j)
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) sb[j] = SS[(VEC * q + j) * SP + wt * 16 + r];
-                } else {
-                    sb = kb_across<T, SP>(SS, 0, wt * 16, r, q);
-                }
-                acc[wt] = Mma<T>::mma(ua, sb, acc[wt]);
+                    for (int wt = 0; wt < NW; ++wt) {
+                        frag sb;
+                        if constexpr (F32) {
+#pragma unroll
+                            for (int jj = 0; jj < 4; ++jj)
+                                sb[jj] = SS[(j * KS + VEC * q + jj) * SP + wt * 16 + r];
+                        } else {
+                            sb = kb_across<T, SP>(SS, j * KS, wt * 16, r, q);
+                        }
+                        acc[wt] = Mma<T>::mma(ua[j], sb, acc[wt]);
+                        // (one K step's operands at a time in registers)
+                        if (wt == NW - 1) __builtin_amdgcn_sched_barrier(0);
+                    }
             }
         }
         if (active) {
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int l = lb * SB + wave * 16 + 4 * q + i;
-                const float e = MODE == kDc ? fast_exp(r_hi[l])
-                                            : fast_exp(prefix_diff(end_hi, end_lo, r_hi[l], r_lo[l]));
+                const float e = MODE == kDc ? fast_exp(rh[i])
+                                            : fast_exp(prefix_diff(end_hi, end_lo, rh[i], rl[i]));
 #pragma unroll
                 for (int wt = 0; wt < NW; ++wt) acc[wt][i] *= e;
             }
@@ -766,8 +791,7 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             // the head's state product into the group's sum (dB: times dt_t)
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int l = lb * SB + wave * 16 + 4 * q + i;
-                const float sc = MODE == kDb ? r_dt[l] : 1.f;
+                const float sc = MODE == kDb ? rdt[i] : 1.f;
 #pragma unroll
                 for (int wt = 0; wt < NW; ++wt) tot[wt][i] += sc * acc[wt][i];
             }
