@@ -503,20 +503,26 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     const float *st = adj + ((size_t)(b * nc + c) * H + h) * P * N;
     const int tr = c * Q + lb * SB + wave * 16 + r;   // this lane's B row
     const T *urow = Bm + (((size_t)b * L + tr) * G + g) * N;
+    constexpr int kq = KS / 4, NSL = WP * kq / 256;   // float4 per thread and slab
     for (int k0 = 0; k0 < N; k0 += KS) {
         const int k = k0 + VEC * q;
+        // (the slab's loads are issued before the barrier that frees the previous one)
+        f32x4 pre[NSL];
+#pragma unroll
+        for (int u = 0; u < NSL; ++u) {
+            const int v = tid + 256 * u, w = v / kq, kr = (v % kq) * 4;
+            pre[u] = w < P && k0 + kr < N ? *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr)
+                                          : zero4();
+        }
+        const frag ua = active && tr < L && k < N ? load_frag(urow + k) : zero_frag<T>();
         __syncthreads();   // (the previous slab is no longer read)
-        constexpr int kq = KS / 4;
-        for (int v = tid; v < WP * kq; v += 256) {
-            const int w = v / kq, kr = (v % kq) * 4;
-            f32x4 f = zero4();
-            if (w < P && k0 + kr < N)
-                f = e_te * *reinterpret_cast<const f32x4 *>(st + (size_t)w * N + k0 + kr);
-            kb_store4(SS + w * SP + kr, f);
+#pragma unroll
+        for (int u = 0; u < NSL; ++u) {
+            const int v = tid + 256 * u, w = v / kq, kr = (v % kq) * 4;
+            kb_store4(SS + w * SP + kr, e_te * pre[u]);
         }
         __syncthreads();
         if (!active) continue;
-        const frag ua = tr < L && k < N ? load_frag(urow + k) : zero_frag<T>();
 #pragma unroll
         for (int wt = 0; wt < NW; ++wt)
             acc[wt] = Mma<T>::mma(ua, load_frag(SS + (wt * 16 + r) * SP + VEC * q), acc[wt]);
@@ -537,19 +543,41 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     // ---- the intra-chunk product, from the chunk's last source block down
     // to the diagonal one
     const T *vsrc = dy + ((size_t)b * L * H + h) * P;
+    // per thread and block: NV operand vectors of dy, NC float4 of C B^T
+    // (rows and columns up to kSB; those past SBK are zeros never read)
+    constexpr int wv = WP / VEC, NV = SBX * wv / 256, NC = SBX * (SBX / 4) / 256;
     for (int sb = nrb - 1; sb >= lb; --sb) {
+        // the block's loads, issued before the barrier that frees the previous block
+        frag vpre[NV];
+        f32x4 cpre[NC];
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+            vpre[u] = sl < SB && ts < L && w0 < P ? load_frag(vsrc + (size_t)ts * H * P + w0) : zero_frag<T>();
+        }
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int v = tid + 256 * u, sl = v / (SBX / 4), tl = (v % (SBX / 4)) * 4;
+            cpre[u] = sl < SB && tl < SB
+                          ? *reinterpret_cast<const f32x4 *>(cb + (cbase + sb * SB + sl) * Q + lb * SB + tl)
+                          : zero4();
+        }
         __syncthreads();   // (the previous block's operands are no longer read)
-        kb_stage_rows<T, WP, VP>(VS, vsrc, (size_t)H * P, c, Q, sb, SB, SBK, L, P);
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC;
+            *reinterpret_cast<frag *>(VS + sl * VP + w0) = vpre[u];
+        }
         // MT[s][t] = (C_s . B_t) e^(acum_s - acum_te) beyond the block,
         // (C_s . B_t) e^(acum_s - acum_t) for s >= t in it (the upper
         // triangle, which the forward leaves unwritten, is selected away)
-        const int mq = SBK / 4;
-        for (int v = tid; v < SBK * mq; v += 256) {
-            const int sl = v / mq, tl = (v % mq) * 4;
+#pragma unroll
+        for (int u = 0; u < NC; ++u) {
+            const int v = tid + 256 * u, sl = v / (SBX / 4), tl = (v % (SBX / 4)) * 4;
             f32x4 f = zero4();
             if (sl < SB && tl < SB) {
                 const int ls = sb * SB + sl, lt0 = lb * SB + tl;
-                const f32x4 cv = *reinterpret_cast<const f32x4 *>(cb + (cbase + ls) * Q + lt0);
+                const f32x4 cv = cpre[u];
                 const float shi = r_hi[ls], slo = r_lo[ls];
                 if (sb > lb) {
                     f = cv * fast_exp(prefix_diff(shi, slo, r_hi[te], r_lo[te]));
