@@ -54,12 +54,6 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-__device__ __forceinline__ double row16_sum_f64(double v) {
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
-}
-
 // Sum over the 16 lanes of each 16-lane group (the lanes of one MFMA row).
 __device__ __forceinline__ float row16_sum(float v) {
 #pragma unroll
@@ -118,8 +112,9 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // times (C_l . B_s); they are the prefix over k < t of (column sum -
 // row sum) of W's strict lower triangle (the entries with s < t, less
 // those with l < t), so this kernel also writes each head's strict row sums
-// (per tile) and column sums (per tile and wave), summed in fp64 from the
-// fp32 entries (the prefix subtracts sums much larger than the result).
+// (per tile) and column sums (per tile and wave): the fp32 entries summed
+// four at a time in fp32, then in fp64 (the prefix subtracts sums much
+// larger than the result).
 //
 // Two launches: DIAG, grid (nrb, nc * G * nhg, b), the diagonal tiles; and
 // grid (nrb (nrb - 1) / 2, nc * G * nhg, b), the tiles below them, where
@@ -183,7 +178,8 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     for (int hh = h0; hh < h1; ++hh) {
         const int h = g * hpg + hh;
         const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
-        double rsum[4] = {0.0, 0.0, 0.0, 0.0}, csum[4] = {0.0, 0.0, 0.0, 0.0};
+        // strict row and column sums of W, four products at a time in fp32
+        float rs[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
         if (active) {
             // scores dy_l . x_s over the headdim
             f32x4 z[4] = {zero4(), zero4(), zero4(), zero4()};
@@ -225,9 +221,9 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
                     for (int i = 0; i < 4; ++i) {
                         const float v = z[st][i] * rf[i] * cf;
                         acc[st][i] += v;
-                        const double w = (double)(v * cbv[st][i]);
-                        rsum[i] += w;
-                        csum[st] += w;
+                        const float w = v * cbv[st][i];
+                        rs[i] += w;
+                        cs[st] += w;
                     }
                 }
             } else {
@@ -244,28 +240,42 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
                         const float e = fast_exp(fminf(prefix_diff(lhi[i], llo[i], shi, slo), 0.f));
                         const float v = cin && scol[st] <= lrow[i] ? z[st][i] * e * sdt : 0.f;
                         acc[st][i] += v;
-                        const double w = scol[st] < lrow[i] ? (double)(v * cbv[st][i]) : 0.0;   // strict
-                        rsum[i] += w;
-                        csum[st] += w;
+                        const float w = scol[st] < lrow[i] ? v * cbv[st][i] : 0.f;   // strict
+                        rs[i] += w;
+                        cs[st] += w;
                     }
                 }
             }
         }
         // strict row sums (complete over the tile's columns) and the wave's
-        // column sums over its 16 rows
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const double v = row16_sum_f64(rsum[i]);
-            if (active && r == 0 && lrow[i] - lb * SB < SB)
-                rowp[(((size_t)(b * H + h) * nc + c) * nrb + sb) * Q + lrow[i]] = v;
+        // column sums over its 16 rows, in fp64 from here on.  Rows: a
+        // butterfly over the 16 lanes of a row group that halves the values
+        // held per lane at its first two steps leaves row 4 q + (r >> 2)'s
+        // sum in lanes 4 (r >> 2) .. + 3.
+        {
+            const bool b3 = r & 8, b2 = r & 4;
+            double k0 = b3 ? rs[2] : rs[0], k1 = b3 ? rs[3] : rs[1];
+            k0 += __shfl_xor((double)(b3 ? rs[0] : rs[2]), 8, kWave);
+            k1 += __shfl_xor((double)(b3 ? rs[1] : rs[3]), 8, kWave);
+            double v = b2 ? k1 : k0;
+            v += __shfl_xor(b2 ? k0 : k1, 4, kWave);
+            v += __shfl_xor(v, 2, kWave);
+            v += __shfl_xor(v, 1, kWave);
+            const int row = wave * 16 + 4 * q + (r >> 2);
+            if (active && (r & 3) == 0 && row < SB)
+                rowp[(((size_t)(b * H + h) * nc + c) * nrb + sb) * Q + lb * SB + row] = v;
         }
-#pragma unroll
-        for (int st = 0; st < 4; ++st) {
-            double v = csum[st];
-            v += __shfl_xor(v, 16, kWave);
-            v += __shfl_xor(v, 32, kWave);
-            if (q == 0 && st * 16 + r < SB)
-                colp[((((size_t)(b * H + h) * nc + c) * nrb + lb) * 4 + wave) * Q + scol[st]] = v;
+        // columns: the same over the four row groups (lanes 16 apart) leaves
+        // column tile q's sum in row group q
+        {
+            const bool b5 = q & 2, b4 = q & 1;
+            double k0 = b5 ? cs[2] : cs[0], k1 = b5 ? cs[3] : cs[1];
+            k0 += __shfl_xor((double)(b5 ? cs[0] : cs[2]), 32, kWave);
+            k1 += __shfl_xor((double)(b5 ? cs[1] : cs[3]), 32, kWave);
+            double v = b4 ? k1 : k0;
+            v += __shfl_xor(b4 ? k0 : k1, 16, kWave);
+            if (q * 16 + r < SB)
+                colp[((((size_t)(b * H + h) * nc + c) * nrb + lb) * 4 + wave) * Q + sb * SB + q * 16 + r] = v;
         }
     }
     if (active) {
