@@ -54,11 +54,19 @@ __device__ __forceinline__ double wave_sum_f64(double v) {
     return v;
 }
 
-// Sum over the 16 lanes of each 16-lane group (the lanes of one MFMA row).
-__device__ __forceinline__ float row16_sum(float v) {
-#pragma unroll
-    for (int d = 8; d >= 1; d >>= 1) v += __shfl_xor(v, d, kWave);
-    return v;
+// Four values per lane summed over the 16 lanes of each 16-lane group (the
+// lanes r of one MFMA output row group): lane r receives the total of value
+// r >> 2.  A butterfly that halves the values each lane holds at its first
+// two steps (5 exchanges instead of 16).
+template <typename F>
+__device__ __forceinline__ F row16_sum4(const F (&v)[4], int r) {
+    const bool b3 = r & 8, b2 = r & 4;
+    const F k0 = (b3 ? v[2] : v[0]) + __shfl_xor(b3 ? v[0] : v[2], 8, kWave);
+    const F k1 = (b3 ? v[3] : v[1]) + __shfl_xor(b3 ? v[1] : v[3], 8, kWave);
+    F t = (b2 ? k1 : k0) + __shfl_xor(b2 ? k0 : k1, 4, kWave);
+    t += __shfl_xor(t, 2, kWave);
+    t += __shfl_xor(t, 1, kWave);
+    return t;
 }
 
 }  // namespace
@@ -248,19 +256,11 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
             }
         }
         // strict row sums (complete over the tile's columns) and the wave's
-        // column sums over its 16 rows, in fp64 from here on.  Rows: a
-        // butterfly over the 16 lanes of a row group that halves the values
-        // held per lane at its first two steps leaves row 4 q + (r >> 2)'s
-        // sum in lanes 4 (r >> 2) .. + 3.
+        // column sums over its 16 rows, in fp64 from here on (row
+        // 4 q + (r >> 2)'s sum in lanes 4 (r >> 2) .. + 3).
         {
-            const bool b3 = r & 8, b2 = r & 4;
-            double k0 = b3 ? rs[2] : rs[0], k1 = b3 ? rs[3] : rs[1];
-            k0 += __shfl_xor((double)(b3 ? rs[0] : rs[2]), 8, kWave);
-            k1 += __shfl_xor((double)(b3 ? rs[1] : rs[3]), 8, kWave);
-            double v = b2 ? k1 : k0;
-            v += __shfl_xor(b2 ? k0 : k1, 4, kWave);
-            v += __shfl_xor(v, 2, kWave);
-            v += __shfl_xor(v, 1, kWave);
+            const double rd[4] = {rs[0], rs[1], rs[2], rs[3]};
+            const double v = row16_sum4(rd, r);
             const int row = wave * 16 + 4 * q + (r >> 2);
             if (active && (r & 3) == 0 && row < SB)
                 rowp[(((size_t)(b * H + h) * nc + c) * nrb + sb) * Q + lb * SB + row] = v;
@@ -406,21 +406,6 @@ __device__ __forceinline__ typename Mma<T>::frag kb_across(const T *tile, int kk
     }
 }
 
-// dy (or C, B) rows of source block sb into VS: row sl = token
-// c Q + sb SB + sl of vsrc (rows rs elements apart), zero past the block, L
-// or the width W; SBK rows of WP columns, 256 threads.
-template <typename T, int WP, int VP>
-__device__ __forceinline__ void kb_stage_rows(T *VS, const T *vsrc, size_t rs, int c, int Q,
-                                              int sb, int SB, int SBK, int L, int W) {
-    constexpr int VEC = Mma<T>::VEC, wv = WP / VEC;
-    for (int v = threadIdx.x; v < SBK * wv; v += 256) {
-        const int sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
-        typename Mma<T>::frag f = zero_frag<T>();
-        if (sl < SB && ts < L && w0 < W) f = load_frag(vsrc + (size_t)ts * rs + w0);
-        *reinterpret_cast<typename Mma<T>::frag *>(VS + sl * VP + w0) = f;
-    }
-}
-
 // ------------------------------------------------------------ dx
 // u_t for the SB rows of row block lb of chunk c, head h, and from it dx_t,
 // x_t . u_t, the state part x_t . (e^(acum_end - acum_t) Lam B_t) and the
@@ -538,16 +523,18 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
             acc[wt] = Mma<T>::mma(ua, load_frag(SS + (wt * 16 + r) * SP + VEC * q), acc[wt]);
     }
     if (active) {
-        // the state part of x . u, per row
+        // the state part of x . u, per row (row 4 q + i's in lanes 4 i ..)
+        float v[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-            float v = 0.f;
+            v[i] = 0.f;
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) v += xv[i][wt] * acc[wt][i];
-            v = row16_sum(v) * rowf[i];
-            if (r == 0 && l < Q) dint[vbase + l] = t < L ? v : 0.f;
+            for (int wt = 0; wt < NW; ++wt) v[i] += xv[i][wt] * acc[wt][i];
+            v[i] *= rowf[i];
         }
+        const float sv = row16_sum4(v, r);
+        const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
+        if ((r & 3) == 0 && l < Q) dint[vbase + l] = t < L ? sv : 0.f;
     }
 
     // ---- the intra-chunk product, from the chunk's last source block down
@@ -621,24 +608,27 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     // ---- the epilogue: dx, x . u, dD (dy from the staged diagonal block)
     if (active) {
         const float Dh = D ? D[h] : 0.f;
-        float dsum = 0.f;
+        float dsum = 0.f, ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl, t = c * Q + l;
             const bool tin = t < L && l < Q;
             const float dtl = r_dt[l];
             const size_t ro = (((size_t)b * L + t) * H + h) * P;
-            float ds = 0.f;
+            ds[i] = 0.f;
 #pragma unroll
             for (int wt = 0; wt < NW; ++wt) {
                 const int p = wt * 16 + r;
                 const float gv = to_f32(VS[sl * VP + p]), u = acc[wt][i];
-                ds += xv[i][wt] * u;
+                ds[i] += xv[i][wt] * u;
                 dsum += gv * xv[i][wt];
                 if (tin && p < P) out[ro + p] = from_f32<T>(Dh * gv + dtl * u);
             }
-            ds = row16_sum(ds);
-            if (r == 0 && l < Q) dd[vbase + l] = tin ? ds : 0.f;
+        }
+        {
+            const float sd = row16_sum4(ds, r);
+            const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
+            if ((r & 3) == 0 && l < Q) dd[vbase + l] = t < L ? sd : 0.f;
         }
         dsum = wave_sum(dsum);
         if (lane == 0) red[wave] = dsum;
@@ -806,25 +796,28 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                 for (int wt = 0; wt < NW; ++wt) acc[wt][i] *= e;
             }
             if constexpr (MODE == kDc) {
-                // the state part of <dy, y - D x>, per row
+                // the state part of <dy, y - D x>, per row (row 4 q + i's
+                // in lanes 4 i ..)
+                float v[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
                     const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
                     const bool tin = t < L && l < Q;
-                    float v = 0.f;
+                    v[i] = 0.f;
 #pragma unroll
                     for (int wt = 0; wt < NW; ++wt) {
                         const int w = wt * 16 + r;
                         if constexpr (CREG) {
-                            v += to_f32(cpos[wt][i]) * acc[wt][i];
+                            v[i] += to_f32(cpos[wt][i]) * acc[wt][i];
                         } else {
                             if (!tin || w >= N) continue;
-                            v += to_f32(Cm[(((size_t)b * L + t) * G + g) * N + w]) * acc[wt][i];
+                            v[i] += to_f32(Cm[(((size_t)b * L + t) * G + g) * N + w]) * acc[wt][i];
                         }
                     }
-                    v = row16_sum(v);
-                    if (r == 0 && l < Q) roff[vbase + l] = tin ? v : 0.f;
                 }
+                const float sv = row16_sum4(v, r);
+                const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
+                if ((r & 3) == 0 && l < Q) roff[vbase + l] = t < L ? sv : 0.f;
             }
             // the head's state product into the group's sum (dB: times dt_t)
 #pragma unroll
@@ -842,21 +835,37 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     if (hgi == 0) {
         const int sb_lo = MODE == kDc ? 0 : lb, sb_hi = MODE == kDc ? lb : nrb - 1;
         const T *vsrc = (MODE == kDb ? Cm : Bm) + ((size_t)b * L * G + g) * N;
+        // per thread and block: NV operand vectors of V, NM of the tile (rows
+        // and columns up to kSB; those past SBK are zeros never read)
+        constexpr int wv = WP / VEC, mv = SBX / VEC, NV = SBX * wv / 256, NM = SBX * mv / 256;
         for (int sb = sb_lo; sb <= sb_hi; ++sb) {
+            // the block's loads, issued before the barrier that frees the
+            // previous block: V's rows, and the tile as stored (its upper
+            // triangle on the diagonal is zero): kDc rows t of this block and
+            // columns s of block sb, kDb rows s of block sb and columns t
+            const int r0 = MODE == kDc ? lb * SB : sb * SB, c0 = MODE == kDc ? sb * SB : lb * SB;
+            frag vpre[NV], mpre[NM];
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC, ts = c * Q + sb * SB + sl;
+                vpre[u] = sl < SB && ts < L && w0 < N ? load_frag(vsrc + (size_t)ts * G * N + w0)
+                                                      : zero_frag<T>();
+            }
+#pragma unroll
+            for (int u = 0; u < NM; ++u) {
+                const int v = tid + 256 * u, i = v / mv, j = (v % mv) * VEC;
+                mpre[u] = i < SB && j < SB ? load_frag(wsm + (cbase + r0 + i) * Q + c0 + j) : zero_frag<T>();
+            }
             __syncthreads();   // (the previous block's V and tile are no longer read)
-            kb_stage_rows<T, WP, VP>(VS, vsrc, (size_t)G * N, c, Q, sb, SB, SBK, L, N);
-            {
-                // the tile as stored (its upper triangle on the diagonal is
-                // zero): kDc rows t of this block and columns s of block sb,
-                // kDb rows s of block sb and columns t
-                const int r0 = MODE == kDc ? lb * SB : sb * SB, c0 = MODE == kDc ? sb * SB : lb * SB;
-                const int mv = SBK / VEC;
-                for (int v = tid; v < SBK * mv; v += 256) {
-                    const int i = v / mv, j = (v % mv) * VEC;
-                    frag f = zero_frag<T>();
-                    if (i < SB && j < SB) f = load_frag(wsm + (cbase + r0 + i) * Q + c0 + j);
-                    *reinterpret_cast<frag *>(MT + i * PITCH + j) = f;
-                }
+#pragma unroll
+            for (int u = 0; u < NV; ++u) {
+                const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC;
+                *reinterpret_cast<frag *>(VS + sl * VP + w0) = vpre[u];
+            }
+#pragma unroll
+            for (int u = 0; u < NM; ++u) {
+                const int v = tid + 256 * u, i = v / mv, j = (v % mv) * VEC;
+                *reinterpret_cast<frag *>(MT + i * PITCH + j) = mpre[u];
             }
             __syncthreads();
             if (!active) continue;
