@@ -128,11 +128,12 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // grid (nrb (nrb - 1) / 2, nc * G * nhg, b), the tiles below them, where
 // every entry is strict and the decay factors through the last row of the
 // column block (one exponential per row and per column, not per entry).
-// 256 threads, no LDS.  Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile
-// of rows l in block lb, columns s in block sb; wave w its rows 16 w ..; it
-// loops over hpw of the group's heads (head group k of nhg) with the tile's
-// sum in registers and writes it as Ws in the operand type, or, with
-// several head groups, as an fp32 partial sum that a separate pass adds up.
+// 256 threads, dynamic LDS 2 x 64 rows of x (pitch P + 16 / sizeof(T)).
+// Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile of rows l in block lb,
+// columns s in block sb; wave w its rows 16 w ..; it loops over hpw of the
+// group's heads (head group k of nhg) with the tile's sum in registers and
+// writes it as Ws in the operand type, or, with several head groups, as an
+// fp32 partial sum that a separate pass adds up.
 template <typename T, bool DIAG>
 __global__ void __launch_bounds__(256)
 kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restrict__ cb,
@@ -181,11 +182,41 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
             const bool ok = active && (!DIAG || (st * 16 + r < SB && scol[st] <= lrow[i]));
             cbv[st][i] = ok ? cb[(cbase + lrow[i]) * Q + scol[st]] : 0.f;
         }
+    // x rows of block sb, one head at a time, shared by the four waves in
+    // LDS (two buffers, rows of pitch XP: conflict-free 16-byte reads along
+    // them); the next head's are loaded into registers while one is used
+    extern __shared__ __align__(16) unsigned char smem_raw[];
+    T *xs = reinterpret_cast<T *>(smem_raw);
+    const int XP = P + (sizeof(T) == 4 ? 4 : 8), xchunks = P / VEC, xtotal = SB * xchunks;
+    // vectors per thread held across a head (a headdim of 64; more are loaded in place)
+    constexpr int XPF = sizeof(T) == 4 ? 4 : 2;
+    frag xpre[XPF];
+    auto xsrc = [&](int hh, int v) -> frag {
+        const int row = v / xchunks, k = (v % xchunks) * VEC, ts = c * Q + sb * SB + row;
+        return ts < L ? load_frag(x + (((size_t)b * L + ts) * H + g * hpg + hh) * P + k) : zero_frag<T>();
+    };
+    auto prefetch = [&](int hh) {
+#pragma unroll
+        for (int u = 0; u < XPF; ++u)
+            if (tid + 256 * u < xtotal) xpre[u] = xsrc(hh, tid + 256 * u);
+    };
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
     const int h0 = hgi * hpw, h1 = min(hpg, h0 + hpw);
+    if (h0 < h1) prefetch(h0);
     for (int hh = h0; hh < h1; ++hh) {
         const int h = g * hpg + hh;
         const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
+        // (the buffer was last read two heads ago, before the previous barrier)
+        T *xb = xs + (size_t)((hh - h0) & 1) * 64 * XP;
+#pragma unroll
+        for (int u = 0; u < XPF; ++u) {
+            const int v = tid + 256 * u;
+            if (v < xtotal) *reinterpret_cast<frag *>(xb + (v / xchunks) * XP + (v % xchunks) * VEC) = xpre[u];
+        }
+        for (int v = tid + 256 * XPF; v < xtotal; v += 256)
+            *reinterpret_cast<frag *>(xb + (v / xchunks) * XP + (v % xchunks) * VEC) = xsrc(hh, v);
+        __syncthreads();
+        if (hh + 1 < h1) prefetch(hh + 1);
         // strict row and column sums of W, four products at a time in fp32
         float rs[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
         if (active) {
@@ -198,10 +229,8 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
                 const frag za = tr < L && k < P ? load_frag(arow + k) : zero_frag<T>();
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    const int ts = c * Q + sb * SB + st * 16 + r;
-                    const frag zb = st * 16 + r < SB && ts < L && k < P
-                                        ? load_frag(x + (((size_t)b * L + ts) * H + h) * P + k)
-                                        : zero_frag<T>();
+                    const frag zb = st * 16 + r < SB && k < P ? load_frag(xb + (st * 16 + r) * XP + k)
+                                                              : zero_frag<T>();
                     z[st] = Mma<T>::mma(za, zb, z[st]);
                 }
             }
@@ -1082,14 +1111,15 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
         const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
         const int hpw = bwd_wsum_heads(ntile, f.nchunks, f.G, f.batch, hpg);
         const int nhg = (hpg + hpw - 1) / hpw;
+        const size_t lds = 2 * 64 * (size_t)(f.P + (sizeof(T) == 4 ? 4 : 8)) * sizeof(T);
         hipLaunchKernelGGL((kb_wsum<T, true>), dim3(nrb, f.nchunks * f.G * nhg, f.batch),
-                           dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
+                           dim3(256), lds, stream, (const T *)f.x, (const T *)a.dy,
                            (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
                            (const float *)f.dtT, (T *)a.wsm, nhg > 1 ? a.wpart : nullptr, a.rowp,
                            a.colp, f.L, f.H, f.G, f.P, f.nchunks, f.Q, hpw);
         if (nrb > 1)
             hipLaunchKernelGGL((kb_wsum<T, false>), dim3(ntile - nrb, f.nchunks * f.G * nhg, f.batch),
-                               dim3(256), 0, stream, (const T *)f.x, (const T *)a.dy,
+                               dim3(256), lds, stream, (const T *)f.x, (const T *)a.dy,
                                (const float *)f.cb, (const float *)f.acum_hi,
                                (const float *)f.acum_lo, (const float *)f.dtT, (T *)a.wsm,
                                nhg > 1 ? a.wpart : nullptr, a.rowp, a.colp, f.L, f.H, f.G, f.P,
