@@ -389,6 +389,8 @@ struct KbLds {
     static size_t bytes(int WP, int sz) {
         return (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64;
     }
+    // kb_dx: + (bf16) the row block's x, then dx, by token, shaped as V
+    static size_t dx_bytes(int WP, int sz) { return bytes(WP, sz) + (sz == 4 ? 0 : v_elems(WP, sz) * sz); }
 };
 
 typedef __bf16 kb_bf16x4 __attribute__((ext_vector_type(4)));
@@ -449,7 +451,7 @@ __device__ __forceinline__ typename Mma<T>::frag kb_across(const T *tile, int kk
 //
 // grid (H, nc * nrb, b) (heads fastest: the workgroups running together
 // share a chunk's C B^T in L2, and with H a multiple of 8 a head's row
-// blocks share an XCD), 256 threads, dynamic LDS KbLds::bytes(16 NW).  Wave
+// blocks share an XCD), 256 threads, dynamic LDS KbLds::dx_bytes(16 NW).  Wave
 // w owns rows 16 w ..; NW 16-column tiles span P.  The source blocks run
 // from the chunk's last down to the diagonal one, which leaves dy of the
 // row block itself staged for the epilogue.  The weighted C B^T block is
@@ -478,7 +480,12 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
-    float *red = r_dt + 256;                             // [4]
+    float *red = r_dt + 256;                             // [16]
+    T *XS = reinterpret_cast<T *>(red + 16);             // (bf16) [SBX][VP]: x, then dx, of the row block
+    // bf16: x and dx pass through LDS as rows (16-byte accesses); fp32 (whose
+    // LDS would then halve the workgroups per CU) keeps x at the lane's
+    // output positions in registers and stores dx from them
+    constexpr bool XST = SZ != 4;
 
     const int nrb = Q > SBX ? Q / SBX : 1;
     const int h = blockIdx.x, c = blockIdx.y / nrb, lb = blockIdx.y % nrb, b = blockIdx.z;
@@ -497,19 +504,37 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
         r_lo[l] = acum_lo[vbase + l];
         r_dt[l] = dtT[vbase + l];
     }
-    // x at this lane's output positions (rows 4 q + i of the wave's 16,
-    // columns 16 wt + r)
-    float xv[4][NW];
+    // x rows of the row block (zero past L or P); per thread NV vectors
+    constexpr int wv = WP / VEC, NV = SBX * wv / 256;
+    const T *xrow = x + ((size_t)b * L * H + h) * P;
+    float xv[XST ? 1 : 4][XST ? 1 : NW];
+    if constexpr (XST) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-        const bool tin = active && t < L && l < Q;
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC, t = c * Q + lb * SB + sl;
+            *reinterpret_cast<frag *>(XS + sl * VP + w0) =
+                sl < SB && t < L && w0 < P ? load_frag(xrow + (size_t)t * H * P + w0) : zero_frag<T>();
+        }
+    } else {
 #pragma unroll
-        for (int wt = 0; wt < NW; ++wt) {
-            const int p = wt * 16 + r;
-            xv[i][wt] = tin && p < P ? to_f32(x[(((size_t)b * L + t) * H + h) * P + p]) : 0.f;
+        for (int i = 0; i < 4; ++i) {
+            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
+            const bool tin = active && t < L && l < Q;
+#pragma unroll
+            for (int wt = 0; wt < NW; ++wt) {
+                const int p = wt * 16 + r;
+                xv[i][wt] = tin && p < P ? to_f32(xrow[(size_t)t * H * P + p]) : 0.f;
+            }
         }
     }
+    // x at this lane's output positions (rows 4 q + i of the wave's 16,
+    // columns 16 wt + r)
+    auto xat = [&](int i, int wt) -> float {
+        if constexpr (XST)
+            return to_f32(XS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]);
+        else
+            return xv[i][wt];
+    };
     __syncthreads();
     const float e_te = fast_exp(prefix_diff(r_hi[Q - 1], r_lo[Q - 1], r_hi[te], r_lo[te]));
     float rowf[4];
@@ -558,7 +583,7 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
         for (int i = 0; i < 4; ++i) {
             v[i] = 0.f;
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) v[i] += xv[i][wt] * acc[wt][i];
+            for (int wt = 0; wt < NW; ++wt) v[i] += xat(i, wt) * acc[wt][i];
             v[i] *= rowf[i];
         }
         const float sv = row16_sum4(v, r);
@@ -571,7 +596,7 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     const T *vsrc = dy + ((size_t)b * L * H + h) * P;
     // per thread and block: NV operand vectors of dy, NC float4 of C B^T
     // (rows and columns up to kSB; those past SBK are zeros never read)
-    constexpr int wv = WP / VEC, NV = SBX * wv / 256, NC = SBX * (SBX / 4) / 256;
+    constexpr int NC = SBX * (SBX / 4) / 256;
     for (int sb = nrb - 1; sb >= lb; --sb) {
         // the block's loads, issued before the barrier that frees the previous block
         frag vpre[NV];
@@ -634,24 +659,30 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
         }
     }
 
-    // ---- the epilogue: dx, x . u, dD (dy from the staged diagonal block)
+    // ---- the epilogue: dx, x . u, dD (dy from the staged diagonal block).
+    // bf16: each wave puts its rows' dx over their x in XS (only it reads
+    // those rows), and the workgroup then stores XS by rows.
     if (active) {
         const float Dh = D ? D[h] : 0.f;
         float dsum = 0.f, ds[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl, t = c * Q + l;
-            const bool tin = t < L && l < Q;
+            const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl;
             const float dtl = r_dt[l];
-            const size_t ro = (((size_t)b * L + t) * H + h) * P;
             ds[i] = 0.f;
 #pragma unroll
             for (int wt = 0; wt < NW; ++wt) {
                 const int p = wt * 16 + r;
-                const float gv = to_f32(VS[sl * VP + p]), u = acc[wt][i];
-                ds[i] += xv[i][wt] * u;
-                dsum += gv * xv[i][wt];
-                if (tin && p < P) out[ro + p] = from_f32<T>(Dh * gv + dtl * u);
+                const float gv = to_f32(VS[sl * VP + p]), xs = xat(i, wt), u = acc[wt][i];
+                ds[i] += xs * u;
+                dsum += gv * xs;
+                if constexpr (XST) {
+                    XS[sl * VP + p] = from_f32<T>(Dh * gv + dtl * u);
+                } else {
+                    const int t = c * Q + l;
+                    if (t < L && l < Q && p < P)
+                        out[((size_t)b * L * H + h) * P + (size_t)t * H * P + p] = from_f32<T>(Dh * gv + dtl * u);
+                }
             }
         }
         {
@@ -663,6 +694,16 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
         if (lane == 0) red[wave] = dsum;
     }
     __syncthreads();
+    if constexpr (XST) {
+        T *orow = out + ((size_t)b * L * H + h) * P;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int v = tid + 256 * u, sl = v / wv, w0 = (v % wv) * VEC, t = c * Q + lb * SB + sl;
+            if (sl < SB && t < L && w0 < P)
+                *reinterpret_cast<frag *>(orow + (size_t)t * H * P + w0) =
+                    *reinterpret_cast<const frag *>(XS + sl * VP + w0);
+        }
+    }
     if (tid == 0) {
         float sdd = 0.f;
         for (int w = 0; w < 4; ++w)
@@ -1056,7 +1097,7 @@ static void launch_dx(const BackwardArgs &a, hipStream_t stream) {
     const ForwardArgs &f = a.f;
     const int nrb = bwd_row_blocks(f.Q);
     hipLaunchKernelGGL((kb_dx<T, NW>), dim3(f.H, f.nchunks * nrb, f.batch), dim3(256),
-                       KbLds::bytes(16 * NW, (int)sizeof(T)), stream, (const T *)f.x,
+                       KbLds::dx_bytes(16 * NW, (int)sizeof(T)), stream, (const T *)f.x,
                        (const T *)f.B, (const T *)a.dy, (const float *)f.cb, (const float *)a.adj,
                        (const float *)f.acum_hi, (const float *)f.acum_lo, (const float *)f.dtT,
                        f.D, (T *)a.dx, a.dint, a.dd, a.dDpart, f.L, f.H, f.G, f.P, f.N,
