@@ -386,8 +386,11 @@ struct KbLds {
                    : (size_t)srows(WP, sz) * spitch(WP, sz, kDb);
     }
     // + prefix sums and dt by token and a reduction slot per wave (fp32)
+    // (kDb / kDc reuse the space for their fp32 output rows, [kSB][WP + 4])
     static size_t bytes(int WP, int sz) {
-        return (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64;
+        const size_t n = (v_elems(WP, sz) + m_elems(sz) + s_elems(WP, sz)) * sz + 3 * 256 * 4 + 64;
+        const size_t o = (size_t)kSB * (WP + 4) * 4;
+        return n > o ? n : o;
     }
     // kb_dx: + (bf16) the row block's x, then dx, by token, shaped as V
     static size_t dx_bytes(int WP, int sz) { return bytes(WP, sz) + (sz == 4 ? 0 : v_elems(WP, sz) * sz); }
@@ -768,21 +771,14 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
     f32x4 tot[NW];
 #pragma unroll
     for (int i = 0; i < NW; ++i) tot[i] = zero4();
-    // kDc: C at this lane's output positions (rows 4 q + i of the wave's 16,
-    // columns 16 wt + r), the same for every head of the group, held in
-    // registers up to 128 columns
-    constexpr bool CREG = MODE == kDc && NW <= 8;
-    T cpos[CREG ? NW : 1][4];
-    if constexpr (CREG) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-            const bool tin = active && t < L && l < Q;
-#pragma unroll
-            for (int wt = 0; wt < NW; ++wt) {
-                const int w = wt * 16 + r;
-                cpos[wt][i] = tin && w < N ? Cm[(((size_t)b * L + t) * G + g) * N + w] : from_f32<T>(0.f);
-            }
+    // kDc: the row block's C rows, the same for every head of the group, in
+    // VS while the heads run (the intra-chunk product reuses VS afterwards)
+    if constexpr (MODE == kDc) {
+        constexpr int wvc = WP / VEC;
+        for (int v = tid; v < SBX * wvc; v += 256) {
+            const int sl = v / wvc, w0 = (v % wvc) * VEC, t = t0 + sl;
+            *reinterpret_cast<frag *>(VS + sl * VP + w0) =
+                sl < SB && t < L && w0 < N ? load_frag(Cm + (((size_t)b * L + t) * G + g) * N + w0) : zero_frag<T>();
         }
     }
 
@@ -871,19 +867,10 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
                 float v[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) {
-                    const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-                    const bool tin = t < L && l < Q;
                     v[i] = 0.f;
 #pragma unroll
-                    for (int wt = 0; wt < NW; ++wt) {
-                        const int w = wt * 16 + r;
-                        if constexpr (CREG) {
-                            v[i] += to_f32(cpos[wt][i]) * acc[wt][i];
-                        } else {
-                            if (!tin || w >= N) continue;
-                            v[i] += to_f32(Cm[(((size_t)b * L + t) * G + g) * N + w]) * acc[wt][i];
-                        }
-                    }
+                    for (int wt = 0; wt < NW; ++wt)
+                        v[i] += to_f32(VS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]) * acc[wt][i];
                 }
                 const float sv = row16_sum4(v, r);
                 const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
@@ -958,23 +945,31 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             }
         }
     }
-    // ---- dB / dC rows of the row block
+    // ---- dB / dC rows of the row block, through LDS (fp32 rows of pitch
+    // WP + 4, over the operand buffers) and stored as rows of 4-vectors;
+    // several head groups write an fp32 partial sum each, added up afterwards
+    constexpr int OP = WP + 4;
+    float *OS = reinterpret_cast<float *>(smem_raw);
+    __syncthreads();   // (the operand buffers are no longer read)
     if (active) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int l = lb * SB + wave * 16 + 4 * q + i, t = c * Q + l;
-            if (t >= L || l >= Q) continue;
+        for (int i = 0; i < 4; ++i)
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) {
-                const int n = wt * 16 + r;
-                if (n >= N) continue;
-                const size_t o = (((size_t)b * L + t) * G + g) * N + n;
-                // (several head groups: an fp32 partial sum each, added up afterwards)
-                if (part)
-                    part[(size_t)hgi * gridDim.z * L * G * N + o] = tot[wt][i];
-                else
-                    out[o] = from_f32<T>(tot[wt][i]);
-            }
+            for (int wt = 0; wt < NW; ++wt) OS[(wave * 16 + 4 * q + i) * OP + wt * 16 + r] = tot[wt][i];
+    }
+    __syncthreads();
+    constexpr int oq = WP / 4;
+    for (int v = tid; v < SB * oq; v += 256) {
+        const int row = v / oq, n0 = (v % oq) * 4, t = t0 + row;
+        if (t >= L || n0 >= N) continue;
+        const f32x4 f = *reinterpret_cast<const f32x4 *>(OS + row * OP + n0);
+        const size_t o = (((size_t)b * L + t) * G + g) * N + n0;
+        if (part) {
+            *reinterpret_cast<f32x4 *>(part + (size_t)hgi * gridDim.z * L * G * N + o) = f;
+        } else if constexpr (F32) {
+            *reinterpret_cast<f32x4 *>(out + o) = f;
+        } else {
+            *reinterpret_cast<kb_bf16x4 *>(out + o) = kb_bf16x4{(bf16)f[0], (bf16)f[1], (bf16)f[2], (bf16)f[3]};
         }
     }
 }
