@@ -768,6 +768,9 @@ def main():
                     help="timed calls per other workload (counter runs use a few)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the other workloads and the decode timing")
+    ap.add_argument("--backward-only", action="store_true",
+                    help="of the other workloads, time only the gradient passes "
+                         "(for kernel traces and counters of the backward)")
     ap.add_argument("--traffic-json", default=os.path.join(ROOT, "profiles", "traffic.json"),
                     help="measured HBM traffic per launch of the dominant kernel "
                          "(from rocprofv3 FETCH_SIZE/WRITE_SIZE runs), if present")
@@ -805,7 +808,7 @@ def main():
     prepared = setup(w, dev)
     peaks = measure_peaks(dev, ev)
     extra, fwd_ms = {}, {}
-    if not args.no_extra:
+    if not args.no_extra and not args.backward_only:
         for name in ("tiny_f32", "mamba2_130m", "mamba2_130m_f32", "grouped_g8"):
             wx = WORKLOADS[name]
             # the tiny forward takes microseconds: 50 per captured graph
@@ -849,6 +852,8 @@ def main():
             w, dev, ev, steps=max(1, xs // 2), warmup=min(10, xs))
         extra["gated_rmsnorm_" + w.name] = time_norm(w, dev, ev, steps=max(1, xs // 2),
                                                      warmup=min(10, xs))
+    if not args.no_extra:
+        xs = args.extra_steps
         for name in ("mamba2_130m", "mamba2_130m_f32", w.name):
             extra["backward_" + name] = time_backward(WORKLOADS[name], dev, ev,
                                                       steps=max(2, min(10, xs // 10)),
