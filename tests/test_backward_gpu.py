@@ -82,6 +82,10 @@ CASES = [
     (1, 257, 4, 96, 128, 4, 128, "bf16", True),
     (1, 512, 2, 128, 256, 1, 256, "bf16", False),
     (2, 333, 6, 64, 128, 1, 64, "bf16", True),
+    # a multiple of 8 chunks: the dB / dC kernels place a chunk's row blocks
+    # on one XCD (a different workgroup-to-tile map)
+    (1, 1024, 4, 64, 128, 2, 128, "bf16", True),
+    (1, 2048, 2, 32, 64, 1, 256, "f32", False),
 ]
 
 
@@ -127,3 +131,42 @@ def test_backward_deterministic(dev):
     for k in KEYS:
         assert np.array_equal(a[k], b[k]), k
     torch.cuda.synchronize()
+
+
+def test_backward_full_size_sampled_heads(dev, oracle_mod):
+    """The 2.7B-shape layer (b4 L8192 H80 P64 N128 G1, Q256, bf16) in the
+    launch configuration bench times, against the oracle on three sampled
+    heads: their dx, ddt and dinit, and dA and dD (sums over the batch).  A
+    head's gradients depend only on its own inputs and the shared B and C,
+    so the oracle runs on those heads alone; dB and dC sum over all 80 heads
+    of the group, which a sample does not give (they are checked every
+    element on the smaller cases)."""
+    import torch
+    from state_space_sequence_amd import libssd
+    from state_space_sequence_amd.inputs import WORKLOADS, to_torch, workload_inputs
+    w = WORKLOADS["mamba2_2p7b"]
+    _say("workload %s, backward, sampled heads" % w.name)
+    inp = workload_inputs(w)
+    g = make_grad_inputs(w.batch, w.seqlen, w.nheads, w.headdim, w.dstate, w.io_dtype, seed=5)
+    t = to_torch(inp, w.io_dtype, dev)
+    dy = torch.from_numpy(g["dy"]).to(torch.bfloat16).to(dev)
+    df = torch.from_numpy(g["dfinal"]).to(dev)
+    out = libssd.ssd_chunk_scan_bwd(t["x"], t["dt"], t["A"], t["B"], t["C"], t["D"],
+                                    t["initial_state"], dy, df, chunk_len=w.chunk_len)
+    torch.cuda.synchronize()
+    heads = [0, 41, 79]
+    hs = torch.tensor(heads, device=dev)
+    got = {"dx": out["dx"].index_select(2, hs), "ddt": out["ddt"].index_select(2, hs),
+           "dinit": out["dinit"].index_select(1, hs), "dA": out["dA"][hs], "dD": out["dD"][hs]}
+    got = {k: v.float().cpu().numpy().astype(np.float64) for k, v in got.items()}
+    del out, t, dy, df
+    D, init = inp["D"], inp["initial_state"]   # (the workload has no initial state)
+    ref = oracle_mod.backward(inp["x"][:, :, heads], inp["dt"][:, :, heads], inp["A"][heads],
+                              inp["B"], inp["C"], None if D is None else D[heads],
+                              None if init is None else init[:, heads], g["dy"][:, :, heads],
+                              g["dfinal"][:, heads])
+    for k in ("dx", "ddt", "dA", "dD", "dinit"):
+        err = float(np.linalg.norm(got[k] - ref[k]) / max(np.linalg.norm(ref[k]), 1e-30))
+        _say("  2.7B heads %s %-5s err=%.3e tol=%.0e" % (heads, k, err, TOL["bf16"]))
+        assert np.all(np.isfinite(got[k])), k
+        assert err <= TOL["bf16"], "%s: %.3e" % (k, err)
