@@ -372,7 +372,7 @@ struct KbLds {
     }
     // + a slab of the state: kb_dx [WP][ks + 16 / sz] (Lam's rows cut to
     // the K-slab's columns), kDb / kDc [srows][WP + 16 / sz] (srows of the
-    // state's rows: the whole of a bf16 headdim of 64, at most 8192 values)
+    // state's rows, one MFMA K step, at most 8192 values)
     static __host__ __device__ constexpr int ks(int sz) { return sz == 4 ? 16 : 32; }
     static __host__ __device__ constexpr int srows(int WP, int sz) {
         return (sz == 4 ? 16 : 32) < 8192 / WP ? (sz == 4 ? 16 : 32) : 8192 / WP;
