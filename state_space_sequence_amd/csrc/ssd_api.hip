@@ -547,8 +547,23 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     if (poison_requested()) {
         if (ssd::launch_poison(workspace, lay.total, stream) != hipSuccess) return SSD_ERR_HIP;
     }
-    const hipError_t err = io_dtype == SSD_BF16 ? ssd::launch_backward<ssd::bf16>(a, stream, events)
-                                                : ssd::launch_backward<float>(a, stream, events);
+    hipError_t err;
+    if (!events) {
+        // the score tiles run on the device's side stream beside the
+        // adjoint products, the reverse state pass and dx (the timed entry
+        // point keeps every kernel on `stream`, in order)
+        std::lock_guard<std::mutex> lock(g_side_mu);
+        Side sd;
+        if (side_for(stream, &sd) != hipSuccess) return SSD_ERR_HIP;
+        a.f.side = sd.stream;
+        a.f.ev_fork = sd.fork;
+        a.f.ev_join = sd.join;
+        err = io_dtype == SSD_BF16 ? ssd::launch_backward<ssd::bf16>(a, stream, nullptr)
+                                   : ssd::launch_backward<float>(a, stream, nullptr);
+    } else {
+        err = io_dtype == SSD_BF16 ? ssd::launch_backward<ssd::bf16>(a, stream, events)
+                                   : ssd::launch_backward<float>(a, stream, events);
+    }
     if (err != hipSuccess) return SSD_ERR_HIP;
     fc.output(dx, nx, es);
     fc.output(ddt, ntok, 4);

@@ -1126,9 +1126,46 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     auto mark = [&]() -> hipError_t {
         return events ? hipEventRecord(events[ev++], stream) : hipSuccess;
     };
+    // Without per-kernel events and with a side stream, the score tiles
+    // (which need only the recompute's prefix sums and C B^T) run on the
+    // side stream beside the adjoint products, the reverse state pass and
+    // dx; dB and dC wait for both.
+    const bool fork = !events && f.side != nullptr;
+    auto launch_wsum = [&](hipStream_t s) {
+        const int nrb = bwd_row_blocks(f.Q);
+        const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
+        const int hpw = bwd_wsum_heads(ntile, f.nchunks, f.G, f.batch, hpg);
+        const int nhg = (hpg + hpw - 1) / hpw;
+        const size_t lds = 2 * 64 * (size_t)(f.P + (sizeof(T) == 4 ? 4 : 8)) * sizeof(T);
+        hipLaunchKernelGGL((kb_wsum<T, true>), dim3(nrb, f.nchunks * f.G * nhg, f.batch),
+                           dim3(256), lds, s, (const T *)f.x, (const T *)a.dy,
+                           (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
+                           (const float *)f.dtT, (T *)a.wsm, nhg > 1 ? a.wpart : nullptr, a.rowp,
+                           a.colp, f.L, f.H, f.G, f.P, f.nchunks, f.Q, hpw);
+        if (nrb > 1)
+            hipLaunchKernelGGL((kb_wsum<T, false>), dim3(ntile - nrb, f.nchunks * f.G * nhg, f.batch),
+                               dim3(256), lds, s, (const T *)f.x, (const T *)a.dy,
+                               (const float *)f.cb, (const float *)f.acum_hi,
+                               (const float *)f.acum_lo, (const float *)f.dtT, (T *)a.wsm,
+                               nhg > 1 ? a.wpart : nullptr, a.rowp, a.colp, f.L, f.H, f.G, f.P,
+                               f.nchunks, f.Q, hpw);
+        if (nhg > 1) {
+            // (entries of a chunk's Q x Q block above its diagonal blocks stay
+            // unwritten and are never read)
+            const size_t n = (size_t)f.batch * f.nchunks * f.G * f.Q * f.Q;
+            hipLaunchKernelGGL(kb_sum_heads<T>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
+                               s, (const float *)a.wpart, (T *)a.wsm, n, nhg);
+        }
+    };
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
     if ((err = launch_split_states<T>(f, stream)) != hipSuccess) return err;
+    if (fork) {
+        if ((err = hipEventRecord(f.ev_fork, stream)) != hipSuccess) return err;
+        if ((err = hipStreamWaitEvent(f.side, f.ev_fork, 0)) != hipSuccess) return err;
+        launch_wsum(f.side);
+        if ((err = hipEventRecord(f.ev_join, f.side)) != hipSuccess) return err;
+    }
     if ((err = mark()) != hipSuccess) return err;
     if ((err = launch_adj_chunk_states<T>(f, a.dy, a.adj, stream)) != hipSuccess) return err;
     if ((err = mark()) != hipSuccess) return err;
@@ -1142,31 +1179,10 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     else
         launch_dx<T, 8>(a, stream);
     if ((err = mark()) != hipSuccess) return err;
-    {
-        const int nrb = bwd_row_blocks(f.Q);
-        const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
-        const int hpw = bwd_wsum_heads(ntile, f.nchunks, f.G, f.batch, hpg);
-        const int nhg = (hpg + hpw - 1) / hpw;
-        const size_t lds = 2 * 64 * (size_t)(f.P + (sizeof(T) == 4 ? 4 : 8)) * sizeof(T);
-        hipLaunchKernelGGL((kb_wsum<T, true>), dim3(nrb, f.nchunks * f.G * nhg, f.batch),
-                           dim3(256), lds, stream, (const T *)f.x, (const T *)a.dy,
-                           (const float *)f.cb, (const float *)f.acum_hi, (const float *)f.acum_lo,
-                           (const float *)f.dtT, (T *)a.wsm, nhg > 1 ? a.wpart : nullptr, a.rowp,
-                           a.colp, f.L, f.H, f.G, f.P, f.nchunks, f.Q, hpw);
-        if (nrb > 1)
-            hipLaunchKernelGGL((kb_wsum<T, false>), dim3(ntile - nrb, f.nchunks * f.G * nhg, f.batch),
-                               dim3(256), lds, stream, (const T *)f.x, (const T *)a.dy,
-                               (const float *)f.cb, (const float *)f.acum_hi,
-                               (const float *)f.acum_lo, (const float *)f.dtT, (T *)a.wsm,
-                               nhg > 1 ? a.wpart : nullptr, a.rowp, a.colp, f.L, f.H, f.G, f.P,
-                               f.nchunks, f.Q, hpw);
-        if (nhg > 1) {
-            // (entries of a chunk's Q x Q block above its diagonal blocks stay
-            // unwritten and are never read)
-            const size_t n = (size_t)f.batch * f.nchunks * f.G * f.Q * f.Q;
-            hipLaunchKernelGGL(kb_sum_heads<T>, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0,
-                               stream, (const float *)a.wpart, (T *)a.wsm, n, nhg);
-        }
+    if (fork) {
+        if ((err = hipStreamWaitEvent(stream, f.ev_join, 0)) != hipSuccess) return err;
+    } else {
+        launch_wsum(stream);
     }
     if ((err = mark()) != hipSuccess) return err;
     if (f.N <= 128)
