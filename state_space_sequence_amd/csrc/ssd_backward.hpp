@@ -71,9 +71,11 @@ inline int bwd_head_groups(int batch, int nc, int nrb, int G, int hpg) {
 constexpr int kBackwardKernels = 9;
 extern const char *const kBackwardKernelNames[kBackwardKernels];
 
-// The first four kernels of the split forward (k1 .. k4), and k3 in its
+// The first four kernels of the split forward (k1 .. k4; `cb_done`, if not
+// null, recorded on `stream` once k1 and k2 are queued), and k3 in its
 // gradient form (G_c = sum_s dy_s exp(acum_s) C_s^T into `out`).
-template <typename T> hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream);
+template <typename T>
+hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream, hipEvent_t cb_done = nullptr);
 template <typename T>
 hipError_t launch_adj_chunk_states(const ForwardArgs &a, const void *dy, float *out,
                                    hipStream_t stream);

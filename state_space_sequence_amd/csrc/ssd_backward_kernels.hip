@@ -1128,8 +1128,9 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     };
     // Without per-kernel events and with a side stream, the score tiles
     // (which need only the recompute's prefix sums and C B^T) run on the
-    // side stream beside the adjoint products, the reverse state pass and
-    // dx; dB and dC wait for both.
+    // side stream beside the recompute's chunk states and their pass, the
+    // adjoint products, the reverse state pass and dx; dB and dC wait for
+    // both.
     const bool fork = !events && f.side != nullptr;
     auto launch_wsum = [&](hipStream_t s) {
         const int nrb = bwd_row_blocks(f.Q);
@@ -1159,9 +1160,11 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     };
     hipError_t err;
     if ((err = mark()) != hipSuccess) return err;
-    if ((err = launch_split_states<T>(f, stream)) != hipSuccess) return err;
+    // (the fork is recorded once the prefix sums and C B^T are queued, so the
+    // score tiles also overlap the recompute's chunk states and their pass)
+    if ((err = launch_split_states<T>(f, stream, fork ? f.ev_fork : nullptr)) != hipSuccess)
+        return err;
     if (fork) {
-        if ((err = hipEventRecord(f.ev_fork, stream)) != hipSuccess) return err;
         if ((err = hipStreamWaitEvent(f.side, f.ev_fork, 0)) != hipSuccess) return err;
         launch_wsum(f.side);
         if ((err = hipEventRecord(f.ev_join, f.side)) != hipSuccess) return err;

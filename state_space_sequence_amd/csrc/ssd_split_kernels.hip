@@ -1045,7 +1045,7 @@ void launch_k3(const ForwardArgs &a, const void *xx, const void *bb, float *out,
 // states, state passing; a.final_state receives the final state): what the
 // gradient pass recomputes.
 template <typename T>
-hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream) {
+hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream, hipEvent_t cb_done) {
     const int nc = a.nchunks, Q = a.Q;
     launch_dA_cumsum(a.dt, a.dtp, a.A, a.acum_hi, a.acum_lo, a.dtT, a.batch, a.L, a.H, nc, Q,
                      stream);
@@ -1053,6 +1053,10 @@ hipError_t launch_split_states(const ForwardArgs &a, hipStream_t stream) {
     hipLaunchKernelGGL(k2_chunk_cb<T>, dim3(nlb * (nlb + 1) / 2, nc * a.G, a.batch),
                        dim3(256), 0, stream, (const T *)a.B, (const T *)a.C, (float *)a.cb, a.L,
                        a.G, a.N, nc, Q);
+    if (cb_done) {
+        const hipError_t err = hipEventRecord(cb_done, stream);
+        if (err != hipSuccess) return err;
+    }
     launch_k3<T, false>(a, a.x, a.B, a.S, nullptr, stream);
     const int PN = a.P * a.N;
     hipLaunchKernelGGL(k4_state_passing, dim3((PN + 1023) / 1024, a.H, a.batch), dim3(256),
@@ -1068,8 +1072,8 @@ hipError_t launch_adj_chunk_states(const ForwardArgs &a, const void *dy, float *
     return hipGetLastError();
 }
 
-template hipError_t launch_split_states<float>(const ForwardArgs &, hipStream_t);
-template hipError_t launch_split_states<bf16>(const ForwardArgs &, hipStream_t);
+template hipError_t launch_split_states<float>(const ForwardArgs &, hipStream_t, hipEvent_t);
+template hipError_t launch_split_states<bf16>(const ForwardArgs &, hipStream_t, hipEvent_t);
 template hipError_t launch_adj_chunk_states<float>(const ForwardArgs &, const void *, float *, hipStream_t);
 template hipError_t launch_adj_chunk_states<bf16>(const ForwardArgs &, const void *, float *, hipStream_t);
 
