@@ -58,15 +58,17 @@ hipError_t scratch_address(hipStream_t stream, void **out) {
 }
 
 // The auxiliary stream and fork/join events on which a segmented fused
-// forward overlaps its first phase: one set per device, created with that
-// device current at the first segmented call and kept until the process
-// ends (default priority; non-blocking with respect to the null stream).
+// forward overlaps its first phase and the gradient pass two of its kernels
+// (a third event marks the recomputed states): one set per device, created
+// with that device current at the first call that uses it and kept until
+// the process ends (default priority; non-blocking with respect to the null
+// stream).
 // The mutex is held across each call's fork ... join sequence, so that
 // concurrent calls never re-record an event between another call's record
 // and its wait.
 struct Side {
     hipStream_t stream = nullptr;
-    hipEvent_t fork = nullptr, join = nullptr;
+    hipEvent_t fork = nullptr, join = nullptr, mid = nullptr;
 };
 std::mutex g_side_mu;
 Side g_side[kMaxDevices];
@@ -85,6 +87,7 @@ hipError_t side_for(hipStream_t stream, Side *out) {
         err = hipStreamCreateWithFlags(&n.stream, hipStreamNonBlocking);
         if (err == hipSuccess) err = hipEventCreateWithFlags(&n.fork, hipEventDisableTiming);
         if (err == hipSuccess) err = hipEventCreateWithFlags(&n.join, hipEventDisableTiming);
+        if (err == hipSuccess) err = hipEventCreateWithFlags(&n.mid, hipEventDisableTiming);
         if (dev != cur) {
             const hipError_t back = hipSetDevice(cur);
             if (err == hipSuccess) err = back;
@@ -549,15 +552,16 @@ ssd_status backward_impl(const void *x, const float *dt, const float *A, const v
     }
     hipError_t err;
     if (!events) {
-        // the score tiles run on the device's side stream beside the
-        // adjoint products, the reverse state pass and dx (the timed entry
-        // point keeps every kernel on `stream`, in order)
+        // the score tiles and dC run on the device's side stream beside the
+        // recompute, the adjoint products, the reverse state pass and dx
+        // (the timed entry point keeps every kernel on `stream`, in order)
         std::lock_guard<std::mutex> lock(g_side_mu);
         Side sd;
         if (side_for(stream, &sd) != hipSuccess) return SSD_ERR_HIP;
         a.f.side = sd.stream;
         a.f.ev_fork = sd.fork;
         a.f.ev_join = sd.join;
+        a.ev_states = sd.mid;
         err = io_dtype == SSD_BF16 ? ssd::launch_backward<ssd::bf16>(a, stream, nullptr)
                                    : ssd::launch_backward<float>(a, stream, nullptr);
     } else {

@@ -35,6 +35,9 @@ struct BackwardArgs {
     float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
     double *dApart; // [b][nc][H]: partial sums of dt * dLoss/d(dt A)
     float *partB, *partC; // [nhg][b][L][G][N]: per head group dB / dC (nhg > 1)
+    // with f.side: recorded on the call's stream once the recomputed states
+    // are queued (the side stream's dC waits for it)
+    hipEvent_t ev_states = nullptr;
 };
 
 // Slices of a state (4 elements per thread, 256 threads) in the reverse

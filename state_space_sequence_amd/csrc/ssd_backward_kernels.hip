@@ -1127,11 +1127,17 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
         return events ? hipEventRecord(events[ev++], stream) : hipSuccess;
     };
     // Without per-kernel events and with a side stream, the score tiles
-    // (which need only the recompute's prefix sums and C B^T) run on the
-    // side stream beside the recompute's chunk states and their pass, the
-    // adjoint products, the reverse state pass and dx; dB and dC wait for
-    // both.
-    const bool fork = !events && f.side != nullptr;
+    // (which need only the recompute's prefix sums and C B^T) and then dC
+    // (which needs them and the recomputed states) run on the side stream,
+    // beside the recompute's chunk states and their pass, the adjoint
+    // products, the reverse state pass and dx; dB waits for both streams.
+    const bool fork = !events && f.side != nullptr && a.ev_states != nullptr;
+    auto launch_dc = [&](hipStream_t s) {
+        if (f.N <= 128)
+            launch_mix<T, kDc, 8>(a, a.dC, a.partC, s);
+        else
+            launch_mix<T, kDc, 16>(a, a.dC, a.partC, s);
+    };
     auto launch_wsum = [&](hipStream_t s) {
         const int nrb = bwd_row_blocks(f.Q);
         const int ntile = nrb * (nrb + 1) / 2, hpg = f.H / f.G;
@@ -1165,8 +1171,11 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     if ((err = launch_split_states<T>(f, stream, fork ? f.ev_fork : nullptr)) != hipSuccess)
         return err;
     if (fork) {
+        if ((err = hipEventRecord(a.ev_states, stream)) != hipSuccess) return err;
         if ((err = hipStreamWaitEvent(f.side, f.ev_fork, 0)) != hipSuccess) return err;
         launch_wsum(f.side);
+        if ((err = hipStreamWaitEvent(f.side, a.ev_states, 0)) != hipSuccess) return err;
+        launch_dc(f.side);
         if ((err = hipEventRecord(f.ev_join, f.side)) != hipSuccess) return err;
     }
     if ((err = mark()) != hipSuccess) return err;
@@ -1193,10 +1202,7 @@ hipError_t launch_backward(const BackwardArgs &a, hipStream_t stream, hipEvent_t
     else
         launch_mix<T, kDb, 16>(a, a.dB, a.partB, stream);
     if ((err = mark()) != hipSuccess) return err;
-    if (f.N <= 128)
-        launch_mix<T, kDc, 8>(a, a.dC, a.partC, stream);
-    else
-        launch_mix<T, kDc, 16>(a, a.dC, a.partC, stream);
+    if (!fork) launch_dc(stream);
     if ((err = mark()) != hipSuccess) return err;
     hipLaunchKernelGGL(kb_ddt, dim3(f.nchunks, f.H, f.batch), dim3(256), 0, stream,
                        (const float *)a.roff, (const float *)a.dint, (const float *)a.dd,
