@@ -38,10 +38,11 @@
  *    the legacy default stream) and nothing synchronises the host: results
  *    are ready when the stream is.  The one state it keeps: a forward on
  *    the fused path that cuts a long sequence of a narrow layer into
- *    segments (see ssd_chunk_scan_fwd) forks part of its work onto an
- *    auxiliary stream of its own and joins it back to `stream` with two
- *    events; that stream and the events are created per device at the first
- *    such call (default priority) and kept until the process ends.
+ *    segments (see ssd_chunk_scan_fwd), and the gradient pass
+ *    (ssd_chunk_scan_bwd, not its _timed form), fork part of their work onto
+ *    an auxiliary stream of the library's and join it back to `stream` with
+ *    events; that stream and three events are created per device at the
+ *    first such call (default priority) and kept until the process ends.
  *  - Errors are reported as status codes, never by exceptions or aborts.
  *    Argument validation happens before anything is enqueued, so a call that
  *    returns SSD_ERR_INVALID_ARGUMENT, SSD_ERR_UNSUPPORTED or
@@ -273,7 +274,9 @@ ssd_status ssd_chunk_scan_fwd_timed(const void *x, const float *dt, const float 
  * The call recomputes the forward's prefix sums, C B^T blocks and chunk
  * states (the split path's first four kernels, with this chunk_len), then
  * runs the gradient kernels; nothing from a forward call is needed.  The
- * outputs must not overlap the inputs or each other.  dA and dD are summed
+ * score tiles and dC run on the library's auxiliary stream of the device
+ * (see above), joined back to `stream` before dB.  The outputs must not
+ * overlap the inputs or each other.  dA and dD are summed
  * in a fixed order: the results are deterministic.  Accumulation is fp32;
  * bf16 runs round the products' operands to bf16 like the forward.  Errors
  * as for ssd_chunk_scan_fwd (dy and the seven outputs but dD and
