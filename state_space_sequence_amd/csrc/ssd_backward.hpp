@@ -47,11 +47,11 @@ inline int bwd_state_slices(int P, int N) { return (P * N + 1023) / 1024; }
 inline int bwd_row_blocks(int Q) { return Q > 64 ? Q / 64 : 1; }
 
 // Heads per workgroup of the dB and dC kernels, which sum over a group's
-// heads: enough head groups for about 8192 workgroups (then each group's
+// heads: enough head groups for about 2048 workgroups (then each group's
 // fp32 partial sum is added up by a separate pass).
 inline int bwd_heads_per_group(int batch, int nc, int nrb, int G, int hpg) {
     const long wg = (long)batch * nc * nrb * G;
-    long ng = (8192 + wg - 1) / wg;
+    long ng = (2048 + wg - 1) / wg;
     if (ng > hpg) ng = hpg;
     if (ng < 1) ng = 1;
     return (int)((hpg + ng - 1) / ng);

@@ -370,9 +370,9 @@ def test_backward_workspace_size(lib):
     assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, G, Q, 1, ctypes.byref(out)) == 0
     fwd_split = 3 * b * H * nc * Q * 4 + b * nc * G * Q * Q * 4 + b * nc * H * P * N * 4 + b * nc * Q * 4
     # the dB / dC kernels split a group's 80 heads so that there are about
-    # 8192 workgroups: 512 (batch x chunks x row blocks) -> 16 groups of 5,
+    # 2048 workgroups: 512 (batch x chunks x row blocks) -> 4 groups of 20,
     # each with an fp32 partial dB and dC
-    nhg = 16
+    nhg = 4
     # the summed-score kernel: 10 tiles x 32 chunks x 4 rows = 1280 workgroups
     # -> 4 head groups of 20 for about 4096, each with fp32 partial tiles
     nhw = 4
