@@ -57,11 +57,11 @@ inline int bwd_heads_per_group(int batch, int nc, int nrb, int G, int hpg) {
     return (int)((hpg + ng - 1) / ng);
 }
 // Heads per workgroup of the summed-score kernel: enough head groups for
-// about 4096 workgroups (each group's fp32 partial tiles are added up by a
+// about 2048 workgroups (each group's fp32 partial tiles are added up by a
 // separate pass).
 inline int bwd_wsum_heads(int ntile, int nc, int G, int batch, int hpg) {
     const long wg = (long)ntile * nc * G * batch;
-    long ng = (4096 + wg - 1) / wg;
+    long ng = (2048 + wg - 1) / wg;
     if (ng > hpg) ng = hpg;
     if (ng < 1) ng = 1;
     return (int)((hpg + ng - 1) / ng);

@@ -188,8 +188,10 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *xs = reinterpret_cast<T *>(smem_raw);
     const int XP = P + (sizeof(T) == 4 ? 4 : 8), xchunks = P / VEC, xtotal = SB * xchunks;
-    // vectors per thread held across a head (a headdim of 64; more are loaded in place)
-    constexpr int XPF = sizeof(T) == 4 ? 4 : 2;
+    // vectors per thread held across a head (the rest are loaded in place):
+    // fp32 a headdim of 64; bf16 half of it, which keeps the kernel within
+    // 128 VGPRs (four waves per SIMD, against three with the whole head)
+    constexpr int XPF = sizeof(T) == 4 ? 4 : 1;
     frag xpre[XPF];
     auto xsrc = [&](int hh, int v) -> frag {
         const int row = v / xchunks, k = (v % xchunks) * VEC, ts = c * Q + sb * SB + row;
@@ -392,8 +394,13 @@ struct KbLds {
         const size_t o = (size_t)kSB * (WP + 4) * 4;
         return n > o ? n : o;
     }
-    // kb_dx: + (bf16) the row block's x, then dx, by token, shaped as V
-    static size_t dx_bytes(int WP, int sz) { return bytes(WP, sz) + (sz == 4 ? 0 : v_elems(WP, sz) * sz); }
+    // kb_dx: its state slabs are done before the first V block is staged,
+    // so they share V's space; + (bf16) the row block's x, then dx, by
+    // token, shaped as V
+    static size_t dx_bytes(int WP, int sz) {
+        const size_t vs = v_elems(WP, sz) > s_elems(WP, sz) ? v_elems(WP, sz) : s_elems(WP, sz);
+        return (vs + m_elems(sz) + (sz == 4 ? 0 : v_elems(WP, sz))) * sz + 3 * 256 * 4 + 64;
+    }
 };
 
 typedef __bf16 kb_bf16x4 __attribute__((ext_vector_type(4)));
@@ -477,10 +484,12 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     constexpr int SP = KbLds::spitch(WP, SZ, kDx);
     static_assert(KS == KbLds::ks(SZ), "state slab width");
     extern __shared__ __align__(16) unsigned char smem_raw[];
+    constexpr size_t VSE = KbLds::v_elems(WP, SZ) > KbLds::s_elems(WP, SZ) ? KbLds::v_elems(WP, SZ)
+                                                                           : KbLds::s_elems(WP, SZ);
     T *VS = reinterpret_cast<T *>(smem_raw);            // [SBX][VP]: dy of the source block
-    T *MT = VS + KbLds::v_elems(WP, SZ);                 // [SBX][PITCH]: weighted C B^T, rows s
-    T *SS = MT + KbLds::m_elems(SZ);                     // [WP][SP]: a K-slab of Lam's rows
-    float *r_hi = reinterpret_cast<float *>(SS + KbLds::s_elems(WP, SZ));
+    T *SS = VS;                                          // [WP][SP]: a K-slab of Lam's rows (before VS is used)
+    T *MT = VS + VSE;                                    // [SBX][PITCH]: weighted C B^T, rows s
+    float *r_hi = reinterpret_cast<float *>(MT + KbLds::m_elems(SZ));
     float *r_lo = r_hi + 256;
     float *r_dt = r_lo + 256;
     float *red = r_dt + 256;                             // [16]

@@ -374,8 +374,8 @@ def test_backward_workspace_size(lib):
     # each with an fp32 partial dB and dC
     nhg = 4
     # the summed-score kernel: 10 tiles x 32 chunks x 4 rows = 1280 workgroups
-    # -> 4 head groups of 20 for about 4096, each with fp32 partial tiles
-    nhw = 4
+    # -> 2 head groups of 40 for about 2048, each with fp32 partial tiles
+    nhw = 2
     extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 3 * b * H * nc * Q * 4 +
              b * nc * G * Q * Q * 2 + b * H * nc * nrb * Q * 8 + b * H * nc * nrb * 4 * Q * 8 +
              b * nc * H * nrb * 4 + b * nc * H * 8 + 2 * nhg * b * L * G * N * 4 +
