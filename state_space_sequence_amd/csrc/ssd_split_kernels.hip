@@ -77,23 +77,30 @@ k1_dA_cumsum(const float *__restrict__ dt, const DtProc dtp, const float *__rest
         }
         if (tid < Q) segst[((size_t)b * nc + c) * Q + tid] = s_st[tid];
     }
-    const int j = tid & 15;
-    for (int r = tid >> 4; r < Q; r += 16) {
-        const int h = h0 + j, t = c * Q + r;
-        float v = 0.f;
-        if (h < H && t < L) {
-            v = dt[((size_t)b * L + t) * H + h];
-            if (dtp.on) v = dt_process(v, dtp.bias ? dtp.bias[h] : 0.f, dtp.softplus, dtp.lo, dtp.hi);
-        }
-        s_dt[j][r] = v;
+    // this thread's tokens r0 + 16 k (Q <= 256: at most 16), all loads
+    // issued before the first is used
+    const int j = tid & 15, r0 = tid >> 4, h = h0 + j;
+    float dv[16];
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int r = r0 + 16 * k, t = c * Q + r;
+        dv[k] = r < Q && h < H && t < L ? dt[((size_t)b * L + t) * H + h] : 0.f;
+    }
+    const float bias = dtp.on && dtp.bias && h < H ? dtp.bias[h] : 0.f;
+#pragma unroll
+    for (int k = 0; k < 16; ++k) {
+        const int r = r0 + 16 * k, t = c * Q + r;
+        if (r < Q)
+            s_dt[j][r] = dtp.on && h < H && t < L ? dt_process(dv[k], bias, dtp.softplus, dtp.lo, dtp.hi)
+                                                  : dv[k];
     }
     __syncthreads();
     const int wave = tid >> 6, lane = tid & 63;
     const int E = Q > 64 ? Q / 64 : 1;
     for (int jj = 0; jj < 4; ++jj) {
-        const int hl = wave * 4 + jj, h = h0 + hl;
-        if (h >= H) break;
-        const double Ah = (double)A[h];
+        const int hl = wave * 4 + jj, hh = h0 + hl;
+        if (hh >= H) break;
+        const double Ah = (double)A[hh];
         double a[4];
         float d[4];
         double run = 0.0;
@@ -111,7 +118,22 @@ k1_dA_cumsum(const float *__restrict__ dt, const DtProc dtp, const float *__rest
         const double incl = wave_inclusive_scan_f64(run, lane);
         double excl = __shfl_up(incl, 1, kWave);
         if (lane == 0) excl = 0.0;
-        const size_t base = ((size_t)(b * H + h) * nc + c) * Q;
+        const size_t base = ((size_t)(b * H + hh) * nc + c) * Q;
+        if (E == 4) {
+            // (Q = 256: the lane's 4 tokens as one 16-byte store per array)
+            f32x4 vh, vl, vd;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                const double v = excl + a[e];
+                vh[e] = (float)v;
+                vl[e] = (float)(v - (double)vh[e]);
+                vd[e] = d[e];
+            }
+            *reinterpret_cast<f32x4 *>(acum_hi + base + 4 * lane) = vh;
+            *reinterpret_cast<f32x4 *>(acum_lo + base + 4 * lane) = vl;
+            *reinterpret_cast<f32x4 *>(dtT + base + 4 * lane) = vd;
+            continue;
+        }
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
             const int idx = lane * E + e;
