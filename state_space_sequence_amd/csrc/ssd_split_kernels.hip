@@ -153,7 +153,7 @@ k1_dA_cumsum(const float *__restrict__ dt, const DtProc dtp, const float *__rest
 // s-block of 64) pair with s-block <= l-block; wave w takes the 16 rows
 // l0 = 64*lb + 16*w against four 16-column s-tiles.  Operands are read
 // straight from global memory: rows of C and B are contiguous in n, which is
-// the MFMA k dimension here.
+// the MFMA k dimension here; a K step's loads are issued a step ahead.
 template <typename T>
 __global__ void __launch_bounds__(256)
 k2_chunk_cb(const T *__restrict__ Bm, const T *__restrict__ Cm,
@@ -177,18 +177,32 @@ k2_chunk_cb(const T *__restrict__ Bm, const T *__restrict__ Cm,
         act[st] = s0[st] < Q && s0[st] <= l0 + 15;
     }
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
-    for (int k0 = 0; k0 < N; k0 += KS) {
+    // the next K step's operands are loaded while this one's MFMAs run
+    typedef typename Mma<T>::frag frag;
+    auto load = [&](int k0, frag &a, frag (&bb)[4]) {
         const int k = k0 + VEC * q;
         const bool kin = k < N;
-        typename Mma<T>::frag a = (tl < L && kin) ? load_frag(crow + k) : zero_frag<T>();
+        a = (tl < L && kin) ? load_frag(crow + k) : zero_frag<T>();
 #pragma unroll
         for (int st = 0; st < 4; ++st) {
-            if (!act[st]) continue;
             const int ts = c * Q + s0[st] + r;
-            typename Mma<T>::frag bb =
-                (ts < L && kin) ? load_frag(Bm + (((size_t)b * L + ts) * G + g) * N + k)
-                                : zero_frag<T>();
-            acc[st] = Mma<T>::mma(a, bb, acc[st]);
+            bb[st] = (act[st] && ts < L && kin) ? load_frag(Bm + (((size_t)b * L + ts) * G + g) * N + k)
+                                                : zero_frag<T>();
+        }
+    };
+    frag a, bb[4];
+    load(0, a, bb);
+    for (int k0 = 0; k0 < N; k0 += KS) {
+        const bool more = k0 + KS < N;
+        frag an, bn[4];
+        if (more) load(k0 + KS, an, bn);
+#pragma unroll
+        for (int st = 0; st < 4; ++st)
+            if (act[st]) acc[st] = Mma<T>::mma(a, bb[st], acc[st]);
+        if (more) {
+            a = an;
+#pragma unroll
+            for (int st = 0; st < 4; ++st) bb[st] = bn[st];
         }
     }
     const size_t base = ((size_t)(b * nc + c) * G + g) * Q;
