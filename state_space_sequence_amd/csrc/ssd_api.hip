@@ -436,7 +436,7 @@ BwdLayout backward_layout(int batch, int seqlen, int nheads, int headdim, int ds
     l.rowp = off;
     off += round_up(b * H * nc * nrb * Q * sizeof(double));
     l.colp = off;
-    off += round_up(b * H * nc * nrb * 4 * Q * sizeof(double));
+    off += round_up(b * H * nc * nrb * Q * sizeof(double));
     l.dDpart = off;
     off += round_up(b * nc * H * nrb * sizeof(float));
     l.dApart = off;

@@ -31,7 +31,7 @@ struct BackwardArgs {
     void *wsm;      // [b][nc][G][Q][Q] io type: the group's summed score tiles Ws
     float *wpart;   // [nhg][b][nc][G][Q][Q]: per head group partial Ws (nhg > 1)
     double *rowp;   // [b][H][nc][nrb][Q]: strict row sums of W per (row block's) tile
-    double *colp;   // [b][H][nc][nrb][4][Q]: strict column sums of W per tile and wave
+    double *colp;   // [b][H][nc][nrb][Q]: strict column sums of W per (column block's) tile
     float *dDpart;  // [b][nc][H][nrb]: partial sums of dy . x
     double *dApart; // [b][nc][H]: partial sums of dt * dLoss/d(dt A)
     float *partB, *partC; // [nhg][b][L][G][N]: per head group dB / dC (nhg > 1)

@@ -120,7 +120,7 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // times (C_l . B_s); they are the prefix over k < t of (column sum -
 // row sum) of W's strict lower triangle (the entries with s < t, less
 // those with l < t), so this kernel also writes each head's strict row sums
-// (per tile) and column sums (per tile and wave): the fp32 entries summed
+// (per tile) and column sums (per tile): the fp32 entries summed
 // four at a time in fp32, then in fp64 (the prefix subtracts sums much
 // larger than the result).
 //
@@ -128,7 +128,8 @@ kb_state_passing(float *__restrict__ adj, const float *__restrict__ S,
 // grid (nrb (nrb - 1) / 2, nc * G * nhg, b), the tiles below them, where
 // every entry is strict and the decay factors through the last row of the
 // column block (one exponential per row and per column, not per entry).
-// 256 threads, dynamic LDS 2 x 64 rows of x (pitch P + 16 / sizeof(T)).
+// 256 threads, dynamic LDS 2 x 64 rows of x (pitch P + 16 / sizeof(T)), and
+// 4 KB of column sums.
 // Workgroup (lb, sb) (sb <= lb) owns the 64 x 64 tile of rows l in block lb,
 // columns s in block sb; wave w its rows 16 w ..; it loops over hpw of the
 // group's heads (head group k of nhg) with the tile's sum in registers and
@@ -204,12 +205,42 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     };
     f32x4 acc[4] = {zero4(), zero4(), zero4(), zero4()};
     const int h0 = hgi * hpw, h1 = min(hpg, h0 + hpw);
-    if (h0 < h1) prefetch(h0);
+    // the four waves' column sums of a head, added up after the next barrier
+    // (two buffers by head)
+    __shared__ double csum[2][4][64];
+    auto put_cols = [&](int hh) {
+        if (tid < SB) {
+            const double *cw = &csum[(hh - h0) & 1][0][tid];
+            colp[(((size_t)(b * H + g * hpg + hh) * nc + c) * nrb + lb) * Q + sb * SB + tid] =
+                ((cw[0] + cw[64]) + cw[128]) + cw[192];
+        }
+    };
+    // The per-token vectors the tile needs, in LDS, one head at a time (two
+    // buffers), loaded a head ahead, one array per wave: DIAG the block's
+    // prefix sums (hi, lo) and dt (waves 0-2); below the diagonal the prefix
+    // sums of row block lb (waves 0, 1) and of column block sb (waves 2, 3),
+    // and the column block's dt (wave 0 again)
+    constexpr int NA = DIAG ? 3 : 5;
+    __shared__ float tokv[2][NA][64];
+    const float *const tsrc = (wave & 1) ? acum_lo : DIAG && wave == 2 ? dtT : acum_hi;
+    const int tblk = (DIAG || wave < 2 ? lb : sb) * SB;
+    float tpre = 0.f, tpre2 = 0.f;
+    auto tok_load = [&](int hh) {
+        const size_t o = ((size_t)(b * H + g * hpg + hh) * nc + c) * Q + lane;
+        if (!DIAG || wave < 3) tpre = lane < SB ? tsrc[o + tblk] : 0.f;
+        if (!DIAG && wave == 0) tpre2 = lane < SB ? dtT[o + sb * SB] : 0.f;
+    };
+    if (h0 < h1) {
+        prefetch(h0);
+        tok_load(h0);
+    }
     for (int hh = h0; hh < h1; ++hh) {
         const int h = g * hpg + hh;
-        const size_t vbase = ((size_t)(b * H + h) * nc + c) * Q;
         // (the buffer was last read two heads ago, before the previous barrier)
         T *xb = xs + (size_t)((hh - h0) & 1) * 64 * XP;
+        const float *tk = &tokv[(hh - h0) & 1][0][0];
+        if (!DIAG || wave < 3) tokv[(hh - h0) & 1][wave][lane] = tpre;
+        if (!DIAG && wave == 0) tokv[(hh - h0) & 1][NA - 1][lane] = tpre2;
 #pragma unroll
         for (int u = 0; u < XPF; ++u) {
             const int v = tid + 256 * u;
@@ -218,7 +249,10 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
         for (int v = tid + 256 * XPF; v < xtotal; v += 256)
             *reinterpret_cast<frag *>(xb + (v / xchunks) * XP + (v % xchunks) * VEC) = xsrc(hh, v);
         __syncthreads();
-        if (hh + 1 < h1) prefetch(hh + 1);
+        if (hh + 1 < h1) {
+            prefetch(hh + 1);
+            tok_load(hh + 1);
+        }
         // strict row and column sums of W, four products at a time in fp32
         float rs[4] = {0.f, 0.f, 0.f, 0.f}, cs[4] = {0.f, 0.f, 0.f, 0.f};
         if (active) {
@@ -239,23 +273,22 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
             float lhi[4], llo[4];
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                lhi[i] = acum_hi[vbase + lrow[i]];
-                llo[i] = acum_lo[vbase + lrow[i]];
+                lhi[i] = tk[wave * 16 + 4 * q + i];
+                llo[i] = tk[64 + wave * 16 + 4 * q + i];
             }
             if constexpr (!DIAG) {
                 // below the diagonal (blocks of 64, all within the chunk)
                 // every entry is strict (s < l) and the decay factors
                 // through te, the last row of block sb: e^(acum_l - acum_s)
                 // = e^(acum_l - acum_te) e^(acum_te - acum_s), both at most 1
-                const int te = sb * SB + SB - 1;
-                const float thi = acum_hi[vbase + te], tlo = acum_lo[vbase + te];
+                const float thi = tk[128 + SB - 1], tlo = tk[192 + SB - 1];
                 float rf[4];
 #pragma unroll
                 for (int i = 0; i < 4; ++i) rf[i] = fast_exp(prefix_diff(lhi[i], llo[i], thi, tlo));
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
-                    const float shi = acum_hi[vbase + scol[st]], slo = acum_lo[vbase + scol[st]];
-                    const float cf = fast_exp(prefix_diff(thi, tlo, shi, slo)) * dtT[vbase + scol[st]];
+                    const float shi = tk[128 + st * 16 + r], slo = tk[192 + st * 16 + r];
+                    const float cf = fast_exp(prefix_diff(thi, tlo, shi, slo)) * tk[256 + st * 16 + r];
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         const float v = z[st][i] * rf[i] * cf;
@@ -269,9 +302,8 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
 #pragma unroll
                 for (int st = 0; st < 4; ++st) {
                     const bool cin = st * 16 + r < SB;
-                    const float shi = cin ? acum_hi[vbase + scol[st]] : 0.f;
-                    const float slo = cin ? acum_lo[vbase + scol[st]] : 0.f;
-                    const float sdt = cin ? dtT[vbase + scol[st]] : 0.f;
+                    const float shi = tk[st * 16 + r], slo = tk[64 + st * 16 + r];
+                    const float sdt = tk[128 + st * 16 + r];   // (0 past SB)
 #pragma unroll
                     for (int i = 0; i < 4; ++i) {
                         // (exponent clamped at 0: the entries above the
@@ -297,7 +329,7 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
                 rowp[(((size_t)(b * H + h) * nc + c) * nrb + sb) * Q + lb * SB + row] = v;
         }
         // columns: the same over the four row groups (lanes 16 apart) leaves
-        // column tile q's sum in row group q
+        // column tile q's sum in row group q; the waves' sums meet in LDS
         {
             const bool b5 = q & 2, b4 = q & 1;
             double k0 = b5 ? cs[2] : cs[0], k1 = b5 ? cs[3] : cs[1];
@@ -305,9 +337,14 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
             k1 += __shfl_xor((double)(b5 ? cs[1] : cs[3]), 32, kWave);
             double v = b4 ? k1 : k0;
             v += __shfl_xor(b4 ? k0 : k1, 16, kWave);
-            if (q * 16 + r < SB)
-                colp[((((size_t)(b * H + h) * nc + c) * nrb + lb) * 4 + wave) * Q + sb * SB + q * 16 + r] = v;
+            csum[(hh - h0) & 1][wave][q * 16 + r] = v;
         }
+        // (the previous head's, visible since this head's barrier)
+        if (hh > h0) put_cols(hh - 1);
+    }
+    if (h0 < h1) {
+        __syncthreads();
+        put_cols(h1 - 1);
     }
     if (active) {
 #pragma unroll
@@ -1046,7 +1083,7 @@ kb_ddt(const float *__restrict__ roff, const float *__restrict__ dint,
     if (in) {
         const int kb = tid / SB;
         for (int lb = kb; lb < nrb; ++lb)
-            for (int w = 0; w < 4; ++w) cr += colp[((tbase + lb) * 4 + w) * Q + tid];
+            cr += colp[(tbase + lb) * Q + tid];
         for (int sb = 0; sb <= kb; ++sb) cr -= rowp[(tbase + sb) * Q + tid];
     }
     const double rect = block_scan_f64(cr, s_tot) - cr;

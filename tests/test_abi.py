@@ -362,7 +362,7 @@ def test_backward_workspace_size(lib):
     adjoint chunk products (a state per chunk), fp64 chunk-end products per
     state slice, three per-token vectors per head, the summed score tiles
     (a C B^T-sized block in the io type), the per-tile strict row sums and
-    per-tile-and-wave column sums, the dD / dA partial sums, and the head
+    column sums, the dD / dA partial sums, and the head
     groups' partial dB and dC."""
     b, L, H, P, N, G, Q = 4, 8192, 80, 64, 128, 1, 256
     nc, nsl, nrb = L // Q, (P * N + 1023) // 1024, Q // 64
@@ -377,7 +377,7 @@ def test_backward_workspace_size(lib):
     # -> 2 head groups of 40 for about 2048, each with fp32 partial tiles
     nhw = 2
     extra = (b * nc * H * P * N * 4 + b * nc * H * nsl * 8 + 3 * b * H * nc * Q * 4 +
-             b * nc * G * Q * Q * 2 + b * H * nc * nrb * Q * 8 + b * H * nc * nrb * 4 * Q * 8 +
+             b * nc * G * Q * Q * 2 + b * H * nc * nrb * Q * 8 + b * H * nc * nrb * Q * 8 +
              b * nc * H * nrb * 4 + b * nc * H * 8 + 2 * nhg * b * L * G * N * 4 +
              nhw * b * nc * G * Q * Q * 4)
     assert out.value >= fwd_split + extra and out.value - (fwd_split + extra) < 16 * 256
