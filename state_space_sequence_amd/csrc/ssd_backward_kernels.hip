@@ -189,13 +189,22 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     extern __shared__ __align__(16) unsigned char smem_raw[];
     T *xs = reinterpret_cast<T *>(smem_raw);
     const int XP = P + (sizeof(T) == 4 ? 4 : 8), xchunks = P / VEC, xtotal = SB * xchunks;
+    // vector v of the block is row v / xchunks, chunk v % xchunks; the
+    // quotient from a float product, exact here (v < 2^11, xchunks <= 32:
+    // (v + 1/2) / xchunks is at least 1 / 64 from an integer)
+    const float xrcp = 1.f / (float)xchunks;
+    auto xrow = [&](int v) -> int { return (int)(((float)v + 0.5f) * xrcp); };
+    auto xlds = [&](int v) -> int {
+        const int row = xrow(v);
+        return row * XP + (v - row * xchunks) * VEC;
+    };
     // vectors per thread held across a head (the rest are loaded in place):
     // fp32 a headdim of 64; bf16 half of it, which keeps the kernel within
     // 128 VGPRs (four waves per SIMD, against three with the whole head)
     constexpr int XPF = sizeof(T) == 4 ? 4 : 1;
     frag xpre[XPF];
     auto xsrc = [&](int hh, int v) -> frag {
-        const int row = v / xchunks, k = (v % xchunks) * VEC, ts = c * Q + sb * SB + row;
+        const int row = xrow(v), k = (v - row * xchunks) * VEC, ts = c * Q + sb * SB + row;
         return ts < L ? load_frag(x + (((size_t)b * L + ts) * H + g * hpg + hh) * P + k) : zero_frag<T>();
     };
     auto prefetch = [&](int hh) {
@@ -244,10 +253,10 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
 #pragma unroll
         for (int u = 0; u < XPF; ++u) {
             const int v = tid + 256 * u;
-            if (v < xtotal) *reinterpret_cast<frag *>(xb + (v / xchunks) * XP + (v % xchunks) * VEC) = xpre[u];
+            if (v < xtotal) *reinterpret_cast<frag *>(xb + xlds(v)) = xpre[u];
         }
         for (int v = tid + 256 * XPF; v < xtotal; v += 256)
-            *reinterpret_cast<frag *>(xb + (v / xchunks) * XP + (v % xchunks) * VEC) = xsrc(hh, v);
+            *reinterpret_cast<frag *>(xb + xlds(v)) = xsrc(hh, v);
         __syncthreads();
         if (hh + 1 < h1) {
             prefetch(hh + 1);
