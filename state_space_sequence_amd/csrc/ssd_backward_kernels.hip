@@ -203,10 +203,15 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
     // 128 VGPRs (four waves per SIMD, against three with the whole head)
     constexpr int XPF = sizeof(T) == 4 ? 4 : 1;
     frag xpre[XPF];
+    // (addresses: a base per block and head, plus a 32-bit offset per lane)
+    const int HP = H * P;
+    const T *xblk = x + ((size_t)b * L + (size_t)c * Q + sb * SB) * HP + (size_t)g * hpg * P;
     auto xsrc = [&](int hh, int v) -> frag {
-        const int row = xrow(v), k = (v - row * xchunks) * VEC, ts = c * Q + sb * SB + row;
-        return ts < L ? load_frag(x + (((size_t)b * L + ts) * H + g * hpg + hh) * P + k) : zero_frag<T>();
+        const int row = xrow(v), k = (v - row * xchunks) * VEC;
+        return c * Q + sb * SB + row < L ? load_frag(xblk + (size_t)hh * P + (row * HP + k)) : zero_frag<T>();
     };
+    const int tr = c * Q + lb * SB + wave * 16 + r;   // this lane's dy row
+    const T *dyrow = dy + ((size_t)b * L + c * Q + lb * SB + wave * 16) * HP + (size_t)g * hpg * P + r * HP;
     auto prefetch = [&](int hh) {
 #pragma unroll
         for (int u = 0; u < XPF; ++u)
@@ -267,8 +272,7 @@ kb_wsum(const T *__restrict__ x, const T *__restrict__ dy, const float *__restri
         if (active) {
             // scores dy_l . x_s over the headdim
             f32x4 z[4] = {zero4(), zero4(), zero4(), zero4()};
-            const int tr = c * Q + lb * SB + wave * 16 + r;
-            const T *arow = dy + (((size_t)b * L + tr) * H + h) * P;
+            const T *arow = dyrow + (size_t)hh * P;
             for (int k0 = 0; k0 < P; k0 += KS) {
                 const int k = k0 + VEC * q;
                 const frag za = tr < L && k < P ? load_frag(arow + k) : zero_frag<T>();
