@@ -383,3 +383,18 @@ def test_backward_workspace_size(lib):
     assert out.value >= fwd_split + extra and out.value - (fwd_split + extra) < 16 * 256
     assert lib.ssd_chunk_scan_bwd_workspace_size(b, L, H, P, N, 3, Q, 1, ctypes.byref(out)) == 1
     assert lib.ssd_chunk_scan_bwd_max_kernels() == 9
+
+
+def test_float_quotient_of_staging_indexes_is_exact():
+    """The gradient pass's score-tile kernel splits a vector index v of its
+    x staging into (row, chunk) as floor((v + 1/2) * fp32(1 / n)) in fp32
+    arithmetic, n = headdim / vector width.  The kernel relies on that being
+    the integer quotient v // n for every index it forms (v below 64 rows x
+    32 chunks) and every n it can see (headdim a multiple of 16, at most 128:
+    n from 2 to 32); this checks all of them in the same fp32 arithmetic."""
+    import numpy as np
+    v = np.arange(0, 64 * 32, dtype=np.int64)
+    for n in range(1, 33):
+        rcp = np.float32(1.0) / np.float32(n)
+        q = ((v.astype(np.float32) + np.float32(0.5)) * rcp).astype(np.float32)
+        assert np.array_equal(np.floor(q).astype(np.int64), v // n), n
