@@ -923,13 +923,23 @@ kb_mix(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ 
             if constexpr (MODE == kDc) {
                 // the state part of <dy, y - D x>, per row (row 4 q + i's
                 // in lanes 4 i ..)
-                float v[4];
+                float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int i = 0; i < 4; ++i) {
-                    v[i] = 0.f;
+                for (int wt = 0; wt < NW; ++wt) {
+                    // C at this lane's accumulator positions (rows 4 q + i,
+                    // column 16 wt + r): bf16 one transposing read
+                    float cv[4];
+                    if constexpr (F32) {
 #pragma unroll
-                    for (int wt = 0; wt < NW; ++wt)
-                        v[i] += to_f32(VS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]) * acc[wt][i];
+                        for (int i = 0; i < 4; ++i) cv[i] = to_f32(VS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]);
+                    } else {
+                        const kb_bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((kb_lds_bf16x4 *)(
+                            (kb_lds_u8 *)VS + ((wave * 16 + 4 * q + (r >> 2)) * VP + wt * 16 + 4 * (r & 3)) * 2));
+#pragma unroll
+                        for (int i = 0; i < 4; ++i) cv[i] = (float)t[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] += cv[i] * acc[wt][i];
                 }
                 const float sv = row16_sum4(v, r);
                 const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
