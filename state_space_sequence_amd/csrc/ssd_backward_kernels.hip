@@ -589,13 +589,22 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
             }
         }
     }
-    // x at this lane's output positions (rows 4 q + i of the wave's 16,
-    // columns 16 wt + r)
-    auto xat = [&](int i, int wt) -> float {
-        if constexpr (XST)
-            return to_f32(XS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]);
-        else
-            return xv[i][wt];
+    // a row-major bf16 tile's values at this lane's output positions (rows
+    // 4 q + i of the wave's 16, column 16 wt + r): one transposing read
+    auto tr4 = [&](const T *tile, int wt, float (&o)[4]) {
+        const kb_bf16x4 t = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((kb_lds_bf16x4 *)(
+            (kb_lds_u8 *)tile + ((wave * 16 + 4 * q + (r >> 2)) * VP + wt * 16 + 4 * (r & 3)) * 2));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) o[i] = (float)t[i];
+    };
+    // x at those positions
+    auto xat4 = [&](int wt, float (&o)[4]) {
+        if constexpr (XST) {
+            tr4(XS, wt, o);
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) o[i] = xv[i][wt];
+        }
     };
     __syncthreads();
     const float e_te = fast_exp(prefix_diff(r_hi[Q - 1], r_lo[Q - 1], r_hi[te], r_lo[te]));
@@ -640,14 +649,16 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     }
     if (active) {
         // the state part of x . u, per row (row 4 q + i's in lanes 4 i ..)
-        float v[4];
+        float v[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            v[i] = 0.f;
+        for (int wt = 0; wt < NW; ++wt) {
+            float xs[4];
+            xat4(wt, xs);
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) v[i] += xat(i, wt) * acc[wt][i];
-            v[i] *= rowf[i];
+            for (int i = 0; i < 4; ++i) v[i] += xs[i] * acc[wt][i];
         }
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] *= rowf[i];
         const float sv = row16_sum4(v, r);
         const int l = lb * SB + wave * 16 + 4 * q + (r >> 2), t = c * Q + l;
         if ((r & 3) == 0 && l < Q) dint[vbase + l] = t < L ? sv : 0.f;
@@ -726,24 +737,34 @@ kb_dx(const T *__restrict__ x, const T *__restrict__ Bm, const T *__restrict__ d
     // those rows), and the workgroup then stores XS by rows.
     if (active) {
         const float Dh = D ? D[h] : 0.f;
-        float dsum = 0.f, ds[4];
+        float dsum = 0.f, ds[4] = {0.f, 0.f, 0.f, 0.f}, dtl[4];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl;
-            const float dtl = r_dt[l];
-            ds[i] = 0.f;
+        for (int i = 0; i < 4; ++i) dtl[i] = r_dt[lb * SB + wave * 16 + 4 * q + i];
 #pragma unroll
-            for (int wt = 0; wt < NW; ++wt) {
-                const int p = wt * 16 + r;
-                const float gv = to_f32(VS[sl * VP + p]), xs = xat(i, wt), u = acc[wt][i];
-                ds[i] += xs * u;
-                dsum += gv * xs;
+        for (int wt = 0; wt < NW; ++wt) {
+            // dy and x at this lane's positions (bf16: read before any of
+            // them is overwritten by dx; each lane writes only its own)
+            float gv[4], xs[4];
+            if constexpr (XST) {
+                tr4(VS, wt, gv);
+            } else {
+#pragma unroll
+                for (int i = 0; i < 4; ++i) gv[i] = to_f32(VS[(wave * 16 + 4 * q + i) * VP + wt * 16 + r]);
+            }
+            xat4(wt, xs);
+            const int p = wt * 16 + r;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int sl = wave * 16 + 4 * q + i, l = lb * SB + sl;
+                const float u = acc[wt][i];
+                ds[i] += xs[i] * u;
+                dsum += gv[i] * xs[i];
                 if constexpr (XST) {
-                    XS[sl * VP + p] = from_f32<T>(Dh * gv + dtl * u);
+                    XS[sl * VP + p] = from_f32<T>(Dh * gv[i] + dtl[i] * u);
                 } else {
                     const int t = c * Q + l;
                     if (t < L && l < Q && p < P)
-                        out[((size_t)b * L * H + h) * P + (size_t)t * H * P + p] = from_f32<T>(Dh * gv + dtl * u);
+                        out[((size_t)b * L * H + h) * P + (size_t)t * H * P + p] = from_f32<T>(Dh * gv[i] + dtl[i] * u);
                 }
             }
         }
